@@ -1,0 +1,127 @@
+"""The routed FP8 expert step end to end (CPU, float64).
+
+TEST INFRASTRUCTURE ONLY: nothing in the product path may import this module.
+
+Steps, in the order of the MindIE-SD ``fused_moe`` execution flow ("执行流程":
+select_experts, dispatch, mlp, combine) with the W8A8 expert step of the metrale
+``fp8_grouped_tc_w8a8.rs`` page (``run_fp8_grouped_w8a8``: quantise the layer input,
+gate+up producing quantised SiLU products, then down):
+
+1. route (``oracle.routing``);
+2. quantise each token row of the hidden state to E4M3 per 128 columns (``oracle.codec``);
+3. gate+up: gu = dequant(xq row) @ dequant(w13[e]), float64.  w13[e] is [H, 2I] with
+   the gate projection in columns [0, I) and the up projection in [I, 2I) (reading of
+   the "gate/up" fused weight in the ``fused_moe`` parameter table);
+4. SwiGLU: h = silu(g) * u = g / (1 + exp(-g)) * u (the "swiglu" activation of the MATE
+   Mega MoE page; no clamp);
+5. re-quantise h per (assignment row, 128 columns of I) to E4M3;
+6. down: o = dequant(hq) @ dequant(w2[e]), w2[e] is [I, H], float64;
+7. combine: y[t] = sum_j w[t, j] * o[(t, j)], float64 (the ``combine`` stage; the MATE
+   page's contiguous bfloat16 output is the caller-side rounding of this value).
+
+Every product of two E4M3 values and two powers of two is exact in float64, so only
+the summation order rounds (relative ~1e-16).
+
+Pins (tests/test_oracle_moe.py): one token, one expert, top-1 equals a dense SwiGLU MLP
+computed by torch in float64 on the dequantised tensors, with the re-quantisation step
+checked separately; combine reduces to a gather for k = 1, w = 1; scaling the routed
+scaling factor scales y; permuting tokens permutes y; a row of y does not depend on the
+other rows.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import codec, routing
+
+
+def silu(g: np.ndarray) -> np.ndarray:
+    return g / (1.0 + np.exp(-g))
+
+
+class QuantizedExperts:
+    """Per-expert E4M3 weights with UE8M0 128x128 block scales, produced on demand.
+
+    ``source(e)`` returns (w13_f32 [H, 2I], w2_f32 [I, H]) as arrays; the oracle
+    quantises them itself and keeps the last few experts."""
+
+    def __init__(self, source, cache: int = 4):
+        self.source = source
+        self.cache = cache
+        self._mem: dict = {}
+
+    def get(self, e: int):
+        if e not in self._mem:
+            w13, w2 = self.source(e)
+            q13, s13 = codec.quant_blocks_128(np.asarray(w13, dtype=np.float64))
+            q2, s2 = codec.quant_blocks_128(np.asarray(w2, dtype=np.float64))
+            if len(self._mem) >= self.cache:
+                self._mem.pop(next(iter(self._mem)))
+            self._mem[e] = (q13, s13, q2, s2)
+        return self._mem[e]
+
+
+def expert_ffn(xq_rows, xs_rows, q13, s13, q2, s2):
+    """One expert on a stack of quantised rows.
+
+    Returns (o float64 [R, H], hq uint8 [R, I], hs uint8 [R, I/128])."""
+    x = codec.dequant_rows_128(xq_rows, xs_rows)
+    w13 = codec.dequant_blocks_128(q13, s13)
+    gu = x @ w13
+    I = w13.shape[1] // 2
+    h = silu(gu[:, :I]) * gu[:, I:]
+    hq, hs = codec.quant_rows_128(h)
+    o = codec.dequant_rows_128(hq, hs) @ codec.dequant_blocks_128(q2, s2)
+    return o, hq, hs
+
+
+def combine(o_flat: np.ndarray, weights: np.ndarray) -> np.ndarray:
+    """y[t] = sum_j weights[t, j] * o_flat[t*k + j]."""
+    T, k = weights.shape
+    o = o_flat.reshape(T, k, -1)
+    return (weights[:, :, None] * o).sum(axis=1)
+
+
+def forward(x_f64, ids, weights, experts: QuantizedExperts, tokens=None):
+    """Expert step for the given routing.
+
+    x_f64 [T, H]: exact values of the bfloat16 hidden state.  ids/weights [T, k].
+    tokens: optional array of token indices; only those rows of y are computed.
+    Returns a dict with y float64 [len(tokens), H], o [len(tokens)*k, H] in flat
+    (t, j) order, hq/hs by assignment, xq/xs of the tokens."""
+    T, k = ids.shape
+    tok = np.arange(T) if tokens is None else np.asarray(tokens)
+    xq, xs = codec.quant_rows_128(x_f64[tok])
+    sub_ids = ids[tok]
+    n = len(tok)
+    H = x_f64.shape[1]
+    o = np.zeros((n * k, H))
+    hq = hs = None
+    flat_ids = sub_ids.reshape(-1)
+    for e in np.unique(flat_ids):
+        rows = np.nonzero(flat_ids == e)[0]            # flat positions (t_local*k + j)
+        q13, s13, q2, s2 = experts.get(int(e))
+        oe, hqe, hse = expert_ffn(xq[rows // k], xs[rows // k], q13, s13, q2, s2)
+        if hq is None:
+            hq = np.zeros((n * k, hqe.shape[1]), dtype=np.uint8)
+            hs = np.zeros((n * k, hse.shape[1]), dtype=np.uint8)
+        o[rows] = oe
+        hq[rows] = hqe
+        hs[rows] = hse
+    y = combine(o, np.asarray(weights, dtype=np.float64)[tok])
+    return {"y": y, "o": o, "hq": hq, "hs": hs, "xq": xq, "xs": xs, "tokens": tok}
+
+
+def route_workload(inputs: dict, p: routing.RouteParams, prelude=None):
+    """Routing for either given logits or the gate prelude.
+
+    prelude: None or (norm_w, router_w, pe_scale, eps).  Returns (ids, weights, margin)
+    where margin is the near-tie measure for scores the device must compute (group
+    scores in mode 1, prelude logits); inf where selection is exact."""
+    if prelude is None:
+        ids, w, gm = routing.route(inputs["logits"], p)
+        margin = gm if p.group_select_mode == 1 and p.group_count > 1 else np.full(len(ids), np.inf)
+        return ids, w, margin
+    norm_w, router_w, pe_scale, eps = prelude
+    ids, w, _, m = routing.route_prelude(inputs["x"], norm_w, router_w, pe_scale, eps, p.top_k)
+    return ids, w * p.routed_scaling_factor, m

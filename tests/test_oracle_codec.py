@@ -1,0 +1,134 @@
+"""Pins of the oracle's E4M3 / UE8M0 codecs and scale rule (CPU only)."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import codec
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def torch_decode_all():
+    return torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_decode_matches_torch_on_all_codes():
+    ours = codec.e4m3_decode_table()
+    ref = torch_decode_all()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(ours[~nan]), np.signbit(ref[~nan]))
+    assert nan.sum() == 2 and ours[0x7E] == 448.0
+
+
+def test_golden_hand_encodings():
+    with open(os.path.join(GOLDEN, "e4m3_hand.txt")) as f:
+        rows = [ln.split()[:2] for ln in f if ln.strip() and not ln.startswith("#")]
+    assert len(rows) >= 10
+    for val, code in rows:
+        assert int(codec.e4m3_encode(np.array([float(val)]))[0]) == int(code, 16), val
+
+
+def test_roundtrip_all_finite_codes():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    assert np.array_equal(codec.e4m3_encode(codec.e4m3_decode(codes)), codes)
+
+
+def _midpoint_set():
+    mags = codec.e4m3_decode_table()[:127]
+    mids = (mags[:-1] + mags[1:]) / 2
+    v = np.concatenate([mids, np.nextafter(mids, np.inf), np.nextafter(mids, -np.inf), mags])
+    return np.concatenate([v, -v])
+
+
+def test_encode_matches_bruteforce():
+    rng = np.random.default_rng(0)
+    v = np.concatenate([_midpoint_set(), rng.normal(0, 100, 2000), rng.normal(0, 0.01, 2000),
+                        [0.0, -0.0, 448.0, 449.0, 1e9, -1e9, 1e-30, -1e-30]])
+    assert np.array_equal(codec.e4m3_encode(v), codec.e4m3_encode_bruteforce(v))
+
+
+def test_encode_matches_torch_cast_in_range():
+    # every bfloat16 bit pattern times 2^s, plus all midpoints; torch saturates differently
+    # above 448 (NaN), so compare only |v| <= 448 -- the scale rule never exceeds it.
+    # torch casts float64 through float32 (rounding twice), so only float32 values are used.
+    pats = (np.arange(65536, dtype=np.uint32) << 16).view(np.float32)
+    pats = pats[np.isfinite(pats) & (np.abs(pats) < 1e30)].astype(np.float64)
+    vals = [pats * 2.0 ** s for s in (-8, 0, 6)] + [_midpoint_set()]
+    v = np.concatenate(vals)
+    v = v[np.isfinite(v) & (np.abs(v) <= 448.0)]
+    v = v[v.astype(np.float32).astype(np.float64) == v]
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codec.e4m3_encode(v), ref)
+
+
+def test_ue8m0_exhaustive():
+    b = np.arange(255)
+    vals = codec.ue8m0_decode(b)
+    assert np.array_equal(vals, np.ldexp(1.0, b - 127))
+    assert np.array_equal(codec.ue8m0_encode(b - 127), b.astype(np.uint8))
+    assert np.isnan(codec.ue8m0_decode(np.array([255]))[0])
+    with pytest.raises(ValueError):
+        codec.ue8m0_encode(np.array([128]))
+
+
+def test_scale_exponent_hand_values():
+    cases = {448.0: 0, np.nextafter(448.0, 1e9): 1, 224.0: -1, np.nextafter(224.0, 1e9): 0,
+             1.0: -8, 1.75: -8, np.nextafter(1.75, 9): -7, 0.0: 0, 1e-300: -127, 1e300: 127,
+             2.0 ** -7: -15, 2.0 ** -6: -14}
+    for a, e in cases.items():
+        assert int(codec.scale_exponent(np.array([a]))[0]) == e, a
+
+
+def test_scale_exponent_invariant():
+    rng = np.random.default_rng(1)
+    amax = np.exp(rng.uniform(-60, 60, 100000))
+    e = codec.scale_exponent(amax)
+    r = amax / np.ldexp(1.0, e)
+    assert ((r > 224.0) & (r <= 448.0)).all()
+
+
+def test_quant_rows_roundtrip_on_representable_groups():
+    rng = np.random.default_rng(2)
+    R, C = 37, 384
+    codes = rng.integers(0, 256, (R, C)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x10
+    e = rng.integers(-20, 20, (R, C // 128))
+    vals = codec.e4m3_decode(codes).reshape(R, C // 128, 128)
+    vals[:, :, 5] = 448.0            # force amax = 448 * 2^e
+    x = (vals * np.ldexp(1.0, e)[:, :, None]).reshape(R, C)
+    q, s = codec.quant_rows_128(x)
+    assert np.array_equal(codec.dequant_rows_128(q, s), x)
+    assert np.array_equal(s.astype(np.int64) - 127, e)
+
+
+def test_quant_rows_group_max_in_expected_set():
+    rng = np.random.default_rng(3)
+    x = rng.normal(0, 1, (64, 512))
+    q, s = codec.quant_rows_128(x)
+    mx = np.abs(codec.e4m3_decode(q)).reshape(64, 4, 128).max(axis=2)
+    # amax / 2^e lies in (224, 448]; E4M3 values there are 224 (reached from (224, 232)),
+    # 240, 256, then steps of 32 up to 448
+    assert set(np.unique(mx)) <= {224.0, 240.0, 256.0, 288.0, 320.0, 352.0, 384.0, 416.0, 448.0}
+
+
+def test_quant_blocks_scales_per_block():
+    rng = np.random.default_rng(4)
+    w = rng.normal(0, 0.02, (256, 384))
+    w[128:, :128] *= 16.0
+    q, s = codec.quant_blocks_128(w)
+    assert s.shape == (2, 3)
+    assert int(s[1, 0]) - int(s[0, 0]) in (3, 4, 5)
+    # each block's largest |code value| is in the [224, 448] band
+    d = np.abs(codec.e4m3_decode(q)).reshape(2, 128, 3, 128).max(axis=(1, 3))
+    assert ((d >= 224) & (d <= 448)).all()
+    rt = codec.dequant_blocks_128(q, s)
+    assert np.abs(rt - w).max() <= np.abs(w).max() * 2.0 ** -3
+
+
+def test_negative_underflow_keeps_sign():
+    q = codec.e4m3_encode(np.array([-1e-6, 1e-6, -0.0, 0.0]))
+    assert list(q) == [0x80, 0x00, 0x80, 0x00]

@@ -1,0 +1,110 @@
+"""Pins of the oracle's expert FFN and combine (CPU only)."""
+import os
+
+import numpy as np
+import torch
+
+from oracle import codec, moe, routing
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _experts_from_dense(w13s, w2s):
+    return moe.QuantizedExperts(lambda e: (w13s[e], w2s[e]), cache=64)
+
+
+def test_golden_hand_ffn():
+    g = {}
+    with open(os.path.join(GOLDEN, "ffn_hand.txt")) as f:
+        for ln in f:
+            if ln.strip() and not ln.startswith("#"):
+                key, val = ln.split()
+                g[key] = val
+    H = I = 128
+    x = np.full((1, H), float(g["x"]))
+    w13 = np.concatenate([np.full((H, I), float(g["w13_gate"])), np.full((H, I), float(g["w13_up"]))], axis=1)
+    w2 = np.full((I, H), float(g["w2"]))
+    ids = np.zeros((1, 1), np.int32)
+    w = np.ones((1, 1))
+    out = moe.forward(x, ids, w, _experts_from_dense([w13], [w2]))
+    assert (out["xq"] == int(g["xq"], 16)).all() and (out["xs"] == int(g["xs"])).all()
+    assert (out["hq"] == int(g["hq"], 16)).all() and (out["hs"] == int(g["hs"])).all()
+    assert (out["y"] == float(g["y"])).all()
+    q13, s13 = codec.quant_blocks_128(w13)
+    assert list(s13[0]) == [112, 113]
+
+
+def test_single_token_single_expert_is_dense_swiglu_mlp():
+    rng = np.random.default_rng(20)
+    H, I = 256, 384
+    x = torch.randn(1, H, generator=torch.Generator().manual_seed(1)).to(torch.bfloat16).double().numpy()
+    w13 = rng.normal(0, 0.02, (H, 2 * I))
+    w2 = rng.normal(0, 0.02, (I, H))
+    ex = _experts_from_dense([w13], [w2])
+    out = moe.forward(x, np.zeros((1, 1), np.int32), np.ones((1, 1)), ex)
+    # textbook dense SwiGLU MLP in torch float64 on the dequantised operands
+    q13, s13, q2, s2 = ex.get(0)
+    xd = torch.from_numpy(codec.dequant_rows_128(out["xq"], out["xs"]))
+    w13d = torch.from_numpy(codec.dequant_blocks_128(q13, s13))
+    w2d = torch.from_numpy(codec.dequant_blocks_128(q2, s2))
+    gu = xd @ w13d
+    h = torch.nn.functional.silu(gu[:, :I]) * gu[:, I:]
+    hq, hs = codec.quant_rows_128(h.numpy())
+    assert np.array_equal(hq, out["hq"]) and np.array_equal(hs, out["hs"])
+    y = torch.from_numpy(codec.dequant_rows_128(hq, hs)) @ w2d
+    np.testing.assert_allclose(out["y"], y.numpy(), rtol=1e-12, atol=1e-15)
+    # and the quantised input really is the per-128 quantisation of x
+    q, s = codec.quant_rows_128(x)
+    assert np.array_equal(q, out["xq"]) and np.array_equal(s, out["xs"])
+
+
+def _random_case(T=12, H=256, I=256, E=4, k=2, seed=0):
+    rng = np.random.default_rng(seed)
+    x = torch.from_numpy(rng.normal(0, 1, (T, H))).to(torch.bfloat16).double().numpy()
+    w13 = [rng.normal(0, 0.02, (H, 2 * I)) for _ in range(E)]
+    w2 = [rng.normal(0, 0.02, (I, H)) for _ in range(E)]
+    logits = rng.normal(0, 1, (T, E)).astype(np.float32)
+    return x, logits, _experts_from_dense(w13, w2)
+
+
+def test_combine_k1_w1_is_gather():
+    x, logits, ex = _random_case(k=1)
+    ids = np.argmax(logits, axis=1).astype(np.int32)[:, None]
+    out = moe.forward(x, ids, np.ones_like(ids, dtype=np.float64), ex)
+    assert np.array_equal(out["y"], out["o"])
+
+
+def test_routed_scaling_factor_is_linear():
+    x, logits, ex = _random_case()
+    p1 = routing.RouteParams(4, 2, "softmax", True, routed_scaling_factor=1.0)
+    p2 = routing.RouteParams(4, 2, "softmax", True, routed_scaling_factor=2.5)
+    ids1, w1, _ = routing.route(logits, p1)
+    ids2, w2, _ = routing.route(logits, p2)
+    assert np.array_equal(ids1, ids2)
+    y1 = moe.forward(x, ids1, w1, ex)["y"]
+    y2 = moe.forward(x, ids2, w2, ex)["y"]
+    np.testing.assert_allclose(y2, 2.5 * y1, rtol=1e-12, atol=1e-14)
+
+
+def test_token_permutation_equivariance_and_row_independence():
+    x, logits, ex = _random_case(T=10, seed=3)
+    p = routing.RouteParams(4, 2, "softmax", True)
+    ids, w, _ = routing.route(logits, p)
+    y = moe.forward(x, ids, w, ex)["y"]
+    perm = np.random.default_rng(4).permutation(10)
+    idsP, wP, _ = routing.route(logits[perm], p)
+    yP = moe.forward(x[perm], idsP, wP, ex)["y"]
+    assert np.array_equal(yP, y[perm])
+    # a sample of rows equals the same rows of the full batch, bit for bit
+    ys = moe.forward(x, ids, w, ex, tokens=np.array([7, 2]))["y"]
+    assert np.array_equal(ys, y[[7, 2]])
+
+
+def test_combine_matches_explicit_sum():
+    rng = np.random.default_rng(5)
+    o = rng.normal(0, 1, (6 * 3, 16))
+    w = rng.uniform(0, 1, (6, 3))
+    y = moe.combine(o, w)
+    for t in range(6):
+        ref = sum(w[t, j] * o[t * 3 + j] for j in range(3))
+        np.testing.assert_allclose(y[t], ref, rtol=1e-15, atol=1e-15)
