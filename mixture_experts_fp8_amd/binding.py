@@ -1,0 +1,322 @@
+"""Thin ctypes binding of libmoe_fp8.so (the C ABI declared in include/moe_fp8.h).
+
+Each function takes torch tensors that already live on the GPU, checks dtypes and
+shapes only as far as needed to marshal pointers, and calls the C entry point of the
+same name on the current HIP stream.  No step of the MoE computation runs here: if the
+library is missing the call fails loudly; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libmoe_fp8.so")
+
+MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_SCORING_SOFTMAX, MOE_SCORING_SIGMOID = 0, 1
+MOE_ROUTE_IDS_GIVEN = 1
+MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
+MOE_FUSED_EXPERT_OUT_BF16 = 1
+
+EXPORTED = ["moe_route", "moe_route_workspace_size", "moe_quant_act", "moe_quant_weight_blocks",
+            "moe_prepack_weights", "moe_grouped_ffn", "moe_ffn_workspace_size", "moe_combine",
+            "moe_fused", "moe_workspace_size", "moe_last_error"]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+class RouteParams(ctypes.Structure):
+    _fields_ = [("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("scoring", ctypes.c_int32),
+                ("renormalize", ctypes.c_int32), ("group_count", ctypes.c_int32), ("k_group", ctypes.c_int32),
+                ("group_select_mode", ctypes.c_int32), ("routed_scaling_factor", ctypes.c_float)]
+
+
+class GatePrelude(ctypes.Structure):
+    _fields_ = [("norm_weight", ctypes.c_void_p), ("router_weight", ctypes.c_void_p),
+                ("per_expert_scale", ctypes.c_void_p), ("rms_eps", ctypes.c_float)]
+
+
+class FfnArgs(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("k", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
+                ("E", ctypes.c_int32), ("xq", ctypes.c_void_p), ("xs", ctypes.c_void_p),
+                ("expert_counts", ctypes.c_void_p), ("expert_offsets", ctypes.c_void_p),
+                ("sorted_assign", ctypes.c_void_p), ("w13", ctypes.c_void_p), ("w13_scale", ctypes.c_void_p),
+                ("w2", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p), ("expert_out", ctypes.c_void_p),
+                ("out_dtype", ctypes.c_int32), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p)]
+
+
+class FusedArgs(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32), ("route", RouteParams),
+                ("hidden_states", ctypes.c_void_p), ("router_logits", ctypes.c_void_p),
+                ("prelude", ctypes.POINTER(GatePrelude)), ("w13", ctypes.c_void_p),
+                ("w13_scale", ctypes.c_void_p), ("w2", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("topk_ids", ctypes.c_void_p), ("topk_weights", ctypes.c_void_p),
+                ("expert_counts", ctypes.c_void_p), ("flags", ctypes.c_int32), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe_fp8.so (built by python -m mixture_experts_fp8_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m mixture_experts_fp8_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        L.moe_last_error.restype = ctypes.c_char_p
+        L.moe_last_error.argtypes = []
+        L.moe_route.restype = ctypes.c_int
+        L.moe_route.argtypes = [ctypes.POINTER(RouteParams), i32, vp, vp, i32, ctypes.POINTER(GatePrelude), i32,
+                                vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_route_workspace_size.restype = sz
+        L.moe_route_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+        L.moe_quant_act.restype = ctypes.c_int
+        L.moe_quant_act.argtypes = [vp, i32, i32, i64, vp, vp, vp]
+        L.moe_quant_weight_blocks.restype = ctypes.c_int
+        L.moe_quant_weight_blocks.argtypes = [vp, i32, i32, i32, vp, vp, vp]
+        L.moe_prepack_weights.restype = ctypes.c_int
+        L.moe_prepack_weights.argtypes = [vp, i32, i32, i32, vp, vp]
+        L.moe_grouped_ffn.restype = ctypes.c_int
+        L.moe_grouped_ffn.argtypes = [ctypes.POINTER(FfnArgs)]
+        L.moe_ffn_workspace_size.restype = sz
+        L.moe_ffn_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+        L.moe_combine.restype = ctypes.c_int
+        L.moe_combine.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp, vp]
+        L.moe_fused.restype = ctypes.c_int
+        L.moe_fused.argtypes = [ctypes.POINTER(FusedArgs)]
+        L.moe_workspace_size.restype = sz
+        L.moe_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+        _lib = L
+    return _lib
+
+
+def moe_last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def _check(rc: int) -> None:
+    if rc != MOE_OK:
+        raise MoeError(rc, moe_last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None) -> None:
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name}: must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A uint8 device buffer whose data pointer is 256-byte aligned."""
+    buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    off = (-buf.data_ptr()) % 256
+    return buf[off:off + nbytes]
+
+
+def route_params(num_experts: int, top_k: int, scoring: str = "softmax", renormalize: bool = False,
+                 group_count: int = 1, k_group: int = 1, group_select_mode: int = 0,
+                 routed_scaling_factor: float = 1.0) -> RouteParams:
+    sc = {"softmax": MOE_SCORING_SOFTMAX, "sigmoid": MOE_SCORING_SIGMOID}[scoring]
+    return RouteParams(num_experts, top_k, sc, int(bool(renormalize)), group_count, k_group,
+                       group_select_mode, routed_scaling_factor)
+
+
+@dataclass
+class Prelude:
+    norm_weight: torch.Tensor        # [H] f32
+    router_weight: torch.Tensor      # [E, H] f32
+    per_expert_scale: Optional[torch.Tensor]   # [E] f32
+    rms_eps: float = 1e-6
+
+    def c(self) -> GatePrelude:
+        return GatePrelude(_ptr(self.norm_weight), _ptr(self.router_weight), _ptr(self.per_expert_scale),
+                           self.rms_eps)
+
+
+# ---- entry points ---------------------------------------------------------------------
+
+def moe_quant_act(x: torch.Tensor):
+    """x bf16 [rows, cols] -> (xq uint8 [rows, cols] E4M3, xs uint8 [rows, cols/128] UE8M0)."""
+    _need(x, "x", torch.bfloat16)
+    rows, cols = x.shape
+    xq = torch.empty(rows, cols, dtype=torch.uint8, device=x.device)
+    xs = torch.empty(rows, max(cols // 128, 1), dtype=torch.uint8, device=x.device)
+    _check(lib().moe_quant_act(_ptr(x), rows, cols, cols, _ptr(xq), _ptr(xs), _stream()))
+    return xq, xs
+
+
+def moe_quant_weight_blocks(w: torch.Tensor):
+    """w f32 [E, K, N] -> (q uint8 [E, K, N] E4M3, scale uint8 [E, K/128, N/128])."""
+    _need(w, "w", torch.float32)
+    E, K, N = w.shape
+    q = torch.empty(E, K, N, dtype=torch.uint8, device=w.device)
+    s = torch.empty(E, max(K // 128, 1), max(N // 128, 1), dtype=torch.uint8, device=w.device)
+    _check(lib().moe_quant_weight_blocks(_ptr(w), E, K, N, _ptr(q), _ptr(s), _stream()))
+    return q, s
+
+
+def moe_prepack_weights(w: torch.Tensor) -> torch.Tensor:
+    """Logical E4M3 [E, K, N] -> packed layout (same number of bytes, flat)."""
+    _need(w, "w", torch.uint8)
+    E, K, N = w.shape
+    out = torch.empty(E * K * N, dtype=torch.uint8, device=w.device)
+    _check(lib().moe_prepack_weights(_ptr(w), E, K, N, _ptr(out), _stream()))
+    return out
+
+
+def moe_route(params: RouteParams, T: int, router_logits: Optional[torch.Tensor] = None,
+              hidden_states: Optional[torch.Tensor] = None, prelude: Optional[Prelude] = None,
+              topk_ids: Optional[torch.Tensor] = None, topk_weights: Optional[torch.Tensor] = None,
+              device=None):
+    """Routing + dispatch.  With topk_ids/topk_weights given, only the dispatch runs.
+
+    Returns dict(topk_ids, topk_weights, expert_counts, expert_offsets, sorted_assign, assign_pos)."""
+    E, k = params.num_experts, params.top_k
+    dev = device or (router_logits.device if router_logits is not None else hidden_states.device)
+    flags = 0
+    if topk_ids is not None:
+        flags = MOE_ROUTE_IDS_GIVEN
+        _need(topk_ids, "topk_ids", torch.int32, (T, k))
+        _need(topk_weights, "topk_weights", torch.float32, (T, k))
+    else:
+        topk_ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+        topk_weights = torch.empty(T, k, dtype=torch.float32, device=dev)
+        if router_logits is not None:
+            _need(router_logits, "router_logits", torch.float32, (T, E))
+    H = 0
+    if hidden_states is not None:
+        _need(hidden_states, "hidden_states", torch.bfloat16)
+        H = hidden_states.shape[1]
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sorted_assign = torch.empty(T * k, dtype=torch.int32, device=dev)
+    assign_pos = torch.empty(T * k, dtype=torch.int32, device=dev)
+    with_pre = int(prelude is not None and flags == 0)
+    nbytes = lib().moe_route_workspace_size(T, E, k, H, with_pre)
+    ws = workspace(max(nbytes, 256), dev)
+    pre = ctypes.byref(prelude.c()) if prelude is not None else None
+    _check(lib().moe_route(ctypes.byref(params), T, _ptr(router_logits), _ptr(hidden_states), H, pre, flags,
+                           _ptr(topk_ids), _ptr(topk_weights), _ptr(counts), _ptr(offsets), _ptr(sorted_assign),
+                           _ptr(assign_pos), _ptr(ws), ws.numel(), _stream()))
+    return {"topk_ids": topk_ids, "topk_weights": topk_weights, "expert_counts": counts,
+            "expert_offsets": offsets, "sorted_assign": sorted_assign, "assign_pos": assign_pos}
+
+
+@dataclass
+class PackedWeights:
+    """Expert weights in the packed layout plus their logical UE8M0 block scales."""
+    E: int
+    H: int
+    I: int
+    w13: torch.Tensor       # packed [E*H*2I]
+    w13_scale: torch.Tensor  # [E, H/128, 2I/128]
+    w2: torch.Tensor        # packed [E*I*H]
+    w2_scale: torch.Tensor  # [E, I/128, H/128]
+
+    @staticmethod
+    def from_logical(w13q: torch.Tensor, w13s: torch.Tensor, w2q: torch.Tensor, w2s: torch.Tensor) -> "PackedWeights":
+        E, H, I2 = w13q.shape
+        return PackedWeights(E, H, I2 // 2, moe_prepack_weights(w13q), w13s.contiguous(),
+                             moe_prepack_weights(w2q), w2s.contiguous())
+
+
+def moe_grouped_ffn(xq: torch.Tensor, xs: torch.Tensor, routing: dict, w: PackedWeights, k: int,
+                    out_dtype=torch.float32) -> torch.Tensor:
+    """Both expert GEMMs; returns expert_out [T*k, H] in expert-sorted slot order."""
+    T, H = xq.shape
+    dt = {torch.float32: MOE_DTYPE_F32, torch.bfloat16: MOE_DTYPE_BF16}[out_dtype]
+    out = torch.empty(T * k, H, dtype=out_dtype, device=xq.device)
+    nbytes = lib().moe_ffn_workspace_size(T, H, w.I, w.E, k)
+    ws = workspace(max(nbytes, 256), xq.device)
+    a = FfnArgs(T, k, H, w.I, w.E, _ptr(xq), _ptr(xs), _ptr(routing["expert_counts"]),
+                _ptr(routing["expert_offsets"]), _ptr(routing["sorted_assign"]), _ptr(w.w13), _ptr(w.w13_scale),
+                _ptr(w.w2), _ptr(w.w2_scale), _ptr(out), dt, _ptr(ws), ws.numel(), _stream())
+    _check(lib().moe_grouped_ffn(ctypes.byref(a)))
+    return out
+
+
+def moe_combine(expert_out: torch.Tensor, assign_pos: torch.Tensor, topk_weights: torch.Tensor) -> torch.Tensor:
+    """y [T, H] bf16 = sum_j w[t, j] * expert_out[assign_pos[t*k + j]]."""
+    T, k = topk_weights.shape
+    H = expert_out.shape[1]
+    dt = {torch.float32: MOE_DTYPE_F32, torch.bfloat16: MOE_DTYPE_BF16}[expert_out.dtype]
+    y = torch.empty(T, H, dtype=torch.bfloat16, device=expert_out.device)
+    _check(lib().moe_combine(_ptr(expert_out), dt, _ptr(assign_pos), _ptr(topk_weights), T, k, H, _ptr(y),
+                             _stream()))
+    return y
+
+
+def moe_workspace_size(T: int, H: int, I: int, E: int, k: int, flags: int = 0) -> int:
+    return lib().moe_workspace_size(T, H, I, E, k, flags)
+
+
+class MoeFused:
+    """Holds the argument struct and workspace of one fused configuration so that repeated
+    calls (benchmark loops, graph capture) only re-issue the C call."""
+
+    def __init__(self, params: RouteParams, T: int, w: PackedWeights, hidden_states: torch.Tensor,
+                 router_logits: Optional[torch.Tensor] = None, prelude: Optional[Prelude] = None,
+                 expert_out_bf16: bool = False, y: Optional[torch.Tensor] = None,
+                 topk_ids: Optional[torch.Tensor] = None, topk_weights: Optional[torch.Tensor] = None,
+                 expert_counts: Optional[torch.Tensor] = None):
+        H = hidden_states.shape[1]
+        _need(hidden_states, "hidden_states", torch.bfloat16, (T, H))
+        if router_logits is not None:
+            _need(router_logits, "router_logits", torch.float32, (T, params.num_experts))
+        self.flags = MOE_FUSED_EXPERT_OUT_BF16 if expert_out_bf16 else 0
+        self.y = y if y is not None else torch.empty(T, H, dtype=torch.bfloat16, device=hidden_states.device)
+        nbytes = lib().moe_workspace_size(T, H, w.I, params.num_experts, params.top_k, self.flags)
+        self.ws = workspace(max(nbytes, 256), hidden_states.device)
+        self._keep = (hidden_states, router_logits, prelude, w, topk_ids, topk_weights, expert_counts)
+        self._pre = prelude.c() if prelude is not None else None
+        self.args = FusedArgs(T, H, w.I, params, _ptr(hidden_states), _ptr(router_logits),
+                              ctypes.pointer(self._pre) if self._pre is not None else None,
+                              _ptr(w.w13), _ptr(w.w13_scale), _ptr(w.w2), _ptr(w.w2_scale), _ptr(self.y),
+                              _ptr(topk_ids), _ptr(topk_weights), _ptr(expert_counts), self.flags, _ptr(self.ws),
+                              self.ws.numel(), None)
+
+    def __call__(self, stream: Optional[int] = None) -> torch.Tensor:
+        self.args.stream = _stream() if stream is None else stream
+        _check(lib().moe_fused(ctypes.byref(self.args)))
+        return self.y
+
+
+def moe_fused(params: RouteParams, hidden_states: torch.Tensor, w: PackedWeights,
+              router_logits: Optional[torch.Tensor] = None, prelude: Optional[Prelude] = None,
+              expert_out_bf16: bool = False, return_routing: bool = False):
+    """The whole step in one C call.  Returns y bf16 [T, H] (and ids, weights, counts)."""
+    T = hidden_states.shape[0]
+    dev = hidden_states.device
+    ids = weights = counts = None
+    if return_routing:
+        ids = torch.empty(T, params.top_k, dtype=torch.int32, device=dev)
+        weights = torch.empty(T, params.top_k, dtype=torch.float32, device=dev)
+        counts = torch.empty(params.num_experts, dtype=torch.int32, device=dev)
+    f = MoeFused(params, T, w, hidden_states, router_logits, prelude, expert_out_bf16, None, ids, weights, counts)
+    y = f()
+    return (y, ids, weights, counts) if return_routing else y

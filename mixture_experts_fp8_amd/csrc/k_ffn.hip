@@ -1,0 +1,483 @@
+// Grouped expert FFN and combine (gfx950).
+//
+// gate+up GEMM with the SwiGLU + E4M3 re-quantisation epilogue, then the down GEMM, as
+// the two W8A8 launches of run_fp8_grouped_w8a8 (metrale "fp8_grouped_tc_w8a8.rs"),
+// and the weighted combine of the MindIE-SD "Fused MoE" flow ("执行流程": combine).
+//
+// Both GEMMs run on the scaled FP8 matrix cores, v_mfma_scale_f32_16x16x128_f8f6f4: one
+// instruction covers exactly one 128-deep K block, so the UE8M0 scale of the activation
+// row and of the weight block enter as the instruction's own scale operands and the fp32
+// accumulator sums already-scaled block products.
+//
+// Work decomposition: the expert-sorted rows are cut into tiles of BM rows that never
+// straddle two experts (tile list built on the device from the expert counts).  A
+// workgroup takes one tile and one 128-wide slice of the output columns.  A rows are
+// staged in LDS (double buffered, gathered through sorted_assign for the gate+up GEMM)
+// in the exact byte order the matrix cores read; B (weights, pre-packed) streams straight
+// from memory into registers PF K-blocks ahead, 2 KB contiguous per operand.
+#include "moe_common.h"
+#include "moe_internal.h"
+
+#include <algorithm>
+
+namespace moe {
+
+// ----------------------------------------------------------------------------------------
+// Tile list: tiles of BM rows per expert, in expert order.
+__global__ __launch_bounds__(1024) void k_tiles(const int32_t* __restrict__ counts, int E, int BM,
+                                                int2* __restrict__ tiles, int32_t* __restrict__ ntiles) {
+    __shared__ int s_tmp[16];
+    const int e = threadIdx.x;
+    const int n = e < E ? (counts[e] + BM - 1) / BM : 0;
+    // inclusive scan over the workgroup
+    const int lane = e & 63, wv = e >> 6;
+    int v = n;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(v, o);
+        if (lane >= o) v += u;
+    }
+    if (lane == 63) s_tmp[wv] = v;
+    __syncthreads();
+    int add = 0;
+    for (int w = 0; w < wv; ++w) add += s_tmp[w];
+    const int start = v + add - n;
+    for (int i = 0; i < n; ++i) tiles[start + i] = make_int2(e, i * BM);
+    if (e == 1023) *ntiles = v + add;
+}
+
+struct G1Args {
+    const uint8_t* xq;
+    const uint8_t* xs;
+    int k, H, I;
+    const int32_t* counts;
+    const int32_t* offsets;
+    const int32_t* sorted_assign;
+    const int2* tiles;
+    const int32_t* ntiles;
+    const uint8_t* w13p;
+    const uint8_t* w13s;
+    uint8_t* hq;
+    uint8_t* hs;
+};
+
+__device__ __forceinline__ v8i lds_frag(const uint8_t* base, int lane) {
+    const uint4 lo = *reinterpret_cast<const uint4*>(base + lane * 16);
+    const uint4 hi = *reinterpret_cast<const uint4*>(base + 1024 + lane * 16);
+    v8i r;
+    r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
+    r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+    return r;
+}
+
+__device__ __forceinline__ v8i gmem_frag(const uint8_t* base, int lane) {
+    const uint4 lo = *reinterpret_cast<const uint4*>(base + lane * 16);
+    const uint4 hi = *reinterpret_cast<const uint4*>(base + 1024 + lane * 16);
+    v8i r;
+    r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
+    r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+    return r;
+}
+
+// gate+up GEMM + SwiGLU + requant.  Wave (wm, wn) computes MFW m-frags x NFW gate frags and
+// the NFW matching up frags; the workgroup covers BM rows x one 128-column block ib of h.
+template <int MFW, int NFW, int WM, int WN, int PF>
+__global__ __launch_bounds__(64 * WM * WN) void k_gemm1(G1Args a) {
+    constexpr int NT = 64 * WM * WN;
+    constexpr int MF = MFW * WM;
+    constexpr int BM = 16 * MF;
+    constexpr int ACH = (BM * 8 + NT - 1) / NT;
+    static_assert(NFW * WN == 8, "a workgroup covers 128 gate + 128 up columns");
+
+    const int tile = blockIdx.x;
+    if (tile >= *a.ntiles) return;
+    const int ib = blockIdx.y;
+    const int2 te = a.tiles[tile];
+    const int e = te.x, m0 = te.y;
+    const int nvalid = min(BM, a.counts[e] - m0);
+    const int rowbase = a.offsets[e] + m0;
+    const int KB = a.H / kGroup;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int wm = wv / WN, wn = wv % WN;
+
+    __shared__ __align__(16) uint8_t s_a[2][MF][kFragBytes];
+    __shared__ uint8_t s_sa[2][BM];
+    __shared__ float s_amax[WN][BM];
+
+    // A gather: chunk q = (row r = q/8, 16-byte column chunk c8 = q%8)
+    int64_t a_src[ACH];
+    int a_dst[ACH];
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) {
+        const int q = tid + i * NT;
+        a_dst[i] = -1;
+        a_src[i] = 0;
+        if (q < BM * 8) {
+            const int r = q >> 3, c8 = q & 7;
+            const int rr = min(r, nvalid - 1);
+            const int tok = a.sorted_assign[rowbase + rr] / a.k;
+            a_src[i] = (int64_t)tok * a.H + c8 * 16;
+            a_dst[i] = (r >> 4) * kFragBytes + (c8 & 1) * 1024 + ((c8 >> 1) * 16 + (r & 15)) * 16;
+        }
+    }
+    int64_t sa_src = -1;
+    if (tid < BM) sa_src = (int64_t)(a.sorted_assign[rowbase + min(tid, nvalid - 1)] / a.k) * KB;
+
+    const int NB16 = 2 * a.I / 16, NBS = 2 * a.I / kGroup;
+    const uint8_t* wb = a.w13p + (int64_t)e * NB16 * KB * kFragBytes;
+    const uint8_t* sb = a.w13s + (int64_t)e * KB * NBS;
+    const int g16 = ib * 8 + wn * NFW;          // first gate n16 of this wave
+    const int u16 = a.I / 16 + g16;             // first up n16
+
+    v8i bq[PF][2 * NFW];
+    v4f accg[MFW][NFW], accu[MFW][NFW];
+#pragma unroll
+    for (int mi = 0; mi < MFW; ++mi)
+#pragma unroll
+        for (int j = 0; j < NFW; ++j) {
+            accg[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
+            accu[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+
+    uint4 areg[ACH];
+    uint8_t sareg = 0;
+    // prologue: A block 0 -> LDS stage 0; B blocks 0..PF-1 -> registers
+#pragma unroll
+    for (int i = 0; i < ACH; ++i)
+        if (a_dst[i] >= 0) areg[i] = *reinterpret_cast<const uint4*>(a.xq + a_src[i]);
+    if (sa_src >= 0) sareg = a.xs[sa_src];
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+        if (p < KB) {
+#pragma unroll
+            for (int j = 0; j < NFW; ++j) {
+                bq[p][j] = gmem_frag(wb + ((int64_t)(g16 + j) * KB + p) * kFragBytes, lane);
+                bq[p][NFW + j] = gmem_frag(wb + ((int64_t)(u16 + j) * KB + p) * kFragBytes, lane);
+            }
+        }
+#pragma unroll
+    for (int i = 0; i < ACH; ++i)
+        if (a_dst[i] >= 0) *reinterpret_cast<uint4*>(&s_a[0][0][0] + a_dst[i]) = areg[i];
+    if (tid < BM) s_sa[0][tid] = sareg;
+    __syncthreads();
+
+    for (int kb0 = 0; kb0 < KB; kb0 += PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+            const int kb = kb0 + p;
+            if (kb < KB) {
+                const int cur = kb & 1;
+                if (kb + 1 < KB) {
+#pragma unroll
+                    for (int i = 0; i < ACH; ++i)
+                        if (a_dst[i] >= 0)
+                            areg[i] = *reinterpret_cast<const uint4*>(a.xq + a_src[i] + (int64_t)(kb + 1) * kGroup);
+                    if (sa_src >= 0) sareg = a.xs[sa_src + kb + 1];
+                }
+                const int sg = sb[kb * NBS + ib];
+                const int su = sb[kb * NBS + a.I / kGroup + ib];
+#pragma unroll
+                for (int mi = 0; mi < MFW; ++mi) {
+                    const int mf = wm * MFW + mi;
+                    const v8i af = lds_frag(&s_a[cur][mf][0], lane);
+                    const int sa = s_sa[cur][mf * 16 + (lane & 15)];
+#pragma unroll
+                    for (int j = 0; j < NFW; ++j) {
+                        accg[mi][j] = mfma_fp8(af, bq[p][j], accg[mi][j], sa, sg);
+                        accu[mi][j] = mfma_fp8(af, bq[p][NFW + j], accu[mi][j], sa, su);
+                    }
+                }
+                if (kb + PF < KB) {
+#pragma unroll
+                    for (int j = 0; j < NFW; ++j) {
+                        bq[p][j] = gmem_frag(wb + ((int64_t)(g16 + j) * KB + kb + PF) * kFragBytes, lane);
+                        bq[p][NFW + j] = gmem_frag(wb + ((int64_t)(u16 + j) * KB + kb + PF) * kFragBytes, lane);
+                    }
+                }
+                if (kb + 1 < KB) {
+#pragma unroll
+                    for (int i = 0; i < ACH; ++i)
+                        if (a_dst[i] >= 0) *reinterpret_cast<uint4*>(&s_a[cur ^ 1][0][0] + a_dst[i]) = areg[i];
+                    if (tid < BM) s_sa[cur ^ 1][tid] = sareg;
+                }
+                __syncthreads();
+            }
+        }
+    }
+
+    // ---- epilogue: h = silu(g) * u; per-row amax over the 128 columns; E4M3 requant
+    float hv[MFW][NFW][4];
+#pragma unroll
+    for (int mi = 0; mi < MFW; ++mi) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float m = 0.f;
+#pragma unroll
+            for (int j = 0; j < NFW; ++j) {
+                const float g = accg[mi][j][i];
+                const float h = g / (1.0f + expf(-g)) * accu[mi][j][i];
+                hv[mi][j][i] = h;
+                m = fmaxf(m, fabsf(h));
+            }
+            m = max16(m);
+            if ((lane & 15) == 0) s_amax[wn][(wm * MFW + mi) * 16 + 4 * (lane >> 4) + i] = m;
+        }
+    }
+    __syncthreads();
+    uint8_t* s_h = &s_a[0][0][0];   // [BM][128] bytes, reuses the A stages
+#pragma unroll
+    for (int mi = 0; mi < MFW; ++mi) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = (wm * MFW + mi) * 16 + 4 * (lane >> 4) + i;
+            float am = s_amax[0][row];
+#pragma unroll
+            for (int w = 1; w < WN; ++w) am = fmaxf(am, s_amax[w][row]);
+            const int ex = scale_exponent(am);
+#pragma unroll
+            for (int j = 0; j < NFW; ++j) {
+                const uint32_t q = cvt2_e4m3(ldexpf(hv[mi][j][i], -ex), 0.f) & 0xFFu;
+                s_h[row * 128 + (wn * NFW + j) * 16 + (lane & 15)] = (uint8_t)q;
+            }
+            if (wn == 0 && (lane & 15) == 0)
+                a.hs[((int64_t)tile * BM + row) * (a.I / kGroup) + ib] = (uint8_t)(ex + 127);
+        }
+    }
+    __syncthreads();
+    const int KB2 = a.I / kGroup;
+    for (int q = tid; q < MF * 128; q += NT) {
+        const int mf = q >> 7, w = q & 127, hh = w >> 6, ln = w & 63;
+        const uint4 v = *reinterpret_cast<const uint4*>(s_h + (mf * 16 + (ln & 15)) * 128 + (ln >> 4) * 32 + hh * 16);
+        *reinterpret_cast<uint4*>(a.hq + (((int64_t)tile * MF + mf) * KB2 + ib) * kFragBytes + hh * 1024 + ln * 16) = v;
+    }
+}
+
+struct G2Args {
+    const uint8_t* hq;
+    const uint8_t* hs;
+    int H, I;
+    const int32_t* counts;
+    const int32_t* offsets;
+    const int2* tiles;
+    const int32_t* ntiles;
+    const uint8_t* w2p;
+    const uint8_t* w2s;
+    void* out;
+    int out_bf16;
+};
+
+// down GEMM: wave (wm, wn) computes MFW m-frags x NFW column frags; the workgroup covers
+// BM rows x 16*NFW*WN output columns.
+template <int MFW, int NFW, int WM, int WN, int PF>
+__global__ __launch_bounds__(64 * WM * WN) void k_gemm2(G2Args a) {
+    constexpr int NT = 64 * WM * WN;
+    constexpr int MF = MFW * WM;
+    constexpr int BM = 16 * MF;
+    constexpr int ACH = (MF * 128 + NT - 1) / NT;
+
+    const int tile = blockIdx.x;
+    if (tile >= *a.ntiles) return;
+    const int2 te = a.tiles[tile];
+    const int e = te.x, m0 = te.y;
+    const int nvalid = min(BM, a.counts[e] - m0);
+    const int rowbase = a.offsets[e] + m0;
+    const int KB = a.I / kGroup;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int wm = wv / WN, wn = wv % WN;
+
+    __shared__ __align__(16) uint8_t s_a[2][MF][kFragBytes];
+    __shared__ uint8_t s_sa[2][BM];
+
+    const uint8_t* abase = a.hq + (int64_t)tile * MF * KB * kFragBytes;   // [mf][kb][2048]
+    const uint8_t* sabase = a.hs + (int64_t)tile * BM * KB;               // [row][kb]
+    const int NB16 = a.H / 16, NBS = a.H / kGroup;
+    const uint8_t* wb = a.w2p + (int64_t)e * NB16 * KB * kFragBytes;
+    const uint8_t* sb = a.w2s + (int64_t)e * KB * NBS;
+    const int n16 = blockIdx.y * (NFW * WN) + wn * NFW;
+
+    v8i bq[PF][NFW];
+    v4f acc[MFW][NFW];
+#pragma unroll
+    for (int mi = 0; mi < MFW; ++mi)
+#pragma unroll
+        for (int j = 0; j < NFW; ++j) acc[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // A copy: chunk q = (mf = q/128, 16-byte piece q%128) of the contiguous 2 KB operand
+    uint4 areg[ACH];
+    uint8_t sareg = 0;
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) {
+        const int q = tid + i * NT;
+        if (q < MF * 128)
+            areg[i] = *reinterpret_cast<const uint4*>(abase + ((int64_t)(q >> 7) * KB) * kFragBytes + (q & 127) * 16);
+    }
+    if (tid < BM) sareg = sabase[tid * KB];
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+        if (p < KB) {
+#pragma unroll
+            for (int j = 0; j < NFW; ++j) bq[p][j] = gmem_frag(wb + ((int64_t)(n16 + j) * KB + p) * kFragBytes, lane);
+        }
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) {
+        const int q = tid + i * NT;
+        if (q < MF * 128) *reinterpret_cast<uint4*>(&s_a[0][0][0] + q * 16) = areg[i];
+    }
+    if (tid < BM) s_sa[0][tid] = sareg;
+    __syncthreads();
+
+    for (int kb0 = 0; kb0 < KB; kb0 += PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+            const int kb = kb0 + p;
+            if (kb < KB) {
+                const int cur = kb & 1;
+                if (kb + 1 < KB) {
+#pragma unroll
+                    for (int i = 0; i < ACH; ++i) {
+                        const int q = tid + i * NT;
+                        if (q < MF * 128)
+                            areg[i] = *reinterpret_cast<const uint4*>(
+                                abase + ((int64_t)(q >> 7) * KB + kb + 1) * kFragBytes + (q & 127) * 16);
+                    }
+                    if (tid < BM) sareg = sabase[tid * KB + kb + 1];
+                }
+#pragma unroll
+                for (int mi = 0; mi < MFW; ++mi) {
+                    const int mf = wm * MFW + mi;
+                    const v8i af = lds_frag(&s_a[cur][mf][0], lane);
+                    const int sa = s_sa[cur][mf * 16 + (lane & 15)];
+#pragma unroll
+                    for (int j = 0; j < NFW; ++j) {
+                        const int sbv = sb[kb * NBS + ((n16 + j) * 16) / kGroup];
+                        acc[mi][j] = mfma_fp8(af, bq[p][j], acc[mi][j], sa, sbv);
+                    }
+                }
+                if (kb + PF < KB) {
+#pragma unroll
+                    for (int j = 0; j < NFW; ++j)
+                        bq[p][j] = gmem_frag(wb + ((int64_t)(n16 + j) * KB + kb + PF) * kFragBytes, lane);
+                }
+                if (kb + 1 < KB) {
+#pragma unroll
+                    for (int i = 0; i < ACH; ++i) {
+                        const int q = tid + i * NT;
+                        if (q < MF * 128) *reinterpret_cast<uint4*>(&s_a[cur ^ 1][0][0] + q * 16) = areg[i];
+                    }
+                    if (tid < BM) s_sa[cur ^ 1][tid] = sareg;
+                }
+                __syncthreads();
+            }
+        }
+    }
+
+    // ---- epilogue: rows in expert-sorted slot order
+#pragma unroll
+    for (int mi = 0; mi < MFW; ++mi) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = (wm * MFW + mi) * 16 + 4 * (lane >> 4) + i;
+            if (row < nvalid) {
+                const int64_t o = (int64_t)(rowbase + row) * a.H;
+#pragma unroll
+                for (int j = 0; j < NFW; ++j) {
+                    const int col = (n16 + j) * 16 + (lane & 15);
+                    if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o + col] = f32_to_bf16(acc[mi][j][i]);
+                    else reinterpret_cast<float*>(a.out)[o + col] = acc[mi][j][i];
+                }
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------------------
+FfnPlan ffn_plan(int T, int k, int E) {
+    const int64_t A = (int64_t)T * k;
+    const int64_t avg = A / E;
+    FfnPlan p;
+    p.BM = avg <= 24 ? 16 : (avg <= 96 ? 64 : 128);
+    p.ntiles_max = (int)(ceil_div(A, p.BM) + std::min<int64_t>(E, A));
+    return p;
+}
+
+// workspace: tiles [ntiles_max] int2 | ntiles int | hq [ntiles_max*BM, I] | hs [ntiles_max*BM, I/128]
+size_t ffn_workspace_bytes(int T, int H, int I, int E, int k) {
+    (void)H;
+    const FfnPlan p = ffn_plan(T, k, E);
+    const size_t rows = (size_t)p.ntiles_max * p.BM;
+    return align256((size_t)p.ntiles_max * 8) + align256(4) + align256(rows * I) + align256(rows * (I / kGroup));
+}
+
+template <int MFW, int NFW1, int NFW2, int WM, int WN, int PF1, int PF2>
+static hipError_t run_ffn(const FfnArgs& f, const FfnPlan& p, int2* tiles, int32_t* ntiles, uint8_t* hq,
+                          uint8_t* hs, hipStream_t st) {
+    G1Args g1{f.xq, f.xs, f.k, f.H, f.I, f.counts, f.offsets, f.sorted_assign, tiles, ntiles, f.w13p, f.w13s, hq, hs};
+    hipLaunchKernelGGL((k_gemm1<MFW, NFW1, WM, WN, PF1>), dim3(p.ntiles_max, f.I / kGroup), dim3(64 * WM * WN), 0,
+                       st, g1);
+    G2Args g2{hq, hs, f.H, f.I, f.counts, f.offsets, tiles, ntiles, f.w2p, f.w2s, f.out, f.out_bf16};
+    const int ncols = 16 * NFW2 * WN;
+    hipLaunchKernelGGL((k_gemm2<MFW, NFW2, WM, WN, PF2>), dim3(p.ntiles_max, f.H / ncols), dim3(64 * WM * WN), 0,
+                       st, g2);
+    return hipGetLastError();
+}
+
+hipError_t launch_grouped_ffn(const FfnArgs& f, void* ws, hipStream_t st) {
+    const FfnPlan p = ffn_plan(f.T, f.k, f.E);
+    const size_t rows = (size_t)p.ntiles_max * p.BM;
+    uint8_t* w = static_cast<uint8_t*>(ws);
+    int2* tiles = reinterpret_cast<int2*>(w);
+    w += align256((size_t)p.ntiles_max * 8);
+    int32_t* ntiles = reinterpret_cast<int32_t*>(w);
+    w += align256(4);
+    uint8_t* hq = w;
+    w += align256(rows * f.I);
+    uint8_t* hs = w;
+    hipLaunchKernelGGL(k_tiles, dim3(1), dim3(1024), 0, st, f.counts, f.E, p.BM, tiles, ntiles);
+    // output columns per workgroup of the down GEMM = 16 * NFW2 * WN = 128, a divisor of H
+    if (p.BM == 16) return run_ffn<1, 2, 2, 1, 4, 4, 4>(f, p, tiles, ntiles, hq, hs, st);
+    if (p.BM == 64) return run_ffn<2, 4, 4, 2, 2, 2, 2>(f, p, tiles, ntiles, hq, hs, st);
+    return run_ffn<4, 4, 4, 2, 2, 2, 2>(f, p, tiles, ntiles, hq, hs, st);
+}
+
+// ----------------------------------------------------------------------------------------
+// Combine: one workgroup per token; each thread owns 4 consecutive columns.
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_combine(const void* __restrict__ eo, const int32_t* __restrict__ pos,
+                                                 const float* __restrict__ w, int k, int H,
+                                                 uint16_t* __restrict__ y) {
+    const int t = blockIdx.x;
+    for (int c4 = threadIdx.x; c4 < H / 4; c4 += 256) {
+        float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+        for (int j = 0; j < k; ++j) {
+            const int p = pos[(int64_t)t * k + j];
+            if (p < 0) continue;   // dropped assignment
+            const float wj = w[(int64_t)t * k + j];
+            float v0, v1, v2, v3;
+            if (BF16) {
+                const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(eo) + (int64_t)p * H + c4 * 4);
+                v0 = bf16_to_f32(u.x & 0xFFFFu); v1 = bf16_to_f32(u.x >> 16);
+                v2 = bf16_to_f32(u.y & 0xFFFFu); v3 = bf16_to_f32(u.y >> 16);
+            } else {
+                const float4 u = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(eo) + (int64_t)p * H + c4 * 4);
+                v0 = u.x; v1 = u.y; v2 = u.z; v3 = u.w;
+            }
+            acc0 = fmaf(wj, v0, acc0);
+            acc1 = fmaf(wj, v1, acc1);
+            acc2 = fmaf(wj, v2, acc2);
+            acc3 = fmaf(wj, v3, acc3);
+        }
+        uint2 o;
+        o.x = (uint32_t)f32_to_bf16(acc0) | ((uint32_t)f32_to_bf16(acc1) << 16);
+        o.y = (uint32_t)f32_to_bf16(acc2) | ((uint32_t)f32_to_bf16(acc3) << 16);
+        *reinterpret_cast<uint2*>(y + (int64_t)t * H + c4 * 4) = o;
+    }
+}
+
+hipError_t launch_combine(const void* eo, int bf16, const int32_t* pos, const float* w, int T, int k, int H,
+                          uint16_t* y, hipStream_t st) {
+    if (bf16) hipLaunchKernelGGL(k_combine<true>, dim3(T), dim3(256), 0, st, eo, pos, w, k, H, y);
+    else hipLaunchKernelGGL(k_combine<false>, dim3(T), dim3(256), 0, st, eo, pos, w, k, H, y);
+    return hipGetLastError();
+}
+
+}  // namespace moe

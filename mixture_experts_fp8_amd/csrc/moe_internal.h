@@ -1,0 +1,64 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- quantisation / layout
+hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, int64_t ld, uint8_t* xq, uint8_t* xs,
+                            hipStream_t st);
+hipError_t launch_quant_weight_blocks(const float* w, int E, int K, int N, uint8_t* q, uint8_t* s,
+                                      hipStream_t st);
+hipError_t launch_prepack(const uint8_t* w, int E, int K, int N, uint8_t* out, hipStream_t st);
+
+// ---- routing and dispatch
+struct RouteCfg {
+    int T, E, k;
+    int scoring;            // 0 softmax, 1 sigmoid
+    int renormalize;
+    int G, k_group, mode;
+    float rsf;
+    int prelude;            // weights = softmax over selected * per_expert_scale
+};
+constexpr int kScatterChunk = 1024;   // assignments per dispatch workgroup
+
+hipError_t launch_gate_prelude(const uint16_t* x, int T, int H, int E, const float* norm_w,
+                               const float* router_w, float eps, float* logits, hipStream_t st);
+hipError_t launch_route(const float* logits, const RouteCfg& c, const float* pe_scale, int32_t* ids,
+                        float* weights, hipStream_t st);
+// hist + scan + scatter; chunk_ws holds nchunks*E int32
+hipError_t launch_dispatch(const int32_t* ids, int A, int E, int32_t* chunk_ws, int32_t* counts,
+                           int32_t* offsets, int32_t* sorted_assign, int32_t* assign_pos, hipStream_t st);
+
+// ---- grouped FFN
+struct FfnPlan {
+    int BM;           // rows per tile
+    int ntiles_max;   // grid bound on tiles
+};
+FfnPlan ffn_plan(int T, int k, int E);
+size_t ffn_workspace_bytes(int T, int H, int I, int E, int k);
+
+struct FfnArgs {
+    int T, k, H, I, E;
+    const uint8_t* xq;
+    const uint8_t* xs;
+    const int32_t* counts;
+    const int32_t* offsets;
+    const int32_t* sorted_assign;
+    const uint8_t* w13p;
+    const uint8_t* w13s;
+    const uint8_t* w2p;
+    const uint8_t* w2s;
+    void* out;
+    int out_bf16;
+};
+hipError_t launch_grouped_ffn(const FfnArgs& a, void* ws, hipStream_t st);
+
+hipError_t launch_combine(const void* eo, int bf16, const int32_t* pos, const float* w, int T, int k, int H,
+                          uint16_t* y, hipStream_t st);
+
+inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+}  // namespace moe

@@ -1,0 +1,100 @@
+"""Shared plumbing of the parity tests: build a workload's inputs on both sides, run the
+oracle for some tokens, run the HIP path, compare.
+
+The two sides meet only through gen (seeded inputs): the oracle quantises its own copy
+of the float32 weights; the GPU path quantises with moe_quant_weight_blocks.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from gen import workloads as W
+from oracle import codec, moe as omoe, routing as orouting
+
+import mixture_experts_fp8_amd as M
+
+
+def oracle_params(wl: W.Workload) -> orouting.RouteParams:
+    return orouting.RouteParams(wl.E, wl.k, wl.scoring, wl.renormalize, wl.group_count, wl.k_group,
+                                wl.group_select_mode, wl.routed_scaling_factor)
+
+
+def device_params(wl: W.Workload):
+    return M.route_params(wl.E, wl.k, wl.scoring, wl.renormalize, wl.group_count, wl.k_group,
+                          wl.group_select_mode, wl.routed_scaling_factor)
+
+
+def oracle_experts(wl: W.Workload, cache: int = 8) -> omoe.QuantizedExperts:
+    def src(e):
+        return (W.expert_weight_f32(wl, "w13", e).numpy(), W.expert_weight_f32(wl, "w2", e).numpy())
+    return omoe.QuantizedExperts(src, cache=cache)
+
+
+def oracle_experts_for(wl: W.Workload, experts, workers: int = 8) -> omoe.QuantizedExperts:
+    """Oracle experts with the listed ones quantised up front, in a thread pool."""
+    import concurrent.futures as cf
+    ex = oracle_experts(wl, cache=max(8, len(experts)))
+    with cf.ThreadPoolExecutor(max_workers=workers) as pool:
+        qs = dict(zip(experts, pool.map(ex.quantize, experts)))
+    ex.preload(qs)
+    return ex
+
+
+def device_weights(wl: W.Workload, device="cuda") -> M.PackedWeights:
+    """Generate each expert's float32 weights on the GPU, quantise and pack them there."""
+    H, I, E = wl.H, wl.I, wl.E
+    w13p = torch.empty(E * H * 2 * I, dtype=torch.uint8, device=device)
+    w2p = torch.empty(E * I * H, dtype=torch.uint8, device=device)
+    w13s = torch.empty(E, H // 128, 2 * I // 128, dtype=torch.uint8, device=device)
+    w2s = torch.empty(E, I // 128, H // 128, dtype=torch.uint8, device=device)
+    for e in range(E):
+        q, s = M.moe_quant_weight_blocks(W.expert_weight_f32(wl, "w13", e, device)[None])
+        w13s[e] = s[0]
+        w13p[e * H * 2 * I:(e + 1) * H * 2 * I] = M.moe_prepack_weights(q)
+        q, s = M.moe_quant_weight_blocks(W.expert_weight_f32(wl, "w2", e, device)[None])
+        w2s[e] = s[0]
+        w2p[e * I * H:(e + 1) * I * H] = M.moe_prepack_weights(q)
+    return M.PackedWeights(E, H, I, w13p, w13s, w2p, w2s)
+
+
+def oracle_route(wl: W.Workload, x_f64=None, logits=None):
+    """(ids, weights, margin) of the oracle for all tokens."""
+    p = oracle_params(wl)
+    if wl.prelude:
+        nw, rw, pe = W.gate_prelude_params(wl)
+        return omoe.route_workload({"x": x_f64}, p, (nw.numpy(), rw.numpy(), pe.numpy(), wl.rms_eps))
+    return omoe.route_workload({"logits": logits.numpy() if torch.is_tensor(logits) else logits}, p)
+
+
+def device_inputs(wl: W.Workload, device="cuda"):
+    """x bf16, logits or prelude tensors on the GPU (same bits as the CPU copies)."""
+    x = W.hidden_bf16(wl, device)
+    if wl.prelude:
+        nw, rw, pe = W.gate_prelude_params(wl, device)
+        return x, None, M.Prelude(nw, rw, pe, wl.rms_eps)
+    return x, W.router_logits(wl, device), None
+
+
+def rel_errors(y_dev: np.ndarray, y_ref: np.ndarray):
+    d = y_dev.astype(np.float64) - y_ref
+    fro = np.linalg.norm(d) / max(np.linalg.norm(y_ref), 1e-300)
+    mx = np.abs(d).max() / max(np.abs(y_ref).max(), 1e-300)
+    return fro, mx
+
+
+def assert_output_close(y_dev: np.ndarray, y_ref: np.ndarray, what: str = ""):
+    """The output bar: relative Frobenius error <= 5e-3 and max |err| <= 2e-2 * max |y|,
+    against the oracle's unrounded float64 y."""
+    fro, mx = rel_errors(y_dev, y_ref)
+    assert fro <= 5e-3 and mx <= 2e-2, f"{what}: rel fro {fro:.3e}, rel max {mx:.3e}"
+    return fro, mx
+
+
+def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact values of a bf16 tensor (bf16 -> fp32 is exact)."""
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def quant_reference(x_bf16_cpu: torch.Tensor):
+    return codec.quant_rows_128(W.bf16_to_f64(x_bf16_cpu))

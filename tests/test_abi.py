@@ -1,0 +1,156 @@
+"""The C ABI without a GPU: the library loads, exports every function include/moe_fp8.h
+declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_fp8_amd as M
+from mixture_experts_fp8_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_fp8.h")
+
+FAKE = 0x10000000   # a non-NULL, 256-aligned pointer value; never dereferenced on error paths
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(moe_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    fns = declared_functions()
+    for f in ["moe_route", "moe_quant_act", "moe_grouped_ffn", "moe_combine", "moe_fused",
+              "moe_workspace_size", "moe_last_error", "moe_prepack_weights", "moe_quant_weight_blocks"]:
+        assert f in fns
+
+
+def test_library_exports_every_declared_symbol():
+    lib = M.lib()
+    for f in declared_functions():
+        assert hasattr(lib, f), f
+    assert sorted(declared_functions()) == sorted(B.EXPORTED)
+
+
+def _route(p, T=4, logits=FAKE, flags=0, ws=FAKE, ws_bytes=1 << 20, prelude=None, hidden=None, H=0, outs=FAKE):
+    return M.lib().moe_route(ctypes.byref(p), T, logits, hidden, H, prelude, flags, outs, outs, outs, outs, outs,
+                             outs, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(num_experts=8, top_k=9), B.MOE_ERR_INVALID, "top_k"),
+    (dict(num_experts=8, top_k=0), B.MOE_ERR_INVALID, "top_k"),
+    (dict(num_experts=0, top_k=1), B.MOE_ERR_INVALID, "num_experts"),
+    (dict(num_experts=2048, top_k=1), B.MOE_ERR_UNSUPPORTED, "exceeds max"),
+    (dict(num_experts=12, top_k=2, group_count=5), B.MOE_ERR_INVALID, "divisible"),
+    (dict(num_experts=16, top_k=2, group_count=4, k_group=5), B.MOE_ERR_INVALID, "k_group"),
+    (dict(num_experts=16, top_k=5, group_count=4, k_group=1), B.MOE_ERR_INVALID, "kept groups"),
+    (dict(num_experts=8, top_k=2, group_count=8, k_group=2, group_select_mode=1), B.MOE_ERR_INVALID, "at least 2"),
+    (dict(num_experts=8, top_k=2, group_count=2, k_group=1, group_select_mode=3), B.MOE_ERR_INVALID, "group_select_mode"),
+    (dict(num_experts=8, top_k=2, routed_scaling_factor=float("inf")), B.MOE_ERR_INVALID, "finite"),
+])
+def test_route_param_validation(kw, code, needle):
+    p = M.route_params(**kw)
+    assert _route(p) == code
+    assert needle in M.moe_last_error()
+
+
+def test_route_other_errors():
+    p = M.route_params(8, 2)
+    assert _route(p, T=0) == B.MOE_ERR_INVALID
+    assert _route(p, logits=None) == B.MOE_ERR_INVALID and "router_logits" in M.moe_last_error()
+    assert _route(p, outs=None) == B.MOE_ERR_INVALID
+    assert _route(p, ws_bytes=16) == B.MOE_ERR_WORKSPACE and "workspace too small" in M.moe_last_error()
+    assert _route(p, ws=FAKE + 4) == B.MOE_ERR_INVALID and "aligned" in M.moe_last_error()
+    assert _route(p, flags=8) == B.MOE_ERR_INVALID
+    pre = B.GatePrelude(None, None, None, 1e-6)
+    assert _route(p, logits=None, prelude=ctypes.byref(pre), hidden=FAKE, H=64) == B.MOE_ERR_INVALID
+    pre = B.GatePrelude(FAKE, FAKE, None, -1.0)
+    assert _route(p, logits=None, prelude=ctypes.byref(pre), hidden=FAKE, H=64) == B.MOE_ERR_INVALID
+    pre = B.GatePrelude(FAKE, FAKE, None, 1e-6)
+    assert _route(p, logits=None, prelude=ctypes.byref(pre), hidden=FAKE, H=1 << 20) == B.MOE_ERR_UNSUPPORTED
+
+
+def test_quant_act_validation():
+    L = M.lib()
+    assert L.moe_quant_act(None, 4, 128, 128, FAKE, FAKE, None) == B.MOE_ERR_INVALID
+    assert L.moe_quant_act(FAKE, 4, 100, 128, FAKE, FAKE, None) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_quant_act(FAKE, 4, 256, 128, FAKE, FAKE, None) == B.MOE_ERR_INVALID     # ld < cols
+    assert L.moe_quant_act(FAKE + 2, 4, 128, 128, FAKE, FAKE, None) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_quant_act(FAKE, 0, 128, 128, FAKE, FAKE, None) == B.MOE_ERR_INVALID
+
+
+def test_weight_helpers_validation():
+    L = M.lib()
+    assert L.moe_quant_weight_blocks(FAKE, 2, 100, 128, FAKE, FAKE, None) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_quant_weight_blocks(None, 2, 128, 128, FAKE, FAKE, None) == B.MOE_ERR_INVALID
+    assert L.moe_prepack_weights(FAKE, 1, 128, 24, FAKE + (1 << 20), None) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_prepack_weights(FAKE, 1, 128, 32, FAKE + 16, None) == B.MOE_ERR_INVALID   # overlap
+    assert "overlap" in M.moe_last_error()
+
+
+def _ffn(**over):
+    a = dict(T=8, k=2, H=256, I=256, E=4, xq=FAKE, xs=FAKE, expert_counts=FAKE, expert_offsets=FAKE,
+             sorted_assign=FAKE, w13=FAKE, w13_scale=FAKE, w2=FAKE, w2_scale=FAKE, expert_out=FAKE,
+             out_dtype=0, workspace=FAKE, workspace_bytes=1 << 30, stream=None)
+    a.update(over)
+    s = B.FfnArgs(**a)
+    return M.lib().moe_grouped_ffn(ctypes.byref(s))
+
+
+def test_grouped_ffn_validation():
+    assert _ffn(H=200) == B.MOE_ERR_UNSUPPORTED and "multiple of 128" in M.moe_last_error()
+    assert _ffn(I=1000) == B.MOE_ERR_UNSUPPORTED
+    assert _ffn(k=5) == B.MOE_ERR_INVALID
+    assert _ffn(w2=None) == B.MOE_ERR_INVALID
+    assert _ffn(w13=FAKE + 8) == B.MOE_ERR_INVALID
+    assert _ffn(out_dtype=7) == B.MOE_ERR_INVALID
+    assert _ffn(workspace_bytes=10) == B.MOE_ERR_WORKSPACE
+    assert M.lib().moe_grouped_ffn(None) == B.MOE_ERR_INVALID
+
+
+def test_combine_validation():
+    L = M.lib()
+    assert L.moe_combine(FAKE, 0, FAKE, FAKE, 4, 2, 130, FAKE, None) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_combine(FAKE, 3, FAKE, FAKE, 4, 2, 128, FAKE, None) == B.MOE_ERR_INVALID
+    assert L.moe_combine(None, 0, FAKE, FAKE, 4, 2, 128, FAKE, None) == B.MOE_ERR_INVALID
+
+
+def _fused(**over):
+    p = over.pop("route", M.route_params(8, 2))
+    a = dict(T=4, H=256, I=256, route=p, hidden_states=FAKE, router_logits=FAKE, prelude=None, w13=FAKE,
+             w13_scale=FAKE, w2=FAKE, w2_scale=FAKE, y=FAKE, topk_ids=None, topk_weights=None,
+             expert_counts=None, flags=0, workspace=FAKE, workspace_bytes=1 << 30, stream=None)
+    a.update(over)
+    return M.lib().moe_fused(ctypes.byref(B.FusedArgs(**a)))
+
+
+def test_fused_validation():
+    assert _fused(route=M.route_params(8, 9)) == B.MOE_ERR_INVALID
+    assert _fused(H=100) == B.MOE_ERR_UNSUPPORTED
+    assert _fused(router_logits=None) == B.MOE_ERR_INVALID
+    assert _fused(y=None) == B.MOE_ERR_INVALID
+    assert _fused(flags=4) == B.MOE_ERR_INVALID
+    assert _fused(workspace_bytes=1000) == B.MOE_ERR_WORKSPACE
+    assert _fused(hidden_states=FAKE + 4) == B.MOE_ERR_UNSUPPORTED
+    assert M.lib().moe_fused(None) == B.MOE_ERR_INVALID
+
+
+def test_workspace_sizes_are_monotone_and_cover_parts():
+    L = M.lib()
+    for (T, H, I, E, k) in [(64, 256, 512, 8, 2), (32, 2816, 768, 128, 8), (4096, 7168, 2048, 256, 8)]:
+        full = L.moe_workspace_size(T, H, I, E, k, 0)
+        assert full >= L.moe_ffn_workspace_size(T, H, I, E, k) + L.moe_route_workspace_size(T, E, k, H, 1)
+        assert L.moe_workspace_size(T, H, I, E, k, B.MOE_FUSED_EXPERT_OUT_BF16) < full
+        assert L.moe_workspace_size(2 * T, H, I, E, k, 0) > full
+    assert L.moe_workspace_size(0, 256, 256, 8, 2, 0) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", "/nonexistent/libmoe_fp8.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        B.lib()
