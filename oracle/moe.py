@@ -50,14 +50,24 @@ class QuantizedExperts:
         self.cache = cache
         self._mem: dict = {}
 
+    def preload(self, quantized: dict) -> None:
+        """Keep already-quantised experts {e: (q13, s13, q2, s2)} (made by this module's
+        codec, e.g. in parallel by a caller) for the next forward."""
+        self.cache = max(self.cache, len(quantized))
+        self._mem.update(quantized)
+
+    def quantize(self, e: int):
+        w13, w2 = self.source(e)
+        q13, s13 = codec.quant_blocks_128(np.asarray(w13, dtype=np.float64))
+        q2, s2 = codec.quant_blocks_128(np.asarray(w2, dtype=np.float64))
+        return q13, s13, q2, s2
+
     def get(self, e: int):
         if e not in self._mem:
-            w13, w2 = self.source(e)
-            q13, s13 = codec.quant_blocks_128(np.asarray(w13, dtype=np.float64))
-            q2, s2 = codec.quant_blocks_128(np.asarray(w2, dtype=np.float64))
+            q = self.quantize(e)
             if len(self._mem) >= self.cache:
                 self._mem.pop(next(iter(self._mem)))
-            self._mem[e] = (q13, s13, q2, s2)
+            self._mem[e] = q
         return self._mem[e]
 
 
