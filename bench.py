@@ -1,0 +1,315 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed FP8 MoE expert step on one MI355X.
+
+    python bench.py [--config 2] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+A step is one moe_fused call: gate prelude / routing, dispatch, activation quantisation,
+gate+up FP8 GEMM with SwiGLU + requantisation, down FP8 GEMM and the weighted combine,
+over one batch of seeded synthetic tokens whose inputs already sit in HBM.  Steps rotate
+through LAYERS copies of the expert weights, as consecutive MoE layers of a model would,
+so the 256 MB Infinity Cache cannot hand a step the weights the previous step read.
+
+Prints one JSON line: throughput (tokens/s) over exactly K timed steps, FP8 TFLOP/s, a
+roofline entry for the dominant kernel (algorithmic bytes or flops per launch divided by
+its average duration, measured with HIP events recorded on the launch stream), and the
+CPU oracle's throughput on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/s + FP8 TFLOP/s; % of FP8-MFMA or HBM roofline, 1 MI355X"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense FP8 matrix, TFLOP/s
+LAYERS = 4
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["mixture_experts_fp8_amd/csrc/k_ffn.hip", "mixture_experts_fp8_amd/csrc/moe_common.h"]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="workload id 1..5 (default 2: Gemma-4-like decode)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0, help="0: the workload's own default sample")
+    ap.add_argument("--expert-out-bf16", action="store_true", help="keep per-assignment expert outputs in bf16")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one plain 1 GiB device copy first (a known-size kernel for HBM counter calibration)")
+    return ap.parse_args()
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (created eagerly) for the library's stage boundaries."""
+
+    def __init__(self, n: int):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.ev = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(h))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed: {rc}")
+            self.ev[i] = h.value
+
+    def elapsed_s(self, i: int, j: int) -> float:
+        ms = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(ms), self.ct.c_void_p(self.ev[i]), self.ct.c_void_p(self.ev[j]))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return ms.value * 1e-3
+
+    def destroy(self):
+        for h in self.ev:
+            self.hip.hipEventDestroy(self.ct.c_void_p(h))
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stage_bytes_flops(wl, counts: np.ndarray, eo_bytes: int):
+    """Algorithmic HBM bytes and FP8 flops per launch of the two GEMM stages.
+
+    gate+up: every active expert's w13 once (H*2I bytes + (H/128)*(2I/128) scale bytes),
+    each token's quantised row once (H + H/128), each assignment's hq row written once
+    (I + I/128).  down: every active expert's w2 once (I*H + (I/128)*(H/128)), each hq
+    row read once (I + I/128), each assignment's output row written once (H * eo_bytes).
+    """
+    H, I, T, A = wl.H, wl.I, wl.T, wl.T * wl.k
+    n_act = int((counts > 0).sum())
+    s13 = (H // 128) * (2 * I // 128)
+    s2 = (I // 128) * (H // 128)
+    g1_bytes = n_act * (H * 2 * I + s13) + T * (H + H // 128) + A * (I + I // 128)
+    g2_bytes = n_act * (I * H + s2) + A * (I + I // 128) + A * H * eo_bytes
+    g1_flops = 4.0 * A * H * I
+    g2_flops = 2.0 * A * H * I
+    return {"gate_up_gemm": (g1_bytes, g1_flops), "down_gemm": (g2_bytes, g2_flops)}, n_act
+
+
+def step_algorithmic_bytes(wl, n_act: int) -> int:
+    """Minimum traffic of a whole step: active experts' weights and scales, x, logits
+    (or the prelude tensors), y, ids and weights."""
+    H, I, T, E, k = wl.H, wl.I, wl.T, wl.E, wl.k
+    b = n_act * (3 * H * I + (H // 128) * (2 * I // 128) + (I // 128) * (H // 128))
+    b += 2 * T * H + 2 * T * H + 8 * T * k
+    b += 4 * E * H + 4 * H + 4 * E if wl.prelude else 4 * T * E
+    return b
+
+
+def roofline_entry(name, dur_s, nbytes, flops, traffic):
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    t_mfma = flops / (PEAK_FP8_TFLOPS * 1e12)
+    if t_hbm >= t_mfma:
+        ach = nbytes / dur_s / 1e9
+        return {"kernel": name, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic, "algorithmic_bytes": int(nbytes),
+                "avg_us": round(dur_s * 1e6, 2)}
+    ach = flops / dur_s / 1e12
+    return {"kernel": name, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": traffic, "algorithmic_flops": flops,
+            "avg_us": round(dur_s * 1e6, 2)}
+
+
+def load_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it was taken
+    on the current kernel source; otherwise None."""
+    p = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, sample_tokens: int):
+    """The oracle as it stands, timed on the host on a bounded sample of the workload's
+    tokens (weights quantised by the oracle beforehand, untimed)."""
+    import concurrent.futures as cf
+
+    from threadpoolctl import threadpool_limits
+
+    from gen import workloads as W
+    from oracle import moe as omoe
+    from oracle import routing as orouting
+
+    x = W.hidden_bf16(wl)
+    xf = W.bf16_to_f64(x)
+    p = orouting.RouteParams(wl.E, wl.k, wl.scoring, wl.renormalize, wl.group_count, wl.k_group,
+                             wl.group_select_mode, wl.routed_scaling_factor)
+    if wl.prelude:
+        nw, rw, pe = W.gate_prelude_params(wl)
+        pre = (nw.numpy(), rw.numpy(), pe.numpy(), wl.rms_eps)
+        inputs = {"x": xf}
+    else:
+        pre = None
+        inputs = {"logits": W.router_logits(wl).numpy()}
+    n = min(sample_tokens, wl.T)
+    tokens = np.linspace(0, wl.T - 1, n).astype(np.int64)
+    ids, _, _ = omoe.route_workload(inputs, p, pre)
+    experts = sorted(set(int(e) for e in ids[tokens].reshape(-1)))
+
+    def src(e):
+        return (W.expert_weight_f32(wl, "w13", e).numpy(), W.expert_weight_f32(wl, "w2", e).numpy())
+
+    ex = omoe.QuantizedExperts(src, cache=len(experts))
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    with cf.ThreadPoolExecutor(max_workers=workers) as pool:   # input preparation, untimed
+        ex.preload(dict(zip(experts, pool.map(ex.quantize, experts))))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        ids, w, _ = omoe.route_workload(inputs, p, pre)        # routing of the whole batch
+        out = omoe.forward(xf, ids, w, ex, tokens=tokens)
+        dt = time.perf_counter() - t0
+    assert out["y"].shape == (n, wl.H)
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} of {wl.T} tokens (evenly spaced), all of their {len(experts)} experts; routing "
+                      f"of the full batch included; {dt:.1f} s on one host thread"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(the expert-parallel exchange across GPUs is not part of it)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mixture_experts_fp8_amd as M
+    from gen import workloads as W
+    from mixture_experts_fp8_amd import binding as B
+
+    wl = W.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] workload {wl.name}: {W.describe(wl)}", file=sys.stderr, flush=True)
+
+    # ---- inputs, resident in HBM before timing
+    x = W.hidden_bf16(wl, dev)
+    logits, pre = None, None
+    if wl.prelude:
+        nw, rw, pe = W.gate_prelude_params(wl, dev)
+        pre = M.Prelude(nw, rw, pe, wl.rms_eps)
+    else:
+        logits = W.router_logits(wl, dev)
+    H, I, E = wl.H, wl.I, wl.E
+    w13p = torch.empty(E * H * 2 * I, dtype=torch.uint8, device=dev)
+    w2p = torch.empty(E * I * H, dtype=torch.uint8, device=dev)
+    w13s = torch.empty(E, H // 128, 2 * I // 128, dtype=torch.uint8, device=dev)
+    w2s = torch.empty(E, I // 128, H // 128, dtype=torch.uint8, device=dev)
+    for e in range(E):
+        q, s = M.moe_quant_weight_blocks(W.expert_weight_f32(wl, "w13", e, dev)[None])
+        w13s[e] = s[0]
+        w13p[e * H * 2 * I:(e + 1) * H * 2 * I] = M.moe_prepack_weights(q)
+        q, s = M.moe_quant_weight_blocks(W.expert_weight_f32(wl, "w2", e, dev)[None])
+        w2s[e] = s[0]
+        w2p[e * I * H:(e + 1) * I * H] = M.moe_prepack_weights(q)
+    layers = [M.PackedWeights(E, H, I, w13p, w13s, w2p, w2s)]
+    for _ in range(LAYERS - 1):
+        layers.append(M.PackedWeights(E, H, I, w13p.clone(), w13s.clone(), w2p.clone(), w2s.clone()))
+    params = M.route_params(wl.E, wl.k, wl.scoring, wl.renormalize, wl.group_count, wl.k_group,
+                            wl.group_select_mode, wl.routed_scaling_factor)
+    counts = torch.zeros(E, dtype=torch.int32, device=dev)
+    y = torch.empty(wl.T, H, dtype=torch.bfloat16, device=dev)
+    calls = [M.MoeFused(params, wl.T, lw, x, logits, pre, args.expert_out_bf16, y=y, expert_counts=counts)
+             for lw in layers]
+    torch.cuda.synchronize()
+
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # ---- warmup, then exactly K timed steps
+    for i in range(args.warmup):
+        calls[i % LAYERS]()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        calls[i % LAYERS]()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed / args.steps * 1e3
+    tokens_per_s = wl.T * args.steps / elapsed
+
+    # ---- per-stage durations from HIP events recorded on the launch stream
+    nst = B.MOE_STAGES
+    evs = [HipEvents(nst + 1) for _ in range(args.steps)]
+    for i in range(args.steps):
+        calls[i % LAYERS](stage_events=evs[i].ev)
+    torch.cuda.synchronize()
+    stage_s = np.zeros(nst)
+    for i in range(args.steps):
+        for s in range(nst):
+            stage_s[s] += evs[i].elapsed_s(s, s + 1)
+        evs[i].destroy()
+    stage_s /= args.steps
+    stages = {B.STAGE_NAMES[s]: round(stage_s[s] * 1e6, 2) for s in range(nst)}
+
+    cnt = counts.cpu().numpy()
+    eo_bytes = 2 if args.expert_out_bf16 else 4
+    per_stage, n_act = stage_bytes_flops(wl, cnt, eo_bytes)
+    dom = max(per_stage, key=lambda n: stage_s[B.STAGE_NAMES.index(n)])
+    nbytes, flops = per_stage[dom]
+    roof = roofline_entry(dom, stage_s[B.STAGE_NAMES.index(dom)], nbytes, flops, load_traffic(wl.name, dom))
+    other = [n for n in per_stage if n != dom][0]
+    roof_other = roofline_entry(other, stage_s[B.STAGE_NAMES.index(other)], *per_stage[other], load_traffic(wl.name, other))
+
+    step_bytes = step_algorithmic_bytes(wl, n_act)
+    total_flops = wl.flops()
+    step_s = elapsed / args.steps
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {W.describe(wl)}", "tokens_per_step": wl.T,
+                   "weight_copies_rotated": LAYERS, "expert_out": "bf16" if args.expert_out_bf16 else "fp32",
+                   "active_experts": n_act},
+        "fp8_tflops": round(total_flops / step_s / 1e12, 3),
+        "step_hbm_frac": round(step_bytes / step_s / 1e9 / PEAK_HBM_GBS, 4),
+        "step_mfma_frac": round(total_flops / step_s / 1e12 / PEAK_FP8_TFLOPS, 4),
+        "step_algorithmic_bytes": int(step_bytes),
+        "stages_us": stages,
+        "roofline": roof,
+        "roofline_other_gemm": roof_other,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        n = args.cpu_sample_tokens or {1: 64, 2: 32, 3: 64, 4: 2, 5: 8}[args.config]
+        out["cpu_baseline"] = cpu_baseline(wl, n)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -212,6 +212,11 @@ int moe_combine(const void* expert_out, int32_t dtype, const int32_t* assign_pos
 /* ---- the whole step -------------------------------------------------------------------- */
 #define MOE_FUSED_EXPERT_OUT_BF16  1   /* keep the per-assignment expert outputs in bf16 */
 
+/* Stage boundaries of moe_fused, for timing: quant_act | route (incl. prelude) | dispatch
+ * (incl. the GEMM tile list) | gate+up GEMM | down GEMM | combine.  The activation
+ * quantisation runs inside the routing kernel, so its own stage is empty. */
+#define MOE_STAGES 6
+
 /* moe_fused: route, dispatch, quant_act, grouped FFN and combine in one call, with no host
  * synchronisation (the single entry point of the MATE page's fp8_fp8_mega_moe, restricted
  * to one GPU).  Output y [T, H] bf16 has the shape of hidden_states ("Fused MoE", return
@@ -221,7 +226,9 @@ int moe_combine(const void* expert_out, int32_t dtype, const int32_t* assign_pos
  *   router_logits     [T, E] float32, or NULL when prelude != NULL.
  *   w13..w2_scale     packed weights and logical scales as for moe_grouped_ffn.
  *   topk_ids, topk_weights, expert_counts   optional outputs ([T,k], [T,k], [E]); NULL to skip.
- *   workspace         >= moe_workspace_size(T, H, I, E, k, flags) bytes (covers the prelude). */
+ *   workspace         >= moe_workspace_size(T, H, I, E, k, flags) bytes (covers the prelude).
+ *   stage_events      NULL, or MOE_STAGES + 1 hipEvent_t (created by the caller) that are
+ *                     recorded on `stream` before the first and after every stage. */
 typedef struct moe_fused_args {
     int32_t T, H, I;
     moe_route_params route;
@@ -240,6 +247,7 @@ typedef struct moe_fused_args {
     void*          workspace;
     size_t         workspace_bytes;
     void*          stream;
+    void* const*   stage_events;
 } moe_fused_args;
 
 int moe_fused(const moe_fused_args* a);

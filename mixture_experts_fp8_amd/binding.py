@@ -62,8 +62,12 @@ class FusedArgs(ctypes.Structure):
                 ("w13_scale", ctypes.c_void_p), ("w2", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p),
                 ("y", ctypes.c_void_p), ("topk_ids", ctypes.c_void_p), ("topk_weights", ctypes.c_void_p),
                 ("expert_counts", ctypes.c_void_p), ("flags", ctypes.c_int32), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p)]
+                ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p),
+                ("stage_events", ctypes.POINTER(ctypes.c_void_p))]
 
+
+MOE_STAGES = 6
+STAGE_NAMES = ["quant_act", "route", "dispatch", "gate_up_gemm", "down_gemm", "combine"]
 
 _lib = None
 
@@ -298,10 +302,19 @@ class MoeFused:
                               ctypes.pointer(self._pre) if self._pre is not None else None,
                               _ptr(w.w13), _ptr(w.w13_scale), _ptr(w.w2), _ptr(w.w2_scale), _ptr(self.y),
                               _ptr(topk_ids), _ptr(topk_weights), _ptr(expert_counts), self.flags, _ptr(self.ws),
-                              self.ws.numel(), None)
+                              self.ws.numel(), None, None)
 
-    def __call__(self, stream: Optional[int] = None) -> torch.Tensor:
+    def __call__(self, stream: Optional[int] = None, stage_events=None) -> torch.Tensor:
+        """stage_events: None or a ctypes array of MOE_STAGES + 1 created hipEvent_t handles
+        that the library records on the stream at the stage boundaries."""
         self.args.stream = _stream() if stream is None else stream
+        if stage_events is None:
+            self.args.stage_events = None
+        else:
+            if len(stage_events) != MOE_STAGES + 1 or not all(stage_events):
+                raise ValueError(f"stage_events: need {MOE_STAGES + 1} created hipEvent_t handles")
+            self._ev_arr = stage_events
+            self.args.stage_events = ctypes.cast(stage_events, ctypes.POINTER(ctypes.c_void_p))
         _check(lib().moe_fused(ctypes.byref(self.args)))
         return self.y
 

@@ -20,6 +20,15 @@
 
 #include <algorithm>
 
+// Decode-tile configurations (fragments per wave, waves per workgroup, K blocks in flight)
+// of the gate+up and the down GEMM; fixed at build time.
+#ifndef MOE_DEC_GEMM1
+#define MOE_DEC_GEMM1 1, 8, 2
+#endif
+#ifndef MOE_DEC_GEMM2
+#define MOE_DEC_GEMM2 2, 4, 2
+#endif
+
 namespace moe {
 
 // ----------------------------------------------------------------------------------------
@@ -46,10 +55,15 @@ __global__ __launch_bounds__(1024) void k_tiles(const int32_t* __restrict__ coun
     if (e == 1023) *ntiles = v + add;
 }
 
+hipError_t launch_tiles(const int32_t* counts, int E, int BM, int2* tiles, int32_t* ntiles, hipStream_t st) {
+    hipLaunchKernelGGL(k_tiles, dim3(1), dim3(1024), 0, st, counts, E, BM, tiles, ntiles);
+    return hipGetLastError();
+}
+
 struct G1Args {
     const uint8_t* xq;
     const uint8_t* xs;
-    int k, H, I;
+    int T, k, H, I;
     const int32_t* counts;
     const int32_t* offsets;
     const int32_t* sorted_assign;
@@ -97,7 +111,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm1(G1Args a) {
     const int nvalid = min(BM, a.counts[e] - m0);
     const int rowbase = a.offsets[e] + m0;
     const int KB = a.H / kGroup;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wv / WN, wn = wv % WN;
 
     __shared__ __align__(16) uint8_t s_a[2][MF][kFragBytes];
@@ -282,7 +296,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm2(G2Args a) {
     const int nvalid = min(BM, a.counts[e] - m0);
     const int rowbase = a.offsets[e] + m0;
     const int KB = a.I / kGroup;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wv / WN, wn = wv % WN;
 
     __shared__ __align__(16) uint8_t s_a[2][MF][kFragBytes];
@@ -391,6 +405,193 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm2(G2Args a) {
 }
 
 // ----------------------------------------------------------------------------------------
+// Decode variants: a tile is one 16-row matrix-core fragment, so there is nothing to share
+// between waves on the A side.  Each wave loads its A fragment (the 16 gathered token rows'
+// 32-byte K slices, L2-resident) and its B fragments (straight from HBM) PF K-blocks ahead
+// into registers; no LDS and no barrier inside the K loop.
+
+__device__ __forceinline__ v8i gmem_a32(const uint8_t* p) {
+    const uint4 lo = *reinterpret_cast<const uint4*>(p);
+    const uint4 hi = *reinterpret_cast<const uint4*>(p + 16);
+    v8i r;
+    r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
+    r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+    return r;
+}
+
+template <int NFW, int WN, int PF>
+__global__ __launch_bounds__(64 * WN) void k_gemm1_dec(G1Args a) {
+    static_assert(NFW * WN == 8, "a workgroup covers 128 gate + 128 up columns");
+    const int tile = blockIdx.x;
+    if (tile >= *a.ntiles) return;
+    const int ib = blockIdx.y;
+    const int2 te = a.tiles[tile];
+    const int e = te.x, m0 = te.y;
+    const int nvalid = min(16, a.counts[e] - m0);
+    const int rowbase = a.offsets[e] + m0;
+    const int KB = a.H / kGroup;
+    const int tid = threadIdx.x, lane = tid & 63, wn = __builtin_amdgcn_readfirstlane(tid >> 6);
+    __shared__ float s_amax[WN][16];
+    __shared__ __align__(16) uint8_t s_h[16 * 128];
+
+    const int tok = a.sorted_assign[rowbase + min(lane & 15, nvalid - 1)] / a.k;
+    const rsrc_t ra = make_rsrc(a.xq, (uint32_t)a.T * a.H);
+    const uint32_t av = (uint32_t)tok * a.H + (lane >> 4) * 32;
+    const uint8_t* sp = a.xs + (int64_t)tok * KB;
+    const int NB16 = 2 * a.I / 16, NBS = 2 * a.I / kGroup;
+    const rsrc_t rw = make_rsrc(a.w13p + (int64_t)e * NB16 * KB * kFragBytes, (uint32_t)NB16 * KB * kFragBytes);
+    const uint8_t* sb = a.w13s + (int64_t)e * KB * NBS;
+    const int g16 = ib * 8 + wn * NFW;
+    const int u16 = a.I / 16 + g16;
+    const uint32_t l16 = lane * 16;
+
+    v8i aq[PF], bq[PF][2 * NFW];
+    int sa[PF];
+    v4f accg[NFW], accu[NFW];
+#pragma unroll
+    for (int j = 0; j < NFW; ++j) accg[j] = accu[j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+        if (p < KB) {
+            aq[p] = buf_a32(ra, av, p * kGroup);
+            sa[p] = sp[p];
+#pragma unroll
+            for (int j = 0; j < NFW; ++j) {
+                bq[p][j] = buf_frag(rw, l16, ((g16 + j) * KB + p) * kFragBytes);
+                bq[p][NFW + j] = buf_frag(rw, l16, ((u16 + j) * KB + p) * kFragBytes);
+            }
+        }
+    for (int kb0 = 0; kb0 < KB; kb0 += PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+            const int kb = kb0 + p;
+            if (kb < KB) {
+                const int sg = sb[kb * NBS + ib];
+                const int su = sb[kb * NBS + a.I / kGroup + ib];
+#pragma unroll
+                for (int j = 0; j < NFW; ++j) {
+                    accg[j] = mfma_fp8(aq[p], bq[p][j], accg[j], sa[p], sg);
+                    accu[j] = mfma_fp8(aq[p], bq[p][NFW + j], accu[j], sa[p], su);
+                }
+                const int kn = kb + PF;
+                if (kn < KB) {
+                    aq[p] = buf_a32(ra, av, kn * kGroup);
+                    sa[p] = sp[kn];
+#pragma unroll
+                    for (int j = 0; j < NFW; ++j) {
+                        bq[p][j] = buf_frag(rw, l16, ((g16 + j) * KB + kn) * kFragBytes);
+                        bq[p][NFW + j] = buf_frag(rw, l16, ((u16 + j) * KB + kn) * kFragBytes);
+                    }
+                }
+            }
+        }
+    }
+    // epilogue: SwiGLU, row amax over the 128 columns (across the WN waves), requant
+    float hv[NFW][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float m = 0.f;
+#pragma unroll
+        for (int j = 0; j < NFW; ++j) {
+            const float g = accg[j][i];
+            const float h = g / (1.0f + expf(-g)) * accu[j][i];
+            hv[j][i] = h;
+            m = fmaxf(m, fabsf(h));
+        }
+        m = max16(m);
+        if ((lane & 15) == 0) s_amax[wn][4 * (lane >> 4) + i] = m;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 4 * (lane >> 4) + i;
+        float am = s_amax[0][row];
+#pragma unroll
+        for (int w = 1; w < WN; ++w) am = fmaxf(am, s_amax[w][row]);
+        const int ex = scale_exponent(am);
+#pragma unroll
+        for (int j = 0; j < NFW; ++j)
+            s_h[row * 128 + (wn * NFW + j) * 16 + (lane & 15)] =
+                (uint8_t)(cvt2_e4m3(ldexpf(hv[j][i], -ex), 0.f) & 0xFFu);
+        if (wn == 0 && (lane & 15) == 0)
+            a.hs[((int64_t)tile * 16 + row) * (a.I / kGroup) + ib] = (uint8_t)(ex + 127);
+    }
+    __syncthreads();
+    const int KB2 = a.I / kGroup;
+    for (int q = tid; q < 128; q += 64 * WN) {
+        const int hh = q >> 6, ln = q & 63;
+        const uint4 v = *reinterpret_cast<const uint4*>(s_h + (ln & 15) * 128 + (ln >> 4) * 32 + hh * 16);
+        *reinterpret_cast<uint4*>(a.hq + ((int64_t)tile * KB2 + ib) * kFragBytes + hh * 1024 + ln * 16) = v;
+    }
+}
+
+template <int NFW, int WN, int PF>
+__global__ __launch_bounds__(64 * WN) void k_gemm2_dec(G2Args a) {
+    const int tile = blockIdx.x;
+    if (tile >= *a.ntiles) return;
+    const int2 te = a.tiles[tile];
+    const int e = te.x, m0 = te.y;
+    const int nvalid = min(16, a.counts[e] - m0);
+    const int rowbase = a.offsets[e] + m0;
+    const int KB = a.I / kGroup;
+    const int lane = threadIdx.x & 63, wn = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const rsrc_t ra = make_rsrc(a.hq + (int64_t)tile * KB * kFragBytes, (uint32_t)KB * kFragBytes);
+    const uint8_t* sp = a.hs + ((int64_t)tile * 16 + (lane & 15)) * KB;
+    const int NB16 = a.H / 16, NBS = a.H / kGroup;
+    const rsrc_t rw = make_rsrc(a.w2p + (int64_t)e * NB16 * KB * kFragBytes, (uint32_t)NB16 * KB * kFragBytes);
+    const uint8_t* sb = a.w2s + (int64_t)e * KB * NBS;
+    const int n16 = blockIdx.y * (NFW * WN) + wn * NFW;
+    const uint32_t l16 = lane * 16;
+
+    v8i aq[PF], bq[PF][NFW];
+    int sa[PF];
+    v4f acc[NFW];
+#pragma unroll
+    for (int j = 0; j < NFW; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+        if (p < KB) {
+            aq[p] = buf_frag(ra, l16, p * kFragBytes);
+            sa[p] = sp[p];
+#pragma unroll
+            for (int j = 0; j < NFW; ++j) bq[p][j] = buf_frag(rw, l16, ((n16 + j) * KB + p) * kFragBytes);
+        }
+    for (int kb0 = 0; kb0 < KB; kb0 += PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+            const int kb = kb0 + p;
+            if (kb < KB) {
+#pragma unroll
+                for (int j = 0; j < NFW; ++j) {
+                    const int sbv = sb[kb * NBS + ((n16 + j) * 16) / kGroup];
+                    acc[j] = mfma_fp8(aq[p], bq[p][j], acc[j], sa[p], sbv);
+                }
+                const int kn = kb + PF;
+                if (kn < KB) {
+                    aq[p] = buf_frag(ra, l16, kn * kFragBytes);
+                    sa[p] = sp[kn];
+#pragma unroll
+                    for (int j = 0; j < NFW; ++j) bq[p][j] = buf_frag(rw, l16, ((n16 + j) * KB + kn) * kFragBytes);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 4 * (lane >> 4) + i;
+        if (row < nvalid) {
+            const int64_t o = (int64_t)(rowbase + row) * a.H;
+#pragma unroll
+            for (int j = 0; j < NFW; ++j) {
+                const int col = (n16 + j) * 16 + (lane & 15);
+                if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o + col] = f32_to_bf16(acc[j][i]);
+                else reinterpret_cast<float*>(a.out)[o + col] = acc[j][i];
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------------------
 FfnPlan ffn_plan(int T, int k, int E) {
     const int64_t A = (int64_t)T * k;
     const int64_t avg = A / E;
@@ -409,74 +610,117 @@ size_t ffn_workspace_bytes(int T, int H, int I, int E, int k) {
 }
 
 template <int MFW, int NFW1, int NFW2, int WM, int WN, int PF1, int PF2>
-static hipError_t run_ffn(const FfnArgs& f, const FfnPlan& p, int2* tiles, int32_t* ntiles, uint8_t* hq,
-                          uint8_t* hs, hipStream_t st) {
-    G1Args g1{f.xq, f.xs, f.k, f.H, f.I, f.counts, f.offsets, f.sorted_assign, tiles, ntiles, f.w13p, f.w13s, hq, hs};
+static hipError_t run_ffn(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid) {
+    G1Args g1{f.xq, f.xs, f.T, f.k, f.H, f.I, f.counts, f.offsets, f.sorted_assign, w.tiles, w.ntiles, f.w13p, f.w13s,
+              w.hq, w.hs};
     hipLaunchKernelGGL((k_gemm1<MFW, NFW1, WM, WN, PF1>), dim3(p.ntiles_max, f.I / kGroup), dim3(64 * WM * WN), 0,
                        st, g1);
-    G2Args g2{hq, hs, f.H, f.I, f.counts, f.offsets, tiles, ntiles, f.w2p, f.w2s, f.out, f.out_bf16};
+    if (mid) {
+        const hipError_t e = hipEventRecord(mid, st);
+        if (e != hipSuccess) return e;
+    }
+    G2Args g2{w.hq, w.hs, f.H, f.I, f.counts, f.offsets, w.tiles, w.ntiles, f.w2p, f.w2s, f.out, f.out_bf16};
     const int ncols = 16 * NFW2 * WN;
     hipLaunchKernelGGL((k_gemm2<MFW, NFW2, WM, WN, PF2>), dim3(p.ntiles_max, f.H / ncols), dim3(64 * WM * WN), 0,
                        st, g2);
     return hipGetLastError();
 }
 
-hipError_t launch_grouped_ffn(const FfnArgs& f, void* ws, hipStream_t st) {
+template <int NFW1, int WN1, int PF1, int NFW2, int WN2, int PF2>
+static hipError_t run_ffn_dec(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid) {
+    G1Args g1{f.xq, f.xs, f.T, f.k, f.H, f.I, f.counts, f.offsets, f.sorted_assign, w.tiles, w.ntiles, f.w13p, f.w13s,
+              w.hq, w.hs};
+    hipLaunchKernelGGL((k_gemm1_dec<NFW1, WN1, PF1>), dim3(p.ntiles_max, f.I / kGroup), dim3(64 * WN1), 0, st, g1);
+    if (mid) {
+        const hipError_t e = hipEventRecord(mid, st);
+        if (e != hipSuccess) return e;
+    }
+    G2Args g2{w.hq, w.hs, f.H, f.I, f.counts, f.offsets, w.tiles, w.ntiles, f.w2p, f.w2s, f.out, f.out_bf16};
+    hipLaunchKernelGGL((k_gemm2_dec<NFW2, WN2, PF2>), dim3(p.ntiles_max, f.H / (16 * NFW2 * WN2)), dim3(64 * WN2), 0,
+                       st, g2);
+    return hipGetLastError();
+}
+
+FfnWs carve_ffn_ws(const FfnArgs& f, void* ws) {
     const FfnPlan p = ffn_plan(f.T, f.k, f.E);
     const size_t rows = (size_t)p.ntiles_max * p.BM;
     uint8_t* w = static_cast<uint8_t*>(ws);
-    int2* tiles = reinterpret_cast<int2*>(w);
+    FfnWs r;
+    r.tiles = reinterpret_cast<int2*>(w);
     w += align256((size_t)p.ntiles_max * 8);
-    int32_t* ntiles = reinterpret_cast<int32_t*>(w);
+    r.ntiles = reinterpret_cast<int32_t*>(w);
     w += align256(4);
-    uint8_t* hq = w;
+    r.hq = w;
     w += align256(rows * f.I);
-    uint8_t* hs = w;
-    hipLaunchKernelGGL(k_tiles, dim3(1), dim3(1024), 0, st, f.counts, f.E, p.BM, tiles, ntiles);
-    // output columns per workgroup of the down GEMM = 16 * NFW2 * WN = 128, a divisor of H
-    if (p.BM == 16) return run_ffn<1, 2, 2, 1, 4, 4, 4>(f, p, tiles, ntiles, hq, hs, st);
-    if (p.BM == 64) return run_ffn<2, 4, 4, 2, 2, 2, 2>(f, p, tiles, ntiles, hq, hs, st);
-    return run_ffn<4, 4, 4, 2, 2, 2, 2>(f, p, tiles, ntiles, hq, hs, st);
+    r.hs = w;
+    return r;
+}
+
+hipError_t launch_grouped_ffn(const FfnArgs& f, void* ws, hipStream_t st, hipEvent_t mid, bool tiles_ready) {
+    const FfnPlan p = ffn_plan(f.T, f.k, f.E);
+    const FfnWs w = carve_ffn_ws(f, ws);
+    if (!tiles_ready) {
+        const hipError_t e = launch_tiles(f.counts, f.E, p.BM, w.tiles, w.ntiles, st);
+        if (e != hipSuccess) return e;
+    }
+    // output columns per workgroup of the down GEMM = 128, a divisor of H
+    if (p.BM == 16) return run_ffn_dec<MOE_DEC_GEMM1, MOE_DEC_GEMM2>(f, p, w, st, mid);
+    if (p.BM == 64) return run_ffn<2, 4, 4, 2, 2, 2, 2>(f, p, w, st, mid);
+    return run_ffn<4, 4, 4, 2, 2, 2, 2>(f, p, w, st, mid);
 }
 
 // ----------------------------------------------------------------------------------------
-// Combine: one workgroup per token; each thread owns 4 consecutive columns.
+// Combine: workgroup (token, 1024-column slice); each thread owns 4 consecutive columns and
+// issues the loads of up to 8 expert rows before summing them in slot order j = 0, 1, ...
+template <bool BF16>
+__device__ __forceinline__ float4 load4(const void* eo, int64_t idx) {
+    if (BF16) {
+        const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(eo) + idx);
+        return make_float4(bf16_to_f32(u.x & 0xFFFFu), bf16_to_f32(u.x >> 16), bf16_to_f32(u.y & 0xFFFFu),
+                           bf16_to_f32(u.y >> 16));
+    }
+    return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(eo) + idx);
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ eo, const int32_t* __restrict__ pos,
                                                  const float* __restrict__ w, int k, int H,
                                                  uint16_t* __restrict__ y) {
     const int t = blockIdx.x;
-    for (int c4 = threadIdx.x; c4 < H / 4; c4 += 256) {
-        float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
-        for (int j = 0; j < k; ++j) {
-            const int p = pos[(int64_t)t * k + j];
-            if (p < 0) continue;   // dropped assignment
-            const float wj = w[(int64_t)t * k + j];
-            float v0, v1, v2, v3;
-            if (BF16) {
-                const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(eo) + (int64_t)p * H + c4 * 4);
-                v0 = bf16_to_f32(u.x & 0xFFFFu); v1 = bf16_to_f32(u.x >> 16);
-                v2 = bf16_to_f32(u.y & 0xFFFFu); v3 = bf16_to_f32(u.y >> 16);
-            } else {
-                const float4 u = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(eo) + (int64_t)p * H + c4 * 4);
-                v0 = u.x; v1 = u.y; v2 = u.z; v3 = u.w;
-            }
-            acc0 = fmaf(wj, v0, acc0);
-            acc1 = fmaf(wj, v1, acc1);
-            acc2 = fmaf(wj, v2, acc2);
-            acc3 = fmaf(wj, v3, acc3);
+    const int c4 = blockIdx.y * 256 + threadIdx.x;
+    if (c4 * 4 >= H) return;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        float4 v[8];
+        float wj[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int j = j0 + u;
+            const int p = j < k ? pos[(int64_t)t * k + j] : -1;
+            wj[u] = p >= 0 ? w[(int64_t)t * k + j] : 0.f;
+            v[u] = p >= 0 ? load4<BF16>(eo, (int64_t)p * H + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-        uint2 o;
-        o.x = (uint32_t)f32_to_bf16(acc0) | ((uint32_t)f32_to_bf16(acc1) << 16);
-        o.y = (uint32_t)f32_to_bf16(acc2) | ((uint32_t)f32_to_bf16(acc3) << 16);
-        *reinterpret_cast<uint2*>(y + (int64_t)t * H + c4 * 4) = o;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (j0 + u < k) {
+                acc.x = fmaf(wj[u], v[u].x, acc.x);
+                acc.y = fmaf(wj[u], v[u].y, acc.y);
+                acc.z = fmaf(wj[u], v[u].z, acc.z);
+                acc.w = fmaf(wj[u], v[u].w, acc.w);
+            }
+        }
     }
+    uint2 o;
+    o.x = (uint32_t)f32_to_bf16(acc.x) | ((uint32_t)f32_to_bf16(acc.y) << 16);
+    o.y = (uint32_t)f32_to_bf16(acc.z) | ((uint32_t)f32_to_bf16(acc.w) << 16);
+    *reinterpret_cast<uint2*>(y + (int64_t)t * H + c4 * 4) = o;
 }
 
 hipError_t launch_combine(const void* eo, int bf16, const int32_t* pos, const float* w, int T, int k, int H,
                           uint16_t* y, hipStream_t st) {
-    if (bf16) hipLaunchKernelGGL(k_combine<true>, dim3(T), dim3(256), 0, st, eo, pos, w, k, H, y);
-    else hipLaunchKernelGGL(k_combine<false>, dim3(T), dim3(256), 0, st, eo, pos, w, k, H, y);
+    const dim3 grid(T, (unsigned)ceil_div(H / 4, 256));
+    if (bf16) hipLaunchKernelGGL(k_combine<true>, grid, dim3(256), 0, st, eo, pos, w, k, H, y);
+    else hipLaunchKernelGGL(k_combine<false>, grid, dim3(256), 0, st, eo, pos, w, k, H, y);
     return hipGetLastError();
 }
 

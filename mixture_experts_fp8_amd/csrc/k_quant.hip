@@ -21,26 +21,7 @@ __global__ __launch_bounds__(256) void k_quant_act(const uint16_t* __restrict__ 
     for (int64_t g = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4; g < ngroups; g += gstride) {
         const int64_t r = g / ngc;
         const int gc = (int)(g - r * ngc);
-        const uint4 v = *reinterpret_cast<const uint4*>(x + r * ld + (int64_t)gc * kGroup + sub * 8);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        float f[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
-            f[2 * i + 1] = bf16_to_f32(w[i] >> 16);
-        }
-        float amax = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
-        amax = max16(amax);
-        const int e = scale_exponent(amax);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = ldexpf(f[i], -e);
-        uint2 q;
-        q.x = cvt4_e4m3(f[0], f[1], f[2], f[3]);
-        q.y = cvt4_e4m3(f[4], f[5], f[6], f[7]);
-        *reinterpret_cast<uint2*>(xq + r * cols + (int64_t)gc * kGroup + sub * 8) = q;
-        if (sub == 0) xs[r * ngc + gc] = (uint8_t)(e + 127);
+        quant_group16(x + r * ld + (int64_t)gc * kGroup, xq + r * cols + (int64_t)gc * kGroup, xs + r * ngc + gc, sub);
     }
 }
 

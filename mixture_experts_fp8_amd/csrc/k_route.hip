@@ -12,49 +12,65 @@
 namespace moe {
 
 // ----------------------------------------------------------------------------------------
-// Gate prelude: logits[t, e] = sum_h ((x[t,h] * r_t) * norm_w[h]) * W_r[e, h] with
-// r_t = 1 / sqrt(mean_h x^2 + eps).  Workgroup (t, expert chunk of 32): the token's
-// normalised row is built in LDS, then each wave takes 8 experts.
-constexpr int kPreludeExperts = 32;
+// Gate prelude: logits[t, e] = r_t * sum_h x[t,h] * norm_w[h] * W_r[e, h], with
+// r_t = 1 / sqrt(mean_h x[t,h]^2 + eps) -- RMSNorm then the float32 router matmul, with the
+// per-token factor r_t applied once to the finished dot product.
+// Workgroup (expert e, 8 tokens), 4 waves splitting H into interleaved 256-wide steps:
+// lane l owns 4 consecutive h per step, loaded as one 16-byte W_r / norm load and one 8-byte
+// load per token; each token's sum of squares comes from the same loaded values.  Partial
+// sums meet in LDS.
+constexpr int kPreT = 8;
 
-__global__ __launch_bounds__(256) void k_gate_prelude(const uint16_t* __restrict__ x, int H, int E,
+__global__ __launch_bounds__(256) void k_gate_prelude(const uint16_t* __restrict__ x, int T, int H, int E,
                                                       const float* __restrict__ norm_w,
                                                       const float* __restrict__ router_w, float eps,
                                                       float* __restrict__ logits) {
-    extern __shared__ float s_xn[];   // [H]
-    __shared__ float s_part[4];
-    const int t = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const uint16_t* xr = x + (int64_t)t * H;
-    float ss = 0.f;
-    for (int h = tid; h < H; h += 256) {
-        const float v = bf16_to_f32(xr[h]);
-        ss = fmaf(v, v, ss);
+    __shared__ float s_part[4][2 * kPreT];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int e = blockIdx.x;
+    const int t0 = blockIdx.y * kPreT;
+    const int nt = min(kPreT, T - t0);
+    const float* wr = router_w + (int64_t)e * H;
+    float d[kPreT], ss[kPreT];
+#pragma unroll
+    for (int t = 0; t < kPreT; ++t) d[t] = ss[t] = 0.f;
+    for (int h = (wv * 64 + lane) * 4; h < H; h += 1024) {
+        const float4 w4 = *reinterpret_cast<const float4*>(wr + h);
+        const float4 n4 = *reinterpret_cast<const float4*>(norm_w + h);
+        const float wn0 = w4.x * n4.x, wn1 = w4.y * n4.y, wn2 = w4.z * n4.z, wn3 = w4.w * n4.w;
+#pragma unroll
+        for (int t = 0; t < kPreT; ++t) {
+            if (t < nt) {
+                const uint2 u = *reinterpret_cast<const uint2*>(x + (int64_t)(t0 + t) * H + h);
+                const float x0 = bf16_to_f32(u.x & 0xFFFFu), x1 = bf16_to_f32(u.x >> 16);
+                const float x2 = bf16_to_f32(u.y & 0xFFFFu), x3 = bf16_to_f32(u.y >> 16);
+                d[t] = fmaf(x0, wn0, fmaf(x1, wn1, fmaf(x2, wn2, fmaf(x3, wn3, d[t]))));
+                ss[t] = fmaf(x0, x0, fmaf(x1, x1, fmaf(x2, x2, fmaf(x3, x3, ss[t]))));
+            }
+        }
     }
-    ss = wave_sum(ss);
-    if (lane == 0) s_part[wv] = ss;
+#pragma unroll
+    for (int t = 0; t < kPreT; ++t) {
+        const float dt = wave_sum(d[t]);
+        const float st = wave_sum(ss[t]);
+        if (lane == 0) {
+            s_part[wv][t] = dt;
+            s_part[wv][kPreT + t] = st;
+        }
+    }
     __syncthreads();
-    const float mean = (s_part[0] + s_part[1] + s_part[2] + s_part[3]) / (float)H;
-    const float r = 1.0f / sqrtf(mean + eps);
-    for (int h = tid; h < H; h += 256) s_xn[h] = (bf16_to_f32(xr[h]) * r) * norm_w[h];
-    __syncthreads();
-    const int e0 = blockIdx.y * kPreludeExperts;
-    for (int i = 0; i < kPreludeExperts / 4; ++i) {
-        const int e = e0 + wv * (kPreludeExperts / 4) + i;
-        if (e >= E) break;
-        const float* wr = router_w + (int64_t)e * H;
-        float acc = 0.f;
-        for (int h = lane; h < H; h += 64) acc = fmaf(s_xn[h], wr[h], acc);
-        acc = wave_sum(acc);
-        if (lane == 0) logits[(int64_t)t * E + e] = acc;
+    if (threadIdx.x < nt) {
+        const int t = threadIdx.x;
+        const float dt = (s_part[0][t] + s_part[1][t]) + (s_part[2][t] + s_part[3][t]);
+        const float st = (s_part[0][kPreT + t] + s_part[1][kPreT + t]) + (s_part[2][kPreT + t] + s_part[3][kPreT + t]);
+        logits[(int64_t)(t0 + t) * E + e] = dt * (1.0f / sqrtf(st / (float)H + eps));
     }
 }
 
 hipError_t launch_gate_prelude(const uint16_t* x, int T, int H, int E, const float* norm_w,
                                const float* router_w, float eps, float* logits, hipStream_t st) {
-    dim3 grid(T, (unsigned)ceil_div(E, kPreludeExperts));
-    hipLaunchKernelGGL(k_gate_prelude, grid, dim3(256), (size_t)H * sizeof(float), st, x, H, E, norm_w,
-                       router_w, eps, logits);
+    dim3 grid((unsigned)E, (unsigned)ceil_div(T, kPreT));
+    hipLaunchKernelGGL(k_gate_prelude, grid, dim3(256), 0, st, x, T, H, E, norm_w, router_w, eps, logits);
     return hipGetLastError();
 }
 
@@ -83,7 +99,7 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 template <int EPL>
 __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, RouteCfg c,
                                                const float* __restrict__ pe_scale, int32_t* __restrict__ ids,
-                                               float* __restrict__ wts) {
+                                               float* __restrict__ wts, QuantOut qo) {
     extern __shared__ unsigned char s_raw[];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int t = blockIdx.x * 4 + wv;
@@ -211,19 +227,39 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
             ids[(int64_t)t * k + j] = id;
             wts[(int64_t)t * k + j] = v;
         }
+        // the token's activation row, quantised per 128 columns (16 lanes per group)
+        if (qo.x) {
+            const int ngc = qo.H / kGroup;
+            const uint16_t* xr = qo.x + (int64_t)t * qo.H;
+            for (int g0 = 0; g0 < ngc; g0 += 32) {
+                uint4 v[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int g = g0 + (lane >> 4) + 4 * i;
+                    if (g < ngc) v[i] = *reinterpret_cast<const uint4*>(xr + g * kGroup + (lane & 15) * 8);
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int g = g0 + (lane >> 4) + 4 * i;
+                    if (g < ngc)
+                        quant_group16_v(v[i], qo.xq + (int64_t)t * qo.H + g * kGroup, qo.xs + (int64_t)t * ngc + g,
+                                        lane & 15);
+                }
+            }
+        }
     }
 }
 
 hipError_t launch_route(const float* logits, const RouteCfg& c, const float* pe_scale, int32_t* ids,
-                        float* weights, hipStream_t st) {
+                        float* weights, hipStream_t st, QuantOut qo) {
     const dim3 grid((unsigned)ceil_div(c.T, 4)), block(256);
     const size_t lds = (size_t)4 * (c.E + 2 * c.k) * 4;
     const int epl = (int)ceil_div(c.E, 64);
-    if (epl <= 1) hipLaunchKernelGGL(k_route<1>, grid, block, lds, st, logits, c, pe_scale, ids, weights);
-    else if (epl <= 2) hipLaunchKernelGGL(k_route<2>, grid, block, lds, st, logits, c, pe_scale, ids, weights);
-    else if (epl <= 4) hipLaunchKernelGGL(k_route<4>, grid, block, lds, st, logits, c, pe_scale, ids, weights);
-    else if (epl <= 8) hipLaunchKernelGGL(k_route<8>, grid, block, lds, st, logits, c, pe_scale, ids, weights);
-    else hipLaunchKernelGGL(k_route<16>, grid, block, lds, st, logits, c, pe_scale, ids, weights);
+    if (epl <= 1) hipLaunchKernelGGL(k_route<1>, grid, block, lds, st, logits, c, pe_scale, ids, weights, qo);
+    else if (epl <= 2) hipLaunchKernelGGL(k_route<2>, grid, block, lds, st, logits, c, pe_scale, ids, weights, qo);
+    else if (epl <= 4) hipLaunchKernelGGL(k_route<4>, grid, block, lds, st, logits, c, pe_scale, ids, weights, qo);
+    else if (epl <= 8) hipLaunchKernelGGL(k_route<8>, grid, block, lds, st, logits, c, pe_scale, ids, weights, qo);
+    else hipLaunchKernelGGL(k_route<16>, grid, block, lds, st, logits, c, pe_scale, ids, weights, qo);
     return hipGetLastError();
 }
 
@@ -342,15 +378,155 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ ids
     }
 }
 
+// Single-workgroup dispatch for small A (8 waves).  Wave w owns the contiguous segment
+// [w*seg, (w+1)*seg) of the flat assignments: pass 1 counts ids per wave, the bases
+// offsets[e] + (earlier waves' count of e) follow from one scan, pass 2 ranks equal ids
+// inside each 64-wide round with ballots and keeps per-wave running positions.  With
+// tiles != nullptr it also writes the GEMM tile list of BM-row tiles.
+constexpr int kOneWaves = 8;
+
+__global__ __launch_bounds__(64 * kOneWaves) void k_dispatch_one(const int32_t* __restrict__ ids, int A, int E,
+                                                                  int nbits, int32_t* __restrict__ counts,
+                                                                  int32_t* __restrict__ offsets,
+                                                                  int32_t* __restrict__ sorted_assign,
+                                                                  int32_t* __restrict__ assign_pos, int BM,
+                                                                  int2* __restrict__ tiles,
+                                                                  int32_t* __restrict__ ntiles) {
+    __shared__ int s_w[kOneWaves][MOE_DISPATCH_MAX_E];   // per-wave counts, then per-wave positions
+    __shared__ int s_tmp[16];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    for (int i = tid; i < kOneWaves * E; i += 64 * kOneWaves) s_w[i / E][i % E] = 0;
+    __syncthreads();
+    const int seg = (int)ceil_div(A, kOneWaves);
+    const int b0 = wv * seg, b1 = min(A, b0 + seg);
+    for (int f = b0 + lane; f < b1; f += 64) {
+        const int e = ids[f];
+        if ((unsigned)e < (unsigned)E) atomicAdd(&s_w[wv][e], 1);
+    }
+    __syncthreads();
+    // per expert: total count, then the exclusive scan over experts and the per-wave bases
+    int tot[2] = {0, 0};
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int e = tid + q * 64 * kOneWaves;
+        if (e < E)
+            for (int w = 0; w < kOneWaves; ++w) tot[q] += s_w[w][e];
+    }
+    // scan of tot over e = tid (q=0) then e = tid + 512 (q=1)
+    int run_base = 0;
+    int excl[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        int v = tot[q];
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int u = __shfl_up(v, o);
+            if (lane >= o) v += u;
+        }
+        if (lane == 63) s_tmp[wv] = v;
+        __syncthreads();
+        int add = 0, all = 0;
+        for (int w = 0; w < kOneWaves; ++w) {
+            if (w < wv) add += s_tmp[w];
+            all += s_tmp[w];
+        }
+        __syncthreads();
+        excl[q] = run_base + add + v - tot[q];
+        run_base += all;
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int e = tid + q * 64 * kOneWaves;
+        if (e < E) {
+            counts[e] = tot[q];
+            offsets[e] = excl[q];
+            if (e == E - 1) offsets[E] = excl[q] + tot[q];
+            int p = excl[q];
+            for (int w = 0; w < kOneWaves; ++w) {
+                const int c = s_w[w][e];
+                s_w[w][e] = p;
+                p += c;
+            }
+        }
+    }
+    __syncthreads();
+    const uint64_t lt = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+    for (int f0 = b0; f0 < b1; f0 += 64) {
+        const int f = f0 + lane;
+        int e = f < b1 ? ids[f] : 0;
+        const bool valid = f < b1 && (unsigned)e < (unsigned)E;
+        if (!valid) e = 0;
+        if (f < b1 && !valid) assign_pos[f] = -1;
+        uint64_t peers = __ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = (e >> b) & 1;
+            const uint64_t bb = __ballot(bit);
+            peers &= bit ? bb : ~bb;
+        }
+        int base = 0;
+        if (valid) base = s_w[wv][e];
+        const int before = __popcll(peers & lt);
+        if (valid) {
+            const int pos = base + before;
+            sorted_assign[pos] = f;
+            assign_pos[f] = pos;
+            if (before == 0) s_w[wv][e] = base + __popcll(peers);
+        }
+    }
+    if (tiles) {
+        // tile list: BM-row tiles per expert in expert order (counts are in global memory now)
+        __syncthreads();
+        int n[2], st[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int e = tid + q * 64 * kOneWaves;
+            n[q] = e < E ? (tot[q] + BM - 1) / BM : 0;
+        }
+        int base2 = 0;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            int v = n[q];
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int u = __shfl_up(v, o);
+                if (lane >= o) v += u;
+            }
+            if (lane == 63) s_tmp[wv] = v;
+            __syncthreads();
+            int add = 0, all = 0;
+            for (int w = 0; w < kOneWaves; ++w) {
+                if (w < wv) add += s_tmp[w];
+                all += s_tmp[w];
+            }
+            __syncthreads();
+            st[q] = base2 + add + v - n[q];
+            base2 += all;
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int e = tid + q * 64 * kOneWaves;
+            for (int i = 0; i < n[q]; ++i) tiles[st[q] + i] = make_int2(e, i * BM);
+        }
+        if (tid == 0) *ntiles = base2;
+    }
+}
+
 hipError_t launch_dispatch(const int32_t* ids, int A, int E, int32_t* chunk_ws, int32_t* counts,
-                           int32_t* offsets, int32_t* sorted_assign, int32_t* assign_pos, hipStream_t st) {
-    const int nchunks = (int)ceil_div(A, kScatterChunk);
+                           int32_t* offsets, int32_t* sorted_assign, int32_t* assign_pos, hipStream_t st,
+                           int BM, int2* tiles, int32_t* ntiles) {
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
+    if (A <= kDispatchOneMaxA) {
+        hipLaunchKernelGGL(k_dispatch_one, dim3(1), dim3(64 * kOneWaves), 0, st, ids, A, E, nbits, counts, offsets,
+                           sorted_assign, assign_pos, BM, tiles, ntiles);
+        return hipGetLastError();
+    }
+    const int nchunks = (int)ceil_div(A, kScatterChunk);
     hipLaunchKernelGGL(k_hist, dim3(nchunks), dim3(256), (size_t)E * 4, st, ids, A, E, chunk_ws);
     hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, chunk_ws, nchunks, E, counts, offsets);
     hipLaunchKernelGGL(k_scatter, dim3(nchunks), dim3(256), (size_t)4 * E * 4, st, ids, A, E, nbits, chunk_ws,
                        sorted_assign, assign_pos);
+    if (tiles) return launch_tiles(counts, E, BM, tiles, ntiles, st);
     return hipGetLastError();
 }
 

@@ -84,7 +84,9 @@ int check_prelude(const char* op, const moe_gate_prelude* g, const uint16_t* hid
         return fail(MOE_ERR_INVALID, "%s: prelude norm_weight and router_weight must not be NULL", op);
     if (!hidden) return fail(MOE_ERR_INVALID, "%s: hidden_states must not be NULL with a prelude", op);
     if (H < 1) return fail(MOE_ERR_INVALID, "%s: H (%d) must be > 0", op, H);
-    if (H > 16384) return fail(MOE_ERR_UNSUPPORTED, "%s: prelude H (%d) exceeds max 16384", op, H);
+    if (H % 4) return fail(MOE_ERR_UNSUPPORTED, "%s: prelude H (%d) must be a multiple of 4", op, H);
+    if (!aligned(g->norm_weight, 16) || !aligned(g->router_weight, 16) || !aligned(hidden, 8))
+        return fail(MOE_ERR_UNSUPPORTED, "%s: prelude weights must be 16-byte and hidden_states 8-byte aligned", op);
     if (!(g->rms_eps >= 0.f) || !std::isfinite(g->rms_eps))
         return fail(MOE_ERR_INVALID, "%s: rms_eps must be finite and >= 0", op);
     return MOE_OK;
@@ -105,6 +107,10 @@ moe::RouteCfg route_cfg(const moe_route_params* p, int T, bool prelude) {
     return c;
 }
 
+size_t route_chunk_bytes(int T, int E, int k) {
+    return align256((size_t)moe::ceil_div((int64_t)T * k, moe::kScatterChunk) * E * 4);
+}
+
 // route + dispatch with all pointers already validated; ws holds route_ws_bytes
 hipError_t do_route(const moe_route_params* p, int T, const float* logits, const uint16_t* hidden, int H,
                     const moe_gate_prelude* g, int flags, int32_t* ids, float* wts, int32_t* counts,
@@ -112,7 +118,7 @@ hipError_t do_route(const moe_route_params* p, int T, const float* logits, const
     const int E = p->num_experts, k = p->top_k;
     const int64_t A = (int64_t)T * k;
     int32_t* chunk_ws = reinterpret_cast<int32_t*>(ws);
-    uint8_t* after = ws + align256((size_t)moe::ceil_div(A, moe::kScatterChunk) * E * 4);
+    uint8_t* after = ws + route_chunk_bytes(T, E, k);
     hipError_t e = hipSuccess;
     if (!(flags & MOE_ROUTE_IDS_GIVEN)) {
         const float* lg = logits;
@@ -330,16 +336,37 @@ int moe_fused(const moe_fused_args* a) {
     if (a->expert_counts) counts = a->expert_counts;
 
     hipStream_t st = static_cast<hipStream_t>(a->stream);
-    hipError_t e = moe::launch_quant_act(a->hidden_states, T, H, H, xq, xs, st);
+    hipEvent_t ev[MOE_STAGES + 1] = {};
+    if (a->stage_events)
+        for (int i = 0; i <= MOE_STAGES; ++i) ev[i] = static_cast<hipEvent_t>(a->stage_events[i]);
+    hipError_t e = hipSuccess;
+    auto mark = [&](int i) {
+        if (e == hipSuccess && ev[i]) e = hipEventRecord(ev[i], st);
+    };
+    const int bf = (a->flags & MOE_FUSED_EXPERT_OUT_BF16) ? 1 : 0;
+    moe::FfnArgs f{T, k, H, I, E, xq, xs, counts, offsets, sorted, a->w13, a->w13_scale, a->w2, a->w2_scale, eo, bf};
+    const moe::FfnWs fw = moe::carve_ffn_ws(f, fws);
+    const moe::FfnPlan plan = moe::ffn_plan(T, k, E);
+    // the activation quantisation runs inside the routing kernel (one wave per token)
+    mark(0);
+    mark(1);
+    float* pl = reinterpret_cast<float*>(rws + route_chunk_bytes(T, E, k));
+    if (e == hipSuccess && a->prelude)
+        e = moe::launch_gate_prelude(a->hidden_states, T, H, E, a->prelude->norm_weight, a->prelude->router_weight,
+                                     a->prelude->rms_eps, pl, st);
     if (e == hipSuccess)
-        e = do_route(&a->route, T, a->router_logits, a->hidden_states, H, a->prelude, 0, ids, wts, counts, offsets,
-                     sorted, pos, rws, st);
-    if (e == hipSuccess) {
-        const int bf = (a->flags & MOE_FUSED_EXPERT_OUT_BF16) ? 1 : 0;
-        moe::FfnArgs f{T, k, H, I, E, xq, xs, counts, offsets, sorted, a->w13, a->w13_scale, a->w2, a->w2_scale, eo, bf};
-        e = moe::launch_grouped_ffn(f, fws, st);
-        if (e == hipSuccess) e = moe::launch_combine(eo, bf, pos, wts, T, k, H, a->y, st);
-    }
+        e = moe::launch_route(a->prelude ? pl : a->router_logits, route_cfg(&a->route, T, a->prelude != nullptr),
+                              a->prelude ? a->prelude->per_expert_scale : nullptr, ids, wts, st,
+                              moe::QuantOut{a->hidden_states, H, xq, xs});
+    mark(2);
+    if (e == hipSuccess)
+        e = moe::launch_dispatch(ids, (int)A, E, reinterpret_cast<int32_t*>(rws), counts, offsets, sorted, pos, st,
+                                 plan.BM, fw.tiles, fw.ntiles);
+    mark(3);
+    if (e == hipSuccess) e = moe::launch_grouped_ffn(f, fws, st, ev[4], true);
+    mark(5);
+    if (e == hipSuccess) e = moe::launch_combine(eo, bf, pos, wts, T, k, H, a->y, st);
+    mark(6);
     if (e != hipSuccess) return hip_fail(op, e);
     return ok();
 }

@@ -76,6 +76,67 @@ __device__ __forceinline__ v4f mfma_fp8(v8i a, v8i b, v4f acc, int sa, int sb) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, sa, 0, sb);
 }
 
+// Quantise one 128-column bf16 group held by 16 consecutive lanes (lane `sub` owns
+// elements 8*sub .. 8*sub+7, passed in v): E4M3 bytes to dq[8*sub ..], the UE8M0 scale
+// byte to *ds (written by sub == 0).  All 16 lanes of the group must be active.
+__device__ __forceinline__ void quant_group16_v(const uint4 v, uint8_t* __restrict__ dq, uint8_t* __restrict__ ds,
+                                                int sub) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+        f[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    amax = max16(amax);
+    const int e = scale_exponent(amax);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = ldexpf(f[i], -e);
+    uint2 q;
+    q.x = cvt4_e4m3(f[0], f[1], f[2], f[3]);
+    q.y = cvt4_e4m3(f[4], f[5], f[6], f[7]);
+    *reinterpret_cast<uint2*>(dq + sub * 8) = q;
+    if (sub == 0) *ds = (uint8_t)(e + 127);
+}
+
+__device__ __forceinline__ void quant_group16(const uint16_t* __restrict__ src, uint8_t* __restrict__ dq,
+                                              uint8_t* __restrict__ ds, int sub) {
+    quant_group16_v(*reinterpret_cast<const uint4*>(src + sub * 8), dq, ds, sub);
+}
+
+// Raw buffer resource over [base, base + bytes): loads take one per-lane 32-bit offset
+// (VGPR) plus a wave-uniform offset (SGPR); reads past `bytes` return zero.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Cache policy of the weight-stream loads: 2 = non-temporal (each weight byte is read once
+// per step; keeping it out of the caches leaves them to the activations and router tensors).
+#ifndef MOE_WLOAD_AUX
+#define MOE_WLOAD_AUX 2
+#endif
+
+// One 2 KB matrix-core operand in packed order: lane l's 32 bytes are the 16 at
+// soff + 16*l and the 16 at soff + 1024 + 16*l.
+__device__ __forceinline__ v8i buf_frag(rsrc_t r, uint32_t lane16, uint32_t soff) {
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    const v4i lo = __builtin_amdgcn_raw_buffer_load_b128(r, lane16, soff, MOE_WLOAD_AUX);
+    const v4i hi = __builtin_amdgcn_raw_buffer_load_b128(r, lane16, soff + 1024, MOE_WLOAD_AUX);
+    return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// 32 contiguous bytes at voff + soff.
+__device__ __forceinline__ v8i buf_a32(rsrc_t r, uint32_t voff, uint32_t soff) {
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    const v4i lo = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    const v4i hi = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff + 16, 0);
+    return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
 __host__ __device__ constexpr inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace moe

@@ -26,11 +26,24 @@ constexpr int kScatterChunk = 1024;   // assignments per dispatch workgroup
 
 hipError_t launch_gate_prelude(const uint16_t* x, int T, int H, int E, const float* norm_w,
                                const float* router_w, float eps, float* logits, hipStream_t st);
+// optional fused activation quantisation in the routing kernel (x == nullptr: none)
+struct QuantOut {
+    const uint16_t* x;   // [T, H] bf16
+    int H;
+    uint8_t* xq;         // [T, H]
+    uint8_t* xs;         // [T, H/128]
+};
 hipError_t launch_route(const float* logits, const RouteCfg& c, const float* pe_scale, int32_t* ids,
-                        float* weights, hipStream_t st);
-// hist + scan + scatter; chunk_ws holds nchunks*E int32
+                        float* weights, hipStream_t st, QuantOut qo = QuantOut{nullptr, 0, nullptr, nullptr});
+// Dispatch (stable counting sort).  A <= kDispatchOneMaxA: one workgroup; otherwise
+// hist + scan + scatter over chunks (chunk_ws holds nchunks*E int32).  With tiles given,
+// also the GEMM tile list for BM-row tiles.
+constexpr int kDispatchOneMaxA = 16384;
+#define MOE_DISPATCH_MAX_E 1024
 hipError_t launch_dispatch(const int32_t* ids, int A, int E, int32_t* chunk_ws, int32_t* counts,
-                           int32_t* offsets, int32_t* sorted_assign, int32_t* assign_pos, hipStream_t st);
+                           int32_t* offsets, int32_t* sorted_assign, int32_t* assign_pos, hipStream_t st,
+                           int BM = 0, int2* tiles = nullptr, int32_t* ntiles = nullptr);
+hipError_t launch_tiles(const int32_t* counts, int E, int BM, int2* tiles, int32_t* ntiles, hipStream_t st);
 
 // ---- grouped FFN
 struct FfnPlan {
@@ -54,7 +67,17 @@ struct FfnArgs {
     void* out;
     int out_bf16;
 };
-hipError_t launch_grouped_ffn(const FfnArgs& a, void* ws, hipStream_t st);
+struct FfnWs {
+    int2* tiles;
+    int32_t* ntiles;
+    uint8_t* hq;
+    uint8_t* hs;
+};
+FfnWs carve_ffn_ws(const FfnArgs& a, void* ws);
+// `mid`: optional event recorded between the gate+up and the down GEMM; tiles_ready: the
+// tile list in the workspace was already written (by launch_dispatch)
+hipError_t launch_grouped_ffn(const FfnArgs& a, void* ws, hipStream_t st, hipEvent_t mid = nullptr,
+                              bool tiles_ready = false);
 
 hipError_t launch_combine(const void* eo, int bf16, const int32_t* pos, const float* w, int T, int k, int H,
                           uint16_t* y, hipStream_t st);

@@ -71,7 +71,10 @@ def test_route_other_errors():
     pre = B.GatePrelude(FAKE, FAKE, None, -1.0)
     assert _route(p, logits=None, prelude=ctypes.byref(pre), hidden=FAKE, H=64) == B.MOE_ERR_INVALID
     pre = B.GatePrelude(FAKE, FAKE, None, 1e-6)
-    assert _route(p, logits=None, prelude=ctypes.byref(pre), hidden=FAKE, H=1 << 20) == B.MOE_ERR_UNSUPPORTED
+    assert _route(p, logits=None, prelude=ctypes.byref(pre), hidden=FAKE, H=66) == B.MOE_ERR_UNSUPPORTED
+    assert "multiple of 4" in M.moe_last_error()
+    pre = B.GatePrelude(FAKE + 4, FAKE, None, 1e-6)
+    assert _route(p, logits=None, prelude=ctypes.byref(pre), hidden=FAKE, H=64) == B.MOE_ERR_UNSUPPORTED
 
 
 def test_quant_act_validation():
