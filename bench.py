@@ -51,14 +51,15 @@ def parse():
 
 
 class HipEvents:
-    """Raw hipEvent_t handles (created eagerly) for the library's stage boundaries."""
+    """Raw hipEvent_t handles (created eagerly) for the library's stage boundaries; only
+    the slots listed in `only` (default: all) get an event, the others stay null."""
 
-    def __init__(self, n: int):
+    def __init__(self, n: int, only=None):
         import ctypes
         self.ct = ctypes
         self.hip = ctypes.CDLL("libamdhip64.so")
         self.ev = (ctypes.c_void_p * n)()
-        for i in range(n):
+        for i in (range(n) if only is None else only):
             h = ctypes.c_void_p()
             rc = self.hip.hipEventCreate(ctypes.byref(h))
             if rc != 0:
@@ -74,7 +75,8 @@ class HipEvents:
 
     def destroy(self):
         for h in self.ev:
-            self.hip.hipEventDestroy(self.ct.c_void_p(h))
+            if h:
+                self.hip.hipEventDestroy(self.ct.c_void_p(h))
 
 
 def kernel_source_hash() -> str:
@@ -272,10 +274,22 @@ def main():
     eo_bytes = 2 if args.expert_out_bf16 else 4
     per_stage, n_act = stage_bytes_flops(wl, cnt, eo_bytes)
     dom = max(per_stage, key=lambda n: stage_s[B.STAGE_NAMES.index(n)])
-    nbytes, flops = per_stage[dom]
-    roof = roofline_entry(dom, stage_s[B.STAGE_NAMES.index(dom)], nbytes, flops, load_traffic(wl.name, dom))
     other = [n for n in per_stage if n != dom][0]
-    roof_other = roofline_entry(other, stage_s[B.STAGE_NAMES.index(other)], *per_stage[other], load_traffic(wl.name, other))
+
+    def kernel_time(name):
+        """Average duration of one stage's kernel, from only the two events around it."""
+        i = B.STAGE_NAMES.index(name)
+        ev2 = [HipEvents(nst + 1, only=(i, i + 1)) for _ in range(args.steps)]
+        for k in range(args.steps):
+            calls[k % LAYERS](stage_events=ev2[k].ev)
+        torch.cuda.synchronize()
+        t = sum(e.elapsed_s(i, i + 1) for e in ev2) / args.steps
+        for e in ev2:
+            e.destroy()
+        return t
+
+    roof = roofline_entry(dom, kernel_time(dom), *per_stage[dom], load_traffic(wl.name, dom))
+    roof_other = roofline_entry(other, kernel_time(other), *per_stage[other], load_traffic(wl.name, other))
 
     step_bytes = step_algorithmic_bytes(wl, n_act)
     total_flops = wl.flops()

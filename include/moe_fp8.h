@@ -227,8 +227,8 @@ int moe_combine(const void* expert_out, int32_t dtype, const int32_t* assign_pos
  *   w13..w2_scale     packed weights and logical scales as for moe_grouped_ffn.
  *   topk_ids, topk_weights, expert_counts   optional outputs ([T,k], [T,k], [E]); NULL to skip.
  *   workspace         >= moe_workspace_size(T, H, I, E, k, flags) bytes (covers the prelude).
- *   stage_events      NULL, or MOE_STAGES + 1 hipEvent_t (created by the caller) that are
- *                     recorded on `stream` before the first and after every stage. */
+ *   stage_events      NULL, or MOE_STAGES + 1 hipEvent_t (created by the caller; NULL entries
+ *                     are skipped) recorded on `stream` before the first and after every stage. */
 typedef struct moe_fused_args {
     int32_t T, H, I;
     moe_route_params route;

@@ -305,14 +305,14 @@ class MoeFused:
                               self.ws.numel(), None, None)
 
     def __call__(self, stream: Optional[int] = None, stage_events=None) -> torch.Tensor:
-        """stage_events: None or a ctypes array of MOE_STAGES + 1 created hipEvent_t handles
-        that the library records on the stream at the stage boundaries."""
+        """stage_events: None or a ctypes array of MOE_STAGES + 1 hipEvent_t handles that the
+        library records on the stream at the stage boundaries (null entries are skipped)."""
         self.args.stream = _stream() if stream is None else stream
         if stage_events is None:
             self.args.stage_events = None
         else:
-            if len(stage_events) != MOE_STAGES + 1 or not all(stage_events):
-                raise ValueError(f"stage_events: need {MOE_STAGES + 1} created hipEvent_t handles")
+            if len(stage_events) != MOE_STAGES + 1:
+                raise ValueError(f"stage_events: need {MOE_STAGES + 1} hipEvent_t slots")
             self._ev_arr = stage_events
             self.args.stage_events = ctypes.cast(stage_events, ctypes.POINTER(ctypes.c_void_p))
         _check(lib().moe_fused(ctypes.byref(self.args)))
