@@ -31,6 +31,8 @@
 
 namespace moe {
 
+constexpr int kMaxKB = 256;   // K blocks (of 128) per GEMM: H and I up to 32768
+
 // ----------------------------------------------------------------------------------------
 // Tile list: tiles of BM rows per expert, in expert order.
 __global__ __launch_bounds__(1024) void k_tiles(const int32_t* __restrict__ counts, int E, int BM,
@@ -433,6 +435,7 @@ __global__ __launch_bounds__(64 * WN) void k_gemm1_dec(G1Args a) {
     const int tid = threadIdx.x, lane = tid & 63, wn = __builtin_amdgcn_readfirstlane(tid >> 6);
     __shared__ float s_amax[WN][16];
     __shared__ __align__(16) uint8_t s_h[16 * 128];
+    __shared__ uint8_t s_sg[kMaxKB], s_su[kMaxKB];   // weight-block scales of this column block
 
     const int tok = a.sorted_assign[rowbase + min(lane & 15, nvalid - 1)] / a.k;
     const rsrc_t ra = make_rsrc(a.xq, (uint32_t)a.T * a.H);
@@ -444,6 +447,11 @@ __global__ __launch_bounds__(64 * WN) void k_gemm1_dec(G1Args a) {
     const int g16 = ib * 8 + wn * NFW;
     const int u16 = a.I / 16 + g16;
     const uint32_t l16 = lane * 16;
+    for (int i = tid; i < KB; i += 64 * WN) {
+        s_sg[i] = sb[i * NBS + ib];
+        s_su[i] = sb[i * NBS + a.I / kGroup + ib];
+    }
+    __syncthreads();
 
     v8i aq[PF], bq[PF][2 * NFW];
     int sa[PF];
@@ -466,8 +474,8 @@ __global__ __launch_bounds__(64 * WN) void k_gemm1_dec(G1Args a) {
         for (int p = 0; p < PF; ++p) {
             const int kb = kb0 + p;
             if (kb < KB) {
-                const int sg = sb[kb * NBS + ib];
-                const int su = sb[kb * NBS + a.I / kGroup + ib];
+                const int sg = s_sg[kb];
+                const int su = s_su[kb];
 #pragma unroll
                 for (int j = 0; j < NFW; ++j) {
                     accg[j] = mfma_fp8(aq[p], bq[p][j], accg[j], sa[p], sg);
@@ -542,6 +550,10 @@ __global__ __launch_bounds__(64 * WN) void k_gemm2_dec(G2Args a) {
     const uint8_t* sb = a.w2s + (int64_t)e * KB * NBS;
     const int n16 = blockIdx.y * (NFW * WN) + wn * NFW;
     const uint32_t l16 = lane * 16;
+    static_assert(NFW * WN == 8, "a workgroup covers one 128-column scale block");
+    __shared__ uint8_t s_sb[kMaxKB];
+    for (int i = threadIdx.x; i < KB; i += 64 * WN) s_sb[i] = sb[i * NBS + blockIdx.y];
+    __syncthreads();
 
     v8i aq[PF], bq[PF][NFW];
     int sa[PF];
@@ -561,11 +573,9 @@ __global__ __launch_bounds__(64 * WN) void k_gemm2_dec(G2Args a) {
         for (int p = 0; p < PF; ++p) {
             const int kb = kb0 + p;
             if (kb < KB) {
+                const int sbv = s_sb[kb];
 #pragma unroll
-                for (int j = 0; j < NFW; ++j) {
-                    const int sbv = sb[kb * NBS + ((n16 + j) * 16) / kGroup];
-                    acc[j] = mfma_fp8(aq[p], bq[p][j], acc[j], sa[p], sbv);
-                }
+                for (int j = 0; j < NFW; ++j) acc[j] = mfma_fp8(aq[p], bq[p][j], acc[j], sa[p], sbv);
                 const int kn = kb + PF;
                 if (kn < KB) {
                     aq[p] = buf_frag(ra, l16, kn * kFragBytes);
@@ -586,6 +596,281 @@ __global__ __launch_bounds__(64 * WN) void k_gemm2_dec(G2Args a) {
                 const int col = (n16 + j) * 16 + (lane & 15);
                 if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o + col] = f32_to_bf16(acc[j][i]);
                 else reinterpret_cast<float*>(a.out)[o + col] = acc[j][i];
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------------------
+// Prefill variants: workgroup tile 128 rows x 256 columns, 4 waves as 2 (rows) x 2
+// (columns), wave tile 64 x 128 (4 x 8 matrix-core fragments).  A and B fragments travel
+// global -> LDS by the LDS-DMA form of the buffer load (no staging registers) through a
+// 3-stage ring; each stage is its own LDS array so the compiler tracks the DMA writes per
+// stage.  Per K block: wait until this wave's DMA for the block has landed, barrier, issue
+// the DMA two blocks ahead, then read fragments from LDS and run 32 MFMAs per wave.  The A
+// row scales of all K blocks are loaded into LDS once per tile.
+
+constexpr int kPfBM = 128, kPfStageA = 8 * kFragBytes, kPfStage = kPfStageA + 16 * kFragBytes;  // 48 KB
+constexpr int kPfMaxKB = 64;     // K blocks whose A scales fit the LDS table
+
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+// vmcnt <= n (n < 16), other counters untouched
+#define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8))
+
+__device__ __forceinline__ void dma16(rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(lds), 16, voff, soff, 0, 0);
+}
+
+// gate+up prefill GEMM; grid (I/128 column blocks, tiles)
+__global__ __launch_bounds__(256, 1) void k_gemm1_pf(G1Args a) {
+    const int ib = blockIdx.x;
+    const int tile = blockIdx.y;
+    if (tile >= *a.ntiles) return;
+    const int2 te = a.tiles[tile];
+    const int e = te.x, m0 = te.y;
+    const int nvalid = min(kPfBM, a.counts[e] - m0);
+    const int rowbase = a.offsets[e] + m0;
+    const int KB = a.H / kGroup;
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wv >> 1, wn = wv & 1;
+
+    __shared__ __align__(16) uint8_t st0[kPfStage], st1[kPfStage], st2[kPfStage];
+    __shared__ uint8_t s_sa[kPfBM * kPfMaxKB];
+    __shared__ uint8_t s_sg[kPfMaxKB], s_su[kPfMaxKB];
+    __shared__ float s_amax[2][kPfBM];
+
+    // A scales of every K block: thread pair (row, half) copies half of the row's KB bytes
+    {
+        const int r = tid >> 1, half = tid & 1;
+        const int tok = a.sorted_assign[rowbase + min(r, nvalid - 1)] / a.k;
+        const uint8_t* src = a.xs + (int64_t)tok * KB;
+        for (int kb = half; kb < KB; kb += 2) s_sa[r * KB + kb] = src[kb];
+    }
+    // this wave's DMA sources: A fragments 2wv, 2wv+1 (rows gathered), B fragments 4wv..4wv+3
+    const rsrc_t ra = make_rsrc(a.xq, (uint32_t)a.T * a.H);
+    uint32_t aoff[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int r = (2 * wv + q) * 16 + (lane & 15);
+        const int tok = a.sorted_assign[rowbase + min(r, nvalid - 1)] / a.k;
+        aoff[q] = (uint32_t)tok * a.H + (lane >> 4) * 32;
+    }
+    const int NB16 = 2 * a.I / 16, NBS = 2 * a.I / kGroup;
+    const rsrc_t rw = make_rsrc(a.w13p + (int64_t)e * NB16 * KB * kFragBytes, (uint32_t)NB16 * KB * kFragBytes);
+    const uint8_t* sb = a.w13s + (int64_t)e * KB * NBS;
+    for (int i = tid; i < KB; i += 256) {
+        s_sg[i] = sb[i * NBS + ib];
+        s_su[i] = sb[i * NBS + a.I / kGroup + ib];
+    }
+    int bn16[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int f = 4 * wv + j;
+        bn16[j] = f < 8 ? ib * 8 + f : a.I / 16 + ib * 8 + (f - 8);
+    }
+    const uint32_t l16 = lane * 16;
+    auto issue = [&](int kb, uint8_t* st) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) dma16(ra, st + (2 * wv + q) * kFragBytes + h * 1024, aoff[q] + h * 16, kb * kGroup);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                dma16(rw, st + kPfStageA + (4 * wv + j) * kFragBytes + h * 1024, l16,
+                      (uint32_t)(bn16[j] * KB + kb) * kFragBytes + h * 1024);
+    };
+
+    v4f accg[4][4], accu[4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) accg[mi][j] = accu[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    __builtin_amdgcn_s_waitcnt(0);   // scale copies done before the DMA count starts
+    issue(0, st0);
+    issue(min(1, KB - 1), st1);
+
+    // Every step issues the DMA of block kb + 2 (clamped to the last block: the duplicate
+    // lands in a stage nobody reads again), so exactly 12 DMA loads per wave follow the
+    // ones of block kb and vmcnt(12) means "block kb has landed".
+    auto step = [&](int kb, const uint8_t* cur, uint8_t* nxt) {
+        WAIT_VMCNT(12);
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS reads and writes done
+        __builtin_amdgcn_s_barrier();
+        issue(min(kb + 2, KB - 1), nxt);
+        v8i af[4];
+        int sa[4];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            const int mf = wm * 4 + mi;
+            af[mi] = lds_frag(cur + mf * kFragBytes, lane);
+            sa[mi] = s_sa[(mf * 16 + (lane & 15)) * KB + kb];
+        }
+        const int sg = s_sg[kb];
+        const int su = s_su[kb];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const v8i bg = lds_frag(cur + kPfStageA + (wn * 4 + j) * kFragBytes, lane);
+            const v8i bu = lds_frag(cur + kPfStageA + (8 + wn * 4 + j) * kFragBytes, lane);
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) {
+                accg[mi][j] = mfma_fp8(af[mi], bg, accg[mi][j], sa[mi], sg);
+                accu[mi][j] = mfma_fp8(af[mi], bu, accu[mi][j], sa[mi], su);
+            }
+        }
+    };
+    int kb0 = 0;
+    for (; kb0 + 3 <= KB; kb0 += 3) {
+        step(kb0, st0, st2);
+        step(kb0 + 1, st1, st0);
+        step(kb0 + 2, st2, st1);
+    }
+    if (kb0 < KB) step(kb0, st0, st2);
+    if (kb0 + 1 < KB) step(kb0 + 1, st1, st0);
+    __builtin_amdgcn_s_waitcnt(0);   // the trailing duplicate DMA must land before LDS is reused
+
+    // ---- epilogue: SwiGLU, row amax over the 128 columns (two waves), requant
+    float hv[4][4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float m = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float g = accg[mi][j][i];
+                const float h = g / (1.0f + expf(-g)) * accu[mi][j][i];
+                hv[mi][j][i] = h;
+                m = fmaxf(m, fabsf(h));
+            }
+            m = max16(m);
+            if ((lane & 15) == 0) s_amax[wn][(wm * 4 + mi) * 16 + 4 * (lane >> 4) + i] = m;
+        }
+    }
+    __syncthreads();
+    uint8_t* s_h = st0;   // [128][128] bytes
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = (wm * 4 + mi) * 16 + 4 * (lane >> 4) + i;
+            const int ex = scale_exponent(fmaxf(s_amax[0][row], s_amax[1][row]));
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                s_h[row * 128 + (wn * 4 + j) * 16 + (lane & 15)] =
+                    (uint8_t)(cvt2_e4m3(ldexpf(hv[mi][j][i], -ex), 0.f) & 0xFFu);
+            if (wn == 0 && (lane & 15) == 0)
+                a.hs[((int64_t)tile * kPfBM + row) * (a.I / kGroup) + ib] = (uint8_t)(ex + 127);
+        }
+    }
+    __syncthreads();
+    const int KB2 = a.I / kGroup;
+    for (int q = tid; q < 8 * 128; q += 256) {
+        const int mf = q >> 7, w = q & 127, hh = w >> 6, ln = w & 63;
+        const uint4 v = *reinterpret_cast<const uint4*>(s_h + (mf * 16 + (ln & 15)) * 128 + (ln >> 4) * 32 + hh * 16);
+        *reinterpret_cast<uint4*>(a.hq + (((int64_t)tile * 8 + mf) * KB2 + ib) * kFragBytes + hh * 1024 + ln * 16) = v;
+    }
+}
+
+// down prefill GEMM; grid (H/256 column blocks, tiles)
+__global__ __launch_bounds__(256, 1) void k_gemm2_pf(G2Args a) {
+    const int nb = blockIdx.x;
+    const int tile = blockIdx.y;
+    if (tile >= *a.ntiles) return;
+    const int2 te = a.tiles[tile];
+    const int e = te.x, m0 = te.y;
+    const int nvalid = min(kPfBM, a.counts[e] - m0);
+    const int rowbase = a.offsets[e] + m0;
+    const int KB = a.I / kGroup;
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wv >> 1, wn = wv & 1;
+
+    __shared__ __align__(16) uint8_t st0[kPfStage], st1[kPfStage], st2[kPfStage];
+    __shared__ uint8_t s_sa[kPfBM * kPfMaxKB];
+    __shared__ uint8_t s_sb[2][kPfMaxKB];   // the two 128-column scale blocks of this workgroup
+
+    {
+        const uint8_t* src = a.hs + (int64_t)tile * kPfBM * KB;   // [row][kb], contiguous for the tile
+        for (int i = tid; i < kPfBM * KB; i += 256) s_sa[i] = src[i];
+    }
+    const rsrc_t ra = make_rsrc(a.hq + (int64_t)tile * 8 * KB * kFragBytes, (uint32_t)8 * KB * kFragBytes);
+    const int NB16 = a.H / 16, NBS = a.H / kGroup;
+    const rsrc_t rw = make_rsrc(a.w2p + (int64_t)e * NB16 * KB * kFragBytes, (uint32_t)NB16 * KB * kFragBytes);
+    const uint8_t* sb = a.w2s + (int64_t)e * KB * NBS;
+    for (int i = tid; i < 2 * KB; i += 256) s_sb[i & 1][i >> 1] = sb[(i >> 1) * NBS + nb * 2 + (i & 1)];
+    const uint32_t l16 = lane * 16;
+    auto issue = [&](int kb, uint8_t* st) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                dma16(ra, st + (2 * wv + q) * kFragBytes + h * 1024, l16,
+                      (uint32_t)((2 * wv + q) * KB + kb) * kFragBytes + h * 1024);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                dma16(rw, st + kPfStageA + (4 * wv + j) * kFragBytes + h * 1024, l16,
+                      (uint32_t)((nb * 16 + 4 * wv + j) * KB + kb) * kFragBytes + h * 1024);
+    };
+
+    v4f acc[4][8];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    __builtin_amdgcn_s_waitcnt(0);
+    issue(0, st0);
+    issue(min(1, KB - 1), st1);
+
+    auto step = [&](int kb, const uint8_t* cur, uint8_t* nxt) {
+        WAIT_VMCNT(12);
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+        issue(min(kb + 2, KB - 1), nxt);
+        v8i af[4];
+        int sa[4];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            const int mf = wm * 4 + mi;
+            af[mi] = lds_frag(cur + mf * kFragBytes, lane);
+            sa[mi] = s_sa[(mf * 16 + (lane & 15)) * KB + kb];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int f = wn * 8 + j;
+            const v8i b = lds_frag(cur + kPfStageA + f * kFragBytes, lane);
+            const int sbv = s_sb[wn][kb];
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) acc[mi][j] = mfma_fp8(af[mi], b, acc[mi][j], sa[mi], sbv);
+        }
+    };
+    int kb0 = 0;
+    for (; kb0 + 3 <= KB; kb0 += 3) {
+        step(kb0, st0, st2);
+        step(kb0 + 1, st1, st0);
+        step(kb0 + 2, st2, st1);
+    }
+    if (kb0 < KB) step(kb0, st0, st2);
+    if (kb0 + 1 < KB) step(kb0 + 1, st1, st0);
+    __builtin_amdgcn_s_waitcnt(0);   // the trailing duplicate DMA must land before LDS is reused
+
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = (wm * 4 + mi) * 16 + 4 * (lane >> 4) + i;
+            if (row < nvalid) {
+                const int64_t o = (int64_t)(rowbase + row) * a.H;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int col = nb * 256 + (wn * 8 + j) * 16 + (lane & 15);
+                    if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o + col] = f32_to_bf16(acc[mi][j][i]);
+                    else reinterpret_cast<float*>(a.out)[o + col] = acc[mi][j][i];
+                }
             }
         }
     }
@@ -641,6 +926,19 @@ static hipError_t run_ffn_dec(const FfnArgs& f, const FfnPlan& p, const FfnWs& w
     return hipGetLastError();
 }
 
+static hipError_t run_ffn_pf(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid) {
+    G1Args g1{f.xq, f.xs, f.T, f.k, f.H, f.I, f.counts, f.offsets, f.sorted_assign, w.tiles, w.ntiles, f.w13p, f.w13s,
+              w.hq, w.hs};
+    hipLaunchKernelGGL(k_gemm1_pf, dim3(f.I / kGroup, p.ntiles_max), dim3(256), 0, st, g1);
+    if (mid) {
+        const hipError_t e = hipEventRecord(mid, st);
+        if (e != hipSuccess) return e;
+    }
+    G2Args g2{w.hq, w.hs, f.H, f.I, f.counts, f.offsets, w.tiles, w.ntiles, f.w2p, f.w2s, f.out, f.out_bf16};
+    hipLaunchKernelGGL(k_gemm2_pf, dim3(f.H / 256, p.ntiles_max), dim3(256), 0, st, g2);
+    return hipGetLastError();
+}
+
 FfnWs carve_ffn_ws(const FfnArgs& f, void* ws) {
     const FfnPlan p = ffn_plan(f.T, f.k, f.E);
     const size_t rows = (size_t)p.ntiles_max * p.BM;
@@ -666,6 +964,8 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, void* ws, hipStream_t st, hipEve
     // output columns per workgroup of the down GEMM = 128, a divisor of H
     if (p.BM == 16) return run_ffn_dec<MOE_DEC_GEMM1, MOE_DEC_GEMM2>(f, p, w, st, mid);
     if (p.BM == 64) return run_ffn<2, 4, 4, 2, 2, 2, 2>(f, p, w, st, mid);
+    if (f.H / kGroup <= kPfMaxKB && f.I / kGroup <= kPfMaxKB && f.H % 256 == 0)
+        return run_ffn_pf(f, p, w, st, mid);
     return run_ffn<4, 4, 4, 2, 2, 2, 2>(f, p, w, st, mid);
 }
 

@@ -142,6 +142,8 @@ int check_ffn_shapes(const char* op, int T, int k, int H, int I, int E) {
         return fail(MOE_ERR_UNSUPPORTED, "%s: num_experts (%d) exceeds max %d", op, E, MOE_MAX_EXPERTS);
     if (H % 128) return fail(MOE_ERR_UNSUPPORTED, "%s: hidden size H (%d) must be a multiple of 128", op, H);
     if (I % 128) return fail(MOE_ERR_UNSUPPORTED, "%s: intermediate size I (%d) must be a multiple of 128", op, I);
+    if (H > 32768 || I > 32768)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: H (%d) and I (%d) must not exceed 32768", op, H, I);
     if ((int64_t)T * k > INT32_MAX / 2)
         return fail(MOE_ERR_UNSUPPORTED, "%s: T * top_k (%lld) too large", op, (long long)T * k);
     return MOE_OK;

@@ -38,7 +38,7 @@ hipError_t launch_route(const float* logits, const RouteCfg& c, const float* pe_
 // Dispatch (stable counting sort).  A <= kDispatchOneMaxA: one workgroup; otherwise
 // hist + scan + scatter over chunks (chunk_ws holds nchunks*E int32).  With tiles given,
 // also the GEMM tile list for BM-row tiles.
-constexpr int kDispatchOneMaxA = 16384;
+constexpr int kDispatchOneMaxA = 4096;
 #define MOE_DISPATCH_MAX_E 1024
 hipError_t launch_dispatch(const int32_t* ids, int A, int E, int32_t* chunk_ws, int32_t* counts,
                            int32_t* offsets, int32_t* sorted_assign, int32_t* assign_pos, hipStream_t st,
