@@ -28,6 +28,13 @@
 #ifndef MOE_DEC_GEMM2
 #define MOE_DEC_GEMM2 2, 4, 2
 #endif
+// Prefill kernels: k_gemm{1,2}_pf (LDS-DMA staging) or k_gemm{1,2}_pfr (register staging)
+#ifndef MOE_PF_GEMM1
+#define MOE_PF_GEMM1 k_gemm1_pfr
+#endif
+#ifndef MOE_PF_GEMM2
+#define MOE_PF_GEMM2 k_gemm2_pfr
+#endif
 
 namespace moe {
 
@@ -877,6 +884,297 @@ __global__ __launch_bounds__(256, 1) void k_gemm2_pf(G2Args a) {
 }
 
 // ----------------------------------------------------------------------------------------
+// Register-staged prefill variants: the same tiles, but each wave loads its 12 16-byte
+// pieces of a K block into registers (buffer loads) and writes them to LDS itself.  Two LDS
+// buffers and two register sets: at step kb the wave issues the loads of block kb+2 into
+// one register set, computes block kb from LDS, then stores the other register set (block
+// kb+1, loaded a step earlier) into the free LDS buffer; one barrier per step.  Plain loads
+// into registers keep the compiler's vmcnt accounting exact.
+
+struct PfLoads {
+    uint4 v[12];
+};
+
+__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t voff, uint32_t soff, int aux) {
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    const v4i x = aux ? __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2)
+                      : __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return make_uint4((uint32_t)x[0], (uint32_t)x[1], (uint32_t)x[2], (uint32_t)x[3]);
+}
+
+__global__ __launch_bounds__(256, 1) void k_gemm1_pfr(G1Args a) {
+    const int ib = blockIdx.x;
+    const int tile = blockIdx.y;
+    if (tile >= *a.ntiles) return;
+    const int2 te = a.tiles[tile];
+    const int e = te.x, m0 = te.y;
+    const int nvalid = min(kPfBM, a.counts[e] - m0);
+    const int rowbase = a.offsets[e] + m0;
+    const int KB = a.H / kGroup;
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wv >> 1, wn = wv & 1;
+
+    __shared__ __align__(16) uint8_t buf[2][kPfStage];
+    __shared__ uint8_t s_sa[kPfBM * kPfMaxKB];
+    __shared__ uint8_t s_sg[kPfMaxKB], s_su[kPfMaxKB];
+    __shared__ float s_amax[2][kPfBM];
+
+    {
+        const int r = tid >> 1, half = tid & 1;
+        const int tok = a.sorted_assign[rowbase + min(r, nvalid - 1)] / a.k;
+        const uint8_t* src = a.xs + (int64_t)tok * KB;
+        for (int kb = half; kb < KB; kb += 2) s_sa[r * KB + kb] = src[kb];
+    }
+    const rsrc_t ra = make_rsrc(a.xq, (uint32_t)a.T * a.H);
+    uint32_t aoff[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int r = (2 * wv + q) * 16 + (lane & 15);
+        const int tok = a.sorted_assign[rowbase + min(r, nvalid - 1)] / a.k;
+        aoff[q] = (uint32_t)tok * a.H + (lane >> 4) * 32;
+    }
+    const int NB16 = 2 * a.I / 16, NBS = 2 * a.I / kGroup;
+    const rsrc_t rw = make_rsrc(a.w13p + (int64_t)e * NB16 * KB * kFragBytes, (uint32_t)NB16 * KB * kFragBytes);
+    const uint8_t* sb = a.w13s + (int64_t)e * KB * NBS;
+    for (int i = tid; i < KB; i += 256) {
+        s_sg[i] = sb[i * NBS + ib];
+        s_su[i] = sb[i * NBS + a.I / kGroup + ib];
+    }
+    int bn16[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int f = 4 * wv + j;
+        bn16[j] = f < 8 ? ib * 8 + f : a.I / 16 + ib * 8 + (f - 8);
+    }
+    const uint32_t l16 = lane * 16;
+    auto load = [&](int kb, PfLoads& L) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) L.v[q * 2 + h] = bload16(ra, aoff[q] + h * 16, kb * kGroup, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                L.v[4 + j * 2 + h] = bload16(rw, l16, (uint32_t)(bn16[j] * KB + kb) * kFragBytes + h * 1024, 0);
+    };
+    auto store = [&](const PfLoads& L, uint8_t* st) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                *reinterpret_cast<uint4*>(st + (2 * wv + q) * kFragBytes + h * 1024 + l16) = L.v[q * 2 + h];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                *reinterpret_cast<uint4*>(st + kPfStageA + (4 * wv + j) * kFragBytes + h * 1024 + l16) = L.v[4 + j * 2 + h];
+    };
+
+    v4f accg[4][4], accu[4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) accg[mi][j] = accu[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    PfLoads R0, R1;
+    load(0, R0);
+    load(min(1, KB - 1), R1);
+    store(R0, buf[0]);
+    __syncthreads();
+
+    auto compute = [&](int kb, const uint8_t* cur) {
+        v8i af[4];
+        int sa[4];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            const int mf = wm * 4 + mi;
+            af[mi] = lds_frag(cur + mf * kFragBytes, lane);
+            sa[mi] = s_sa[(mf * 16 + (lane & 15)) * KB + kb];
+        }
+        const int sg = s_sg[kb];
+        const int su = s_su[kb];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const v8i bg = lds_frag(cur + kPfStageA + (wn * 4 + j) * kFragBytes, lane);
+            const v8i bu = lds_frag(cur + kPfStageA + (8 + wn * 4 + j) * kFragBytes, lane);
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) {
+                accg[mi][j] = mfma_fp8(af[mi], bg, accg[mi][j], sa[mi], sg);
+                accu[mi][j] = mfma_fp8(af[mi], bu, accu[mi][j], sa[mi], su);
+            }
+        }
+    };
+    // step kb (even): LDS buf0 = block kb, R1 = block kb+1 in flight; issue kb+2 into R0
+    int kb = 0;
+    for (; kb + 2 <= KB; kb += 2) {
+        load(min(kb + 2, KB - 1), R0);
+        compute(kb, buf[0]);
+        store(R1, buf[1]);
+        __syncthreads();
+        load(min(kb + 3, KB - 1), R1);
+        compute(kb + 1, buf[1]);
+        store(R0, buf[0]);
+        __syncthreads();
+    }
+    if (kb < KB) {
+        compute(kb, buf[0]);
+        __syncthreads();
+    }
+
+    float hv[4][4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float m = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float g = accg[mi][j][i];
+                const float h = g / (1.0f + expf(-g)) * accu[mi][j][i];
+                hv[mi][j][i] = h;
+                m = fmaxf(m, fabsf(h));
+            }
+            m = max16(m);
+            if ((lane & 15) == 0) s_amax[wn][(wm * 4 + mi) * 16 + 4 * (lane >> 4) + i] = m;
+        }
+    }
+    __syncthreads();
+    uint8_t* s_h = buf[0];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = (wm * 4 + mi) * 16 + 4 * (lane >> 4) + i;
+            const int ex = scale_exponent(fmaxf(s_amax[0][row], s_amax[1][row]));
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                s_h[row * 128 + (wn * 4 + j) * 16 + (lane & 15)] =
+                    (uint8_t)(cvt2_e4m3(ldexpf(hv[mi][j][i], -ex), 0.f) & 0xFFu);
+            if (wn == 0 && (lane & 15) == 0)
+                a.hs[((int64_t)tile * kPfBM + row) * (a.I / kGroup) + ib] = (uint8_t)(ex + 127);
+        }
+    }
+    __syncthreads();
+    const int KB2 = a.I / kGroup;
+    for (int q = tid; q < 8 * 128; q += 256) {
+        const int mf = q >> 7, w = q & 127, hh = w >> 6, ln = w & 63;
+        const uint4 v = *reinterpret_cast<const uint4*>(s_h + (mf * 16 + (ln & 15)) * 128 + (ln >> 4) * 32 + hh * 16);
+        *reinterpret_cast<uint4*>(a.hq + (((int64_t)tile * 8 + mf) * KB2 + ib) * kFragBytes + hh * 1024 + ln * 16) = v;
+    }
+}
+
+__global__ __launch_bounds__(256, 1) void k_gemm2_pfr(G2Args a) {
+    const int nb = blockIdx.x;
+    const int tile = blockIdx.y;
+    if (tile >= *a.ntiles) return;
+    const int2 te = a.tiles[tile];
+    const int e = te.x, m0 = te.y;
+    const int nvalid = min(kPfBM, a.counts[e] - m0);
+    const int rowbase = a.offsets[e] + m0;
+    const int KB = a.I / kGroup;
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wv >> 1, wn = wv & 1;
+
+    __shared__ __align__(16) uint8_t buf[2][kPfStage];
+    __shared__ uint8_t s_sa[kPfBM * kPfMaxKB];
+    __shared__ uint8_t s_sb[2][kPfMaxKB];
+    {
+        const uint8_t* src = a.hs + (int64_t)tile * kPfBM * KB;
+        for (int i = tid; i < kPfBM * KB; i += 256) s_sa[i] = src[i];
+    }
+    const rsrc_t ra = make_rsrc(a.hq + (int64_t)tile * 8 * KB * kFragBytes, (uint32_t)8 * KB * kFragBytes);
+    const int NB16 = a.H / 16, NBS = a.H / kGroup;
+    const rsrc_t rw = make_rsrc(a.w2p + (int64_t)e * NB16 * KB * kFragBytes, (uint32_t)NB16 * KB * kFragBytes);
+    const uint8_t* sb = a.w2s + (int64_t)e * KB * NBS;
+    for (int i = tid; i < 2 * KB; i += 256) s_sb[i & 1][i >> 1] = sb[(i >> 1) * NBS + nb * 2 + (i & 1)];
+    const uint32_t l16 = lane * 16;
+    auto load = [&](int kb, PfLoads& L) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                L.v[q * 2 + h] = bload16(ra, l16, (uint32_t)((2 * wv + q) * KB + kb) * kFragBytes + h * 1024, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                L.v[4 + j * 2 + h] = bload16(rw, l16, (uint32_t)((nb * 16 + 4 * wv + j) * KB + kb) * kFragBytes + h * 1024, 0);
+    };
+    auto store = [&](const PfLoads& L, uint8_t* st) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                *reinterpret_cast<uint4*>(st + (2 * wv + q) * kFragBytes + h * 1024 + l16) = L.v[q * 2 + h];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                *reinterpret_cast<uint4*>(st + kPfStageA + (4 * wv + j) * kFragBytes + h * 1024 + l16) = L.v[4 + j * 2 + h];
+    };
+
+    v4f acc[4][8];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    PfLoads R0, R1;
+    load(0, R0);
+    load(min(1, KB - 1), R1);
+    store(R0, buf[0]);
+    __syncthreads();
+
+    auto compute = [&](int kb, const uint8_t* cur) {
+        v8i af[4];
+        int sa[4];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            const int mf = wm * 4 + mi;
+            af[mi] = lds_frag(cur + mf * kFragBytes, lane);
+            sa[mi] = s_sa[(mf * 16 + (lane & 15)) * KB + kb];
+        }
+        const int sbv = s_sb[wn][kb];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const v8i b = lds_frag(cur + kPfStageA + (wn * 8 + j) * kFragBytes, lane);
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) acc[mi][j] = mfma_fp8(af[mi], b, acc[mi][j], sa[mi], sbv);
+        }
+    };
+    int kb = 0;
+    for (; kb + 2 <= KB; kb += 2) {
+        load(min(kb + 2, KB - 1), R0);
+        compute(kb, buf[0]);
+        store(R1, buf[1]);
+        __syncthreads();
+        load(min(kb + 3, KB - 1), R1);
+        compute(kb + 1, buf[1]);
+        store(R0, buf[0]);
+        __syncthreads();
+    }
+    if (kb < KB) compute(kb, buf[0]);
+
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = (wm * 4 + mi) * 16 + 4 * (lane >> 4) + i;
+            if (row < nvalid) {
+                const int64_t o = (int64_t)(rowbase + row) * a.H;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int col = nb * 256 + (wn * 8 + j) * 16 + (lane & 15);
+                    if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o + col] = f32_to_bf16(acc[mi][j][i]);
+                    else reinterpret_cast<float*>(a.out)[o + col] = acc[mi][j][i];
+                }
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------------------
 FfnPlan ffn_plan(int T, int k, int E) {
     const int64_t A = (int64_t)T * k;
     const int64_t avg = A / E;
@@ -929,13 +1227,13 @@ static hipError_t run_ffn_dec(const FfnArgs& f, const FfnPlan& p, const FfnWs& w
 static hipError_t run_ffn_pf(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid) {
     G1Args g1{f.xq, f.xs, f.T, f.k, f.H, f.I, f.counts, f.offsets, f.sorted_assign, w.tiles, w.ntiles, f.w13p, f.w13s,
               w.hq, w.hs};
-    hipLaunchKernelGGL(k_gemm1_pf, dim3(f.I / kGroup, p.ntiles_max), dim3(256), 0, st, g1);
+    hipLaunchKernelGGL(MOE_PF_GEMM1, dim3(f.I / kGroup, p.ntiles_max), dim3(256), 0, st, g1);
     if (mid) {
         const hipError_t e = hipEventRecord(mid, st);
         if (e != hipSuccess) return e;
     }
     G2Args g2{w.hq, w.hs, f.H, f.I, f.counts, f.offsets, w.tiles, w.ntiles, f.w2p, f.w2s, f.out, f.out_bf16};
-    hipLaunchKernelGGL(k_gemm2_pf, dim3(f.H / 256, p.ntiles_max), dim3(256), 0, st, g2);
+    hipLaunchKernelGGL(MOE_PF_GEMM2, dim3(f.H / 256, p.ntiles_max), dim3(256), 0, st, g2);
     return hipGetLastError();
 }
 
