@@ -28,12 +28,14 @@
 #ifndef MOE_DEC_GEMM2
 #define MOE_DEC_GEMM2 2, 4, 2
 #endif
-// Prefill kernels: k_gemm{1,2}_pf (LDS-DMA staging) or k_gemm{1,2}_pfr (register staging)
+// Prefill kernels: k_gemm{1,2}_pfn<PFB> (waves split the columns; A staged in LDS, B
+// streamed into registers), k_gemm{1,2}_pfr (2x2 waves, both operands register-staged
+// through LDS) or k_gemm{1,2}_pf (2x2 waves, LDS-DMA staging)
 #ifndef MOE_PF_GEMM1
-#define MOE_PF_GEMM1 k_gemm1_pfr
+#define MOE_PF_GEMM1 k_gemm1_pfr<2>
 #endif
 #ifndef MOE_PF_GEMM2
-#define MOE_PF_GEMM2 k_gemm2_pfr
+#define MOE_PF_GEMM2 k_gemm2_pfr<2>
 #endif
 
 namespace moe {
@@ -902,6 +904,7 @@ __device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t voff, uint32_t soff,
     return make_uint4((uint32_t)x[0], (uint32_t)x[1], (uint32_t)x[2], (uint32_t)x[3]);
 }
 
+template <int NR>
 __global__ __launch_bounds__(256, 1) void k_gemm1_pfr(G1Args a) {
     const int ib = blockIdx.x;
     const int tile = blockIdx.y;
@@ -977,10 +980,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm1_pfr(G1Args a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) accg[mi][j] = accu[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    PfLoads R0, R1;
-    load(0, R0);
-    load(min(1, KB - 1), R1);
-    store(R0, buf[0]);
+    PfLoads R[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) load(min(r, KB - 1), R[r]);
+    store(R[0], buf[0]);
     __syncthreads();
 
     auto compute = [&](int kb, const uint8_t* cur) {
@@ -1005,22 +1008,27 @@ __global__ __launch_bounds__(256, 1) void k_gemm1_pfr(G1Args a) {
             }
         }
     };
-    // step kb (even): LDS buf0 = block kb, R1 = block kb+1 in flight; issue kb+2 into R0
+    // step kb: LDS buffer kb%2 holds block kb; register set kb%NR is free (its block was
+    // stored a step ago) and takes block kb+NR; after the MMAs, register set (kb+1)%NR
+    // (block kb+1, loaded NR-1 steps ago) goes to LDS buffer (kb+1)%2.
+    // Loads and stores are unconditional (block indices clamped to the last block; the
+    // duplicates land in buffers nobody reads) so the number of loads in flight is the same
+    // on every path and the compiler's vmcnt waits stay exact.
+    auto step = [&](int kb, const int ri, const int bi) {
+        load(min(kb + NR, KB - 1), R[ri]);
+        compute(kb, buf[bi]);
+        store(R[(ri + 1) % NR], buf[bi ^ 1]);
+        __syncthreads();
+    };
+    constexpr int U = NR == 3 ? 6 : (NR == 4 ? 4 : 2);
     int kb = 0;
-    for (; kb + 2 <= KB; kb += 2) {
-        load(min(kb + 2, KB - 1), R0);
-        compute(kb, buf[0]);
-        store(R1, buf[1]);
-        __syncthreads();
-        load(min(kb + 3, KB - 1), R1);
-        compute(kb + 1, buf[1]);
-        store(R0, buf[0]);
-        __syncthreads();
+    for (; kb + U <= KB; kb += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) step(kb + u, u % NR, u & 1);
     }
-    if (kb < KB) {
-        compute(kb, buf[0]);
-        __syncthreads();
-    }
+#pragma unroll
+    for (int u = 0; u < U - 1; ++u)
+        if (kb + u < KB) step(kb + u, u % NR, u & 1);
 
     float hv[4][4][4];
 #pragma unroll
@@ -1064,6 +1072,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm1_pfr(G1Args a) {
     }
 }
 
+template <int NR>
 __global__ __launch_bounds__(256, 1) void k_gemm2_pfr(G2Args a) {
     const int nb = blockIdx.x;
     const int tile = blockIdx.y;
@@ -1120,10 +1129,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm2_pfr(G2Args a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    PfLoads R0, R1;
-    load(0, R0);
-    load(min(1, KB - 1), R1);
-    store(R0, buf[0]);
+    PfLoads R[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) load(min(r, KB - 1), R[r]);
+    store(R[0], buf[0]);
     __syncthreads();
 
     auto compute = [&](int kb, const uint8_t* cur) {
@@ -1143,18 +1152,27 @@ __global__ __launch_bounds__(256, 1) void k_gemm2_pfr(G2Args a) {
             for (int mi = 0; mi < 4; ++mi) acc[mi][j] = mfma_fp8(af[mi], b, acc[mi][j], sa[mi], sbv);
         }
     };
+    // step kb: LDS buffer kb%2 holds block kb; register set kb%NR is free (its block was
+    // stored a step ago) and takes block kb+NR; after the MMAs, register set (kb+1)%NR
+    // (block kb+1, loaded NR-1 steps ago) goes to LDS buffer (kb+1)%2.
+    // Loads and stores are unconditional (block indices clamped to the last block; the
+    // duplicates land in buffers nobody reads) so the number of loads in flight is the same
+    // on every path and the compiler's vmcnt waits stay exact.
+    auto step = [&](int kb, const int ri, const int bi) {
+        load(min(kb + NR, KB - 1), R[ri]);
+        compute(kb, buf[bi]);
+        store(R[(ri + 1) % NR], buf[bi ^ 1]);
+        __syncthreads();
+    };
+    constexpr int U = NR == 3 ? 6 : (NR == 4 ? 4 : 2);
     int kb = 0;
-    for (; kb + 2 <= KB; kb += 2) {
-        load(min(kb + 2, KB - 1), R0);
-        compute(kb, buf[0]);
-        store(R1, buf[1]);
-        __syncthreads();
-        load(min(kb + 3, KB - 1), R1);
-        compute(kb + 1, buf[1]);
-        store(R0, buf[0]);
-        __syncthreads();
+    for (; kb + U <= KB; kb += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) step(kb + u, u % NR, u & 1);
     }
-    if (kb < KB) compute(kb, buf[0]);
+#pragma unroll
+    for (int u = 0; u < U - 1; ++u)
+        if (kb + u < KB) step(kb + u, u % NR, u & 1);
 
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
@@ -1175,11 +1193,266 @@ __global__ __launch_bounds__(256, 1) void k_gemm2_pfr(G2Args a) {
 }
 
 // ----------------------------------------------------------------------------------------
+// Column-split prefill variants: wave w owns all 8 row fragments of the 128-row tile and 4
+// column fragments, so no B fragment is shared between waves.  A (the 8 row fragments of a
+// K block, 16 KB) is staged once in LDS for all four waves, register-staged and double
+// buffered (thread t owns the 16-byte pieces t, t+256, t+512, t+768; piece p sits at byte
+// 16p of the LDS block, i.e. fragment p/128 in matrix-core order).  B fragments stream from
+// memory straight into each wave's registers PFB K blocks ahead.  LDS traffic per K block
+// and workgroup: 16 KB written + 64 KB read.
+
+template <bool kG1, int PFB>
+struct PfnCore {
+    // one K block: 8 row fragments x 4 column fragments of MFMAs for this wave
+    static __device__ __forceinline__ void mma(v4f (&acc)[8][4], const uint8_t* ab, const v8i (&b)[4],
+                                               const uint8_t* s_sa, int KB, int kb, int lane, const int (&sbv)[4]) {
+#pragma unroll
+        for (int mf = 0; mf < 8; ++mf) {
+            const v8i af = lds_frag(ab + mf * kFragBytes, lane);
+            const int sa = s_sa[(mf * 16 + (lane & 15)) * KB + kb];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[mf][j] = mfma_fp8(af, b[j], acc[mf][j], sa, sbv[j]);
+        }
+    }
+};
+
+template <int PFB>
+__global__ __launch_bounds__(256, 1) void k_gemm1_pfn(G1Args a) {
+    const int ib = blockIdx.x;
+    const int tile = blockIdx.y;
+    if (tile >= *a.ntiles) return;
+    const int2 te = a.tiles[tile];
+    const int e = te.x, m0 = te.y;
+    const int nvalid = min(kPfBM, a.counts[e] - m0);
+    const int rowbase = a.offsets[e] + m0;
+    const int KB = a.H / kGroup;
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    __shared__ __align__(16) uint8_t abuf[2][8 * kFragBytes];
+    __shared__ uint8_t s_sa[kPfBM * kPfMaxKB];
+    __shared__ uint8_t s_sg[kPfMaxKB], s_su[kPfMaxKB];
+    __shared__ float s_amax[4][kPfBM];
+
+    {
+        const int r = tid >> 1, half = tid & 1;
+        const int tok = a.sorted_assign[rowbase + min(r, nvalid - 1)] / a.k;
+        const uint8_t* src = a.xs + (int64_t)tok * KB;
+        for (int kb = half; kb < KB; kb += 2) s_sa[r * KB + kb] = src[kb];
+    }
+    const int NB16 = 2 * a.I / 16, NBS = 2 * a.I / kGroup;
+    const uint8_t* sb = a.w13s + (int64_t)e * KB * NBS;
+    for (int i = tid; i < KB; i += 256) {
+        s_sg[i] = sb[i * NBS + ib];
+        s_su[i] = sb[i * NBS + a.I / kGroup + ib];
+    }
+    const rsrc_t ra = make_rsrc(a.xq, (uint32_t)a.T * a.H);
+    uint32_t aoff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int p = tid + 256 * i, mf = p >> 7, hh = (p >> 6) & 1, ln = p & 63;
+        const int r = mf * 16 + (ln & 15);
+        const int tok = a.sorted_assign[rowbase + min(r, nvalid - 1)] / a.k;
+        aoff[i] = (uint32_t)tok * a.H + (ln >> 4) * 32 + hh * 16;
+    }
+    const rsrc_t rw = make_rsrc(a.w13p + (int64_t)e * NB16 * KB * kFragBytes, (uint32_t)NB16 * KB * kFragBytes);
+    const int g16 = ib * 8 + 2 * wv, u16 = a.I / 16 + g16;
+    const int bn16[4] = {g16, g16 + 1, u16, u16 + 1};
+    const uint32_t l16 = lane * 16;
+
+    v4f acc[8][4];
+#pragma unroll
+    for (int mf = 0; mf < 8; ++mf)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[mf][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    uint4 R[2][4];
+    v8i bq[PFB][4];
+    auto loadA = [&](int kb, uint4 (&r)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = bload16(ra, aoff[i], kb * kGroup, 0);
+    };
+    auto storeA = [&](const uint4 (&r)[4], uint8_t* ab) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(ab + (tid + 256 * i) * 16) = r[i];
+    };
+    auto loadB = [&](int kb, v8i (&b)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j] = buf_frag(rw, l16, (uint32_t)(bn16[j] * KB + kb) * kFragBytes);
+    };
+    loadA(0, R[0]);
+    if (KB > 1) loadA(1, R[1]);
+#pragma unroll
+    for (int p = 0; p < PFB; ++p)
+        if (p < KB) loadB(p, bq[p]);
+    storeA(R[0], abuf[0]);
+    __syncthreads();
+
+    auto step = [&](int kb, const int p, const int ab) {
+        if (kb + 2 < KB) loadA(kb + 2, R[ab]);
+        const int sg = s_sg[kb], su = s_su[kb];
+        const int sbv[4] = {sg, sg, su, su};
+        PfnCore<true, PFB>::mma(acc, abuf[ab], bq[p], s_sa, KB, kb, lane, sbv);
+        if (kb + PFB < KB) loadB(kb + PFB, bq[p]);
+        if (kb + 1 < KB) storeA(R[ab ^ 1], abuf[ab ^ 1]);
+        __syncthreads();
+    };
+    static_assert(PFB == 2 || PFB == 4, "the K loop is unrolled by 4");
+    for (int kb = 0; kb < KB; kb += 4) {
+        step(kb, 0, 0);
+        if (kb + 1 < KB) step(kb + 1, 1 % PFB, 1);
+        if (kb + 2 < KB) step(kb + 2, 2 % PFB, 0);
+        if (kb + 3 < KB) step(kb + 3, 3 % PFB, 1);
+    }
+
+    // ---- epilogue: SwiGLU on this wave's 32 columns, row amax over the four waves, requant
+    float hv[8][2][4];
+#pragma unroll
+    for (int mf = 0; mf < 8; ++mf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float m = 0.f;
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const float g = acc[mf][jj][i];
+                const float h = g / (1.0f + expf(-g)) * acc[mf][2 + jj][i];
+                hv[mf][jj][i] = h;
+                m = fmaxf(m, fabsf(h));
+            }
+            m = max16(m);
+            if ((lane & 15) == 0) s_amax[wv][mf * 16 + 4 * (lane >> 4) + i] = m;
+        }
+    }
+    __syncthreads();
+    uint8_t* s_h = abuf[0];   // [128][128] bytes
+#pragma unroll
+    for (int mf = 0; mf < 8; ++mf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = mf * 16 + 4 * (lane >> 4) + i;
+            const float am = fmaxf(fmaxf(s_amax[0][row], s_amax[1][row]), fmaxf(s_amax[2][row], s_amax[3][row]));
+            const int ex = scale_exponent(am);
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+                s_h[row * 128 + (2 * wv + jj) * 16 + (lane & 15)] =
+                    (uint8_t)(cvt2_e4m3(ldexpf(hv[mf][jj][i], -ex), 0.f) & 0xFFu);
+            if (wv == 0 && (lane & 15) == 0)
+                a.hs[((int64_t)tile * kPfBM + row) * (a.I / kGroup) + ib] = (uint8_t)(ex + 127);
+        }
+    }
+    __syncthreads();
+    const int KB2 = a.I / kGroup;
+    for (int q = tid; q < 8 * 128; q += 256) {
+        const int mf = q >> 7, w = q & 127, hh = w >> 6, ln = w & 63;
+        const uint4 v = *reinterpret_cast<const uint4*>(s_h + (mf * 16 + (ln & 15)) * 128 + (ln >> 4) * 32 + hh * 16);
+        *reinterpret_cast<uint4*>(a.hq + (((int64_t)tile * 8 + mf) * KB2 + ib) * kFragBytes + hh * 1024 + ln * 16) = v;
+    }
+}
+
+template <int PFB>
+__global__ __launch_bounds__(256, 1) void k_gemm2_pfn(G2Args a) {
+    const int nb = blockIdx.x;
+    const int tile = blockIdx.y;
+    if (tile >= *a.ntiles) return;
+    const int2 te = a.tiles[tile];
+    const int e = te.x, m0 = te.y;
+    const int nvalid = min(kPfBM, a.counts[e] - m0);
+    const int rowbase = a.offsets[e] + m0;
+    const int KB = a.I / kGroup;
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    __shared__ __align__(16) uint8_t abuf[2][8 * kFragBytes];
+    __shared__ uint8_t s_sa[kPfBM * kPfMaxKB];
+    __shared__ uint8_t s_sb[2][kPfMaxKB];   // the workgroup's two 128-column scale blocks
+    {
+        const uint8_t* src = a.hs + (int64_t)tile * kPfBM * KB;
+        for (int i = tid; i < kPfBM * KB; i += 256) s_sa[i] = src[i];
+    }
+    const int NB16 = a.H / 16, NBS = a.H / kGroup;
+    const uint8_t* sb = a.w2s + (int64_t)e * KB * NBS;
+    for (int i = tid; i < 2 * KB; i += 256) s_sb[i & 1][i >> 1] = sb[(i >> 1) * NBS + nb * 2 + (i & 1)];
+    const rsrc_t ra = make_rsrc(a.hq + (int64_t)tile * 8 * KB * kFragBytes, (uint32_t)8 * KB * kFragBytes);
+    const rsrc_t rw = make_rsrc(a.w2p + (int64_t)e * NB16 * KB * kFragBytes, (uint32_t)NB16 * KB * kFragBytes);
+    const int n16 = nb * 16 + 4 * wv;
+    const int sblk = wv >> 1;   // this wave's 64 columns lie in scale block nb*2 + wv/2
+    const uint32_t l16 = lane * 16;
+
+    v4f acc[8][4];
+#pragma unroll
+    for (int mf = 0; mf < 8; ++mf)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[mf][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    uint4 R[2][4];
+    v8i bq[PFB][4];
+    auto loadA = [&](int kb, uint4 (&r)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int p = tid + 256 * i;
+            r[i] = bload16(ra, (p & 127) * 16, (uint32_t)((p >> 7) * KB + kb) * kFragBytes, 0);
+        }
+    };
+    auto storeA = [&](const uint4 (&r)[4], uint8_t* ab) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(ab + (tid + 256 * i) * 16) = r[i];
+    };
+    auto loadB = [&](int kb, v8i (&b)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j] = buf_frag(rw, l16, (uint32_t)((n16 + j) * KB + kb) * kFragBytes);
+    };
+    loadA(0, R[0]);
+    if (KB > 1) loadA(1, R[1]);
+#pragma unroll
+    for (int p = 0; p < PFB; ++p)
+        if (p < KB) loadB(p, bq[p]);
+    storeA(R[0], abuf[0]);
+    __syncthreads();
+
+    auto step = [&](int kb, const int p, const int ab) {
+        if (kb + 2 < KB) loadA(kb + 2, R[ab]);
+        const int s = s_sb[sblk][kb];
+        const int sbv[4] = {s, s, s, s};
+        PfnCore<false, PFB>::mma(acc, abuf[ab], bq[p], s_sa, KB, kb, lane, sbv);
+        if (kb + PFB < KB) loadB(kb + PFB, bq[p]);
+        if (kb + 1 < KB) storeA(R[ab ^ 1], abuf[ab ^ 1]);
+        __syncthreads();
+    };
+    static_assert(PFB == 2 || PFB == 4, "the K loop is unrolled by 4");
+    for (int kb = 0; kb < KB; kb += 4) {
+        step(kb, 0, 0);
+        if (kb + 1 < KB) step(kb + 1, 1 % PFB, 1);
+        if (kb + 2 < KB) step(kb + 2, 2 % PFB, 0);
+        if (kb + 3 < KB) step(kb + 3, 3 % PFB, 1);
+    }
+
+#pragma unroll
+    for (int mf = 0; mf < 8; ++mf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = mf * 16 + 4 * (lane >> 4) + i;
+            if (row < nvalid) {
+                const int64_t o = (int64_t)(rowbase + row) * a.H;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int col = (n16 + j) * 16 + (lane & 15);
+                    if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o + col] = f32_to_bf16(acc[mf][j][i]);
+                    else reinterpret_cast<float*>(a.out)[o + col] = acc[mf][j][i];
+                }
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------------------
+// Decode tiles (16 rows) while experts average at most this many rows; 128-row tiles above.
+#ifndef MOE_DEC_MAX_AVG_ROWS
+#define MOE_DEC_MAX_AVG_ROWS 24
+#endif
+
 FfnPlan ffn_plan(int T, int k, int E) {
     const int64_t A = (int64_t)T * k;
     const int64_t avg = A / E;
     FfnPlan p;
-    p.BM = avg <= 24 ? 16 : (avg <= 96 ? 64 : 128);
+    p.BM = avg <= MOE_DEC_MAX_AVG_ROWS ? 16 : 128;
     p.ntiles_max = (int)(ceil_div(A, p.BM) + std::min<int64_t>(E, A));
     return p;
 }
@@ -1227,13 +1500,13 @@ static hipError_t run_ffn_dec(const FfnArgs& f, const FfnPlan& p, const FfnWs& w
 static hipError_t run_ffn_pf(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid) {
     G1Args g1{f.xq, f.xs, f.T, f.k, f.H, f.I, f.counts, f.offsets, f.sorted_assign, w.tiles, w.ntiles, f.w13p, f.w13s,
               w.hq, w.hs};
-    hipLaunchKernelGGL(MOE_PF_GEMM1, dim3(f.I / kGroup, p.ntiles_max), dim3(256), 0, st, g1);
+    hipLaunchKernelGGL((MOE_PF_GEMM1), dim3(f.I / kGroup, p.ntiles_max), dim3(256), 0, st, g1);
     if (mid) {
         const hipError_t e = hipEventRecord(mid, st);
         if (e != hipSuccess) return e;
     }
     G2Args g2{w.hq, w.hs, f.H, f.I, f.counts, f.offsets, w.tiles, w.ntiles, f.w2p, f.w2s, f.out, f.out_bf16};
-    hipLaunchKernelGGL(MOE_PF_GEMM2, dim3(f.H / 256, p.ntiles_max), dim3(256), 0, st, g2);
+    hipLaunchKernelGGL((MOE_PF_GEMM2), dim3(f.H / 256, p.ntiles_max), dim3(256), 0, st, g2);
     return hipGetLastError();
 }
 
@@ -1261,7 +1534,8 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, void* ws, hipStream_t st, hipEve
     }
     // output columns per workgroup of the down GEMM = 128, a divisor of H
     if (p.BM == 16) return run_ffn_dec<MOE_DEC_GEMM1, MOE_DEC_GEMM2>(f, p, w, st, mid);
-    if (p.BM == 64) return run_ffn<2, 4, 4, 2, 2, 2, 2>(f, p, w, st, mid);
+    // 128-row tiles: the staged kernels need the tile's A scales in LDS and 256-column
+    // down-GEMM blocks; other shapes take the plain 128-row kernels
     if (f.H / kGroup <= kPfMaxKB && f.I / kGroup <= kPfMaxKB && f.H % 256 == 0)
         return run_ffn_pf(f, p, w, st, mid);
     return run_ffn<4, 4, 4, 2, 2, 2, 2>(f, p, w, st, mid);

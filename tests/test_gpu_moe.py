@@ -25,7 +25,9 @@ SMALL = {
     "T1_E1_k1": W.Workload(120, "one", T=1, H=128, I=128, E=1, k=1),
     "ragged": W.Workload(121, "ragged", T=37, H=256, I=384, E=5, k=3),
     "k_equals_E": W.Workload(122, "kE", T=19, H=128, I=256, E=4, k=4, renormalize=False),
-    "bm64_path": W.Workload(123, "bm64", T=640, H=256, I=256, E=64, k=6, bias="normal1.5"),
+    "staged_tiles_skewed": W.Workload(123, "bm128s", T=640, H=256, I=256, E=16, k=6, bias="normal1.5"),
+    "plain_tiles_H384": W.Workload(128, "bm128p", T=600, H=384, I=256, E=8, k=3),
+    "staged_tiles_K_not_multiple_of_3": W.Workload(129, "bm128k", T=700, H=512, I=640, E=8, k=2),
     "bm128_path": W.Workload(124, "bm128", T=1100, H=256, I=384, E=8, k=2),
     "sigmoid_groups": W.Workload(125, "grp", T=96, H=384, I=256, E=32, k=4, scoring="sigmoid", group_count=4,
                                  k_group=2, group_select_mode=1, routed_scaling_factor=2.5),
