@@ -28,14 +28,17 @@
 #ifndef MOE_DEC_GEMM2
 #define MOE_DEC_GEMM2 2, 4, 2
 #endif
-// Prefill kernels: k_gemm{1,2}_pfn<PFB> (waves split the columns; A staged in LDS, B
-// streamed into registers), k_gemm{1,2}_pfr (2x2 waves, both operands register-staged
-// through LDS) or k_gemm{1,2}_pf (2x2 waves, LDS-DMA staging)
+// Prefill kernels (128 x 256 tiles): k_gemm{1,2}_pf8 (2x4 waves of 64x64, two waves per
+// SIMD; 512 threads), k_gemm{1,2}_pfr (2x2 waves of 64x128; 256 threads), k_gemm{1,2}_pfn
+// (waves split the columns) or k_gemm{1,2}_pf (LDS-DMA staging; 256 threads)
 #ifndef MOE_PF_GEMM1
-#define MOE_PF_GEMM1 k_gemm1_pfr<2>
+#define MOE_PF_GEMM1 k_gemm1_pf8<2>
 #endif
 #ifndef MOE_PF_GEMM2
-#define MOE_PF_GEMM2 k_gemm2_pfr<2>
+#define MOE_PF_GEMM2 k_gemm2_pf8<2>
+#endif
+#ifndef MOE_PF_THREADS
+#define MOE_PF_THREADS 512
 #endif
 
 namespace moe {
@@ -1443,6 +1446,281 @@ __global__ __launch_bounds__(256, 1) void k_gemm2_pfn(G2Args a) {
 }
 
 // ----------------------------------------------------------------------------------------
+// 8-wave prefill variants: the 128 x 256 tile split over 2 (rows) x 4 (columns) waves of
+// 64 x 64 (4 x 4 fragments), two waves per SIMD so one wave's LDS and load waits overlap the
+// other's matrix-core work.  Operands are register-staged through two LDS buffers as in the
+// 4-wave variant; each of the 512 threads moves 6 16-byte pieces per K block (2 of A, 4 of B).
+// Piece p of a stage sits at byte 16 p: fragment p / 128, half (p / 64) % 2, lane p % 64.
+
+struct Pf8Loads {
+    uint4 v[6];
+};
+
+template <int NR>
+__global__ __launch_bounds__(512, 1) void k_gemm1_pf8(G1Args a) {
+    const int ib = blockIdx.x;
+    const int tile = blockIdx.y;
+    if (tile >= *a.ntiles) return;
+    const int2 te = a.tiles[tile];
+    const int e = te.x, m0 = te.y;
+    const int nvalid = min(kPfBM, a.counts[e] - m0);
+    const int rowbase = a.offsets[e] + m0;
+    const int KB = a.H / kGroup;
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wv >> 2, wn = wv & 3;
+
+    __shared__ __align__(16) uint8_t buf[2][kPfStage];
+    __shared__ uint8_t s_sa[kPfBM * kPfMaxKB];
+    __shared__ uint8_t s_sg[kPfMaxKB], s_su[kPfMaxKB];
+    __shared__ float s_amax[4][kPfBM];
+
+    if (tid < 2 * kPfBM) {
+        const int r = tid >> 1, half = tid & 1;
+        const int tok = a.sorted_assign[rowbase + min(r, nvalid - 1)] / a.k;
+        const uint8_t* src = a.xs + (int64_t)tok * KB;
+        for (int kb = half; kb < KB; kb += 2) s_sa[r * KB + kb] = src[kb];
+    }
+    const int NB16 = 2 * a.I / 16, NBS = 2 * a.I / kGroup;
+    const uint8_t* sb = a.w13s + (int64_t)e * KB * NBS;
+    for (int i = tid; i < KB; i += 512) {
+        s_sg[i] = sb[i * NBS + ib];
+        s_su[i] = sb[i * NBS + a.I / kGroup + ib];
+    }
+    const rsrc_t ra = make_rsrc(a.xq, (uint32_t)a.T * a.H);
+    const rsrc_t rw = make_rsrc(a.w13p + (int64_t)e * NB16 * KB * kFragBytes, (uint32_t)NB16 * KB * kFragBytes);
+    uint32_t aoff[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int p = tid + 512 * i, mf = p >> 7, hh = (p >> 6) & 1, ln = p & 63;
+        const int r = mf * 16 + (ln & 15);
+        const int tok = a.sorted_assign[rowbase + min(r, nvalid - 1)] / a.k;
+        aoff[i] = (uint32_t)tok * a.H + (ln >> 4) * 32 + hh * 16;
+    }
+    int bsoff[4];   // wave-uniform byte offset of the piece's fragment row and half
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int q = wv * 64 + 512 * i, f = q >> 7, hh = (q >> 6) & 1;
+        const int n16 = f < 8 ? ib * 8 + f : a.I / 16 + ib * 8 + (f - 8);
+        bsoff[i] = __builtin_amdgcn_readfirstlane(n16 * KB * kFragBytes + hh * 1024);
+    }
+    const uint32_t l16 = lane * 16;
+    auto load = [&](int kb, Pf8Loads& L) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) L.v[i] = bload16(ra, aoff[i], kb * kGroup, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) L.v[2 + i] = bload16(rw, l16, (uint32_t)(bsoff[i] + kb * kFragBytes), 0);
+    };
+    auto store = [&](const Pf8Loads& L, uint8_t* st) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(st + (tid + 512 * i) * 16) = L.v[i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(st + kPfStageA + (tid + 512 * i) * 16) = L.v[2 + i];
+    };
+
+    v4f acc[4][4];   // [row fragment][gate 0, 1 | up 2, 3]
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    Pf8Loads R[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) load(min(r, KB - 1), R[r]);
+    store(R[0], buf[0]);
+    __syncthreads();
+
+    auto compute = [&](int kb, const uint8_t* cur) {
+        v8i af[4];
+        int sa[4];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            const int mf = wm * 4 + mi;
+            af[mi] = lds_frag(cur + mf * kFragBytes, lane);
+            sa[mi] = s_sa[(mf * 16 + (lane & 15)) * KB + kb];
+        }
+        const int sg = s_sg[kb], su = s_su[kb];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int f = j < 2 ? 2 * wn + j : 8 + 2 * wn + (j - 2);
+            const v8i b = lds_frag(cur + kPfStageA + f * kFragBytes, lane);
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) acc[mi][j] = mfma_fp8(af[mi], b, acc[mi][j], sa[mi], j < 2 ? sg : su);
+        }
+    };
+    // Same step order as the 4-wave kernel: load block kb+NR, compute block kb, store block kb+1.
+    auto step = [&](int kb, const int ri, const int bi) {
+        load(min(kb + NR, KB - 1), R[ri]);
+        compute(kb, buf[bi]);
+        store(R[(ri + 1) % NR], buf[bi ^ 1]);
+        __syncthreads();
+    };
+    constexpr int U = NR == 3 ? 6 : (NR == 4 ? 4 : 2);
+    int kb = 0;
+    for (; kb + U <= KB; kb += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) step(kb + u, u % NR, u & 1);
+    }
+#pragma unroll
+    for (int u = 0; u < U - 1; ++u)
+        if (kb + u < KB) step(kb + u, u % NR, u & 1);
+
+    float hv[4][2][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float m = 0.f;
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const float g = acc[mi][jj][i];
+                const float h = g / (1.0f + expf(-g)) * acc[mi][2 + jj][i];
+                hv[mi][jj][i] = h;
+                m = fmaxf(m, fabsf(h));
+            }
+            m = max16(m);
+            if ((lane & 15) == 0) s_amax[wn][(wm * 4 + mi) * 16 + 4 * (lane >> 4) + i] = m;
+        }
+    }
+    __syncthreads();
+    uint8_t* s_h = buf[0];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = (wm * 4 + mi) * 16 + 4 * (lane >> 4) + i;
+            const float am = fmaxf(fmaxf(s_amax[0][row], s_amax[1][row]), fmaxf(s_amax[2][row], s_amax[3][row]));
+            const int ex = scale_exponent(am);
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+                s_h[row * 128 + (2 * wn + jj) * 16 + (lane & 15)] =
+                    (uint8_t)(cvt2_e4m3(ldexpf(hv[mi][jj][i], -ex), 0.f) & 0xFFu);
+            if (wn == 0 && (lane & 15) == 0)
+                a.hs[((int64_t)tile * kPfBM + row) * (a.I / kGroup) + ib] = (uint8_t)(ex + 127);
+        }
+    }
+    __syncthreads();
+    const int KB2 = a.I / kGroup;
+    for (int q = tid; q < 8 * 128; q += 512) {
+        const int mf = q >> 7, w = q & 127, hh = w >> 6, ln = w & 63;
+        const uint4 v = *reinterpret_cast<const uint4*>(s_h + (mf * 16 + (ln & 15)) * 128 + (ln >> 4) * 32 + hh * 16);
+        *reinterpret_cast<uint4*>(a.hq + (((int64_t)tile * 8 + mf) * KB2 + ib) * kFragBytes + hh * 1024 + ln * 16) = v;
+    }
+}
+
+template <int NR>
+__global__ __launch_bounds__(512, 1) void k_gemm2_pf8(G2Args a) {
+    const int nb = blockIdx.x;
+    const int tile = blockIdx.y;
+    if (tile >= *a.ntiles) return;
+    const int2 te = a.tiles[tile];
+    const int e = te.x, m0 = te.y;
+    const int nvalid = min(kPfBM, a.counts[e] - m0);
+    const int rowbase = a.offsets[e] + m0;
+    const int KB = a.I / kGroup;
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wv >> 2, wn = wv & 3;
+
+    __shared__ __align__(16) uint8_t buf[2][kPfStage];
+    __shared__ uint8_t s_sa[kPfBM * kPfMaxKB];
+    __shared__ uint8_t s_sb[2][kPfMaxKB];
+    {
+        const uint8_t* src = a.hs + (int64_t)tile * kPfBM * KB;
+        for (int i = tid; i < kPfBM * KB; i += 512) s_sa[i] = src[i];
+    }
+    const int NB16 = a.H / 16, NBS = a.H / kGroup;
+    const uint8_t* sb = a.w2s + (int64_t)e * KB * NBS;
+    for (int i = tid; i < 2 * KB; i += 512) s_sb[i & 1][i >> 1] = sb[(i >> 1) * NBS + nb * 2 + (i & 1)];
+    const rsrc_t ra = make_rsrc(a.hq + (int64_t)tile * 8 * KB * kFragBytes, (uint32_t)8 * KB * kFragBytes);
+    const rsrc_t rw = make_rsrc(a.w2p + (int64_t)e * NB16 * KB * kFragBytes, (uint32_t)NB16 * KB * kFragBytes);
+    const uint32_t l16 = lane * 16;
+    int asoff[2], bsoff[4];   // wave-uniform byte offsets of the pieces' fragment rows and halves
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int p = wv * 64 + 512 * i, mf = p >> 7, hh = (p >> 6) & 1;
+        asoff[i] = __builtin_amdgcn_readfirstlane(mf * KB * kFragBytes + hh * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int q = wv * 64 + 512 * i, f = q >> 7, hh = (q >> 6) & 1;
+        bsoff[i] = __builtin_amdgcn_readfirstlane((nb * 16 + f) * KB * kFragBytes + hh * 1024);
+    }
+    auto load = [&](int kb, Pf8Loads& L) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) L.v[i] = bload16(ra, l16, (uint32_t)(asoff[i] + kb * kFragBytes), 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) L.v[2 + i] = bload16(rw, l16, (uint32_t)(bsoff[i] + kb * kFragBytes), 0);
+    };
+    auto store = [&](const Pf8Loads& L, uint8_t* st) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(st + (tid + 512 * i) * 16) = L.v[i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(st + kPfStageA + (tid + 512 * i) * 16) = L.v[2 + i];
+    };
+
+    v4f acc[4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    Pf8Loads R[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) load(min(r, KB - 1), R[r]);
+    store(R[0], buf[0]);
+    __syncthreads();
+
+    auto compute = [&](int kb, const uint8_t* cur) {
+        v8i af[4];
+        int sa[4];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            const int mf = wm * 4 + mi;
+            af[mi] = lds_frag(cur + mf * kFragBytes, lane);
+            sa[mi] = s_sa[(mf * 16 + (lane & 15)) * KB + kb];
+        }
+        const int sbv = s_sb[wn >> 1][kb];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const v8i b = lds_frag(cur + kPfStageA + (wn * 4 + j) * kFragBytes, lane);
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) acc[mi][j] = mfma_fp8(af[mi], b, acc[mi][j], sa[mi], sbv);
+        }
+    };
+    auto step = [&](int kb, const int ri, const int bi) {
+        load(min(kb + NR, KB - 1), R[ri]);
+        compute(kb, buf[bi]);
+        store(R[(ri + 1) % NR], buf[bi ^ 1]);
+        __syncthreads();
+    };
+    constexpr int U = NR == 3 ? 6 : (NR == 4 ? 4 : 2);
+    int kb = 0;
+    for (; kb + U <= KB; kb += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) step(kb + u, u % NR, u & 1);
+    }
+#pragma unroll
+    for (int u = 0; u < U - 1; ++u)
+        if (kb + u < KB) step(kb + u, u % NR, u & 1);
+
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = (wm * 4 + mi) * 16 + 4 * (lane >> 4) + i;
+            if (row < nvalid) {
+                const int64_t o = (int64_t)(rowbase + row) * a.H;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int col = nb * 256 + (wn * 4 + j) * 16 + (lane & 15);
+                    if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o + col] = f32_to_bf16(acc[mi][j][i]);
+                    else reinterpret_cast<float*>(a.out)[o + col] = acc[mi][j][i];
+                }
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------------------
 // Decode tiles (16 rows) while experts average at most this many rows; 128-row tiles above.
 #ifndef MOE_DEC_MAX_AVG_ROWS
 #define MOE_DEC_MAX_AVG_ROWS 24
@@ -1500,13 +1778,13 @@ static hipError_t run_ffn_dec(const FfnArgs& f, const FfnPlan& p, const FfnWs& w
 static hipError_t run_ffn_pf(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid) {
     G1Args g1{f.xq, f.xs, f.T, f.k, f.H, f.I, f.counts, f.offsets, f.sorted_assign, w.tiles, w.ntiles, f.w13p, f.w13s,
               w.hq, w.hs};
-    hipLaunchKernelGGL((MOE_PF_GEMM1), dim3(f.I / kGroup, p.ntiles_max), dim3(256), 0, st, g1);
+    hipLaunchKernelGGL((MOE_PF_GEMM1), dim3(f.I / kGroup, p.ntiles_max), dim3(MOE_PF_THREADS), 0, st, g1);
     if (mid) {
         const hipError_t e = hipEventRecord(mid, st);
         if (e != hipSuccess) return e;
     }
     G2Args g2{w.hq, w.hs, f.H, f.I, f.counts, f.offsets, w.tiles, w.ntiles, f.w2p, f.w2s, f.out, f.out_bf16};
-    hipLaunchKernelGGL((MOE_PF_GEMM2), dim3(f.H / 256, p.ntiles_max), dim3(256), 0, st, g2);
+    hipLaunchKernelGGL((MOE_PF_GEMM2), dim3(f.H / 256, p.ntiles_max), dim3(MOE_PF_THREADS), 0, st, g2);
     return hipGetLastError();
 }
 
