@@ -28,18 +28,6 @@
 #ifndef MOE_DEC_GEMM2
 #define MOE_DEC_GEMM2 2, 4, 2
 #endif
-// Prefill kernels (128 x 256 tiles): k_gemm{1,2}_pf8 (2x4 waves of 64x64, two waves per
-// SIMD; 512 threads), k_gemm{1,2}_pfr (2x2 waves of 64x128; 256 threads), k_gemm{1,2}_pfn
-// (waves split the columns) or k_gemm{1,2}_pf (LDS-DMA staging; 256 threads)
-#ifndef MOE_PF_GEMM1
-#define MOE_PF_GEMM1 k_gemm1_pf8<2>
-#endif
-#ifndef MOE_PF_GEMM2
-#define MOE_PF_GEMM2 k_gemm2_pf8<2>
-#endif
-#ifndef MOE_PF_THREADS
-#define MOE_PF_THREADS 512
-#endif
 
 namespace moe {
 
@@ -614,880 +602,104 @@ __global__ __launch_bounds__(64 * WN) void k_gemm2_dec(G2Args a) {
 }
 
 // ----------------------------------------------------------------------------------------
-// Prefill variants: workgroup tile 128 rows x 256 columns, 4 waves as 2 (rows) x 2
-// (columns), wave tile 64 x 128 (4 x 8 matrix-core fragments).  A and B fragments travel
-// global -> LDS by the LDS-DMA form of the buffer load (no staging registers) through a
-// 3-stage ring; each stage is its own LDS array so the compiler tracks the DMA writes per
-// stage.  Per K block: wait until this wave's DMA for the block has landed, barrier, issue
-// the DMA two blocks ahead, then read fragments from LDS and run 32 MFMAs per wave.  The A
-// row scales of all K blocks are loaded into LDS once per tile.
+// Prefill kernels: workgroup tile 128 rows x 256 columns, 8 waves as 2 (rows) x 4 (columns)
+// of 64 x 64 (4 x 4 matrix-core fragments), two waves per SIMD so one wave's LDS waits
+// overlap the other's matrix-core work.  Operands travel global -> LDS by the LDS-DMA form
+// of the buffer load (no staging registers, no LDS store instructions) through a 3-stage
+// ring of 48 KB stages, so two K blocks (96 KB per CU) are in flight while the waves compute
+// the third.  Each of the 512 threads moves 6 16-byte pieces per K block (2 of A, 4 of B);
+// piece p of a stage sits at byte 16 p: fragment p / 128, half (p / 64) % 2, lane p % 64.
+// The A row scales of all K blocks and the weight block scales of the workgroup's columns
+// sit in LDS.
 
 constexpr int kPfBM = 128, kPfStageA = 8 * kFragBytes, kPfStage = kPfStageA + 16 * kFragBytes;  // 48 KB
 constexpr int kPfMaxKB = 64;     // K blocks whose A scales fit the LDS table
 
-#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
-// vmcnt <= n (n < 16), other counters untouched
-#define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8))
+// Work order of the prefill grids (one dimension, ncol * tiles workgroups rounded up to a
+// multiple of kXcds).  Workgroup L runs on XCD L % kXcds (the dispatcher deals workgroups to
+// the XCDs in turn), so XCD x takes the contiguous share x of the work list; the list walks
+// super-blocks of kPfGroupTiles consecutive tiles (mostly one expert), and inside a
+// super-block the column block is the outer index.  The workgroups that run together on one
+// XCD then share both their A tiles and their weight column blocks through that XCD's L2.
+constexpr int kXcds = 8;
+#ifndef MOE_PF_GROUP_TILES
+#define MOE_PF_GROUP_TILES 4
+#endif
+constexpr int kPfGroupTiles = MOE_PF_GROUP_TILES;
 
-__device__ __forceinline__ void dma16(rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(lds), 16, voff, soff, 0, 0);
-}
-
-// gate+up prefill GEMM; grid (I/128 column blocks, tiles)
-__global__ __launch_bounds__(256, 1) void k_gemm1_pf(G1Args a) {
-    const int ib = blockIdx.x;
-    const int tile = blockIdx.y;
-    if (tile >= *a.ntiles) return;
-    const int2 te = a.tiles[tile];
-    const int e = te.x, m0 = te.y;
-    const int nvalid = min(kPfBM, a.counts[e] - m0);
-    const int rowbase = a.offsets[e] + m0;
-    const int KB = a.H / kGroup;
-    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wv >> 1, wn = wv & 1;
-
-    __shared__ __align__(16) uint8_t st0[kPfStage], st1[kPfStage], st2[kPfStage];
-    __shared__ uint8_t s_sa[kPfBM * kPfMaxKB];
-    __shared__ uint8_t s_sg[kPfMaxKB], s_su[kPfMaxKB];
-    __shared__ float s_amax[2][kPfBM];
-
-    // A scales of every K block: thread pair (row, half) copies half of the row's KB bytes
-    {
-        const int r = tid >> 1, half = tid & 1;
-        const int tok = a.sorted_assign[rowbase + min(r, nvalid - 1)] / a.k;
-        const uint8_t* src = a.xs + (int64_t)tok * KB;
-        for (int kb = half; kb < KB; kb += 2) s_sa[r * KB + kb] = src[kb];
-    }
-    // this wave's DMA sources: A fragments 2wv, 2wv+1 (rows gathered), B fragments 4wv..4wv+3
-    const rsrc_t ra = make_rsrc(a.xq, (uint32_t)a.T * a.H);
-    uint32_t aoff[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int r = (2 * wv + q) * 16 + (lane & 15);
-        const int tok = a.sorted_assign[rowbase + min(r, nvalid - 1)] / a.k;
-        aoff[q] = (uint32_t)tok * a.H + (lane >> 4) * 32;
-    }
-    const int NB16 = 2 * a.I / 16, NBS = 2 * a.I / kGroup;
-    const rsrc_t rw = make_rsrc(a.w13p + (int64_t)e * NB16 * KB * kFragBytes, (uint32_t)NB16 * KB * kFragBytes);
-    const uint8_t* sb = a.w13s + (int64_t)e * KB * NBS;
-    for (int i = tid; i < KB; i += 256) {
-        s_sg[i] = sb[i * NBS + ib];
-        s_su[i] = sb[i * NBS + a.I / kGroup + ib];
-    }
-    int bn16[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int f = 4 * wv + j;
-        bn16[j] = f < 8 ? ib * 8 + f : a.I / 16 + ib * 8 + (f - 8);
-    }
-    const uint32_t l16 = lane * 16;
-    auto issue = [&](int kb, uint8_t* st) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) dma16(ra, st + (2 * wv + q) * kFragBytes + h * 1024, aoff[q] + h * 16, kb * kGroup);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                dma16(rw, st + kPfStageA + (4 * wv + j) * kFragBytes + h * 1024, l16,
-                      (uint32_t)(bn16[j] * KB + kb) * kFragBytes + h * 1024);
-    };
-
-    v4f accg[4][4], accu[4][4];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) accg[mi][j] = accu[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    __builtin_amdgcn_s_waitcnt(0);   // scale copies done before the DMA count starts
-    issue(0, st0);
-    issue(min(1, KB - 1), st1);
-
-    // Every step issues the DMA of block kb + 2 (clamped to the last block: the duplicate
-    // lands in a stage nobody reads again), so exactly 12 DMA loads per wave follow the
-    // ones of block kb and vmcnt(12) means "block kb has landed".
-    auto step = [&](int kb, const uint8_t* cur, uint8_t* nxt) {
-        WAIT_VMCNT(12);
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS reads and writes done
-        __builtin_amdgcn_s_barrier();
-        issue(min(kb + 2, KB - 1), nxt);
-        v8i af[4];
-        int sa[4];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            const int mf = wm * 4 + mi;
-            af[mi] = lds_frag(cur + mf * kFragBytes, lane);
-            sa[mi] = s_sa[(mf * 16 + (lane & 15)) * KB + kb];
-        }
-        const int sg = s_sg[kb];
-        const int su = s_su[kb];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const v8i bg = lds_frag(cur + kPfStageA + (wn * 4 + j) * kFragBytes, lane);
-            const v8i bu = lds_frag(cur + kPfStageA + (8 + wn * 4 + j) * kFragBytes, lane);
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
-                accg[mi][j] = mfma_fp8(af[mi], bg, accg[mi][j], sa[mi], sg);
-                accu[mi][j] = mfma_fp8(af[mi], bu, accu[mi][j], sa[mi], su);
-            }
-        }
-    };
-    int kb0 = 0;
-    for (; kb0 + 3 <= KB; kb0 += 3) {
-        step(kb0, st0, st2);
-        step(kb0 + 1, st1, st0);
-        step(kb0 + 2, st2, st1);
-    }
-    if (kb0 < KB) step(kb0, st0, st2);
-    if (kb0 + 1 < KB) step(kb0 + 1, st1, st0);
-    __builtin_amdgcn_s_waitcnt(0);   // the trailing duplicate DMA must land before LDS is reused
-
-    // ---- epilogue: SwiGLU, row amax over the 128 columns (two waves), requant
-    float hv[4][4][4];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float m = 0.f;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float g = accg[mi][j][i];
-                const float h = g / (1.0f + expf(-g)) * accu[mi][j][i];
-                hv[mi][j][i] = h;
-                m = fmaxf(m, fabsf(h));
-            }
-            m = max16(m);
-            if ((lane & 15) == 0) s_amax[wn][(wm * 4 + mi) * 16 + 4 * (lane >> 4) + i] = m;
-        }
-    }
-    __syncthreads();
-    uint8_t* s_h = st0;   // [128][128] bytes
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = (wm * 4 + mi) * 16 + 4 * (lane >> 4) + i;
-            const int ex = scale_exponent(fmaxf(s_amax[0][row], s_amax[1][row]));
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                s_h[row * 128 + (wn * 4 + j) * 16 + (lane & 15)] =
-                    (uint8_t)(cvt2_e4m3(ldexpf(hv[mi][j][i], -ex), 0.f) & 0xFFu);
-            if (wn == 0 && (lane & 15) == 0)
-                a.hs[((int64_t)tile * kPfBM + row) * (a.I / kGroup) + ib] = (uint8_t)(ex + 127);
-        }
-    }
-    __syncthreads();
-    const int KB2 = a.I / kGroup;
-    for (int q = tid; q < 8 * 128; q += 256) {
-        const int mf = q >> 7, w = q & 127, hh = w >> 6, ln = w & 63;
-        const uint4 v = *reinterpret_cast<const uint4*>(s_h + (mf * 16 + (ln & 15)) * 128 + (ln >> 4) * 32 + hh * 16);
-        *reinterpret_cast<uint4*>(a.hq + (((int64_t)tile * 8 + mf) * KB2 + ib) * kFragBytes + hh * 1024 + ln * 16) = v;
-    }
-}
-
-// down prefill GEMM; grid (H/256 column blocks, tiles)
-__global__ __launch_bounds__(256, 1) void k_gemm2_pf(G2Args a) {
-    const int nb = blockIdx.x;
-    const int tile = blockIdx.y;
-    if (tile >= *a.ntiles) return;
-    const int2 te = a.tiles[tile];
-    const int e = te.x, m0 = te.y;
-    const int nvalid = min(kPfBM, a.counts[e] - m0);
-    const int rowbase = a.offsets[e] + m0;
-    const int KB = a.I / kGroup;
-    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wv >> 1, wn = wv & 1;
-
-    __shared__ __align__(16) uint8_t st0[kPfStage], st1[kPfStage], st2[kPfStage];
-    __shared__ uint8_t s_sa[kPfBM * kPfMaxKB];
-    __shared__ uint8_t s_sb[2][kPfMaxKB];   // the two 128-column scale blocks of this workgroup
-
-    {
-        const uint8_t* src = a.hs + (int64_t)tile * kPfBM * KB;   // [row][kb], contiguous for the tile
-        for (int i = tid; i < kPfBM * KB; i += 256) s_sa[i] = src[i];
-    }
-    const rsrc_t ra = make_rsrc(a.hq + (int64_t)tile * 8 * KB * kFragBytes, (uint32_t)8 * KB * kFragBytes);
-    const int NB16 = a.H / 16, NBS = a.H / kGroup;
-    const rsrc_t rw = make_rsrc(a.w2p + (int64_t)e * NB16 * KB * kFragBytes, (uint32_t)NB16 * KB * kFragBytes);
-    const uint8_t* sb = a.w2s + (int64_t)e * KB * NBS;
-    for (int i = tid; i < 2 * KB; i += 256) s_sb[i & 1][i >> 1] = sb[(i >> 1) * NBS + nb * 2 + (i & 1)];
-    const uint32_t l16 = lane * 16;
-    auto issue = [&](int kb, uint8_t* st) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                dma16(ra, st + (2 * wv + q) * kFragBytes + h * 1024, l16,
-                      (uint32_t)((2 * wv + q) * KB + kb) * kFragBytes + h * 1024);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                dma16(rw, st + kPfStageA + (4 * wv + j) * kFragBytes + h * 1024, l16,
-                      (uint32_t)((nb * 16 + 4 * wv + j) * KB + kb) * kFragBytes + h * 1024);
-    };
-
-    v4f acc[4][8];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    __builtin_amdgcn_s_waitcnt(0);
-    issue(0, st0);
-    issue(min(1, KB - 1), st1);
-
-    auto step = [&](int kb, const uint8_t* cur, uint8_t* nxt) {
-        WAIT_VMCNT(12);
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        __builtin_amdgcn_s_barrier();
-        issue(min(kb + 2, KB - 1), nxt);
-        v8i af[4];
-        int sa[4];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            const int mf = wm * 4 + mi;
-            af[mi] = lds_frag(cur + mf * kFragBytes, lane);
-            sa[mi] = s_sa[(mf * 16 + (lane & 15)) * KB + kb];
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int f = wn * 8 + j;
-            const v8i b = lds_frag(cur + kPfStageA + f * kFragBytes, lane);
-            const int sbv = s_sb[wn][kb];
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) acc[mi][j] = mfma_fp8(af[mi], b, acc[mi][j], sa[mi], sbv);
-        }
-    };
-    int kb0 = 0;
-    for (; kb0 + 3 <= KB; kb0 += 3) {
-        step(kb0, st0, st2);
-        step(kb0 + 1, st1, st0);
-        step(kb0 + 2, st2, st1);
-    }
-    if (kb0 < KB) step(kb0, st0, st2);
-    if (kb0 + 1 < KB) step(kb0 + 1, st1, st0);
-    __builtin_amdgcn_s_waitcnt(0);   // the trailing duplicate DMA must land before LDS is reused
-
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = (wm * 4 + mi) * 16 + 4 * (lane >> 4) + i;
-            if (row < nvalid) {
-                const int64_t o = (int64_t)(rowbase + row) * a.H;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int col = nb * 256 + (wn * 8 + j) * 16 + (lane & 15);
-                    if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o + col] = f32_to_bf16(acc[mi][j][i]);
-                    else reinterpret_cast<float*>(a.out)[o + col] = acc[mi][j][i];
-                }
-            }
-        }
-    }
+__device__ __forceinline__ bool pf_work_item(int ncol, int ntiles, int& tile, int& col) {
+    const int total = ntiles * ncol;
+    const int per = (total + kXcds - 1) / kXcds;
+    const int L = blockIdx.x;
+    const int w = (L % kXcds) * per + L / kXcds;
+    if (L / kXcds >= per || w >= total) return false;
+    const int sb = w / (kPfGroupTiles * ncol), r = w - sb * kPfGroupTiles * ncol;
+    const int t0 = sb * kPfGroupTiles;
+    const int g = min(kPfGroupTiles, ntiles - t0);
+    col = r / g;
+    tile = t0 + r - col * g;
+    return true;
 }
 
 // ----------------------------------------------------------------------------------------
-// Register-staged prefill variants: the same tiles, but each wave loads its 12 16-byte
-// pieces of a K block into registers (buffer loads) and writes them to LDS itself.  Two LDS
-// buffers and two register sets: at step kb the wave issues the loads of block kb+2 into
-// one register set, computes block kb from LDS, then stores the other register set (block
-// kb+1, loaded a step earlier) into the free LDS buffer; one barrier per step.  Plain loads
-// into registers keep the compiler's vmcnt accounting exact.
+// The DMA is issued from inline asm: the compiler does not track it, so it inserts no wait
+// before the LDS reads of the other stages (it cannot tell which stage a DMA writes and
+// would wait for all of them); completion of a stage is awaited explicitly (each thread's
+// own DMAs by vmcnt, then a barrier for everyone's).  No register receives data from these
+// loads.  A scales are kept per K block ([kb][row]) so that the 16 rows a wave reads sit in
+// consecutive bytes (no LDS bank conflicts).
 
-struct PfLoads {
-    uint4 v[12];
-};
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+constexpr int kPfdStages = 3;
 
-__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t voff, uint32_t soff, int aux) {
-    typedef int v4i __attribute__((ext_vector_type(4)));
-    const v4i x = aux ? __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2)
-                      : __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-    return make_uint4((uint32_t)x[0], (uint32_t)x[1], (uint32_t)x[2], (uint32_t)x[3]);
+// Buffer descriptor in scalar registers (the base and size are wave-uniform).
+__device__ __forceinline__ v4i_t make_srd(const void* base, uint32_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    v4i_t r;
+    r[0] = (int)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    r[1] = (int)(__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) & 0xFFFFu);   // stride 0
+    r[2] = (int)__builtin_amdgcn_readfirstlane(bytes);
+    r[3] = 0x00020000;
+    return r;
 }
 
-template <int NR>
-__global__ __launch_bounds__(256, 1) void k_gemm1_pfr(G1Args a) {
-    const int ib = blockIdx.x;
-    const int tile = blockIdx.y;
-    if (tile >= *a.ntiles) return;
-    const int2 te = a.tiles[tile];
-    const int e = te.x, m0 = te.y;
-    const int nvalid = min(kPfBM, a.counts[e] - m0);
-    const int rowbase = a.offsets[e] + m0;
-    const int KB = a.H / kGroup;
-    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wv >> 1, wn = wv & 1;
-
-    __shared__ __align__(16) uint8_t buf[2][kPfStage];
-    __shared__ uint8_t s_sa[kPfBM * kPfMaxKB];
-    __shared__ uint8_t s_sg[kPfMaxKB], s_su[kPfMaxKB];
-    __shared__ float s_amax[2][kPfBM];
-
-    {
-        const int r = tid >> 1, half = tid & 1;
-        const int tok = a.sorted_assign[rowbase + min(r, nvalid - 1)] / a.k;
-        const uint8_t* src = a.xs + (int64_t)tok * KB;
-        for (int kb = half; kb < KB; kb += 2) s_sa[r * KB + kb] = src[kb];
-    }
-    const rsrc_t ra = make_rsrc(a.xq, (uint32_t)a.T * a.H);
-    uint32_t aoff[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int r = (2 * wv + q) * 16 + (lane & 15);
-        const int tok = a.sorted_assign[rowbase + min(r, nvalid - 1)] / a.k;
-        aoff[q] = (uint32_t)tok * a.H + (lane >> 4) * 32;
-    }
-    const int NB16 = 2 * a.I / 16, NBS = 2 * a.I / kGroup;
-    const rsrc_t rw = make_rsrc(a.w13p + (int64_t)e * NB16 * KB * kFragBytes, (uint32_t)NB16 * KB * kFragBytes);
-    const uint8_t* sb = a.w13s + (int64_t)e * KB * NBS;
-    for (int i = tid; i < KB; i += 256) {
-        s_sg[i] = sb[i * NBS + ib];
-        s_su[i] = sb[i * NBS + a.I / kGroup + ib];
-    }
-    int bn16[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int f = 4 * wv + j;
-        bn16[j] = f < 8 ? ib * 8 + f : a.I / 16 + ib * 8 + (f - 8);
-    }
-    const uint32_t l16 = lane * 16;
-    auto load = [&](int kb, PfLoads& L) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) L.v[q * 2 + h] = bload16(ra, aoff[q] + h * 16, kb * kGroup, 0);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                L.v[4 + j * 2 + h] = bload16(rw, l16, (uint32_t)(bn16[j] * KB + kb) * kFragBytes + h * 1024, 0);
-    };
-    auto store = [&](const PfLoads& L, uint8_t* st) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                *reinterpret_cast<uint4*>(st + (2 * wv + q) * kFragBytes + h * 1024 + l16) = L.v[q * 2 + h];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                *reinterpret_cast<uint4*>(st + kPfStageA + (4 * wv + j) * kFragBytes + h * 1024 + l16) = L.v[4 + j * 2 + h];
-    };
-
-    v4f accg[4][4], accu[4][4];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) accg[mi][j] = accu[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    PfLoads R[NR];
-#pragma unroll
-    for (int r = 0; r < NR; ++r) load(min(r, KB - 1), R[r]);
-    store(R[0], buf[0]);
-    __syncthreads();
-
-    auto compute = [&](int kb, const uint8_t* cur) {
-        v8i af[4];
-        int sa[4];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            const int mf = wm * 4 + mi;
-            af[mi] = lds_frag(cur + mf * kFragBytes, lane);
-            sa[mi] = s_sa[(mf * 16 + (lane & 15)) * KB + kb];
-        }
-        const int sg = s_sg[kb];
-        const int su = s_su[kb];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const v8i bg = lds_frag(cur + kPfStageA + (wn * 4 + j) * kFragBytes, lane);
-            const v8i bu = lds_frag(cur + kPfStageA + (8 + wn * 4 + j) * kFragBytes, lane);
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
-                accg[mi][j] = mfma_fp8(af[mi], bg, accg[mi][j], sa[mi], sg);
-                accu[mi][j] = mfma_fp8(af[mi], bu, accu[mi][j], sa[mi], su);
-            }
-        }
-    };
-    // step kb: LDS buffer kb%2 holds block kb; register set kb%NR is free (its block was
-    // stored a step ago) and takes block kb+NR; after the MMAs, register set (kb+1)%NR
-    // (block kb+1, loaded NR-1 steps ago) goes to LDS buffer (kb+1)%2.
-    // Loads and stores are unconditional (block indices clamped to the last block; the
-    // duplicates land in buffers nobody reads) so the number of loads in flight is the same
-    // on every path and the compiler's vmcnt waits stay exact.
-    auto step = [&](int kb, const int ri, const int bi) {
-        load(min(kb + NR, KB - 1), R[ri]);
-        compute(kb, buf[bi]);
-        store(R[(ri + 1) % NR], buf[bi ^ 1]);
-        __syncthreads();
-    };
-    constexpr int U = NR == 3 ? 6 : (NR == 4 ? 4 : 2);
-    int kb = 0;
-    for (; kb + U <= KB; kb += U) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) step(kb + u, u % NR, u & 1);
-    }
-#pragma unroll
-    for (int u = 0; u < U - 1; ++u)
-        if (kb + u < KB) step(kb + u, u % NR, u & 1);
-
-    float hv[4][4][4];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float m = 0.f;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float g = accg[mi][j][i];
-                const float h = g / (1.0f + expf(-g)) * accu[mi][j][i];
-                hv[mi][j][i] = h;
-                m = fmaxf(m, fabsf(h));
-            }
-            m = max16(m);
-            if ((lane & 15) == 0) s_amax[wn][(wm * 4 + mi) * 16 + 4 * (lane >> 4) + i] = m;
-        }
-    }
-    __syncthreads();
-    uint8_t* s_h = buf[0];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = (wm * 4 + mi) * 16 + 4 * (lane >> 4) + i;
-            const int ex = scale_exponent(fmaxf(s_amax[0][row], s_amax[1][row]));
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                s_h[row * 128 + (wn * 4 + j) * 16 + (lane & 15)] =
-                    (uint8_t)(cvt2_e4m3(ldexpf(hv[mi][j][i], -ex), 0.f) & 0xFFu);
-            if (wn == 0 && (lane & 15) == 0)
-                a.hs[((int64_t)tile * kPfBM + row) * (a.I / kGroup) + ib] = (uint8_t)(ex + 127);
-        }
-    }
-    __syncthreads();
-    const int KB2 = a.I / kGroup;
-    for (int q = tid; q < 8 * 128; q += 256) {
-        const int mf = q >> 7, w = q & 127, hh = w >> 6, ln = w & 63;
-        const uint4 v = *reinterpret_cast<const uint4*>(s_h + (mf * 16 + (ln & 15)) * 128 + (ln >> 4) * 32 + hh * 16);
-        *reinterpret_cast<uint4*>(a.hq + (((int64_t)tile * 8 + mf) * KB2 + ib) * kFragBytes + hh * 1024 + ln * 16) = v;
-    }
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p);
 }
 
-template <int NR>
-__global__ __launch_bounds__(256, 1) void k_gemm2_pfr(G2Args a) {
-    const int nb = blockIdx.x;
-    const int tile = blockIdx.y;
-    if (tile >= *a.ntiles) return;
-    const int2 te = a.tiles[tile];
-    const int e = te.x, m0 = te.y;
-    const int nvalid = min(kPfBM, a.counts[e] - m0);
-    const int rowbase = a.offsets[e] + m0;
-    const int KB = a.I / kGroup;
-    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wv >> 1, wn = wv & 1;
-
-    __shared__ __align__(16) uint8_t buf[2][kPfStage];
-    __shared__ uint8_t s_sa[kPfBM * kPfMaxKB];
-    __shared__ uint8_t s_sb[2][kPfMaxKB];
-    {
-        const uint8_t* src = a.hs + (int64_t)tile * kPfBM * KB;
-        for (int i = tid; i < kPfBM * KB; i += 256) s_sa[i] = src[i];
-    }
-    const rsrc_t ra = make_rsrc(a.hq + (int64_t)tile * 8 * KB * kFragBytes, (uint32_t)8 * KB * kFragBytes);
-    const int NB16 = a.H / 16, NBS = a.H / kGroup;
-    const rsrc_t rw = make_rsrc(a.w2p + (int64_t)e * NB16 * KB * kFragBytes, (uint32_t)NB16 * KB * kFragBytes);
-    const uint8_t* sb = a.w2s + (int64_t)e * KB * NBS;
-    for (int i = tid; i < 2 * KB; i += 256) s_sb[i & 1][i >> 1] = sb[(i >> 1) * NBS + nb * 2 + (i & 1)];
-    const uint32_t l16 = lane * 16;
-    auto load = [&](int kb, PfLoads& L) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                L.v[q * 2 + h] = bload16(ra, l16, (uint32_t)((2 * wv + q) * KB + kb) * kFragBytes + h * 1024, 0);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                L.v[4 + j * 2 + h] = bload16(rw, l16, (uint32_t)((nb * 16 + 4 * wv + j) * KB + kb) * kFragBytes + h * 1024, 0);
-    };
-    auto store = [&](const PfLoads& L, uint8_t* st) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                *reinterpret_cast<uint4*>(st + (2 * wv + q) * kFragBytes + h * 1024 + l16) = L.v[q * 2 + h];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                *reinterpret_cast<uint4*>(st + kPfStageA + (4 * wv + j) * kFragBytes + h * 1024 + l16) = L.v[4 + j * 2 + h];
-    };
-
-    v4f acc[4][8];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    PfLoads R[NR];
-#pragma unroll
-    for (int r = 0; r < NR; ++r) load(min(r, KB - 1), R[r]);
-    store(R[0], buf[0]);
-    __syncthreads();
-
-    auto compute = [&](int kb, const uint8_t* cur) {
-        v8i af[4];
-        int sa[4];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            const int mf = wm * 4 + mi;
-            af[mi] = lds_frag(cur + mf * kFragBytes, lane);
-            sa[mi] = s_sa[(mf * 16 + (lane & 15)) * KB + kb];
-        }
-        const int sbv = s_sb[wn][kb];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const v8i b = lds_frag(cur + kPfStageA + (wn * 8 + j) * kFragBytes, lane);
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) acc[mi][j] = mfma_fp8(af[mi], b, acc[mi][j], sa[mi], sbv);
-        }
-    };
-    // step kb: LDS buffer kb%2 holds block kb; register set kb%NR is free (its block was
-    // stored a step ago) and takes block kb+NR; after the MMAs, register set (kb+1)%NR
-    // (block kb+1, loaded NR-1 steps ago) goes to LDS buffer (kb+1)%2.
-    // Loads and stores are unconditional (block indices clamped to the last block; the
-    // duplicates land in buffers nobody reads) so the number of loads in flight is the same
-    // on every path and the compiler's vmcnt waits stay exact.
-    auto step = [&](int kb, const int ri, const int bi) {
-        load(min(kb + NR, KB - 1), R[ri]);
-        compute(kb, buf[bi]);
-        store(R[(ri + 1) % NR], buf[bi ^ 1]);
-        __syncthreads();
-    };
-    constexpr int U = NR == 3 ? 6 : (NR == 4 ? 4 : 2);
-    int kb = 0;
-    for (; kb + U <= KB; kb += U) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) step(kb + u, u % NR, u & 1);
-    }
-#pragma unroll
-    for (int u = 0; u < U - 1; ++u)
-        if (kb + u < KB) step(kb + u, u % NR, u & 1);
-
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = (wm * 4 + mi) * 16 + 4 * (lane >> 4) + i;
-            if (row < nvalid) {
-                const int64_t o = (int64_t)(rowbase + row) * a.H;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int col = nb * 256 + (wn * 8 + j) * 16 + (lane & 15);
-                    if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o + col] = f32_to_bf16(acc[mi][j][i]);
-                    else reinterpret_cast<float*>(a.out)[o + col] = acc[mi][j][i];
-                }
-            }
-        }
-    }
+// 16 bytes per lane from the buffer at voff + soff into LDS at m0base + 16 * lane.
+__device__ __forceinline__ void dma16_async(const v4i_t& srd, uint32_t m0base, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(m0base), "v"(voff), "s"(srd), "s"(soff)
+                 : "memory", "m0");
 }
 
-// ----------------------------------------------------------------------------------------
-// Column-split prefill variants: wave w owns all 8 row fragments of the 128-row tile and 4
-// column fragments, so no B fragment is shared between waves.  A (the 8 row fragments of a
-// K block, 16 KB) is staged once in LDS for all four waves, register-staged and double
-// buffered (thread t owns the 16-byte pieces t, t+256, t+512, t+768; piece p sits at byte
-// 16p of the LDS block, i.e. fragment p/128 in matrix-core order).  B fragments stream from
-// memory straight into each wave's registers PFB K blocks ahead.  LDS traffic per K block
-// and workgroup: 16 KB written + 64 KB read.
-
-template <bool kG1, int PFB>
-struct PfnCore {
-    // one K block: 8 row fragments x 4 column fragments of MFMAs for this wave
-    static __device__ __forceinline__ void mma(v4f (&acc)[8][4], const uint8_t* ab, const v8i (&b)[4],
-                                               const uint8_t* s_sa, int KB, int kb, int lane, const int (&sbv)[4]) {
-#pragma unroll
-        for (int mf = 0; mf < 8; ++mf) {
-            const v8i af = lds_frag(ab + mf * kFragBytes, lane);
-            const int sa = s_sa[(mf * 16 + (lane & 15)) * KB + kb];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[mf][j] = mfma_fp8(af, b[j], acc[mf][j], sa, sbv[j]);
-        }
-    }
-};
-
-template <int PFB>
-__global__ __launch_bounds__(256, 1) void k_gemm1_pfn(G1Args a) {
-    const int ib = blockIdx.x;
-    const int tile = blockIdx.y;
-    if (tile >= *a.ntiles) return;
-    const int2 te = a.tiles[tile];
-    const int e = te.x, m0 = te.y;
-    const int nvalid = min(kPfBM, a.counts[e] - m0);
-    const int rowbase = a.offsets[e] + m0;
-    const int KB = a.H / kGroup;
-    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-
-    __shared__ __align__(16) uint8_t abuf[2][8 * kFragBytes];
-    __shared__ uint8_t s_sa[kPfBM * kPfMaxKB];
-    __shared__ uint8_t s_sg[kPfMaxKB], s_su[kPfMaxKB];
-    __shared__ float s_amax[4][kPfBM];
-
-    {
-        const int r = tid >> 1, half = tid & 1;
-        const int tok = a.sorted_assign[rowbase + min(r, nvalid - 1)] / a.k;
-        const uint8_t* src = a.xs + (int64_t)tok * KB;
-        for (int kb = half; kb < KB; kb += 2) s_sa[r * KB + kb] = src[kb];
-    }
-    const int NB16 = 2 * a.I / 16, NBS = 2 * a.I / kGroup;
-    const uint8_t* sb = a.w13s + (int64_t)e * KB * NBS;
-    for (int i = tid; i < KB; i += 256) {
-        s_sg[i] = sb[i * NBS + ib];
-        s_su[i] = sb[i * NBS + a.I / kGroup + ib];
-    }
-    const rsrc_t ra = make_rsrc(a.xq, (uint32_t)a.T * a.H);
-    uint32_t aoff[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int p = tid + 256 * i, mf = p >> 7, hh = (p >> 6) & 1, ln = p & 63;
-        const int r = mf * 16 + (ln & 15);
-        const int tok = a.sorted_assign[rowbase + min(r, nvalid - 1)] / a.k;
-        aoff[i] = (uint32_t)tok * a.H + (ln >> 4) * 32 + hh * 16;
-    }
-    const rsrc_t rw = make_rsrc(a.w13p + (int64_t)e * NB16 * KB * kFragBytes, (uint32_t)NB16 * KB * kFragBytes);
-    const int g16 = ib * 8 + 2 * wv, u16 = a.I / 16 + g16;
-    const int bn16[4] = {g16, g16 + 1, u16, u16 + 1};
-    const uint32_t l16 = lane * 16;
-
-    v4f acc[8][4];
-#pragma unroll
-    for (int mf = 0; mf < 8; ++mf)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[mf][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    uint4 R[2][4];
-    v8i bq[PFB][4];
-    auto loadA = [&](int kb, uint4 (&r)[4]) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) r[i] = bload16(ra, aoff[i], kb * kGroup, 0);
-    };
-    auto storeA = [&](const uint4 (&r)[4], uint8_t* ab) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(ab + (tid + 256 * i) * 16) = r[i];
-    };
-    auto loadB = [&](int kb, v8i (&b)[4]) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) b[j] = buf_frag(rw, l16, (uint32_t)(bn16[j] * KB + kb) * kFragBytes);
-    };
-    loadA(0, R[0]);
-    if (KB > 1) loadA(1, R[1]);
-#pragma unroll
-    for (int p = 0; p < PFB; ++p)
-        if (p < KB) loadB(p, bq[p]);
-    storeA(R[0], abuf[0]);
-    __syncthreads();
-
-    auto step = [&](int kb, const int p, const int ab) {
-        if (kb + 2 < KB) loadA(kb + 2, R[ab]);
-        const int sg = s_sg[kb], su = s_su[kb];
-        const int sbv[4] = {sg, sg, su, su};
-        PfnCore<true, PFB>::mma(acc, abuf[ab], bq[p], s_sa, KB, kb, lane, sbv);
-        if (kb + PFB < KB) loadB(kb + PFB, bq[p]);
-        if (kb + 1 < KB) storeA(R[ab ^ 1], abuf[ab ^ 1]);
-        __syncthreads();
-    };
-    static_assert(PFB == 2 || PFB == 4, "the K loop is unrolled by 4");
-    for (int kb = 0; kb < KB; kb += 4) {
-        step(kb, 0, 0);
-        if (kb + 1 < KB) step(kb + 1, 1 % PFB, 1);
-        if (kb + 2 < KB) step(kb + 2, 2 % PFB, 0);
-        if (kb + 3 < KB) step(kb + 3, 3 % PFB, 1);
-    }
-
-    // ---- epilogue: SwiGLU on this wave's 32 columns, row amax over the four waves, requant
-    float hv[8][2][4];
-#pragma unroll
-    for (int mf = 0; mf < 8; ++mf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float m = 0.f;
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const float g = acc[mf][jj][i];
-                const float h = g / (1.0f + expf(-g)) * acc[mf][2 + jj][i];
-                hv[mf][jj][i] = h;
-                m = fmaxf(m, fabsf(h));
-            }
-            m = max16(m);
-            if ((lane & 15) == 0) s_amax[wv][mf * 16 + 4 * (lane >> 4) + i] = m;
-        }
-    }
-    __syncthreads();
-    uint8_t* s_h = abuf[0];   // [128][128] bytes
-#pragma unroll
-    for (int mf = 0; mf < 8; ++mf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = mf * 16 + 4 * (lane >> 4) + i;
-            const float am = fmaxf(fmaxf(s_amax[0][row], s_amax[1][row]), fmaxf(s_amax[2][row], s_amax[3][row]));
-            const int ex = scale_exponent(am);
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
-                s_h[row * 128 + (2 * wv + jj) * 16 + (lane & 15)] =
-                    (uint8_t)(cvt2_e4m3(ldexpf(hv[mf][jj][i], -ex), 0.f) & 0xFFu);
-            if (wv == 0 && (lane & 15) == 0)
-                a.hs[((int64_t)tile * kPfBM + row) * (a.I / kGroup) + ib] = (uint8_t)(ex + 127);
-        }
-    }
-    __syncthreads();
-    const int KB2 = a.I / kGroup;
-    for (int q = tid; q < 8 * 128; q += 256) {
-        const int mf = q >> 7, w = q & 127, hh = w >> 6, ln = w & 63;
-        const uint4 v = *reinterpret_cast<const uint4*>(s_h + (mf * 16 + (ln & 15)) * 128 + (ln >> 4) * 32 + hh * 16);
-        *reinterpret_cast<uint4*>(a.hq + (((int64_t)tile * 8 + mf) * KB2 + ib) * kFragBytes + hh * 1024 + ln * 16) = v;
-    }
+// Wait until at most N of this thread's vector-memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-template <int PFB>
-__global__ __launch_bounds__(256, 1) void k_gemm2_pfn(G2Args a) {
-    const int nb = blockIdx.x;
-    const int tile = blockIdx.y;
-    if (tile >= *a.ntiles) return;
+__global__ __launch_bounds__(512, 1) void k_gemm1_pf(G1Args a) {
+    int ib, tile;
+    if (!pf_work_item(a.I / kGroup, __builtin_amdgcn_readfirstlane(*a.ntiles), tile, ib)) return;
     const int2 te = a.tiles[tile];
-    const int e = te.x, m0 = te.y;
+    const int e = __builtin_amdgcn_readfirstlane(te.x), m0 = __builtin_amdgcn_readfirstlane(te.y);
     const int nvalid = min(kPfBM, a.counts[e] - m0);
-    const int rowbase = a.offsets[e] + m0;
-    const int KB = a.I / kGroup;
-    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-
-    __shared__ __align__(16) uint8_t abuf[2][8 * kFragBytes];
-    __shared__ uint8_t s_sa[kPfBM * kPfMaxKB];
-    __shared__ uint8_t s_sb[2][kPfMaxKB];   // the workgroup's two 128-column scale blocks
-    {
-        const uint8_t* src = a.hs + (int64_t)tile * kPfBM * KB;
-        for (int i = tid; i < kPfBM * KB; i += 256) s_sa[i] = src[i];
-    }
-    const int NB16 = a.H / 16, NBS = a.H / kGroup;
-    const uint8_t* sb = a.w2s + (int64_t)e * KB * NBS;
-    for (int i = tid; i < 2 * KB; i += 256) s_sb[i & 1][i >> 1] = sb[(i >> 1) * NBS + nb * 2 + (i & 1)];
-    const rsrc_t ra = make_rsrc(a.hq + (int64_t)tile * 8 * KB * kFragBytes, (uint32_t)8 * KB * kFragBytes);
-    const rsrc_t rw = make_rsrc(a.w2p + (int64_t)e * NB16 * KB * kFragBytes, (uint32_t)NB16 * KB * kFragBytes);
-    const int n16 = nb * 16 + 4 * wv;
-    const int sblk = wv >> 1;   // this wave's 64 columns lie in scale block nb*2 + wv/2
-    const uint32_t l16 = lane * 16;
-
-    v4f acc[8][4];
-#pragma unroll
-    for (int mf = 0; mf < 8; ++mf)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[mf][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    uint4 R[2][4];
-    v8i bq[PFB][4];
-    auto loadA = [&](int kb, uint4 (&r)[4]) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int p = tid + 256 * i;
-            r[i] = bload16(ra, (p & 127) * 16, (uint32_t)((p >> 7) * KB + kb) * kFragBytes, 0);
-        }
-    };
-    auto storeA = [&](const uint4 (&r)[4], uint8_t* ab) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(ab + (tid + 256 * i) * 16) = r[i];
-    };
-    auto loadB = [&](int kb, v8i (&b)[4]) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) b[j] = buf_frag(rw, l16, (uint32_t)((n16 + j) * KB + kb) * kFragBytes);
-    };
-    loadA(0, R[0]);
-    if (KB > 1) loadA(1, R[1]);
-#pragma unroll
-    for (int p = 0; p < PFB; ++p)
-        if (p < KB) loadB(p, bq[p]);
-    storeA(R[0], abuf[0]);
-    __syncthreads();
-
-    auto step = [&](int kb, const int p, const int ab) {
-        if (kb + 2 < KB) loadA(kb + 2, R[ab]);
-        const int s = s_sb[sblk][kb];
-        const int sbv[4] = {s, s, s, s};
-        PfnCore<false, PFB>::mma(acc, abuf[ab], bq[p], s_sa, KB, kb, lane, sbv);
-        if (kb + PFB < KB) loadB(kb + PFB, bq[p]);
-        if (kb + 1 < KB) storeA(R[ab ^ 1], abuf[ab ^ 1]);
-        __syncthreads();
-    };
-    static_assert(PFB == 2 || PFB == 4, "the K loop is unrolled by 4");
-    for (int kb = 0; kb < KB; kb += 4) {
-        step(kb, 0, 0);
-        if (kb + 1 < KB) step(kb + 1, 1 % PFB, 1);
-        if (kb + 2 < KB) step(kb + 2, 2 % PFB, 0);
-        if (kb + 3 < KB) step(kb + 3, 3 % PFB, 1);
-    }
-
-#pragma unroll
-    for (int mf = 0; mf < 8; ++mf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = mf * 16 + 4 * (lane >> 4) + i;
-            if (row < nvalid) {
-                const int64_t o = (int64_t)(rowbase + row) * a.H;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int col = (n16 + j) * 16 + (lane & 15);
-                    if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o + col] = f32_to_bf16(acc[mf][j][i]);
-                    else reinterpret_cast<float*>(a.out)[o + col] = acc[mf][j][i];
-                }
-            }
-        }
-    }
-}
-
-// ----------------------------------------------------------------------------------------
-// 8-wave prefill variants: the 128 x 256 tile split over 2 (rows) x 4 (columns) waves of
-// 64 x 64 (4 x 4 fragments), two waves per SIMD so one wave's LDS and load waits overlap the
-// other's matrix-core work.  Operands are register-staged through two LDS buffers as in the
-// 4-wave variant; each of the 512 threads moves 6 16-byte pieces per K block (2 of A, 4 of B).
-// Piece p of a stage sits at byte 16 p: fragment p / 128, half (p / 64) % 2, lane p % 64.
-
-struct Pf8Loads {
-    uint4 v[6];
-};
-
-template <int NR>
-__global__ __launch_bounds__(512, 1) void k_gemm1_pf8(G1Args a) {
-    const int ib = blockIdx.x;
-    const int tile = blockIdx.y;
-    if (tile >= *a.ntiles) return;
-    const int2 te = a.tiles[tile];
-    const int e = te.x, m0 = te.y;
-    const int nvalid = min(kPfBM, a.counts[e] - m0);
-    const int rowbase = a.offsets[e] + m0;
+    const int rowbase = __builtin_amdgcn_readfirstlane(a.offsets[e] + m0);
     const int KB = a.H / kGroup;
     const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wv >> 2, wn = wv & 3;
 
-    __shared__ __align__(16) uint8_t buf[2][kPfStage];
-    __shared__ uint8_t s_sa[kPfBM * kPfMaxKB];
+    __shared__ __align__(16) uint8_t buf[kPfdStages * kPfStage];
+    __shared__ __align__(16) uint8_t s_sa[kPfMaxKB * kPfBM];   // [kb][row]
     __shared__ uint8_t s_sg[kPfMaxKB], s_su[kPfMaxKB];
     __shared__ float s_amax[4][kPfBM];
 
-    if (tid < 2 * kPfBM) {
-        const int r = tid >> 1, half = tid & 1;
-        const int tok = a.sorted_assign[rowbase + min(r, nvalid - 1)] / a.k;
-        const uint8_t* src = a.xs + (int64_t)tok * KB;
-        for (int kb = half; kb < KB; kb += 2) s_sa[r * KB + kb] = src[kb];
-    }
     const int NB16 = 2 * a.I / 16, NBS = 2 * a.I / kGroup;
-    const uint8_t* sb = a.w13s + (int64_t)e * KB * NBS;
-    for (int i = tid; i < KB; i += 512) {
-        s_sg[i] = sb[i * NBS + ib];
-        s_su[i] = sb[i * NBS + a.I / kGroup + ib];
-    }
-    const rsrc_t ra = make_rsrc(a.xq, (uint32_t)a.T * a.H);
-    const rsrc_t rw = make_rsrc(a.w13p + (int64_t)e * NB16 * KB * kFragBytes, (uint32_t)NB16 * KB * kFragBytes);
+    const v4i_t ra = make_srd(a.xq, (uint32_t)a.T * a.H);
+    const v4i_t rw = make_srd(a.w13p + (int64_t)e * NB16 * KB * kFragBytes, (uint32_t)NB16 * KB * kFragBytes);
     uint32_t aoff[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -1496,7 +708,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pf8(G1Args a) {
         const int tok = a.sorted_assign[rowbase + min(r, nvalid - 1)] / a.k;
         aoff[i] = (uint32_t)tok * a.H + (ln >> 4) * 32 + hh * 16;
     }
-    int bsoff[4];   // wave-uniform byte offset of the piece's fragment row and half
+    uint32_t bsoff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int q = wv * 64 + 512 * i, f = q >> 7, hh = (q >> 6) & 1;
@@ -1504,18 +716,28 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pf8(G1Args a) {
         bsoff[i] = __builtin_amdgcn_readfirstlane(n16 * KB * kFragBytes + hh * 1024);
     }
     const uint32_t l16 = lane * 16;
-    auto load = [&](int kb, Pf8Loads& L) {
+    const uint32_t lds_w = lds_addr(buf) + wv * 64 * 16;   // this wave's 1 KB piece row of stage 0
+    auto issue = [&](int kb, int s) {
+        const uint32_t st = __builtin_amdgcn_readfirstlane(lds_w + s * kPfStage);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) L.v[i] = bload16(ra, aoff[i], kb * kGroup, 0);
+        for (int i = 0; i < 2; ++i) dma16_async(ra, st + i * 512 * 16, aoff[i], kb * kGroup);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) L.v[2 + i] = bload16(rw, l16, (uint32_t)(bsoff[i] + kb * kFragBytes), 0);
+        for (int i = 0; i < 4; ++i) dma16_async(rw, st + kPfStageA + i * 512 * 16, l16, bsoff[i] + kb * kFragBytes);
     };
-    auto store = [&](const Pf8Loads& L, uint8_t* st) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(st + (tid + 512 * i) * 16) = L.v[i];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(st + kPfStageA + (tid + 512 * i) * 16) = L.v[2 + i];
-    };
+    issue(0, 0);
+    if (KB > 1) issue(1, 1);
+
+    {   // scales, while the first two blocks load
+        const int r = tid >> 2, q = tid & 3;
+        const int tok = a.sorted_assign[rowbase + min(r, nvalid - 1)] / a.k;
+        const uint8_t* src = a.xs + (int64_t)tok * KB;
+        for (int kb = q; kb < KB; kb += 4) s_sa[kb * kPfBM + r] = src[kb];
+        const uint8_t* sb = a.w13s + (int64_t)e * KB * NBS;
+        for (int i = tid; i < KB; i += 512) {
+            s_sg[i] = sb[i * NBS + ib];
+            s_su[i] = sb[i * NBS + a.I / kGroup + ib];
+        }
+    }
 
     v4f acc[4][4];   // [row fragment][gate 0, 1 | up 2, 3]
 #pragma unroll
@@ -1523,46 +745,30 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pf8(G1Args a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    Pf8Loads R[NR];
-#pragma unroll
-    for (int r = 0; r < NR; ++r) load(min(r, KB - 1), R[r]);
-    store(R[0], buf[0]);
-    __syncthreads();
-
-    auto compute = [&](int kb, const uint8_t* cur) {
-        v8i af[4];
+    int s = 0;
+    for (int kb = 0; kb < KB; ++kb) {
+        // block kb has landed once at most the next block's 6 DMAs of this thread are pending
+        if (kb + 1 < KB) wait_vm<6>(); else wait_vm<0>();
+        __syncthreads();   // everyone's block kb is in LDS; everyone is done with stage (kb + 2) % 3
+        if (kb + 2 < KB) issue(kb + 2, s == 0 ? 2 : s - 1);
+        const uint8_t* cur = buf + s * kPfStage;
+        v8i af[4], bf[4];
         int sa[4];
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
             const int mf = wm * 4 + mi;
             af[mi] = lds_frag(cur + mf * kFragBytes, lane);
-            sa[mi] = s_sa[(mf * 16 + (lane & 15)) * KB + kb];
+            sa[mi] = s_sa[kb * kPfBM + mf * 16 + (lane & 15)];
         }
         const int sg = s_sg[kb], su = s_su[kb];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int f = j < 2 ? 2 * wn + j : 8 + 2 * wn + (j - 2);
-            const v8i b = lds_frag(cur + kPfStageA + f * kFragBytes, lane);
+        for (int j = 0; j < 4; ++j) bf[j] = lds_frag(cur + kPfStageA + (j < 2 ? 2 * wn + j : 6 + 2 * wn + j) * kFragBytes, lane);
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi) acc[mi][j] = mfma_fp8(af[mi], b, acc[mi][j], sa[mi], j < 2 ? sg : su);
-        }
-    };
-    // Same step order as the 4-wave kernel: load block kb+NR, compute block kb, store block kb+1.
-    auto step = [&](int kb, const int ri, const int bi) {
-        load(min(kb + NR, KB - 1), R[ri]);
-        compute(kb, buf[bi]);
-        store(R[(ri + 1) % NR], buf[bi ^ 1]);
-        __syncthreads();
-    };
-    constexpr int U = NR == 3 ? 6 : (NR == 4 ? 4 : 2);
-    int kb = 0;
-    for (; kb + U <= KB; kb += U) {
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int u = 0; u < U; ++u) step(kb + u, u % NR, u & 1);
+            for (int mi = 0; mi < 4; ++mi) acc[mi][j] = mfma_fp8(af[mi], bf[j], acc[mi][j], sa[mi], j < 2 ? sg : su);
+        s = s == 2 ? 0 : s + 1;
     }
-#pragma unroll
-    for (int u = 0; u < U - 1; ++u)
-        if (kb + u < KB) step(kb + u, u % NR, u & 1);
 
     float hv[4][2][4];
 #pragma unroll
@@ -1581,8 +787,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pf8(G1Args a) {
             if ((lane & 15) == 0) s_amax[wn][(wm * 4 + mi) * 16 + 4 * (lane >> 4) + i] = m;
         }
     }
-    __syncthreads();
-    uint8_t* s_h = buf[0];
+    __syncthreads();   // also: every wave is done reading the stages before buf is reused
+    uint8_t* s_h = buf;
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
@@ -1607,33 +813,26 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pf8(G1Args a) {
     }
 }
 
-template <int NR>
-__global__ __launch_bounds__(512, 1) void k_gemm2_pf8(G2Args a) {
-    const int nb = blockIdx.x;
-    const int tile = blockIdx.y;
-    if (tile >= *a.ntiles) return;
+__global__ __launch_bounds__(512, 1) void k_gemm2_pf(G2Args a) {
+    int nb, tile;
+    if (!pf_work_item(a.H / 256, __builtin_amdgcn_readfirstlane(*a.ntiles), tile, nb)) return;
     const int2 te = a.tiles[tile];
-    const int e = te.x, m0 = te.y;
+    const int e = __builtin_amdgcn_readfirstlane(te.x), m0 = __builtin_amdgcn_readfirstlane(te.y);
     const int nvalid = min(kPfBM, a.counts[e] - m0);
-    const int rowbase = a.offsets[e] + m0;
+    const int rowbase = __builtin_amdgcn_readfirstlane(a.offsets[e] + m0);
     const int KB = a.I / kGroup;
     const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wv >> 2, wn = wv & 3;
 
-    __shared__ __align__(16) uint8_t buf[2][kPfStage];
-    __shared__ uint8_t s_sa[kPfBM * kPfMaxKB];
+    __shared__ __align__(16) uint8_t buf[kPfdStages * kPfStage];
+    __shared__ __align__(16) uint8_t s_sa[kPfMaxKB * kPfBM];   // [kb][row]
     __shared__ uint8_t s_sb[2][kPfMaxKB];
-    {
-        const uint8_t* src = a.hs + (int64_t)tile * kPfBM * KB;
-        for (int i = tid; i < kPfBM * KB; i += 512) s_sa[i] = src[i];
-    }
+
     const int NB16 = a.H / 16, NBS = a.H / kGroup;
-    const uint8_t* sb = a.w2s + (int64_t)e * KB * NBS;
-    for (int i = tid; i < 2 * KB; i += 512) s_sb[i & 1][i >> 1] = sb[(i >> 1) * NBS + nb * 2 + (i & 1)];
-    const rsrc_t ra = make_rsrc(a.hq + (int64_t)tile * 8 * KB * kFragBytes, (uint32_t)8 * KB * kFragBytes);
-    const rsrc_t rw = make_rsrc(a.w2p + (int64_t)e * NB16 * KB * kFragBytes, (uint32_t)NB16 * KB * kFragBytes);
+    const v4i_t ra = make_srd(a.hq + (int64_t)tile * 8 * KB * kFragBytes, (uint32_t)8 * KB * kFragBytes);
+    const v4i_t rw = make_srd(a.w2p + (int64_t)e * NB16 * KB * kFragBytes, (uint32_t)NB16 * KB * kFragBytes);
     const uint32_t l16 = lane * 16;
-    int asoff[2], bsoff[4];   // wave-uniform byte offsets of the pieces' fragment rows and halves
+    uint32_t asoff[2], bsoff[4];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int p = wv * 64 + 512 * i, mf = p >> 7, hh = (p >> 6) & 1;
@@ -1644,18 +843,25 @@ __global__ __launch_bounds__(512, 1) void k_gemm2_pf8(G2Args a) {
         const int q = wv * 64 + 512 * i, f = q >> 7, hh = (q >> 6) & 1;
         bsoff[i] = __builtin_amdgcn_readfirstlane((nb * 16 + f) * KB * kFragBytes + hh * 1024);
     }
-    auto load = [&](int kb, Pf8Loads& L) {
+    const uint32_t lds_w = lds_addr(buf) + wv * 64 * 16;
+    auto issue = [&](int kb, int s) {
+        const uint32_t st = __builtin_amdgcn_readfirstlane(lds_w + s * kPfStage);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) L.v[i] = bload16(ra, l16, (uint32_t)(asoff[i] + kb * kFragBytes), 0);
+        for (int i = 0; i < 2; ++i) dma16_async(ra, st + i * 512 * 16, l16, asoff[i] + kb * kFragBytes);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) L.v[2 + i] = bload16(rw, l16, (uint32_t)(bsoff[i] + kb * kFragBytes), 0);
+        for (int i = 0; i < 4; ++i) dma16_async(rw, st + kPfStageA + i * 512 * 16, l16, bsoff[i] + kb * kFragBytes);
     };
-    auto store = [&](const Pf8Loads& L, uint8_t* st) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(st + (tid + 512 * i) * 16) = L.v[i];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(st + kPfStageA + (tid + 512 * i) * 16) = L.v[2 + i];
-    };
+    issue(0, 0);
+    if (KB > 1) issue(1, 1);
+    {
+        const uint8_t* src = a.hs + (int64_t)tile * kPfBM * KB;   // [row][kb]
+        for (int i = tid; i < kPfBM * KB; i += 512) {
+            const int r = i / KB, kb = i - r * KB;
+            s_sa[kb * kPfBM + r] = src[i];
+        }
+        const uint8_t* sb = a.w2s + (int64_t)e * KB * NBS;
+        for (int i = tid; i < 2 * KB; i += 512) s_sb[i & 1][i >> 1] = sb[(i >> 1) * NBS + nb * 2 + (i & 1)];
+    }
 
     v4f acc[4][4];
 #pragma unroll
@@ -1663,44 +869,29 @@ __global__ __launch_bounds__(512, 1) void k_gemm2_pf8(G2Args a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    Pf8Loads R[NR];
-#pragma unroll
-    for (int r = 0; r < NR; ++r) load(min(r, KB - 1), R[r]);
-    store(R[0], buf[0]);
-    __syncthreads();
-
-    auto compute = [&](int kb, const uint8_t* cur) {
-        v8i af[4];
+    int s = 0;
+    for (int kb = 0; kb < KB; ++kb) {
+        if (kb + 1 < KB) wait_vm<6>(); else wait_vm<0>();
+        __syncthreads();
+        if (kb + 2 < KB) issue(kb + 2, s == 0 ? 2 : s - 1);
+        const uint8_t* cur = buf + s * kPfStage;
+        v8i af[4], bf[4];
         int sa[4];
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
             const int mf = wm * 4 + mi;
             af[mi] = lds_frag(cur + mf * kFragBytes, lane);
-            sa[mi] = s_sa[(mf * 16 + (lane & 15)) * KB + kb];
+            sa[mi] = s_sa[kb * kPfBM + mf * 16 + (lane & 15)];
         }
         const int sbv = s_sb[wn >> 1][kb];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const v8i b = lds_frag(cur + kPfStageA + (wn * 4 + j) * kFragBytes, lane);
+        for (int j = 0; j < 4; ++j) bf[j] = lds_frag(cur + kPfStageA + (wn * 4 + j) * kFragBytes, lane);
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi) acc[mi][j] = mfma_fp8(af[mi], b, acc[mi][j], sa[mi], sbv);
-        }
-    };
-    auto step = [&](int kb, const int ri, const int bi) {
-        load(min(kb + NR, KB - 1), R[ri]);
-        compute(kb, buf[bi]);
-        store(R[(ri + 1) % NR], buf[bi ^ 1]);
-        __syncthreads();
-    };
-    constexpr int U = NR == 3 ? 6 : (NR == 4 ? 4 : 2);
-    int kb = 0;
-    for (; kb + U <= KB; kb += U) {
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int u = 0; u < U; ++u) step(kb + u, u % NR, u & 1);
+            for (int mi = 0; mi < 4; ++mi) acc[mi][j] = mfma_fp8(af[mi], bf[j], acc[mi][j], sa[mi], sbv);
+        s = s == 2 ? 0 : s + 1;
     }
-#pragma unroll
-    for (int u = 0; u < U - 1; ++u)
-        if (kb + u < KB) step(kb + u, u % NR, u & 1);
 
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
@@ -1778,13 +969,15 @@ static hipError_t run_ffn_dec(const FfnArgs& f, const FfnPlan& p, const FfnWs& w
 static hipError_t run_ffn_pf(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid) {
     G1Args g1{f.xq, f.xs, f.T, f.k, f.H, f.I, f.counts, f.offsets, f.sorted_assign, w.tiles, w.ntiles, f.w13p, f.w13s,
               w.hq, w.hs};
-    hipLaunchKernelGGL((MOE_PF_GEMM1), dim3(f.I / kGroup, p.ntiles_max), dim3(MOE_PF_THREADS), 0, st, g1);
+    hipLaunchKernelGGL(k_gemm1_pf, dim3(ceil_div((int64_t)(f.I / kGroup) * p.ntiles_max, kXcds) * kXcds),
+                       dim3(512), 0, st, g1);
     if (mid) {
         const hipError_t e = hipEventRecord(mid, st);
         if (e != hipSuccess) return e;
     }
     G2Args g2{w.hq, w.hs, f.H, f.I, f.counts, f.offsets, w.tiles, w.ntiles, f.w2p, f.w2s, f.out, f.out_bf16};
-    hipLaunchKernelGGL((MOE_PF_GEMM2), dim3(f.H / 256, p.ntiles_max), dim3(MOE_PF_THREADS), 0, st, g2);
+    hipLaunchKernelGGL(k_gemm2_pf, dim3(ceil_div((int64_t)(f.H / 256) * p.ntiles_max, kXcds) * kXcds),
+                       dim3(512), 0, st, g2);
     return hipGetLastError();
 }
 

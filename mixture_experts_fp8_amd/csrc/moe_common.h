@@ -108,10 +108,16 @@ __device__ __forceinline__ void quant_group16(const uint16_t* __restrict__ src, 
 }
 
 // Raw buffer resource over [base, base + bytes): loads take one per-lane 32-bit offset
-// (VGPR) plus a wave-uniform offset (SGPR); reads past `bytes` return zero.
+// (VGPR) plus a wave-uniform offset (SGPR); reads past `bytes` return zero.  A resource
+// lives in scalar registers, so base and bytes must be wave-uniform; they are passed through
+// readfirstlane so the compiler knows it and never wraps the loads in a waterfall loop.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    void* ub = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
 // Cache policy of the weight-stream loads: 2 = non-temporal (each weight byte is read once

@@ -28,7 +28,9 @@ codes; encode agrees with a brute-force nearest-code search and with the torch c
 every representable value, every midpoint and its neighbours; UE8M0 round-trips all
 255 finite codes; the scale rule is checked against hand values and its invariant
 (amax / 2^e in (224, 448]); quantise-dequantise is the identity on groups built from
-representable values.
+representable values; the decision margin matches hand values (0 at a rounding midpoint
+and at a scale boundary) and no perturbation below it changes a code, while one just
+above it at the closest element does.
 """
 from __future__ import annotations
 
@@ -143,6 +145,36 @@ def quant_rows_128(v: np.ndarray):
     e = scale_exponent(np.abs(g).max(axis=2))
     q = quantize_group(g, e[:, :, None]).reshape(R, C)
     return q, ue8m0_encode(e)
+
+
+def decision_margin_rows_128(v: np.ndarray) -> np.ndarray:
+    """How far each row's quantisation decisions (``quant_rows_128``) are from flipping.
+
+    For a [R, C] array returns [R]: the smallest relative distance, over the row, from an
+    element's |v| / 2^e to the nearest E4M3 rounding midpoint (the value halfway between
+    two adjacent magnitudes, where round-to-nearest changes code), and from each group's
+    amax to the two scale boundaries 448 * 2^(e-1) and 448 * 2^e (where the scale rule
+    changes e).  A computation of v carrying relative error below this margin takes every
+    decision of the row the same way; zero elements take no rounding decision.  Rows of
+    all-zero groups get +inf."""
+    v = np.asarray(v, dtype=np.float64)
+    R, C = v.shape
+    if C % GROUP:
+        raise ValueError("columns must be a multiple of 128")
+    g = np.abs(v.reshape(R, C // GROUP, GROUP))
+    amax = g.max(axis=2)
+    e = scale_exponent(amax)
+    s = np.ldexp(g, -e[:, :, None])
+    mags = np.unique(np.abs(e4m3_decode_table()[np.isfinite(e4m3_decode_table())]))   # 0 .. 448
+    mids = (mags[1:] + mags[:-1]) / 2
+    i = np.clip(np.searchsorted(mids, s), 1, len(mids) - 1)
+    d = np.minimum(np.abs(s - mids[i - 1]), np.abs(s - mids[i]))
+    rel = np.where(s > 0, d / np.where(s > 0, s, 1.0), np.inf)
+    pos = amax > 0
+    lo = E4M3_MAX * np.ldexp(1.0, e - 1)
+    hi = E4M3_MAX * np.ldexp(1.0, e)
+    srel = np.where(pos, np.minimum(np.abs(amax / lo - 1), np.abs(amax / hi - 1)), np.inf)
+    return np.minimum(rel.min(axis=(1, 2)), srel.min(axis=1))
 
 
 def dequant_rows_128(q: np.ndarray, s: np.ndarray) -> np.ndarray:

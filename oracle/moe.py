@@ -74,7 +74,9 @@ class QuantizedExperts:
 def expert_ffn(xq_rows, xs_rows, q13, s13, q2, s2):
     """One expert on a stack of quantised rows.
 
-    Returns (o float64 [R, H], hq uint8 [R, I], hs uint8 [R, I/128])."""
+    Returns (o float64 [R, H], hq uint8 [R, I], hs uint8 [R, I/128], margin float64 [R]),
+    margin being the re-quantisation's decision margin per row
+    (``codec.decision_margin_rows_128``)."""
     x = codec.dequant_rows_128(xq_rows, xs_rows)
     w13 = codec.dequant_blocks_128(q13, s13)
     gu = x @ w13
@@ -82,7 +84,7 @@ def expert_ffn(xq_rows, xs_rows, q13, s13, q2, s2):
     h = silu(gu[:, :I]) * gu[:, I:]
     hq, hs = codec.quant_rows_128(h)
     o = codec.dequant_rows_128(hq, hs) @ codec.dequant_blocks_128(q2, s2)
-    return o, hq, hs
+    return o, hq, hs, codec.decision_margin_rows_128(h)
 
 
 def combine(o_flat: np.ndarray, weights: np.ndarray) -> np.ndarray:
@@ -98,7 +100,9 @@ def forward(x_f64, ids, weights, experts: QuantizedExperts, tokens=None):
     x_f64 [T, H]: exact values of the bfloat16 hidden state.  ids/weights [T, k].
     tokens: optional array of token indices; only those rows of y are computed.
     Returns a dict with y float64 [len(tokens), H], o [len(tokens)*k, H] in flat
-    (t, j) order, hq/hs by assignment, xq/xs of the tokens."""
+    (t, j) order, hq/hs by assignment, xq/xs of the tokens, and the re-quantisation
+    decision margin by assignment ("qmargin") and by token ("qmargin_tok", the smallest
+    over its k assignments)."""
     T, k = ids.shape
     tok = np.arange(T) if tokens is None else np.asarray(tokens)
     xq, xs = codec.quant_rows_128(x_f64[tok])
@@ -106,20 +110,23 @@ def forward(x_f64, ids, weights, experts: QuantizedExperts, tokens=None):
     n = len(tok)
     H = x_f64.shape[1]
     o = np.zeros((n * k, H))
+    qm = np.full(n * k, np.inf)
     hq = hs = None
     flat_ids = sub_ids.reshape(-1)
     for e in np.unique(flat_ids):
         rows = np.nonzero(flat_ids == e)[0]            # flat positions (t_local*k + j)
         q13, s13, q2, s2 = experts.get(int(e))
-        oe, hqe, hse = expert_ffn(xq[rows // k], xs[rows // k], q13, s13, q2, s2)
+        oe, hqe, hse, qme = expert_ffn(xq[rows // k], xs[rows // k], q13, s13, q2, s2)
         if hq is None:
             hq = np.zeros((n * k, hqe.shape[1]), dtype=np.uint8)
             hs = np.zeros((n * k, hse.shape[1]), dtype=np.uint8)
         o[rows] = oe
         hq[rows] = hqe
         hs[rows] = hse
+        qm[rows] = qme
     y = combine(o, np.asarray(weights, dtype=np.float64)[tok])
-    return {"y": y, "o": o, "hq": hq, "hs": hs, "xq": xq, "xs": xs, "tokens": tok}
+    return {"y": y, "o": o, "hq": hq, "hs": hs, "xq": xq, "xs": xs, "tokens": tok,
+            "qmargin": qm, "qmargin_tok": qm.reshape(n, k).min(axis=1)}
 
 
 def route_workload(inputs: dict, p: routing.RouteParams, prelude=None):

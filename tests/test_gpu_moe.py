@@ -29,6 +29,7 @@ SMALL = {
     "plain_tiles_H384": W.Workload(128, "bm128p", T=600, H=384, I=256, E=8, k=3),
     "staged_tiles_K_not_multiple_of_3": W.Workload(129, "bm128k", T=700, H=512, I=640, E=8, k=2),
     "bm128_path": W.Workload(124, "bm128", T=1100, H=256, I=384, E=8, k=2),
+    "staged_tiles_single_k_block": W.Workload(130, "bm128kb1", T=700, H=256, I=128, E=4, k=2),
     "sigmoid_groups": W.Workload(125, "grp", T=96, H=384, I=256, E=32, k=4, scoring="sigmoid", group_count=4,
                                  k_group=2, group_select_mode=1, routed_scaling_factor=2.5),
     "prelude_small": W.Workload(126, "pre", T=9, H=512, I=256, E=16, k=4, prelude=True),
@@ -66,7 +67,7 @@ def test_fused_small(name):
     ok = margin >= 1e-5
     assert np.array_equal(ids[ok], ids_ref[ok])
     assert counts.sum() == wl.T * wl.k
-    fro, mx = HN.assert_output_close(HN.bf16_to_f64(y)[ok], ref["y"][ok], name)
+    fro, mx = HN.assert_output_close(HN.bf16_to_f64(y)[ok], ref["y"][ok], name, ref["qmargin_tok"][ok])
     print(f"  rel fro {fro:.2e} rel max {mx:.2e}", flush=True)
 
 
@@ -81,11 +82,11 @@ def test_grouped_ffn_unit_cfg1():
     assert np.array_equal(r["topk_ids"].cpu().numpy(), ids_ref)
     pos = r["assign_pos"].cpu().numpy().astype(np.int64)
     got = eo.cpu().numpy().astype(np.float64)[pos]          # back to flat (t, j) order
-    HN.assert_output_close(got, ref["o"], "expert_out")
+    HN.assert_output_close(got, ref["o"], "expert_out", ref["qmargin"])
     eob = M.moe_grouped_ffn(xq, xs, r, w, wl.k, out_dtype=torch.bfloat16)
-    HN.assert_output_close(HN.bf16_to_f64(eob)[pos], ref["o"], "expert_out bf16")
+    HN.assert_output_close(HN.bf16_to_f64(eob)[pos], ref["o"], "expert_out bf16", ref["qmargin"])
     y = M.moe_combine(eo, r["assign_pos"], r["topk_weights"])
-    HN.assert_output_close(HN.bf16_to_f64(y), ref["y"], "combine")
+    HN.assert_output_close(HN.bf16_to_f64(y), ref["y"], "combine", ref["qmargin_tok"])
 
 
 def test_golden_hand_ffn_through_device():
@@ -118,7 +119,7 @@ def test_all_tokens_on_one_expert_and_empty_experts():
     ids_ref, w_ref, _ = omoe.route_workload({"logits": logits.numpy()}, HN.oracle_params(wl))
     assert np.array_equal(ids, ids_ref)
     ref = omoe.forward(xf, ids_ref, w_ref, HN.oracle_experts(wl, cache=16))
-    HN.assert_output_close(HN.bf16_to_f64(y), ref["y"], "skew")
+    HN.assert_output_close(HN.bf16_to_f64(y), ref["y"], "skew", ref["qmargin_tok"])
 
 
 def test_determinism_and_row_independence():
@@ -143,7 +144,7 @@ def test_fused_workload_full(cfg):
     ref, ids_ref, _, margin = _oracle(wl, workers=int(os.environ.get("ORACLE_WORKERS", "8")))
     ok = margin >= 1e-5
     assert np.array_equal(ids[ok], ids_ref[ok])
-    fro, mx = HN.assert_output_close(HN.bf16_to_f64(y)[ok], ref["y"][ok], f"cfg{cfg}")
+    fro, mx = HN.assert_output_close(HN.bf16_to_f64(y)[ok], ref["y"][ok], f"cfg{cfg}", ref["qmargin_tok"][ok])
     print(f"  rel fro {fro:.2e} rel max {mx:.2e} active experts {(counts > 0).sum()}", flush=True)
 
 
@@ -156,5 +157,5 @@ def test_fused_workload_sampled(cfg, ntok):
     ref, ids_ref, _, margin = _oracle(wl, tokens=tokens, workers=int(os.environ.get("ORACLE_WORKERS", "8")))
     assert np.array_equal(ids[margin >= 1e-6], ids_ref[margin >= 1e-6])
     assert counts.sum() == wl.T * wl.k
-    fro, mx = HN.assert_output_close(HN.bf16_to_f64(y)[tokens], ref["y"], f"cfg{cfg}")
+    fro, mx = HN.assert_output_close(HN.bf16_to_f64(y)[tokens], ref["y"], f"cfg{cfg}", ref["qmargin_tok"])
     print(f"  rel fro {fro:.2e} rel max {mx:.2e}", flush=True)

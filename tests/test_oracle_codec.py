@@ -132,3 +132,47 @@ def test_quant_blocks_scales_per_block():
 def test_negative_underflow_keeps_sign():
     q = codec.e4m3_encode(np.array([-1e-6, 1e-6, -0.0, 0.0]))
     assert list(q) == [0x80, 0x00, 0x80, 0x00]
+
+
+def test_decision_margin_hand_values():
+    # 256 and 1.0 sit 2^-5 (relative) below the midpoints 248 and 0.96875 to their lower
+    # neighbours 240 and 0.9375; the scale boundaries 224 and 448 are farther away
+    row = np.ones(128)
+    row[0] = 256.0
+    assert codec.decision_margin_rows_128(row[None])[0] == 2.0 ** -5
+    mid = row.copy()
+    mid[5] = 1.0625                       # halfway between 1.0 and 1.125
+    assert codec.decision_margin_rows_128(mid[None])[0] == 0.0
+    for amax in (448.0, 448.0 * 8, 448.0 * 2.0 ** -20):   # amax on a scale boundary
+        b = row / 256.0 * amax
+        assert codec.decision_margin_rows_128(b[None])[0] == 0.0
+    zero = np.zeros((1, 256))
+    assert codec.decision_margin_rows_128(zero)[0] == np.inf
+    two = np.concatenate([np.zeros(128), row])[None]     # the zero group takes no decision
+    assert codec.decision_margin_rows_128(two)[0] == 2.0 ** -5
+    assert codec.decision_margin_rows_128(np.concatenate([row, mid])[None])[0] == 0.0
+
+
+def test_decision_margin_bounds_single_element_perturbations():
+    # brute force: no single element moved by a relative amount just below the margin
+    # changes a code or a scale; some element moved just above it does
+    rng = np.random.default_rng(7)
+    R, C = 6, 128
+    v = rng.standard_normal((R, C)) * np.exp2(rng.integers(-6, 7, size=(R, 1)))
+    m = codec.decision_margin_rows_128(v)
+    q0, s0 = codec.quant_rows_128(v)
+    for r in range(R):
+        changed_above = False
+        for f in (1 - 1e-6, 1 + 1e-6):
+            t = m[r] * f
+            for i in range(C):
+                for sign in (-1.0, 1.0):
+                    w = v[r].copy()
+                    w[i] *= 1 + sign * t
+                    q, s = codec.quant_rows_128(w[None])
+                    same = np.array_equal(q[0], q0[r]) and np.array_equal(s[0], s0[r])
+                    if f < 1:
+                        assert same, (r, i, sign)
+                    elif not same:
+                        changed_above = True
+        assert changed_above, r
