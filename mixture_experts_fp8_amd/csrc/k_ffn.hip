@@ -726,8 +726,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pf(G1Args a) {
     };
     issue(0, 0);
     if (KB > 1) issue(1, 1);
+    if (KB > 2) issue(2, 2);
 
-    {   // scales, while the first two blocks load
+    {   // scales, while the first blocks load
         const int r = tid >> 2, q = tid & 3;
         const int tok = a.sorted_assign[rowbase + min(r, nvalid - 1)] / a.k;
         const uint8_t* src = a.xs + (int64_t)tok * KB;
@@ -745,29 +746,51 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pf(G1Args a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    int s = 0;
-    for (int kb = 0; kb < KB; ++kb) {
-        // block kb has landed once at most the next block's 6 DMAs of this thread are pending
-        if (kb + 1 < KB) wait_vm<6>(); else wait_vm<0>();
-        __syncthreads();   // everyone's block kb is in LDS; everyone is done with stage (kb + 2) % 3
-        if (kb + 2 < KB) issue(kb + 2, s == 0 ? 2 : s - 1);
-        const uint8_t* cur = buf + s * kPfStage;
-        v8i af[4], bf[4];
-        int sa[4];
+    // Fragments of one K block in registers: read from LDS one step before the MFMAs use
+    // them, so the reads of block kb+1 overlap the matrix-core work on block kb.
+    struct Frags {
+        v8i a[4], b[4];
+        int sa[4], sg, su;
+    };
+    auto read = [&](int kb, int st, Frags& F) {
+        const uint8_t* cur = buf + st * kPfStage;
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
             const int mf = wm * 4 + mi;
-            af[mi] = lds_frag(cur + mf * kFragBytes, lane);
-            sa[mi] = s_sa[kb * kPfBM + mf * 16 + (lane & 15)];
+            F.a[mi] = lds_frag(cur + mf * kFragBytes, lane);
+            F.sa[mi] = s_sa[kb * kPfBM + mf * 16 + (lane & 15)];
         }
-        const int sg = s_sg[kb], su = s_su[kb];
+        F.sg = s_sg[kb];
+        F.su = s_su[kb];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bf[j] = lds_frag(cur + kPfStageA + (j < 2 ? 2 * wn + j : 6 + 2 * wn + j) * kFragBytes, lane);
+        for (int j = 0; j < 4; ++j) F.b[j] = lds_frag(cur + kPfStageA + (j < 2 ? 2 * wn + j : 6 + 2 * wn + j) * kFragBytes, lane);
+    };
+    // step kb (stage st holds block kb, whose fragments F already hold or are receiving):
+    // wait until block kb+1 has landed everywhere (the barrier also finds every wave done
+    // reading stage st), refill stage st with block kb+3, read block kb+1 into G, then the
+    // 16 MFMAs of block kb.
+    auto step = [&](int kb, int st, Frags& F, Frags& G) {
+        if (kb + 2 < KB) wait_vm<6>(); else wait_vm<0>();
+        __syncthreads();
+        if (kb + 3 < KB) issue(kb + 3, st);
+        if (kb + 1 < KB) read(kb + 1, st == 2 ? 0 : st + 1, G);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi) acc[mi][j] = mfma_fp8(af[mi], bf[j], acc[mi][j], sa[mi], j < 2 ? sg : su);
-        s = s == 2 ? 0 : s + 1;
+            for (int mi = 0; mi < 4; ++mi) acc[mi][j] = mfma_fp8(F.a[mi], F.b[j], acc[mi][j], F.sa[mi], j < 2 ? F.sg : F.su);
+    };
+    if (KB > 2) wait_vm<12>(); else if (KB > 1) wait_vm<6>(); else wait_vm<0>();
+    __syncthreads();
+    Frags F0, F1;
+    read(0, 0, F0);
+    int st = 0;
+    for (int kb = 0; kb < KB; kb += 2) {
+        step(kb, st, F0, F1);
+        st = st == 2 ? 0 : st + 1;
+        if (kb + 1 < KB) {
+            step(kb + 1, st, F1, F0);
+            st = st == 2 ? 0 : st + 1;
+        }
     }
 
     float hv[4][2][4];
@@ -853,6 +876,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm2_pf(G2Args a) {
     };
     issue(0, 0);
     if (KB > 1) issue(1, 1);
+    if (KB > 2) issue(2, 2);
     {
         const uint8_t* src = a.hs + (int64_t)tile * kPfBM * KB;   // [row][kb]
         for (int i = tid; i < kPfBM * KB; i += 512) {
@@ -863,34 +887,51 @@ __global__ __launch_bounds__(512, 1) void k_gemm2_pf(G2Args a) {
         for (int i = tid; i < 2 * KB; i += 512) s_sb[i & 1][i >> 1] = sb[(i >> 1) * NBS + nb * 2 + (i & 1)];
     }
 
+
     v4f acc[4][4];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    int s = 0;
-    for (int kb = 0; kb < KB; ++kb) {
-        if (kb + 1 < KB) wait_vm<6>(); else wait_vm<0>();
-        __syncthreads();
-        if (kb + 2 < KB) issue(kb + 2, s == 0 ? 2 : s - 1);
-        const uint8_t* cur = buf + s * kPfStage;
-        v8i af[4], bf[4];
-        int sa[4];
+    struct Frags {
+        v8i a[4], b[4];
+        int sa[4], sb;
+    };
+    auto read = [&](int kb, int st, Frags& F) {
+        const uint8_t* cur = buf + st * kPfStage;
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
             const int mf = wm * 4 + mi;
-            af[mi] = lds_frag(cur + mf * kFragBytes, lane);
-            sa[mi] = s_sa[kb * kPfBM + mf * 16 + (lane & 15)];
+            F.a[mi] = lds_frag(cur + mf * kFragBytes, lane);
+            F.sa[mi] = s_sa[kb * kPfBM + mf * 16 + (lane & 15)];
         }
-        const int sbv = s_sb[wn >> 1][kb];
+        F.sb = s_sb[wn >> 1][kb];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bf[j] = lds_frag(cur + kPfStageA + (wn * 4 + j) * kFragBytes, lane);
+        for (int j = 0; j < 4; ++j) F.b[j] = lds_frag(cur + kPfStageA + (wn * 4 + j) * kFragBytes, lane);
+    };
+    auto step = [&](int kb, int st, Frags& F, Frags& G) {
+        if (kb + 2 < KB) wait_vm<6>(); else wait_vm<0>();
+        __syncthreads();
+        if (kb + 3 < KB) issue(kb + 3, st);
+        if (kb + 1 < KB) read(kb + 1, st == 2 ? 0 : st + 1, G);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi) acc[mi][j] = mfma_fp8(af[mi], bf[j], acc[mi][j], sa[mi], sbv);
-        s = s == 2 ? 0 : s + 1;
+            for (int mi = 0; mi < 4; ++mi) acc[mi][j] = mfma_fp8(F.a[mi], F.b[j], acc[mi][j], F.sa[mi], F.sb);
+    };
+    if (KB > 2) wait_vm<12>(); else if (KB > 1) wait_vm<6>(); else wait_vm<0>();
+    __syncthreads();
+    Frags F0, F1;
+    read(0, 0, F0);
+    int st = 0;
+    for (int kb = 0; kb < KB; kb += 2) {
+        step(kb, st, F0, F1);
+        st = st == 2 ? 0 : st + 1;
+        if (kb + 1 < KB) {
+            step(kb + 1, st, F1, F0);
+            st = st == 2 ? 0 : st + 1;
+        }
     }
 
 #pragma unroll
