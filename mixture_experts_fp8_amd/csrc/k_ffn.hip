@@ -75,6 +75,7 @@ struct G1Args {
     const uint8_t* w13s;
     uint8_t* hq;
     uint8_t* hs;
+    int ord;    // work order of the 128-row-tile kernels: 1 super-tiles (ord_item), 0 column blocks
 };
 
 __device__ __forceinline__ v8i lds_frag(const uint8_t* base, int lane) {
@@ -280,6 +281,7 @@ struct G2Args {
     const uint8_t* w2s;
     void* out;
     int out_bf16;
+    int ord;
 };
 
 // down GEMM: wave (wm, wn) computes MFW m-frags x NFW column frags; the workgroup covers
@@ -627,10 +629,11 @@ constexpr int kXcds = 8;
 #endif
 constexpr int kPfGroupTiles = MOE_PF_GROUP_TILES;
 
-__device__ __forceinline__ bool pf_work_item(int ncol, int ntiles, int& tile, int& col) {
+__device__ __forceinline__ bool pf_work_item(int ord, int ncol, int ntiles, int& tile, int& col) {
+    const int L = blockIdx.x;
+    if (ord) return ord_item(L % kXcds, L / kXcds, ntiles, ncol, tile, col);
     const int total = ntiles * ncol;
     const int per = (total + kXcds - 1) / kXcds;
-    const int L = blockIdx.x;
     const int w = (L % kXcds) * per + L / kXcds;
     if (L / kXcds >= per || w >= total) return false;
     const int sb = w / (kPfGroupTiles * ncol), r = w - sb * kPfGroupTiles * ncol;
@@ -683,7 +686,7 @@ __device__ __forceinline__ void wait_vm() {
 
 __global__ __launch_bounds__(512, 1) void k_gemm1_pf(G1Args a) {
     int ib, tile;
-    if (!pf_work_item(a.I / kGroup, __builtin_amdgcn_readfirstlane(*a.ntiles), tile, ib)) return;
+    if (!pf_work_item(a.ord, a.I / kGroup, __builtin_amdgcn_readfirstlane(*a.ntiles), tile, ib)) return;
     const int2 te = a.tiles[tile];
     const int e = __builtin_amdgcn_readfirstlane(te.x), m0 = __builtin_amdgcn_readfirstlane(te.y);
     const int nvalid = min(kPfBM, a.counts[e] - m0);
@@ -823,8 +826,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pf(G1Args a) {
             for (int jj = 0; jj < 2; ++jj)
                 s_h[row * 128 + (2 * wn + jj) * 16 + (lane & 15)] =
                     (uint8_t)(cvt2_e4m3(ldexpf(hv[mi][jj][i], -ex), 0.f) & 0xFFu);
-            if (wn == 0 && (lane & 15) == 0)
-                a.hs[((int64_t)tile * kPfBM + row) * (a.I / kGroup) + ib] = (uint8_t)(ex + 127);
+            if (wn == 0 && (lane & 15) == 0)   // [tile][kb][row % 16][row / 16]
+                a.hs[(((int64_t)tile * (a.I / kGroup) + ib) * 16 + (row & 15)) * 8 + (row >> 4)] = (uint8_t)(ex + 127);
         }
     }
     __syncthreads();
@@ -838,7 +841,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pf(G1Args a) {
 
 __global__ __launch_bounds__(512, 1) void k_gemm2_pf(G2Args a) {
     int nb, tile;
-    if (!pf_work_item(a.H / 256, __builtin_amdgcn_readfirstlane(*a.ntiles), tile, nb)) return;
+    if (!pf_work_item(a.ord, a.H / 256, __builtin_amdgcn_readfirstlane(*a.ntiles), tile, nb)) return;
     const int2 te = a.tiles[tile];
     const int e = __builtin_amdgcn_readfirstlane(te.x), m0 = __builtin_amdgcn_readfirstlane(te.y);
     const int nvalid = min(kPfBM, a.counts[e] - m0);
@@ -878,10 +881,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm2_pf(G2Args a) {
     if (KB > 1) issue(1, 1);
     if (KB > 2) issue(2, 2);
     {
-        const uint8_t* src = a.hs + (int64_t)tile * kPfBM * KB;   // [row][kb]
+        const uint8_t* src = a.hs + (int64_t)tile * kPfBM * KB;   // [kb][row % 16][row / 16]
         for (int i = tid; i < kPfBM * KB; i += 512) {
-            const int r = i / KB, kb = i - r * KB;
-            s_sa[kb * kPfBM + r] = src[i];
+            const int kb = i >> 7, w = i & 127;
+            s_sa[kb * kPfBM + (w & 7) * 16 + (w >> 3)] = src[i];
         }
         const uint8_t* sb = a.w2s + (int64_t)e * KB * NBS;
         for (int i = tid; i < 2 * KB; i += 512) s_sb[i & 1][i >> 1] = sb[(i >> 1) * NBS + nb * 2 + (i & 1)];
@@ -958,6 +961,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm2_pf(G2Args a) {
 #define MOE_DEC_MAX_AVG_ROWS 24
 #endif
 
+// The super-tile order pays off once the tiles fill several of its 64-tile windows.
+int ffn_super_tile_order(int ntiles_max) { return ntiles_max >= 512 ? 1 : 0; }
+
 FfnPlan ffn_plan(int T, int k, int E) {
     const int64_t A = (int64_t)T * k;
     const int64_t avg = A / E;
@@ -968,24 +974,27 @@ FfnPlan ffn_plan(int T, int k, int E) {
 }
 
 // workspace: tiles [ntiles_max] int2 | ntiles int | hq [ntiles_max*BM, I] | hs [ntiles_max*BM, I/128]
+//            | (128-row tiles) down-GEMM weight-scale table [E][H/128][I/128] u32
 size_t ffn_workspace_bytes(int T, int H, int I, int E, int k) {
-    (void)H;
     const FfnPlan p = ffn_plan(T, k, E);
     const size_t rows = (size_t)p.ntiles_max * p.BM;
-    return align256((size_t)p.ntiles_max * 8) + align256(4) + align256(rows * I) + align256(rows * (I / kGroup));
+    size_t n = align256((size_t)p.ntiles_max * 8) + align256(4) + align256(rows * I) + align256(rows * (I / kGroup));
+    if (p.BM == 128) n += align256(ffn_rb_scale_table_bytes(H, I, E));
+    return n;
 }
 
 template <int MFW, int NFW1, int NFW2, int WM, int WN, int PF1, int PF2>
 static hipError_t run_ffn(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid) {
     G1Args g1{f.xq, f.xs, f.T, f.k, f.H, f.I, f.counts, f.offsets, f.sorted_assign, w.tiles, w.ntiles, f.w13p, f.w13s,
-              w.hq, w.hs};
+              w.hq, w.hs, ffn_super_tile_order(p.ntiles_max)};
     hipLaunchKernelGGL((k_gemm1<MFW, NFW1, WM, WN, PF1>), dim3(p.ntiles_max, f.I / kGroup), dim3(64 * WM * WN), 0,
                        st, g1);
     if (mid) {
         const hipError_t e = hipEventRecord(mid, st);
         if (e != hipSuccess) return e;
     }
-    G2Args g2{w.hq, w.hs, f.H, f.I, f.counts, f.offsets, w.tiles, w.ntiles, f.w2p, f.w2s, f.out, f.out_bf16};
+    G2Args g2{w.hq, w.hs, f.H, f.I, f.counts, f.offsets, w.tiles, w.ntiles, f.w2p, f.w2s, f.out, f.out_bf16,
+              ffn_super_tile_order(p.ntiles_max)};
     const int ncols = 16 * NFW2 * WN;
     hipLaunchKernelGGL((k_gemm2<MFW, NFW2, WM, WN, PF2>), dim3(p.ntiles_max, f.H / ncols), dim3(64 * WM * WN), 0,
                        st, g2);
@@ -995,13 +1004,14 @@ static hipError_t run_ffn(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hi
 template <int NFW1, int WN1, int PF1, int NFW2, int WN2, int PF2>
 static hipError_t run_ffn_dec(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid) {
     G1Args g1{f.xq, f.xs, f.T, f.k, f.H, f.I, f.counts, f.offsets, f.sorted_assign, w.tiles, w.ntiles, f.w13p, f.w13s,
-              w.hq, w.hs};
+              w.hq, w.hs, ffn_super_tile_order(p.ntiles_max)};
     hipLaunchKernelGGL((k_gemm1_dec<NFW1, WN1, PF1>), dim3(p.ntiles_max, f.I / kGroup), dim3(64 * WN1), 0, st, g1);
     if (mid) {
         const hipError_t e = hipEventRecord(mid, st);
         if (e != hipSuccess) return e;
     }
-    G2Args g2{w.hq, w.hs, f.H, f.I, f.counts, f.offsets, w.tiles, w.ntiles, f.w2p, f.w2s, f.out, f.out_bf16};
+    G2Args g2{w.hq, w.hs, f.H, f.I, f.counts, f.offsets, w.tiles, w.ntiles, f.w2p, f.w2s, f.out, f.out_bf16,
+              ffn_super_tile_order(p.ntiles_max)};
     hipLaunchKernelGGL((k_gemm2_dec<NFW2, WN2, PF2>), dim3(p.ntiles_max, f.H / (16 * NFW2 * WN2)), dim3(64 * WN2), 0,
                        st, g2);
     return hipGetLastError();
@@ -1009,16 +1019,23 @@ static hipError_t run_ffn_dec(const FfnArgs& f, const FfnPlan& p, const FfnWs& w
 
 static hipError_t run_ffn_pf(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid) {
     G1Args g1{f.xq, f.xs, f.T, f.k, f.H, f.I, f.counts, f.offsets, f.sorted_assign, w.tiles, w.ntiles, f.w13p, f.w13s,
-              w.hq, w.hs};
-    hipLaunchKernelGGL(k_gemm1_pf, dim3(ceil_div((int64_t)(f.I / kGroup) * p.ntiles_max, kXcds) * kXcds),
-                       dim3(512), 0, st, g1);
+              w.hq, w.hs, ffn_super_tile_order(p.ntiles_max)};
+    const int grid1 = g1.ord ? kXcds * ord_ranks(p.ntiles_max, f.I / kGroup)
+                             : (int)(ceil_div((int64_t)(f.I / kGroup) * p.ntiles_max, kXcds) * kXcds);
+    hipLaunchKernelGGL(k_gemm1_pf, dim3(grid1), dim3(512), 0, st, g1);
     if (mid) {
         const hipError_t e = hipEventRecord(mid, st);
         if (e != hipSuccess) return e;
     }
-    G2Args g2{w.hq, w.hs, f.H, f.I, f.counts, f.offsets, w.tiles, w.ntiles, f.w2p, f.w2s, f.out, f.out_bf16};
-    hipLaunchKernelGGL(k_gemm2_pf, dim3(ceil_div((int64_t)(f.H / 256) * p.ntiles_max, kXcds) * kXcds),
-                       dim3(512), 0, st, g2);
+    G2Args g2{w.hq, w.hs, f.H, f.I, f.counts, f.offsets, w.tiles, w.ntiles, f.w2p, f.w2s, f.out, f.out_bf16,
+              ffn_super_tile_order(p.ntiles_max)};
+#ifndef MOE_NO_RB
+    // the persistent down GEMM (k_ffn_rb.hip) where its item tables fit
+    if (ffn_rb_supported(f.H, f.I, f.E, p.ntiles_max)) return launch_gemm2_rb(f, w, p.ntiles_max, g2.ord, st);
+#endif
+    const int grid2 = g2.ord ? kXcds * ord_ranks(p.ntiles_max, f.H / 256)
+                             : (int)(ceil_div((int64_t)(f.H / 256) * p.ntiles_max, kXcds) * kXcds);
+    hipLaunchKernelGGL(k_gemm2_pf, dim3(grid2), dim3(512), 0, st, g2);
     return hipGetLastError();
 }
 
@@ -1034,6 +1051,8 @@ FfnWs carve_ffn_ws(const FfnArgs& f, void* ws) {
     r.hq = w;
     w += align256(rows * f.I);
     r.hs = w;
+    w += align256(rows * (f.I / kGroup));
+    r.bs = p.BM == 128 ? reinterpret_cast<uint32_t*>(w) : nullptr;
     return r;
 }
 

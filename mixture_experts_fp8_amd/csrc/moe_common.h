@@ -145,4 +145,28 @@ __device__ __forceinline__ v8i buf_a32(rsrc_t r, uint32_t voff, uint32_t soff) {
 
 __host__ __device__ constexpr inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Work order of the 128-row-tile GEMMs (items = tile x column block).  The workgroups of
+// one XCD share its L2; all XCDs share the Infinity Cache.  Items come in super-tiles of
+// 8 consecutive tiles x 4 column blocks (32 items, one per workgroup running on an XCD, so
+// an XCD fetches 8 A tiles and 4 weight column blocks for 32 items).  Super-tiles go to the
+// XCDs in windows of 8 consecutive tile groups: within a window XCD x takes tile group x, and
+// all XCDs step through the column groups together, so at any time the 8 XCDs work on 64
+// consecutive tiles (mostly one expert) and the same weight columns, which the Infinity
+// Cache then serves from one HBM read.  Rank r of XCD x -> item (tile, col); false for the
+// holes past the last tile or column.
+constexpr int kOrdTiles = 8, kOrdCols = 4, kOrdXcds = 8, kOrdSlots = kOrdTiles * kOrdCols;
+__host__ __device__ inline int ord_ranks(int ntiles, int ncol) {
+    const int ngroups = (ntiles + kOrdTiles - 1) / kOrdTiles;
+    const int nwin = (ngroups + kOrdXcds - 1) / kOrdXcds;
+    return nwin * ((ncol + kOrdCols - 1) / kOrdCols) * kOrdSlots;
+}
+__host__ __device__ inline bool ord_item(int x, int r, int ntiles, int ncol, int& tile, int& col) {
+    const int ncg = (ncol + kOrdCols - 1) / kOrdCols;
+    const int s = r / kOrdSlots, j = r - s * kOrdSlots;
+    const int win = s / ncg, cg = s - win * ncg;
+    tile = (win * kOrdXcds + x) * kOrdTiles + j % kOrdTiles;
+    col = cg * kOrdCols + j / kOrdTiles;
+    return tile < ntiles && col < ncol;
+}
+
 }  // namespace moe

@@ -72,12 +72,19 @@ struct FfnWs {
     int32_t* ntiles;
     uint8_t* hq;
     uint8_t* hs;
+    uint32_t* bs;        // 128-row tiles: down-GEMM weight-block scales per [expert][column block][kb]
 };
 FfnWs carve_ffn_ws(const FfnArgs& a, void* ws);
 // `mid`: optional event recorded between the gate+up and the down GEMM; tiles_ready: the
 // tile list in the workspace was already written (by launch_dispatch)
 hipError_t launch_grouped_ffn(const FfnArgs& a, void* ws, hipStream_t st, hipEvent_t mid = nullptr,
                               bool tiles_ready = false);
+
+int ffn_super_tile_order(int ntiles_max);
+// persistent down GEMM for 128-row tiles (k_ffn_rb.hip)
+bool ffn_rb_supported(int H, int I, int E, int ntiles_max);
+size_t ffn_rb_scale_table_bytes(int H, int I, int E);
+hipError_t launch_gemm2_rb(const FfnArgs& f, const FfnWs& w, int ntiles_max, int ord, hipStream_t st);
 
 hipError_t launch_combine(const void* eo, int bf16, const int32_t* pos, const float* w, int T, int k, int H,
                           uint16_t* y, hipStream_t st);
