@@ -304,25 +304,57 @@ __device__ int block_inclusive_scan_1024(int v, int* s_tmp /*[16]*/) {
 }
 
 // One workgroup: chunk_counts -> per-chunk bases (offsets[e] + earlier chunks), counts, offsets.
-__global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ cc, int nchunks, int E,
+// gpe = 1024 / E' threads share an expert (E' = E rounded up to a power of two); thread
+// (g, e) owns the contiguous chunks [g * cpt, (g + 1) * cpt), so its loads are independent
+// of one another; the per-thread sums are scanned across g, then the expert totals across e.
+__global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ cc, int nchunks, int E, int Ep,
                                                int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
     __shared__ int s_tmp[16];
-    const int e = threadIdx.x;
-    int run = 0;
-    if (e < E) {
-        for (int c = 0; c < nchunks; ++c) {
-            const int v = cc[(int64_t)c * E + e];
-            cc[(int64_t)c * E + e] = run;
-            run += v;
+    __shared__ int s_part[1024];
+    const int gpe = 1024 / Ep, e = threadIdx.x % Ep, g = threadIdx.x / Ep;
+    const int cpt = (nchunks + gpe - 1) / gpe, c0 = g * cpt, c1 = min(nchunks, c0 + cpt);
+    const bool act = e < E;
+    int sum = 0;
+    if (act) {
+        for (int c = c0; c < c1; c += 16) {
+            int v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v[u] = c + u < c1 ? cc[(int64_t)(c + u) * E + e] : 0;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) sum += v[u];
         }
     }
-    const int incl = block_inclusive_scan_1024(e < E ? run : 0, s_tmp);
-    const int off = incl - (e < E ? run : 0);
-    if (e < E) {
-        counts[e] = run;
-        offsets[e] = off;
-        if (e == E - 1) offsets[E] = incl;
-        for (int c = 0; c < nchunks; ++c) cc[(int64_t)c * E + e] += off;
+    s_part[threadIdx.x] = sum;
+    __syncthreads();
+    int before = 0, run = 0;   // this thread's chunks start after `before` of expert e's ids
+    for (int h = 0; h < gpe; ++h) {
+        const int x = s_part[h * Ep + e];
+        before += h < g ? x : 0;
+        run += x;
+    }
+    // expert offsets: scan of the totals over e (one contributor per expert: g == 0)
+    const int incl = block_inclusive_scan_1024(act && g == 0 ? run : 0, s_tmp);
+    __syncthreads();
+    if (g == 0) s_part[e] = incl - (act ? run : 0);
+    __syncthreads();
+    const int off = s_part[e];
+    if (act) {
+        if (g == 0) {
+            counts[e] = run;
+            offsets[e] = off;
+            if (e == E - 1) offsets[E] = off + run;
+        }
+        int p = off + before;
+        for (int c = c0; c < c1; c += 16) {
+            int v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v[u] = c + u < c1 ? cc[(int64_t)(c + u) * E + e] : 0;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                if (c + u < c1) cc[(int64_t)(c + u) * E + e] = p;
+                p += v[u];
+            }
+        }
     }
 }
 
@@ -523,7 +555,9 @@ hipError_t launch_dispatch(const int32_t* ids, int A, int E, int32_t* chunk_ws, 
     }
     const int nchunks = (int)ceil_div(A, kScatterChunk);
     hipLaunchKernelGGL(k_hist, dim3(nchunks), dim3(256), (size_t)E * 4, st, ids, A, E, chunk_ws);
-    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, chunk_ws, nchunks, E, counts, offsets);
+    int Ep = 1;
+    while (Ep < E) Ep <<= 1;
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, chunk_ws, nchunks, E, Ep, counts, offsets);
     hipLaunchKernelGGL(k_scatter, dim3(nchunks), dim3(256), (size_t)4 * E * 4, st, ids, A, E, nbits, chunk_ws,
                        sorted_assign, assign_pos);
     if (tiles) return launch_tiles(counts, E, BM, tiles, ntiles, st);

@@ -154,10 +154,30 @@ def test_dispatch_of_given_ids_with_skew_and_empty_experts():
     # every token on expert 3 first, most experts empty; more than one dispatch chunk
     T, k, E = 3000, 4, 40
     r = np.random.default_rng(1)
+    print("dispatch skew", T, k, E, flush=True)
     ids = np.stack([np.concatenate([[3], r.choice([e for e in range(E) if e != 3], k - 1, replace=False)])
                     for _ in range(T)]).astype(np.int32)
     ids[ids > 30] = 7                     # experts 31..39 empty
     ids[:, 1:] = np.where(ids[:, 1:] == 3, 8, ids[:, 1:])
+    w = r.uniform(0, 1, (T, k)).astype(np.float32)
+    got = M.moe_route(M.route_params(E, k), T, topk_ids=torch.from_numpy(ids).to(DEV),
+                      topk_weights=torch.from_numpy(w).to(DEV), device=DEV)
+    counts, offsets, sa, ap = orouting.permute(ids, E)
+    assert np.array_equal(got["expert_counts"].cpu().numpy(), counts)
+    assert np.array_equal(got["expert_offsets"].cpu().numpy(), offsets)
+    assert np.array_equal(got["sorted_assign"].cpu().numpy(), sa)
+    assert np.array_equal(got["assign_pos"].cpu().numpy(), ap)
+
+
+@pytest.mark.parametrize("T,k,E", [(75000, 4, 100), (20000, 8, 1024), (5000, 1, 3), (40000, 6, 256)])
+def test_dispatch_many_chunks(T, k, E):
+    # hundreds of dispatch chunks, expert counts that are not powers of two, E = 1024, k = 1:
+    # the chunk-parallel scan and the scatter must still give the stable counting sort
+    print("dispatch chunks", T, k, E, flush=True)
+    r = np.random.default_rng(T + E)
+    p = r.zipf(1.3, size=E).astype(np.float64)
+    p /= p.sum()
+    ids = np.stack([r.choice(E, k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
     w = r.uniform(0, 1, (T, k)).astype(np.float32)
     got = M.moe_route(M.route_params(E, k), T, topk_ids=torch.from_numpy(ids).to(DEV),
                       topk_weights=torch.from_numpy(w).to(DEV), device=DEV)
