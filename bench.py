@@ -33,7 +33,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense FP8 matrix, TFLOP/s
 LAYERS = 4
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["mixture_experts_fp8_amd/csrc/k_ffn.hip", "mixture_experts_fp8_amd/csrc/moe_common.h"]
+KERNEL_SOURCES = ["mixture_experts_fp8_amd/csrc/k_ffn.hip", "mixture_experts_fp8_amd/csrc/k_ffn_rb.hip",
+                  "mixture_experts_fp8_amd/csrc/k_mx.hip", "mixture_experts_fp8_amd/csrc/moe_common.h"]
 
 
 def parse():
@@ -45,6 +46,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0, help="0: the workload's own default sample")
     ap.add_argument("--expert-out-bf16", action="store_true", help="keep per-assignment expert outputs in bf16")
+    ap.add_argument("--quant", default="fp8", choices=["fp8", "mxfp8", "w4a8"],
+                    help="fp8: E4M3 with 128-element scales (default); mxfp8: 32-element scales; "
+                         "w4a8: E2M1 weights with MXFP8 activations")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (a known-size kernel for HBM counter calibration)")
     return ap.parse_args()
@@ -87,30 +91,36 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def stage_bytes_flops(wl, counts: np.ndarray, eo_bytes: int):
+# bytes per weight element and elements per scale byte: (weights, activation groups, weight groups)
+SCHEME_BYTES = {"fp8": (1.0, 128, 128 * 128), "mxfp8": (1.0, 32, 32), "w4a8": (0.5, 32, 32)}
+
+
+def stage_bytes_flops(wl, counts: np.ndarray, eo_bytes: int, quant: str = "fp8"):
     """Algorithmic HBM bytes and FP8 flops per launch of the two GEMM stages.
 
-    gate+up: every active expert's w13 once (H*2I bytes + (H/128)*(2I/128) scale bytes),
-    each token's quantised row once (H + H/128), each assignment's hq row written once
-    (I + I/128).  down: every active expert's w2 once (I*H + (I/128)*(H/128)), each hq
-    row read once (I + I/128), each assignment's output row written once (H * eo_bytes).
+    gate+up: every active expert's w13 once (H*2I weight elements at wb bytes each plus
+    one scale byte per weight group), each token's quantised row once (H + H/ga), each
+    assignment's hq row written once (I + I/ga).  down: every active expert's w2 once, each
+    hq row read once, each assignment's output row written once (H * eo_bytes).  wb = 1 for
+    E4M3 weights and 0.5 for E2M1; groups of ga = 128 (or 32) activations and gw = 128 x 128
+    (or 32) weights per scale byte.
     """
+    wb, ga, gw = SCHEME_BYTES[quant]
     H, I, T, A = wl.H, wl.I, wl.T, wl.T * wl.k
     n_act = int((counts > 0).sum())
-    s13 = (H // 128) * (2 * I // 128)
-    s2 = (I // 128) * (H // 128)
-    g1_bytes = n_act * (H * 2 * I + s13) + T * (H + H // 128) + A * (I + I // 128)
-    g2_bytes = n_act * (I * H + s2) + A * (I + I // 128) + A * H * eo_bytes
+    g1_bytes = n_act * (H * 2 * I * wb + H * 2 * I / gw) + T * (H + H / ga) + A * (I + I / ga)
+    g2_bytes = n_act * (I * H * wb + I * H / gw) + A * (I + I / ga) + A * H * eo_bytes
     g1_flops = 4.0 * A * H * I
     g2_flops = 2.0 * A * H * I
-    return {"gate_up_gemm": (g1_bytes, g1_flops), "down_gemm": (g2_bytes, g2_flops)}, n_act
+    return {"gate_up_gemm": (int(g1_bytes), g1_flops), "down_gemm": (int(g2_bytes), g2_flops)}, n_act
 
 
-def step_algorithmic_bytes(wl, n_act: int) -> int:
+def step_algorithmic_bytes(wl, n_act: int, quant: str = "fp8") -> int:
     """Minimum traffic of a whole step: active experts' weights and scales, x, logits
     (or the prelude tensors), y, ids and weights."""
+    wb, _, gw = SCHEME_BYTES[quant]
     H, I, T, E, k = wl.H, wl.I, wl.T, wl.E, wl.k
-    b = n_act * (3 * H * I + (H // 128) * (2 * I // 128) + (I // 128) * (H // 128))
+    b = int(n_act * (3 * H * I * wb + 3 * H * I / gw))
     b += 2 * T * H + 2 * T * H + 8 * T * k
     b += 4 * E * H + 4 * H + 4 * E if wl.prelude else 4 * T * E
     return b
@@ -143,7 +153,7 @@ def load_traffic(workload: str, kernel: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, sample_tokens: int, min_seconds: float = 10.0):
+def cpu_baseline(wl, sample_tokens: int, quant: str = "fp8", min_seconds: float = 10.0):
     """The oracle as it stands, timed on the host on a bounded sample of the workload's
     tokens (weights quantised by the oracle beforehand, untimed)."""
     import concurrent.futures as cf
@@ -152,6 +162,7 @@ def cpu_baseline(wl, sample_tokens: int, min_seconds: float = 10.0):
 
     from gen import workloads as W
     from oracle import moe as omoe
+    from oracle import mx as omx
     from oracle import routing as orouting
 
     x = W.hidden_bf16(wl)
@@ -173,7 +184,11 @@ def cpu_baseline(wl, sample_tokens: int, min_seconds: float = 10.0):
     def src(e):
         return (W.expert_weight_f32(wl, "w13", e).numpy(), W.expert_weight_f32(wl, "w2", e).numpy())
 
-    ex = omoe.QuantizedExperts(src, cache=len(experts))
+    if quant == "fp8":
+        ex, fwd = omoe.QuantizedExperts(src, cache=len(experts)), omoe.forward
+    else:
+        fmt = omx.FMT_E2M1 if quant == "w4a8" else omx.FMT_E4M3
+        ex, fwd = omx.QuantizedExpertsMX(src, fmt, cache=len(experts)), omx.forward
     workers = max(1, min(16, len(os.sched_getaffinity(0))))
     with cf.ThreadPoolExecutor(max_workers=workers) as pool:   # input preparation, untimed
         ex.preload(dict(zip(experts, pool.map(ex.quantize, experts))))
@@ -182,7 +197,7 @@ def cpu_baseline(wl, sample_tokens: int, min_seconds: float = 10.0):
         t0 = time.perf_counter()
         while True:   # whole passes over the sample until at least min_seconds have gone by
             ids, w, _ = omoe.route_workload(inputs, p, pre)    # routing of the whole batch
-            out = omoe.forward(xf, ids, w, ex, tokens=tokens)
+            out = fwd(xf, ids, w, ex, tokens=tokens)
             reps += 1
             dt = time.perf_counter() - t0
             if dt >= min_seconds:
@@ -220,20 +235,36 @@ def main():
     else:
         logits = W.router_logits(wl, dev)
     H, I, E = wl.H, wl.I, wl.E
-    w13p = torch.empty(E * H * 2 * I, dtype=torch.uint8, device=dev)
-    w2p = torch.empty(E * I * H, dtype=torch.uint8, device=dev)
-    w13s = torch.empty(E, H // 128, 2 * I // 128, dtype=torch.uint8, device=dev)
-    w2s = torch.empty(E, I // 128, H // 128, dtype=torch.uint8, device=dev)
-    for e in range(E):
-        q, s = M.moe_quant_weight_blocks(W.expert_weight_f32(wl, "w13", e, dev)[None])
-        w13s[e] = s[0]
-        w13p[e * H * 2 * I:(e + 1) * H * 2 * I] = M.moe_prepack_weights(q)
-        q, s = M.moe_quant_weight_blocks(W.expert_weight_f32(wl, "w2", e, dev)[None])
-        w2s[e] = s[0]
-        w2p[e * I * H:(e + 1) * I * H] = M.moe_prepack_weights(q)
-    layers = [M.PackedWeights(E, H, I, w13p, w13s, w2p, w2s)]
+    quant = M.QUANT_SCHEMES[args.quant]
+    if quant == M.MOE_QUANT_FP8_BLOCK128:
+        w13p = torch.empty(E * H * 2 * I, dtype=torch.uint8, device=dev)
+        w2p = torch.empty(E * I * H, dtype=torch.uint8, device=dev)
+        w13s = torch.empty(E, H // 128, 2 * I // 128, dtype=torch.uint8, device=dev)
+        w2s = torch.empty(E, I // 128, H // 128, dtype=torch.uint8, device=dev)
+        for e in range(E):
+            q, s = M.moe_quant_weight_blocks(W.expert_weight_f32(wl, "w13", e, dev)[None])
+            w13s[e] = s[0]
+            w13p[e * H * 2 * I:(e + 1) * H * 2 * I] = M.moe_prepack_weights(q)
+            q, s = M.moe_quant_weight_blocks(W.expert_weight_f32(wl, "w2", e, dev)[None])
+            w2s[e] = s[0]
+            w2p[e * I * H:(e + 1) * I * H] = M.moe_prepack_weights(q)
+    else:
+        wfmt = M.MOE_WFMT_E2M1 if quant == M.MOE_QUANT_W4A8 else M.MOE_WFMT_E4M3
+        n13, n2 = H * 2 * I // (2 if wfmt else 1), I * H // (2 if wfmt else 1)
+        w13p = torch.empty(E * n13, dtype=torch.uint8, device=dev)
+        w2p = torch.empty(E * n2, dtype=torch.uint8, device=dev)
+        w13s = torch.empty(E * H * 2 * I // 32, dtype=torch.uint8, device=dev)
+        w2s = torch.empty(E * I * H // 32, dtype=torch.uint8, device=dev)
+        for e in range(E):
+            q, s = M.moe_quant_weight_mx(W.expert_weight_f32(wl, "w13", e, dev)[None], wfmt)
+            pq, ps = M.moe_prepack_weights_mx(q, s, wfmt)
+            w13p[e * n13:(e + 1) * n13], w13s[e * ps.numel():(e + 1) * ps.numel()] = pq, ps
+            q, s = M.moe_quant_weight_mx(W.expert_weight_f32(wl, "w2", e, dev)[None], wfmt)
+            pq, ps = M.moe_prepack_weights_mx(q, s, wfmt)
+            w2p[e * n2:(e + 1) * n2], w2s[e * ps.numel():(e + 1) * ps.numel()] = pq, ps
+    layers = [M.PackedWeights(E, H, I, w13p, w13s, w2p, w2s, quant)]
     for _ in range(LAYERS - 1):
-        layers.append(M.PackedWeights(E, H, I, w13p.clone(), w13s.clone(), w2p.clone(), w2s.clone()))
+        layers.append(M.PackedWeights(E, H, I, w13p.clone(), w13s.clone(), w2p.clone(), w2s.clone(), quant))
     params = M.route_params(wl.E, wl.k, wl.scoring, wl.renormalize, wl.group_count, wl.k_group,
                             wl.group_select_mode, wl.routed_scaling_factor)
     counts = torch.zeros(E, dtype=torch.int32, device=dev)
@@ -277,7 +308,7 @@ def main():
 
     cnt = counts.cpu().numpy()
     eo_bytes = 2 if args.expert_out_bf16 else 4
-    per_stage, n_act = stage_bytes_flops(wl, cnt, eo_bytes)
+    per_stage, n_act = stage_bytes_flops(wl, cnt, eo_bytes, args.quant)
     dom = max(per_stage, key=lambda n: stage_s[B.STAGE_NAMES.index(n)])
     other = [n for n in per_stage if n != dom][0]
 
@@ -293,10 +324,11 @@ def main():
             e.destroy()
         return t
 
-    roof = roofline_entry(dom, kernel_time(dom), *per_stage[dom], load_traffic(wl.name, dom))
-    roof_other = roofline_entry(other, kernel_time(other), *per_stage[other], load_traffic(wl.name, other))
+    tname = wl.name if args.quant == "fp8" else f"{wl.name}_{args.quant}"
+    roof = roofline_entry(dom, kernel_time(dom), *per_stage[dom], load_traffic(tname, dom))
+    roof_other = roofline_entry(other, kernel_time(other), *per_stage[other], load_traffic(tname, other))
 
-    step_bytes = step_algorithmic_bytes(wl, n_act)
+    step_bytes = step_algorithmic_bytes(wl, n_act, args.quant)
     total_flops = wl.flops()
     step_s = elapsed / args.steps
     out = {
@@ -310,10 +342,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "dtype": {"fp8": "fp8_e4m3 (fp32 accumulate)", "mxfp8": "mxfp8_e4m3 (fp32 accumulate)",
+                  "w4a8": "fp4_e2m1 weights x fp8_e4m3 activations (fp32 accumulate)"}[args.quant],
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: {W.describe(wl)}", "tokens_per_step": wl.T,
                    "weight_copies_rotated": LAYERS, "expert_out": "bf16" if args.expert_out_bf16 else "fp32",
+                   "quant": {"fp8": "E4M3, UE8M0 per (row,128) / 128x128 block", "mxfp8": "E4M3, UE8M0 per 32",
+                             "w4a8": "E2M1 weights + E4M3 activations, UE8M0 per 32"}[args.quant],
                    "active_experts": n_act},
         "fp8_tflops": round(total_flops / step_s / 1e12, 3),
         "step_hbm_frac": round(step_bytes / step_s / 1e9 / PEAK_HBM_GBS, 4),
@@ -326,7 +361,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         n = args.cpu_sample_tokens or {1: 64, 2: 32, 3: 64, 4: 2, 5: 8}[args.config]
-        out["cpu_baseline"] = cpu_baseline(wl, n)
+        out["cpu_baseline"] = cpu_baseline(wl, n, args.quant)
     print(json.dumps(out), flush=True)
 
 

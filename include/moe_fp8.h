@@ -160,6 +160,57 @@ int moe_quant_weight_blocks(const float* w, int32_t E, int32_t K, int32_t N,
 int moe_prepack_weights(const uint8_t* w, int32_t E, int32_t K, int32_t N,
                         uint8_t* packed, void* stream);
 
+/* ---- micro-scaled schemes (one UE8M0 scale per 32 elements) ------------------------ */
+/* Quantisation schemes of the grouped FFN (moe_ffn_args.quant, moe_fused_args.quant):
+ *   MOE_QUANT_FP8_BLOCK128  E4M3 activations per (row, 128 columns), E4M3 weights per
+ *                           128 x 128 block (the scheme above; the default, value 0).
+ *   MOE_QUANT_MXFP8         E4M3 activations per (row, 32 columns), E4M3 weights per (32 rows
+ *                           of K, one column) ("Fused MoE" page, section "MXFP8 dynamic quant
+ *                           MoE": E4M3 weights whose MX scales run along K; the MATE Mega MoE
+ *                           recipe (1, 1, 32)).
+ *   MOE_QUANT_W4A8          the MXFP8 activations with E2M1 (FP4) weights per (32 x 1) (the
+ *                           FP8 x FP4 path of the DeepGEMM Mega MoE pull request, whose W8A8
+ *                           variant keeps its UE8M0 scale handling and switches the weights
+ *                           from e2m1 to e4m3).
+ * Every 32-element group uses the rule of moe_quant_act with the format's largest magnitude
+ * M (448 for E4M3, 6 for E2M1): e = the smallest integer with amax <= M * 2^e, clamped to
+ * [-127, 127], e = 0 for an all-zero group; codes = RNE(v / 2^e), ties to the even code, sign
+ * of zero kept.  The SwiGLU output is re-quantised to E4M3 per (row, 32 columns) in both MX
+ * schemes.  E2M1 is the OCP 4-bit float: sign, 2 exponent bits (bias 1), 1 mantissa bit,
+ * magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+#define MOE_QUANT_FP8_BLOCK128  0
+#define MOE_QUANT_MXFP8         1
+#define MOE_QUANT_W4A8          2
+#define MOE_WFMT_E4M3           0
+#define MOE_WFMT_E2M1           1
+
+/* moe_quant_act_mx: E4M3 per (row, 32-column group), the MX activation quantisation.
+ *   x [rows, ld] bf16 (first `cols` used; ld % 8 == 0, 16-byte aligned); xq [rows, cols]
+ *   E4M3 out; xs [rows, cols/32] UE8M0 out.  cols % 32 == 0.  Bit-exact. */
+int moe_quant_act_mx(const uint16_t* x, int32_t rows, int32_t cols, int64_t ld,
+                     uint8_t* xq, uint8_t* xs, void* stream);
+
+/* moe_quant_weight_mx: float32 [E, K, N] -> codes + UE8M0 scale [E, K/32, N], one scale per
+ * (32 consecutive rows of K, one column).  wfmt MOE_WFMT_E4M3: codes [E, K, N], one byte
+ * each; MOE_WFMT_E2M1: codes [E, K, N/2], column 2c in the low nibble of byte c.
+ * K % 32 == 0, N % 2 == 0.  Bit-exact.  An offline helper, not part of the timed step. */
+int moe_quant_weight_mx(const float* w, int32_t E, int32_t K, int32_t N, int32_t wfmt,
+                        uint8_t* q, uint8_t* scale, void* stream);
+
+/* moe_prepack_weights_mx: logical MX weights (as moe_quant_weight_mx writes them) -> the
+ * packed layout the MX GEMMs read (the matrix-core instruction's K order, so that one
+ * per-lane scale covers one 32-row group).
+ *   E4M3: E*K*N bytes; byte ((e*(N/16) + n16)*(K/128) + kb)*2048 + h*1024 + lane*16 + b
+ *         holds row kb*128 + h*64 + (lane/16)*16 + b of column n16*16 + lane%16.
+ *   E2M1: E*K*N/2 bytes; byte ((e*(N/16) + n16)*(K/128) + kb)*1024 + lane*16 + b holds rows
+ *         kb*128 + (lane/16)*32 + 2b (low nibble) and 2b + 1 (high nibble) of column
+ *         n16*16 + lane%16.
+ *   scales: E*K*N/32 bytes; byte ((e*(N/16) + n16)*(K/128) + kb)*64 + lane is the scale of
+ *         rows kb*128 + (lane/16)*32 .. +31 of column n16*16 + lane%16.
+ * K % 128 == 0, N % 16 == 0.  Outputs must not alias the inputs. */
+int moe_prepack_weights_mx(const uint8_t* q, const uint8_t* scale, int32_t E, int32_t K, int32_t N,
+                           int32_t wfmt, uint8_t* packed, uint8_t* packed_scale, void* stream);
+
 /* ---- grouped expert FFN ------------------------------------------------------------ */
 #define MOE_DTYPE_F32   0
 #define MOE_DTYPE_BF16  1
@@ -196,9 +247,13 @@ typedef struct moe_ffn_args {
     void*          workspace;
     size_t         workspace_bytes;
     void*          stream;
+    int32_t        quant;       /* MOE_QUANT_*; the MX schemes take xs [T, H/32] from
+                                   moe_quant_act_mx and the packed MX weights and scales of
+                                   moe_prepack_weights_mx in w13 / w13_scale / w2 / w2_scale */
 } moe_ffn_args;
 
 int moe_grouped_ffn(const moe_ffn_args* a);
+/* covers every quantisation scheme */
 size_t moe_ffn_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k);
 
 /* moe_combine: y[t, c] = bf16_RNE( sum_{j<k} topk_weights[t, j] * expert_out[assign_pos[t*k+j], c] ),
@@ -248,6 +303,7 @@ typedef struct moe_fused_args {
     size_t         workspace_bytes;
     void*          stream;
     void* const*   stage_events;
+    int32_t        quant;       /* MOE_QUANT_*: packed weights and scales of that scheme */
 } moe_fused_args;
 
 int moe_fused(const moe_fused_args* a);

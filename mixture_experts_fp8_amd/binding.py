@@ -22,10 +22,14 @@ MOE_SCORING_SOFTMAX, MOE_SCORING_SIGMOID = 0, 1
 MOE_ROUTE_IDS_GIVEN = 1
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 MOE_FUSED_EXPERT_OUT_BF16 = 1
+MOE_QUANT_FP8_BLOCK128, MOE_QUANT_MXFP8, MOE_QUANT_W4A8 = 0, 1, 2
+MOE_WFMT_E4M3, MOE_WFMT_E2M1 = 0, 1
+QUANT_SCHEMES = {"fp8": MOE_QUANT_FP8_BLOCK128, "mxfp8": MOE_QUANT_MXFP8, "w4a8": MOE_QUANT_W4A8}
 
 EXPORTED = ["moe_route", "moe_route_workspace_size", "moe_quant_act", "moe_quant_weight_blocks",
             "moe_prepack_weights", "moe_grouped_ffn", "moe_ffn_workspace_size", "moe_combine",
-            "moe_fused", "moe_workspace_size", "moe_last_error"]
+            "moe_fused", "moe_workspace_size", "moe_last_error", "moe_quant_act_mx", "moe_quant_weight_mx",
+            "moe_prepack_weights_mx"]
 
 
 class MoeError(RuntimeError):
@@ -52,7 +56,7 @@ class FfnArgs(ctypes.Structure):
                 ("sorted_assign", ctypes.c_void_p), ("w13", ctypes.c_void_p), ("w13_scale", ctypes.c_void_p),
                 ("w2", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p), ("expert_out", ctypes.c_void_p),
                 ("out_dtype", ctypes.c_int32), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p)]
+                ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p), ("quant", ctypes.c_int32)]
 
 
 class FusedArgs(ctypes.Structure):
@@ -63,7 +67,7 @@ class FusedArgs(ctypes.Structure):
                 ("y", ctypes.c_void_p), ("topk_ids", ctypes.c_void_p), ("topk_weights", ctypes.c_void_p),
                 ("expert_counts", ctypes.c_void_p), ("flags", ctypes.c_int32), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p),
-                ("stage_events", ctypes.POINTER(ctypes.c_void_p))]
+                ("stage_events", ctypes.POINTER(ctypes.c_void_p)), ("quant", ctypes.c_int32)]
 
 
 MOE_STAGES = 6
@@ -103,6 +107,12 @@ def lib() -> ctypes.CDLL:
         L.moe_fused.argtypes = [ctypes.POINTER(FusedArgs)]
         L.moe_workspace_size.restype = sz
         L.moe_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+        L.moe_quant_act_mx.restype = ctypes.c_int
+        L.moe_quant_act_mx.argtypes = [vp, i32, i32, i64, vp, vp, vp]
+        L.moe_quant_weight_mx.restype = ctypes.c_int
+        L.moe_quant_weight_mx.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp]
+        L.moe_prepack_weights_mx.restype = ctypes.c_int
+        L.moe_prepack_weights_mx.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -193,6 +203,37 @@ def moe_prepack_weights(w: torch.Tensor) -> torch.Tensor:
     return out
 
 
+def moe_quant_act_mx(x: torch.Tensor):
+    """x bf16 [rows, cols] -> (xq uint8 [rows, cols] E4M3, xs uint8 [rows, cols/32] UE8M0)."""
+    _need(x, "x", torch.bfloat16)
+    rows, cols = x.shape
+    xq = torch.empty(rows, cols, dtype=torch.uint8, device=x.device)
+    xs = torch.empty(rows, max(cols // 32, 1), dtype=torch.uint8, device=x.device)
+    _check(lib().moe_quant_act_mx(_ptr(x), rows, cols, cols, _ptr(xq), _ptr(xs), _stream()))
+    return xq, xs
+
+
+def moe_quant_weight_mx(w: torch.Tensor, wfmt: int):
+    """w f32 [E, K, N] -> (codes uint8 [E, K, N] (E4M3) or [E, K, N/2] (E2M1), scale uint8 [E, K/32, N])."""
+    _need(w, "w", torch.float32)
+    E, K, N = w.shape
+    q = torch.empty(E, K, N // 2 if wfmt == MOE_WFMT_E2M1 else N, dtype=torch.uint8, device=w.device)
+    s = torch.empty(E, max(K // 32, 1), N, dtype=torch.uint8, device=w.device)
+    _check(lib().moe_quant_weight_mx(_ptr(w), E, K, N, wfmt, _ptr(q), _ptr(s), _stream()))
+    return q, s
+
+
+def moe_prepack_weights_mx(q: torch.Tensor, s: torch.Tensor, wfmt: int):
+    """Logical MX weights (moe_quant_weight_mx) -> (packed codes, packed scales), flat."""
+    _need(q, "q", torch.uint8)
+    _need(s, "scale", torch.uint8)
+    E, K, N = s.shape[0], q.shape[1], s.shape[2]
+    pq = torch.empty(q.numel(), dtype=torch.uint8, device=q.device)
+    ps = torch.empty(s.numel(), dtype=torch.uint8, device=q.device)
+    _check(lib().moe_prepack_weights_mx(_ptr(q), _ptr(s), E, K, N, wfmt, _ptr(pq), _ptr(ps), _stream()))
+    return pq, ps
+
+
 def moe_route(params: RouteParams, T: int, router_logits: Optional[torch.Tensor] = None,
               hidden_states: Optional[torch.Tensor] = None, prelude: Optional[Prelude] = None,
               topk_ids: Optional[torch.Tensor] = None, topk_weights: Optional[torch.Tensor] = None,
@@ -241,12 +282,24 @@ class PackedWeights:
     w13_scale: torch.Tensor  # [E, H/128, 2I/128]
     w2: torch.Tensor        # packed [E*I*H]
     w2_scale: torch.Tensor  # [E, I/128, H/128]
+    quant: int = MOE_QUANT_FP8_BLOCK128   # MX schemes: packed MX weights and packed scales
 
     @staticmethod
     def from_logical(w13q: torch.Tensor, w13s: torch.Tensor, w2q: torch.Tensor, w2s: torch.Tensor) -> "PackedWeights":
         E, H, I2 = w13q.shape
         return PackedWeights(E, H, I2 // 2, moe_prepack_weights(w13q), w13s.contiguous(),
                              moe_prepack_weights(w2q), w2s.contiguous())
+
+
+def pack_weights_mx(w13: torch.Tensor, w2: torch.Tensor, quant: int) -> PackedWeights:
+    """float32 w13 [E, H, 2I] and w2 [E, I, H] -> packed weights of an MX scheme."""
+    wfmt = MOE_WFMT_E2M1 if quant == MOE_QUANT_W4A8 else MOE_WFMT_E4M3
+    E, H, I2 = w13.shape
+    q13, s13 = moe_quant_weight_mx(w13, wfmt)
+    q2, s2 = moe_quant_weight_mx(w2, wfmt)
+    p13, ps13 = moe_prepack_weights_mx(q13, s13, wfmt)
+    p2, ps2 = moe_prepack_weights_mx(q2, s2, wfmt)
+    return PackedWeights(E, H, I2 // 2, p13, ps13, p2, ps2, quant)
 
 
 def moe_grouped_ffn(xq: torch.Tensor, xs: torch.Tensor, routing: dict, w: PackedWeights, k: int,
@@ -259,7 +312,7 @@ def moe_grouped_ffn(xq: torch.Tensor, xs: torch.Tensor, routing: dict, w: Packed
     ws = workspace(max(nbytes, 256), xq.device)
     a = FfnArgs(T, k, H, w.I, w.E, _ptr(xq), _ptr(xs), _ptr(routing["expert_counts"]),
                 _ptr(routing["expert_offsets"]), _ptr(routing["sorted_assign"]), _ptr(w.w13), _ptr(w.w13_scale),
-                _ptr(w.w2), _ptr(w.w2_scale), _ptr(out), dt, _ptr(ws), ws.numel(), _stream())
+                _ptr(w.w2), _ptr(w.w2_scale), _ptr(out), dt, _ptr(ws), ws.numel(), _stream(), w.quant)
     _check(lib().moe_grouped_ffn(ctypes.byref(a)))
     return out
 
@@ -302,7 +355,7 @@ class MoeFused:
                               ctypes.pointer(self._pre) if self._pre is not None else None,
                               _ptr(w.w13), _ptr(w.w13_scale), _ptr(w.w2), _ptr(w.w2_scale), _ptr(self.y),
                               _ptr(topk_ids), _ptr(topk_weights), _ptr(expert_counts), self.flags, _ptr(self.ws),
-                              self.ws.numel(), None, None)
+                              self.ws.numel(), None, None, w.quant)
 
     def __call__(self, stream: Optional[int] = None, stage_events=None) -> torch.Tensor:
         """stage_events: None or a ctypes array of MOE_STAGES + 1 hipEvent_t handles that the

@@ -964,23 +964,27 @@ __global__ __launch_bounds__(512, 1) void k_gemm2_pf(G2Args a) {
 // The super-tile order pays off once the tiles fill several of its 64-tile windows.
 int ffn_super_tile_order(int ntiles_max) { return ntiles_max >= 512 ? 1 : 0; }
 
-FfnPlan ffn_plan(int T, int k, int E) {
+FfnPlan ffn_plan(int T, int k, int E, int quant) {
     const int64_t A = (int64_t)T * k;
     const int64_t avg = A / E;
     FfnPlan p;
-    p.BM = avg <= MOE_DEC_MAX_AVG_ROWS ? 16 : 128;
+    p.BM = (avg <= MOE_DEC_MAX_AVG_ROWS || quant != kQuantFp8Block128) ? 16 : 128;
     p.ntiles_max = (int)(ceil_div(A, p.BM) + std::min<int64_t>(E, A));
     return p;
 }
 
 // workspace: tiles [ntiles_max] int2 | ntiles int | hq [ntiles_max*BM, I] | hs [ntiles_max*BM, I/128]
 //            | (128-row tiles) down-GEMM weight-scale table [E][H/128][I/128] u32
-size_t ffn_workspace_bytes(int T, int H, int I, int E, int k) {
-    const FfnPlan p = ffn_plan(T, k, E);
+static size_t ffn_ws_plan(const FfnPlan& p, int H, int I, int E) {
     const size_t rows = (size_t)p.ntiles_max * p.BM;
-    size_t n = align256((size_t)p.ntiles_max * 8) + align256(4) + align256(rows * I) + align256(rows * (I / kGroup));
+    // hs holds one scale per 32 columns of h (the MX schemes; the 128 scheme uses a quarter)
+    size_t n = align256((size_t)p.ntiles_max * 8) + align256(4) + align256(rows * I) + align256(rows * (I / 32));
     if (p.BM == 128) n += align256(ffn_rb_scale_table_bytes(H, I, E));
     return n;
+}
+size_t ffn_workspace_bytes(int T, int H, int I, int E, int k) {
+    return std::max(ffn_ws_plan(ffn_plan(T, k, E, kQuantFp8Block128), H, I, E),
+                    ffn_ws_plan(ffn_plan(T, k, E, kQuantMxfp8), H, I, E));
 }
 
 template <int MFW, int NFW1, int NFW2, int WM, int WN, int PF1, int PF2>
@@ -1040,7 +1044,7 @@ static hipError_t run_ffn_pf(const FfnArgs& f, const FfnPlan& p, const FfnWs& w,
 }
 
 FfnWs carve_ffn_ws(const FfnArgs& f, void* ws) {
-    const FfnPlan p = ffn_plan(f.T, f.k, f.E);
+    const FfnPlan p = ffn_plan(f.T, f.k, f.E, f.quant);
     const size_t rows = (size_t)p.ntiles_max * p.BM;
     uint8_t* w = static_cast<uint8_t*>(ws);
     FfnWs r;
@@ -1051,18 +1055,19 @@ FfnWs carve_ffn_ws(const FfnArgs& f, void* ws) {
     r.hq = w;
     w += align256(rows * f.I);
     r.hs = w;
-    w += align256(rows * (f.I / kGroup));
+    w += align256(rows * (f.I / 32));
     r.bs = p.BM == 128 ? reinterpret_cast<uint32_t*>(w) : nullptr;
     return r;
 }
 
 hipError_t launch_grouped_ffn(const FfnArgs& f, void* ws, hipStream_t st, hipEvent_t mid, bool tiles_ready) {
-    const FfnPlan p = ffn_plan(f.T, f.k, f.E);
+    const FfnPlan p = ffn_plan(f.T, f.k, f.E, f.quant);
     const FfnWs w = carve_ffn_ws(f, ws);
     if (!tiles_ready) {
         const hipError_t e = launch_tiles(f.counts, f.E, p.BM, w.tiles, w.ntiles, st);
         if (e != hipSuccess) return e;
     }
+    if (f.quant != kQuantFp8Block128) return launch_ffn_mx(f, p, w, st, mid);
     // output columns per workgroup of the down GEMM = 128, a divisor of H
     if (p.BM == 16) return run_ffn_dec<MOE_DEC_GEMM1, MOE_DEC_GEMM2>(f, p, w, st, mid);
     // 128-row tiles: the staged kernels need the tile's A scales in LDS and 256-column

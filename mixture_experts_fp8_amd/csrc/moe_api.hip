@@ -239,6 +239,55 @@ int moe_prepack_weights(const uint8_t* w, int32_t E, int32_t K, int32_t N, uint8
     return ok();
 }
 
+int moe_quant_act_mx(const uint16_t* x, int32_t rows, int32_t cols, int64_t ld, uint8_t* xq, uint8_t* xs,
+                     void* stream) {
+    const char* op = "moe_quant_act_mx";
+    if (!x || !xq || !xs) return fail(MOE_ERR_INVALID, "%s: pointers must not be NULL", op);
+    if (rows < 1 || cols < 1) return fail(MOE_ERR_INVALID, "%s: rows (%d) and cols (%d) must be > 0", op, rows, cols);
+    if (cols % 32) return fail(MOE_ERR_UNSUPPORTED, "%s: cols (%d) must be a multiple of 32", op, cols);
+    if (ld < cols) return fail(MOE_ERR_INVALID, "%s: ld (%lld) must be >= cols (%d)", op, (long long)ld, cols);
+    if (ld % 8 || !aligned(x, 16)) return fail(MOE_ERR_UNSUPPORTED, "%s: x must be 16-byte aligned with ld %% 8 == 0", op);
+    if (!aligned(xq, 8)) return fail(MOE_ERR_UNSUPPORTED, "%s: xq must be 8-byte aligned", op);
+    const hipError_t e = moe::launch_quant_act_mx(x, rows, cols, ld, xq, xs, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(op, e);
+    return ok();
+}
+
+int moe_quant_weight_mx(const float* w, int32_t E, int32_t K, int32_t N, int32_t wfmt, uint8_t* q, uint8_t* scale,
+                        void* stream) {
+    const char* op = "moe_quant_weight_mx";
+    if (!w || !q || !scale) return fail(MOE_ERR_INVALID, "%s: pointers must not be NULL", op);
+    if (E < 1 || K < 1 || N < 1) return fail(MOE_ERR_INVALID, "%s: E, K, N (%d, %d, %d) must be > 0", op, E, K, N);
+    if (wfmt != MOE_WFMT_E4M3 && wfmt != MOE_WFMT_E2M1)
+        return fail(MOE_ERR_INVALID, "%s: wfmt (%d) must be MOE_WFMT_E4M3 or MOE_WFMT_E2M1", op, wfmt);
+    if (K % 32 || N % 2) return fail(MOE_ERR_UNSUPPORTED, "%s: K (%d) must be a multiple of 32 and N (%d) even", op, K, N);
+    const hipError_t e = moe::launch_quant_weight_mx(w, E, K, N, wfmt, q, scale, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(op, e);
+    return ok();
+}
+
+int moe_prepack_weights_mx(const uint8_t* q, const uint8_t* scale, int32_t E, int32_t K, int32_t N, int32_t wfmt,
+                           uint8_t* packed, uint8_t* packed_scale, void* stream) {
+    const char* op = "moe_prepack_weights_mx";
+    if (!q || !scale || !packed || !packed_scale) return fail(MOE_ERR_INVALID, "%s: pointers must not be NULL", op);
+    if (E < 1 || K < 1 || N < 1) return fail(MOE_ERR_INVALID, "%s: E, K, N (%d, %d, %d) must be > 0", op, E, K, N);
+    if (wfmt != MOE_WFMT_E4M3 && wfmt != MOE_WFMT_E2M1)
+        return fail(MOE_ERR_INVALID, "%s: wfmt (%d) must be MOE_WFMT_E4M3 or MOE_WFMT_E2M1", op, wfmt);
+    if (K % 128 || N % 16) return fail(MOE_ERR_UNSUPPORTED, "%s: K (%d) must be a multiple of 128 and N (%d) of 16", op, K, N);
+    if (!aligned(packed, 16)) return fail(MOE_ERR_UNSUPPORTED, "%s: packed must be 16-byte aligned", op);
+    const uintptr_t nq = (uintptr_t)E * K * N / (wfmt == MOE_WFMT_E2M1 ? 2 : 1), ns = (uintptr_t)E * K * N / 32;
+    auto overlap = [](const void* a, uintptr_t na, const void* b, uintptr_t nb) {
+        return (uintptr_t)a < (uintptr_t)b + nb && (uintptr_t)b < (uintptr_t)a + na;
+    };
+    if (overlap(q, nq, packed, nq) || overlap(scale, ns, packed_scale, ns) || overlap(q, nq, packed_scale, ns) ||
+        overlap(scale, ns, packed, nq))
+        return fail(MOE_ERR_INVALID, "%s: outputs must not overlap the inputs", op);
+    const hipError_t e = moe::launch_prepack_mx(q, scale, E, K, N, wfmt, packed, packed_scale,
+                                                static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(op, e);
+    return ok();
+}
+
 size_t moe_ffn_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k) {
     if (T < 1 || H < 1 || I < 128 || E < 1 || k < 1) return 0;
     return moe::ffn_workspace_bytes(T, H, I, E, k);
@@ -255,6 +304,8 @@ int moe_grouped_ffn(const moe_ffn_args* a) {
     if (a->out_dtype != MOE_DTYPE_F32 && a->out_dtype != MOE_DTYPE_BF16)
         return fail(MOE_ERR_INVALID, "%s: out_dtype (%d) must be MOE_DTYPE_F32 or MOE_DTYPE_BF16", op, a->out_dtype);
     if (!aligned(a->xq, 16)) return fail(MOE_ERR_UNSUPPORTED, "%s: xq must be 16-byte aligned", op);
+    if (a->quant != MOE_QUANT_FP8_BLOCK128 && a->quant != MOE_QUANT_MXFP8 && a->quant != MOE_QUANT_W4A8)
+        return fail(MOE_ERR_INVALID, "%s: quant (%d) must be one of MOE_QUANT_*", op, a->quant);
     const size_t need = moe::ffn_workspace_bytes(a->T, a->H, a->I, a->E, a->k);
     if (!a->workspace || a->workspace_bytes < need)
         return fail(MOE_ERR_WORKSPACE, "%s: workspace too small: need %zu bytes, have %zu", op, need,
@@ -262,7 +313,7 @@ int moe_grouped_ffn(const moe_ffn_args* a) {
     if (!aligned(a->workspace, 256)) return fail(MOE_ERR_INVALID, "%s: workspace must be 256-byte aligned", op);
     moe::FfnArgs f{a->T, a->k, a->H, a->I, a->E, a->xq, a->xs, a->expert_counts, a->expert_offsets,
                    a->sorted_assign, a->w13, a->w13_scale, a->w2, a->w2_scale, a->expert_out,
-                   a->out_dtype == MOE_DTYPE_BF16};
+                   a->out_dtype == MOE_DTYPE_BF16, a->quant};
     const hipError_t e = moe::launch_grouped_ffn(f, a->workspace, static_cast<hipStream_t>(a->stream));
     if (e != hipSuccess) return hip_fail(op, e);
     return ok();
@@ -290,7 +341,7 @@ size_t moe_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k,
     const size_t A = (size_t)T * k;
     const size_t eo = (flags & MOE_FUSED_EXPERT_OUT_BF16) ? 2 : 4;
     return 4 * align256(A * 4) + align256((size_t)E * 4) + align256((size_t)(E + 1) * 4) +
-           route_ws_bytes(T, E, k, 1) + align256((size_t)T * H) + align256((size_t)T * (H / 128)) +
+           route_ws_bytes(T, E, k, 1) + align256((size_t)T * H) + align256((size_t)T * (H / 32)) +
            moe::ffn_workspace_bytes(T, H, I, E, k) + align256(A * H * eo);
 }
 
@@ -309,6 +360,8 @@ int moe_fused(const moe_fused_args* a) {
     }
     if ((rc = check_weights(op, a->w13, a->w13_scale, a->w2, a->w2_scale))) return rc;
     if (a->flags & ~MOE_FUSED_EXPERT_OUT_BF16) return fail(MOE_ERR_INVALID, "%s: unknown flags 0x%x", op, a->flags);
+    if (a->quant != MOE_QUANT_FP8_BLOCK128 && a->quant != MOE_QUANT_MXFP8 && a->quant != MOE_QUANT_W4A8)
+        return fail(MOE_ERR_INVALID, "%s: quant (%d) must be one of MOE_QUANT_*", op, a->quant);
     if (!aligned(a->hidden_states, 16) || !aligned(a->y, 8))
         return fail(MOE_ERR_UNSUPPORTED, "%s: hidden_states must be 16-byte and y 8-byte aligned", op);
     const size_t need = moe_workspace_size(T, H, I, E, k, a->flags);
@@ -329,7 +382,7 @@ int moe_fused(const moe_fused_args* a) {
     uint8_t* rws = w;
     w += route_ws_bytes(T, E, k, 1);
     uint8_t* xq = take((size_t)T * H);
-    uint8_t* xs = take((size_t)T * (H / 128));
+    uint8_t* xs = take((size_t)T * (H / 32));
     uint8_t* fws = w;
     w += moe::ffn_workspace_bytes(T, H, I, E, k);
     void* eo = take(A * H * ((a->flags & MOE_FUSED_EXPERT_OUT_BF16) ? 2 : 4));
@@ -346,11 +399,15 @@ int moe_fused(const moe_fused_args* a) {
         if (e == hipSuccess && ev[i]) e = hipEventRecord(ev[i], st);
     };
     const int bf = (a->flags & MOE_FUSED_EXPERT_OUT_BF16) ? 1 : 0;
-    moe::FfnArgs f{T, k, H, I, E, xq, xs, counts, offsets, sorted, a->w13, a->w13_scale, a->w2, a->w2_scale, eo, bf};
+    const bool mx = a->quant != MOE_QUANT_FP8_BLOCK128;
+    moe::FfnArgs f{T, k, H, I, E, xq, xs, counts, offsets, sorted, a->w13, a->w13_scale, a->w2, a->w2_scale, eo, bf,
+                   a->quant};
     const moe::FfnWs fw = moe::carve_ffn_ws(f, fws);
-    const moe::FfnPlan plan = moe::ffn_plan(T, k, E);
-    // the activation quantisation runs inside the routing kernel (one wave per token)
+    const moe::FfnPlan plan = moe::ffn_plan(T, k, E, a->quant);
+    // the 128-group activation quantisation runs inside the routing kernel (one wave per
+    // token); the 32-group one is its own launch
     mark(0);
+    if (e == hipSuccess && mx) e = moe::launch_quant_act_mx(a->hidden_states, T, H, H, xq, xs, st);
     mark(1);
     float* pl = reinterpret_cast<float*>(rws + route_chunk_bytes(T, E, k));
     if (e == hipSuccess && a->prelude)
@@ -359,7 +416,8 @@ int moe_fused(const moe_fused_args* a) {
     if (e == hipSuccess)
         e = moe::launch_route(a->prelude ? pl : a->router_logits, route_cfg(&a->route, T, a->prelude != nullptr),
                               a->prelude ? a->prelude->per_expert_scale : nullptr, ids, wts, st,
-                              moe::QuantOut{a->hidden_states, H, xq, xs});
+                              mx ? moe::QuantOut{nullptr, 0, nullptr, nullptr}
+                                 : moe::QuantOut{a->hidden_states, H, xq, xs});
     mark(2);
     if (e == hipSuccess)
         e = moe::launch_dispatch(ids, (int)A, E, reinterpret_cast<int32_t*>(rws), counts, offsets, sorted, pos, st,

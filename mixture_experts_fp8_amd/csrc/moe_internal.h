@@ -6,12 +6,24 @@
 
 namespace moe {
 
+// ---- quantisation schemes of the grouped FFN (values of moe_ffn_args.quant)
+constexpr int kQuantFp8Block128 = 0;   // E4M3 per (row, 128), weights per 128 x 128 block
+constexpr int kQuantMxfp8 = 1;         // E4M3 per (row, 32), E4M3 weights per (32 x 1)
+constexpr int kQuantW4A8 = 2;          // E4M3 per (row, 32), E2M1 weights per (32 x 1)
+constexpr int kWfmtE4M3 = 0, kWfmtE2M1 = 1;
+
 // ---- quantisation / layout
 hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, int64_t ld, uint8_t* xq, uint8_t* xs,
                             hipStream_t st);
 hipError_t launch_quant_weight_blocks(const float* w, int E, int K, int N, uint8_t* q, uint8_t* s,
                                       hipStream_t st);
 hipError_t launch_prepack(const uint8_t* w, int E, int K, int N, uint8_t* out, hipStream_t st);
+hipError_t launch_quant_act_mx(const uint16_t* x, int rows, int cols, int64_t ld, uint8_t* xq, uint8_t* xs,
+                               hipStream_t st);
+hipError_t launch_quant_weight_mx(const float* w, int E, int K, int N, int wfmt, uint8_t* q, uint8_t* s,
+                                  hipStream_t st);
+hipError_t launch_prepack_mx(const uint8_t* q, const uint8_t* s, int E, int K, int N, int wfmt, uint8_t* packed,
+                             uint8_t* packed_s, hipStream_t st);
 
 // ---- routing and dispatch
 struct RouteCfg {
@@ -50,7 +62,8 @@ struct FfnPlan {
     int BM;           // rows per tile
     int ntiles_max;   // grid bound on tiles
 };
-FfnPlan ffn_plan(int T, int k, int E);
+FfnPlan ffn_plan(int T, int k, int E, int quant = kQuantFp8Block128);
+// covers every quantisation scheme
 size_t ffn_workspace_bytes(int T, int H, int I, int E, int k);
 
 struct FfnArgs {
@@ -66,6 +79,7 @@ struct FfnArgs {
     const uint8_t* w2s;
     void* out;
     int out_bf16;
+    int quant;       // kQuant*; for the MX schemes w13s / w2s are the packed MX scales
 };
 struct FfnWs {
     int2* tiles;
@@ -79,6 +93,8 @@ FfnWs carve_ffn_ws(const FfnArgs& a, void* ws);
 // tile list in the workspace was already written (by launch_dispatch)
 hipError_t launch_grouped_ffn(const FfnArgs& a, void* ws, hipStream_t st, hipEvent_t mid = nullptr,
                               bool tiles_ready = false);
+// MX schemes on 16-row tiles (k_mx.hip)
+hipError_t launch_ffn_mx(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid);
 
 int ffn_super_tile_order(int ntiles_max);
 // persistent down GEMM for 128-row tiles (k_ffn_rb.hip)

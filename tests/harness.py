@@ -58,6 +58,42 @@ def device_weights(wl: W.Workload, device="cuda") -> M.PackedWeights:
     return M.PackedWeights(E, H, I, w13p, w13s, w2p, w2s)
 
 
+def device_weights_mx(wl: W.Workload, quant: int, device="cuda") -> M.PackedWeights:
+    """Generate, MX-quantise and pack each expert's weights on the GPU (scheme `quant`)."""
+    H, I, E = wl.H, wl.I, wl.E
+    wfmt = M.MOE_WFMT_E2M1 if quant == M.MOE_QUANT_W4A8 else M.MOE_WFMT_E4M3
+    div = 2 if wfmt == M.MOE_WFMT_E2M1 else 1
+    n13, n2 = H * 2 * I // div, I * H // div
+    w13p = torch.empty(E * n13, dtype=torch.uint8, device=device)
+    w2p = torch.empty(E * n2, dtype=torch.uint8, device=device)
+    w13s = torch.empty(E * H * 2 * I // 32, dtype=torch.uint8, device=device)
+    w2s = torch.empty(E * I * H // 32, dtype=torch.uint8, device=device)
+    for e in range(E):
+        q, s = M.moe_quant_weight_mx(W.expert_weight_f32(wl, "w13", e, device)[None], wfmt)
+        pq, ps = M.moe_prepack_weights_mx(q, s, wfmt)
+        w13p[e * n13:(e + 1) * n13] = pq
+        w13s[e * ps.numel():(e + 1) * ps.numel()] = ps
+        q, s = M.moe_quant_weight_mx(W.expert_weight_f32(wl, "w2", e, device)[None], wfmt)
+        pq, ps = M.moe_prepack_weights_mx(q, s, wfmt)
+        w2p[e * n2:(e + 1) * n2] = pq
+        w2s[e * ps.numel():(e + 1) * ps.numel()] = ps
+    return M.PackedWeights(E, H, I, w13p, w13s, w2p, w2s, quant)
+
+
+def oracle_experts_mx_for(wl: W.Workload, fmt: str, experts, workers: int = 8):
+    """MX oracle experts (weights in `fmt`) with the listed ones quantised up front."""
+    import concurrent.futures as cf
+    from oracle import mx as omx
+
+    def src(e):
+        return (W.expert_weight_f32(wl, "w13", e).numpy(), W.expert_weight_f32(wl, "w2", e).numpy())
+    ex = omx.QuantizedExpertsMX(src, fmt, cache=max(8, len(experts)))
+    with cf.ThreadPoolExecutor(max_workers=workers) as pool:
+        qs = dict(zip(experts, pool.map(ex.quantize, experts)))
+    ex.preload(qs)
+    return ex
+
+
 def oracle_route(wl: W.Workload, x_f64=None, logits=None):
     """(ids, weights, margin) of the oracle for all tokens."""
     p = oracle_params(wl)

@@ -24,7 +24,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     fns = declared_functions()
     for f in ["moe_route", "moe_quant_act", "moe_grouped_ffn", "moe_combine", "moe_fused",
-              "moe_workspace_size", "moe_last_error", "moe_prepack_weights", "moe_quant_weight_blocks"]:
+              "moe_workspace_size", "moe_last_error", "moe_prepack_weights", "moe_quant_weight_blocks",
+              "moe_quant_act_mx", "moe_quant_weight_mx", "moe_prepack_weights_mx"]:
         assert f in fns
 
 
@@ -95,6 +96,20 @@ def test_weight_helpers_validation():
     assert "overlap" in M.moe_last_error()
 
 
+def test_mx_helpers_validation():
+    L = M.lib()
+    assert L.moe_quant_act_mx(FAKE, 4, 48, 48, FAKE, FAKE, None) == B.MOE_ERR_UNSUPPORTED   # cols % 32
+    assert L.moe_quant_act_mx(None, 4, 64, 64, FAKE, FAKE, None) == B.MOE_ERR_INVALID
+    assert L.moe_quant_act_mx(FAKE, 4, 64, 32, FAKE, FAKE, None) == B.MOE_ERR_INVALID      # ld < cols
+    assert L.moe_quant_weight_mx(FAKE, 1, 64, 64, 2, FAKE, FAKE, None) == B.MOE_ERR_INVALID  # wfmt
+    assert L.moe_quant_weight_mx(FAKE, 1, 48, 64, 0, FAKE, FAKE, None) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_quant_weight_mx(FAKE, 1, 64, 63, 1, FAKE, FAKE, None) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_prepack_weights_mx(FAKE, FAKE + (1 << 24), 1, 96, 64, 0, FAKE + (2 << 24), FAKE + (3 << 24),
+                                    None) == B.MOE_ERR_UNSUPPORTED   # K % 128
+    assert L.moe_prepack_weights_mx(FAKE, FAKE + (1 << 24), 1, 128, 64, 1, FAKE + 16, FAKE + (3 << 24),
+                                    None) == B.MOE_ERR_INVALID and "overlap" in M.moe_last_error()
+
+
 def _ffn(**over):
     a = dict(T=8, k=2, H=256, I=256, E=4, xq=FAKE, xs=FAKE, expert_counts=FAKE, expert_offsets=FAKE,
              sorted_assign=FAKE, w13=FAKE, w13_scale=FAKE, w2=FAKE, w2_scale=FAKE, expert_out=FAKE,
@@ -112,6 +127,7 @@ def test_grouped_ffn_validation():
     assert _ffn(w13=FAKE + 8) == B.MOE_ERR_INVALID
     assert _ffn(out_dtype=7) == B.MOE_ERR_INVALID
     assert _ffn(workspace_bytes=10) == B.MOE_ERR_WORKSPACE
+    assert _ffn(quant=3) == B.MOE_ERR_INVALID and "quant" in M.moe_last_error()
     assert M.lib().moe_grouped_ffn(None) == B.MOE_ERR_INVALID
 
 
@@ -139,6 +155,7 @@ def test_fused_validation():
     assert _fused(flags=4) == B.MOE_ERR_INVALID
     assert _fused(workspace_bytes=1000) == B.MOE_ERR_WORKSPACE
     assert _fused(hidden_states=FAKE + 4) == B.MOE_ERR_UNSUPPORTED
+    assert _fused(quant=-1) == B.MOE_ERR_INVALID
     assert M.lib().moe_fused(None) == B.MOE_ERR_INVALID
 
 

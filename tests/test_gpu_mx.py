@@ -1,0 +1,158 @@
+"""GPU parity of the micro-scaled schemes (MXFP8, W4A8) against the oracle (oracle.mx).
+
+Quantisers and the pre-pack are compared bit for bit; the expert step end to end with the
+output bar of the 128-group path (relative Frobenius <= 5e-3, max |err| <= 2e-2 max |y|).
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from gen import rng, workloads as W
+from oracle import mx as omx
+
+import harness as HN
+
+pytestmark = pytest.mark.gpu
+
+M = pytest.importorskip("mixture_experts_fp8_amd")
+DEV = "cuda"
+SCHEMES = {"mxfp8": (1, omx.FMT_E4M3), "w4a8": (2, omx.FMT_E2M1)}
+
+
+def test_quant_act_mx_bit_exact():
+    r = np.random.default_rng(11)
+    R, C = 97, 416
+    x = r.standard_normal((R, C)) * np.exp2(r.integers(-30, 30, size=(R, 1)))
+    x[3] = 0.0                                  # all-zero groups
+    x[5, 32:64] = 0.0
+    x[7, :32] = 1.0625 * 2.0 ** -3              # E4M3 midpoints after scaling
+    x[7, 0] = 448 * 2.0 ** -3
+    xb = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)
+    xq, xs = M.moe_quant_act_mx(xb.to(DEV))
+    q, s = omx.quant_rows_32(W.bf16_to_f64(xb))
+    assert np.array_equal(xq.cpu().numpy(), q)
+    assert np.array_equal(xs.cpu().numpy(), s)
+
+
+@pytest.mark.parametrize("scheme", list(SCHEMES))
+def test_quant_weight_mx_bit_exact(scheme):
+    _, fmt = SCHEMES[scheme]
+    wfmt = M.MOE_WFMT_E2M1 if fmt == omx.FMT_E2M1 else M.MOE_WFMT_E4M3
+    E, K, N = 3, 256, 96
+    w = rng.normal_f32(rng.stream_key(0, 201, 0), E * K * N, 0.02).view(E, K, N)
+    w[1, :32, 5] = 0.0                                               # an all-zero group
+    w[2, 32:64, 7] = torch.tensor([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0] * 4) * 2.0 ** -9   # E2M1 ties
+    q, s = M.moe_quant_weight_mx(w.to(DEV), wfmt)
+    for e in range(E):
+        qr, sr = omx.quant_weight_k32(w[e].double().numpy(), fmt)
+        if fmt == omx.FMT_E2M1:
+            qr = (qr[:, 0::2] & 15) | ((qr[:, 1::2] & 15) << 4)
+        assert np.array_equal(q[e].cpu().numpy(), qr), e
+        assert np.array_equal(s[e].cpu().numpy(), sr), e
+
+
+@pytest.mark.parametrize("scheme", list(SCHEMES))
+def test_prepack_mx_layout(scheme):
+    _, fmt = SCHEMES[scheme]
+    wfmt = M.MOE_WFMT_E2M1 if fmt == omx.FMT_E2M1 else M.MOE_WFMT_E4M3
+    E, K, N = 2, 256, 48
+    g = torch.Generator().manual_seed(12)
+    q = torch.randint(0, 256, (E, K, N // 2 if wfmt else N), generator=g, dtype=torch.uint8)
+    s = torch.randint(0, 256, (E, K // 32, N), generator=g, dtype=torch.uint8)
+    pq, ps = M.moe_prepack_weights_mx(q.to(DEV), s.to(DEV), wfmt)
+    pq, ps, qn, sn = pq.cpu().numpy(), ps.cpu().numpy(), q.numpy(), s.numpy()
+    for e in range(E):
+        for n16 in range(N // 16):
+            for kb in range(K // 128):
+                blk = (e * (N // 16) + n16) * (K // 128) + kb
+                for lane in (0, 5, 16, 31, 47, 63):
+                    n, k0 = n16 * 16 + lane % 16, kb * 128 + (lane // 16) * 32
+                    assert ps[blk * 64 + lane] == sn[e, k0 // 32, n]
+                    for b in (0, 7, 15):
+                        if wfmt:
+                            lo = (qn[e, k0 + 2 * b, n // 2] >> (4 * (n % 2))) & 15
+                            hi = (qn[e, k0 + 2 * b + 1, n // 2] >> (4 * (n % 2))) & 15
+                            assert pq[blk * 1024 + lane * 16 + b] == lo | (hi << 4)
+                        else:
+                            for h in (0, 1):
+                                k = kb * 128 + h * 64 + (lane // 16) * 16 + b
+                                assert pq[blk * 2048 + h * 1024 + lane * 16 + b] == qn[e, k, n]
+
+
+def _run(wl, quant, w=None):
+    x, logits, pre = HN.device_inputs(wl)
+    w = w or HN.device_weights_mx(wl, quant)
+    y, ids, wts, counts = M.moe_fused(HN.device_params(wl), x, w, router_logits=logits, prelude=pre,
+                                      return_routing=True)
+    torch.cuda.synchronize()
+    return y, ids.cpu().numpy(), counts.cpu().numpy()
+
+
+def _oracle(wl, fmt, tokens=None):
+    x = W.hidden_bf16(wl)
+    xf = W.bf16_to_f64(x)
+    logits = None if wl.prelude else W.router_logits(wl)
+    ids, w, margin = HN.oracle_route(wl, x_f64=xf, logits=logits)
+    tok = np.arange(wl.T) if tokens is None else np.asarray(tokens)
+    experts = sorted(set(int(e) for e in ids[tok].reshape(-1)))
+    ex = HN.oracle_experts_mx_for(wl, fmt, experts, workers=int(os.environ.get("ORACLE_WORKERS", "8")))
+    return omx.forward(xf, ids, w, ex, tokens=tok), ids, margin
+
+
+SMALL = {
+    "cfg1": W.CONFIGS[1],
+    "ragged": W.Workload(131, "mx_ragged", T=37, H=256, I=384, E=5, k=3),
+    "T1": W.Workload(132, "mx_one", T=1, H=128, I=128, E=1, k=1),
+    "prelude": W.Workload(133, "mx_pre", T=9, H=512, I=256, E=16, k=4, prelude=True),
+}
+
+
+@pytest.mark.parametrize("scheme", list(SCHEMES))
+@pytest.mark.parametrize("name", list(SMALL))
+def test_mx_fused_small(scheme, name):
+    quant, fmt = SCHEMES[scheme]
+    wl = SMALL[name]
+    print("mx fused", scheme, name, W.describe(wl), flush=True)
+    y, ids, counts = _run(wl, quant)
+    ref, ids_ref, margin = _oracle(wl, fmt)
+    ok = margin >= 1e-5
+    assert np.array_equal(ids[ok], ids_ref[ok])
+    fro, mxe = HN.assert_output_close(HN.bf16_to_f64(y)[ok], ref["y"][ok], f"{scheme} {name}", ref["qmargin_tok"][ok])
+    print(f"  rel fro {fro:.2e} rel max {mxe:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("scheme", list(SCHEMES))
+@pytest.mark.parametrize("cfg,ntok", [(2, None), (3, 48), (5, 4)])
+def test_mx_fused_workloads(scheme, cfg, ntok):
+    quant, fmt = SCHEMES[scheme]
+    wl = W.CONFIGS[cfg]
+    print("mx fused workload", scheme, cfg, W.describe(wl), flush=True)
+    y, ids, counts = _run(wl, quant)
+    tokens = None if ntok is None else np.linspace(0, wl.T - 1, ntok).astype(np.int64)
+    ref, ids_ref, margin = _oracle(wl, fmt, tokens)
+    tok = np.arange(wl.T) if tokens is None else tokens
+    ok = margin[tok] >= 1e-5
+    assert np.array_equal(ids[tok][ok], ids_ref[tok][ok])
+    assert counts.sum() == wl.T * wl.k
+    fro, mxe = HN.assert_output_close(HN.bf16_to_f64(y)[tok][ok], ref["y"][ok], f"{scheme} cfg{cfg}",
+                                      ref["qmargin_tok"][ok])
+    print(f"  rel fro {fro:.2e} rel max {mxe:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("scheme", list(SCHEMES))
+def test_mx_grouped_ffn_unit_and_bf16_out(scheme):
+    quant, fmt = SCHEMES[scheme]
+    wl = W.CONFIGS[1]
+    x, logits, _ = HN.device_inputs(wl)
+    w = HN.device_weights_mx(wl, quant)
+    r = M.moe_route(HN.device_params(wl), wl.T, router_logits=logits)
+    xq, xs = M.moe_quant_act_mx(x)
+    ref, ids_ref, _ = _oracle(wl, fmt)
+    assert np.array_equal(xq.cpu().numpy(), ref["xq"]) and np.array_equal(xs.cpu().numpy(), ref["xs"])
+    pos = r["assign_pos"].cpu().numpy().astype(np.int64)
+    for dt in (torch.float32, torch.bfloat16):
+        eo = M.moe_grouped_ffn(xq, xs, r, w, wl.k, out_dtype=dt)
+        HN.assert_output_close(eo.float().cpu().numpy().astype(np.float64)[pos], ref["o"], f"{scheme} o {dt}",
+                               ref["qmargin"])
