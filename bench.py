@@ -42,7 +42,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, help="workload id 1..5 (default 2: Gemma-4-like decode)")
+    ap.add_argument("--config", type=int, default=2,
+                    help="workload id 1..5 (default 2: Gemma-4-like decode); 6: one 8-GPU expert-parallel shard of 4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0, help="0: the workload's own default sample")
     ap.add_argument("--expert-out-bf16", action="store_true", help="keep per-assignment expert outputs in bf16")
@@ -360,7 +361,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        n = args.cpu_sample_tokens or {1: 64, 2: 32, 3: 64, 4: 2, 5: 8}[args.config]
+        n = args.cpu_sample_tokens or {1: 64, 2: 32, 3: 64, 4: 2, 5: 8, 6: 2}[args.config]
         out["cpu_baseline"] = cpu_baseline(wl, n, args.quant)
     print(json.dumps(out), flush=True)
 

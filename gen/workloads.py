@@ -8,7 +8,9 @@ The five shapes follow the workloads the pages describe or imply:
   1152) of the DeepGEMM W8A8 Mega MoE pull request ("Testing");
 * a tiny case, a DeepSeek-V3-shaped prefill with group-limited sigmoid routing (the
   group knobs of the MindIE-SD ``fused_moe`` parameter table) and a large prefill with
-  a Zipf-skewed expert load.
+  a Zipf-skewed expert load;
+* one expert-parallel shard of that prefill (32 local experts, ~1024 rows each), the
+  per-GPU shape of the MATE Mega MoE expert-parallel path on 8 ranks.
 
 Value recipes (all seeded, all synthetic; no dataset is involved):
 
@@ -91,6 +93,13 @@ CONFIGS = {
                 routed_scaling_factor=2.5),
     5: Workload(5, "prefill_zipf", T=16384, H=4096, I=1536, E=128, k=8, scoring="softmax",
                 renormalize=True, bias="zipf"),
+    # One expert-parallel shard of the DeepSeek-V3-shaped prefill on 8 GPUs: the GPU holds 32
+    # of the 256 experts and receives every assignment routed to them, about 8x the rows per
+    # expert of the one-GPU case (32768 assignments over 32 experts, ~1024 rows each).  Routing
+    # keeps the group-limited sigmoid knobs on the local experts (8 groups of 4).
+    6: Workload(6, "ep8_shard_dsv3", T=4096, H=7168, I=2048, E=32, k=8, scoring="sigmoid",
+                renormalize=True, group_count=8, k_group=4, group_select_mode=1,
+                routed_scaling_factor=2.5),
 }
 
 

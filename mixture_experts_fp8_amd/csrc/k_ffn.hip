@@ -684,6 +684,23 @@ __device__ __forceinline__ void wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
+// Scaled FP8 matrix-core product taking the A scale from byte ba of sa and the B scale from
+// byte bb of sb (the instruction's scale byte selects; ba, bb are constants after unrolling).
+__device__ __forceinline__ v4f mfma_fp8_sel(int ba, int bb, v8i a, v8i b, v4f acc, int sa, int sb) {
+#define MOE_SEL(A, B) return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, A, sa, B, sb)
+    switch (ba * 2 + bb) {
+        case 0: MOE_SEL(0, 0);
+        case 1: MOE_SEL(0, 1);
+        case 2: MOE_SEL(1, 0);
+        case 3: MOE_SEL(1, 1);
+        case 4: MOE_SEL(2, 0);
+        case 5: MOE_SEL(2, 1);
+        case 6: MOE_SEL(3, 0);
+        default: MOE_SEL(3, 1);
+    }
+#undef MOE_SEL
+}
+
 __global__ __launch_bounds__(512, 1) void k_gemm1_pf(G1Args a) {
     int ib, tile;
     if (!pf_work_item(a.ord, a.I / kGroup, __builtin_amdgcn_readfirstlane(*a.ntiles), tile, ib)) return;
@@ -696,21 +713,26 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pf(G1Args a) {
     const int wm = wv >> 2, wn = wv & 3;
 
     __shared__ __align__(16) uint8_t buf[kPfdStages * kPfStage];
-    __shared__ __align__(16) uint8_t s_sa[kPfMaxKB * kPfBM];   // [kb][row]
-    __shared__ uint8_t s_sg[kPfMaxKB], s_su[kPfMaxKB];
+    __shared__ __align__(16) uint8_t s_sa[kPfMaxKB * kPfBM];   // [kb][wm][row % 16][fragment of wm]
+    __shared__ uint16_t s_sgu[kPfMaxKB];                      // gate scale | up scale << 8
     __shared__ float s_amax[4][kPfBM];
 
     const int NB16 = 2 * a.I / 16, NBS = 2 * a.I / kGroup;
     const v4i_t ra = make_srd(a.xq, (uint32_t)a.T * a.H);
     const v4i_t rw = make_srd(a.w13p + (int64_t)e * NB16 * KB * kFragBytes, (uint32_t)NB16 * KB * kFragBytes);
+    // A pieces: wave instruction i moves rows 8 (wv + 8 i) .. +7, whole 128-byte lines; lane l
+    // brings 16-byte chunk (l % 8) ^ (l / 8) of row 8 (wv + 8 i) + l / 8 to slot l % 8 of
+    // that row in LDS, i.e. chunk c of row r sits at r * 128 + 16 (c ^ (r % 8)).
+    const int rs = tid >> 2;   // the row whose A scales this thread stages
+    int tok[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        const int r = i < 2 ? 8 * (wv + 8 * i) + (lane >> 3) : rs;
+        tok[i] = a.sorted_assign[rowbase + min(r, nvalid - 1)] / a.k;
+    }
     uint32_t aoff[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int p = tid + 512 * i, mf = p >> 7, hh = (p >> 6) & 1, ln = p & 63;
-        const int r = mf * 16 + (ln & 15);
-        const int tok = a.sorted_assign[rowbase + min(r, nvalid - 1)] / a.k;
-        aoff[i] = (uint32_t)tok * a.H + (ln >> 4) * 32 + hh * 16;
-    }
+    for (int i = 0; i < 2; ++i) aoff[i] = (uint32_t)tok[i] * a.H + (((lane & 7) ^ (lane >> 3)) << 4);
     uint32_t bsoff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -727,20 +749,34 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pf(G1Args a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) dma16_async(rw, st + kPfStageA + i * 512 * 16, l16, bsoff[i] + kb * kFragBytes);
     };
+    // Scales are loaded before the first DMAs are issued and stored after: the wait for them
+    // then also covers those DMAs, which the first K block needs anyway.  Thread tid stages
+    // the scales of row tid / 4 for K blocks tid % 4 + 4 t.
+    uint32_t sv[kPfMaxKB / 4];
+    {
+        const uint8_t* src = a.xs + (int64_t)tok[2] * KB;
+#pragma unroll
+        for (int t = 0; t < kPfMaxKB / 4; ++t) {
+            const int kb = (tid & 3) + 4 * t;
+            sv[t] = kb < KB ? src[kb] : 0u;
+        }
+    }
+    uint32_t sgu = 0;
+    if (tid < KB) {
+        const uint8_t* sb = a.w13s + ((int64_t)e * KB + tid) * NBS;
+        sgu = (uint32_t)sb[ib] | (uint32_t)sb[a.I / kGroup + ib] << 8;
+    }
     issue(0, 0);
     if (KB > 1) issue(1, 1);
     if (KB > 2) issue(2, 2);
-
-    {   // scales, while the first blocks load
-        const int r = tid >> 2, q = tid & 3;
-        const int tok = a.sorted_assign[rowbase + min(r, nvalid - 1)] / a.k;
-        const uint8_t* src = a.xs + (int64_t)tok * KB;
-        for (int kb = q; kb < KB; kb += 4) s_sa[kb * kPfBM + r] = src[kb];
-        const uint8_t* sb = a.w13s + (int64_t)e * KB * NBS;
-        for (int i = tid; i < KB; i += 512) {
-            s_sg[i] = sb[i * NBS + ib];
-            s_su[i] = sb[i * NBS + a.I / kGroup + ib];
+    {
+        const int sa_pos = (rs >> 6) * 64 + (rs & 15) * 4 + ((rs >> 4) & 3);
+#pragma unroll
+        for (int t = 0; t < kPfMaxKB / 4; ++t) {
+            const int kb = (tid & 3) + 4 * t;
+            if (kb < KB) s_sa[kb * kPfBM + sa_pos] = (uint8_t)sv[t];
         }
+        if (tid < KB) s_sgu[tid] = (uint16_t)sgu;
     }
 
     v4f acc[4][4];   // [row fragment][gate 0, 1 | up 2, 3]
@@ -751,20 +787,24 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pf(G1Args a) {
 
     // Fragments of one K block in registers: read from LDS one step before the MFMAs use
     // them, so the reads of block kb+1 overlap the matrix-core work on block kb.
+    // F.sa byte mi: the scale of row 16 (4 wm + mi) + lane % 16; F.sgu byte 0 gate, byte 1 up.
     struct Frags {
         v8i a[4], b[4];
-        int sa[4], sg, su;
+        int sa, sgu;
     };
+    const int r16 = lane & 15, x8 = r16 & 7;
     auto read = [&](int kb, int st, Frags& F) {
         const uint8_t* cur = buf + st * kPfStage;
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
-            const int mf = wm * 4 + mi;
-            F.a[mi] = lds_frag(cur + mf * kFragBytes, lane);
-            F.sa[mi] = s_sa[kb * kPfBM + mf * 16 + (lane & 15)];
+            // row 16 mf + r16, K chunks 2 (lane / 16) and 2 (lane / 16) + 1 of the swizzled rows
+            const uint8_t* rowp = cur + ((wm * 4 + mi) * 16 + r16) * kGroup;
+            const uint4 lo = *reinterpret_cast<const uint4*>(rowp + (((2 * (lane >> 4)) ^ x8) << 4));
+            const uint4 hi = *reinterpret_cast<const uint4*>(rowp + (((2 * (lane >> 4) + 1) ^ x8) << 4));
+            F.a[mi] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         }
-        F.sg = s_sg[kb];
-        F.su = s_su[kb];
+        F.sa = *reinterpret_cast<const int*>(s_sa + kb * kPfBM + wm * 64 + r16 * 4);
+        F.sgu = s_sgu[kb];
 #pragma unroll
         for (int j = 0; j < 4; ++j) F.b[j] = lds_frag(cur + kPfStageA + (j < 2 ? 2 * wn + j : 6 + 2 * wn + j) * kFragBytes, lane);
     };
@@ -780,7 +820,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pf(G1Args a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi) acc[mi][j] = mfma_fp8(F.a[mi], F.b[j], acc[mi][j], F.sa[mi], j < 2 ? F.sg : F.su);
+            for (int mi = 0; mi < 4; ++mi) acc[mi][j] = mfma_fp8_sel(mi, j >> 1, F.a[mi], F.b[j], acc[mi][j], F.sa, F.sgu);
     };
     if (KB > 2) wait_vm<12>(); else if (KB > 1) wait_vm<6>(); else wait_vm<0>();
     __syncthreads();
@@ -805,7 +845,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pf(G1Args a) {
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
                 const float g = acc[mi][jj][i];
-                const float h = g / (1.0f + expf(-g)) * acc[mi][2 + jj][i];
+                const float h = g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.44269504f)) * acc[mi][2 + jj][i];
                 hv[mi][jj][i] = h;
                 m = fmaxf(m, fabsf(h));
             }

@@ -5,16 +5,18 @@
 // v_mfma_scale_f32_16x16x128_f8f6f4 with the per-(row, 128) activation scales and the
 // 128x128 weight-block scales as the instruction's UE8M0 operand scales.
 //
-// Work: an item is (128-row tile, 256 output columns).  One workgroup of 8 waves (two per
-// SIMD) runs on each CU and walks its share of the item list; wave w owns 32 of the 256
-// columns for all 128 rows (8 x 2 fragments, 64 fp32 accumulators per lane), so no two waves
-// load the same weights.
+// Work: an item is (MT consecutive 128-row tiles of one expert, 256 output columns).  One
+// workgroup of 8 waves (two per SIMD) runs on each CU and walks its share of the item list;
+// wave w owns 32 of the 256 columns for all 128 MT rows (8 MT x 2 fragments), so no two
+// waves load the same weights.  MT = 2 halves the weight bytes per flop, but its 128
+// accumulator registers per lane leave room for only one K block in flight (P = 1), and that
+// measured slower than MT = 1 with four blocks in flight, the default.
 //
 // Operand streams run over one flattened sequence of K blocks covering all of the
 // workgroup's items, so the next item's loads are in flight during the current item's
 // epilogue (the output stores):
-//   * A (the tile's hq slot, 16 KB per K block, already in matrix-core order) goes
-//     global -> LDS by the LDS-DMA form of the buffer load into a ring of P + 1 stages,
+//   * A (the item's hq tile slots, 16 KB per tile and K block, already in matrix-core order)
+//     goes global -> LDS by the LDS-DMA form of the buffer load into a ring of P + 1 stages,
 //     P blocks ahead;
 //   * B (pre-packed weights, 4 KB per wave per K block) goes straight into a register ring,
 //     P blocks ahead, two 1 KB coalesced loads per fragment;
@@ -25,7 +27,7 @@
 //     the matrix-core instruction that consumes it, so no load has to land early.
 // Each K block: wait for this thread's DMA of the block, barrier (everyone's DMA landed;
 // everyone is done with the stage about to be refilled), DMA block + P, B and scale loads of
-// block + P, then the 8 A fragments from LDS and 16 matrix-core instructions per wave.
+// block + P, then the 8 MT A fragments from LDS and 16 MT matrix-core instructions per wave.
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -141,31 +143,44 @@ __device__ __forceinline__ void rb_tile_col(int w, int ncol, int ntiles, int& ti
     tile = t0 + r - col * g;
 }
 
-// Item table in LDS: {tile, column block, expert, first sorted row}, and valid rows.  The
-// workgroup's items are the valid ones among ranks j, j + nx, j + 2 nx, ... of its XCD's
-// share of the super-tile order (ord_item), in that order.  Returns the item count.
+// Item table in LDS: {tile, column block, expert, first sorted row}, and valid rows.  An
+// item covers MT consecutive 128-row tiles of one expert: with MT = 2 only a tile that starts
+// an expert's even 256-row block leads an item, and the item's rows run on into the next
+// tile when the expert has one.  The workgroup's items are the valid ones among its
+// candidates, in order: with the super-tile order (ord) ranks j, j + nx, ... of its XCD's
+// share (ord_item); otherwise its contiguous share of the column-block order (rb_sched).
+// Returns the item count.
+template <int MT>
 __device__ __forceinline__ int rb_fill_items(int ord, int ncol, int ntiles, const int2* tiles, const int32_t* counts,
                                              const int32_t* offsets, int4* s_it, int* s_nv, int cap, int* s_cnt) {
-    if (!ord) {
-        const RbSched s = rb_sched(ntiles * ncol);
-        for (int i = threadIdx.x; i < s.n; i += kRbThreads) {
-            int tile, col;
-            rb_tile_col(s.base + s.stride * i, ncol, ntiles, tile, col);
-            const int2 te = tiles[tile];
-            s_it[i] = make_int4(tile, col, te.x, offsets[te.x] + te.y);
-            s_nv[i] = min(kRbBM, counts[te.x] - te.y);
-        }
-        return min(s.n, cap);
-    }
-    const int total = ord_ranks(ntiles, ncol);   // ranks per XCD
     const int nx = gridDim.x / kRbXcds, x = blockIdx.x % kRbXcds, j = blockIdx.x / kRbXcds;
-    const int ncand = j < total ? (total - 1 - j) / nx + 1 : 0;
+    const RbSched sch = rb_sched(ntiles * ncol);
+    int ncand;
+    if (ord) {
+        const int total = ord_ranks(ntiles, ncol);   // ranks per XCD
+        ncand = j < total ? (total - 1 - j) / nx + 1 : 0;
+    } else {
+        ncand = sch.n;
+    }
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     int base = 0;
     for (int c0 = 0; c0 < ncand; c0 += kRbThreads) {
         const int c = c0 + threadIdx.x;
         int tile = 0, col = 0;
-        const bool v = c < ncand && ord_item(x, j + nx * c, ntiles, ncol, tile, col);
+        bool v = false;
+        if (c < ncand) {
+            if (ord) {
+                v = ord_item(x, j + nx * c, ntiles, ncol, tile, col);
+            } else {
+                rb_tile_col(sch.base + sch.stride * c, ncol, ntiles, tile, col);
+                v = true;
+            }
+        }
+        int2 te = make_int2(0, 0);
+        if (v) {
+            te = tiles[tile];
+            if (MT == 2) v = te.y % (2 * kRbBM) == 0;
+        }
         const uint64_t m = __ballot(v);
         if (lane == 0) s_cnt[wv] = __popcll(m);
         __syncthreads();
@@ -176,9 +191,8 @@ __device__ __forceinline__ int rb_fill_items(int ord, int ncol, int ntiles, cons
         }
         const int pos = off + __popcll(m & ((1ull << lane) - 1));
         if (v && pos < cap) {
-            const int2 te = tiles[tile];
             s_it[pos] = make_int4(tile, col, te.x, offsets[te.x] + te.y);
-            s_nv[pos] = min(kRbBM, counts[te.x] - te.y);
+            s_nv[pos] = min(MT * kRbBM, counts[te.x] - te.y);
         }
         base += tot;
         __syncthreads();
@@ -216,14 +230,15 @@ struct Rb2Args {
     int ord;                    // 1: super-tile work order (ord_item), 0: column blocks per tile group
 };
 
-template <int P>
+template <int P, int MT>
 __global__ __launch_bounds__(kRbThreads, 1) void k_gemm2_rb(Rb2Args a) {
-    constexpr int R = P + 1, NST = P + 1;
-    // per K block and thread: 2 DMA + 4 B + 1 A-scale + 1 B-scale
-    constexpr int kOpsAfter = 6 + (P - 1) * 8;
+    constexpr int R = P + 1, NST = P + 1, MF = 8 * MT;   // MF 16-row fragments per item
+    // per K block and thread: 2 MT DMA + 4 B + MT A-scale + 1 B-scale
+    constexpr int kOpsPerStep = 2 * MT + 4 + MT + 1;
+    constexpr int kOpsAfter = (kOpsPerStep - 2 * MT) + (P - 1) * kOpsPerStep;
     static_assert(kOpsAfter <= 63, "vmcnt range");
 
-    __shared__ __align__(16) uint8_t ring[NST * kRbStage];
+    __shared__ __align__(16) uint8_t ring[NST * MT * kRbStage];
     __shared__ int4 s_it[kRb2MaxItems];
     __shared__ int s_nv[kRb2MaxItems];
 
@@ -233,22 +248,22 @@ __global__ __launch_bounds__(kRbThreads, 1) void k_gemm2_rb(Rb2Args a) {
     const int NB16 = a.H / 16, NBS = a.H / kGroup;
     __shared__ int s_cnt[kRbWaves];
     RbSched sch;
-    sch.n = rb_fill_items(a.ord, ncol, ntiles, a.tiles, a.counts, a.offsets, s_it, s_nv, kRb2MaxItems, s_cnt);
+    sch.n = rb_fill_items<MT>(a.ord, ncol, ntiles, a.tiles, a.counts, a.offsets, s_it, s_nv, kRb2MaxItems, s_cnt);
     if (sch.n <= 0) return;
     __syncthreads();
     const int G = sch.n * KB;
 
-    // ---- A stream: the tile slot of hq, 8 fragments of 2 KB per K block; piece q of this
-    // thread is fragment 4q + wv/2, half wv%2, lane
+    // ---- A stream: the item's hq tile slots (consecutive), 8 MT fragments of 2 KB per K
+    // block; piece q of this thread is fragment 4q + wv/2, half wv%2, lane
     const v4i_rb ra = rb_srd(a.hq, (uint32_t)a.ntiles_max * 8 * KB * kFragBytes);
     const uint32_t lds_ring = rb_lds_addr(ring) + wv * 1024;
     const uint32_t apiece = (uint32_t)((wv >> 1) * KB * kFragBytes + (wv & 1) * 1024 + lane * 16);
     int a_i = 0, a_kb = 0;
     uint32_t abase = __builtin_amdgcn_readfirstlane((uint32_t)s_it[0].x * 8 * KB * kFragBytes);
     auto dma_a = [&](int g) __attribute__((always_inline)) {
-        const uint32_t st = __builtin_amdgcn_readfirstlane(lds_ring + (g % NST) * kRbStage);
+        const uint32_t st = __builtin_amdgcn_readfirstlane(lds_ring + (g % NST) * (MT * kRbStage));
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
+        for (int q = 0; q < 2 * MT; ++q)
             rb_dma16(ra, st + q * 8192, apiece, abase + (uint32_t)(4 * q * KB + a_kb) * kFragBytes);
         const bool wrap = ++a_kb == KB;
         a_kb = wrap ? 0 : a_kb;
@@ -273,13 +288,15 @@ __global__ __launch_bounds__(kRbThreads, 1) void k_gemm2_rb(Rb2Args a) {
     };
     b_setup(0);
     v8i Bf[R][2];
-    v2i_t Sa[R];
+    v2i_t Sa[R][MT];
     int Sb[R];
     const uint32_t l16 = lane * 16, la8 = (lane & 15) * 8;
-    auto load_b = [&](v8i* bf, v2i_t& sa, int& sb) __attribute__((always_inline)) {
+    auto load_b = [&](v8i* bf, v2i_t* sa, int& sb) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) bf[j] = rb_frag(rw, l16, bo[j] + b_kb * kFragBytes);
-        sa = __builtin_amdgcn_raw_buffer_load_b64(rsa, la8, sao + b_kb * kRbBM, 0);
+#pragma unroll
+        for (int t = 0; t < MT; ++t)   // tile t of the item: its hs block follows the previous one
+            sa[t] = __builtin_amdgcn_raw_buffer_load_b64(rsa, la8, sao + (t * KB + b_kb) * kRbBM, 0);
         sb = __builtin_amdgcn_raw_buffer_load_b32(rbs, 0, sbo + b_kb * 4, 0);
         const bool wrap = ++b_kb == KB;
         b_kb = wrap ? 0 : b_kb;
@@ -287,9 +304,9 @@ __global__ __launch_bounds__(kRbThreads, 1) void k_gemm2_rb(Rb2Args a) {
         b_setup(b_i);
     };
 
-    v4f acc[8][2];
+    v4f acc[MF][2];
 #pragma unroll
-    for (int mi = 0; mi < 8; ++mi)
+    for (int mi = 0; mi < MF; ++mi)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
@@ -304,24 +321,26 @@ __global__ __launch_bounds__(kRbThreads, 1) void k_gemm2_rb(Rb2Args a) {
         const int4 it = s_it[c_i];
         const int col = __builtin_amdgcn_readfirstlane(it.y), rowbase = __builtin_amdgcn_readfirstlane(it.w);
         const int nvalid = __builtin_amdgcn_readfirstlane(s_nv[c_i]);
+        // lane holds rows r0 + 16 mi + i; one per-lane row limit keeps the 4 MF row
+        // tests as comparisons with constants
+        const int r0 = 4 * (lane >> 4), lim = nvalid - r0;
+        const int64_t o0 = (int64_t)(rowbase + r0) * a.H + col * 256 + wv * 32 + (lane & 15);
 #pragma unroll
-        for (int mi = 0; mi < 8; ++mi) {
+        for (int mi = 0; mi < MF; ++mi) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int row = mi * 16 + 4 * (lane >> 4) + i;
-                if (row < nvalid) {
-                    const int64_t o = (int64_t)(rowbase + row) * a.H;
+                if (mi * 16 + i < lim) {
+                    const int64_t o = o0 + (int64_t)(mi * 16 + i) * a.H;
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
-                        const int c = col * 256 + (wv * 2 + j) * 16 + (lane & 15);
-                        if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o + c] = f32_to_bf16(acc[mi][j][i]);
-                        else reinterpret_cast<float*>(a.out)[o + c] = acc[mi][j][i];
+                        if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o + j * 16] = f32_to_bf16(acc[mi][j][i]);
+                        else reinterpret_cast<float*>(a.out)[o + j * 16] = acc[mi][j][i];
                     }
                 }
             }
         }
 #pragma unroll
-        for (int mi = 0; mi < 8; ++mi)
+        for (int mi = 0; mi < MF; ++mi)
 #pragma unroll
             for (int j = 0; j < 2; ++j) acc[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
     };
@@ -332,12 +351,23 @@ __global__ __launch_bounds__(kRbThreads, 1) void k_gemm2_rb(Rb2Args a) {
         __syncthreads();
         dma_a(s + P);
         load_b(Bf[un], Sa[un], Sb[un]);
-        const uint8_t* cur = ring + (s % NST) * kRbStage;
+        const uint8_t* cur = ring + (s % NST) * (MT * kRbStage);
+        // an item whose expert has no second tile skips the second tile's fragments
+        const bool second = MT == 2 && __builtin_amdgcn_readfirstlane(s_nv[c_i]) > kRbBM;
+        // fragment mi + 1 is read from LDS while the instructions of fragment mi run; the
+        // scheduling barriers keep the compiler from hoisting all 8 MT reads (registers)
+        v8i af = rb_lds_frag(cur, lane);
 #pragma unroll
-        for (int mi = 0; mi < 8; ++mi) {
-            const v8i af = rb_lds_frag(cur + mi * kFragBytes, lane);
+        for (int mi = 0; mi < MF; ++mi) {
+            v8i an = af;
+            if (mi + 1 < MF) an = rb_lds_frag(cur + (mi + 1) * kFragBytes, lane);
+            if (mi < 8 || second) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) acc[mi][j] = rb_mfma_sel(mi & 3, af, Bf[u][j], acc[mi][j], Sa[u][mi >> 2], Sb[u]);
+                for (int j = 0; j < 2; ++j)
+                    acc[mi][j] = rb_mfma_sel(mi & 3, af, Bf[u][j], acc[mi][j], Sa[u][mi >> 3][(mi & 7) >> 2], Sb[u]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            af = an;
         }
         if (++c_kb == KB) {
             epilogue();
@@ -357,8 +387,12 @@ __global__ __launch_bounds__(kRbThreads, 1) void k_gemm2_rb(Rb2Args a) {
 }
 
 // ----------------------------------------------------------------------------------------
+// K blocks in flight and 128-row tiles per item of the persistent down GEMM
 #ifndef MOE_RB_P
 #define MOE_RB_P 4
+#endif
+#ifndef MOE_RB_MT
+#define MOE_RB_MT 1
 #endif
 
 static int rb_grid() {
@@ -398,7 +432,7 @@ hipError_t launch_gemm2_rb(const FfnArgs& f, const FfnWs& w, int ntiles_max, int
                        f.E, KB, NBS, w.bs);
     Rb2Args g2{w.hq, w.hs, w.bs, f.H, f.I, f.E, ntiles_max, w.tiles, w.ntiles, f.counts, f.offsets, f.w2p, f.out,
                f.out_bf16, ord};
-    hipLaunchKernelGGL(k_gemm2_rb<MOE_RB_P>, dim3(rb_grid()), dim3(kRbThreads), 0, st, g2);
+    hipLaunchKernelGGL((k_gemm2_rb<MOE_RB_P, MOE_RB_MT>), dim3(rb_grid()), dim3(kRbThreads), 0, st, g2);
     return hipGetLastError();
 }
 

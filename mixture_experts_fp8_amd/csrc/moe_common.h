@@ -60,12 +60,21 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// Max over aligned groups of 16 lanes.
+// Lane exchange inside rows of 16 lanes by a DPP control word (a VALU operand modifier, no
+// LDS round trip as with ds_bpermute): 0xB1 swaps neighbours, 0x4E swaps pairs within a
+// quad, 0x124 / 0x128 rotate the row by 4 / 8 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Max over aligned groups of 16 lanes (the hardware rows): within quads, then across the
+// four quads by rotating the row by 4 and 8 lanes.
 __device__ __forceinline__ float max16(float v) {
-    v = fmaxf(v, __shfl_xor(v, 1));
-    v = fmaxf(v, __shfl_xor(v, 2));
-    v = fmaxf(v, __shfl_xor(v, 4));
-    v = fmaxf(v, __shfl_xor(v, 8));
+    v = fmaxf(v, dpp_f32<0xB1>(v));
+    v = fmaxf(v, dpp_f32<0x4E>(v));
+    v = fmaxf(v, dpp_f32<0x124>(v));
+    v = fmaxf(v, dpp_f32<0x128>(v));
     return v;
 }
 

@@ -148,7 +148,7 @@ def test_fused_workload_full(cfg):
     print(f"  rel fro {fro:.2e} rel max {mx:.2e} active experts {(counts > 0).sum()}", flush=True)
 
 
-@pytest.mark.parametrize("cfg,ntok", [(4, 2), (5, 4)])
+@pytest.mark.parametrize("cfg,ntok", [(4, 2), (5, 4), (6, 3)])
 def test_fused_workload_sampled(cfg, ntok):
     wl = W.CONFIGS[cfg]
     print("fused sampled", cfg, W.describe(wl), flush=True)
