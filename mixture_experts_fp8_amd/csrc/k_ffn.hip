@@ -76,6 +76,8 @@ struct G1Args {
     uint8_t* hq;
     uint8_t* hs;
     int ord;    // work order of the 128-row-tile kernels: 1 super-tiles (ord_item), 0 column blocks
+    const int32_t* pairs;    // 256-row items: first tile of each pair, and the pair count
+    const int32_t* npairs;
 };
 
 __device__ __forceinline__ v8i lds_frag(const uint8_t* base, int lane) {
@@ -282,6 +284,8 @@ struct G2Args {
     void* out;
     int out_bf16;
     int ord;
+    const int32_t* pairs;
+    const int32_t* npairs;
 };
 
 // down GEMM: wave (wm, wn) computes MFW m-frags x NFW column frags; the workgroup covers
@@ -653,6 +657,7 @@ __device__ __forceinline__ bool pf_work_item(int ord, int ncol, int ntiles, int&
 // consecutive bytes (no LDS bank conflicts).
 
 typedef int v4i_t __attribute__((ext_vector_type(4)));
+typedef int v2i_t __attribute__((ext_vector_type(2)));
 constexpr int kPfdStages = 3;
 
 // Buffer descriptor in scalar registers (the base and size are wave-uniform).
@@ -996,6 +1001,318 @@ __global__ __launch_bounds__(512, 1) void k_gemm2_pf(G2Args a) {
 }
 
 // ----------------------------------------------------------------------------------------
+// 256-row items for experts with many rows: an item is a pair of consecutive 128-row tiles
+// of one expert (the second may be absent) and 256 columns, so each K block moves 64 KB
+// (A 32 KB + B 32 KB) per 256 x 256 x 128 product instead of 48 KB per 128 x 256 x 128:
+// a third fewer bytes from L2 per flop, and the per-item fill and epilogue spread over twice
+// the work.  8 waves as 2 (rows) x 4 (columns), each 128 x 64 (8 x 4 fragments, 128
+// accumulator registers per lane), two waves per SIMD.  Two 64 KB LDS stages: block kb + 1
+// loads while the waves compute block kb.  The tile list and the hq / hs layouts are those
+// of the 128-row tiles.
+constexpr int kP2Rows = 256, kP2StageA = 16 * kFragBytes, kP2Stage = kP2StageA + 16 * kFragBytes;   // 64 KB
+
+// Pair list: for each expert, pairs[] holds the index of the first tile of each of its
+// ceil(count / 256) pairs (tiles of 128 rows in expert order, as k_tiles writes them).
+__global__ __launch_bounds__(1024) void k_pairs(const int32_t* __restrict__ counts, int E, int32_t* __restrict__ pairs,
+                                                int32_t* __restrict__ npairs) {
+    __shared__ int s_t[16], s_p[16];
+    const int e = threadIdx.x;
+    const int c = e < E ? counts[e] : 0;
+    const int nt = (c + kPfBM - 1) / kPfBM, np = (c + kP2Rows - 1) / kP2Rows;
+    const int lane = e & 63, wv = e >> 6;
+    int vt = nt, vp = np;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int ut = __shfl_up(vt, o), up = __shfl_up(vp, o);
+        if (lane >= o) {
+            vt += ut;
+            vp += up;
+        }
+    }
+    if (lane == 63) {
+        s_t[wv] = vt;
+        s_p[wv] = vp;
+    }
+    __syncthreads();
+    int at = 0, ap = 0;
+    for (int w = 0; w < wv; ++w) {
+        at += s_t[w];
+        ap += s_p[w];
+    }
+    const int t0 = vt + at - nt, p0 = vp + ap - np;
+    for (int i = 0; i < np; ++i) pairs[p0 + i] = t0 + 2 * i;
+    if (e == 1023) *npairs = vp + ap;
+}
+
+__global__ __launch_bounds__(512, 1) void k_gemm1_p2(G1Args a) {
+    int ib, pair;
+    if (!pf_work_item(a.ord, a.I / kGroup, __builtin_amdgcn_readfirstlane(*a.npairs), pair, ib)) return;
+    const int t0 = __builtin_amdgcn_readfirstlane(a.pairs[pair]);
+    const int2 te = a.tiles[t0];
+    const int e = __builtin_amdgcn_readfirstlane(te.x), m0 = __builtin_amdgcn_readfirstlane(te.y);
+    const int nvalid = min(kP2Rows, a.counts[e] - m0);
+    const bool second = nvalid > kPfBM;
+    const int rowbase = __builtin_amdgcn_readfirstlane(a.offsets[e] + m0);
+    const int KB = a.H / kGroup;
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wv >> 2, wn = wv & 3;
+
+    __shared__ __align__(16) uint8_t buf[2 * kP2Stage];
+    __shared__ __align__(16) uint8_t s_sa[kPfMaxKB * kP2Rows];   // [kb][wm][row % 16][fragment of wm]
+    __shared__ uint16_t s_sgu[kPfMaxKB];                        // gate scale | up scale << 8
+    __shared__ float s_amax[4][kP2Rows];
+
+    const int NB16 = 2 * a.I / 16, NBS = 2 * a.I / kGroup;
+    const v4i_t ra = make_srd(a.xq, (uint32_t)a.T * a.H);
+    const v4i_t rw = make_srd(a.w13p + (int64_t)e * NB16 * KB * kFragBytes, (uint32_t)NB16 * KB * kFragBytes);
+    // A: wave instruction i moves rows 8 (wv + 8 i) .. +7 as whole lines into the XOR-swizzled
+    // row layout (chunk c of row r at r * 128 + 16 (c ^ (r % 8))), as the 128-row kernel does
+    const int rs = tid >> 1;   // the row whose A scales this thread stages (with its neighbour)
+    int tok[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        const int r = i < 4 ? 8 * (wv + 8 * i) + (lane >> 3) : rs;
+        tok[i] = a.sorted_assign[rowbase + min(r, nvalid - 1)] / a.k;
+    }
+    uint32_t aoff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) aoff[i] = (uint32_t)tok[i] * a.H + (((lane & 7) ^ (lane >> 3)) << 4);
+    uint32_t bsoff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int q = wv * 64 + 512 * i, f = q >> 7, hh = (q >> 6) & 1;
+        const int n16 = f < 8 ? ib * 8 + f : a.I / 16 + ib * 8 + (f - 8);
+        bsoff[i] = __builtin_amdgcn_readfirstlane(n16 * KB * kFragBytes + hh * 1024);
+    }
+    const uint32_t l16 = lane * 16;
+    const uint32_t lds_w = lds_addr(buf) + wv * 1024;
+    auto issue = [&](int kb, int s) __attribute__((always_inline)) {
+        const uint32_t st = __builtin_amdgcn_readfirstlane(lds_w + s * kP2Stage);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16_async(ra, st + i * 8192, aoff[i], kb * kGroup);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16_async(rw, st + kP2StageA + i * 8192, l16, bsoff[i] + kb * kFragBytes);
+    };
+    // scales: loaded before the first DMAs, stored after (their wait also covers block 0)
+    uint32_t sv[kPfMaxKB / 2];
+    {
+        const uint8_t* src = a.xs + (int64_t)tok[4] * KB;
+#pragma unroll
+        for (int t = 0; t < kPfMaxKB / 2; ++t) {
+            const int kb = (tid & 1) + 2 * t;
+            sv[t] = kb < KB ? src[kb] : 0u;
+        }
+    }
+    uint32_t sgu = 0;
+    if (tid < KB) {
+        const uint8_t* sb = a.w13s + ((int64_t)e * KB + tid) * NBS;
+        sgu = (uint32_t)sb[ib] | (uint32_t)sb[a.I / kGroup + ib] << 8;
+    }
+    issue(0, 0);
+    {
+        const int sa_pos = (rs >> 7) * 128 + (rs & 15) * 8 + ((rs >> 4) & 7);
+#pragma unroll
+        for (int t = 0; t < kPfMaxKB / 2; ++t) {
+            const int kb = (tid & 1) + 2 * t;
+            if (kb < KB) s_sa[kb * kP2Rows + sa_pos] = (uint8_t)sv[t];
+        }
+        if (tid < KB) s_sgu[tid] = (uint16_t)sgu;
+    }
+
+    v4f acc[8][4];   // [row fragment][gate 0, 1 | up 2, 3]
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    const int r16 = lane & 15, x8 = r16 & 7, c2 = 2 * (lane >> 4);
+    // the rows of a missing second tile are not computed
+    const bool active = wm == 0 || second;
+    for (int kb = 0; kb < KB; ++kb) {
+        wait_vm<0>();      // block kb landed (this thread's pieces) ...
+        __syncthreads();   // ... and everyone's; every wave is done with block kb - 1's stage
+        if (kb + 1 < KB) issue(kb + 1, (kb + 1) & 1);
+        if (active) {
+            const uint8_t* cur = buf + (kb & 1) * kP2Stage;
+            const v2i_t sa = *reinterpret_cast<const v2i_t*>(s_sa + kb * kP2Rows + wm * 128 + r16 * 8);
+            const int sg = s_sgu[kb];
+            v8i bf[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                bf[j] = lds_frag(cur + kP2StageA + (j < 2 ? 2 * wn + j : 6 + 2 * wn + j) * kFragBytes, lane);
+#pragma unroll
+            for (int mi = 0; mi < 8; ++mi) {
+                const uint8_t* rowp = cur + ((wm * 8 + mi) * 16 + r16) * kGroup;
+                const uint4 lo = *reinterpret_cast<const uint4*>(rowp + ((c2 ^ x8) << 4));
+                const uint4 hi = *reinterpret_cast<const uint4*>(rowp + (((c2 + 1) ^ x8) << 4));
+                const v8i af = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[mi][j] = mfma_fp8_sel(mi & 3, j >> 1, af, bf[j], acc[mi][j], sa[mi >> 2], sg);
+            }
+        }
+    }
+
+    // SwiGLU, per-row amax over the item's 128 h columns, E4M3 requantisation
+    float hv[8][2][4];
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float m = 0.f;
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const float g = acc[mi][jj][i];
+                const float h = g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.44269504f)) * acc[mi][2 + jj][i];
+                hv[mi][jj][i] = h;
+                m = fmaxf(m, fabsf(h));
+            }
+            m = max16(m);
+            if (r16 == 0) s_amax[wn][(wm * 8 + mi) * 16 + 4 * (lane >> 4) + i] = m;
+        }
+    }
+    __syncthreads();   // also: every wave is done reading the stages before buf is reused
+    uint8_t* s_h = buf;   // [256 rows][128]
+    const int KB2 = a.I / kGroup;
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = (wm * 8 + mi) * 16 + 4 * (lane >> 4) + i;
+            const float am = fmaxf(fmaxf(s_amax[0][row], s_amax[1][row]), fmaxf(s_amax[2][row], s_amax[3][row]));
+            const int ex = scale_exponent(am);
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+                s_h[row * 128 + (2 * wn + jj) * 16 + r16] = (uint8_t)(cvt2_e4m3(ldexpf(hv[mi][jj][i], -ex), 0.f) & 0xFFu);
+            if (wn == 0 && r16 == 0 && active) {   // [tile][kb][row % 16][row / 16]
+                const int rl = row & 127;
+                a.hs[(((int64_t)(t0 + wm) * KB2 + ib) * 16 + (rl & 15)) * 8 + (rl >> 4)] = (uint8_t)(ex + 127);
+            }
+        }
+    }
+    __syncthreads();
+    const int nf = second ? 16 : 8;
+    for (int q = tid; q < nf * 128; q += 512) {
+        const int mf = q >> 7, w = q & 127, hh = w >> 6, ln = w & 63;
+        const uint4 v = *reinterpret_cast<const uint4*>(s_h + (mf * 16 + (ln & 15)) * 128 + (ln >> 4) * 32 + hh * 16);
+        *reinterpret_cast<uint4*>(a.hq + (((int64_t)t0 * 8 + mf) * KB2 + ib) * kFragBytes + hh * 1024 + ln * 16) = v;
+    }
+}
+
+__global__ __launch_bounds__(512, 1) void k_gemm2_p2(G2Args a) {
+    int nb, pair;
+    if (!pf_work_item(a.ord, a.H / 256, __builtin_amdgcn_readfirstlane(*a.npairs), pair, nb)) return;
+    const int t0 = __builtin_amdgcn_readfirstlane(a.pairs[pair]);
+    const int2 te = a.tiles[t0];
+    const int e = __builtin_amdgcn_readfirstlane(te.x), m0 = __builtin_amdgcn_readfirstlane(te.y);
+    const int nvalid = min(kP2Rows, a.counts[e] - m0);
+    const bool second = nvalid > kPfBM;
+    const int rowbase = __builtin_amdgcn_readfirstlane(a.offsets[e] + m0);
+    const int KB = a.I / kGroup;
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wv >> 2, wn = wv & 3;
+
+    __shared__ __align__(16) uint8_t buf[2 * kP2Stage];
+    __shared__ __align__(16) uint8_t s_hs[2 * kPfMaxKB * kPfBM];   // [tile of the pair][kb][row % 16][row / 16]
+    __shared__ uint16_t s_sb[kPfMaxKB];                            // scales of column blocks 2 nb, 2 nb + 1
+
+    const int NB16 = a.H / 16, NBS = a.H / kGroup;
+    const int nt = second ? 2 : 1;
+    // a missing second tile reads as zeros (outside the descriptor's range)
+    const v4i_t ra = make_srd(a.hq + (int64_t)t0 * 8 * KB * kFragBytes, (uint32_t)nt * 8 * KB * kFragBytes);
+    const v4i_t rw = make_srd(a.w2p + (int64_t)e * NB16 * KB * kFragBytes, (uint32_t)NB16 * KB * kFragBytes);
+    const uint32_t l16 = lane * 16;
+    // piece group g = wv + 8 i: fragment g / 2, half g % 2 (A: of the pair's 16 row
+    // fragments; B: of the item's 16 column fragments)
+    uint32_t asoff[4], bsoff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int g = wv + 8 * i;
+        asoff[i] = __builtin_amdgcn_readfirstlane((g >> 1) * KB * kFragBytes + (g & 1) * 1024);
+        bsoff[i] = __builtin_amdgcn_readfirstlane((nb * 16 + (g >> 1)) * KB * kFragBytes + (g & 1) * 1024);
+    }
+    const uint32_t lds_w = lds_addr(buf) + wv * 1024;
+    auto issue = [&](int kb, int s) __attribute__((always_inline)) {
+        const uint32_t st = __builtin_amdgcn_readfirstlane(lds_w + s * kP2Stage);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16_async(ra, st + i * 8192, l16, asoff[i] + kb * kFragBytes);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16_async(rw, st + kP2StageA + i * 8192, l16, bsoff[i] + kb * kFragBytes);
+    };
+    // scales (loaded before the first DMAs, stored after): the pair's hs blocks as dwords
+    // (same layout in LDS), the two weight-block scales per K block
+    const int nsd = nt * KB * 32;   // dwords
+    uint32_t sv[kPfMaxKB / 4];
+    {
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(a.hs + (int64_t)t0 * KB * kPfBM);
+#pragma unroll
+        for (int t = 0; t < kPfMaxKB / 4; ++t) {
+            const int i = tid + 512 * t;
+            sv[t] = i < nsd ? src[i] : 0u;
+        }
+    }
+    uint32_t sbv = 0;
+    if (tid < KB) {
+        const uint8_t* sb = a.w2s + ((int64_t)e * KB + tid) * NBS + nb * 2;
+        sbv = (uint32_t)sb[0] | (uint32_t)sb[1] << 8;
+    }
+    issue(0, 0);
+    {
+#pragma unroll
+        for (int t = 0; t < kPfMaxKB / 4; ++t) {
+            const int i = tid + 512 * t;
+            if (i < nsd) reinterpret_cast<uint32_t*>(s_hs)[i] = sv[t];
+        }
+        if (tid < KB) s_sb[tid] = (uint16_t)sbv;
+    }
+
+    v4f acc[8][4];
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    const int r16 = lane & 15;
+    const bool active = wm == 0 || second;
+    for (int kb = 0; kb < KB; ++kb) {
+        wait_vm<0>();
+        __syncthreads();
+        if (kb + 1 < KB) issue(kb + 1, (kb + 1) & 1);
+        if (active) {
+            const uint8_t* cur = buf + (kb & 1) * kP2Stage;
+            const v2i_t sa = *reinterpret_cast<const v2i_t*>(s_hs + ((wm * KB + kb) * 16 + r16) * 8);
+            const int sb = (s_sb[kb] >> (8 * (wn >> 1))) & 0xFF;
+            v8i bf[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bf[j] = lds_frag(cur + kP2StageA + (wn * 4 + j) * kFragBytes, lane);
+#pragma unroll
+            for (int mi = 0; mi < 8; ++mi) {
+                const v8i af = lds_frag(cur + (wm * 8 + mi) * kFragBytes, lane);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[mi][j] = mfma_fp8_sel(mi & 3, 0, af, bf[j], acc[mi][j], sa[mi >> 2], sb);
+            }
+        }
+    }
+
+    // lane holds rows wm * 128 + 16 mi + r0 + i; one per-lane limit for the row tests
+    const int r0 = 4 * (lane >> 4), lim = nvalid - wm * kPfBM - r0;
+    const int64_t o0 = (int64_t)(rowbase + wm * kPfBM + r0) * a.H + nb * 256 + wn * 64 + r16;
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (mi * 16 + i < lim) {
+                const int64_t o = o0 + (int64_t)(mi * 16 + i) * a.H;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o + j * 16] = f32_to_bf16(acc[mi][j][i]);
+                    else reinterpret_cast<float*>(a.out)[o + j * 16] = acc[mi][j][i];
+                }
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------------------
 // Decode tiles (16 rows) while experts average at most this many rows; 128-row tiles above.
 #ifndef MOE_DEC_MAX_AVG_ROWS
 #define MOE_DEC_MAX_AVG_ROWS 24
@@ -1004,22 +1321,32 @@ __global__ __launch_bounds__(512, 1) void k_gemm2_pf(G2Args a) {
 // The super-tile order pays off once the tiles fill several of its 64-tile windows.
 int ffn_super_tile_order(int ntiles_max) { return ntiles_max >= 512 ? 1 : 0; }
 
+// 256-row items (tile pairs) once experts average at least this many rows.
+#ifndef MOE_PAIR_MIN_AVG_ROWS
+#define MOE_PAIR_MIN_AVG_ROWS 256
+#endif
+
 FfnPlan ffn_plan(int T, int k, int E, int quant) {
     const int64_t A = (int64_t)T * k;
     const int64_t avg = A / E;
     FfnPlan p;
     p.BM = (avg <= MOE_DEC_MAX_AVG_ROWS || quant != kQuantFp8Block128) ? 16 : 128;
     p.ntiles_max = (int)(ceil_div(A, p.BM) + std::min<int64_t>(E, A));
+    p.pairs = p.BM == 128 && avg >= MOE_PAIR_MIN_AVG_ROWS;
+    // an expert's pairs number ceil(tiles / 2)
+    p.npairs_max = (p.ntiles_max + (int)std::min<int64_t>(E, A)) / 2 + 1;
     return p;
 }
 
 // workspace: tiles [ntiles_max] int2 | ntiles int | hq [ntiles_max*BM, I] | hs [ntiles_max*BM, I/128]
 //            | (128-row tiles) down-GEMM weight-scale table [E][H/128][I/128] u32
+//            | pairs [npairs_max] int | npairs int
 static size_t ffn_ws_plan(const FfnPlan& p, int H, int I, int E) {
     const size_t rows = (size_t)p.ntiles_max * p.BM;
     // hs holds one scale per 32 columns of h (the MX schemes; the 128 scheme uses a quarter)
     size_t n = align256((size_t)p.ntiles_max * 8) + align256(4) + align256(rows * I) + align256(rows * (I / 32));
     if (p.BM == 128) n += align256(ffn_rb_scale_table_bytes(H, I, E));
+    n += align256((size_t)p.npairs_max * 4) + align256(4);
     return n;
 }
 size_t ffn_workspace_bytes(int T, int H, int I, int E, int k) {
@@ -1083,6 +1410,26 @@ static hipError_t run_ffn_pf(const FfnArgs& f, const FfnPlan& p, const FfnWs& w,
     return hipGetLastError();
 }
 
+static hipError_t run_ffn_p2(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid) {
+    hipLaunchKernelGGL(k_pairs, dim3(1), dim3(1024), 0, st, f.counts, f.E, w.pairs, w.npairs);
+    const int ord = ffn_super_tile_order(p.ntiles_max);
+    G1Args g1{f.xq, f.xs, f.T, f.k, f.H, f.I, f.counts, f.offsets, f.sorted_assign, w.tiles, w.ntiles, f.w13p, f.w13s,
+              w.hq, w.hs, ord, w.pairs, w.npairs};
+    const int grid1 = ord ? kXcds * ord_ranks(p.npairs_max, f.I / kGroup)
+                          : (int)(ceil_div((int64_t)(f.I / kGroup) * p.npairs_max, kXcds) * kXcds);
+    hipLaunchKernelGGL(k_gemm1_p2, dim3(grid1), dim3(512), 0, st, g1);
+    if (mid) {
+        const hipError_t e = hipEventRecord(mid, st);
+        if (e != hipSuccess) return e;
+    }
+    G2Args g2{w.hq, w.hs, f.H, f.I, f.counts, f.offsets, w.tiles, w.ntiles, f.w2p, f.w2s, f.out, f.out_bf16, ord,
+              w.pairs, w.npairs};
+    const int grid2 = ord ? kXcds * ord_ranks(p.npairs_max, f.H / 256)
+                          : (int)(ceil_div((int64_t)(f.H / 256) * p.npairs_max, kXcds) * kXcds);
+    hipLaunchKernelGGL(k_gemm2_p2, dim3(grid2), dim3(512), 0, st, g2);
+    return hipGetLastError();
+}
+
 FfnWs carve_ffn_ws(const FfnArgs& f, void* ws) {
     const FfnPlan p = ffn_plan(f.T, f.k, f.E, f.quant);
     const size_t rows = (size_t)p.ntiles_max * p.BM;
@@ -1097,6 +1444,10 @@ FfnWs carve_ffn_ws(const FfnArgs& f, void* ws) {
     r.hs = w;
     w += align256(rows * (f.I / 32));
     r.bs = p.BM == 128 ? reinterpret_cast<uint32_t*>(w) : nullptr;
+    if (p.BM == 128) w += align256(ffn_rb_scale_table_bytes(f.H, f.I, f.E));
+    r.pairs = reinterpret_cast<int32_t*>(w);
+    w += align256((size_t)p.npairs_max * 4);
+    r.npairs = reinterpret_cast<int32_t*>(w);
     return r;
 }
 
@@ -1112,8 +1463,12 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, void* ws, hipStream_t st, hipEve
     if (p.BM == 16) return run_ffn_dec<MOE_DEC_GEMM1, MOE_DEC_GEMM2>(f, p, w, st, mid);
     // 128-row tiles: the staged kernels need the tile's A scales in LDS and 256-column
     // down-GEMM blocks; other shapes take the plain 128-row kernels
-    if (f.H / kGroup <= kPfMaxKB && f.I / kGroup <= kPfMaxKB && f.H % 256 == 0)
+    if (f.H / kGroup <= kPfMaxKB && f.I / kGroup <= kPfMaxKB && f.H % 256 == 0) {
+#ifndef MOE_NO_PAIRS
+        if (p.pairs) return run_ffn_p2(f, p, w, st, mid);
+#endif
         return run_ffn_pf(f, p, w, st, mid);
+    }
     return run_ffn<4, 4, 4, 2, 2, 2, 2>(f, p, w, st, mid);
 }
 

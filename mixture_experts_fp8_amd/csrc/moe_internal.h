@@ -61,6 +61,8 @@ hipError_t launch_tiles(const int32_t* counts, int E, int BM, int2* tiles, int32
 struct FfnPlan {
     int BM;           // rows per tile
     int ntiles_max;   // grid bound on tiles
+    int pairs;        // 1: the 128-row tiles run as 256-row items (pairs of tiles)
+    int npairs_max;   // grid bound on pairs
 };
 FfnPlan ffn_plan(int T, int k, int E, int quant = kQuantFp8Block128);
 // covers every quantisation scheme
@@ -87,6 +89,8 @@ struct FfnWs {
     uint8_t* hq;
     uint8_t* hs;
     uint32_t* bs;        // 128-row tiles: down-GEMM weight-block scales per [expert][column block][kb]
+    int32_t* pairs;      // 256-row items: index of the first tile of each pair
+    int32_t* npairs;
 };
 FfnWs carve_ffn_ws(const FfnArgs& a, void* ws);
 // `mid`: optional event recorded between the gate+up and the down GEMM; tiles_ready: the

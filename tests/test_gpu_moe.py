@@ -30,6 +30,10 @@ SMALL = {
     "staged_tiles_K_not_multiple_of_3": W.Workload(129, "bm128k", T=700, H=512, I=640, E=8, k=2),
     "bm128_path": W.Workload(124, "bm128", T=1100, H=256, I=384, E=8, k=2),
     "staged_tiles_single_k_block": W.Workload(130, "bm128kb1", T=700, H=256, I=128, E=4, k=2),
+    # experts averaging >= 256 rows: 256-row items (tile pairs), with single-tile pairs and
+    # ragged second tiles from the skew
+    "tile_pairs_skewed": W.Workload(131, "p2s", T=1500, H=256, I=256, E=8, k=4, bias="normal1.5"),
+    "tile_pairs_zipf_kb6": W.Workload(132, "p2z", T=900, H=768, I=384, E=6, k=2, bias="zipf"),
     "sigmoid_groups": W.Workload(125, "grp", T=96, H=384, I=256, E=32, k=4, scoring="sigmoid", group_count=4,
                                  k_group=2, group_select_mode=1, routed_scaling_factor=2.5),
     "prelude_small": W.Workload(126, "pre", T=9, H=512, I=256, E=16, k=4, prelude=True),
