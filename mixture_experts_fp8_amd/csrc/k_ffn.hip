@@ -19,6 +19,7 @@
 #include "moe_internal.h"
 
 #include <algorithm>
+#include <type_traits>
 
 // Decode-tile configurations (fragments per wave, waves per workgroup, K blocks in flight)
 // of the gate+up and the down GEMM; fixed at build time.
@@ -706,6 +707,49 @@ __device__ __forceinline__ v4f mfma_fp8_sel(int ba, int bb, v8i a, v8i b, v4f ac
 #undef MOE_SEL
 }
 
+// ---- epilogue helpers of the gate/up kernels
+// Max over each aligned group of 16 lanes for four values at once: the four DPP chains are
+// interleaved, so no step waits on its own predecessor.
+__device__ __forceinline__ void max16x4(float (&m)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m[i] = fmaxf(m[i], dpp_f32<0xB1>(m[i]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m[i] = fmaxf(m[i], dpp_f32<0x4E>(m[i]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m[i] = fmaxf(m[i], dpp_f32<0x124>(m[i]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m[i] = fmaxf(m[i], dpp_f32<0x128>(m[i]));
+}
+
+// SwiGLU of one 16-row fragment: gate columns acc[jj], up columns acc[2 + jj] (jj = 0, 1)
+// -> h[jj][i]; m[i] = max |h| of row 4 (lane / 16) + i over the 32 columns of the two
+// fragments (in every lane of the 16-lane group).
+__device__ __forceinline__ void swiglu_frag(const v4f* acc, float (&h)[2][4], float (&m)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        m[i] = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const float g = acc[jj][i];
+            h[jj][i] = g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.44269504f)) * acc[2 + jj][i];
+            m[i] = fmaxf(m[i], fabsf(h[jj][i]));
+        }
+    }
+    max16x4(m);
+}
+
+// E4M3 bytes of a lane quad's 4 x 4 block (lane 4Q + q of a 16-lane group holds column
+// 4Q + q of rows 0..3, scaled by 2^-ex[i]), transposed within the quad (two DPP exchanges
+// and a byte select): the result holds row q, columns 4Q .. 4Q + 3 (byte k = column 4Q + k).
+__device__ __forceinline__ uint32_t e4m3_quad_rows(const float (&h)[4], const int (&ex)[4], int q) {
+    const int x = (int)cvt4_e4m3(ldexpf(h[0], -ex[0]), ldexpf(h[1], -ex[1]), ldexpf(h[2], -ex[2]), ldexpf(h[3], -ex[3]));
+    const int z = __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);   // lane q ^ 2
+    const int x1 = q < 2 ? (int)(((uint32_t)x & 0xFFFFu) | ((uint32_t)z << 16))
+                         : (int)(((uint32_t)z >> 16) | ((uint32_t)x & 0xFFFF0000u));
+    const int w = __builtin_amdgcn_update_dpp(0, x1, 0xB1, 0xF, 0xF, false);  // lane q ^ 1
+    return __builtin_amdgcn_perm((uint32_t)w, (uint32_t)x1, (q & 1) ? 0x03070105u : 0x06020400u);
+}
+
 __global__ __launch_bounds__(512, 1) void k_gemm1_pf(G1Args a) {
     int ib, tile;
     if (!pf_work_item(a.ord, a.I / kGroup, __builtin_amdgcn_readfirstlane(*a.ntiles), tile, ib)) return;
@@ -720,7 +764,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pf(G1Args a) {
     __shared__ __align__(16) uint8_t buf[kPfdStages * kPfStage];
     __shared__ __align__(16) uint8_t s_sa[kPfMaxKB * kPfBM];   // [kb][wm][row % 16][fragment of wm]
     __shared__ uint16_t s_sgu[kPfMaxKB];                      // gate scale | up scale << 8
-    __shared__ float s_amax[4][kPfBM];
+    __shared__ __align__(16) float s_amax[kPfBM][4];   // [row][column wave]
 
     const int NB16 = 2 * a.I / 16, NBS = 2 * a.I / kGroup;
     const v4i_t ra = make_srd(a.xq, (uint32_t)a.T * a.H);
@@ -798,6 +842,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pf(G1Args a) {
         int sa, sgu;
     };
     const int r16 = lane & 15, x8 = r16 & 7;
+    // row fragments of this wave holding valid rows (the rest are skipped: wave-uniform)
+    const int nact = __builtin_amdgcn_readfirstlane(min(4, max(0, (nvalid - wm * 64 + 15) >> 4)));
     auto read = [&](int kb, int st, Frags& F) {
         const uint8_t* cur = buf + st * kPfStage;
 #pragma unroll
@@ -817,7 +863,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pf(G1Args a) {
     // wait until block kb+1 has landed everywhere (the barrier also finds every wave done
     // reading stage st), refill stage st with block kb+3, read block kb+1 into G, then the
     // 16 MFMAs of block kb.
-    auto step = [&](int kb, int st, Frags& F, Frags& G) {
+    auto step = [&](int kb, int st, Frags& F, Frags& G) __attribute__((always_inline)) {
         if (kb + 2 < KB) wait_vm<6>(); else wait_vm<0>();
         __syncthreads();
         if (kb + 3 < KB) issue(kb + 3, st);
@@ -825,7 +871,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pf(G1Args a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi) acc[mi][j] = mfma_fp8_sel(mi, j >> 1, F.a[mi], F.b[j], acc[mi][j], F.sa, F.sgu);
+            for (int mi = 0; mi < 4; ++mi)
+                if (mi < nact) acc[mi][j] = mfma_fp8_sel(mi, j >> 1, F.a[mi], F.b[j], acc[mi][j], F.sa, F.sgu);
     };
     if (KB > 2) wait_vm<12>(); else if (KB > 1) wait_vm<6>(); else wait_vm<0>();
     __syncthreads();
@@ -841,45 +888,49 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pf(G1Args a) {
         }
     }
 
+    // SwiGLU and per-row amax over the tile's 128 h columns (4 waves x 2 fragments)
     float hv[4][2][4];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
+        if (mi < nact) {
+            float m[4];
+            swiglu_frag(acc[mi], hv[mi], m);
+            if (r16 == 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float m = 0.f;
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const float g = acc[mi][jj][i];
-                const float h = g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.44269504f)) * acc[mi][2 + jj][i];
-                hv[mi][jj][i] = h;
-                m = fmaxf(m, fabsf(h));
+                for (int i = 0; i < 4; ++i) s_amax[(wm * 4 + mi) * 16 + 4 * (lane >> 4) + i][wn] = m[i];
             }
-            m = max16(m);
-            if ((lane & 15) == 0) s_amax[wn][(wm * 4 + mi) * 16 + 4 * (lane >> 4) + i] = m;
         }
     }
     __syncthreads();   // also: every wave is done reading the stages before buf is reused
+    // E4M3 requantisation; h staged as [128 rows][128] bytes, 16-byte chunks XOR-swizzled by
+    // row % 8, one dword (4 columns of one row) per lane and fragment
     uint8_t* s_h = buf;
+    const int q = lane & 3, g4 = 4 * (lane >> 4);
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
+        if (mi < nact) {
+            int ex[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = (wm * 4 + mi) * 16 + 4 * (lane >> 4) + i;
-            const float am = fmaxf(fmaxf(s_amax[0][row], s_amax[1][row]), fmaxf(s_amax[2][row], s_amax[3][row]));
-            const int ex = scale_exponent(am);
+            for (int i = 0; i < 4; ++i) {
+                const int row = (wm * 4 + mi) * 16 + g4 + i;
+                const float4 am4 = *reinterpret_cast<const float4*>(s_amax[row]);
+                ex[i] = scale_exponent(fmaxf(fmaxf(am4.x, am4.y), fmaxf(am4.z, am4.w)));
+                if (wn == 0 && r16 == 0)   // [tile][kb][row % 16][row / 16]
+                    a.hs[(((int64_t)tile * (a.I / kGroup) + ib) * 16 + (row & 15)) * 8 + (row >> 4)] = (uint8_t)(ex[i] + 127);
+            }
+            const int row = (wm * 4 + mi) * 16 + g4 + q;
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj)
-                s_h[row * 128 + (2 * wn + jj) * 16 + (lane & 15)] =
-                    (uint8_t)(cvt2_e4m3(ldexpf(hv[mi][jj][i], -ex), 0.f) & 0xFFu);
-            if (wn == 0 && (lane & 15) == 0)   // [tile][kb][row % 16][row / 16]
-                a.hs[(((int64_t)tile * (a.I / kGroup) + ib) * 16 + (row & 15)) * 8 + (row >> 4)] = (uint8_t)(ex + 127);
+                *reinterpret_cast<uint32_t*>(s_h + row * 128 + (((2 * wn + jj) ^ (row & 7)) << 4) + 4 * (r16 >> 2)) =
+                    e4m3_quad_rows(hv[mi][jj], ex, q);
         }
     }
     __syncthreads();
     const int KB2 = a.I / kGroup;
     for (int q = tid; q < 8 * 128; q += 512) {
         const int mf = q >> 7, w = q & 127, hh = w >> 6, ln = w & 63;
-        const uint4 v = *reinterpret_cast<const uint4*>(s_h + (mf * 16 + (ln & 15)) * 128 + (ln >> 4) * 32 + hh * 16);
+        const int R = mf * 16 + (ln & 15);
+        const uint4 v = *reinterpret_cast<const uint4*>(s_h + R * 128 + (((2 * (ln >> 4) + hh) ^ (R & 7)) << 4));
         *reinterpret_cast<uint4*>(a.hq + (((int64_t)tile * 8 + mf) * KB2 + ib) * kFragBytes + hh * 1024 + ln * 16) = v;
     }
 }
@@ -1060,7 +1111,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_p2(G1Args a) {
     __shared__ __align__(16) uint8_t buf[2 * kP2Stage];
     __shared__ __align__(16) uint8_t s_sa[kPfMaxKB * kP2Rows];   // [kb][wm][row % 16][fragment of wm]
     __shared__ uint16_t s_sgu[kPfMaxKB];                        // gate scale | up scale << 8
-    __shared__ float s_amax[4][kP2Rows];
+    __shared__ __align__(16) float s_amax[kP2Rows][4];   // [row][column wave]
 
     const int NB16 = 2 * a.I / 16, NBS = 2 * a.I / kGroup;
     const v4i_t ra = make_srd(a.xq, (uint32_t)a.T * a.H);
@@ -1126,74 +1177,104 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_p2(G1Args a) {
         for (int j = 0; j < 4; ++j) acc[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
     const int r16 = lane & 15, x8 = r16 & 7, c2 = 2 * (lane >> 4);
-    // the rows of a missing second tile are not computed
-    const bool active = wm == 0 || second;
-    for (int kb = 0; kb < KB; ++kb) {
-        wait_vm<0>();      // block kb landed (this thread's pieces) ...
-        __syncthreads();   // ... and everyone's; every wave is done with block kb - 1's stage
-        if (kb + 1 < KB) issue(kb + 1, (kb + 1) & 1);
-        if (active) {
-            const uint8_t* cur = buf + (kb & 1) * kP2Stage;
-            const v2i_t sa = *reinterpret_cast<const v2i_t*>(s_sa + kb * kP2Rows + wm * 128 + r16 * 8);
-            const int sg = s_sgu[kb];
-            v8i bf[4];
+    // row fragments of this wave holding valid rows (the rest are skipped: wave-uniform)
+    const int nact = __builtin_amdgcn_readfirstlane(min(8, max(0, (nvalid - wm * kPfBM + 15) >> 4)));
+    auto loop = [&](auto FULL) __attribute__((always_inline)) {
+        for (int kb = 0; kb < KB; ++kb) {
+            wait_vm<0>();      // block kb landed (this thread's pieces) ...
+            __syncthreads();   // ... and everyone's; every wave is done with block kb - 1's stage
+            if (kb + 1 < KB) issue(kb + 1, (kb + 1) & 1);
+            if (nact > 0) {
+                const uint8_t* cur = buf + (kb & 1) * kP2Stage;
+                const v2i_t sa = *reinterpret_cast<const v2i_t*>(s_sa + kb * kP2Rows + wm * 128 + r16 * 8);
+                const int sg = s_sgu[kb];
+                v8i bf[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bf[j] = lds_frag(cur + kP2StageA + (j < 2 ? 2 * wn + j : 6 + 2 * wn + j) * kFragBytes, lane);
+                for (int j = 0; j < 4; ++j)
+                    bf[j] = lds_frag(cur + kP2StageA + (j < 2 ? 2 * wn + j : 6 + 2 * wn + j) * kFragBytes, lane);
+                auto afrag = [&](int mi) __attribute__((always_inline)) {
+                    const uint8_t* rowp = cur + ((wm * 8 + mi) * 16 + r16) * kGroup;
+                    const uint4 lo = *reinterpret_cast<const uint4*>(rowp + ((c2 ^ x8) << 4));
+                    const uint4 hi = *reinterpret_cast<const uint4*>(rowp + (((c2 + 1) ^ x8) << 4));
+                    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                };
+                // row fragments in pairs, the next pair's LDS reads in flight during this
+                // pair's 8 matrix-core instructions (the scheduling barrier keeps that order)
+                v8i a0 = afrag(0), a1 = afrag(1);
 #pragma unroll
-            for (int mi = 0; mi < 8; ++mi) {
-                const uint8_t* rowp = cur + ((wm * 8 + mi) * 16 + r16) * kGroup;
-                const uint4 lo = *reinterpret_cast<const uint4*>(rowp + ((c2 ^ x8) << 4));
-                const uint4 hi = *reinterpret_cast<const uint4*>(rowp + (((c2 + 1) ^ x8) << 4));
-                const v8i af = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                for (int p = 0; p < 4; ++p) {
+                    v8i n0 = a0, n1 = a1;
+                    if (p < 3) {
+                        n0 = afrag(2 * p + 2);
+                        n1 = afrag(2 * p + 3);
+                    }
+                    if (decltype(FULL)::value || 2 * p < nact) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[mi][j] = mfma_fp8_sel(mi & 3, j >> 1, af, bf[j], acc[mi][j], sa[mi >> 2], sg);
+                        for (int j = 0; j < 4; ++j)
+                            acc[2 * p][j] = mfma_fp8_sel(2 * p & 3, j >> 1, a0, bf[j], acc[2 * p][j], sa[p >> 1], sg);
+                    }
+                    if (decltype(FULL)::value || 2 * p + 1 < nact) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            acc[2 * p + 1][j] =
+                                mfma_fp8_sel((2 * p + 1) & 3, j >> 1, a1, bf[j], acc[2 * p + 1][j], sa[p >> 1], sg);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    a0 = n0;
+                    a1 = n1;
+                }
             }
         }
-    }
+    };
+    if (nact == 8) loop(std::true_type{});
+    else loop(std::false_type{});
 
-    // SwiGLU, per-row amax over the item's 128 h columns, E4M3 requantisation
+    // SwiGLU, per-row amax over the item's 128 h columns (4 waves x 2 fragments)
     float hv[8][2][4];
 #pragma unroll
     for (int mi = 0; mi < 8; ++mi) {
+        if (mi < nact) {
+            float m[4];
+            swiglu_frag(acc[mi], hv[mi], m);
+            if (r16 == 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float m = 0.f;
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const float g = acc[mi][jj][i];
-                const float h = g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.44269504f)) * acc[mi][2 + jj][i];
-                hv[mi][jj][i] = h;
-                m = fmaxf(m, fabsf(h));
+                for (int i = 0; i < 4; ++i) s_amax[(wm * 8 + mi) * 16 + 4 * (lane >> 4) + i][wn] = m[i];
             }
-            m = max16(m);
-            if (r16 == 0) s_amax[wn][(wm * 8 + mi) * 16 + 4 * (lane >> 4) + i] = m;
         }
     }
     __syncthreads();   // also: every wave is done reading the stages before buf is reused
-    uint8_t* s_h = buf;   // [256 rows][128]
+    // E4M3 requantisation; h staged as [256 rows][128] bytes, 16-byte chunks XOR-swizzled by
+    // row % 8, one dword (4 columns of one row) per lane and fragment
+    uint8_t* s_h = buf;
     const int KB2 = a.I / kGroup;
+    const int q = lane & 3, g4 = 4 * (lane >> 4);
 #pragma unroll
     for (int mi = 0; mi < 8; ++mi) {
+        if (mi < nact) {
+            int ex[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = (wm * 8 + mi) * 16 + 4 * (lane >> 4) + i;
-            const float am = fmaxf(fmaxf(s_amax[0][row], s_amax[1][row]), fmaxf(s_amax[2][row], s_amax[3][row]));
-            const int ex = scale_exponent(am);
+            for (int i = 0; i < 4; ++i) {
+                const int row = (wm * 8 + mi) * 16 + g4 + i;
+                const float4 am4 = *reinterpret_cast<const float4*>(s_amax[row]);
+                ex[i] = scale_exponent(fmaxf(fmaxf(am4.x, am4.y), fmaxf(am4.z, am4.w)));
+                if (wn == 0 && r16 == 0) {   // [tile][kb][row % 16][row / 16]
+                    const int rl = row & 127;
+                    a.hs[(((int64_t)(t0 + wm) * KB2 + ib) * 16 + (rl & 15)) * 8 + (rl >> 4)] = (uint8_t)(ex[i] + 127);
+                }
+            }
+            const int row = (wm * 8 + mi) * 16 + g4 + q;
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj)
-                s_h[row * 128 + (2 * wn + jj) * 16 + r16] = (uint8_t)(cvt2_e4m3(ldexpf(hv[mi][jj][i], -ex), 0.f) & 0xFFu);
-            if (wn == 0 && r16 == 0 && active) {   // [tile][kb][row % 16][row / 16]
-                const int rl = row & 127;
-                a.hs[(((int64_t)(t0 + wm) * KB2 + ib) * 16 + (rl & 15)) * 8 + (rl >> 4)] = (uint8_t)(ex + 127);
-            }
+                *reinterpret_cast<uint32_t*>(s_h + row * 128 + (((2 * wn + jj) ^ (row & 7)) << 4) + 4 * (r16 >> 2)) =
+                    e4m3_quad_rows(hv[mi][jj], ex, q);
         }
     }
     __syncthreads();
     const int nf = second ? 16 : 8;
     for (int q = tid; q < nf * 128; q += 512) {
         const int mf = q >> 7, w = q & 127, hh = w >> 6, ln = w & 63;
-        const uint4 v = *reinterpret_cast<const uint4*>(s_h + (mf * 16 + (ln & 15)) * 128 + (ln >> 4) * 32 + hh * 16);
+        const int R = mf * 16 + (ln & 15);
+        const uint4 v = *reinterpret_cast<const uint4*>(s_h + R * 128 + (((2 * (ln >> 4) + hh) ^ (R & 7)) << 4));
         *reinterpret_cast<uint4*>(a.hq + (((int64_t)t0 * 8 + mf) * KB2 + ib) * kFragBytes + hh * 1024 + ln * 16) = v;
     }
 }
@@ -1272,7 +1353,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm2_p2(G2Args a) {
         for (int j = 0; j < 4; ++j) acc[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
     const int r16 = lane & 15;
-    const bool active = wm == 0 || second;
+    const int nact = __builtin_amdgcn_readfirstlane(min(8, max(0, (nvalid - wm * kPfBM + 15) >> 4)));
+    const bool active = nact > 0;
     for (int kb = 0; kb < KB; ++kb) {
         wait_vm<0>();
         __syncthreads();
@@ -1284,11 +1366,26 @@ __global__ __launch_bounds__(512, 1) void k_gemm2_p2(G2Args a) {
             v8i bf[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) bf[j] = lds_frag(cur + kP2StageA + (wn * 4 + j) * kFragBytes, lane);
+            v8i a0 = lds_frag(cur + (wm * 8) * kFragBytes, lane), a1 = lds_frag(cur + (wm * 8 + 1) * kFragBytes, lane);
 #pragma unroll
-            for (int mi = 0; mi < 8; ++mi) {
-                const v8i af = lds_frag(cur + (wm * 8 + mi) * kFragBytes, lane);
+            for (int p = 0; p < 4; ++p) {
+                v8i n0 = a0, n1 = a1;
+                if (p < 3) {
+                    n0 = lds_frag(cur + (wm * 8 + 2 * p + 2) * kFragBytes, lane);
+                    n1 = lds_frag(cur + (wm * 8 + 2 * p + 3) * kFragBytes, lane);
+                }
+                if (2 * p < nact) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[mi][j] = mfma_fp8_sel(mi & 3, 0, af, bf[j], acc[mi][j], sa[mi >> 2], sb);
+                    for (int j = 0; j < 4; ++j) acc[2 * p][j] = mfma_fp8_sel(2 * p & 3, 0, a0, bf[j], acc[2 * p][j], sa[p >> 1], sb);
+                }
+                if (2 * p + 1 < nact) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[2 * p + 1][j] = mfma_fp8_sel((2 * p + 1) & 3, 0, a1, bf[j], acc[2 * p + 1][j], sa[p >> 1], sb);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                a0 = n0;
+                a1 = n1;
             }
         }
     }
@@ -1323,7 +1420,7 @@ int ffn_super_tile_order(int ntiles_max) { return ntiles_max >= 512 ? 1 : 0; }
 
 // 256-row items (tile pairs) once experts average at least this many rows.
 #ifndef MOE_PAIR_MIN_AVG_ROWS
-#define MOE_PAIR_MIN_AVG_ROWS 256
+#define MOE_PAIR_MIN_AVG_ROWS 128
 #endif
 
 FfnPlan ffn_plan(int T, int k, int E, int quant) {

@@ -352,8 +352,8 @@ __global__ __launch_bounds__(kRbThreads, 1) void k_gemm2_rb(Rb2Args a) {
         dma_a(s + P);
         load_b(Bf[un], Sa[un], Sb[un]);
         const uint8_t* cur = ring + (s % NST) * (MT * kRbStage);
-        // an item whose expert has no second tile skips the second tile's fragments
-        const bool second = MT == 2 && __builtin_amdgcn_readfirstlane(s_nv[c_i]) > kRbBM;
+        // fragments holding no valid row of the item are skipped (the count is uniform)
+        const int nact = min(MF, (__builtin_amdgcn_readfirstlane(s_nv[c_i]) + 15) >> 4);
         // fragment mi + 1 is read from LDS while the instructions of fragment mi run; the
         // scheduling barriers keep the compiler from hoisting all 8 MT reads (registers)
         v8i af = rb_lds_frag(cur, lane);
@@ -361,7 +361,7 @@ __global__ __launch_bounds__(kRbThreads, 1) void k_gemm2_rb(Rb2Args a) {
         for (int mi = 0; mi < MF; ++mi) {
             v8i an = af;
             if (mi + 1 < MF) an = rb_lds_frag(cur + (mi + 1) * kFragBytes, lane);
-            if (mi < 8 || second) {
+            if (mi < nact) {
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     acc[mi][j] = rb_mfma_sel(mi & 3, af, Bf[u][j], acc[mi][j], Sa[u][mi >> 3][(mi & 7) >> 2], Sb[u]);

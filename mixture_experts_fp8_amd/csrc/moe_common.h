@@ -26,12 +26,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // amax = 1.m * 2^(E-127) and 448 = 1.75 * 2^8, so e = E - 135, plus one when the
 // mantissa exceeds 1.75.  Subnormal amax (< 2^-126) needs e <= -135 and clamps to -127.
 __device__ __forceinline__ int scale_exponent(float amax) {
-    uint32_t u = __float_as_uint(amax) & 0x7FFFFFFFu;
-    if (u == 0) return 0;
-    int E = (int)(u >> 23);
-    if (E == 0) return -127;
-    int e = E - 135 + ((u & 0x7FFFFFu) > 0x600000u ? 1 : 0);
-    return e < -127 ? -127 : (e > 127 ? 127 : e);
+    // branch-free: 0 for amax == 0, -127 for subnormal amax, else the clamped exponent
+    const uint32_t u = __float_as_uint(amax) & 0x7FFFFFFFu;
+    const int E = (int)(u >> 23);
+    const int e = E - 135 + ((u & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+    const int r = E == 0 ? (u == 0 ? 0 : -127) : e;
+    return min(max(r, -127), 127);
 }
 
 // Two floats -> two E4M3FN bytes in the low 16 bits (round to nearest even; OCP format
