@@ -34,7 +34,8 @@ PEAK_FP8_TFLOPS = 5000.0       # MI355X dense FP8 matrix, TFLOP/s
 LAYERS = 4
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["mixture_experts_fp8_amd/csrc/k_ffn.hip", "mixture_experts_fp8_amd/csrc/k_ffn_rb.hip",
-                  "mixture_experts_fp8_amd/csrc/k_mx.hip", "mixture_experts_fp8_amd/csrc/moe_common.h"]
+                  "mixture_experts_fp8_amd/csrc/k_mx.hip", "mixture_experts_fp8_amd/csrc/moe_common.h",
+                  "mixture_experts_fp8_amd/csrc/work_items.h"]
 
 
 def parse():

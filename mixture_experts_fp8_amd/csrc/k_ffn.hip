@@ -17,6 +17,7 @@
 // from memory into registers PF K-blocks ahead, 2 KB contiguous per operand.
 #include "moe_common.h"
 #include "moe_internal.h"
+#include "work_items.h"
 
 #include <algorithm>
 #include <type_traits>
@@ -935,6 +936,222 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pf(G1Args a) {
     }
 }
 
+// ----------------------------------------------------------------------------------------
+// Persistent gate/up GEMM on 128-row tiles (the tile shape, operand layouts and epilogue of
+// k_gemm1_pf).  One workgroup per CU walks its item list (tile, I column block) as one
+// stream of K blocks through two 48 KB LDS stages, so no item starts from an empty pipeline:
+//   * the sorted assignment ids of item n + 1's rows reach LDS by a dword LDS-DMA issued at
+//     item n's first K block;
+//   * its A row scales (gathered through those ids) and gate/up weight scales are loaded at
+//     item n's K block KB - 2 and stored to the other half of a double table at block KB - 1,
+//     right after that block's wait (so the loads' own wait costs nothing);
+//   * its first K block is issued at item n's last block, before item n's epilogue.
+// Needs KB >= 2 (the scale loads sit at block KB - 2) and KB <= 4 SVN.
+constexpr int kPpMaxItems = 256;
+
+// 4 bytes per lane from the buffer at voff + soff into LDS at m0base + 4 * lane.
+__device__ __forceinline__ void dma4_async(const v4i_t& srd, uint32_t m0base, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :
+                 : "s"(m0base), "v"(voff), "s"(srd), "s"(soff)
+                 : "memory", "m0");
+}
+
+template <int SVN>   // scale bytes a thread stages per item: KB <= 4 SVN
+__global__ __launch_bounds__(512, 1) void k_gemm1_pp(G1Args a) {
+    __shared__ __align__(16) uint8_t buf[2 * kPfStage];
+    __shared__ __align__(16) uint8_t s_sa[2][kPfMaxKB * kPfBM];   // [item parity][kb][wm][row % 16][fragment of wm]
+    __shared__ uint16_t s_sgu[2][kPfMaxKB];                      // gate scale | up scale << 8
+    __shared__ __align__(16) int s_tok[2][kPfBM];                // sorted assignment ids of the item's rows
+    __shared__ __align__(16) float s_amax[kPfBM][4];
+    __shared__ int4 s_it[kPpMaxItems];                           // tile, column block, expert, first sorted row
+    __shared__ int s_nv[kPpMaxItems];
+    __shared__ int s_cnt[kItWaves];
+
+    const int ncol = a.I / kGroup, KB = a.H / kGroup;
+    // (uniform: the loops below run on scalar counters)
+    const int cnt = __builtin_amdgcn_readfirstlane(it_fill_items<1>(
+        a.ord, ncol, __builtin_amdgcn_readfirstlane(*a.ntiles), a.tiles, a.counts, a.offsets, s_it, s_nv, kPpMaxItems, s_cnt));
+    if (cnt <= 0) return;
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wv >> 2, wn = wv & 3;
+    const int r16 = lane & 15, x8 = r16 & 7;
+    const int NB16 = 2 * a.I / 16, NBS = 2 * a.I / kGroup;
+    const v4i_t ra = make_srd(a.xq, (uint32_t)a.T * a.H);
+    const v4i_t rtok = make_srd(a.sorted_assign, (uint32_t)a.T * a.k * 4);
+    const uint32_t lds_w = lds_addr(buf) + wv * 1024, l16 = lane * 16;
+    const int rs = tid >> 2;   // the row whose A scales this thread stages
+
+    // ---- per-item helpers (n: item index; all reads of the item table are uniform)
+    auto tok_dma = [&](int n) __attribute__((always_inline)) {   // ids of item n's 128 rows
+        if (wv < 2) {
+            const int rowbase = __builtin_amdgcn_readfirstlane(s_it[n].w);
+            dma4_async(rtok, __builtin_amdgcn_readfirstlane(lds_addr(s_tok[n & 1]) + wv * 256), lane * 4,
+                       (uint32_t)(rowbase + wv * 64) * 4);
+        }
+    };
+    uint32_t sv[SVN], sgu = 0;
+    auto scale_loads = [&](int n) __attribute__((always_inline)) {
+        const int4 it = s_it[n];
+        const int ib = __builtin_amdgcn_readfirstlane(it.y), e = __builtin_amdgcn_readfirstlane(it.z);
+        const int nv = __builtin_amdgcn_readfirstlane(s_nv[n]);
+        const uint8_t* src = a.xs + (int64_t)(s_tok[n & 1][min(rs, nv - 1)] / a.k) * KB;
+#pragma unroll
+        for (int t = 0; t < SVN; ++t) {
+            const int kb = (tid & 3) + 4 * t;
+            sv[t] = kb < KB ? src[kb] : 0u;
+        }
+        if (tid < KB) {
+            const uint8_t* sb = a.w13s + ((int64_t)e * KB + tid) * NBS;
+            sgu = (uint32_t)sb[ib] | (uint32_t)sb[ncol + ib] << 8;
+        }
+    };
+    auto scale_stores = [&](int n) __attribute__((always_inline)) {
+        const int sa_pos = (rs >> 6) * 64 + (rs & 15) * 4 + ((rs >> 4) & 3);
+#pragma unroll
+        for (int t = 0; t < SVN; ++t) {
+            const int kb = (tid & 3) + 4 * t;
+            if (kb < KB) s_sa[n & 1][kb * kPfBM + sa_pos] = (uint8_t)sv[t];
+        }
+        if (tid < KB) s_sgu[n & 1][tid] = (uint16_t)sgu;
+    };
+    // DMA stream state: the item whose blocks are being issued
+    uint32_t aoff[2], bsoff[4];
+    v4i_t rw;
+    auto dma_item = [&](int n) __attribute__((always_inline)) {
+        const int4 it = s_it[n];
+        const int ib = __builtin_amdgcn_readfirstlane(it.y), e = __builtin_amdgcn_readfirstlane(it.z);
+        const int nv = __builtin_amdgcn_readfirstlane(s_nv[n]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {   // rows 8 (wv + 8 i) + lane / 8, whole lines, swizzled chunks
+            const int r = 8 * (wv + 8 * i) + (lane >> 3);
+            aoff[i] = (uint32_t)(s_tok[n & 1][min(r, nv - 1)] / a.k) * a.H + (((lane & 7) ^ (lane >> 3)) << 4);
+        }
+        rw = make_srd(a.w13p + (int64_t)e * NB16 * KB * kFragBytes, (uint32_t)NB16 * KB * kFragBytes);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = wv * 64 + 512 * i, f = q >> 7, hh = (q >> 6) & 1;
+            const int n16 = f < 8 ? ib * 8 + f : a.I / 16 + ib * 8 + (f - 8);
+            bsoff[i] = __builtin_amdgcn_readfirstlane(n16 * KB * kFragBytes + hh * 1024);
+        }
+    };
+    auto issue = [&](int kb, int s) __attribute__((always_inline)) {
+        const uint32_t st = __builtin_amdgcn_readfirstlane(lds_w + s * kPfStage);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) dma16_async(ra, st + i * 8192, aoff[i], __builtin_amdgcn_readfirstlane(kb * kGroup));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            dma16_async(rw, st + kPfStageA + i * 8192, l16, __builtin_amdgcn_readfirstlane(bsoff[i] + kb * kFragBytes));
+    };
+
+    // ---- first item: ids, scales, first block; the second item's ids
+    tok_dma(0);
+    wait_vm<0>();
+    __syncthreads();
+    scale_loads(0);
+    dma_item(0);
+    issue(0, 0);
+    if (cnt > 1) tok_dma(1);
+    scale_stores(0);
+
+    v4f acc[4][4];   // [row fragment][gate 0, 1 | up 2, 3]
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    int g = 0;   // global K-block step
+    for (int n = 0; n < cnt; ++n) {
+        const int4 it = s_it[n];
+        const int tile = __builtin_amdgcn_readfirstlane(it.x), ib = __builtin_amdgcn_readfirstlane(it.y);
+        const int nvalid = __builtin_amdgcn_readfirstlane(s_nv[n]);
+        const int nact = min(4, max(0, (nvalid - wm * 64 + 15) >> 4));
+        const bool more = n + 1 < cnt;
+        for (int kb = 0; kb < KB; ++kb, ++g) {
+            wait_vm<0>();      // block g landed (this thread's pieces) ...
+            __syncthreads();   // ... and everyone's; every wave is done with block g - 1's stage
+            if (kb == KB - 1 && more) scale_stores(n + 1);
+            if (kb + 1 < KB) {
+                issue(kb + 1, (g + 1) & 1);
+            } else if (more) {
+                dma_item(n + 1);
+                issue(0, (g + 1) & 1);
+            }
+            if (kb == 0 && n + 2 < cnt) tok_dma(n + 2);
+            if (kb == KB - 2 && more) scale_loads(n + 1);
+
+            const uint8_t* cur = buf + (g & 1) * kPfStage;
+            const int sa = *reinterpret_cast<const int*>(s_sa[n & 1] + kb * kPfBM + wm * 64 + r16 * 4);
+            const int sg = s_sgu[n & 1][kb];
+            v8i bf[4], af[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                bf[j] = lds_frag(cur + kPfStageA + (j < 2 ? 2 * wn + j : 6 + 2 * wn + j) * kFragBytes, lane);
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) {
+                const uint8_t* rowp = cur + ((wm * 4 + mi) * 16 + r16) * kGroup;
+                const uint4 lo = *reinterpret_cast<const uint4*>(rowp + (((2 * (lane >> 4)) ^ x8) << 4));
+                const uint4 hi = *reinterpret_cast<const uint4*>(rowp + (((2 * (lane >> 4) + 1) ^ x8) << 4));
+                af[mi] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            }
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+                if (mi < nact) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[mi][j] = mfma_fp8_sel(mi, j >> 1, af[mi], bf[j], acc[mi][j], sa, sg);
+                }
+        }
+
+        // ---- epilogue of item n (the next item's first block is in flight in the other stage)
+        float hv[4][2][4];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            if (mi < nact) {
+                float m[4];
+                swiglu_frag(acc[mi], hv[mi], m);
+                if (r16 == 0) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) s_amax[(wm * 4 + mi) * 16 + 4 * (lane >> 4) + i][wn] = m[i];
+                }
+            }
+        }
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        __syncthreads();   // also: every wave is done reading the stage of block g - 1
+        uint8_t* s_h = buf + ((g - 1) & 1) * kPfStage;   // [128 rows][128], chunks swizzled by row % 8
+        const int q = lane & 3, g4 = 4 * (lane >> 4);
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            if (mi < nact) {
+                int ex[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = (wm * 4 + mi) * 16 + g4 + i;
+                    const float4 am4 = *reinterpret_cast<const float4*>(s_amax[row]);
+                    ex[i] = scale_exponent(fmaxf(fmaxf(am4.x, am4.y), fmaxf(am4.z, am4.w)));
+                    if (wn == 0 && r16 == 0)   // [tile][kb][row % 16][row / 16]
+                        a.hs[(((int64_t)tile * ncol + ib) * 16 + (row & 15)) * 8 + (row >> 4)] = (uint8_t)(ex[i] + 127);
+                }
+                const int row = (wm * 4 + mi) * 16 + g4 + q;
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+                    *reinterpret_cast<uint32_t*>(s_h + row * 128 + (((2 * wn + jj) ^ (row & 7)) << 4) + 4 * (r16 >> 2)) =
+                        e4m3_quad_rows(hv[mi][jj], ex, q);
+            }
+        }
+        __syncthreads();
+        for (int qq = tid; qq < 8 * 128; qq += 512) {
+            const int mf = qq >> 7, w = qq & 127, hh = w >> 6, ln = w & 63;
+            const int R = mf * 16 + (ln & 15);
+            const uint4 v = *reinterpret_cast<const uint4*>(s_h + R * 128 + (((2 * (ln >> 4) + hh) ^ (R & 7)) << 4));
+            *reinterpret_cast<uint4*>(a.hq + (((int64_t)tile * 8 + mf) * ncol + ib) * kFragBytes + hh * 1024 + ln * 16) = v;
+        }
+    }
+    wait_vm<0>();
+}
+
 __global__ __launch_bounds__(512, 1) void k_gemm2_pf(G2Args a) {
     int nb, tile;
     if (!pf_work_item(a.ord, a.H / 256, __builtin_amdgcn_readfirstlane(*a.ntiles), tile, nb)) return;
@@ -1488,9 +1705,21 @@ static hipError_t run_ffn_dec(const FfnArgs& f, const FfnPlan& p, const FfnWs& w
 static hipError_t run_ffn_pf(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid) {
     G1Args g1{f.xq, f.xs, f.T, f.k, f.H, f.I, f.counts, f.offsets, f.sorted_assign, w.tiles, w.ntiles, f.w13p, f.w13s,
               w.hq, w.hs, ffn_super_tile_order(p.ntiles_max)};
-    const int grid1 = g1.ord ? kXcds * ord_ranks(p.ntiles_max, f.I / kGroup)
-                             : (int)(ceil_div((int64_t)(f.I / kGroup) * p.ntiles_max, kXcds) * kXcds);
-    hipLaunchKernelGGL(k_gemm1_pf, dim3(grid1), dim3(512), 0, st, g1);
+    const int KB1 = f.H / kGroup, pgrid = persistent_grid();
+#ifndef MOE_NO_PP
+    // the persistent kernel where its staged scales and item table fit
+    if (KB1 >= 2 && KB1 <= 32 && persistent_items_per_wg(p.ntiles_max, f.I / kGroup, pgrid) <= kPpMaxItems) {
+        if (KB1 <= 8) hipLaunchKernelGGL(k_gemm1_pp<2>, dim3(pgrid), dim3(512), 0, st, g1);
+        else if (KB1 <= 16) hipLaunchKernelGGL(k_gemm1_pp<4>, dim3(pgrid), dim3(512), 0, st, g1);
+        else hipLaunchKernelGGL(k_gemm1_pp<8>, dim3(pgrid), dim3(512), 0, st, g1);
+    } else
+#endif
+    {
+        const int grid1 = g1.ord ? kXcds * ord_ranks(p.ntiles_max, f.I / kGroup)
+                                 : (int)(ceil_div((int64_t)(f.I / kGroup) * p.ntiles_max, kXcds) * kXcds);
+        hipLaunchKernelGGL(k_gemm1_pf, dim3(grid1), dim3(512), 0, st, g1);
+    }
+    (void)pgrid;
     if (mid) {
         const hipError_t e = hipEventRecord(mid, st);
         if (e != hipSuccess) return e;

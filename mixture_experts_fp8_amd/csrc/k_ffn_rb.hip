@@ -30,6 +30,7 @@
 // block + P, then the 8 MT A fragments from LDS and 16 MT matrix-core instructions per wave.
 #include "moe_common.h"
 #include "moe_internal.h"
+#include "work_items.h"
 
 #include <algorithm>
 #include <type_traits>
@@ -43,7 +44,6 @@ constexpr int kRbThreads = 64 * kRbWaves;     // two waves per SIMD
 constexpr int kRbStage = kRbBM * kGroup;      // A bytes per K block (8 fragments)
 constexpr int kRb2MaxItems = 256;             // items per workgroup (LDS item table)
 constexpr int kRbXcds = 8;
-constexpr int kRbGroupTiles = 4;              // tiles per super-block of the work order
 
 typedef int v2i_t __attribute__((ext_vector_type(2)));
 typedef int v4i_rb __attribute__((ext_vector_type(4)));
@@ -112,94 +112,6 @@ __device__ __forceinline__ v4f rb_mfma_sel(int sel, v8i a, v8i b, v4f acc, int s
     }
 }
 
-// The items of persistent workgroup L: the list of ntiles * ncol items is cut into kRbXcds
-// contiguous shares, share x for the workgroups on XCD x (workgroup L runs on XCD L % 8);
-// inside a share the nx workgroups of the XCD take items j, j + nx, ... so the ones running
-// together walk consecutive items.  Item w: super-block w / (4 * ncol) of 4 consecutive
-// tiles (mostly one expert), column block outer inside it, so concurrent workgroups share
-// A rows and weight columns through the XCD's L2.
-struct RbSched {
-    int base, stride, n;
-};
-__device__ __forceinline__ RbSched rb_sched(int total) {
-    const int nx = gridDim.x / kRbXcds;
-    const int L = blockIdx.x, x = L % kRbXcds, j = L / kRbXcds;
-    const int per = (total + kRbXcds - 1) / kRbXcds;
-    RbSched s;
-    s.base = x * per + j;
-    s.stride = nx;
-    const int in_share = j < per ? (per - 1 - j) / nx + 1 : 0;
-    const int lim = total - s.base;   // items w = base + nx * i < total
-    const int in_total = lim > 0 ? (lim - 1) / nx + 1 : 0;
-    s.n = min(in_share, in_total);
-    return s;
-}
-
-__device__ __forceinline__ void rb_tile_col(int w, int ncol, int ntiles, int& tile, int& col) {
-    const int sb = w / (kRbGroupTiles * ncol), r = w - sb * kRbGroupTiles * ncol;
-    const int t0 = sb * kRbGroupTiles;
-    const int g = min(kRbGroupTiles, ntiles - t0);
-    col = r / g;
-    tile = t0 + r - col * g;
-}
-
-// Item table in LDS: {tile, column block, expert, first sorted row}, and valid rows.  An
-// item covers MT consecutive 128-row tiles of one expert: with MT = 2 only a tile that starts
-// an expert's even 256-row block leads an item, and the item's rows run on into the next
-// tile when the expert has one.  The workgroup's items are the valid ones among its
-// candidates, in order: with the super-tile order (ord) ranks j, j + nx, ... of its XCD's
-// share (ord_item); otherwise its contiguous share of the column-block order (rb_sched).
-// Returns the item count.
-template <int MT>
-__device__ __forceinline__ int rb_fill_items(int ord, int ncol, int ntiles, const int2* tiles, const int32_t* counts,
-                                             const int32_t* offsets, int4* s_it, int* s_nv, int cap, int* s_cnt) {
-    const int nx = gridDim.x / kRbXcds, x = blockIdx.x % kRbXcds, j = blockIdx.x / kRbXcds;
-    const RbSched sch = rb_sched(ntiles * ncol);
-    int ncand;
-    if (ord) {
-        const int total = ord_ranks(ntiles, ncol);   // ranks per XCD
-        ncand = j < total ? (total - 1 - j) / nx + 1 : 0;
-    } else {
-        ncand = sch.n;
-    }
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    int base = 0;
-    for (int c0 = 0; c0 < ncand; c0 += kRbThreads) {
-        const int c = c0 + threadIdx.x;
-        int tile = 0, col = 0;
-        bool v = false;
-        if (c < ncand) {
-            if (ord) {
-                v = ord_item(x, j + nx * c, ntiles, ncol, tile, col);
-            } else {
-                rb_tile_col(sch.base + sch.stride * c, ncol, ntiles, tile, col);
-                v = true;
-            }
-        }
-        int2 te = make_int2(0, 0);
-        if (v) {
-            te = tiles[tile];
-            if (MT == 2) v = te.y % (2 * kRbBM) == 0;
-        }
-        const uint64_t m = __ballot(v);
-        if (lane == 0) s_cnt[wv] = __popcll(m);
-        __syncthreads();
-        int off = base, tot = 0;
-        for (int w = 0; w < kRbWaves; ++w) {
-            off += w < wv ? s_cnt[w] : 0;
-            tot += s_cnt[w];
-        }
-        const int pos = off + __popcll(m & ((1ull << lane) - 1));
-        if (v && pos < cap) {
-            s_it[pos] = make_int4(tile, col, te.x, offsets[te.x] + te.y);
-            s_nv[pos] = min(MT * kRbBM, counts[te.x] - te.y);
-        }
-        base += tot;
-        __syncthreads();
-    }
-    return min(base, cap);
-}
-
 // ----------------------------------------------------------------------------------------
 // Per-call table of the down GEMM's weight-block scales as dwords in [expert][column block][kb]
 // order, so a wave's scale for a K block is one aligned uniform load whose byte 0 feeds the
@@ -247,8 +159,8 @@ __global__ __launch_bounds__(kRbThreads, 1) void k_gemm2_rb(Rb2Args a) {
     const int ncol = a.H / 256, KB = a.I / kGroup;
     const int NB16 = a.H / 16, NBS = a.H / kGroup;
     __shared__ int s_cnt[kRbWaves];
-    RbSched sch;
-    sch.n = rb_fill_items<MT>(a.ord, ncol, ntiles, a.tiles, a.counts, a.offsets, s_it, s_nv, kRb2MaxItems, s_cnt);
+    ItSched sch;
+    sch.n = it_fill_items<MT>(a.ord, ncol, ntiles, a.tiles, a.counts, a.offsets, s_it, s_nv, kRb2MaxItems, s_cnt);
     if (sch.n <= 0) return;
     __syncthreads();
     const int G = sch.n * KB;
@@ -395,7 +307,7 @@ __global__ __launch_bounds__(kRbThreads, 1) void k_gemm2_rb(Rb2Args a) {
 #define MOE_RB_MT 1
 #endif
 
-static int rb_grid() {
+int persistent_grid() {
     static int cached[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -408,7 +320,7 @@ static int rb_grid() {
     return cached[dev];
 }
 
-static int64_t rb_items_per_wg(int ntiles_max, int ncol, int grid) {
+int64_t persistent_items_per_wg(int ntiles_max, int ncol, int grid) {
     // the larger of the two work orders' per-workgroup counts
     const int64_t nx = grid / kRbXcds;
     return std::max(ceil_div(ord_ranks(ntiles_max, ncol), nx), ceil_div(ceil_div((int64_t)ntiles_max * ncol, kRbXcds), nx));
@@ -420,7 +332,7 @@ bool ffn_rb_supported(int H, int I, int E, int ntiles_max) {
     const int64_t lim = (int64_t)1 << 32;
     if ((int64_t)ntiles_max * kRbBM * I >= lim || (int64_t)H * I >= lim || (int64_t)E * H * I / (kGroup * kGroup) * 4 >= lim)
         return false;
-    return rb_items_per_wg(ntiles_max, H / 256, rb_grid()) <= kRb2MaxItems;
+    return persistent_items_per_wg(ntiles_max, H / 256, persistent_grid()) <= kRb2MaxItems;
 }
 
 size_t ffn_rb_scale_table_bytes(int H, int I, int E) { return (size_t)E * (I / kGroup) * (H / kGroup) * 4; }
@@ -432,7 +344,7 @@ hipError_t launch_gemm2_rb(const FfnArgs& f, const FfnWs& w, int ntiles_max, int
                        f.E, KB, NBS, w.bs);
     Rb2Args g2{w.hq, w.hs, w.bs, f.H, f.I, f.E, ntiles_max, w.tiles, w.ntiles, f.counts, f.offsets, f.w2p, f.out,
                f.out_bf16, ord};
-    hipLaunchKernelGGL((k_gemm2_rb<MOE_RB_P, MOE_RB_MT>), dim3(rb_grid()), dim3(kRbThreads), 0, st, g2);
+    hipLaunchKernelGGL((k_gemm2_rb<MOE_RB_P, MOE_RB_MT>), dim3(persistent_grid()), dim3(kRbThreads), 0, st, g2);
     return hipGetLastError();
 }
 

@@ -103,6 +103,10 @@ hipError_t launch_ffn_mx(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hip
 int ffn_super_tile_order(int ntiles_max);
 // persistent down GEMM for 128-row tiles (k_ffn_rb.hip)
 bool ffn_rb_supported(int H, int I, int E, int ntiles_max);
+// persistent kernels: workgroups (the CU count, a multiple of 8) and the largest item count
+// one workgroup takes from ntiles_max x ncol items in either work order
+int persistent_grid();
+int64_t persistent_items_per_wg(int ntiles_max, int ncol, int grid);
 size_t ffn_rb_scale_table_bytes(int H, int I, int E);
 hipError_t launch_gemm2_rb(const FfnArgs& f, const FfnWs& w, int ntiles_max, int ord, hipStream_t st);
 

@@ -34,6 +34,12 @@ SMALL = {
     # ragged second tiles from the skew
     "tile_pairs_skewed": W.Workload(131, "p2s", T=1500, H=256, I=256, E=8, k=4, bias="normal1.5"),
     "tile_pairs_zipf_kb6": W.Workload(132, "p2z", T=900, H=768, I=384, E=6, k=2, bias="zipf"),
+    # experts averaging 25..127 rows: 128-row tiles, the persistent gate/up kernel for
+    # 2 <= H/128 <= 32 (several tiles per workgroup on this few-item grid only when skewed)
+    # and the per-tile kernel for a single K block
+    "persistent_tiles_skewed": W.Workload(133, "ppS", T=900, H=512, I=384, E=32, k=3, bias="normal1.5"),
+    "persistent_tiles_kb12": W.Workload(134, "pp12", T=700, H=1536, I=256, E=16, k=2),
+    "staged_tiles_kb1": W.Workload(135, "pfkb1", T=800, H=128, I=256, E=16, k=2),
     "sigmoid_groups": W.Workload(125, "grp", T=96, H=384, I=256, E=32, k=4, scoring="sigmoid", group_count=4,
                                  k_group=2, group_select_mode=1, routed_scaling_factor=2.5),
     "prelude_small": W.Workload(126, "pre", T=9, H=512, I=256, E=16, k=4, prelude=True),
