@@ -85,15 +85,26 @@ __device__ __forceinline__ uint32_t ordered_bits(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Wave maximum of 64-bit keys (all lanes active): DPP butterfly inside each 16-lane row on
+// both halves, then the four row maxima read from lanes 0, 16, 32, 48 (uniform result).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
+    const uint64_t w = ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)v);
+    return w > v ? w : v;
+}
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    v = dpp_max_u64<0xB1>(v);
+    v = dpp_max_u64<0x4E>(v);
+    v = dpp_max_u64<0x124>(v);
+    v = dpp_max_u64<0x128>(v);
+    uint64_t r = 0;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint32_t lo = __shfl_xor((uint32_t)v, o);
-        const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o);
-        const uint64_t w = ((uint64_t)hi << 32) | lo;
-        v = w > v ? w : v;
+    for (int l = 0; l < 64; l += 16) {
+        const uint64_t w = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), l) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+        r = w > r ? w : r;
     }
-    return v;
+    return r;
 }
 
 template <int EPL>

@@ -47,25 +47,38 @@ __device__ __forceinline__ uint32_t cvt4_e4m3(float a, float b, float c, float d
     return (uint32_t)r;
 }
 
-template <typename T>
-__device__ __forceinline__ T wave_max(T v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
-    return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
-}
-
 // Lane exchange inside rows of 16 lanes by a DPP control word (a VALU operand modifier, no
 // LDS round trip as with ds_bpermute): 0xB1 swaps neighbours, 0x4E swaps pairs within a
 // quad, 0x124 / 0x128 rotate the row by 4 / 8 lanes.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Wave64 reductions (all 64 lanes active): a butterfly inside each row of 16 lanes by DPP
+// (neighbours, pairs, rotations by 4 and 8), then the four row results read from lanes 0,
+// 16, 32, 48 and combined as (r0 . r1) . (r2 . r3); the result is uniform.
+template <typename Op>
+__device__ __forceinline__ float wave_reduce_f32(float v, Op op) {
+    v = op(v, dpp_f32<0xB1>(v));
+    v = op(v, dpp_f32<0x4E>(v));
+    v = op(v, dpp_f32<0x124>(v));
+    v = op(v, dpp_f32<0x128>(v));
+    const int b = __float_as_int(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(b, 0)), r1 = __int_as_float(__builtin_amdgcn_readlane(b, 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(b, 32)), r3 = __int_as_float(__builtin_amdgcn_readlane(b, 48));
+    return op(op(r0, r1), op(r2, r3));
+}
+__device__ __forceinline__ float wave_max(float v) {
+    return wave_reduce_f32(v, [](float x, float y) { return fmaxf(x, y); });
+}
+__device__ __forceinline__ float wave_sum(float v) {
+    return wave_reduce_f32(v, [](float x, float y) { return x + y; });
 }
 
 // Max over aligned groups of 16 lanes (the hardware rows): within quads, then across the
