@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--config", type=int, default=2,
                     help="workload id 1..5 (default 2: Gemma-4-like decode); 6: one 8-GPU expert-parallel shard of 4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--shared", action="store_true",
+                    help="add one shared expert (same H, I) run on every token in the same launches")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0, help="0: the workload's own default sample")
     ap.add_argument("--expert-out-bf16", action="store_true", help="keep per-assignment expert outputs in bf16")
     ap.add_argument("--quant", default="fp8", choices=["fp8", "mxfp8", "w4a8"],
@@ -108,7 +110,7 @@ def stage_bytes_flops(wl, counts: np.ndarray, eo_bytes: int, quant: str = "fp8")
     (or 32) weights per scale byte.
     """
     wb, ga, gw = SCHEME_BYTES[quant]
-    H, I, T, A = wl.H, wl.I, wl.T, wl.T * wl.k
+    H, I, T, A = wl.H, wl.I, wl.T, wl.T * (wl.k + wl.shared)
     n_act = int((counts > 0).sum())
     g1_bytes = n_act * (H * 2 * I * wb + H * 2 * I / gw) + T * (H + H / ga) + A * (I + I / ga)
     g2_bytes = n_act * (I * H * wb + I * H / gw) + A * (I + I / ga) + A * H * eo_bytes
@@ -123,7 +125,7 @@ def step_algorithmic_bytes(wl, n_act: int, quant: str = "fp8") -> int:
     wb, _, gw = SCHEME_BYTES[quant]
     H, I, T, E, k = wl.H, wl.I, wl.T, wl.E, wl.k
     b = int(n_act * (3 * H * I * wb + 3 * H * I / gw))
-    b += 2 * T * H + 2 * T * H + 8 * T * k
+    b += 2 * T * H + 2 * T * H + 8 * T * (k + wl.shared)
     b += 4 * E * H + 4 * H + 4 * E if wl.prelude else 4 * T * E
     return b
 
@@ -181,7 +183,7 @@ def cpu_baseline(wl, sample_tokens: int, quant: str = "fp8", min_seconds: float 
     n = min(sample_tokens, wl.T)
     tokens = np.linspace(0, wl.T - 1, n).astype(np.int64)
     ids, _, _ = omoe.route_workload(inputs, p, pre)
-    experts = sorted(set(int(e) for e in ids[tokens].reshape(-1)))
+    experts = sorted(set(int(e) for e in ids[tokens].reshape(-1)) | ({wl.E} if wl.shared else set()))
 
     def src(e):
         return (W.expert_weight_f32(wl, "w13", e).numpy(), W.expert_weight_f32(wl, "w2", e).numpy())
@@ -199,6 +201,9 @@ def cpu_baseline(wl, sample_tokens: int, quant: str = "fp8", min_seconds: float 
         t0 = time.perf_counter()
         while True:   # whole passes over the sample until at least min_seconds have gone by
             ids, w, _ = omoe.route_workload(inputs, p, pre)    # routing of the whole batch
+            if wl.shared:   # the shared expert as slot k with weight 1 (oracle.moe.forward_shared)
+                ids = np.concatenate([ids, np.full((len(ids), 1), wl.E, dtype=ids.dtype)], axis=1)
+                w = np.concatenate([np.asarray(w, dtype=np.float64), np.ones((len(w), 1))], axis=1)
             out = fwd(xf, ids, w, ex, tokens=tokens)
             reps += 1
             dt = time.perf_counter() - t0
@@ -224,6 +229,8 @@ def main():
     from mixture_experts_fp8_amd import binding as B
 
     wl = W.CONFIGS[args.config]
+    if args.shared:
+        wl = wl.replace(shared=1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] workload {wl.name}: {W.describe(wl)}", file=sys.stderr, flush=True)
@@ -236,7 +243,7 @@ def main():
         pre = M.Prelude(nw, rw, pe, wl.rms_eps)
     else:
         logits = W.router_logits(wl, dev)
-    H, I, E = wl.H, wl.I, wl.E
+    H, I, E = wl.H, wl.I, wl.E + wl.shared   # the shared expert's weights come last
     quant = M.QUANT_SCHEMES[args.quant]
     if quant == M.MOE_QUANT_FP8_BLOCK128:
         w13p = torch.empty(E * H * 2 * I, dtype=torch.uint8, device=dev)
@@ -271,8 +278,8 @@ def main():
                             wl.group_select_mode, wl.routed_scaling_factor)
     counts = torch.zeros(E, dtype=torch.int32, device=dev)
     y = torch.empty(wl.T, H, dtype=torch.bfloat16, device=dev)
-    calls = [M.MoeFused(params, wl.T, lw, x, logits, pre, args.expert_out_bf16, y=y, expert_counts=counts)
-             for lw in layers]
+    calls = [M.MoeFused(params, wl.T, lw, x, logits, pre, args.expert_out_bf16, y=y, expert_counts=counts,
+                        shared_expert=bool(wl.shared)) for lw in layers]
     torch.cuda.synchronize()
 
     if args.calib_copy:
@@ -326,7 +333,7 @@ def main():
             e.destroy()
         return t
 
-    tname = wl.name if args.quant == "fp8" else f"{wl.name}_{args.quant}"
+    tname = (wl.name + ("_shared" if wl.shared else "")) + ("" if args.quant == "fp8" else f"_{args.quant}")
     roof = roofline_entry(dom, kernel_time(dom), *per_stage[dom], load_traffic(tname, dom))
     roof_other = roofline_entry(other, kernel_time(other), *per_stage[other], load_traffic(tname, other))
 

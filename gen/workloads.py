@@ -66,6 +66,7 @@ class Workload:
     rms_eps: float = 1e-6
     bias: str = "none"             # "none" | "normal1.5" | "zipf"
     seed: int = 0
+    shared: int = 0                # 1: one shared expert (weights of expert index E) on every token
 
     @property
     def A(self) -> int:
@@ -78,8 +79,9 @@ class Workload:
         return rng.stream_key(self.seed, self.cfg, stream, index)
 
     def flops(self) -> float:
-        """Algorithmic FP8 GEMM flops: gate+up (2*A*H*2I) plus down (2*A*I*H)."""
-        return 6.0 * self.T * self.k * self.H * self.I
+        """Algorithmic FP8 GEMM flops: gate+up (2*A*H*2I) plus down (2*A*I*H), over the
+        routed assignments and the shared expert's T rows."""
+        return 6.0 * self.T * (self.k + self.shared) * self.H * self.I
 
 
 CONFIGS = {
@@ -155,8 +157,9 @@ def make_small_inputs(wl: Workload, device="cpu") -> dict:
         d["norm_w"], d["router_w"], d["pe_scale"] = gate_prelude_params(wl, device)
     else:
         d["logits"] = router_logits(wl, device)
-    d["w13"] = torch.stack([expert_weight_f32(wl, "w13", e, device) for e in range(wl.E)])
-    d["w2"] = torch.stack([expert_weight_f32(wl, "w2", e, device) for e in range(wl.E)])
+    ne = wl.E + wl.shared   # the shared expert's weights come last (index E)
+    d["w13"] = torch.stack([expert_weight_f32(wl, "w13", e, device) for e in range(ne)])
+    d["w2"] = torch.stack([expert_weight_f32(wl, "w2", e, device) for e in range(ne)])
     return d
 
 
@@ -173,6 +176,8 @@ def describe(wl: Workload) -> str:
         r += f" rsf={wl.routed_scaling_factor}"
     if wl.prelude:
         r += " +RMSNorm/router prelude"
+    if wl.shared:
+        r += " +shared expert"
     if wl.bias != "none":
         r += f" bias={wl.bias}"
     return f"T={wl.T} H={wl.H} I={wl.I} E={wl.E} k={wl.k} ({r})"

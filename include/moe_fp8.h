@@ -266,6 +266,14 @@ int moe_combine(const void* expert_out, int32_t dtype, const int32_t* assign_pos
 
 /* ---- the whole step -------------------------------------------------------------------- */
 #define MOE_FUSED_EXPERT_OUT_BF16  1   /* keep the per-assignment expert outputs in bf16 */
+/* One shared expert (the metrale grouped FP8 MoE page's shared gate/up/down, "GroupedExpertIo"
+ * and the W8A8 gate_up / down launches that also take the shared projections): every token also
+ * runs through expert E, whose weights follow the E routed experts' in w13..w2_scale (E + 1
+ * experts, same H and I and packing), and its output is added to y with weight 1 (the routed
+ * weights keep routed_scaling_factor).  It runs in the same grouped launches as an extra
+ * expert with T rows: topk_ids / topk_weights then have k + 1 columns (column k = E, weight
+ * 1.0) and expert_counts E + 1 entries.  moe_workspace_size takes the same flags. */
+#define MOE_FUSED_SHARED_EXPERT    2
 
 /* Stage boundaries of moe_fused, for timing: quant_act | route (incl. prelude) | dispatch
  * (incl. the GEMM tile list) | gate+up GEMM | down GEMM | combine.  The activation
@@ -280,7 +288,9 @@ int moe_combine(const void* expert_out, int32_t dtype, const int32_t* assign_pos
  *   hidden_states     [T, H] bf16.
  *   router_logits     [T, E] float32, or NULL when prelude != NULL.
  *   w13..w2_scale     packed weights and logical scales as for moe_grouped_ffn.
- *   topk_ids, topk_weights, expert_counts   optional outputs ([T,k], [T,k], [E]); NULL to skip.
+ *   topk_ids, topk_weights, expert_counts   optional outputs ([T,k], [T,k], [E]; with
+ *                     MOE_FUSED_SHARED_EXPERT [T,k+1], [T,k+1], [E+1]); NULL to skip.
+ *   flags             MOE_FUSED_EXPERT_OUT_BF16 | MOE_FUSED_SHARED_EXPERT.
  *   workspace         >= moe_workspace_size(T, H, I, E, k, flags) bytes (covers the prelude).
  *   stage_events      NULL, or MOE_STAGES + 1 hipEvent_t (created by the caller; NULL entries
  *                     are skipped) recorded on `stream` before the first and after every stage. */

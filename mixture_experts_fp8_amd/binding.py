@@ -22,6 +22,7 @@ MOE_SCORING_SOFTMAX, MOE_SCORING_SIGMOID = 0, 1
 MOE_ROUTE_IDS_GIVEN = 1
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 MOE_FUSED_EXPERT_OUT_BF16 = 1
+MOE_FUSED_SHARED_EXPERT = 2
 MOE_QUANT_FP8_BLOCK128, MOE_QUANT_MXFP8, MOE_QUANT_W4A8 = 0, 1, 2
 MOE_WFMT_E4M3, MOE_WFMT_E2M1 = 0, 1
 QUANT_SCHEMES = {"fp8": MOE_QUANT_FP8_BLOCK128, "mxfp8": MOE_QUANT_MXFP8, "w4a8": MOE_QUANT_W4A8}
@@ -340,12 +341,16 @@ class MoeFused:
                  router_logits: Optional[torch.Tensor] = None, prelude: Optional[Prelude] = None,
                  expert_out_bf16: bool = False, y: Optional[torch.Tensor] = None,
                  topk_ids: Optional[torch.Tensor] = None, topk_weights: Optional[torch.Tensor] = None,
-                 expert_counts: Optional[torch.Tensor] = None):
+                 expert_counts: Optional[torch.Tensor] = None, shared_expert: bool = False):
         H = hidden_states.shape[1]
         _need(hidden_states, "hidden_states", torch.bfloat16, (T, H))
         if router_logits is not None:
             _need(router_logits, "router_logits", torch.float32, (T, params.num_experts))
-        self.flags = MOE_FUSED_EXPERT_OUT_BF16 if expert_out_bf16 else 0
+        if w.E != params.num_experts + int(shared_expert):
+            raise ValueError(f"weights hold {w.E} experts; need num_experts + {int(shared_expert)} "
+                             f"= {params.num_experts + int(shared_expert)}")
+        self.flags = ((MOE_FUSED_EXPERT_OUT_BF16 if expert_out_bf16 else 0) |
+                      (MOE_FUSED_SHARED_EXPERT if shared_expert else 0))
         self.y = y if y is not None else torch.empty(T, H, dtype=torch.bfloat16, device=hidden_states.device)
         nbytes = lib().moe_workspace_size(T, H, w.I, params.num_experts, params.top_k, self.flags)
         self.ws = workspace(max(nbytes, 256), hidden_states.device)
@@ -374,15 +379,19 @@ class MoeFused:
 
 def moe_fused(params: RouteParams, hidden_states: torch.Tensor, w: PackedWeights,
               router_logits: Optional[torch.Tensor] = None, prelude: Optional[Prelude] = None,
-              expert_out_bf16: bool = False, return_routing: bool = False):
-    """The whole step in one C call.  Returns y bf16 [T, H] (and ids, weights, counts)."""
+              expert_out_bf16: bool = False, return_routing: bool = False, shared_expert: bool = False):
+    """The whole step in one C call.  Returns y bf16 [T, H] (and ids, weights, counts).
+    shared_expert: w holds num_experts + 1 experts, the last one run on every token and added
+    with weight 1 (ids / weights then have top_k + 1 columns, counts num_experts + 1 entries)."""
     T = hidden_states.shape[0]
     dev = hidden_states.device
     ids = weights = counts = None
+    sh = int(shared_expert)
     if return_routing:
-        ids = torch.empty(T, params.top_k, dtype=torch.int32, device=dev)
-        weights = torch.empty(T, params.top_k, dtype=torch.float32, device=dev)
-        counts = torch.empty(params.num_experts, dtype=torch.int32, device=dev)
-    f = MoeFused(params, T, w, hidden_states, router_logits, prelude, expert_out_bf16, None, ids, weights, counts)
+        ids = torch.empty(T, params.top_k + sh, dtype=torch.int32, device=dev)
+        weights = torch.empty(T, params.top_k + sh, dtype=torch.float32, device=dev)
+        counts = torch.empty(params.num_experts + sh, dtype=torch.int32, device=dev)
+    f = MoeFused(params, T, w, hidden_states, router_logits, prelude, expert_out_bf16, None, ids, weights, counts,
+                 shared_expert)
     y = f()
     return (y, ids, weights, counts) if return_routing else y

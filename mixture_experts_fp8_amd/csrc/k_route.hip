@@ -235,8 +235,12 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
             if (normalise) v = v / denom;
             if (c.prelude && pe_scale) v *= pe_scale[id];
             v *= c.rsf;
-            ids[(int64_t)t * k + j] = id;
-            wts[(int64_t)t * k + j] = v;
+            ids[(int64_t)t * c.ld + j] = id;
+            wts[(int64_t)t * c.ld + j] = v;
+        }
+        if (c.shared_id >= 0 && lane == 0) {   // the shared expert, unweighted
+            ids[(int64_t)t * c.ld + k] = c.shared_id;
+            wts[(int64_t)t * c.ld + k] = 1.0f;
         }
         // the token's activation row, quantised per 128 columns (16 lanes per group)
         if (qo.x) {

@@ -104,6 +104,8 @@ moe::RouteCfg route_cfg(const moe_route_params* p, int T, bool prelude) {
     c.mode = p->group_select_mode;
     c.rsf = p->routed_scaling_factor;
     c.prelude = prelude ? 1 : 0;
+    c.ld = c.k;
+    c.shared_id = -1;
     return c;
 }
 
@@ -338,6 +340,10 @@ int moe_combine(const void* expert_out, int32_t dtype, const int32_t* assign_pos
 // fused workspace: ids | weights | counts | offsets | sorted | pos | route ws | xq | xs | ffn ws | expert_out
 size_t moe_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, int32_t flags) {
     if (T < 1 || H < 128 || I < 128 || E < 1 || k < 1) return 0;
+    if (flags & MOE_FUSED_SHARED_EXPERT) {   // one more expert, one more column per token
+        ++E;
+        ++k;
+    }
     const size_t A = (size_t)T * k;
     const size_t eo = (flags & MOE_FUSED_EXPERT_OUT_BF16) ? 2 : 4;
     return 4 * align256(A * 4) + align256((size_t)E * 4) + align256((size_t)(E + 1) * 4) +
@@ -351,7 +357,9 @@ int moe_fused(const moe_fused_args* a) {
     int rc = check_route_params(op, &a->route, a->T);
     if (rc) return rc;
     const int T = a->T, H = a->H, I = a->I, E = a->route.num_experts, k = a->route.top_k;
-    if ((rc = check_ffn_shapes(op, T, k, H, I, E))) return rc;
+    // with the shared expert the FFN, dispatch and combine see E + 1 experts and k + 1 slots
+    const int sh = (a->flags & MOE_FUSED_SHARED_EXPERT) ? 1 : 0, Ef = E + sh, kf = k + sh;
+    if ((rc = check_ffn_shapes(op, T, kf, H, I, Ef))) return rc;
     if (!a->hidden_states || !a->y) return fail(MOE_ERR_INVALID, "%s: hidden_states and y must not be NULL", op);
     if (a->prelude) {
         if ((rc = check_prelude(op, a->prelude, a->hidden_states, H))) return rc;
@@ -359,7 +367,8 @@ int moe_fused(const moe_fused_args* a) {
         return fail(MOE_ERR_INVALID, "%s: router_logits must not be NULL without a prelude", op);
     }
     if ((rc = check_weights(op, a->w13, a->w13_scale, a->w2, a->w2_scale))) return rc;
-    if (a->flags & ~MOE_FUSED_EXPERT_OUT_BF16) return fail(MOE_ERR_INVALID, "%s: unknown flags 0x%x", op, a->flags);
+    if (a->flags & ~(MOE_FUSED_EXPERT_OUT_BF16 | MOE_FUSED_SHARED_EXPERT))
+        return fail(MOE_ERR_INVALID, "%s: unknown flags 0x%x", op, a->flags);
     if (a->quant != MOE_QUANT_FP8_BLOCK128 && a->quant != MOE_QUANT_MXFP8 && a->quant != MOE_QUANT_W4A8)
         return fail(MOE_ERR_INVALID, "%s: quant (%d) must be one of MOE_QUANT_*", op, a->quant);
     if (!aligned(a->hidden_states, 16) || !aligned(a->y, 8))
@@ -370,21 +379,21 @@ int moe_fused(const moe_fused_args* a) {
                     a->workspace ? a->workspace_bytes : (size_t)0);
     if (!aligned(a->workspace, 256)) return fail(MOE_ERR_INVALID, "%s: workspace must be 256-byte aligned", op);
 
-    const size_t A = (size_t)T * k;
+    const size_t A = (size_t)T * kf;
     uint8_t* w = static_cast<uint8_t*>(a->workspace);
     auto take = [&](size_t n) { uint8_t* p = w; w += align256(n); return p; };
     int32_t* ids = reinterpret_cast<int32_t*>(take(A * 4));
     float* wts = reinterpret_cast<float*>(take(A * 4));
-    int32_t* counts = reinterpret_cast<int32_t*>(take((size_t)E * 4));
-    int32_t* offsets = reinterpret_cast<int32_t*>(take((size_t)(E + 1) * 4));
+    int32_t* counts = reinterpret_cast<int32_t*>(take((size_t)Ef * 4));
+    int32_t* offsets = reinterpret_cast<int32_t*>(take((size_t)(Ef + 1) * 4));
     int32_t* sorted = reinterpret_cast<int32_t*>(take(A * 4));
     int32_t* pos = reinterpret_cast<int32_t*>(take(A * 4));
     uint8_t* rws = w;
-    w += route_ws_bytes(T, E, k, 1);
+    w += route_ws_bytes(T, Ef, kf, 1);
     uint8_t* xq = take((size_t)T * H);
     uint8_t* xs = take((size_t)T * (H / 32));
     uint8_t* fws = w;
-    w += moe::ffn_workspace_bytes(T, H, I, E, k);
+    w += moe::ffn_workspace_bytes(T, H, I, Ef, kf);
     void* eo = take(A * H * ((a->flags & MOE_FUSED_EXPERT_OUT_BF16) ? 2 : 4));
     if (a->topk_ids) ids = a->topk_ids;
     if (a->topk_weights) wts = a->topk_weights;
@@ -400,32 +409,35 @@ int moe_fused(const moe_fused_args* a) {
     };
     const int bf = (a->flags & MOE_FUSED_EXPERT_OUT_BF16) ? 1 : 0;
     const bool mx = a->quant != MOE_QUANT_FP8_BLOCK128;
-    moe::FfnArgs f{T, k, H, I, E, xq, xs, counts, offsets, sorted, a->w13, a->w13_scale, a->w2, a->w2_scale, eo, bf,
+    moe::FfnArgs f{T, kf, H, I, Ef, xq, xs, counts, offsets, sorted, a->w13, a->w13_scale, a->w2, a->w2_scale, eo, bf,
                    a->quant};
     const moe::FfnWs fw = moe::carve_ffn_ws(f, fws);
-    const moe::FfnPlan plan = moe::ffn_plan(T, k, E, a->quant);
+    const moe::FfnPlan plan = moe::ffn_plan(T, kf, Ef, a->quant);
+    moe::RouteCfg rcfg = route_cfg(&a->route, T, a->prelude != nullptr);
+    rcfg.ld = kf;
+    rcfg.shared_id = sh ? E : -1;
     // the 128-group activation quantisation runs inside the routing kernel (one wave per
     // token); the 32-group one is its own launch
     mark(0);
     if (e == hipSuccess && mx) e = moe::launch_quant_act_mx(a->hidden_states, T, H, H, xq, xs, st);
     mark(1);
-    float* pl = reinterpret_cast<float*>(rws + route_chunk_bytes(T, E, k));
+    float* pl = reinterpret_cast<float*>(rws + route_chunk_bytes(T, Ef, kf));
     if (e == hipSuccess && a->prelude)
         e = moe::launch_gate_prelude(a->hidden_states, T, H, E, a->prelude->norm_weight, a->prelude->router_weight,
                                      a->prelude->rms_eps, pl, st);
     if (e == hipSuccess)
-        e = moe::launch_route(a->prelude ? pl : a->router_logits, route_cfg(&a->route, T, a->prelude != nullptr),
-                              a->prelude ? a->prelude->per_expert_scale : nullptr, ids, wts, st,
+        e = moe::launch_route(a->prelude ? pl : a->router_logits, rcfg, a->prelude ? a->prelude->per_expert_scale : nullptr,
+                              ids, wts, st,
                               mx ? moe::QuantOut{nullptr, 0, nullptr, nullptr}
                                  : moe::QuantOut{a->hidden_states, H, xq, xs});
     mark(2);
     if (e == hipSuccess)
-        e = moe::launch_dispatch(ids, (int)A, E, reinterpret_cast<int32_t*>(rws), counts, offsets, sorted, pos, st,
+        e = moe::launch_dispatch(ids, (int)A, Ef, reinterpret_cast<int32_t*>(rws), counts, offsets, sorted, pos, st,
                                  plan.BM, fw.tiles, fw.ntiles);
     mark(3);
     if (e == hipSuccess) e = moe::launch_grouped_ffn(f, fws, st, ev[4], true);
     mark(5);
-    if (e == hipSuccess) e = moe::launch_combine(eo, bf, pos, wts, T, k, H, a->y, st);
+    if (e == hipSuccess) e = moe::launch_combine(eo, bf, pos, wts, T, kf, H, a->y, st);
     mark(6);
     if (e != hipSuccess) return hip_fail(op, e);
     return ok();

@@ -33,6 +33,8 @@ struct RouteCfg {
     int G, k_group, mode;
     float rsf;
     int prelude;            // weights = softmax over selected * per_expert_scale
+    int ld;                 // row stride of ids / weights (>= k)
+    int shared_id;          // >= 0: column k of each row gets this expert with weight 1
 };
 constexpr int kScatterChunk = 1024;   // assignments per dispatch workgroup
 

@@ -26,7 +26,8 @@ Pins (tests/test_oracle_moe.py): one token, one expert, top-1 equals a dense Swi
 computed by torch in float64 on the dequantised tensors, with the re-quantisation step
 checked separately; combine reduces to a gather for k = 1, w = 1; scaling the routed
 scaling factor scales y; permuting tokens permutes y; a row of y does not depend on the
-other rows.
+other rows.  The shared expert (``forward_shared``): with all routed weights zero y is the
+dense SwiGLU MLP of the shared weights, and y minus the routed-only y is that MLP's output.
 """
 from __future__ import annotations
 
@@ -127,6 +128,23 @@ def forward(x_f64, ids, weights, experts: QuantizedExperts, tokens=None):
     y = combine(o, np.asarray(weights, dtype=np.float64)[tok])
     return {"y": y, "o": o, "hq": hq, "hs": hs, "xq": xq, "xs": xs, "tokens": tok,
             "qmargin": qm, "qmargin_tok": qm.reshape(n, k).min(axis=1)}
+
+
+def forward_shared(x_f64, ids, weights, experts: QuantizedExperts, shared: int, tokens=None):
+    """Routed experts plus one shared expert that every token runs through, added with
+    weight 1 (the metrale grouped FP8 MoE page: the W8A8 gate_up and down launches also take
+    the shared expert's gate/up/down projections and write its activations and output
+    beside the routed ones):
+
+        y[t] = sum_j weights[t, j] * o_{ids[t, j]}(t) + o_shared(t),
+
+    o_shared being the same quantised SwiGLU FFN (steps 2-6) with expert ``shared``'s
+    weights.  Written as the routed forward over k + 1 slots, slot k holding the shared
+    expert with weight 1; the result dict is the routed one over those k + 1 slots."""
+    T = ids.shape[0]
+    ids_all = np.concatenate([np.asarray(ids), np.full((T, 1), shared, dtype=np.asarray(ids).dtype)], axis=1)
+    w_all = np.concatenate([np.asarray(weights, dtype=np.float64), np.ones((T, 1))], axis=1)
+    return forward(x_f64, ids_all, w_all, experts, tokens)
 
 
 def route_workload(inputs: dict, p: routing.RouteParams, prelude=None):

@@ -43,7 +43,7 @@ def oracle_experts_for(wl: W.Workload, experts, workers: int = 8) -> omoe.Quanti
 
 def device_weights(wl: W.Workload, device="cuda") -> M.PackedWeights:
     """Generate each expert's float32 weights on the GPU, quantise and pack them there."""
-    H, I, E = wl.H, wl.I, wl.E
+    H, I, E = wl.H, wl.I, wl.E + wl.shared   # the shared expert's weights come last
     w13p = torch.empty(E * H * 2 * I, dtype=torch.uint8, device=device)
     w2p = torch.empty(E * I * H, dtype=torch.uint8, device=device)
     w13s = torch.empty(E, H // 128, 2 * I // 128, dtype=torch.uint8, device=device)
@@ -60,7 +60,7 @@ def device_weights(wl: W.Workload, device="cuda") -> M.PackedWeights:
 
 def device_weights_mx(wl: W.Workload, quant: int, device="cuda") -> M.PackedWeights:
     """Generate, MX-quantise and pack each expert's weights on the GPU (scheme `quant`)."""
-    H, I, E = wl.H, wl.I, wl.E
+    H, I, E = wl.H, wl.I, wl.E + wl.shared
     wfmt = M.MOE_WFMT_E2M1 if quant == M.MOE_QUANT_W4A8 else M.MOE_WFMT_E4M3
     div = 2 if wfmt == M.MOE_WFMT_E2M1 else 1
     n13, n2 = H * 2 * I // div, I * H // div

@@ -165,6 +165,8 @@ def test_workspace_sizes_are_monotone_and_cover_parts():
         full = L.moe_workspace_size(T, H, I, E, k, 0)
         assert full >= L.moe_ffn_workspace_size(T, H, I, E, k) + L.moe_route_workspace_size(T, E, k, H, 1)
         assert L.moe_workspace_size(T, H, I, E, k, B.MOE_FUSED_EXPERT_OUT_BF16) < full
+        # the shared expert adds one expert and one slot per token
+        assert L.moe_workspace_size(T, H, I, E, k, B.MOE_FUSED_SHARED_EXPERT) > full
         assert L.moe_workspace_size(2 * T, H, I, E, k, 0) > full
     assert L.moe_workspace_size(0, 256, 256, 8, 2, 0) == 0
 

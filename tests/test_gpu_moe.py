@@ -169,3 +169,52 @@ def test_fused_workload_sampled(cfg, ntok):
     assert counts.sum() == wl.T * wl.k
     fro, mx = HN.assert_output_close(HN.bf16_to_f64(y)[tokens], ref["y"], f"cfg{cfg}", ref["qmargin_tok"])
     print(f"  rel fro {fro:.2e} rel max {mx:.2e}", flush=True)
+
+
+# ---- one shared expert (weights of expert index E) run on every token in the same launches
+SHARED = {
+    "shared_small": W.Workload(140, "sh", T=96, H=256, I=256, E=8, k=2, shared=1),
+    "shared_prelude_decode_tiles": W.Workload(141, "shd", T=9, H=512, I=256, E=16, k=4, prelude=True, shared=1),
+    "shared_tile_pairs": W.Workload(142, "shp", T=700, H=256, I=384, E=4, k=2, shared=1),
+    "shared_persistent_tiles": W.Workload(143, "shpp", T=600, H=512, I=256, E=32, k=3, bias="normal1.5", shared=1),
+    "shared_decode_gemma4": W.CONFIGS[2].replace(cfg=144, shared=1),
+}
+
+
+def _check_shared(wl, tokens=None, workers=8):
+    x, logits, pre = HN.device_inputs(wl)
+    w = HN.device_weights(wl)
+    y, ids, wts, counts = M.moe_fused(HN.device_params(wl), x, w, router_logits=logits, prelude=pre,
+                                      return_routing=True, shared_expert=True)
+    torch.cuda.synchronize()
+    ids, wts, counts = ids.cpu().numpy(), wts.cpu().numpy(), counts.cpu().numpy()
+    E, k = wl.E, wl.k
+    # column k holds the shared expert with weight 1 for every token; it has T rows
+    assert ids.shape == (wl.T, k + 1) and (ids[:, k] == E).all() and (wts[:, k] == 1.0).all()
+    assert counts.shape == (E + 1,) and counts[E] == wl.T and counts.sum() == wl.T * (k + 1)
+    xf = W.bf16_to_f64(W.hidden_bf16(wl))
+    ids_ref, w_ref, margin = HN.oracle_route(wl, x_f64=xf, logits=None if wl.prelude else W.router_logits(wl))
+    ok = margin >= 1e-5
+    assert np.array_equal(ids[ok, :k], ids_ref[ok])
+    tok = np.arange(wl.T) if tokens is None else np.asarray(tokens)
+    experts = sorted(set(int(e) for e in ids_ref[tok].reshape(-1)) | {E})
+    ex = HN.oracle_experts_for(wl, experts, workers=workers)
+    ref = omoe.forward_shared(xf, ids_ref, w_ref, ex, shared=E, tokens=tok)
+    sel = ok[tok]
+    fro, mx = HN.assert_output_close(HN.bf16_to_f64(y)[tok][sel], ref["y"][sel], wl.name, ref["qmargin_tok"][sel])
+    print(f"  rel fro {fro:.2e} rel max {mx:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("name", list(SHARED))
+def test_fused_shared_expert(name):
+    wl = SHARED[name]
+    print("fused shared", name, W.describe(wl), flush=True)
+    _check_shared(wl)
+
+
+def test_fused_shared_expert_dsv3_prefill_sampled():
+    # the DeepSeek-V3-shaped prefill with its one shared expert (same I), sampled tokens
+    wl = W.CONFIGS[4].replace(cfg=145, shared=1)
+    print("fused shared sampled", W.describe(wl), flush=True)
+    _check_shared(wl, tokens=np.linspace(0, wl.T - 1, 2).astype(np.int64),
+                  workers=int(os.environ.get("ORACLE_WORKERS", "8")))

@@ -156,3 +156,28 @@ def test_mx_grouped_ffn_unit_and_bf16_out(scheme):
         eo = M.moe_grouped_ffn(xq, xs, r, w, wl.k, out_dtype=dt)
         HN.assert_output_close(eo.float().cpu().numpy().astype(np.float64)[pos], ref["o"], f"{scheme} o {dt}",
                                ref["qmargin"])
+
+
+@pytest.mark.parametrize("scheme", list(SCHEMES))
+def test_mx_fused_shared_expert(scheme):
+    quant, fmt = SCHEMES[scheme]
+    wl = W.Workload(146, "mx_shared", T=40, H=256, I=256, E=6, k=2, shared=1)
+    print("mx fused shared", scheme, W.describe(wl), flush=True)
+    x, logits, _ = HN.device_inputs(wl)
+    w = HN.device_weights_mx(wl, quant)
+    y, ids, wts, counts = M.moe_fused(HN.device_params(wl), x, w, router_logits=logits, return_routing=True,
+                                      shared_expert=True)
+    torch.cuda.synchronize()
+    ids = ids.cpu().numpy()
+    xf = W.bf16_to_f64(W.hidden_bf16(wl))
+    ids_ref, w_ref, margin = HN.oracle_route(wl, x_f64=xf, logits=W.router_logits(wl))
+    ok = margin >= 1e-5
+    assert (ids[:, wl.k] == wl.E).all() and np.array_equal(ids[ok, :wl.k], ids_ref[ok])
+    assert counts.cpu().numpy()[wl.E] == wl.T
+    # the shared expert as slot k with weight 1, as the FP8 oracle's forward_shared defines it
+    ids_all = np.concatenate([ids_ref, np.full((wl.T, 1), wl.E, dtype=ids_ref.dtype)], axis=1)
+    w_all = np.concatenate([np.asarray(w_ref, dtype=np.float64), np.ones((wl.T, 1))], axis=1)
+    ex = HN.oracle_experts_mx_for(wl, fmt, sorted(set(int(e) for e in ids_ref.reshape(-1)) | {wl.E}))
+    ref = omx.forward(xf, ids_all, w_all, ex)
+    fro, mxe = HN.assert_output_close(HN.bf16_to_f64(y)[ok], ref["y"][ok], f"{scheme} shared", ref["qmargin_tok"][ok])
+    print(f"  rel fro {fro:.2e} rel max {mxe:.2e}", flush=True)

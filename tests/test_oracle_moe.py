@@ -108,3 +108,39 @@ def test_combine_matches_explicit_sum():
     for t in range(6):
         ref = sum(w[t, j] * o[t * 3 + j] for j in range(3))
         np.testing.assert_allclose(y[t], ref, rtol=1e-15, atol=1e-15)
+
+
+def _dense_swiglu_mlp(ex, e, xq, xs):
+    """Textbook dense SwiGLU MLP in torch float64 on the dequantised operands of expert e,
+    with the re-quantisation of h between the projections."""
+    q13, s13, q2, s2 = ex.get(e)
+    xd = torch.from_numpy(codec.dequant_rows_128(xq, xs))
+    gu = xd @ torch.from_numpy(codec.dequant_blocks_128(q13, s13))
+    I = gu.shape[1] // 2
+    h = torch.nn.functional.silu(gu[:, :I]) * gu[:, I:]
+    hq, hs = codec.quant_rows_128(h.numpy())
+    return (torch.from_numpy(codec.dequant_rows_128(hq, hs)) @ torch.from_numpy(codec.dequant_blocks_128(q2, s2))).numpy()
+
+
+def test_shared_expert_alone_is_dense_swiglu_mlp():
+    # all routed weights zero: y is the shared expert's dense MLP of every token
+    T, E, k = 7, 4, 2
+    x, logits, ex = _random_case(T=T, E=E + 1, k=k, seed=5)
+    ids = np.tile(np.arange(k, dtype=np.int32), (T, 1))
+    out = moe.forward_shared(x, ids, np.zeros((T, k)), ex, shared=E)
+    ref = _dense_swiglu_mlp(ex, E, out["xq"], out["xs"])
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-12, atol=1e-15)
+    assert out["o"].shape == (T * (k + 1), x.shape[1])
+
+
+def test_shared_expert_adds_its_mlp_to_the_routed_output():
+    T, E, k = 9, 6, 3
+    x, logits, ex = _random_case(T=T, E=E + 1, k=k, seed=6)
+    p = routing.RouteParams(num_experts=E, top_k=k, scoring="softmax", renormalize=True)
+    ids, w, _ = routing.route(logits[:, :E], p)
+    routed = moe.forward(x, ids, w, ex)
+    both = moe.forward_shared(x, ids, w, ex, shared=E)
+    ref = _dense_swiglu_mlp(ex, E, routed["xq"], routed["xs"])
+    np.testing.assert_allclose(both["y"] - routed["y"], ref, rtol=1e-9, atol=1e-12)
+    # the routed slots are untouched: same per-assignment outputs in slots 0..k-1
+    np.testing.assert_array_equal(both["o"].reshape(T, k + 1, -1)[:, :k], routed["o"].reshape(T, k, -1))
