@@ -1799,8 +1799,9 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, void* ws, hipStream_t st, hipEve
 }
 
 // ----------------------------------------------------------------------------------------
-// Combine: workgroup (token, 1024-column slice); each thread owns 4 consecutive columns and
-// issues the loads of up to 8 expert rows before summing them in slot order j = 0, 1, ...
+// Combine: workgroup (token, 256 x 4 x MOE_COMBINE_CPT-column slice); each thread owns
+// MOE_COMBINE_CPT groups of 4 consecutive columns and issues the loads of up to 8 expert rows
+// for all of them before summing them in slot order j = 0, 1, ...
 template <bool BF16>
 __device__ __forceinline__ float4 load4(const void* eo, int64_t idx) {
     if (BF16) {
@@ -1811,45 +1812,66 @@ __device__ __forceinline__ float4 load4(const void* eo, int64_t idx) {
     return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(eo) + idx);
 }
 
-template <bool BF16>
+template <bool BF16, int CPT>
 __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ eo, const int32_t* __restrict__ pos,
                                                  const float* __restrict__ w, int k, int H,
                                                  uint16_t* __restrict__ y) {
+    // thread: CPT groups of 4 columns, 256 * 4 apart; all of a slot's loads are issued before
+    // the sums
     const int t = blockIdx.x;
-    const int c4 = blockIdx.y * 256 + threadIdx.x;
-    if (c4 * 4 >= H) return;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int c40 = blockIdx.y * 256 * CPT + threadIdx.x;
+    float4 acc[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) acc[c] = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j0 = 0; j0 < k; j0 += 8) {
-        float4 v[8];
+        float4 v[8][CPT];
         float wj[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int j = j0 + u;
             const int p = j < k ? pos[(int64_t)t * k + j] : -1;
             wj[u] = p >= 0 ? w[(int64_t)t * k + j] : 0.f;
-            v[u] = p >= 0 ? load4<BF16>(eo, (int64_t)p * H + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+                const int c4 = c40 + c * 256;
+                v[u][c] = (p >= 0 && c4 * 4 < H) ? load4<BF16>(eo, (int64_t)p * H + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             if (j0 + u < k) {
-                acc.x = fmaf(wj[u], v[u].x, acc.x);
-                acc.y = fmaf(wj[u], v[u].y, acc.y);
-                acc.z = fmaf(wj[u], v[u].z, acc.z);
-                acc.w = fmaf(wj[u], v[u].w, acc.w);
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) {
+                    acc[c].x = fmaf(wj[u], v[u][c].x, acc[c].x);
+                    acc[c].y = fmaf(wj[u], v[u][c].y, acc[c].y);
+                    acc[c].z = fmaf(wj[u], v[u][c].z, acc[c].z);
+                    acc[c].w = fmaf(wj[u], v[u][c].w, acc[c].w);
+                }
             }
         }
     }
-    uint2 o;
-    o.x = (uint32_t)f32_to_bf16(acc.x) | ((uint32_t)f32_to_bf16(acc.y) << 16);
-    o.y = (uint32_t)f32_to_bf16(acc.z) | ((uint32_t)f32_to_bf16(acc.w) << 16);
-    *reinterpret_cast<uint2*>(y + (int64_t)t * H + c4 * 4) = o;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+        const int c4 = c40 + c * 256;
+        if (c4 * 4 < H) {
+            uint2 o;
+            o.x = (uint32_t)f32_to_bf16(acc[c].x) | ((uint32_t)f32_to_bf16(acc[c].y) << 16);
+            o.y = (uint32_t)f32_to_bf16(acc[c].z) | ((uint32_t)f32_to_bf16(acc[c].w) << 16);
+            *reinterpret_cast<uint2*>(y + (int64_t)t * H + c4 * 4) = o;
+        }
+    }
 }
+
+#ifndef MOE_COMBINE_CPT
+#define MOE_COMBINE_CPT 4
+#endif
 
 hipError_t launch_combine(const void* eo, int bf16, const int32_t* pos, const float* w, int T, int k, int H,
                           uint16_t* y, hipStream_t st) {
-    const dim3 grid(T, (unsigned)ceil_div(H / 4, 256));
-    if (bf16) hipLaunchKernelGGL(k_combine<true>, grid, dim3(256), 0, st, eo, pos, w, k, H, y);
-    else hipLaunchKernelGGL(k_combine<false>, grid, dim3(256), 0, st, eo, pos, w, k, H, y);
+    constexpr int C = MOE_COMBINE_CPT;
+    const dim3 grid(T, (unsigned)ceil_div(H / 4, 256 * C));
+    if (bf16) hipLaunchKernelGGL((k_combine<true, C>), grid, dim3(256), 0, st, eo, pos, w, k, H, y);
+    else hipLaunchKernelGGL((k_combine<false, C>), grid, dim3(256), 0, st, eo, pos, w, k, H, y);
     return hipGetLastError();
 }
 
