@@ -939,15 +939,17 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pf(G1Args a) {
 // ----------------------------------------------------------------------------------------
 // Persistent gate/up GEMM on 128-row tiles (the tile shape, operand layouts and epilogue of
 // k_gemm1_pf).  One workgroup per CU walks its item list (tile, I column block) as one
-// stream of K blocks through two 48 KB LDS stages, so no item starts from an empty pipeline:
+// stream of K blocks through three 48 KB LDS stages (two blocks in flight), so no item starts
+// from an empty pipeline:
 //   * the sorted assignment ids of item n + 1's rows reach LDS by a dword LDS-DMA issued at
 //     item n's first K block;
 //   * its A row scales (gathered through those ids) and gate/up weight scales are loaded at
-//     item n's K block KB - 2 and stored to the other half of a double table at block KB - 1,
-//     right after that block's wait (so the loads' own wait costs nothing);
-//   * its first K block is issued at item n's last block, before item n's epilogue.
-// Needs KB >= 2 (the scale loads sit at block KB - 2) and KB <= 4 SVN.
-constexpr int kPpMaxItems = 256;
+//     item n's K block KB - 2 and stored to the other half of a double table at block KB - 1;
+//   * its first two K blocks are issued at item n's last two blocks.
+// Waits: before computing block g, every vector-memory op older than block g + 1's DMA must be
+// done (vmcnt <= 6: that DMA is 6 ops per thread), so the ids DMA and the scale loads are
+// issued before a step's block DMA.  Needs 2 <= KB <= 32 and KB <= 4 SVN.
+constexpr int kPpMaxItems = 128, kPpMaxKB = 32, kPpStages = 3;
 
 // 4 bytes per lane from the buffer at voff + soff into LDS at m0base + 4 * lane.
 __device__ __forceinline__ void dma4_async(const v4i_t& srd, uint32_t m0base, uint32_t voff, uint32_t soff) {
@@ -959,9 +961,9 @@ __device__ __forceinline__ void dma4_async(const v4i_t& srd, uint32_t m0base, ui
 
 template <int SVN>   // scale bytes a thread stages per item: KB <= 4 SVN
 __global__ __launch_bounds__(512, 1) void k_gemm1_pp(G1Args a) {
-    __shared__ __align__(16) uint8_t buf[2 * kPfStage];
-    __shared__ __align__(16) uint8_t s_sa[2][kPfMaxKB * kPfBM];   // [item parity][kb][wm][row % 16][fragment of wm]
-    __shared__ uint16_t s_sgu[2][kPfMaxKB];                      // gate scale | up scale << 8
+    __shared__ __align__(16) uint8_t buf[kPpStages * kPfStage];
+    __shared__ __align__(16) uint8_t s_sa[2][kPpMaxKB * kPfBM];   // [item parity][kb][wm][row % 16][fragment of wm]
+    __shared__ uint16_t s_sgu[2][kPpMaxKB];                      // gate scale | up scale << 8
     __shared__ __align__(16) int s_tok[2][kPfBM];                // sorted assignment ids of the item's rows
     __shared__ __align__(16) float s_amax[kPfBM][4];
     __shared__ int4 s_it[kPpMaxItems];                           // tile, column block, expert, first sorted row
@@ -1044,14 +1046,24 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pp(G1Args a) {
             dma16_async(rw, st + kPfStageA + i * 8192, l16, __builtin_amdgcn_readfirstlane(bsoff[i] + kb * kFragBytes));
     };
 
-    // ---- first item: ids, scales, first block; the second item's ids
+    // ---- first item: ids (and the second item's), scales, first two blocks
     tok_dma(0);
+    if (cnt > 1) tok_dma(1);
     wait_vm<0>();
     __syncthreads();
     scale_loads(0);
+    const int G = cnt * KB;   // K blocks of the whole stream
     dma_item(0);
     issue(0, 0);
-    if (cnt > 1) tok_dma(1);
+    int dn = 0, dkb = 1;      // the next block to issue: item dn, K block dkb
+    if (1 < G) {
+        if (dkb == KB) {
+            dn = 1;
+            dkb = 0;
+            dma_item(1);
+        }
+        issue(dkb, 1);
+    }
     scale_stores(0);
 
     v4f acc[4][4];   // [row fragment][gate 0, 1 | up 2, 3]
@@ -1060,7 +1072,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pp(G1Args a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    int g = 0;   // global K-block step
+    int g = 0, sg3 = 0;   // global K-block step and its stage (g % 3)
     for (int n = 0; n < cnt; ++n) {
         const int4 it = s_it[n];
         const int tile = __builtin_amdgcn_readfirstlane(it.x), ib = __builtin_amdgcn_readfirstlane(it.y);
@@ -1068,19 +1080,23 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pp(G1Args a) {
         const int nact = min(4, max(0, (nvalid - wm * 64 + 15) >> 4));
         const bool more = n + 1 < cnt;
         for (int kb = 0; kb < KB; ++kb, ++g) {
-            wait_vm<0>();      // block g landed (this thread's pieces) ...
-            __syncthreads();   // ... and everyone's; every wave is done with block g - 1's stage
+            if (g + 1 < G) wait_vm<6>();   // block g landed (block g + 1's 6 DMAs may be in flight) ...
+            else wait_vm<0>();
+            __syncthreads();               // ... everywhere; every wave is done with block g - 1's stage
+            // the ids DMA and scale loads go before this step's block DMA (see the waits above)
             if (kb == KB - 1 && more) scale_stores(n + 1);
-            if (kb + 1 < KB) {
-                issue(kb + 1, (g + 1) & 1);
-            } else if (more) {
-                dma_item(n + 1);
-                issue(0, (g + 1) & 1);
-            }
-            if (kb == 0 && n + 2 < cnt) tok_dma(n + 2);
             if (kb == KB - 2 && more) scale_loads(n + 1);
+            if (kb == 0 && n + 2 < cnt) tok_dma(n + 2);
+            if (g + 2 < G) {   // block g + 2 into the stage of block g - 1
+                if (++dkb == KB) {
+                    dkb = 0;
+                    dma_item(++dn);
+                }
+                issue(dkb, sg3 == 0 ? 2 : sg3 - 1);
+            }
 
-            const uint8_t* cur = buf + (g & 1) * kPfStage;
+            const uint8_t* cur = buf + sg3 * kPfStage;
+            sg3 = sg3 == 2 ? 0 : sg3 + 1;
             const int sa = *reinterpret_cast<const int*>(s_sa[n & 1] + kb * kPfBM + wm * 64 + r16 * 4);
             const int sg = s_sgu[n & 1][kb];
             v8i bf[4], af[4];
@@ -1120,7 +1136,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pp(G1Args a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
         __syncthreads();   // also: every wave is done reading the stage of block g - 1
-        uint8_t* s_h = buf + ((g - 1) & 1) * kPfStage;   // [128 rows][128], chunks swizzled by row % 8
+        // h staged in the stage of the item's last block (the next two blocks are in the others)
+        uint8_t* s_h = buf + (sg3 == 0 ? 2 : sg3 - 1) * kPfStage;   // [128 rows][128], chunks swizzled by row % 8
         const int q = lane & 3, g4 = 4 * (lane >> 4);
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
@@ -1708,7 +1725,7 @@ static hipError_t run_ffn_pf(const FfnArgs& f, const FfnPlan& p, const FfnWs& w,
     const int KB1 = f.H / kGroup, pgrid = persistent_grid();
 #ifndef MOE_NO_PP
     // the persistent kernel where its staged scales and item table fit
-    if (KB1 >= 2 && KB1 <= 32 && persistent_items_per_wg(p.ntiles_max, f.I / kGroup, pgrid) <= kPpMaxItems) {
+    if (KB1 >= 2 && KB1 <= kPpMaxKB && persistent_items_per_wg(p.ntiles_max, f.I / kGroup, pgrid) <= kPpMaxItems) {
         if (KB1 <= 8) hipLaunchKernelGGL(k_gemm1_pp<2>, dim3(pgrid), dim3(512), 0, st, g1);
         else if (KB1 <= 16) hipLaunchKernelGGL(k_gemm1_pp<4>, dim3(pgrid), dim3(512), 0, st, g1);
         else hipLaunchKernelGGL(k_gemm1_pp<8>, dim3(pgrid), dim3(512), 0, st, g1);
