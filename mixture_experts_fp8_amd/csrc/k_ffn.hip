@@ -1753,8 +1753,14 @@ static hipError_t run_ffn_pf(const FfnArgs& f, const FfnPlan& p, const FfnWs& w,
     return hipGetLastError();
 }
 
-static hipError_t run_ffn_p2(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid) {
-    hipLaunchKernelGGL(k_pairs, dim3(1), dim3(1024), 0, st, f.counts, f.E, w.pairs, w.npairs);
+hipError_t launch_pairs(const int32_t* counts, int E, int32_t* pairs, int32_t* npairs, hipStream_t st) {
+    hipLaunchKernelGGL(k_pairs, dim3(1), dim3(1024), 0, st, counts, E, pairs, npairs);
+    return hipGetLastError();
+}
+
+static hipError_t run_ffn_p2(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid,
+                             bool pairs_ready) {
+    if (!pairs_ready) hipLaunchKernelGGL(k_pairs, dim3(1), dim3(1024), 0, st, f.counts, f.E, w.pairs, w.npairs);
     const int ord = ffn_super_tile_order(p.ntiles_max);
     G1Args g1{f.xq, f.xs, f.T, f.k, f.H, f.I, f.counts, f.offsets, f.sorted_assign, w.tiles, w.ntiles, f.w13p, f.w13s,
               w.hq, w.hs, ord, w.pairs, w.npairs};
@@ -1794,7 +1800,8 @@ FfnWs carve_ffn_ws(const FfnArgs& f, void* ws) {
     return r;
 }
 
-hipError_t launch_grouped_ffn(const FfnArgs& f, void* ws, hipStream_t st, hipEvent_t mid, bool tiles_ready) {
+hipError_t launch_grouped_ffn(const FfnArgs& f, void* ws, hipStream_t st, hipEvent_t mid, bool tiles_ready,
+                              bool pairs_ready) {
     const FfnPlan p = ffn_plan(f.T, f.k, f.E, f.quant);
     const FfnWs w = carve_ffn_ws(f, ws);
     if (!tiles_ready) {
@@ -1808,7 +1815,7 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, void* ws, hipStream_t st, hipEve
     // down-GEMM blocks; other shapes take the plain 128-row kernels
     if (f.H / kGroup <= kPfMaxKB && f.I / kGroup <= kPfMaxKB && f.H % 256 == 0) {
 #ifndef MOE_NO_PAIRS
-        if (p.pairs) return run_ffn_p2(f, p, w, st, mid);
+        if (p.pairs) return run_ffn_p2(f, p, w, st, mid, pairs_ready);
 #endif
         return run_ffn_pf(f, p, w, st, mid);
     }

@@ -56,7 +56,10 @@ constexpr int kDispatchOneMaxA = 4096;
 #define MOE_DISPATCH_MAX_E 1024
 hipError_t launch_dispatch(const int32_t* ids, int A, int E, int32_t* chunk_ws, int32_t* counts,
                            int32_t* offsets, int32_t* sorted_assign, int32_t* assign_pos, hipStream_t st,
-                           int BM = 0, int2* tiles = nullptr, int32_t* ntiles = nullptr);
+                           int BM = 0, int2* tiles = nullptr, int32_t* ntiles = nullptr, int32_t* pairs = nullptr,
+                           int32_t* npairs = nullptr);
+// pair list of the 256-row items from the expert counts (k_ffn.hip)
+hipError_t launch_pairs(const int32_t* counts, int E, int32_t* pairs, int32_t* npairs, hipStream_t st);
 hipError_t launch_tiles(const int32_t* counts, int E, int BM, int2* tiles, int32_t* ntiles, hipStream_t st);
 
 // ---- grouped FFN
@@ -98,7 +101,7 @@ FfnWs carve_ffn_ws(const FfnArgs& a, void* ws);
 // `mid`: optional event recorded between the gate+up and the down GEMM; tiles_ready: the
 // tile list in the workspace was already written (by launch_dispatch)
 hipError_t launch_grouped_ffn(const FfnArgs& a, void* ws, hipStream_t st, hipEvent_t mid = nullptr,
-                              bool tiles_ready = false);
+                              bool tiles_ready = false, bool pairs_ready = false);
 // MX schemes on 16-row tiles (k_mx.hip)
 hipError_t launch_ffn_mx(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid);
 
