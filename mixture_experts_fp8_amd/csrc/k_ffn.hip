@@ -1828,12 +1828,14 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, void* ws, hipStream_t st, hipEve
 // for all of them before summing them in slot order j = 0, 1, ...
 template <bool BF16>
 __device__ __forceinline__ float4 load4(const void* eo, int64_t idx) {
+    // expert_out is read exactly once: non-temporal loads keep it from displacing cached lines
     if (BF16) {
-        const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(eo) + idx);
-        return make_float4(bf16_to_f32(u.x & 0xFFFFu), bf16_to_f32(u.x >> 16), bf16_to_f32(u.y & 0xFFFFu),
-                           bf16_to_f32(u.y >> 16));
+        const v2i_t u = __builtin_nontemporal_load(reinterpret_cast<const v2i_t*>(reinterpret_cast<const uint16_t*>(eo) + idx));
+        return make_float4(bf16_to_f32((uint32_t)u[0] & 0xFFFFu), bf16_to_f32((uint32_t)u[0] >> 16),
+                           bf16_to_f32((uint32_t)u[1] & 0xFFFFu), bf16_to_f32((uint32_t)u[1] >> 16));
     }
-    return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(eo) + idx);
+    const v4f v = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(reinterpret_cast<const float*>(eo) + idx));
+    return make_float4(v[0], v[1], v[2], v[3]);
 }
 
 template <bool BF16, int CPT>

@@ -11,6 +11,8 @@
 
 namespace moe {
 
+typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
+
 // ----------------------------------------------------------------------------------------
 // Gate prelude: logits[t, e] = r_t * sum_h x[t,h] * norm_w[h] * W_r[e, h], with
 // r_t = 1 / sqrt(mean_h x[t,h]^2 + eps) -- RMSNorm then the float32 router matmul, with the
@@ -251,7 +253,10 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const int g = g0 + (lane >> 4) + 4 * i;
-                    if (g < ngc) v[i] = *reinterpret_cast<const uint4*>(xr + g * kGroup + (lane & 15) * 8);
+                    if (g < ngc) {   // the row is read once: non-temporal
+                        const v4u_t u = __builtin_nontemporal_load(reinterpret_cast<const v4u_t*>(xr + g * kGroup + (lane & 15) * 8));
+                        v[i] = make_uint4(u[0], u[1], u[2], u[3]);
+                    }
                 }
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
