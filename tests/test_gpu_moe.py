@@ -171,6 +171,31 @@ def test_fused_workload_sampled(cfg, ntok):
     print(f"  rel fro {fro:.2e} rel max {mx:.2e}", flush=True)
 
 
+# Tile pairs at H/128 = 16 and 32 with a few hundred 256-row items over a few skewed experts:
+# full pairs, ragged second tiles and single-tile pairs, several items per expert and column
+# block.  Every 8th token is compared: sorted rows follow token order within an expert, so
+# every 256-row item holds sampled rows.
+MEDIUM = {
+    "persistent_tile_pairs_kb16": W.Workload(136, "p2pk16", T=4096, H=2048, I=2048, E=4, k=2, bias="normal1.5"),
+    "persistent_tile_pairs_kb32": W.Workload(137, "p2pk32", T=6144, H=4096, I=1024, E=4, k=2, bias="normal1.5"),
+}
+
+
+@pytest.mark.parametrize("name", list(MEDIUM))
+def test_fused_medium_sampled(name):
+    wl = MEDIUM[name]
+    print("fused medium", name, W.describe(wl), flush=True)
+    y, ids, _, counts, _ = _run_fused(wl)
+    tokens = np.arange(0, wl.T, 8)
+    ref, ids_ref, _, margin = _oracle(wl, tokens=tokens, workers=int(os.environ.get("ORACLE_WORKERS", "8")))
+    ok = margin >= 1e-5
+    assert np.array_equal(ids[ok], ids_ref[ok])
+    assert counts.sum() == wl.T * wl.k
+    sel = ok[tokens]
+    fro, mx = HN.assert_output_close(HN.bf16_to_f64(y)[tokens][sel], ref["y"][sel], name, ref["qmargin_tok"][sel])
+    print(f"  rel fro {fro:.2e} rel max {mx:.2e}", flush=True)
+
+
 # ---- one shared expert (weights of expert index E) run on every token in the same launches
 SHARED = {
     "shared_small": W.Workload(140, "sh", T=96, H=256, I=256, E=8, k=2, shared=1),
