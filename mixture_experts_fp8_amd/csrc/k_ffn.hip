@@ -751,6 +751,26 @@ __device__ __forceinline__ uint32_t e4m3_quad_rows(const float (&h)[4], const in
     return __builtin_amdgcn_perm((uint32_t)w, (uint32_t)x1, (q & 1) ? 0x03070105u : 0x06020400u);
 }
 
+// One thread per row r < nrows: the row's E4M3 scale exponent (from the four column waves'
+// maxima) as the biased byte, in row order (s_ex) and in the order of the hs blocks,
+// [tile of the item][row % 16][row / 16] (s_exT), which a few 16-byte stores then copy out.
+__device__ __forceinline__ void row_exponents(const float (*s_amax)[4], uint8_t* s_ex, uint8_t* s_exT, int nrows) {
+    const int r = threadIdx.x;
+    if (r < nrows) {
+        const float4 am4 = *reinterpret_cast<const float4*>(s_amax[r]);
+        const uint8_t b = (uint8_t)(scale_exponent(fmaxf(fmaxf(am4.x, am4.y), fmaxf(am4.z, am4.w))) + 127);
+        s_ex[r] = b;
+        s_exT[(r >> 7) * 128 + (r & 15) * 8 + ((r >> 4) & 7)] = b;
+    }
+}
+
+// The exponents of rows row0 .. row0 + 3 (row0 % 4 == 0) from s_ex.
+__device__ __forceinline__ void load_exponents4(const uint8_t* s_ex, int row0, int (&ex)[4]) {
+    const uint32_t b4 = *reinterpret_cast<const uint32_t*>(s_ex + row0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ex[i] = (int)((b4 >> (8 * i)) & 0xFFu) - 127;
+}
+
 __global__ __launch_bounds__(512, 1) void k_gemm1_pf(G1Args a) {
     int ib, tile;
     if (!pf_work_item(a.ord, a.I / kGroup, __builtin_amdgcn_readfirstlane(*a.ntiles), tile, ib)) return;
@@ -766,6 +786,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pf(G1Args a) {
     __shared__ __align__(16) uint8_t s_sa[kPfMaxKB * kPfBM];   // [kb][wm][row % 16][fragment of wm]
     __shared__ uint16_t s_sgu[kPfMaxKB];                      // gate scale | up scale << 8
     __shared__ __align__(16) float s_amax[kPfBM][4];   // [row][column wave]
+    __shared__ __align__(16) uint8_t s_ex[kPfBM], s_exT[kPfBM];
 
     const int NB16 = 2 * a.I / 16, NBS = 2 * a.I / kGroup;
     const v4i_t ra = make_srd(a.xq, (uint32_t)a.T * a.H);
@@ -903,6 +924,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pf(G1Args a) {
         }
     }
     __syncthreads();   // also: every wave is done reading the stages before buf is reused
+    row_exponents(s_amax, s_ex, s_exT, kPfBM);
+    __syncthreads();
     // E4M3 requantisation; h staged as [128 rows][128] bytes, 16-byte chunks XOR-swizzled by
     // row % 8, one dword (4 columns of one row) per lane and fragment
     uint8_t* s_h = buf;
@@ -911,14 +934,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pf(G1Args a) {
     for (int mi = 0; mi < 4; ++mi) {
         if (mi < nact) {
             int ex[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = (wm * 4 + mi) * 16 + g4 + i;
-                const float4 am4 = *reinterpret_cast<const float4*>(s_amax[row]);
-                ex[i] = scale_exponent(fmaxf(fmaxf(am4.x, am4.y), fmaxf(am4.z, am4.w)));
-                if (wn == 0 && r16 == 0)   // [tile][kb][row % 16][row / 16]
-                    a.hs[(((int64_t)tile * (a.I / kGroup) + ib) * 16 + (row & 15)) * 8 + (row >> 4)] = (uint8_t)(ex[i] + 127);
-            }
+            load_exponents4(s_ex, (wm * 4 + mi) * 16 + g4, ex);
             const int row = (wm * 4 + mi) * 16 + g4 + q;
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj)
@@ -934,6 +950,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pf(G1Args a) {
         const uint4 v = *reinterpret_cast<const uint4*>(s_h + R * 128 + (((2 * (ln >> 4) + hh) ^ (R & 7)) << 4));
         *reinterpret_cast<uint4*>(a.hq + (((int64_t)tile * 8 + mf) * KB2 + ib) * kFragBytes + hh * 1024 + ln * 16) = v;
     }
+    if (tid < 8)   // the tile's hs block for this column block: [row % 16][row / 16]
+        *reinterpret_cast<uint4*>(a.hs + ((int64_t)tile * KB2 + ib) * 128 + tid * 16) =
+            *reinterpret_cast<const uint4*>(s_exT + tid * 16);
 }
 
 // ----------------------------------------------------------------------------------------
@@ -966,6 +985,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pp(G1Args a) {
     __shared__ uint16_t s_sgu[2][kPpMaxKB];                      // gate scale | up scale << 8
     __shared__ __align__(16) int s_tok[2][kPfBM];                // sorted assignment ids of the item's rows
     __shared__ __align__(16) float s_amax[kPfBM][4];
+    __shared__ __align__(16) uint8_t s_ex[kPfBM], s_exT[kPfBM];
     __shared__ int4 s_it[kPpMaxItems];                           // tile, column block, expert, first sorted row
     __shared__ int s_nv[kPpMaxItems];
     __shared__ int s_cnt[kItWaves];
@@ -1136,6 +1156,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pp(G1Args a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
         __syncthreads();   // also: every wave is done reading the stage of block g - 1
+        row_exponents(s_amax, s_ex, s_exT, kPfBM);
+        __syncthreads();
         // h staged in the stage of the item's last block (the next two blocks are in the others)
         uint8_t* s_h = buf + (sg3 == 0 ? 2 : sg3 - 1) * kPfStage;   // [128 rows][128], chunks swizzled by row % 8
         const int q = lane & 3, g4 = 4 * (lane >> 4);
@@ -1143,14 +1165,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pp(G1Args a) {
         for (int mi = 0; mi < 4; ++mi) {
             if (mi < nact) {
                 int ex[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = (wm * 4 + mi) * 16 + g4 + i;
-                    const float4 am4 = *reinterpret_cast<const float4*>(s_amax[row]);
-                    ex[i] = scale_exponent(fmaxf(fmaxf(am4.x, am4.y), fmaxf(am4.z, am4.w)));
-                    if (wn == 0 && r16 == 0)   // [tile][kb][row % 16][row / 16]
-                        a.hs[(((int64_t)tile * ncol + ib) * 16 + (row & 15)) * 8 + (row >> 4)] = (uint8_t)(ex[i] + 127);
-                }
+                load_exponents4(s_ex, (wm * 4 + mi) * 16 + g4, ex);
                 const int row = (wm * 4 + mi) * 16 + g4 + q;
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj)
@@ -1165,6 +1180,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pp(G1Args a) {
             const uint4 v = *reinterpret_cast<const uint4*>(s_h + R * 128 + (((2 * (ln >> 4) + hh) ^ (R & 7)) << 4));
             *reinterpret_cast<uint4*>(a.hq + (((int64_t)tile * 8 + mf) * ncol + ib) * kFragBytes + hh * 1024 + ln * 16) = v;
         }
+        if (tid < 8)   // the tile's hs block for this column block: [row % 16][row / 16]
+            *reinterpret_cast<uint4*>(a.hs + ((int64_t)tile * ncol + ib) * 128 + tid * 16) =
+                *reinterpret_cast<const uint4*>(s_exT + tid * 16);
     }
     wait_vm<0>();
 }
@@ -1346,6 +1364,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_p2(G1Args a) {
     __shared__ __align__(16) uint8_t s_sa[kPfMaxKB * kP2Rows];   // [kb][wm][row % 16][fragment of wm]
     __shared__ uint16_t s_sgu[kPfMaxKB];                        // gate scale | up scale << 8
     __shared__ __align__(16) float s_amax[kP2Rows][4];   // [row][column wave]
+    __shared__ __align__(16) uint8_t s_ex[kP2Rows], s_exT[kP2Rows];
 
     const int NB16 = 2 * a.I / 16, NBS = 2 * a.I / kGroup;
     const v4i_t ra = make_srd(a.xq, (uint32_t)a.T * a.H);
@@ -1477,6 +1496,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_p2(G1Args a) {
         }
     }
     __syncthreads();   // also: every wave is done reading the stages before buf is reused
+    row_exponents(s_amax, s_ex, s_exT, second ? kP2Rows : kPfBM);
+    __syncthreads();
     // E4M3 requantisation; h staged as [256 rows][128] bytes, 16-byte chunks XOR-swizzled by
     // row % 8, one dword (4 columns of one row) per lane and fragment
     uint8_t* s_h = buf;
@@ -1486,16 +1507,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_p2(G1Args a) {
     for (int mi = 0; mi < 8; ++mi) {
         if (mi < nact) {
             int ex[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = (wm * 8 + mi) * 16 + g4 + i;
-                const float4 am4 = *reinterpret_cast<const float4*>(s_amax[row]);
-                ex[i] = scale_exponent(fmaxf(fmaxf(am4.x, am4.y), fmaxf(am4.z, am4.w)));
-                if (wn == 0 && r16 == 0) {   // [tile][kb][row % 16][row / 16]
-                    const int rl = row & 127;
-                    a.hs[(((int64_t)(t0 + wm) * KB2 + ib) * 16 + (rl & 15)) * 8 + (rl >> 4)] = (uint8_t)(ex[i] + 127);
-                }
-            }
+            load_exponents4(s_ex, (wm * 8 + mi) * 16 + g4, ex);
             const int row = (wm * 8 + mi) * 16 + g4 + q;
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj)
@@ -1511,6 +1523,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_p2(G1Args a) {
         const uint4 v = *reinterpret_cast<const uint4*>(s_h + R * 128 + (((2 * (ln >> 4) + hh) ^ (R & 7)) << 4));
         *reinterpret_cast<uint4*>(a.hq + (((int64_t)t0 * 8 + mf) * KB2 + ib) * kFragBytes + hh * 1024 + ln * 16) = v;
     }
+    if (tid < (second ? 16 : 8))   // the pair's hs blocks for this column block: [row % 16][row / 16]
+        *reinterpret_cast<uint4*>(a.hs + ((int64_t)(t0 + (tid >> 3)) * KB2 + ib) * 128 + (tid & 7) * 16) =
+            *reinterpret_cast<const uint4*>(s_exT + tid * 16);
 }
 
 __global__ __launch_bounds__(512, 1) void k_gemm2_p2(G2Args a) {
