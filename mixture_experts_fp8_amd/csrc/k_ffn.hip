@@ -78,8 +78,8 @@ struct G1Args {
     uint8_t* hq;
     uint8_t* hs;
     int ord;    // work order of the 128-row-tile kernels: 1 super-tiles (ord_item), 0 column blocks
-    const int32_t* pairs;    // 256-row items: first tile of each pair, and the pair count
-    const int32_t* npairs;
+    const int4* pairs;       // 256-row items: {first tile, expert, first sorted row, valid rows}
+    const int32_t* npairs;   // and the pair count
 };
 
 __device__ __forceinline__ v8i lds_frag(const uint8_t* base, int lane) {
@@ -286,7 +286,7 @@ struct G2Args {
     void* out;
     int out_bf16;
     int ord;
-    const int32_t* pairs;
+    const int4* pairs;
     const int32_t* npairs;
 };
 
@@ -1314,10 +1314,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm2_pf(G2Args a) {
 // of the 128-row tiles.
 constexpr int kP2Rows = 256, kP2StageA = 16 * kFragBytes, kP2Stage = kP2StageA + 16 * kFragBytes;   // 64 KB
 
-// Pair list: for each expert, pairs[] holds the index of the first tile of each of its
-// ceil(count / 256) pairs (tiles of 128 rows in expert order, as k_tiles writes them).
-__global__ __launch_bounds__(1024) void k_pairs(const int32_t* __restrict__ counts, int E, int32_t* __restrict__ pairs,
-                                                int32_t* __restrict__ npairs) {
+// Pair list: for each expert, one entry per 256-row item (ceil(count / 256) of them) holding
+// the index of its first tile (tiles of 128 rows in expert order, as k_tiles writes them),
+// the expert, the item's first row in the sorted order and its valid rows, so that a GEMM
+// workgroup finds its rows with one load.
+__global__ __launch_bounds__(1024) void k_pairs(const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+                                                int E, int4* __restrict__ pairs, int32_t* __restrict__ npairs) {
     __shared__ int s_t[16], s_p[16];
     const int e = threadIdx.x;
     const int c = e < E ? counts[e] : 0;
@@ -1343,19 +1345,18 @@ __global__ __launch_bounds__(1024) void k_pairs(const int32_t* __restrict__ coun
         ap += s_p[w];
     }
     const int t0 = vt + at - nt, p0 = vp + ap - np;
-    for (int i = 0; i < np; ++i) pairs[p0 + i] = t0 + 2 * i;
+    const int off = e < E ? offsets[e] : 0;
+    for (int i = 0; i < np; ++i) pairs[p0 + i] = make_int4(t0 + 2 * i, e, off + kP2Rows * i, min(kP2Rows, c - kP2Rows * i));
     if (e == 1023) *npairs = vp + ap;
 }
 
 __global__ __launch_bounds__(512, 1) void k_gemm1_p2(G1Args a) {
     int ib, pair;
     if (!pf_work_item(a.ord, a.I / kGroup, __builtin_amdgcn_readfirstlane(*a.npairs), pair, ib)) return;
-    const int t0 = __builtin_amdgcn_readfirstlane(a.pairs[pair]);
-    const int2 te = a.tiles[t0];
-    const int e = __builtin_amdgcn_readfirstlane(te.x), m0 = __builtin_amdgcn_readfirstlane(te.y);
-    const int nvalid = min(kP2Rows, a.counts[e] - m0);
+    const int4 pi = a.pairs[pair];
+    const int t0 = __builtin_amdgcn_readfirstlane(pi.x), e = __builtin_amdgcn_readfirstlane(pi.y);
+    const int rowbase = __builtin_amdgcn_readfirstlane(pi.z), nvalid = __builtin_amdgcn_readfirstlane(pi.w);
     const bool second = nvalid > kPfBM;
-    const int rowbase = __builtin_amdgcn_readfirstlane(a.offsets[e] + m0);
     const int KB = a.H / kGroup;
     const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wv >> 2, wn = wv & 3;
@@ -1531,12 +1532,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_p2(G1Args a) {
 __global__ __launch_bounds__(512, 1) void k_gemm2_p2(G2Args a) {
     int nb, pair;
     if (!pf_work_item(a.ord, a.H / 256, __builtin_amdgcn_readfirstlane(*a.npairs), pair, nb)) return;
-    const int t0 = __builtin_amdgcn_readfirstlane(a.pairs[pair]);
-    const int2 te = a.tiles[t0];
-    const int e = __builtin_amdgcn_readfirstlane(te.x), m0 = __builtin_amdgcn_readfirstlane(te.y);
-    const int nvalid = min(kP2Rows, a.counts[e] - m0);
+    const int4 pi = a.pairs[pair];
+    const int t0 = __builtin_amdgcn_readfirstlane(pi.x), e = __builtin_amdgcn_readfirstlane(pi.y);
+    const int rowbase = __builtin_amdgcn_readfirstlane(pi.z), nvalid = __builtin_amdgcn_readfirstlane(pi.w);
     const bool second = nvalid > kPfBM;
-    const int rowbase = __builtin_amdgcn_readfirstlane(a.offsets[e] + m0);
     const int KB = a.I / kGroup;
     const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wv >> 2, wn = wv & 3;
@@ -1686,13 +1685,13 @@ FfnPlan ffn_plan(int T, int k, int E, int quant) {
 
 // workspace: tiles [ntiles_max] int2 | ntiles int | hq [ntiles_max*BM, I] | hs [ntiles_max*BM, I/128]
 //            | (128-row tiles) down-GEMM weight-scale table [E][H/128][I/128] u32
-//            | pairs [npairs_max] int | npairs int
+//            | pairs [npairs_max] int4 | npairs int
 static size_t ffn_ws_plan(const FfnPlan& p, int H, int I, int E) {
     const size_t rows = (size_t)p.ntiles_max * p.BM;
     // hs holds one scale per 32 columns of h (the MX schemes; the 128 scheme uses a quarter)
     size_t n = align256((size_t)p.ntiles_max * 8) + align256(4) + align256(rows * I) + align256(rows * (I / 32));
     if (p.BM == 128) n += align256(ffn_rb_scale_table_bytes(H, I, E));
-    n += align256((size_t)p.npairs_max * 4) + align256(4);
+    n += align256((size_t)p.npairs_max * 16) + align256(4);
     return n;
 }
 size_t ffn_workspace_bytes(int T, int H, int I, int E, int k) {
@@ -1768,14 +1767,16 @@ static hipError_t run_ffn_pf(const FfnArgs& f, const FfnPlan& p, const FfnWs& w,
     return hipGetLastError();
 }
 
-hipError_t launch_pairs(const int32_t* counts, int E, int32_t* pairs, int32_t* npairs, hipStream_t st) {
-    hipLaunchKernelGGL(k_pairs, dim3(1), dim3(1024), 0, st, counts, E, pairs, npairs);
+hipError_t launch_pairs(const int32_t* counts, const int32_t* offsets, int E, int4* pairs, int32_t* npairs,
+                        hipStream_t st) {
+    hipLaunchKernelGGL(k_pairs, dim3(1), dim3(1024), 0, st, counts, offsets, E, pairs, npairs);
     return hipGetLastError();
 }
 
 static hipError_t run_ffn_p2(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid,
                              bool pairs_ready) {
-    if (!pairs_ready) hipLaunchKernelGGL(k_pairs, dim3(1), dim3(1024), 0, st, f.counts, f.E, w.pairs, w.npairs);
+    if (!pairs_ready)
+        hipLaunchKernelGGL(k_pairs, dim3(1), dim3(1024), 0, st, f.counts, f.offsets, f.E, w.pairs, w.npairs);
     const int ord = ffn_super_tile_order(p.ntiles_max);
     G1Args g1{f.xq, f.xs, f.T, f.k, f.H, f.I, f.counts, f.offsets, f.sorted_assign, w.tiles, w.ntiles, f.w13p, f.w13s,
               w.hq, w.hs, ord, w.pairs, w.npairs};
@@ -1809,8 +1810,8 @@ FfnWs carve_ffn_ws(const FfnArgs& f, void* ws) {
     w += align256(rows * (f.I / 32));
     r.bs = p.BM == 128 ? reinterpret_cast<uint32_t*>(w) : nullptr;
     if (p.BM == 128) w += align256(ffn_rb_scale_table_bytes(f.H, f.I, f.E));
-    r.pairs = reinterpret_cast<int32_t*>(w);
-    w += align256((size_t)p.npairs_max * 4);
+    r.pairs = reinterpret_cast<int4*>(w);
+    w += align256((size_t)p.npairs_max * 16);
     r.npairs = reinterpret_cast<int32_t*>(w);
     return r;
 }

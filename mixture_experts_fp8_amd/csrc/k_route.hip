@@ -328,11 +328,12 @@ __device__ int block_inclusive_scan_1024(int v, int* s_tmp /*[16]*/) {
 // (g, e) owns the contiguous chunks [g * cpt, (g + 1) * cpt), so its loads are independent
 // of one another; the per-thread sums are scanned across g, then the expert totals across e.
 // With `tiles`, it also writes the GEMM tile list (expert order, BM rows per tile) and, with
-// `pairs`, the pair list of the 256-row items (first tile of each pair), as k_tiles / k_pairs do.
+// `pairs`, the pair list of the 256-row items ({first tile, expert, first sorted row, valid
+// rows} per pair), as k_tiles / k_pairs do.
 __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ cc, int nchunks, int E, int Ep,
                                                int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int BM,
                                                int2* __restrict__ tiles, int32_t* __restrict__ ntiles,
-                                               int32_t* __restrict__ pairs, int32_t* __restrict__ npairs) {
+                                               int4* __restrict__ pairs, int32_t* __restrict__ npairs) {
     __shared__ int s_tmp[16];
     __shared__ int s_part[1024];
     const int gpe = 1024 / Ep, e = threadIdx.x % Ep, g = threadIdx.x / Ep;
@@ -389,7 +390,8 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ cc, int nch
         if (own) {
             const int t0 = it - nt, p0 = ip - np;
             for (int i = 0; i < nt; ++i) tiles[t0 + i] = make_int2(e, i * BM);
-            for (int i = 0; i < np; ++i) pairs[p0 + i] = t0 + 2 * i;
+            for (int i = 0; i < np; ++i)
+                pairs[p0 + i] = make_int4(t0 + 2 * i, e, off + 2 * BM * i, min(2 * BM, run - 2 * BM * i));
             if (e == E - 1) {
                 *ntiles = it;
                 if (pairs) *npairs = ip;
@@ -585,13 +587,13 @@ __global__ __launch_bounds__(64 * kOneWaves) void k_dispatch_one(const int32_t* 
 
 hipError_t launch_dispatch(const int32_t* ids, int A, int E, int32_t* chunk_ws, int32_t* counts,
                            int32_t* offsets, int32_t* sorted_assign, int32_t* assign_pos, hipStream_t st,
-                           int BM, int2* tiles, int32_t* ntiles, int32_t* pairs, int32_t* npairs) {
+                           int BM, int2* tiles, int32_t* ntiles, int4* pairs, int32_t* npairs) {
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
     if (A <= kDispatchOneMaxA) {
         hipLaunchKernelGGL(k_dispatch_one, dim3(1), dim3(64 * kOneWaves), 0, st, ids, A, E, nbits, counts, offsets,
                            sorted_assign, assign_pos, BM, tiles, ntiles);
-        if (pairs) return launch_pairs(counts, E, pairs, npairs, st);
+        if (pairs) return launch_pairs(counts, offsets, E, pairs, npairs, st);
         return hipGetLastError();
     }
     const int nchunks = (int)ceil_div(A, kScatterChunk);

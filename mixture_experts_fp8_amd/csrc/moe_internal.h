@@ -56,10 +56,11 @@ constexpr int kDispatchOneMaxA = 4096;
 #define MOE_DISPATCH_MAX_E 1024
 hipError_t launch_dispatch(const int32_t* ids, int A, int E, int32_t* chunk_ws, int32_t* counts,
                            int32_t* offsets, int32_t* sorted_assign, int32_t* assign_pos, hipStream_t st,
-                           int BM = 0, int2* tiles = nullptr, int32_t* ntiles = nullptr, int32_t* pairs = nullptr,
+                           int BM = 0, int2* tiles = nullptr, int32_t* ntiles = nullptr, int4* pairs = nullptr,
                            int32_t* npairs = nullptr);
 // pair list of the 256-row items from the expert counts (k_ffn.hip)
-hipError_t launch_pairs(const int32_t* counts, int E, int32_t* pairs, int32_t* npairs, hipStream_t st);
+hipError_t launch_pairs(const int32_t* counts, const int32_t* offsets, int E, int4* pairs, int32_t* npairs,
+                        hipStream_t st);
 hipError_t launch_tiles(const int32_t* counts, int E, int BM, int2* tiles, int32_t* ntiles, hipStream_t st);
 
 // ---- grouped FFN
@@ -94,7 +95,7 @@ struct FfnWs {
     uint8_t* hq;
     uint8_t* hs;
     uint32_t* bs;        // 128-row tiles: down-GEMM weight-block scales per [expert][column block][kb]
-    int32_t* pairs;      // 256-row items: index of the first tile of each pair
+    int4* pairs;         // 256-row items: {first tile, expert, first sorted row, valid rows} per pair
     int32_t* npairs;
 };
 FfnWs carve_ffn_ws(const FfnArgs& a, void* ws);

@@ -99,6 +99,29 @@ def test_grouped_ffn_unit_cfg1():
     HN.assert_output_close(HN.bf16_to_f64(y), ref["y"], "combine", ref["qmargin_tok"])
 
 
+@pytest.mark.parametrize("name", ["tile_pairs_skewed", "persistent_tiles_kb12"])
+def test_separate_entry_points_match_fused(name):
+    # moe_route -> moe_quant_act -> moe_grouped_ffn -> moe_combine on the 256-row-item and
+    # persistent-tile paths (the grouped FFN builds its own tile / pair lists here): the same
+    # bits as the fused call, and the oracle's expert outputs
+    wl = SMALL[name]
+    x, logits, _ = HN.device_inputs(wl)
+    w = HN.device_weights(wl)
+    r = M.moe_route(HN.device_params(wl), wl.T, router_logits=logits)
+    xq, xs = M.moe_quant_act(x)
+    eo = M.moe_grouped_ffn(xq, xs, r, w, wl.k)
+    y = M.moe_combine(eo, r["assign_pos"], r["topk_weights"])
+    yf = M.moe_fused(HN.device_params(wl), x, w, router_logits=logits)
+    assert torch.equal(y, yf)
+    ref, ids_ref, _, margin = _oracle(wl)
+    ok = margin >= 1e-5
+    assert np.array_equal(r["topk_ids"].cpu().numpy()[ok], ids_ref[ok])
+    pos = r["assign_pos"].cpu().numpy().astype(np.int64)
+    got = eo.cpu().numpy().astype(np.float64)[pos]          # back to flat (t, j) order
+    okf = np.repeat(ok, wl.k)
+    HN.assert_output_close(got[okf], ref["o"][okf], "expert_out", ref["qmargin"][okf])
+
+
 def test_golden_hand_ffn_through_device():
     # x = 1, gate weights 2^-7, up 2^-6, down 2^-7 -> y = 1.5 exactly (tests/golden/ffn_hand.txt)
     H = I = 128
