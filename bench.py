@@ -35,7 +35,7 @@ LAYERS = 4
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["mixture_experts_fp8_amd/csrc/k_ffn.hip", "mixture_experts_fp8_amd/csrc/k_ffn_rb.hip",
                   "mixture_experts_fp8_amd/csrc/k_mx.hip", "mixture_experts_fp8_amd/csrc/moe_common.h",
-                  "mixture_experts_fp8_amd/csrc/work_items.h"]
+                  "mixture_experts_fp8_amd/csrc/work_items.h", "mixture_experts_fp8_amd/csrc/k_w16.hip"]
 
 
 def parse():
@@ -50,9 +50,9 @@ def parse():
                     help="add one shared expert (same H, I) run on every token in the same launches")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0, help="0: the workload's own default sample")
     ap.add_argument("--expert-out-bf16", action="store_true", help="keep per-assignment expert outputs in bf16")
-    ap.add_argument("--quant", default="fp8", choices=["fp8", "mxfp8", "w4a8"],
+    ap.add_argument("--quant", default="fp8", choices=["fp8", "mxfp8", "w4a8", "w8a16"],
                     help="fp8: E4M3 with 128-element scales (default); mxfp8: 32-element scales; "
-                         "w4a8: E2M1 weights with MXFP8 activations")
+                         "w4a8: E2M1 weights with MXFP8 activations; w8a16: the fp8 weights with bf16 activations")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (a known-size kernel for HBM counter calibration)")
     return ap.parse_args()
@@ -95,25 +95,35 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-# bytes per weight element and elements per scale byte: (weights, activation groups, weight groups)
-SCHEME_BYTES = {"fp8": (1.0, 128, 128 * 128), "mxfp8": (1.0, 32, 32), "w4a8": (0.5, 32, 32)}
+# bytes per weight element, bytes per activation element, activation elements per scale byte
+# (0: no activation scales) and weight elements per scale byte
+SCHEME_BYTES = {"fp8": (1.0, 1, 128, 128 * 128), "mxfp8": (1.0, 1, 32, 32), "w4a8": (0.5, 1, 32, 32),
+                "w8a16": (1.0, 2, 0, 128 * 128)}
+# peak of the matrix-core type each scheme contracts in (TFLOP/s, dense)
+SCHEME_PEAK = {"fp8": 5000.0, "mxfp8": 5000.0, "w4a8": 5000.0, "w8a16": 2500.0}
+
+
+def act_bytes(n: int, ab: int, ga: int) -> float:
+    """Bytes of n activation elements and their scales."""
+    return n * ab + (n / ga if ga else 0)
 
 
 def stage_bytes_flops(wl, counts: np.ndarray, eo_bytes: int, quant: str = "fp8"):
     """Algorithmic HBM bytes and FP8 flops per launch of the two GEMM stages.
 
     gate+up: every active expert's w13 once (H*2I weight elements at wb bytes each plus
-    one scale byte per weight group), each token's quantised row once (H + H/ga), each
-    assignment's hq row written once (I + I/ga).  down: every active expert's w2 once, each
-    hq row read once, each assignment's output row written once (H * eo_bytes).  wb = 1 for
-    E4M3 weights and 0.5 for E2M1; groups of ga = 128 (or 32) activations and gw = 128 x 128
-    (or 32) weights per scale byte.
+    one scale byte per weight group), each token's activation row once (H elements at ab
+    bytes plus H/ga scale bytes), each assignment's h row written once (I elements, I/ga
+    scales).  down: every active expert's w2 once, each h row read once, each assignment's
+    output row written once (H * eo_bytes).  wb = 1 for E4M3 weights and 0.5 for E2M1; ab = 1
+    for E4M3 activations and 2 for bf16 (W8A16, no activation scales); groups of ga = 128 (or
+    32) activations and gw = 128 x 128 (or 32) weights per scale byte.
     """
-    wb, ga, gw = SCHEME_BYTES[quant]
+    wb, ab, ga, gw = SCHEME_BYTES[quant]
     H, I, T, A = wl.H, wl.I, wl.T, wl.T * (wl.k + wl.shared)
     n_act = int((counts > 0).sum())
-    g1_bytes = n_act * (H * 2 * I * wb + H * 2 * I / gw) + T * (H + H / ga) + A * (I + I / ga)
-    g2_bytes = n_act * (I * H * wb + I * H / gw) + A * (I + I / ga) + A * H * eo_bytes
+    g1_bytes = n_act * (H * 2 * I * wb + H * 2 * I / gw) + act_bytes(T * H, ab, ga) + act_bytes(A * I, ab, ga)
+    g2_bytes = n_act * (I * H * wb + I * H / gw) + act_bytes(A * I, ab, ga) + A * H * eo_bytes
     g1_flops = 4.0 * A * H * I
     g2_flops = 2.0 * A * H * I
     return {"gate_up_gemm": (int(g1_bytes), g1_flops), "down_gemm": (int(g2_bytes), g2_flops)}, n_act
@@ -122,7 +132,7 @@ def stage_bytes_flops(wl, counts: np.ndarray, eo_bytes: int, quant: str = "fp8")
 def step_algorithmic_bytes(wl, n_act: int, quant: str = "fp8") -> int:
     """Minimum traffic of a whole step: active experts' weights and scales, x, logits
     (or the prelude tensors), y, ids and weights."""
-    wb, _, gw = SCHEME_BYTES[quant]
+    wb, _, _, gw = SCHEME_BYTES[quant]
     H, I, T, E, k = wl.H, wl.I, wl.T, wl.E, wl.k
     b = int(n_act * (3 * H * I * wb + 3 * H * I / gw))
     b += 2 * T * H + 2 * T * H + 8 * T * (k + wl.shared)
@@ -130,17 +140,17 @@ def step_algorithmic_bytes(wl, n_act: int, quant: str = "fp8") -> int:
     return b
 
 
-def roofline_entry(name, dur_s, nbytes, flops, traffic):
+def roofline_entry(name, dur_s, nbytes, flops, traffic, peak_tflops=PEAK_FP8_TFLOPS):
     t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
-    t_mfma = flops / (PEAK_FP8_TFLOPS * 1e12)
+    t_mfma = flops / (peak_tflops * 1e12)
     if t_hbm >= t_mfma:
         ach = nbytes / dur_s / 1e9
         return {"kernel": name, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic, "algorithmic_bytes": int(nbytes),
                 "avg_us": round(dur_s * 1e6, 2)}
     ach = flops / dur_s / 1e12
-    return {"kernel": name, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(ach / PEAK_FP8_TFLOPS, 4), "traffic": traffic, "algorithmic_flops": flops,
+    return {"kernel": name, "bound": "mfma", "achieved": round(ach, 1), "peak": peak_tflops, "unit": "TFLOP/s",
+            "frac": round(ach / peak_tflops, 4), "traffic": traffic, "algorithmic_flops": flops,
             "avg_us": round(dur_s * 1e6, 2)}
 
 
@@ -168,6 +178,7 @@ def cpu_baseline(wl, sample_tokens: int, quant: str = "fp8", min_seconds: float 
     from oracle import moe as omoe
     from oracle import mx as omx
     from oracle import routing as orouting
+    from oracle import w8a16 as ow16
 
     x = W.hidden_bf16(wl)
     xf = W.bf16_to_f64(x)
@@ -188,8 +199,9 @@ def cpu_baseline(wl, sample_tokens: int, quant: str = "fp8", min_seconds: float 
     def src(e):
         return (W.expert_weight_f32(wl, "w13", e).numpy(), W.expert_weight_f32(wl, "w2", e).numpy())
 
-    if quant == "fp8":
-        ex, fwd = omoe.QuantizedExperts(src, cache=len(experts)), omoe.forward
+    if quant in ("fp8", "w8a16"):
+        ex = omoe.QuantizedExperts(src, cache=len(experts))
+        fwd = omoe.forward if quant == "fp8" else ow16.forward
     else:
         fmt = omx.FMT_E2M1 if quant == "w4a8" else omx.FMT_E4M3
         ex, fwd = omx.QuantizedExpertsMX(src, fmt, cache=len(experts)), omx.forward
@@ -245,7 +257,7 @@ def main():
         logits = W.router_logits(wl, dev)
     H, I, E = wl.H, wl.I, wl.E + wl.shared   # the shared expert's weights come last
     quant = M.QUANT_SCHEMES[args.quant]
-    if quant == M.MOE_QUANT_FP8_BLOCK128:
+    if quant in (M.MOE_QUANT_FP8_BLOCK128, M.MOE_QUANT_W8A16):   # W8A16 reads the same packed weights
         w13p = torch.empty(E * H * 2 * I, dtype=torch.uint8, device=dev)
         w2p = torch.empty(E * I * H, dtype=torch.uint8, device=dev)
         w13s = torch.empty(E, H // 128, 2 * I // 128, dtype=torch.uint8, device=dev)
@@ -334,8 +346,9 @@ def main():
         return t
 
     tname = (wl.name + ("_shared" if wl.shared else "")) + ("" if args.quant == "fp8" else f"_{args.quant}")
-    roof = roofline_entry(dom, kernel_time(dom), *per_stage[dom], load_traffic(tname, dom))
-    roof_other = roofline_entry(other, kernel_time(other), *per_stage[other], load_traffic(tname, other))
+    peak = SCHEME_PEAK[args.quant]
+    roof = roofline_entry(dom, kernel_time(dom), *per_stage[dom], load_traffic(tname, dom), peak)
+    roof_other = roofline_entry(other, kernel_time(other), *per_stage[other], load_traffic(tname, other), peak)
 
     step_bytes = step_algorithmic_bytes(wl, n_act, args.quant)
     total_flops = wl.flops()
@@ -352,16 +365,18 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"fp8": "fp8_e4m3 (fp32 accumulate)", "mxfp8": "mxfp8_e4m3 (fp32 accumulate)",
-                  "w4a8": "fp4_e2m1 weights x fp8_e4m3 activations (fp32 accumulate)"}[args.quant],
+                  "w4a8": "fp4_e2m1 weights x fp8_e4m3 activations (fp32 accumulate)",
+                  "w8a16": "fp8_e4m3 weights decoded to bf16 x bf16 activations (fp32 accumulate)"}[args.quant],
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: {W.describe(wl)}", "tokens_per_step": wl.T,
                    "weight_copies_rotated": LAYERS, "expert_out": "bf16" if args.expert_out_bf16 else "fp32",
                    "quant": {"fp8": "E4M3, UE8M0 per (row,128) / 128x128 block", "mxfp8": "E4M3, UE8M0 per 32",
-                             "w4a8": "E2M1 weights + E4M3 activations, UE8M0 per 32"}[args.quant],
+                             "w4a8": "E2M1 weights + E4M3 activations, UE8M0 per 32",
+                             "w8a16": "E4M3 weights, UE8M0 per 128x128 block; bf16 activations"}[args.quant],
                    "active_experts": n_act},
         "fp8_tflops": round(total_flops / step_s / 1e12, 3),
         "step_hbm_frac": round(step_bytes / step_s / 1e9 / PEAK_HBM_GBS, 4),
-        "step_mfma_frac": round(total_flops / step_s / 1e12 / PEAK_FP8_TFLOPS, 4),
+        "step_mfma_frac": round(total_flops / step_s / 1e12 / SCHEME_PEAK[args.quant], 4),
         "step_algorithmic_bytes": int(step_bytes),
         "stages_us": stages,
         "roofline": roof,

@@ -177,10 +177,18 @@ int moe_prepack_weights(const uint8_t* w, int32_t E, int32_t K, int32_t N,
  * [-127, 127], e = 0 for an all-zero group; codes = RNE(v / 2^e), ties to the even code, sign
  * of zero kept.  The SwiGLU output is re-quantised to E4M3 per (row, 32 columns) in both MX
  * schemes.  E2M1 is the OCP 4-bit float: sign, 2 exponent bits (bias 1), 1 mantissa bit,
- * magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+ * magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+ *   MOE_QUANT_W8A16         weight-only: the E4M3 weights and 128 x 128 scales of
+ *                           MOE_QUANT_FP8_BLOCK128 (same packing), bf16 activations (the
+ *                           metrale grouped FP8 MoE page, module notes: the experts decode
+ *                           W8A16 unless FP8 activations are published; the W8A8 step differs
+ *                           only by the activation rounding).  gu = x @ dequant(w13) with x
+ *                           the bf16 hidden state as is; h = silu(g) * u rounded once to bf16
+ *                           (RNE); expert_out = h @ dequant(w2).  Float32 accumulation. */
 #define MOE_QUANT_FP8_BLOCK128  0
 #define MOE_QUANT_MXFP8         1
 #define MOE_QUANT_W4A8          2
+#define MOE_QUANT_W8A16         3
 #define MOE_WFMT_E4M3           0
 #define MOE_WFMT_E2M1           1
 
@@ -250,6 +258,9 @@ typedef struct moe_ffn_args {
     int32_t        quant;       /* MOE_QUANT_*; the MX schemes take xs [T, H/32] from
                                    moe_quant_act_mx and the packed MX weights and scales of
                                    moe_prepack_weights_mx in w13 / w13_scale / w2 / w2_scale */
+    const uint16_t* x;          /* MOE_QUANT_W8A16 only: the bf16 hidden states [T, H]
+                                   (16-byte aligned); xq and xs are then unused and may be
+                                   NULL.  Ignored by the other schemes. */
 } moe_ffn_args;
 
 int moe_grouped_ffn(const moe_ffn_args* a);

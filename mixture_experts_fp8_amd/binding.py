@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import dataclasses
 from dataclasses import dataclass
 from typing import Optional
 
@@ -23,9 +24,10 @@ MOE_ROUTE_IDS_GIVEN = 1
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 MOE_FUSED_EXPERT_OUT_BF16 = 1
 MOE_FUSED_SHARED_EXPERT = 2
-MOE_QUANT_FP8_BLOCK128, MOE_QUANT_MXFP8, MOE_QUANT_W4A8 = 0, 1, 2
+MOE_QUANT_FP8_BLOCK128, MOE_QUANT_MXFP8, MOE_QUANT_W4A8, MOE_QUANT_W8A16 = 0, 1, 2, 3
 MOE_WFMT_E4M3, MOE_WFMT_E2M1 = 0, 1
-QUANT_SCHEMES = {"fp8": MOE_QUANT_FP8_BLOCK128, "mxfp8": MOE_QUANT_MXFP8, "w4a8": MOE_QUANT_W4A8}
+QUANT_SCHEMES = {"fp8": MOE_QUANT_FP8_BLOCK128, "mxfp8": MOE_QUANT_MXFP8, "w4a8": MOE_QUANT_W4A8,
+                 "w8a16": MOE_QUANT_W8A16}
 
 EXPORTED = ["moe_route", "moe_route_workspace_size", "moe_quant_act", "moe_quant_weight_blocks",
             "moe_prepack_weights", "moe_grouped_ffn", "moe_ffn_workspace_size", "moe_combine",
@@ -57,7 +59,8 @@ class FfnArgs(ctypes.Structure):
                 ("sorted_assign", ctypes.c_void_p), ("w13", ctypes.c_void_p), ("w13_scale", ctypes.c_void_p),
                 ("w2", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p), ("expert_out", ctypes.c_void_p),
                 ("out_dtype", ctypes.c_int32), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p), ("quant", ctypes.c_int32)]
+                ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p), ("quant", ctypes.c_int32),
+                ("x", ctypes.c_void_p)]
 
 
 class FusedArgs(ctypes.Structure):
@@ -291,6 +294,13 @@ class PackedWeights:
         return PackedWeights(E, H, I2 // 2, moe_prepack_weights(w13q), w13s.contiguous(),
                              moe_prepack_weights(w2q), w2s.contiguous())
 
+    def with_quant(self, quant: int) -> "PackedWeights":
+        """The same packed E4M3 weights and 128 x 128 scales under another scheme that reads
+        them (MOE_QUANT_W8A16)."""
+        if self.quant != MOE_QUANT_FP8_BLOCK128 or quant not in (MOE_QUANT_FP8_BLOCK128, MOE_QUANT_W8A16):
+            raise ValueError("only the 128-block E4M3 weights serve both MOE_QUANT_FP8_BLOCK128 and MOE_QUANT_W8A16")
+        return dataclasses.replace(self, quant=quant)
+
 
 def pack_weights_mx(w13: torch.Tensor, w2: torch.Tensor, quant: int) -> PackedWeights:
     """float32 w13 [E, H, 2I] and w2 [E, I, H] -> packed weights of an MX scheme."""
@@ -303,17 +313,26 @@ def pack_weights_mx(w13: torch.Tensor, w2: torch.Tensor, quant: int) -> PackedWe
     return PackedWeights(E, H, I2 // 2, p13, ps13, p2, ps2, quant)
 
 
-def moe_grouped_ffn(xq: torch.Tensor, xs: torch.Tensor, routing: dict, w: PackedWeights, k: int,
-                    out_dtype=torch.float32) -> torch.Tensor:
-    """Both expert GEMMs; returns expert_out [T*k, H] in expert-sorted slot order."""
-    T, H = xq.shape
+def moe_grouped_ffn(xq: Optional[torch.Tensor], xs: Optional[torch.Tensor], routing: dict, w: PackedWeights, k: int,
+                    out_dtype=torch.float32, x: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Both expert GEMMs; returns expert_out [T*k, H] in expert-sorted slot order.
+    MOE_QUANT_W8A16 weights take the bf16 hidden states x [T, H] instead of xq / xs."""
+    if w.quant == MOE_QUANT_W8A16:
+        if x is None:
+            raise ValueError("MOE_QUANT_W8A16 takes the bf16 hidden states x")
+        T, H = x.shape
+        _need(x, "x", torch.bfloat16, (T, H))
+        dev = x.device
+    else:
+        T, H = xq.shape
+        dev = xq.device
     dt = {torch.float32: MOE_DTYPE_F32, torch.bfloat16: MOE_DTYPE_BF16}[out_dtype]
-    out = torch.empty(T * k, H, dtype=out_dtype, device=xq.device)
+    out = torch.empty(T * k, H, dtype=out_dtype, device=dev)
     nbytes = lib().moe_ffn_workspace_size(T, H, w.I, w.E, k)
-    ws = workspace(max(nbytes, 256), xq.device)
+    ws = workspace(max(nbytes, 256), dev)
     a = FfnArgs(T, k, H, w.I, w.E, _ptr(xq), _ptr(xs), _ptr(routing["expert_counts"]),
                 _ptr(routing["expert_offsets"]), _ptr(routing["sorted_assign"]), _ptr(w.w13), _ptr(w.w13_scale),
-                _ptr(w.w2), _ptr(w.w2_scale), _ptr(out), dt, _ptr(ws), ws.numel(), _stream(), w.quant)
+                _ptr(w.w2), _ptr(w.w2_scale), _ptr(out), dt, _ptr(ws), ws.numel(), _stream(), w.quant, _ptr(x))
     _check(lib().moe_grouped_ffn(ctypes.byref(a)))
     return out
 

@@ -1686,17 +1686,22 @@ FfnPlan ffn_plan(int T, int k, int E, int quant) {
 // workspace: tiles [ntiles_max] int2 | ntiles int | hq [ntiles_max*BM, I] | hs [ntiles_max*BM, I/128]
 //            | (128-row tiles) down-GEMM weight-scale table [E][H/128][I/128] u32
 //            | pairs [npairs_max] int4 | npairs int
-static size_t ffn_ws_plan(const FfnPlan& p, int H, int I, int E) {
+// bytes per element of h in the hq region: E4M3, or bf16 for W8A16
+static size_t h_bytes(int quant) { return quant == kQuantW8A16 ? 2 : 1; }
+
+static size_t ffn_ws_plan(const FfnPlan& p, int H, int I, int E, int quant) {
     const size_t rows = (size_t)p.ntiles_max * p.BM;
     // hs holds one scale per 32 columns of h (the MX schemes; the 128 scheme uses a quarter)
-    size_t n = align256((size_t)p.ntiles_max * 8) + align256(4) + align256(rows * I) + align256(rows * (I / 32));
+    size_t n = align256((size_t)p.ntiles_max * 8) + align256(4) + align256(rows * I * h_bytes(quant)) +
+               align256(rows * (I / 32));
     if (p.BM == 128) n += align256(ffn_rb_scale_table_bytes(H, I, E));
     n += align256((size_t)p.npairs_max * 16) + align256(4);
     return n;
 }
 size_t ffn_workspace_bytes(int T, int H, int I, int E, int k) {
-    return std::max(ffn_ws_plan(ffn_plan(T, k, E, kQuantFp8Block128), H, I, E),
-                    ffn_ws_plan(ffn_plan(T, k, E, kQuantMxfp8), H, I, E));
+    return std::max({ffn_ws_plan(ffn_plan(T, k, E, kQuantFp8Block128), H, I, E, kQuantFp8Block128),
+                     ffn_ws_plan(ffn_plan(T, k, E, kQuantMxfp8), H, I, E, kQuantMxfp8),
+                     ffn_ws_plan(ffn_plan(T, k, E, kQuantW8A16), H, I, E, kQuantW8A16)});
 }
 
 template <int MFW, int NFW1, int NFW2, int WM, int WN, int PF1, int PF2>
@@ -1805,7 +1810,7 @@ FfnWs carve_ffn_ws(const FfnArgs& f, void* ws) {
     r.ntiles = reinterpret_cast<int32_t*>(w);
     w += align256(4);
     r.hq = w;
-    w += align256(rows * f.I);
+    w += align256(rows * f.I * h_bytes(f.quant));
     r.hs = w;
     w += align256(rows * (f.I / 32));
     r.bs = p.BM == 128 ? reinterpret_cast<uint32_t*>(w) : nullptr;
@@ -1824,6 +1829,7 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, void* ws, hipStream_t st, hipEve
         const hipError_t e = launch_tiles(f.counts, f.E, p.BM, w.tiles, w.ntiles, st);
         if (e != hipSuccess) return e;
     }
+    if (f.quant == kQuantW8A16) return launch_ffn_w16(f, p, w, st, mid);
     if (f.quant != kQuantFp8Block128) return launch_ffn_mx(f, p, w, st, mid);
     // output columns per workgroup of the down GEMM = 128, a divisor of H
     if (p.BM == 16) return run_ffn_dec<MOE_DEC_GEMM1, MOE_DEC_GEMM2>(f, p, w, st, mid);

@@ -41,6 +41,10 @@ size_t route_ws_bytes(int T, int E, int k, int with_prelude) {
     return b;
 }
 
+bool valid_quant(int q) {
+    return q == MOE_QUANT_FP8_BLOCK128 || q == MOE_QUANT_MXFP8 || q == MOE_QUANT_W4A8 || q == MOE_QUANT_W8A16;
+}
+
 int check_route_params(const char* op, const moe_route_params* p, int T) {
     if (!p) return fail(MOE_ERR_INVALID, "%s: route params must not be NULL", op);
     const int E = p->num_experts;
@@ -300,14 +304,17 @@ int moe_grouped_ffn(const moe_ffn_args* a) {
     if (!a) return fail(MOE_ERR_INVALID, "%s: args must not be NULL", op);
     int rc = check_ffn_shapes(op, a->T, a->k, a->H, a->I, a->E);
     if (rc) return rc;
-    if (!a->xq || !a->xs || !a->expert_counts || !a->expert_offsets || !a->sorted_assign || !a->expert_out)
+    if (!valid_quant(a->quant)) return fail(MOE_ERR_INVALID, "%s: quant (%d) must be one of MOE_QUANT_*", op, a->quant);
+    const bool w16 = a->quant == MOE_QUANT_W8A16;
+    if (w16 ? !a->x : (!a->xq || !a->xs))
+        return fail(MOE_ERR_INVALID, "%s: %s must not be NULL", op, w16 ? "x" : "xq and xs");
+    if (!a->expert_counts || !a->expert_offsets || !a->sorted_assign || !a->expert_out)
         return fail(MOE_ERR_INVALID, "%s: pointers must not be NULL", op);
     if ((rc = check_weights(op, a->w13, a->w13_scale, a->w2, a->w2_scale))) return rc;
     if (a->out_dtype != MOE_DTYPE_F32 && a->out_dtype != MOE_DTYPE_BF16)
         return fail(MOE_ERR_INVALID, "%s: out_dtype (%d) must be MOE_DTYPE_F32 or MOE_DTYPE_BF16", op, a->out_dtype);
-    if (!aligned(a->xq, 16)) return fail(MOE_ERR_UNSUPPORTED, "%s: xq must be 16-byte aligned", op);
-    if (a->quant != MOE_QUANT_FP8_BLOCK128 && a->quant != MOE_QUANT_MXFP8 && a->quant != MOE_QUANT_W4A8)
-        return fail(MOE_ERR_INVALID, "%s: quant (%d) must be one of MOE_QUANT_*", op, a->quant);
+    if (!aligned(w16 ? (const void*)a->x : (const void*)a->xq, 16))
+        return fail(MOE_ERR_UNSUPPORTED, "%s: %s must be 16-byte aligned", op, w16 ? "x" : "xq");
     const size_t need = moe::ffn_workspace_bytes(a->T, a->H, a->I, a->E, a->k);
     if (!a->workspace || a->workspace_bytes < need)
         return fail(MOE_ERR_WORKSPACE, "%s: workspace too small: need %zu bytes, have %zu", op, need,
@@ -315,7 +322,7 @@ int moe_grouped_ffn(const moe_ffn_args* a) {
     if (!aligned(a->workspace, 256)) return fail(MOE_ERR_INVALID, "%s: workspace must be 256-byte aligned", op);
     moe::FfnArgs f{a->T, a->k, a->H, a->I, a->E, a->xq, a->xs, a->expert_counts, a->expert_offsets,
                    a->sorted_assign, a->w13, a->w13_scale, a->w2, a->w2_scale, a->expert_out,
-                   a->out_dtype == MOE_DTYPE_BF16, a->quant};
+                   a->out_dtype == MOE_DTYPE_BF16, a->quant, w16 ? a->x : nullptr};
     const hipError_t e = moe::launch_grouped_ffn(f, a->workspace, static_cast<hipStream_t>(a->stream));
     if (e != hipSuccess) return hip_fail(op, e);
     return ok();
@@ -369,8 +376,7 @@ int moe_fused(const moe_fused_args* a) {
     if ((rc = check_weights(op, a->w13, a->w13_scale, a->w2, a->w2_scale))) return rc;
     if (a->flags & ~(MOE_FUSED_EXPERT_OUT_BF16 | MOE_FUSED_SHARED_EXPERT))
         return fail(MOE_ERR_INVALID, "%s: unknown flags 0x%x", op, a->flags);
-    if (a->quant != MOE_QUANT_FP8_BLOCK128 && a->quant != MOE_QUANT_MXFP8 && a->quant != MOE_QUANT_W4A8)
-        return fail(MOE_ERR_INVALID, "%s: quant (%d) must be one of MOE_QUANT_*", op, a->quant);
+    if (!valid_quant(a->quant)) return fail(MOE_ERR_INVALID, "%s: quant (%d) must be one of MOE_QUANT_*", op, a->quant);
     if (!aligned(a->hidden_states, 16) || !aligned(a->y, 8))
         return fail(MOE_ERR_UNSUPPORTED, "%s: hidden_states must be 16-byte and y 8-byte aligned", op);
     const size_t need = moe_workspace_size(T, H, I, E, k, a->flags);
@@ -408,9 +414,10 @@ int moe_fused(const moe_fused_args* a) {
         if (e == hipSuccess && ev[i]) e = hipEventRecord(ev[i], st);
     };
     const int bf = (a->flags & MOE_FUSED_EXPERT_OUT_BF16) ? 1 : 0;
-    const bool mx = a->quant != MOE_QUANT_FP8_BLOCK128;
+    const bool mx = a->quant == MOE_QUANT_MXFP8 || a->quant == MOE_QUANT_W4A8;
+    const bool w16 = a->quant == MOE_QUANT_W8A16;   // the bf16 hidden states go in as they are
     moe::FfnArgs f{T, kf, H, I, Ef, xq, xs, counts, offsets, sorted, a->w13, a->w13_scale, a->w2, a->w2_scale, eo, bf,
-                   a->quant};
+                   a->quant, w16 ? a->hidden_states : nullptr};
     const moe::FfnWs fw = moe::carve_ffn_ws(f, fws);
     const moe::FfnPlan plan = moe::ffn_plan(T, kf, Ef, a->quant);
     moe::RouteCfg rcfg = route_cfg(&a->route, T, a->prelude != nullptr);
@@ -428,8 +435,8 @@ int moe_fused(const moe_fused_args* a) {
     if (e == hipSuccess)
         e = moe::launch_route(a->prelude ? pl : a->router_logits, rcfg, a->prelude ? a->prelude->per_expert_scale : nullptr,
                               ids, wts, st,
-                              mx ? moe::QuantOut{nullptr, 0, nullptr, nullptr}
-                                 : moe::QuantOut{a->hidden_states, H, xq, xs});
+                              mx || w16 ? moe::QuantOut{nullptr, 0, nullptr, nullptr}
+                                        : moe::QuantOut{a->hidden_states, H, xq, xs});
     mark(2);
     if (e == hipSuccess)
         e = moe::launch_dispatch(ids, (int)A, Ef, reinterpret_cast<int32_t*>(rws), counts, offsets, sorted, pos, st,

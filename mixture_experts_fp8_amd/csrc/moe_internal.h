@@ -10,6 +10,7 @@ namespace moe {
 constexpr int kQuantFp8Block128 = 0;   // E4M3 per (row, 128), weights per 128 x 128 block
 constexpr int kQuantMxfp8 = 1;         // E4M3 per (row, 32), E4M3 weights per (32 x 1)
 constexpr int kQuantW4A8 = 2;          // E4M3 per (row, 32), E2M1 weights per (32 x 1)
+constexpr int kQuantW8A16 = 3;         // bf16 activations, E4M3 weights per 128 x 128 block
 constexpr int kWfmtE4M3 = 0, kWfmtE2M1 = 1;
 
 // ---- quantisation / layout
@@ -88,6 +89,7 @@ struct FfnArgs {
     void* out;
     int out_bf16;
     int quant;       // kQuant*; for the MX schemes w13s / w2s are the packed MX scales
+    const uint16_t* x = nullptr;   // kQuantW8A16: the bf16 hidden states [T, H] (xq, xs unused)
 };
 struct FfnWs {
     int2* tiles;
@@ -105,6 +107,8 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, void* ws, hipStream_t st, hipEve
                               bool tiles_ready = false, bool pairs_ready = false);
 // MX schemes on 16-row tiles (k_mx.hip)
 hipError_t launch_ffn_mx(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid);
+// W8A16 on 16-row tiles (k_w16.hip); h in bf16 takes the hq region (sized 2 bytes per element)
+hipError_t launch_ffn_w16(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid);
 
 int ffn_super_tile_order(int ntiles_max);
 // persistent down GEMM for 128-row tiles (k_ffn_rb.hip)

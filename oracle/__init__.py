@@ -14,7 +14,10 @@ routing  softmax / sigmoid top-k routing, group-limited selection, the RMSNorm +
          router gate prelude, and the stable expert permutation.
 moe      the expert FFN (gate+up, SwiGLU, re-quantisation, down) and the weighted
          top-k combine, for all tokens or a sample of them.
+mx       the micro-scaled schemes (MXFP8, W4A8): 32-element groups, E2M1.
+w8a16    the weight-only scheme: E4M3 block-scaled weights, bf16 activations, h rounded
+         once to bf16.
 
 Every function is pinned; none is "parity unpinned".
 """
-from . import codec, routing, moe  # noqa: F401
+from . import codec, routing, moe, mx, w8a16  # noqa: F401

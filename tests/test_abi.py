@@ -127,7 +127,11 @@ def test_grouped_ffn_validation():
     assert _ffn(w13=FAKE + 8) == B.MOE_ERR_INVALID
     assert _ffn(out_dtype=7) == B.MOE_ERR_INVALID
     assert _ffn(workspace_bytes=10) == B.MOE_ERR_WORKSPACE
-    assert _ffn(quant=3) == B.MOE_ERR_INVALID and "quant" in M.moe_last_error()
+    assert _ffn(quant=4) == B.MOE_ERR_INVALID and "quant" in M.moe_last_error()
+    # W8A16 takes the bf16 hidden states in x (xq / xs unused), 16-byte aligned
+    assert _ffn(quant=3) == B.MOE_ERR_INVALID and "x must not be NULL" in M.moe_last_error()
+    assert _ffn(quant=3, x=FAKE + 8) == B.MOE_ERR_UNSUPPORTED and "aligned" in M.moe_last_error()
+    assert _ffn(quant=0, xq=None) == B.MOE_ERR_INVALID
     assert M.lib().moe_grouped_ffn(None) == B.MOE_ERR_INVALID
 
 
@@ -156,6 +160,7 @@ def test_fused_validation():
     assert _fused(workspace_bytes=1000) == B.MOE_ERR_WORKSPACE
     assert _fused(hidden_states=FAKE + 4) == B.MOE_ERR_UNSUPPORTED
     assert _fused(quant=-1) == B.MOE_ERR_INVALID
+    assert _fused(quant=4) == B.MOE_ERR_INVALID
     assert M.lib().moe_fused(None) == B.MOE_ERR_INVALID
 
 
