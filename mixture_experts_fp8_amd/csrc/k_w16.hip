@@ -17,7 +17,7 @@
 //
 // Gate+up: workgroup = one tile x one 128-column block of h (8 waves, one gate and one up
 // fragment each); SiLU(g) * u in float32, rounded once to bf16 (RNE) into hb [tile][16][I].
-// Down: workgroup = one tile x 128 output columns (4 waves x 2 fragments); A = the tile's hb
+// Down: workgroup = one tile x 128 output columns (2 waves x 4 fragments); A = the tile's hb
 // rows; out = expert_out rows in sorted-slot order, float32 or bf16.
 #include "moe_common.h"
 #include "moe_internal.h"
@@ -227,17 +227,30 @@ __global__ __launch_bounds__(64 * WN) void k_gemm2_w16(W16G2Args a) {
     }
 }
 
+// down-GEMM shape: fragments per wave, waves, K blocks in flight (NFW * WN = 8)
+#ifndef MOE_W16_GEMM2
+#define MOE_W16_GEMM2 4, 2, 2
+#endif
+#ifndef MOE_W16_PF1
+#define MOE_W16_PF1 2
+#endif
+
+template <int NFW, int WN, int PF>
+static void launch_gemm2_w16(const W16G2Args& g2, int ntiles_max, int H, hipStream_t st) {
+    hipLaunchKernelGGL((k_gemm2_w16<NFW, WN, PF>), dim3(ntiles_max, H / kGroup), dim3(64 * WN), 0, st, g2);
+}
+
 hipError_t launch_ffn_w16(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid) {
     if (f.H / kGroup > kW16MaxKB || f.I / kGroup > kW16MaxKB) return hipErrorInvalidValue;
     uint16_t* hb = reinterpret_cast<uint16_t*>(w.hq);
     W16G1Args g1{f.x, f.T, f.k, f.H, f.I, f.counts, f.offsets, f.sorted_assign, w.tiles, w.ntiles, f.w13p, f.w13s, hb};
-    hipLaunchKernelGGL(k_gemm1_w16<2>, dim3(p.ntiles_max, f.I / kGroup), dim3(512), 0, st, g1);
+    hipLaunchKernelGGL(k_gemm1_w16<MOE_W16_PF1>, dim3(p.ntiles_max, f.I / kGroup), dim3(512), 0, st, g1);
     if (mid) {
         const hipError_t e = hipEventRecord(mid, st);
         if (e != hipSuccess) return e;
     }
     W16G2Args g2{hb, f.H, f.I, f.counts, f.offsets, w.tiles, w.ntiles, f.w2p, f.w2s, f.out, f.out_bf16};
-    hipLaunchKernelGGL((k_gemm2_w16<2, 4, 2>), dim3(p.ntiles_max, f.H / kGroup), dim3(256), 0, st, g2);
+    launch_gemm2_w16<MOE_W16_GEMM2>(g2, p.ntiles_max, f.H, st);
     return hipGetLastError();
 }
 
