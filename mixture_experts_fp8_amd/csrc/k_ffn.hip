@@ -437,46 +437,61 @@ __global__ __launch_bounds__(64 * WN) void k_gemm1_dec(G1Args a) {
     const int ib = blockIdx.y;
     const int2 te = a.tiles[tile];
     const int e = te.x, m0 = te.y;
-    const int nvalid = min(16, a.counts[e] - m0);
-    const int rowbase = a.offsets[e] + m0;
     const int KB = a.H / kGroup;
     const int tid = threadIdx.x, lane = tid & 63, wn = __builtin_amdgcn_readfirstlane(tid >> 6);
     __shared__ float s_amax[WN][16];
     __shared__ __align__(16) uint8_t s_h[16 * 128];
     __shared__ uint8_t s_sg[kMaxKB], s_su[kMaxKB];   // weight-block scales of this column block
 
-    const int tok = a.sorted_assign[rowbase + min(lane & 15, nvalid - 1)] / a.k;
-    const rsrc_t ra = make_rsrc(a.xq, (uint32_t)a.T * a.H);
-    const uint32_t av = (uint32_t)tok * a.H + (lane >> 4) * 32;
-    const uint8_t* sp = a.xs + (int64_t)tok * KB;
     const int NB16 = 2 * a.I / 16, NBS = 2 * a.I / kGroup;
     const rsrc_t rw = make_rsrc(a.w13p + (int64_t)e * NB16 * KB * kFragBytes, (uint32_t)NB16 * KB * kFragBytes);
     const uint8_t* sb = a.w13s + (int64_t)e * KB * NBS;
     const int g16 = ib * 8 + wn * NFW;
     const int u16 = a.I / 16 + g16;
     const uint32_t l16 = lane * 16;
-    for (int i = tid; i < KB; i += 64 * WN) {
-        s_sg[i] = sb[i * NBS + ib];
-        s_su[i] = sb[i * NBS + a.I / kGroup + ib];
+    // request order: the token id (oldest, so waiting for it waits for nothing else), the
+    // block scales, the first PF weight blocks, then the activations that need the id; the
+    // weight stream starts with the workgroup instead of after a round trip for the scales
+    static_assert(64 * WN >= kMaxKB, "one scale pair per thread");
+    const int nvalid = min(16, a.counts[e] - m0);
+    const int rowbase = a.offsets[e] + m0;
+    const int f0 = a.sorted_assign[rowbase + min(lane & 15, nvalid - 1)];   // used after the weight requests
+    const int si = min(tid, KB - 1);   // every thread loads (no branch: the wait for the id stays exact)
+    const uint8_t sg8 = sb[si * NBS + ib], su8 = sb[si * NBS + a.I / kGroup + ib];
+    v8i aq[PF], bq[PF][2 * NFW];
+    int sa[PF];
+    // unconditional (blocks p >= KB are never used; the buffer loads stay inside their
+    // descriptors' ranges or read zero), so no branch blurs the waits
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+#pragma unroll
+        for (int j = 0; j < NFW; ++j) {
+            bq[p][j] = buf_frag(rw, l16, ((g16 + j) * KB + p) * kFragBytes);
+            bq[p][NFW + j] = buf_frag(rw, l16, ((u16 + j) * KB + p) * kFragBytes);
+        }
+    __builtin_amdgcn_sched_barrier(0);
+    const int tok = f0 / a.k;
+    const rsrc_t ra = make_rsrc(a.xq, (uint32_t)a.T * a.H);
+    const uint32_t av = (uint32_t)tok * a.H + (lane >> 4) * 32;
+    const uint8_t* sp = a.xs + (int64_t)tok * KB;
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+        aq[p] = buf_a32(ra, av, p * kGroup);
+        sa[p] = sp[min(p, KB - 1)];
+    }
+    if (tid < KB) {
+        s_sg[tid] = sg8;
+        s_su[tid] = su8;
     }
     __syncthreads();
 
-    v8i aq[PF], bq[PF][2 * NFW];
-    int sa[PF];
     v4f accg[NFW], accu[NFW];
 #pragma unroll
     for (int j = 0; j < NFW; ++j) accg[j] = accu[j] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int p = 0; p < PF; ++p)
-        if (p < KB) {
-            aq[p] = buf_a32(ra, av, p * kGroup);
-            sa[p] = sp[p];
-#pragma unroll
-            for (int j = 0; j < NFW; ++j) {
-                bq[p][j] = buf_frag(rw, l16, ((g16 + j) * KB + p) * kFragBytes);
-                bq[p][NFW + j] = buf_frag(rw, l16, ((u16 + j) * KB + p) * kFragBytes);
-            }
-        }
+    // The refills are unconditional: past the last block their offsets point outside the
+    // descriptors' ranges (bit 31 set), so they read zero without touching memory.  With no
+    // branch around them the loaded registers need no merge copies, and the waits stay at
+    // "the block about to be used" instead of draining the whole pipeline.
     for (int kb0 = 0; kb0 < KB; kb0 += PF) {
 #pragma unroll
         for (int p = 0; p < PF; ++p) {
@@ -489,16 +504,17 @@ __global__ __launch_bounds__(64 * WN) void k_gemm1_dec(G1Args a) {
                     accg[j] = mfma_fp8(aq[p], bq[p][j], accg[j], sa[p], sg);
                     accu[j] = mfma_fp8(aq[p], bq[p][NFW + j], accu[j], sa[p], su);
                 }
-                const int kn = kb + PF;
-                if (kn < KB) {
-                    aq[p] = buf_a32(ra, av, kn * kGroup);
-                    sa[p] = sp[kn];
+            }
+            const int kn = kb + PF;
+            const bool more = kn < KB;
+            const int kc = more ? kn : 0;
+            const uint32_t off_ok = more ? 0u : 0x80000000u;
+            aq[p] = buf_a32(ra, av | off_ok, kc * kGroup);
+            sa[p] = sp[min(kn, KB - 1)];
 #pragma unroll
-                    for (int j = 0; j < NFW; ++j) {
-                        bq[p][j] = buf_frag(rw, l16, ((g16 + j) * KB + kn) * kFragBytes);
-                        bq[p][NFW + j] = buf_frag(rw, l16, ((u16 + j) * KB + kn) * kFragBytes);
-                    }
-                }
+            for (int j = 0; j < NFW; ++j) {
+                bq[p][j] = buf_frag(rw, l16 | off_ok, ((g16 + j) * KB + kc) * kFragBytes);
+                bq[p][NFW + j] = buf_frag(rw, l16 | off_ok, ((u16 + j) * KB + kc) * kFragBytes);
             }
         }
     }
@@ -559,23 +575,29 @@ __global__ __launch_bounds__(64 * WN) void k_gemm2_dec(G2Args a) {
     const int n16 = blockIdx.y * (NFW * WN) + wn * NFW;
     const uint32_t l16 = lane * 16;
     static_assert(NFW * WN == 8, "a workgroup covers one 128-column scale block");
+    static_assert(64 * WN >= kMaxKB, "one scale per thread");
     __shared__ uint8_t s_sb[kMaxKB];
-    for (int i = threadIdx.x; i < KB; i += 64 * WN) s_sb[i] = sb[i * NBS + blockIdx.y];
+    // the block scale, the first PF weight and h blocks, then the row scales, all requested
+    // before the one barrier (the loads are unconditional: no branch blurs the waits; blocks
+    // p >= KB read inside their descriptors' ranges or zero and are never used)
+    const uint8_t sb8 = sb[min((int)threadIdx.x, KB - 1) * NBS + blockIdx.y];
+    int sa[PF];
+#pragma unroll
+    for (int p = 0; p < PF; ++p) sa[p] = sp[min(p, KB - 1)];
+    __builtin_amdgcn_sched_barrier(0);
+    v8i aq[PF], bq[PF][NFW];
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+#pragma unroll
+        for (int j = 0; j < NFW; ++j) bq[p][j] = buf_frag(rw, l16, ((n16 + j) * KB + p) * kFragBytes);
+        aq[p] = buf_frag(ra, l16, p * kFragBytes);
+    }
+    if ((int)threadIdx.x < KB) s_sb[threadIdx.x] = sb8;
     __syncthreads();
 
-    v8i aq[PF], bq[PF][NFW];
-    int sa[PF];
     v4f acc[NFW];
 #pragma unroll
     for (int j = 0; j < NFW; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int p = 0; p < PF; ++p)
-        if (p < KB) {
-            aq[p] = buf_frag(ra, l16, p * kFragBytes);
-            sa[p] = sp[p];
-#pragma unroll
-            for (int j = 0; j < NFW; ++j) bq[p][j] = buf_frag(rw, l16, ((n16 + j) * KB + p) * kFragBytes);
-        }
     for (int kb0 = 0; kb0 < KB; kb0 += PF) {
 #pragma unroll
         for (int p = 0; p < PF; ++p) {
