@@ -1416,7 +1416,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_p2(G1Args a) {
     auto issue = [&](int kb, int s) __attribute__((always_inline)) {
         const uint32_t st = __builtin_amdgcn_readfirstlane(lds_w + s * kP2Stage);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma16_async(ra, st + i * 8192, aoff[i], kb * kGroup);
+        for (int i = 0; i < 4; ++i)   // rows 128.. only for a pair with a second tile (uniform)
+            if (i < 2 || second) dma16_async(ra, st + i * 8192, aoff[i], kb * kGroup);
 #pragma unroll
         for (int i = 0; i < 4; ++i) dma16_async(rw, st + kP2StageA + i * 8192, l16, bsoff[i] + kb * kFragBytes);
     };
@@ -1585,7 +1586,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm2_p2(G2Args a) {
     auto issue = [&](int kb, int s) __attribute__((always_inline)) {
         const uint32_t st = __builtin_amdgcn_readfirstlane(lds_w + s * kP2Stage);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma16_async(ra, st + i * 8192, l16, asoff[i] + kb * kFragBytes);
+        for (int i = 0; i < 4; ++i)   // fragments 8.. only for a pair with a second tile (uniform)
+            if (i < 2 || second) dma16_async(ra, st + i * 8192, l16, asoff[i] + kb * kFragBytes);
 #pragma unroll
         for (int i = 0; i < 4; ++i) dma16_async(rw, st + kP2StageA + i * 8192, l16, bsoff[i] + kb * kFragBytes);
     };
