@@ -230,8 +230,8 @@ def cpu_baseline(wl, sample_tokens: int, quant: str = "fp8", min_seconds: float 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              f"(the expert-parallel exchange across GPUs is not part of it)", file=sys.stderr)
+        print(f"bench.py: the expert step runs on one GPU with every expert local; --gpus {args.gpus} is "
+              f"not supported (there is no expert-parallel exchange across GPUs)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -43,7 +43,7 @@ extern "C" {
 /* ---- return codes ------------------------------------------------------------------ */
 #define MOE_OK               0
 #define MOE_ERR_INVALID      1  /* a null pointer, a non-positive size, an inconsistent shape */
-#define MOE_ERR_UNSUPPORTED  2  /* a valid shape this build does not handle (e.g. H % 128)  */
+#define MOE_ERR_UNSUPPORTED  2  /* a valid shape the library does not handle (e.g. H % 128) */
 #define MOE_ERR_WORKSPACE    3  /* workspace_bytes below what the call needs                */
 #define MOE_ERR_HIP          4  /* a HIP runtime error while enqueuing                      */
 
