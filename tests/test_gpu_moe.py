@@ -266,3 +266,48 @@ def test_fused_shared_expert_dsv3_prefill_sampled():
     print("fused shared sampled", W.describe(wl), flush=True)
     _check_shared(wl, tokens=np.linspace(0, wl.T - 1, 2).astype(np.int64),
                   workers=int(os.environ.get("ORACLE_WORKERS", "8")))
+
+
+# ---- seeded shape sweep: every GEMM path (16-row tiles, persistent and staged 128-row tiles,
+# 256-row pairs), both scorings with and without group limits, k from 1 to 8, expert_out in
+# fp32 and bf16.  The shapes come from a fixed seed, so the list is the same on every run.
+def _sweep_shapes(n=14):
+    r = np.random.default_rng(4242)
+    out = []
+    for i in range(n):
+        regime = i % 4   # 0: decode tiles, 1: 128-row tiles, 2: tile pairs, 3: single K block / odd sizes
+        E = int(r.choice([4, 8, 16, 32, 64]))
+        k = int(r.integers(1, min(8, E) + 1))
+        H = 128 * int(r.integers(1, 13))
+        I = 128 * int(r.integers(1, 9))
+        avg = {0: r.integers(1, 20), 1: r.integers(30, 120), 2: r.integers(140, 400), 3: r.integers(1, 300)}[regime]
+        T = max(1, int(avg * E // k))
+        if regime == 3:
+            H = 128
+        scoring = "sigmoid" if r.random() < 0.4 else "softmax"
+        G = int(r.choice([g for g in (1, 2, 4) if E % g == 0 and E // g >= 2])) if scoring == "sigmoid" else 1
+        kg = int(r.integers(1, G + 1)) if G > 1 else 1
+        if G > 1 and kg * (E // G) < k:
+            kg = G
+        out.append(W.Workload(160 + i, f"sweep{i}", T=T, H=H, I=I, E=E, k=k, scoring=scoring,
+                              renormalize=bool(r.random() < 0.7), group_count=G, k_group=kg,
+                              group_select_mode=int(r.integers(0, 2)), routed_scaling_factor=float(r.choice([1.0, 2.5])),
+                              bias=str(r.choice(["none", "normal1.5", "zipf"]))))
+    return out
+
+
+SWEEP = _sweep_shapes()
+
+
+@pytest.mark.parametrize("i", range(len(SWEEP)))
+def test_fused_shape_sweep(i):
+    wl = SWEEP[i]
+    bf = i % 2 == 1
+    print("fused sweep", i, W.describe(wl), "expert_out bf16" if bf else "", flush=True)
+    y, ids, _, counts, _ = _run_fused(wl, expert_out_bf16=bf)
+    ref, ids_ref, _, margin = _oracle(wl)
+    ok = margin >= 1e-5
+    assert np.array_equal(ids[ok], ids_ref[ok])
+    assert counts.sum() == wl.T * wl.k
+    fro, mx = HN.assert_output_close(HN.bf16_to_f64(y)[ok], ref["y"][ok], wl.name, ref["qmargin_tok"][ok])
+    print(f"  rel fro {fro:.2e} rel max {mx:.2e}", flush=True)
