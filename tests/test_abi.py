@@ -161,6 +161,9 @@ def test_fused_validation():
     assert _fused(hidden_states=FAKE + 4) == B.MOE_ERR_UNSUPPORTED
     assert _fused(quant=-1) == B.MOE_ERR_INVALID
     assert _fused(quant=4) == B.MOE_ERR_INVALID
+    # 1024 routed experts plus the shared one exceed the dispatch's expert limit
+    assert _fused(route=M.route_params(1024, 8), flags=B.MOE_FUSED_SHARED_EXPERT) == B.MOE_ERR_UNSUPPORTED
+    assert "exceeds max" in M.moe_last_error()
     assert M.lib().moe_fused(None) == B.MOE_ERR_INVALID
 
 

@@ -43,6 +43,10 @@ SMALL = {
     "sigmoid_groups": W.Workload(125, "grp", T=96, H=384, I=256, E=32, k=4, scoring="sigmoid", group_count=4,
                                  k_group=2, group_select_mode=1, routed_scaling_factor=2.5),
     "prelude_small": W.Workload(126, "pre", T=9, H=512, I=256, E=16, k=4, prelude=True),
+    # the largest expert count the routing and dispatch kernels take (E = 1024), through the
+    # single-workgroup dispatch (A <= 4096) and the chunked one
+    "E1024_single_wg_dispatch": W.Workload(138, "e1k", T=300, H=128, I=128, E=1024, k=8),
+    "E1024_chunked_dispatch": W.Workload(139, "e1kc", T=1200, H=128, I=256, E=1024, k=8, bias="normal1.5"),
 }
 
 
