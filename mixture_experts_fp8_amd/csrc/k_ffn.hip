@@ -1690,9 +1690,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm2_p2(G2Args a) {
 // The super-tile order pays off once the tiles fill several of its 64-tile windows.
 int ffn_super_tile_order(int ntiles_max) { return ntiles_max >= 512 ? 1 : 0; }
 
-// 256-row items (tile pairs) once experts average at least this many rows.
+// 256-row items (tile pairs) once experts average at least this many rows; the down GEMM
+// takes them from a lower average on (measured: at 64 rows per expert, of which half the
+// experts are empty, 256-row down items beat the persistent 128-row kernel while the gate/up
+// GEMM stays faster on 128-row tiles).
 #ifndef MOE_PAIR_MIN_AVG_ROWS
 #define MOE_PAIR_MIN_AVG_ROWS 128
+#endif
+#ifndef MOE_PAIR_DOWN_MIN_AVG_ROWS
+#define MOE_PAIR_DOWN_MIN_AVG_ROWS 64
 #endif
 
 FfnPlan ffn_plan(int T, int k, int E, int quant) {
@@ -1702,6 +1708,7 @@ FfnPlan ffn_plan(int T, int k, int E, int quant) {
     p.BM = (avg <= MOE_DEC_MAX_AVG_ROWS || quant != kQuantFp8Block128) ? 16 : 128;
     p.ntiles_max = (int)(ceil_div(A, p.BM) + std::min<int64_t>(E, A));
     p.pairs = p.BM == 128 && avg >= MOE_PAIR_MIN_AVG_ROWS;
+    p.pairs_down = p.pairs || (p.BM == 128 && avg >= MOE_PAIR_DOWN_MIN_AVG_ROWS);
     // an expert's pairs number ceil(tiles / 2)
     p.npairs_max = (p.ntiles_max + (int)std::min<int64_t>(E, A)) / 2 + 1;
     return p;
@@ -1762,7 +1769,17 @@ static hipError_t run_ffn_dec(const FfnArgs& f, const FfnPlan& p, const FfnWs& w
     return hipGetLastError();
 }
 
-static hipError_t run_ffn_pf(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid) {
+static hipError_t launch_gemm2_p2(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, int ord, hipStream_t st) {
+    G2Args g2{w.hq, w.hs, f.H, f.I, f.counts, f.offsets, w.tiles, w.ntiles, f.w2p, f.w2s, f.out, f.out_bf16, ord,
+              w.pairs, w.npairs};
+    const int grid2 = ord ? kXcds * ord_ranks(p.npairs_max, f.H / 256)
+                          : (int)(ceil_div((int64_t)(f.H / 256) * p.npairs_max, kXcds) * kXcds);
+    hipLaunchKernelGGL(k_gemm2_p2, dim3(grid2), dim3(512), 0, st, g2);
+    return hipGetLastError();
+}
+
+static hipError_t run_ffn_pf(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid,
+                             bool pairs_ready) {
     G1Args g1{f.xq, f.xs, f.T, f.k, f.H, f.I, f.counts, f.offsets, f.sorted_assign, w.tiles, w.ntiles, f.w13p, f.w13s,
               w.hq, w.hs, ffn_super_tile_order(p.ntiles_max)};
     const int KB1 = f.H / kGroup, pgrid = persistent_grid();
@@ -1783,6 +1800,11 @@ static hipError_t run_ffn_pf(const FfnArgs& f, const FfnPlan& p, const FfnWs& w,
     if (mid) {
         const hipError_t e = hipEventRecord(mid, st);
         if (e != hipSuccess) return e;
+    }
+    if (p.pairs_down) {   // 256-row down items over the same hq / hs tile slots
+        if (!pairs_ready)
+            hipLaunchKernelGGL(k_pairs, dim3(1), dim3(1024), 0, st, f.counts, f.offsets, f.E, w.pairs, w.npairs);
+        return launch_gemm2_p2(f, p, w, ffn_super_tile_order(p.ntiles_max), st);
     }
     G2Args g2{w.hq, w.hs, f.H, f.I, f.counts, f.offsets, w.tiles, w.ntiles, f.w2p, f.w2s, f.out, f.out_bf16,
               ffn_super_tile_order(p.ntiles_max)};
@@ -1816,12 +1838,7 @@ static hipError_t run_ffn_p2(const FfnArgs& f, const FfnPlan& p, const FfnWs& w,
         const hipError_t e = hipEventRecord(mid, st);
         if (e != hipSuccess) return e;
     }
-    G2Args g2{w.hq, w.hs, f.H, f.I, f.counts, f.offsets, w.tiles, w.ntiles, f.w2p, f.w2s, f.out, f.out_bf16, ord,
-              w.pairs, w.npairs};
-    const int grid2 = ord ? kXcds * ord_ranks(p.npairs_max, f.H / 256)
-                          : (int)(ceil_div((int64_t)(f.H / 256) * p.npairs_max, kXcds) * kXcds);
-    hipLaunchKernelGGL(k_gemm2_p2, dim3(grid2), dim3(512), 0, st, g2);
-    return hipGetLastError();
+    return launch_gemm2_p2(f, p, w, ord, st);
 }
 
 FfnWs carve_ffn_ws(const FfnArgs& f, void* ws) {
@@ -1863,7 +1880,7 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, void* ws, hipStream_t st, hipEve
 #ifndef MOE_NO_PAIRS
         if (p.pairs) return run_ffn_p2(f, p, w, st, mid, pairs_ready);
 #endif
-        return run_ffn_pf(f, p, w, st, mid);
+        return run_ffn_pf(f, p, w, st, mid, pairs_ready);
     }
     return run_ffn<4, 4, 4, 2, 2, 2, 2>(f, p, w, st, mid);
 }

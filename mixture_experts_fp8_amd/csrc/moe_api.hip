@@ -440,9 +440,9 @@ int moe_fused(const moe_fused_args* a) {
     mark(2);
     if (e == hipSuccess)
         e = moe::launch_dispatch(ids, (int)A, Ef, reinterpret_cast<int32_t*>(rws), counts, offsets, sorted, pos, st,
-                                 plan.BM, fw.tiles, fw.ntiles, plan.pairs ? fw.pairs : nullptr, fw.npairs);
+                                 plan.BM, fw.tiles, fw.ntiles, plan.pairs_down ? fw.pairs : nullptr, fw.npairs);
     mark(3);
-    if (e == hipSuccess) e = moe::launch_grouped_ffn(f, fws, st, ev[4], true, plan.pairs != 0);
+    if (e == hipSuccess) e = moe::launch_grouped_ffn(f, fws, st, ev[4], true, plan.pairs_down != 0);
     mark(5);
     if (e == hipSuccess) e = moe::launch_combine(eo, bf, pos, wts, T, kf, H, a->y, st);
     mark(6);

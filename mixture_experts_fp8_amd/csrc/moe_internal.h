@@ -69,6 +69,8 @@ struct FfnPlan {
     int BM;           // rows per tile
     int ntiles_max;   // grid bound on tiles
     int pairs;        // 1: the 128-row tiles run as 256-row items (pairs of tiles)
+    int pairs_down;   // 1: the down GEMM runs on pairs (always with pairs; also below their
+                      //    threshold, where gate/up keeps 128-row tiles)
     int npairs_max;   // grid bound on pairs
 };
 FfnPlan ffn_plan(int T, int k, int E, int quant = kQuantFp8Block128);
