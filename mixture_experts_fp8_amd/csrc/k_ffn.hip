@@ -1689,6 +1689,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm2_p2(G2Args a) {
 
 // The super-tile order pays off once the tiles fill several of its 64-tile windows.
 int ffn_super_tile_order(int ntiles_max) { return ntiles_max >= 512 ? 1 : 0; }
+// The 256-row down GEMM takes the super-tile order from twice as many tiles on: on the
+// DeepSeek-V3-shaped prefill (512 tiles, one pair per expert, so no two pairs share weight
+// columns) the column-block order measured 3% faster for it, while its gate/up GEMM and the
+// Zipf prefill's (1152 tiles, many pairs per expert) keep gaining from super-tiles.
+static int ffn_super_tile_order_down(int ntiles_max) { return ntiles_max >= 1024 ? 1 : 0; }
 
 // 256-row items (tile pairs) once experts average at least this many rows; the down GEMM
 // takes them from a lower average on (measured: at 64 rows per expert, of which half the
@@ -1804,7 +1809,7 @@ static hipError_t run_ffn_pf(const FfnArgs& f, const FfnPlan& p, const FfnWs& w,
     if (p.pairs_down) {   // 256-row down items over the same hq / hs tile slots
         if (!pairs_ready)
             hipLaunchKernelGGL(k_pairs, dim3(1), dim3(1024), 0, st, f.counts, f.offsets, f.E, w.pairs, w.npairs);
-        return launch_gemm2_p2(f, p, w, ffn_super_tile_order(p.ntiles_max), st);
+        return launch_gemm2_p2(f, p, w, ffn_super_tile_order_down(p.ntiles_max), st);
     }
     G2Args g2{w.hq, w.hs, f.H, f.I, f.counts, f.offsets, w.tiles, w.ntiles, f.w2p, f.w2s, f.out, f.out_bf16,
               ffn_super_tile_order(p.ntiles_max)};
@@ -1838,7 +1843,7 @@ static hipError_t run_ffn_p2(const FfnArgs& f, const FfnPlan& p, const FfnWs& w,
         const hipError_t e = hipEventRecord(mid, st);
         if (e != hipSuccess) return e;
     }
-    return launch_gemm2_p2(f, p, w, ord, st);
+    return launch_gemm2_p2(f, p, w, ffn_super_tile_order_down(p.ntiles_max), st);
 }
 
 FfnWs carve_ffn_ws(const FfnArgs& f, void* ws) {
