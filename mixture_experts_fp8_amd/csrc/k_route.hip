@@ -19,9 +19,11 @@ typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
 // per-token factor r_t applied once to the finished dot product.
 // Workgroup (expert e, 8 tokens), 4 waves splitting H into interleaved 256-wide steps:
 // lane l owns 4 consecutive h per step, loaded as one 16-byte W_r / norm load and one 8-byte
-// load per token; each token's sum of squares comes from the same loaded values.  Partial
-// sums meet in LDS.
+// load per token; each token's sum of squares comes from the same loaded values.  The loads
+// of kPreB steps are issued before any of their sums (one memory round trip per kPreB steps;
+// the sums still run in h order).  Partial sums meet in LDS.
 constexpr int kPreT = 8;
+constexpr int kPreB = 4;
 
 __global__ __launch_bounds__(256) void k_gate_prelude(const uint16_t* __restrict__ x, int T, int H, int E,
                                                       const float* __restrict__ norm_w,
@@ -36,18 +38,34 @@ __global__ __launch_bounds__(256) void k_gate_prelude(const uint16_t* __restrict
     float d[kPreT], ss[kPreT];
 #pragma unroll
     for (int t = 0; t < kPreT; ++t) d[t] = ss[t] = 0.f;
-    for (int h = (wv * 64 + lane) * 4; h < H; h += 1024) {
-        const float4 w4 = *reinterpret_cast<const float4*>(wr + h);
-        const float4 n4 = *reinterpret_cast<const float4*>(norm_w + h);
-        const float wn0 = w4.x * n4.x, wn1 = w4.y * n4.y, wn2 = w4.z * n4.z, wn3 = w4.w * n4.w;
+    for (int hb = (wv * 64 + lane) * 4; hb < H; hb += 1024 * kPreB) {
+        float4 w4[kPreB], n4[kPreB];
+        uint2 u[kPreB][kPreT];
 #pragma unroll
-        for (int t = 0; t < kPreT; ++t) {
-            if (t < nt) {
-                const uint2 u = *reinterpret_cast<const uint2*>(x + (int64_t)(t0 + t) * H + h);
-                const float x0 = bf16_to_f32(u.x & 0xFFFFu), x1 = bf16_to_f32(u.x >> 16);
-                const float x2 = bf16_to_f32(u.y & 0xFFFFu), x3 = bf16_to_f32(u.y >> 16);
-                d[t] = fmaf(x0, wn0, fmaf(x1, wn1, fmaf(x2, wn2, fmaf(x3, wn3, d[t]))));
-                ss[t] = fmaf(x0, x0, fmaf(x1, x1, fmaf(x2, x2, fmaf(x3, x3, ss[t]))));
+        for (int i = 0; i < kPreB; ++i) {
+            const int h = hb + 1024 * i;
+            if (h < H) {
+                w4[i] = *reinterpret_cast<const float4*>(wr + h);
+                n4[i] = *reinterpret_cast<const float4*>(norm_w + h);
+#pragma unroll
+                for (int t = 0; t < kPreT; ++t)
+                    if (t < nt) u[i][t] = *reinterpret_cast<const uint2*>(x + (int64_t)(t0 + t) * H + h);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kPreB; ++i) {
+            if (hb + 1024 * i < H) {
+                const float wn0 = w4[i].x * n4[i].x, wn1 = w4[i].y * n4[i].y;
+                const float wn2 = w4[i].z * n4[i].z, wn3 = w4[i].w * n4[i].w;
+#pragma unroll
+                for (int t = 0; t < kPreT; ++t) {
+                    if (t < nt) {
+                        const float x0 = bf16_to_f32(u[i][t].x & 0xFFFFu), x1 = bf16_to_f32(u[i][t].x >> 16);
+                        const float x2 = bf16_to_f32(u[i][t].y & 0xFFFFu), x3 = bf16_to_f32(u[i][t].y >> 16);
+                        d[t] = fmaf(x0, wn0, fmaf(x1, wn1, fmaf(x2, wn2, fmaf(x3, wn3, d[t]))));
+                        ss[t] = fmaf(x0, x0, fmaf(x1, x1, fmaf(x2, x2, fmaf(x3, x3, ss[t]))));
+                    }
+                }
             }
         }
     }
@@ -77,10 +95,7 @@ hipError_t launch_gate_prelude(const uint16_t* x, int T, int H, int E, const flo
 }
 
 // ----------------------------------------------------------------------------------------
-// Top-k routing: one wave64 per token, 4 tokens per workgroup.  Lane l holds experts
-// l, l+64, ... (EPL per lane).  Selection runs on 64-bit keys
-// (order-preserving float bits << 32 | ~id): the wave maximum is the largest value with
-// the lowest id, which is exactly "descending score, ties to the lower id".
+// Top-k routing: order-preserving keys and the wave maximum over them.
 
 __device__ __forceinline__ uint32_t ordered_bits(float f) {
     uint32_t u = (f == 0.0f) ? 0u : __float_as_uint(f);   // +0 and -0 compare equal
@@ -109,29 +124,64 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     return r;
 }
 
+// The token row's activation quantisation (per 128 columns, 16 lanes per group): loads of
+// the 32 groups from g0 on, then their E4M3 codes and UE8M0 scales.  The row is read once:
+// non-temporal.
+__device__ __forceinline__ void xrow_load(const QuantOut& qo, int t, int g0, int lane, uint4 (&v)[8]) {
+    const int ngc = qo.H / kGroup;
+    const uint16_t* xr = qo.x + (int64_t)t * qo.H;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int g = g0 + (lane >> 4) + 4 * i;
+        if (g < ngc) {
+            const v4u_t u = __builtin_nontemporal_load(reinterpret_cast<const v4u_t*>(xr + g * kGroup + (lane & 15) * 8));
+            v[i] = make_uint4(u[0], u[1], u[2], u[3]);
+        }
+    }
+}
+__device__ __forceinline__ void xrow_quant(const QuantOut& qo, int t, int g0, int lane, const uint4 (&v)[8]) {
+    const int ngc = qo.H / kGroup;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int g = g0 + (lane >> 4) + 4 * i;
+        if (g < ngc)
+            quant_group16_v(v[i], qo.xq + (int64_t)t * qo.H + g * kGroup, qo.xs + (int64_t)t * ngc + g, lane & 15);
+    }
+}
+
+// One token's routing on one wave64 (every wave of the workgroup calls it once: it holds
+// workgroup barriers).  Lane l holds experts l, l+64, ... (EPL per lane).  Selection runs on
+// 64-bit keys (order-preserving float bits << 32 | ~id): the wave maximum is the largest
+// value with the lowest id, which is exactly "descending score, ties to the lower id".
+// s_wave is the wave's LDS: E scores, then k selected ids, logits and per-expert scales.
+// The logits, the per-expert scales and the activation row's first 32 groups are requested
+// together at the start, so the row's loads are in flight during the selection.
 template <int EPL>
-__global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, RouteCfg c,
-                                               const float* __restrict__ pe_scale, int32_t* __restrict__ ids,
-                                               float* __restrict__ wts, QuantOut qo) {
-    extern __shared__ unsigned char s_raw[];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int t = blockIdx.x * 4 + wv;
+__device__ __forceinline__ void route_token(const float* __restrict__ logits, const RouteCfg& c,
+                                            const float* __restrict__ pe_scale, int32_t* __restrict__ ids,
+                                            float* __restrict__ wts, const QuantOut& qo, int t, float* s_wave) {
+    const int lane = threadIdx.x & 63;
     const int E = c.E, k = c.k;
-    // per wave: scores [E] float, selected ids [k] int, selected logits [k] float
-    float* s_score = reinterpret_cast<float*>(s_raw) + (size_t)wv * (E + 2 * k);
+    float* s_score = s_wave;
     int* s_sel = reinterpret_cast<int*>(s_score + E);
     float* s_sell = reinterpret_cast<float*>(s_sel + k);
+    float* s_selp = s_sell + k;
     const bool active = t < c.T;
 
-    float lg[EPL], sc[EPL];
+    float lg[EPL], sc[EPL], pe[EPL];
     uint32_t avail = 0;   // bit i: expert lane + 64 i exists and is still selectable
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = lane + 64 * i;
         const bool ok = active && e < E;
         lg[i] = ok ? logits[(int64_t)t * E + e] : -INFINITY;
+        pe[i] = (ok && pe_scale) ? pe_scale[e] : 1.0f;
         if (ok) avail |= 1u << i;
     }
+    const bool quant = active && qo.x != nullptr;
+    uint4 xv[8];
+    if (quant) xrow_load(qo, t, 0, lane, xv);
+
     // scores
     float mx = -INFINITY;
 #pragma unroll
@@ -205,7 +255,10 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
             s_sel[j] = id;
 #pragma unroll
             for (int i = 0; i < EPL; ++i)
-                if (i == (id >> 6)) s_sell[j] = lg[i];
+                if (i == (id >> 6)) {
+                    s_sell[j] = lg[i];
+                    s_selp[j] = pe[i];
+                }
         }
     }
     __syncthreads();
@@ -235,7 +288,7 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
             else if (c.renormalize || c.prelude) v = expf(l - lsel0);
             else v = expf(l - mx) / sum;
             if (normalise) v = v / denom;
-            if (c.prelude && pe_scale) v *= pe_scale[id];
+            if (c.prelude && pe_scale) v *= s_selp[j];
             v *= c.rsf;
             ids[(int64_t)t * c.ld + j] = id;
             wts[(int64_t)t * c.ld + j] = v;
@@ -244,36 +297,30 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
             ids[(int64_t)t * c.ld + k] = c.shared_id;
             wts[(int64_t)t * c.ld + k] = 1.0f;
         }
-        // the token's activation row, quantised per 128 columns (16 lanes per group)
-        if (qo.x) {
+        if (quant) {
             const int ngc = qo.H / kGroup;
-            const uint16_t* xr = qo.x + (int64_t)t * qo.H;
             for (int g0 = 0; g0 < ngc; g0 += 32) {
-                uint4 v[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int g = g0 + (lane >> 4) + 4 * i;
-                    if (g < ngc) {   // the row is read once: non-temporal
-                        const v4u_t u = __builtin_nontemporal_load(reinterpret_cast<const v4u_t*>(xr + g * kGroup + (lane & 15) * 8));
-                        v[i] = make_uint4(u[0], u[1], u[2], u[3]);
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int g = g0 + (lane >> 4) + 4 * i;
-                    if (g < ngc)
-                        quant_group16_v(v[i], qo.xq + (int64_t)t * qo.H + g * kGroup, qo.xs + (int64_t)t * ngc + g,
-                                        lane & 15);
-                }
+                if (g0 > 0) xrow_load(qo, t, g0, lane, xv);
+                xrow_quant(qo, t, g0, lane, xv);
             }
         }
     }
 }
 
+// Top-k routing over many workgroups: one wave per token, 4 tokens per workgroup.
+template <int EPL>
+__global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, RouteCfg c,
+                                               const float* __restrict__ pe_scale, int32_t* __restrict__ ids,
+                                               float* __restrict__ wts, QuantOut qo) {
+    extern __shared__ float s_route[];
+    const int wv = threadIdx.x >> 6;
+    route_token<EPL>(logits, c, pe_scale, ids, wts, qo, blockIdx.x * 4 + wv, s_route + (size_t)wv * (c.E + 3 * c.k));
+}
+
 hipError_t launch_route(const float* logits, const RouteCfg& c, const float* pe_scale, int32_t* ids,
                         float* weights, hipStream_t st, QuantOut qo) {
     const dim3 grid((unsigned)ceil_div(c.T, 4)), block(256);
-    const size_t lds = (size_t)4 * (c.E + 2 * c.k) * 4;
+    const size_t lds = (size_t)4 * (c.E + 3 * c.k) * 4;
     const int epl = (int)ceil_div(c.E, 64);
     if (epl <= 1) hipLaunchKernelGGL(k_route<1>, grid, block, lds, st, logits, c, pe_scale, ids, weights, qo);
     else if (epl <= 2) hipLaunchKernelGGL(k_route<2>, grid, block, lds, st, logits, c, pe_scale, ids, weights, qo);
@@ -473,10 +520,17 @@ __global__ __launch_bounds__(64 * kOneWaves) void k_dispatch_one(const int32_t* 
     __syncthreads();
     const int seg = (int)ceil_div(A, kOneWaves);
     const int b0 = wv * seg, b1 = min(A, b0 + seg);
-    for (int f = b0 + lane; f < b1; f += 64) {
-        const int e = ids[f];
-        if ((unsigned)e < (unsigned)E) atomicAdd(&s_w[wv][e], 1);
+    // the lane's ids stay in registers for the second pass (seg <= 64 * kOneRounds)
+    constexpr int kOneRounds = kDispatchOneMaxA / kOneWaves / 64;
+    int ev[kOneRounds];
+#pragma unroll
+    for (int r = 0; r < kOneRounds; ++r) {
+        const int f = b0 + 64 * r + lane;
+        ev[r] = f < b1 ? ids[f] : -1;
     }
+#pragma unroll
+    for (int r = 0; r < kOneRounds; ++r)
+        if ((unsigned)ev[r] < (unsigned)E) atomicAdd(&s_w[wv][ev[r]], 1);
     __syncthreads();
     // per expert: total count, then the exclusive scan over experts and the per-wave bases
     int tot[2] = {0, 0};
@@ -525,9 +579,12 @@ __global__ __launch_bounds__(64 * kOneWaves) void k_dispatch_one(const int32_t* 
     }
     __syncthreads();
     const uint64_t lt = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
-    for (int f0 = b0; f0 < b1; f0 += 64) {
+#pragma unroll
+    for (int r = 0; r < kOneRounds; ++r) {
+        const int f0 = b0 + 64 * r;
+        if (f0 >= b1) break;   // wave-uniform
         const int f = f0 + lane;
-        int e = f < b1 ? ids[f] : 0;
+        int e = f < b1 ? ev[r] : 0;
         const bool valid = f < b1 && (unsigned)e < (unsigned)E;
         if (!valid) e = 0;
         if (f < b1 && !valid) assign_pos[f] = -1;

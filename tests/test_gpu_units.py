@@ -110,6 +110,13 @@ ROUTE_CASES = {
     "E1024_k1": W.CONFIGS[1].replace(cfg=106, T=70, E=1024, k=1),
     "k_equals_E": W.CONFIGS[1].replace(cfg=107, T=33, E=8, k=8),
     "T1": W.CONFIGS[1].replace(cfg=108, T=1, E=5, k=3),
+    # group-limited sigmoid routing on 256 experts for a decode-sized batch, 4 experts per
+    # lane without renormalisation, and an odd batch past a multiple of the 4 tokens per
+    # workgroup
+    "small_dsv3_like": W.CONFIGS[4].replace(cfg=109, T=48),
+    "small_E200_no_renorm": W.CONFIGS[1].replace(cfg=110, T=64, E=200, k=6, renormalize=False,
+                                                 routed_scaling_factor=1.3),
+    "T65_odd_batch": W.CONFIGS[2].replace(cfg=111, T=65, prelude=False),
 }
 
 
@@ -138,6 +145,17 @@ def test_route_and_dispatch(name):
     got = M.moe_route(HN.device_params(wl), wl.T, router_logits=logits.to(DEV))
     n_amb = _check_routing(wl, got, ids_ref, w_ref, margin, tau=1e-6)
     assert n_amb == 0
+
+
+def test_route_rows_independent_of_batch():
+    # a token's ids and weights do not depend on the batch around it: the first 64 tokens of
+    # a 65-token batch against the same 64 tokens alone, bit for bit
+    wl = W.CONFIGS[4].replace(cfg=112, T=65)
+    logits = W.router_logits(wl).to(DEV)
+    big = M.moe_route(HN.device_params(wl), 65, router_logits=logits)
+    small = M.moe_route(HN.device_params(wl), 64, router_logits=logits[:64].contiguous())
+    assert torch.equal(big["topk_ids"][:64], small["topk_ids"])
+    assert torch.equal(big["topk_weights"][:64], small["topk_weights"])
 
 
 def test_route_gate_prelude():
