@@ -304,7 +304,14 @@ int moe_combine(const void* expert_out, int32_t dtype, const int32_t* assign_pos
  *   flags             MOE_FUSED_EXPERT_OUT_BF16 | MOE_FUSED_SHARED_EXPERT.
  *   workspace         >= moe_workspace_size(T, H, I, E, k, flags) bytes (covers the prelude).
  *   stage_events      NULL, or MOE_STAGES + 1 hipEvent_t (created by the caller; NULL entries
- *                     are skipped) recorded on `stream` before the first and after every stage. */
+ *                     are skipped) recorded on `stream` before the first and after every stage.
+ *   act_q, act_scales optional outputs (each NULL, or 16-byte aligned device memory that the
+ *                     call writes and then reads): the activations quantised for the gate+up
+ *                     GEMM go there instead of into the workspace.  act_q [T, H] E4M3FN codes
+ *                     (all three activation-quantising schemes use E4M3); act_scales UE8M0,
+ *                     [T, H/128] for MOE_QUANT_FP8, [T, H/32] for MOE_QUANT_MXFP8 and
+ *                     MOE_QUANT_W4A8.  MOE_QUANT_W8A16 quantises no activations: both must be
+ *                     NULL then. */
 typedef struct moe_fused_args {
     int32_t T, H, I;
     moe_route_params route;
@@ -325,6 +332,8 @@ typedef struct moe_fused_args {
     void*          stream;
     void* const*   stage_events;
     int32_t        quant;       /* MOE_QUANT_*: packed weights and scales of that scheme */
+    uint8_t*       act_q;       /* optional: the step's quantised activations go here */
+    uint8_t*       act_scales;  /* optional: their UE8M0 scales */
 } moe_fused_args;
 
 int moe_fused(const moe_fused_args* a);

@@ -71,7 +71,8 @@ class FusedArgs(ctypes.Structure):
                 ("y", ctypes.c_void_p), ("topk_ids", ctypes.c_void_p), ("topk_weights", ctypes.c_void_p),
                 ("expert_counts", ctypes.c_void_p), ("flags", ctypes.c_int32), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p),
-                ("stage_events", ctypes.POINTER(ctypes.c_void_p)), ("quant", ctypes.c_int32)]
+                ("stage_events", ctypes.POINTER(ctypes.c_void_p)), ("quant", ctypes.c_int32),
+                ("act_q", ctypes.c_void_p), ("act_scales", ctypes.c_void_p)]
 
 
 MOE_STAGES = 6
@@ -360,7 +361,8 @@ class MoeFused:
                  router_logits: Optional[torch.Tensor] = None, prelude: Optional[Prelude] = None,
                  expert_out_bf16: bool = False, y: Optional[torch.Tensor] = None,
                  topk_ids: Optional[torch.Tensor] = None, topk_weights: Optional[torch.Tensor] = None,
-                 expert_counts: Optional[torch.Tensor] = None, shared_expert: bool = False):
+                 expert_counts: Optional[torch.Tensor] = None, shared_expert: bool = False,
+                 act_q: Optional[torch.Tensor] = None, act_scales: Optional[torch.Tensor] = None):
         H = hidden_states.shape[1]
         _need(hidden_states, "hidden_states", torch.bfloat16, (T, H))
         if router_logits is not None:
@@ -373,13 +375,18 @@ class MoeFused:
         self.y = y if y is not None else torch.empty(T, H, dtype=torch.bfloat16, device=hidden_states.device)
         nbytes = lib().moe_workspace_size(T, H, w.I, params.num_experts, params.top_k, self.flags)
         self.ws = workspace(max(nbytes, 256), hidden_states.device)
-        self._keep = (hidden_states, router_logits, prelude, w, topk_ids, topk_weights, expert_counts)
+        if act_q is not None:
+            _need(act_q, "act_q", torch.uint8, (T, H))
+        if act_scales is not None:
+            _need(act_scales, "act_scales", torch.uint8, (T, H // (128 if w.quant == MOE_QUANT_FP8_BLOCK128 else 32)))
+        self._keep = (hidden_states, router_logits, prelude, w, topk_ids, topk_weights, expert_counts, act_q,
+                      act_scales)
         self._pre = prelude.c() if prelude is not None else None
         self.args = FusedArgs(T, H, w.I, params, _ptr(hidden_states), _ptr(router_logits),
                               ctypes.pointer(self._pre) if self._pre is not None else None,
                               _ptr(w.w13), _ptr(w.w13_scale), _ptr(w.w2), _ptr(w.w2_scale), _ptr(self.y),
                               _ptr(topk_ids), _ptr(topk_weights), _ptr(expert_counts), self.flags, _ptr(self.ws),
-                              self.ws.numel(), None, None, w.quant)
+                              self.ws.numel(), None, None, w.quant, _ptr(act_q), _ptr(act_scales))
 
     def __call__(self, stream: Optional[int] = None, stage_events=None) -> torch.Tensor:
         """stage_events: None or a ctypes array of MOE_STAGES + 1 hipEvent_t handles that the
@@ -398,10 +405,13 @@ class MoeFused:
 
 def moe_fused(params: RouteParams, hidden_states: torch.Tensor, w: PackedWeights,
               router_logits: Optional[torch.Tensor] = None, prelude: Optional[Prelude] = None,
-              expert_out_bf16: bool = False, return_routing: bool = False, shared_expert: bool = False):
+              expert_out_bf16: bool = False, return_routing: bool = False, shared_expert: bool = False,
+              act_q: Optional[torch.Tensor] = None, act_scales: Optional[torch.Tensor] = None):
     """The whole step in one C call.  Returns y bf16 [T, H] (and ids, weights, counts).
     shared_expert: w holds num_experts + 1 experts, the last one run on every token and added
-    with weight 1 (ids / weights then have top_k + 1 columns, counts num_experts + 1 entries)."""
+    with weight 1 (ids / weights then have top_k + 1 columns, counts num_experts + 1 entries).
+    act_q, act_scales: optional uint8 tensors ([T, H] and [T, H/128], or [T, H/32] for the
+    micro-scaled schemes) that receive the step's quantised activations."""
     T = hidden_states.shape[0]
     dev = hidden_states.device
     ids = weights = counts = None
@@ -411,6 +421,6 @@ def moe_fused(params: RouteParams, hidden_states: torch.Tensor, w: PackedWeights
         weights = torch.empty(T, params.top_k + sh, dtype=torch.float32, device=dev)
         counts = torch.empty(params.num_experts + sh, dtype=torch.int32, device=dev)
     f = MoeFused(params, T, w, hidden_states, router_logits, prelude, expert_out_bf16, None, ids, weights, counts,
-                 shared_expert)
+                 shared_expert, act_q, act_scales)
     y = f()
     return (y, ids, weights, counts) if return_routing else y

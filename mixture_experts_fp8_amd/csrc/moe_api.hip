@@ -384,6 +384,11 @@ int moe_fused(const moe_fused_args* a) {
         return fail(MOE_ERR_WORKSPACE, "%s: workspace too small: need %zu bytes, have %zu", op, need,
                     a->workspace ? a->workspace_bytes : (size_t)0);
     if (!aligned(a->workspace, 256)) return fail(MOE_ERR_INVALID, "%s: workspace must be 256-byte aligned", op);
+    if ((a->act_q && !aligned(a->act_q, 16)) || (a->act_scales && !aligned(a->act_scales, 16)))
+        return fail(MOE_ERR_INVALID, "%s: act_q and act_scales must be 16-byte aligned", op);
+    if (a->quant == MOE_QUANT_W8A16 && (a->act_q || a->act_scales))
+        return fail(MOE_ERR_INVALID, "%s: MOE_QUANT_W8A16 quantises no activations: act_q and act_scales must be NULL",
+                    op);
 
     const size_t A = (size_t)T * kf;
     uint8_t* w = static_cast<uint8_t*>(a->workspace);
@@ -398,6 +403,8 @@ int moe_fused(const moe_fused_args* a) {
     w += route_ws_bytes(T, Ef, kf, 1);
     uint8_t* xq = take((size_t)T * H);
     uint8_t* xs = take((size_t)T * (H / 32));
+    if (a->act_q) xq = a->act_q;
+    if (a->act_scales) xs = a->act_scales;
     uint8_t* fws = w;
     w += moe::ffn_workspace_bytes(T, H, I, Ef, kf);
     void* eo = take(A * H * ((a->flags & MOE_FUSED_EXPERT_OUT_BF16) ? 2 : 4));

@@ -161,6 +161,11 @@ def test_fused_validation():
     assert _fused(hidden_states=FAKE + 4) == B.MOE_ERR_UNSUPPORTED
     assert _fused(quant=-1) == B.MOE_ERR_INVALID
     assert _fused(quant=4) == B.MOE_ERR_INVALID
+    # the optional quantised-activation outputs: 16-byte aligned, and none for W8A16
+    assert _fused(act_q=FAKE + 8) == B.MOE_ERR_INVALID
+    assert _fused(act_scales=FAKE + 4) == B.MOE_ERR_INVALID
+    assert _fused(quant=B.MOE_QUANT_W8A16, act_q=FAKE) == B.MOE_ERR_INVALID
+    assert "W8A16" in M.moe_last_error()
     # 1024 routed experts plus the shared one exceed the dispatch's expert limit
     assert _fused(route=M.route_params(1024, 8), flags=B.MOE_FUSED_SHARED_EXPERT) == B.MOE_ERR_UNSUPPORTED
     assert "exceeds max" in M.moe_last_error()

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 from gen import workloads as W
-from oracle import moe as omoe
+from oracle import codec, moe as omoe
 
 import harness as HN
 
@@ -124,6 +124,27 @@ def test_separate_entry_points_match_fused(name):
     got = eo.cpu().numpy().astype(np.float64)[pos]          # back to flat (t, j) order
     okf = np.repeat(ok, wl.k)
     HN.assert_output_close(got[okf], ref["o"][okf], "expert_out", ref["qmargin"][okf])
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3])
+def test_fused_activation_quant_bit_exact(cfg):
+    # the fused call quantises the activations inside its routing kernel (one wave per token);
+    # its E4M3 codes and UE8M0 scales must be the oracle's per-(row, 128) quantisation exactly,
+    # and taking them in caller buffers must not change y
+    wl = W.CONFIGS[cfg]
+    print("fused act quant", W.describe(wl), flush=True)
+    x, logits, pre = HN.device_inputs(wl)
+    w = HN.device_weights(wl)
+    p = HN.device_params(wl)
+    xq = torch.empty(wl.T, wl.H, dtype=torch.uint8, device=DEV)
+    xs = torch.empty(wl.T, wl.H // 128, dtype=torch.uint8, device=DEV)
+    y = M.moe_fused(p, x, w, router_logits=logits, prelude=pre, act_q=xq, act_scales=xs)
+    y0 = M.moe_fused(p, x, w, router_logits=logits, prelude=pre)
+    torch.cuda.synchronize()
+    q_ref, s_ref = codec.quant_rows_128(W.bf16_to_f64(W.hidden_bf16(wl)))
+    assert np.array_equal(xs.cpu().numpy(), s_ref)
+    assert np.array_equal(xq.cpu().numpy(), q_ref)
+    assert torch.equal(y, y0)
 
 
 def test_golden_hand_ffn_through_device():

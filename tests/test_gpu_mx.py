@@ -181,3 +181,24 @@ def test_mx_fused_shared_expert(scheme):
     ref = omx.forward(xf, ids_all, w_all, ex)
     fro, mxe = HN.assert_output_close(HN.bf16_to_f64(y)[ok], ref["y"][ok], f"{scheme} shared", ref["qmargin_tok"][ok])
     print(f"  rel fro {fro:.2e} rel max {mxe:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("scheme", list(SCHEMES))
+def test_mx_fused_activation_quant_bit_exact(scheme):
+    # the fused call's 32-group activation quantisation, taken in caller buffers: the
+    # oracle's E4M3 codes and UE8M0 scales exactly, and y unchanged by taking them
+    quant, _ = SCHEMES[scheme]
+    wl = W.CONFIGS[2]
+    print("mx fused act quant", scheme, W.describe(wl), flush=True)
+    x, logits, pre = HN.device_inputs(wl)
+    w = HN.device_weights_mx(wl, quant)
+    p = HN.device_params(wl)
+    xq = torch.empty(wl.T, wl.H, dtype=torch.uint8, device=DEV)
+    xs = torch.empty(wl.T, wl.H // 32, dtype=torch.uint8, device=DEV)
+    y = M.moe_fused(p, x, w, router_logits=logits, prelude=pre, act_q=xq, act_scales=xs)
+    y0 = M.moe_fused(p, x, w, router_logits=logits, prelude=pre)
+    torch.cuda.synchronize()
+    q, s = omx.quant_rows_32(W.bf16_to_f64(W.hidden_bf16(wl)))
+    assert np.array_equal(xq.cpu().numpy(), q)
+    assert np.array_equal(xs.cpu().numpy(), s)
+    assert torch.equal(y, y0)
