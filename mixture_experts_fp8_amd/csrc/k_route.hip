@@ -17,12 +17,12 @@ typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
 // Gate prelude: logits[t, e] = r_t * sum_h x[t,h] * norm_w[h] * W_r[e, h], with
 // r_t = 1 / sqrt(mean_h x[t,h]^2 + eps) -- RMSNorm then the float32 router matmul, with the
 // per-token factor r_t applied once to the finished dot product.
-// Workgroup (expert e, 8 tokens), 4 waves splitting H into interleaved 256-wide steps:
+// Workgroup (expert e, 4 tokens), 4 waves splitting H into interleaved 256-wide steps:
 // lane l owns 4 consecutive h per step, loaded as one 16-byte W_r / norm load and one 8-byte
 // load per token; each token's sum of squares comes from the same loaded values.  The loads
 // of kPreB steps are issued before any of their sums (one memory round trip per kPreB steps;
 // the sums still run in h order).  Partial sums meet in LDS.
-constexpr int kPreT = 8;
+constexpr int kPreT = 4;
 constexpr int kPreB = 4;
 
 __global__ __launch_bounds__(256) void k_gate_prelude(const uint16_t* __restrict__ x, int T, int H, int E,
@@ -307,20 +307,20 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, co
     }
 }
 
-// Top-k routing over many workgroups: one wave per token, 4 tokens per workgroup.
+// Top-k routing over many workgroups: one wave per token, one token per workgroup (spreads a
+// decode batch's tokens over as many CUs as it has tokens).
 template <int EPL>
-__global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, RouteCfg c,
+__global__ __launch_bounds__(64) void k_route(const float* __restrict__ logits, RouteCfg c,
                                                const float* __restrict__ pe_scale, int32_t* __restrict__ ids,
                                                float* __restrict__ wts, QuantOut qo) {
     extern __shared__ float s_route[];
-    const int wv = threadIdx.x >> 6;
-    route_token<EPL>(logits, c, pe_scale, ids, wts, qo, blockIdx.x * 4 + wv, s_route + (size_t)wv * (c.E + 3 * c.k));
+    route_token<EPL>(logits, c, pe_scale, ids, wts, qo, blockIdx.x, s_route);
 }
 
 hipError_t launch_route(const float* logits, const RouteCfg& c, const float* pe_scale, int32_t* ids,
                         float* weights, hipStream_t st, QuantOut qo) {
-    const dim3 grid((unsigned)ceil_div(c.T, 4)), block(256);
-    const size_t lds = (size_t)4 * (c.E + 3 * c.k) * 4;
+    const dim3 grid((unsigned)c.T), block(64);
+    const size_t lds = (size_t)(c.E + 3 * c.k) * 4;
     const int epl = (int)ceil_div(c.E, 64);
     if (epl <= 1) hipLaunchKernelGGL(k_route<1>, grid, block, lds, st, logits, c, pe_scale, ids, weights, qo);
     else if (epl <= 2) hipLaunchKernelGGL(k_route<2>, grid, block, lds, st, logits, c, pe_scale, ids, weights, qo);
