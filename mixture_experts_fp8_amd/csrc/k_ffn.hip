@@ -1891,34 +1891,28 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, void* ws, hipStream_t st, hipEve
 }
 
 // ----------------------------------------------------------------------------------------
-// Combine: workgroup (token, 256 x 4 x MOE_COMBINE_CPT-column slice); each thread owns
-// MOE_COMBINE_CPT groups of 4 consecutive columns and issues the loads of up to 8 expert rows
-// for all of them before summing them in slot order j = 0, 1, ...
-template <bool BF16>
-__device__ __forceinline__ float4 load4(const void* eo, int64_t idx) {
-    // expert_out is read exactly once: non-temporal loads keep it from displacing cached lines
-    if (BF16) {
-        const v2i_t u = __builtin_nontemporal_load(reinterpret_cast<const v2i_t*>(reinterpret_cast<const uint16_t*>(eo) + idx));
-        return make_float4(bf16_to_f32((uint32_t)u[0] & 0xFFFFu), bf16_to_f32((uint32_t)u[0] >> 16),
-                           bf16_to_f32((uint32_t)u[1] & 0xFFFFu), bf16_to_f32((uint32_t)u[1] >> 16));
-    }
-    const v4f v = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(reinterpret_cast<const float*>(eo) + idx));
-    return make_float4(v[0], v[1], v[2], v[3]);
-}
+// Combine: workgroup (token, 256 x CPT column groups); a group is the 16 bytes of one
+// expert row that one load brings in: 4 float32 columns, or 8 bf16 ones.  Each thread owns
+// CPT groups 256 apart and issues the loads of up to 8 expert rows for all of them before
+// summing them in slot order j = 0, 1, ... (expert_out is read exactly once: non-temporal
+// loads keep it from displacing cached lines).
+typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
 
 template <bool BF16, int CPT>
 __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ eo, const int32_t* __restrict__ pos,
                                                  const float* __restrict__ w, int k, int H,
                                                  uint16_t* __restrict__ y) {
-    // thread: CPT groups of 4 columns, 256 * 4 apart; all of a slot's loads are issued before
-    // the sums
+    constexpr int CW = BF16 ? 8 : 4;   // columns per group
     const int t = blockIdx.x;
-    const int c40 = blockIdx.y * 256 * CPT + threadIdx.x;
-    float4 acc[CPT];
+    const int g0 = blockIdx.y * 256 * CPT + threadIdx.x;
+    const int ng = H / CW;
+    float acc[CPT][CW];
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) acc[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c = 0; c < CPT; ++c)
+#pragma unroll
+        for (int i = 0; i < CW; ++i) acc[c][i] = 0.f;
     for (int j0 = 0; j0 < k; j0 += 8) {
-        float4 v[8][CPT];
+        v4u_t v[8][CPT];
         float wj[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -1927,8 +1921,14 @@ __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ eo, co
             wj[u] = p >= 0 ? w[(int64_t)t * k + j] : 0.f;
 #pragma unroll
             for (int c = 0; c < CPT; ++c) {
-                const int c4 = c40 + c * 256;
-                v[u][c] = (p >= 0 && c4 * 4 < H) ? load4<BF16>(eo, (int64_t)p * H + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+                const int g = g0 + c * 256;
+                if (p >= 0 && g < ng) {
+                    const int64_t off = ((int64_t)p * H + (int64_t)g * CW) * (BF16 ? 2 : 4);
+                    v[u][c] = __builtin_nontemporal_load(
+                        reinterpret_cast<const v4u_t*>(reinterpret_cast<const uint8_t*>(eo) + off));
+                } else {
+                    v[u][c] = v4u_t{0u, 0u, 0u, 0u};
+                }
             }
         }
 #pragma unroll
@@ -1936,40 +1936,48 @@ __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ eo, co
             if (j0 + u < k) {
 #pragma unroll
                 for (int c = 0; c < CPT; ++c) {
-                    acc[c].x = fmaf(wj[u], v[u][c].x, acc[c].x);
-                    acc[c].y = fmaf(wj[u], v[u][c].y, acc[c].y);
-                    acc[c].z = fmaf(wj[u], v[u][c].z, acc[c].z);
-                    acc[c].w = fmaf(wj[u], v[u][c].w, acc[c].w);
+#pragma unroll
+                    for (int i = 0; i < CW; ++i) {
+                        float x;
+                        if constexpr (BF16) x = bf16_to_f32(i & 1 ? v[u][c][i / 2] >> 16 : v[u][c][i / 2] & 0xFFFFu);
+                        else x = __uint_as_float(v[u][c][i]);
+                        acc[c][i] = fmaf(wj[u], x, acc[c][i]);
+                    }
                 }
             }
         }
     }
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-        const int c4 = c40 + c * 256;
-        if (c4 * 4 < H) {
-            uint2 o;
-            o.x = (uint32_t)f32_to_bf16(acc[c].x) | ((uint32_t)f32_to_bf16(acc[c].y) << 16);
-            o.y = (uint32_t)f32_to_bf16(acc[c].z) | ((uint32_t)f32_to_bf16(acc[c].w) << 16);
-            *reinterpret_cast<uint2*>(y + (int64_t)t * H + c4 * 4) = o;
+        const int g = g0 + c * 256;
+        if (g < ng) {
+            uint32_t o[CW / 2];
+#pragma unroll
+            for (int i = 0; i < CW / 2; ++i)
+                o[i] = (uint32_t)f32_to_bf16(acc[c][2 * i]) | ((uint32_t)f32_to_bf16(acc[c][2 * i + 1]) << 16);
+            if constexpr (BF16) *reinterpret_cast<uint4*>(y + (int64_t)t * H + g * CW) = make_uint4(o[0], o[1], o[2], o[3]);
+            else *reinterpret_cast<uint2*>(y + (int64_t)t * H + g * CW) = make_uint2(o[0], o[1]);
         }
     }
 }
 
 // Column groups per thread: the largest of 4, 2, 1 whose 256 x CPT slots the row fills.
-// More groups per thread put more independent loads in flight (H = 4096: 4 measured best);
-// for short rows the unused slots only cost registers and occupancy (H = 768: 1 cut the
-// combine from 14.6 to 11.8 us).
+// More groups per thread put more independent loads in flight (fp32 rows of H = 4096: 4
+// measured best); for short rows the unused slots only cost registers and occupancy (fp32
+// rows of H = 768: 1 cut the combine from 14.6 to 11.8 us).
 template <bool BF16>
 static void launch_combine_t(const void* eo, const int32_t* pos, const float* w, int T, int k, int H, uint16_t* y,
                              hipStream_t st) {
-    const int q = H / 4;
-    if (q >= 256 * 4)
-        hipLaunchKernelGGL((k_combine<BF16, 4>), dim3(T, (unsigned)ceil_div(q, 256 * 4)), dim3(256), 0, st, eo, pos, w, k, H, y);
-    else if (q >= 256 * 2)
-        hipLaunchKernelGGL((k_combine<BF16, 2>), dim3(T, (unsigned)ceil_div(q, 256 * 2)), dim3(256), 0, st, eo, pos, w, k, H, y);
+    const int ng = H / (BF16 ? 8 : 4);
+    if (ng >= 256 * 4)
+        hipLaunchKernelGGL((k_combine<BF16, 4>), dim3(T, (unsigned)ceil_div(ng, 256 * 4)), dim3(256), 0, st, eo, pos, w,
+                           k, H, y);
+    else if (ng >= 256 * 2)
+        hipLaunchKernelGGL((k_combine<BF16, 2>), dim3(T, (unsigned)ceil_div(ng, 256 * 2)), dim3(256), 0, st, eo, pos, w,
+                           k, H, y);
     else
-        hipLaunchKernelGGL((k_combine<BF16, 1>), dim3(T, (unsigned)ceil_div(q, 256)), dim3(256), 0, st, eo, pos, w, k, H, y);
+        hipLaunchKernelGGL((k_combine<BF16, 1>), dim3(T, (unsigned)ceil_div(ng, 256)), dim3(256), 0, st, eo, pos, w, k,
+                           H, y);
 }
 
 hipError_t launch_combine(const void* eo, int bf16, const int32_t* pos, const float* w, int T, int k, int H,

@@ -206,8 +206,10 @@ def test_dispatch_many_chunks(T, k, E):
     assert np.array_equal(got["assign_pos"].cpu().numpy(), ap)
 
 
-def test_combine_parity_on_generated_expert_out():
-    T, k, H = 37, 3, 384
+# (T, k, H): fp32 rows take 1, 2 or 4 column groups per thread at H = 384, 2816, 4096 and
+# bf16 rows 1, 2, 4 at H = 2816, 4096, 8192; k = 9 runs the slot loop twice
+@pytest.mark.parametrize("T,k,H", [(37, 3, 384), (5, 8, 2816), (4, 9, 4096), (3, 2, 8192)])
+def test_combine_parity_on_generated_expert_out(T, k, H):
     eo = rng.normal_f32(rng.stream_key(0, 200, 0), T * k * H, 1.0).view(T * k, H)
     w = rng.uniform_f32(rng.stream_key(0, 200, 1), T * k, 0.0, 1.0).view(T, k)
     perm = torch.from_numpy(np.random.default_rng(2).permutation(T * k).astype(np.int32))
