@@ -124,9 +124,11 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     return r;
 }
 
-// The token row's activation quantisation (per 128 columns, 16 lanes per group): loads of
-// the 32 groups from g0 on, then their E4M3 codes and UE8M0 scales.  The row is read once:
-// non-temporal.
+// The token row's activation quantisation: loads of the 128-column blocks g0 .. g0 + 31
+// (16 lanes per block, 8 columns per lane), then their E4M3 codes and UE8M0 scales per group
+// of qo.group columns -- 128 (one scale per block, amax over the 16 lanes) or 32 (four scales
+// per block, amax over aligned quads of lanes); the scale rule is the same.  The row is read
+// once: non-temporal.
 __device__ __forceinline__ void xrow_load(const QuantOut& qo, int t, int g0, int lane, uint4 (&v)[8]) {
     const int ngc = qo.H / kGroup;
     const uint16_t* xr = qo.x + (int64_t)t * qo.H;
@@ -139,13 +141,44 @@ __device__ __forceinline__ void xrow_load(const QuantOut& qo, int t, int g0, int
         }
     }
 }
+// 8 bf16 values of a 32-column group whose other 24 sit in the lane's quad.
+__device__ __forceinline__ void quant_group4_v(const uint4 v, uint8_t* __restrict__ dq, uint8_t* __restrict__ ds,
+                                               int sub) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+        f[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    amax = fmaxf(amax, dpp_f32<0xB1>(amax));
+    amax = fmaxf(amax, dpp_f32<0x4E>(amax));
+    const int e = scale_exponent(amax);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = ldexpf(f[i], -e);
+    uint2 q;
+    q.x = cvt4_e4m3(f[0], f[1], f[2], f[3]);
+    q.y = cvt4_e4m3(f[4], f[5], f[6], f[7]);
+    *reinterpret_cast<uint2*>(dq + sub * 8) = q;
+    if ((sub & 3) == 0) *ds = (uint8_t)(e + 127);
+}
+
 __device__ __forceinline__ void xrow_quant(const QuantOut& qo, int t, int g0, int lane, const uint4 (&v)[8]) {
     const int ngc = qo.H / kGroup;
+    const int nsc = qo.H / qo.group;   // scales per row
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int g = g0 + (lane >> 4) + 4 * i;
-        if (g < ngc)
-            quant_group16_v(v[i], qo.xq + (int64_t)t * qo.H + g * kGroup, qo.xs + (int64_t)t * ngc + g, lane & 15);
+        if (g < ngc) {
+            uint8_t* dq = qo.xq + (int64_t)t * qo.H + g * kGroup;
+            if (qo.group == kGroup)
+                quant_group16_v(v[i], dq, qo.xs + (int64_t)t * nsc + g, lane & 15);
+            else
+                quant_group4_v(v[i], dq, qo.xs + (int64_t)t * nsc + g * (kGroup / 32) + (lane & 15) / 4, lane & 15);
+        }
     }
 }
 

@@ -430,10 +430,9 @@ int moe_fused(const moe_fused_args* a) {
     moe::RouteCfg rcfg = route_cfg(&a->route, T, a->prelude != nullptr);
     rcfg.ld = kf;
     rcfg.shared_id = sh ? E : -1;
-    // the 128-group activation quantisation runs inside the routing kernel (one wave per
-    // token); the 32-group one is its own launch
+    // the activation quantisation (128- or 32-column groups) runs inside the routing kernel,
+    // one wave per token
     mark(0);
-    if (e == hipSuccess && mx) e = moe::launch_quant_act_mx(a->hidden_states, T, H, H, xq, xs, st);
     mark(1);
     float* pl = reinterpret_cast<float*>(rws + route_chunk_bytes(T, Ef, kf));
     if (e == hipSuccess && a->prelude)
@@ -442,8 +441,8 @@ int moe_fused(const moe_fused_args* a) {
     if (e == hipSuccess)
         e = moe::launch_route(a->prelude ? pl : a->router_logits, rcfg, a->prelude ? a->prelude->per_expert_scale : nullptr,
                               ids, wts, st,
-                              mx || w16 ? moe::QuantOut{nullptr, 0, nullptr, nullptr}
-                                        : moe::QuantOut{a->hidden_states, H, xq, xs});
+                              w16 ? moe::QuantOut{nullptr, 0, nullptr, nullptr, 128}
+                                  : moe::QuantOut{a->hidden_states, H, xq, xs, mx ? 32 : 128});
     mark(2);
     if (e == hipSuccess)
         e = moe::launch_dispatch(ids, (int)A, Ef, reinterpret_cast<int32_t*>(rws), counts, offsets, sorted, pos, st,

@@ -45,11 +45,12 @@ hipError_t launch_gate_prelude(const uint16_t* x, int T, int H, int E, const flo
 struct QuantOut {
     const uint16_t* x;   // [T, H] bf16
     int H;
-    uint8_t* xq;         // [T, H]
-    uint8_t* xs;         // [T, H/128]
+    uint8_t* xq;         // [T, H] E4M3
+    uint8_t* xs;         // [T, H/group] UE8M0
+    int group;           // elements per scale: 128, or 32 for the micro-scaled schemes
 };
 hipError_t launch_route(const float* logits, const RouteCfg& c, const float* pe_scale, int32_t* ids,
-                        float* weights, hipStream_t st, QuantOut qo = QuantOut{nullptr, 0, nullptr, nullptr});
+                        float* weights, hipStream_t st, QuantOut qo = QuantOut{nullptr, 0, nullptr, nullptr, 128});
 // Dispatch (stable counting sort).  A <= kDispatchOneMaxA: one workgroup; otherwise
 // hist + scan + scatter over chunks (chunk_ws holds nchunks*E int32).  With tiles given,
 // also the GEMM tile list for BM-row tiles.
