@@ -126,7 +126,7 @@ def test_separate_entry_points_match_fused(name):
     HN.assert_output_close(got[okf], ref["o"][okf], "expert_out", ref["qmargin"][okf])
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
 def test_fused_activation_quant_bit_exact(cfg):
     # the fused call quantises the activations inside its routing kernel (one wave per token);
     # its E4M3 codes and UE8M0 scales must be the oracle's per-(row, 128) quantisation exactly,
