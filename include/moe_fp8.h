@@ -29,6 +29,9 @@
  *     ids and permutation indices are int32.  Row-major throughout.
  *   - Reentrant; the library keeps no device memory of its own and allocates nothing:
  *     temporaries live in the caller's workspace (moe_workspace_size).
+ *   - Size limits of the expert step (MOE_ERR_UNSUPPORTED beyond them): H and I multiples of
+ *     128 and at most 32768; T * top_k < 2^29; T * H < 2^31 and 2 * I * H < 2^31 (the kernels
+ *     address activation rows and one expert's weights with 32-bit offsets).
  */
 #ifndef MOE_FP8_H
 #define MOE_FP8_H
@@ -261,6 +264,21 @@ typedef struct moe_ffn_args {
     const uint16_t* x;          /* MOE_QUANT_W8A16 only: the bf16 hidden states [T, H]
                                    (16-byte aligned); xq and xs are then unused and may be
                                    NULL.  Ignored by the other schemes. */
+    /* Optional test outputs (NULL in production; all three NULL, or debug_h and debug_hq and,
+     * except for MOE_QUANT_W8A16, debug_hs).  They expose the SwiGLU + re-quantisation step of
+     * the gate+up epilogue (the "SiLU products are quantised to E4M3 per (row, 128 group)" of
+     * the fp8_grouped_tc_w8a8.rs module doc) for a unit check, each [T*k, ...] in sorted-slot
+     * order (row s = expert_offsets[e] + i):
+     *   debug_h   float32 [T*k, I]: h = silu(g) * u as the epilogue computed it, before the
+     *             re-quantisation;
+     *   debug_hq  [T*k, I] the re-quantised h that the down GEMM reads, copied out of its
+     *             operand layout: E4M3 codes, or bf16 (2 bytes each) for MOE_QUANT_W8A16;
+     *   debug_hs  [T*k, I/128] its UE8M0 scales ([T*k, I/32] for the MX schemes).
+     * The gate+up GEMM then runs a variant that also stores h, and one more kernel copies hq
+     * and hs out; expert_out is the same as without them. */
+    float*         debug_h;
+    uint8_t*       debug_hq;
+    uint8_t*       debug_hs;
 } moe_ffn_args;
 
 int moe_grouped_ffn(const moe_ffn_args* a);
@@ -270,7 +288,9 @@ size_t moe_ffn_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_
 /* moe_combine: y[t, c] = bf16_RNE( sum_{j<k} topk_weights[t, j] * expert_out[assign_pos[t*k+j], c] ),
  * the sum taken in float32 in increasing j (the `combine` stage: restore token order and
  * merge; the MATE page's contiguous bfloat16 output).  Deterministic.
- *   expert_out [T*k, H] of dtype MOE_DTYPE_F32 or MOE_DTYPE_BF16; y [T, H] bf16, contiguous. */
+ *   expert_out [T*k, H] of dtype MOE_DTYPE_F32 or MOE_DTYPE_BF16, 16-byte aligned;
+ *   y [T, H] bf16, contiguous, 8-byte aligned.  H % 4 == 0; T * k < 2^29.
+ *   assign_pos entries < 0 are skipped (dropped assignments). */
 int moe_combine(const void* expert_out, int32_t dtype, const int32_t* assign_pos,
                 const float* topk_weights, int32_t T, int32_t k, int32_t H,
                 uint16_t* y, void* stream);

@@ -60,7 +60,8 @@ class FfnArgs(ctypes.Structure):
                 ("w2", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p), ("expert_out", ctypes.c_void_p),
                 ("out_dtype", ctypes.c_int32), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p), ("quant", ctypes.c_int32),
-                ("x", ctypes.c_void_p)]
+                ("x", ctypes.c_void_p), ("debug_h", ctypes.c_void_p), ("debug_hq", ctypes.c_void_p),
+                ("debug_hs", ctypes.c_void_p)]
 
 
 class FusedArgs(ctypes.Structure):
@@ -315,9 +316,12 @@ def pack_weights_mx(w13: torch.Tensor, w2: torch.Tensor, quant: int) -> PackedWe
 
 
 def moe_grouped_ffn(xq: Optional[torch.Tensor], xs: Optional[torch.Tensor], routing: dict, w: PackedWeights, k: int,
-                    out_dtype=torch.float32, x: Optional[torch.Tensor] = None) -> torch.Tensor:
+                    out_dtype=torch.float32, x: Optional[torch.Tensor] = None, debug: bool = False):
     """Both expert GEMMs; returns expert_out [T*k, H] in expert-sorted slot order.
-    MOE_QUANT_W8A16 weights take the bf16 hidden states x [T, H] instead of xq / xs."""
+    MOE_QUANT_W8A16 weights take the bf16 hidden states x [T, H] instead of xq / xs.
+    debug: also return (expert_out, h, hq, hs), the test outputs of moe_ffn_args: float32 h
+    [T*k, I] before re-quantisation, the re-quantised hq [T*k, I] (uint8 E4M3, or bfloat16 for
+    W8A16) and hs [T*k, I/128] ([T*k, I/32] for the MX schemes; None for W8A16), sorted order."""
     if w.quant == MOE_QUANT_W8A16:
         if x is None:
             raise ValueError("MOE_QUANT_W8A16 takes the bf16 hidden states x")
@@ -331,11 +335,22 @@ def moe_grouped_ffn(xq: Optional[torch.Tensor], xs: Optional[torch.Tensor], rout
     out = torch.empty(T * k, H, dtype=out_dtype, device=dev)
     nbytes = lib().moe_ffn_workspace_size(T, H, w.I, w.E, k)
     ws = workspace(max(nbytes, 256), dev)
+    dh = dhq = dhs = None
+    if debug:
+        A = T * k
+        dh = torch.empty(A, w.I, dtype=torch.float32, device=dev)
+        if w.quant == MOE_QUANT_W8A16:
+            dhq = torch.empty(A, w.I, dtype=torch.bfloat16, device=dev)
+        else:
+            dhq = torch.empty(A, w.I, dtype=torch.uint8, device=dev)
+            dhs = torch.empty(A, w.I // (128 if w.quant == MOE_QUANT_FP8_BLOCK128 else 32), dtype=torch.uint8,
+                              device=dev)
     a = FfnArgs(T, k, H, w.I, w.E, _ptr(xq), _ptr(xs), _ptr(routing["expert_counts"]),
                 _ptr(routing["expert_offsets"]), _ptr(routing["sorted_assign"]), _ptr(w.w13), _ptr(w.w13_scale),
-                _ptr(w.w2), _ptr(w.w2_scale), _ptr(out), dt, _ptr(ws), ws.numel(), _stream(), w.quant, _ptr(x))
+                _ptr(w.w2), _ptr(w.w2_scale), _ptr(out), dt, _ptr(ws), ws.numel(), _stream(), w.quant, _ptr(x),
+                _ptr(dh), _ptr(dhq), _ptr(dhs))
     _check(lib().moe_grouped_ffn(ctypes.byref(a)))
-    return out
+    return (out, dh, dhq, dhs) if debug else out
 
 
 def moe_combine(expert_out: torch.Tensor, assign_pos: torch.Tensor, topk_weights: torch.Tensor) -> torch.Tensor:

@@ -1682,11 +1682,6 @@ __global__ __launch_bounds__(512, 1) void k_gemm2_p2(G2Args a) {
 }
 
 // ----------------------------------------------------------------------------------------
-// Decode tiles (16 rows) while experts average at most this many rows; 128-row tiles above.
-#ifndef MOE_DEC_MAX_AVG_ROWS
-#define MOE_DEC_MAX_AVG_ROWS 24
-#endif
-
 // The super-tile order pays off once the tiles fill several of its 64-tile windows.
 int ffn_super_tile_order(int ntiles_max) { return ntiles_max >= 512 ? 1 : 0; }
 // The 256-row down GEMM takes the super-tile order from twice as many tiles on: on the
@@ -1694,51 +1689,6 @@ int ffn_super_tile_order(int ntiles_max) { return ntiles_max >= 512 ? 1 : 0; }
 // columns) the column-block order measured 3% faster for it, while its gate/up GEMM and the
 // Zipf prefill's (1152 tiles, many pairs per expert) keep gaining from super-tiles.
 static int ffn_super_tile_order_down(int ntiles_max) { return ntiles_max >= 1024 ? 1 : 0; }
-
-// 256-row items (tile pairs) once experts average at least this many rows; the down GEMM
-// takes them from a lower average on (measured: at 64 rows per expert, of which half the
-// experts are empty, 256-row down items beat the persistent 128-row kernel while the gate/up
-// GEMM stays faster on 128-row tiles).
-#ifndef MOE_PAIR_MIN_AVG_ROWS
-#define MOE_PAIR_MIN_AVG_ROWS 128
-#endif
-#ifndef MOE_PAIR_DOWN_MIN_AVG_ROWS
-#define MOE_PAIR_DOWN_MIN_AVG_ROWS 64
-#endif
-
-FfnPlan ffn_plan(int T, int k, int E, int quant) {
-    const int64_t A = (int64_t)T * k;
-    const int64_t avg = A / E;
-    FfnPlan p;
-    p.BM = (avg <= MOE_DEC_MAX_AVG_ROWS || quant != kQuantFp8Block128) ? 16 : 128;
-    p.ntiles_max = (int)(ceil_div(A, p.BM) + std::min<int64_t>(E, A));
-    p.pairs = p.BM == 128 && avg >= MOE_PAIR_MIN_AVG_ROWS;
-    p.pairs_down = p.pairs || (p.BM == 128 && avg >= MOE_PAIR_DOWN_MIN_AVG_ROWS);
-    // an expert's pairs number ceil(tiles / 2)
-    p.npairs_max = (p.ntiles_max + (int)std::min<int64_t>(E, A)) / 2 + 1;
-    return p;
-}
-
-// workspace: tiles [ntiles_max] int2 | ntiles int | hq [ntiles_max*BM, I] | hs [ntiles_max*BM, I/128]
-//            | (128-row tiles) down-GEMM weight-scale table [E][H/128][I/128] u32
-//            | pairs [npairs_max] int4 | npairs int
-// bytes per element of h in the hq region: E4M3, or bf16 for W8A16
-static size_t h_bytes(int quant) { return quant == kQuantW8A16 ? 2 : 1; }
-
-static size_t ffn_ws_plan(const FfnPlan& p, int H, int I, int E, int quant) {
-    const size_t rows = (size_t)p.ntiles_max * p.BM;
-    // hs holds one scale per 32 columns of h (the MX schemes; the 128 scheme uses a quarter)
-    size_t n = align256((size_t)p.ntiles_max * 8) + align256(4) + align256(rows * I * h_bytes(quant)) +
-               align256(rows * (I / 32));
-    if (p.BM == 128) n += align256(ffn_rb_scale_table_bytes(H, I, E));
-    n += align256((size_t)p.npairs_max * 16) + align256(4);
-    return n;
-}
-size_t ffn_workspace_bytes(int T, int H, int I, int E, int k) {
-    return std::max({ffn_ws_plan(ffn_plan(T, k, E, kQuantFp8Block128), H, I, E, kQuantFp8Block128),
-                     ffn_ws_plan(ffn_plan(T, k, E, kQuantMxfp8), H, I, E, kQuantMxfp8),
-                     ffn_ws_plan(ffn_plan(T, k, E, kQuantW8A16), H, I, E, kQuantW8A16)});
-}
 
 template <int MFW, int NFW1, int NFW2, int WM, int WN, int PF1, int PF2>
 static hipError_t run_ffn(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid) {
@@ -1847,23 +1797,16 @@ static hipError_t run_ffn_p2(const FfnArgs& f, const FfnPlan& p, const FfnWs& w,
 }
 
 FfnWs carve_ffn_ws(const FfnArgs& f, void* ws) {
-    const FfnPlan p = ffn_plan(f.T, f.k, f.E, f.quant);
-    const size_t rows = (size_t)p.ntiles_max * p.BM;
+    const FfnWsLayout l = ffn_ws_layout(f.T, f.H, f.I, f.E, f.k, f.quant);
     uint8_t* w = static_cast<uint8_t*>(ws);
     FfnWs r;
-    r.tiles = reinterpret_cast<int2*>(w);
-    w += align256((size_t)p.ntiles_max * 8);
-    r.ntiles = reinterpret_cast<int32_t*>(w);
-    w += align256(4);
-    r.hq = w;
-    w += align256(rows * f.I * h_bytes(f.quant));
-    r.hs = w;
-    w += align256(rows * (f.I / 32));
-    r.bs = p.BM == 128 ? reinterpret_cast<uint32_t*>(w) : nullptr;
-    if (p.BM == 128) w += align256(ffn_rb_scale_table_bytes(f.H, f.I, f.E));
-    r.pairs = reinterpret_cast<int4*>(w);
-    w += align256((size_t)p.npairs_max * 16);
-    r.npairs = reinterpret_cast<int32_t*>(w);
+    r.tiles = reinterpret_cast<int2*>(w + l.tiles);
+    r.ntiles = reinterpret_cast<int32_t*>(w + l.ntiles);
+    r.hq = w + l.hq;
+    r.hs = w + l.hs;
+    r.bs = ffn_plan(f.T, f.k, f.E, f.quant).BM == 128 ? reinterpret_cast<uint32_t*>(w + l.bs) : nullptr;
+    r.pairs = reinterpret_cast<int4*>(w + l.pairs);
+    r.npairs = reinterpret_cast<int32_t*>(w + l.npairs);
     return r;
 }
 
@@ -1891,18 +1834,23 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, void* ws, hipStream_t st, hipEve
 }
 
 // ----------------------------------------------------------------------------------------
-// Combine: workgroup (token, 256 x CPT column groups); a group is the 16 bytes of one
-// expert row that one load brings in: 4 float32 columns, or 8 bf16 ones.  Each thread owns
+// Combine: workgroup (token, 256 x CPT column groups); a group is the columns of one
+// expert row that one load brings in: 16 bytes (4 float32 columns, or 8 bf16 ones), or 8
+// bytes (4 bf16 columns) for bf16 rows whose length is not a multiple of 8.  Each thread owns
 // CPT groups 256 apart and issues the loads of up to 8 expert rows for all of them before
 // summing them in slot order j = 0, 1, ... (expert_out is read exactly once: non-temporal
 // loads keep it from displacing cached lines).
 typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
+typedef unsigned v2u_t __attribute__((ext_vector_type(2)));
 
-template <bool BF16, int CPT>
+template <bool BF16, int CW, int CPT>
 __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ eo, const int32_t* __restrict__ pos,
                                                  const float* __restrict__ w, int k, int H,
                                                  uint16_t* __restrict__ y) {
-    constexpr int CW = BF16 ? 8 : 4;   // columns per group
+    static_assert(BF16 ? (CW == 8 || CW == 4) : CW == 4, "16-byte groups, or 8-byte bf16 groups");
+    constexpr int EB = BF16 ? 2 : 4;        // bytes per expert_out element
+    constexpr int NW = CW * EB / 4;         // dwords per group load
+    typedef std::conditional_t<NW == 4, v4u_t, v2u_t> ld_t;
     const int t = blockIdx.x;
     const int g0 = blockIdx.y * 256 * CPT + threadIdx.x;
     const int ng = H / CW;
@@ -1912,7 +1860,7 @@ __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ eo, co
 #pragma unroll
         for (int i = 0; i < CW; ++i) acc[c][i] = 0.f;
     for (int j0 = 0; j0 < k; j0 += 8) {
-        v4u_t v[8][CPT];
+        ld_t v[8][CPT];
         float wj[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -1923,11 +1871,11 @@ __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ eo, co
             for (int c = 0; c < CPT; ++c) {
                 const int g = g0 + c * 256;
                 if (p >= 0 && g < ng) {
-                    const int64_t off = ((int64_t)p * H + (int64_t)g * CW) * (BF16 ? 2 : 4);
+                    const int64_t off = ((int64_t)p * H + (int64_t)g * CW) * EB;
                     v[u][c] = __builtin_nontemporal_load(
-                        reinterpret_cast<const v4u_t*>(reinterpret_cast<const uint8_t*>(eo) + off));
+                        reinterpret_cast<const ld_t*>(reinterpret_cast<const uint8_t*>(eo) + off));
                 } else {
-                    v[u][c] = v4u_t{0u, 0u, 0u, 0u};
+                    v[u][c] = ld_t{};
                 }
             }
         }
@@ -1955,7 +1903,7 @@ __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ eo, co
 #pragma unroll
             for (int i = 0; i < CW / 2; ++i)
                 o[i] = (uint32_t)f32_to_bf16(acc[c][2 * i]) | ((uint32_t)f32_to_bf16(acc[c][2 * i + 1]) << 16);
-            if constexpr (BF16) *reinterpret_cast<uint4*>(y + (int64_t)t * H + g * CW) = make_uint4(o[0], o[1], o[2], o[3]);
+            if constexpr (CW == 8) *reinterpret_cast<uint4*>(y + (int64_t)t * H + g * CW) = make_uint4(o[0], o[1], o[2], o[3]);
             else *reinterpret_cast<uint2*>(y + (int64_t)t * H + g * CW) = make_uint2(o[0], o[1]);
         }
     }
@@ -1965,25 +1913,27 @@ __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ eo, co
 // More groups per thread put more independent loads in flight (fp32 rows of H = 4096: 4
 // measured best); for short rows the unused slots only cost registers and occupancy (fp32
 // rows of H = 768: 1 cut the combine from 14.6 to 11.8 us).
-template <bool BF16>
+template <bool BF16, int CW>
 static void launch_combine_t(const void* eo, const int32_t* pos, const float* w, int T, int k, int H, uint16_t* y,
                              hipStream_t st) {
-    const int ng = H / (BF16 ? 8 : 4);
+    const int ng = H / CW;
     if (ng >= 256 * 4)
-        hipLaunchKernelGGL((k_combine<BF16, 4>), dim3(T, (unsigned)ceil_div(ng, 256 * 4)), dim3(256), 0, st, eo, pos, w,
-                           k, H, y);
+        hipLaunchKernelGGL((k_combine<BF16, CW, 4>), dim3(T, (unsigned)ceil_div(ng, 256 * 4)), dim3(256), 0, st, eo,
+                           pos, w, k, H, y);
     else if (ng >= 256 * 2)
-        hipLaunchKernelGGL((k_combine<BF16, 2>), dim3(T, (unsigned)ceil_div(ng, 256 * 2)), dim3(256), 0, st, eo, pos, w,
-                           k, H, y);
+        hipLaunchKernelGGL((k_combine<BF16, CW, 2>), dim3(T, (unsigned)ceil_div(ng, 256 * 2)), dim3(256), 0, st, eo,
+                           pos, w, k, H, y);
     else
-        hipLaunchKernelGGL((k_combine<BF16, 1>), dim3(T, (unsigned)ceil_div(ng, 256)), dim3(256), 0, st, eo, pos, w, k,
-                           H, y);
+        hipLaunchKernelGGL((k_combine<BF16, CW, 1>), dim3(T, (unsigned)ceil_div(ng, 256)), dim3(256), 0, st, eo, pos,
+                           w, k, H, y);
 }
 
 hipError_t launch_combine(const void* eo, int bf16, const int32_t* pos, const float* w, int T, int k, int H,
                           uint16_t* y, hipStream_t st) {
-    if (bf16) launch_combine_t<true>(eo, pos, w, T, k, H, y, st);
-    else launch_combine_t<false>(eo, pos, w, T, k, H, y, st);
+    // bf16 rows of a length that is a multiple of 8 load 16 bytes per group, the rest 8
+    if (bf16 && H % 8 == 0) launch_combine_t<true, 8>(eo, pos, w, T, k, H, y, st);
+    else if (bf16) launch_combine_t<true, 4>(eo, pos, w, T, k, H, y, st);
+    else launch_combine_t<false, 4>(eo, pos, w, T, k, H, y, st);
     return hipGetLastError();
 }
 

@@ -335,8 +335,6 @@ bool ffn_rb_supported(int H, int I, int E, int ntiles_max) {
     return persistent_items_per_wg(ntiles_max, H / 256, persistent_grid()) <= kRb2MaxItems;
 }
 
-size_t ffn_rb_scale_table_bytes(int H, int I, int E) { return (size_t)E * (I / kGroup) * (H / kGroup) * 4; }
-
 hipError_t launch_gemm2_rb(const FfnArgs& f, const FfnWs& w, int ntiles_max, int ord, hipStream_t st) {
     const int KB = f.I / kGroup, NBS = f.H / kGroup;
     const int64_t n = (int64_t)f.E * KB * NBS;

@@ -4,14 +4,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
-namespace moe {
+#include "moe_plan.h"
 
-// ---- quantisation schemes of the grouped FFN (values of moe_ffn_args.quant)
-constexpr int kQuantFp8Block128 = 0;   // E4M3 per (row, 128), weights per 128 x 128 block
-constexpr int kQuantMxfp8 = 1;         // E4M3 per (row, 32), E4M3 weights per (32 x 1)
-constexpr int kQuantW4A8 = 2;          // E4M3 per (row, 32), E2M1 weights per (32 x 1)
-constexpr int kQuantW8A16 = 3;         // bf16 activations, E4M3 weights per 128 x 128 block
-constexpr int kWfmtE4M3 = 0, kWfmtE2M1 = 1;
+namespace moe {
 
 // ---- quantisation / layout
 hipError_t launch_quant_act(const uint16_t* x, int rows, int cols, int64_t ld, uint8_t* xq, uint8_t* xs,
@@ -37,7 +32,6 @@ struct RouteCfg {
     int ld;                 // row stride of ids / weights (>= k)
     int shared_id;          // >= 0: column k of each row gets this expert with weight 1
 };
-constexpr int kScatterChunk = 1024;   // assignments per dispatch workgroup
 
 hipError_t launch_gate_prelude(const uint16_t* x, int T, int H, int E, const float* norm_w,
                                const float* router_w, float eps, float* logits, hipStream_t st);
@@ -54,8 +48,6 @@ hipError_t launch_route(const float* logits, const RouteCfg& c, const float* pe_
 // Dispatch (stable counting sort).  A <= kDispatchOneMaxA: one workgroup; otherwise
 // hist + scan + scatter over chunks (chunk_ws holds nchunks*E int32).  With tiles given,
 // also the GEMM tile list for BM-row tiles.
-constexpr int kDispatchOneMaxA = 4096;
-#define MOE_DISPATCH_MAX_E 1024
 hipError_t launch_dispatch(const int32_t* ids, int A, int E, int32_t* chunk_ws, int32_t* counts,
                            int32_t* offsets, int32_t* sorted_assign, int32_t* assign_pos, hipStream_t st,
                            int BM = 0, int2* tiles = nullptr, int32_t* ntiles = nullptr, int4* pairs = nullptr,
@@ -65,19 +57,7 @@ hipError_t launch_pairs(const int32_t* counts, const int32_t* offsets, int E, in
                         hipStream_t st);
 hipError_t launch_tiles(const int32_t* counts, int E, int BM, int2* tiles, int32_t* ntiles, hipStream_t st);
 
-// ---- grouped FFN
-struct FfnPlan {
-    int BM;           // rows per tile
-    int ntiles_max;   // grid bound on tiles
-    int pairs;        // 1: the 128-row tiles run as 256-row items (pairs of tiles)
-    int pairs_down;   // 1: the down GEMM runs on pairs (always with pairs; also below their
-                      //    threshold, where gate/up keeps 128-row tiles)
-    int npairs_max;   // grid bound on pairs
-};
-FfnPlan ffn_plan(int T, int k, int E, int quant = kQuantFp8Block128);
-// covers every quantisation scheme
-size_t ffn_workspace_bytes(int T, int H, int I, int E, int k);
-
+// ---- grouped FFN (plan and workspace layout: moe_plan.h)
 struct FfnArgs {
     int T, k, H, I, E;
     const uint8_t* xq;
@@ -93,6 +73,11 @@ struct FfnArgs {
     int out_bf16;
     int quant;       // kQuant*; for the MX schemes w13s / w2s are the packed MX scales
     const uint16_t* x = nullptr;   // kQuantW8A16: the bf16 hidden states [T, H] (xq, xs unused)
+    // optional test outputs (moe_ffn_args.debug_*): float32 h before re-quantisation, and the
+    // re-quantised h and scales unpacked from the down GEMM's operand order, [A, I] in sorted order
+    float* debug_h = nullptr;
+    uint8_t* debug_hq = nullptr;
+    uint8_t* debug_hs = nullptr;
 };
 struct FfnWs {
     int2* tiles;
@@ -120,12 +105,9 @@ bool ffn_rb_supported(int H, int I, int E, int ntiles_max);
 // one workgroup takes from ntiles_max x ncol items in either work order
 int persistent_grid();
 int64_t persistent_items_per_wg(int ntiles_max, int ncol, int grid);
-size_t ffn_rb_scale_table_bytes(int H, int I, int E);
 hipError_t launch_gemm2_rb(const FfnArgs& f, const FfnWs& w, int ntiles_max, int ord, hipStream_t st);
 
 hipError_t launch_combine(const void* eo, int bf16, const int32_t* pos, const float* w, int T, int k, int H,
                           uint16_t* y, hipStream_t st);
-
-inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 }  // namespace moe

@@ -133,11 +133,35 @@ def test_grouped_ffn_validation():
     assert _ffn(quant=3, x=FAKE + 8) == B.MOE_ERR_UNSUPPORTED and "aligned" in M.moe_last_error()
     assert _ffn(quant=0, xq=None) == B.MOE_ERR_INVALID
     assert M.lib().moe_grouped_ffn(None) == B.MOE_ERR_INVALID
+    # the test outputs come as a set: debug_h with debug_hq (and debug_hs except for W8A16)
+    assert _ffn(debug_hq=FAKE) == B.MOE_ERR_INVALID and "only with debug_h" in M.moe_last_error()
+    assert _ffn(debug_h=FAKE, debug_hq=FAKE) == B.MOE_ERR_INVALID and "debug_hs" in M.moe_last_error()
+    assert _ffn(debug_h=FAKE, debug_hq=FAKE, debug_hs=FAKE, workspace_bytes=10) == B.MOE_ERR_WORKSPACE
+
+
+def test_32bit_offset_limits():
+    # products the kernels address with 32-bit offsets are bounded before any launch
+    assert _ffn(T=(1 << 31) // 256, H=256) == B.MOE_ERR_UNSUPPORTED and "T * H" in M.moe_last_error()
+    # just below the bounds the shapes pass (a too-small workspace then stops the call)
+    assert _ffn(T=(1 << 31) // 256 - 1, H=256, workspace_bytes=10) == B.MOE_ERR_WORKSPACE
+    assert _ffn(H=32768, I=32768) == B.MOE_ERR_UNSUPPORTED and "2 * I * H" in M.moe_last_error()
+    assert _ffn(H=32768, I=32640, workspace_bytes=10) == B.MOE_ERR_WORKSPACE
+    assert _ffn(T=1 << 28, k=2) == B.MOE_ERR_UNSUPPORTED and "2^29" in M.moe_last_error()
+    assert _fused(T=(1 << 31) // 256) == B.MOE_ERR_UNSUPPORTED and "T * H" in M.moe_last_error()
+    p = M.route_params(8, 8)
+    assert _route(p, T=1 << 26) == B.MOE_ERR_UNSUPPORTED and "2^29" in M.moe_last_error()
+    L = M.lib()
+    assert L.moe_combine(FAKE, 0, FAKE, FAKE, 1 << 27, 4, 128, FAKE, None) == B.MOE_ERR_UNSUPPORTED
+    pre = B.GatePrelude(FAKE, FAKE, None, 1e-6)
+    assert _route(M.route_params(8, 2), T=1 << 20, logits=None, prelude=ctypes.byref(pre), hidden=FAKE,
+                  H=4096) == B.MOE_ERR_UNSUPPORTED
 
 
 def test_combine_validation():
     L = M.lib()
     assert L.moe_combine(FAKE, 0, FAKE, FAKE, 4, 2, 130, FAKE, None) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_combine(FAKE, 1, FAKE, FAKE, 4, 2, 130, FAKE, None) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_combine(FAKE, 0, FAKE, FAKE, 4, 2, 128, FAKE + 4, None) == B.MOE_ERR_UNSUPPORTED   # y alignment
     assert L.moe_combine(FAKE, 3, FAKE, FAKE, 4, 2, 128, FAKE, None) == B.MOE_ERR_INVALID
     assert L.moe_combine(None, 0, FAKE, FAKE, 4, 2, 128, FAKE, None) == B.MOE_ERR_INVALID
 
