@@ -80,7 +80,9 @@ struct G1Args {
     int ord;    // work order of the 128-row-tile kernels: 1 super-tiles (ord_item), 0 column blocks
     const int4* pairs;       // 256-row items: {first tile, expert, first sorted row, valid rows}
     const int32_t* npairs;   // and the pair count
+    float* htap;             // test output: float32 h [A, I] in sorted order (kernels built with TAP)
 };
+
 
 __device__ __forceinline__ v8i lds_frag(const uint8_t* base, int lane) {
     const uint4 lo = *reinterpret_cast<const uint4*>(base + lane * 16);
@@ -102,7 +104,7 @@ __device__ __forceinline__ v8i gmem_frag(const uint8_t* base, int lane) {
 
 // gate+up GEMM + SwiGLU + requant.  Wave (wm, wn) computes MFW m-frags x NFW gate frags and
 // the NFW matching up frags; the workgroup covers BM rows x one 128-column block ib of h.
-template <int MFW, int NFW, int WM, int WN, int PF>
+template <int MFW, int NFW, int WM, int WN, int PF, bool TAP>
 __global__ __launch_bounds__(64 * WM * WN) void k_gemm1(G1Args a) {
     constexpr int NT = 64 * WM * WN;
     constexpr int MF = MFW * WM;
@@ -239,6 +241,8 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm1(G1Args a) {
                 const float h = g / (1.0f + expf(-g)) * accu[mi][j][i];
                 hv[mi][j][i] = h;
                 m = fmaxf(m, fabsf(h));
+                tap_h<TAP>(a.htap, a.I, rowbase, (wm * MFW + mi) * 16 + 4 * (lane >> 4) + i, nvalid,
+                           ib * 128 + (wn * NFW + j) * 16 + (lane & 15), h);
             }
             m = max16(m);
             if ((lane & 15) == 0) s_amax[wn][(wm * MFW + mi) * 16 + 4 * (lane >> 4) + i] = m;
@@ -429,7 +433,7 @@ __device__ __forceinline__ v8i gmem_a32(const uint8_t* p) {
     return r;
 }
 
-template <int NFW, int WN, int PF>
+template <int NFW, int WN, int PF, bool TAP>
 __global__ __launch_bounds__(64 * WN) void k_gemm1_dec(G1Args a) {
     static_assert(NFW * WN == 8, "a workgroup covers 128 gate + 128 up columns");
     const int tile = blockIdx.x;
@@ -529,6 +533,7 @@ __global__ __launch_bounds__(64 * WN) void k_gemm1_dec(G1Args a) {
             const float h = g / (1.0f + expf(-g)) * accu[j][i];
             hv[j][i] = h;
             m = fmaxf(m, fabsf(h));
+            tap_h<TAP>(a.htap, a.I, rowbase, 4 * (lane >> 4) + i, nvalid, ib * 128 + (wn * NFW + j) * 16 + (lane & 15), h);
         }
         m = max16(m);
         if ((lane & 15) == 0) s_amax[wn][4 * (lane >> 4) + i] = m;
@@ -773,6 +778,21 @@ __device__ __forceinline__ uint32_t e4m3_quad_rows(const float (&h)[4], const in
     return __builtin_amdgcn_perm((uint32_t)w, (uint32_t)x1, (q & 1) ? 0x03070105u : 0x06020400u);
 }
 
+// Test output of a 16-row fragment's SwiGLU (swiglu_frag): lane l holds rows row0 + 4 (l / 16)
+// + i of columns col0 + 16 jj + l % 16.
+template <bool TAP>
+__device__ __forceinline__ void tap_frag(float* htap, int I, int rowbase, int row0, int nvalid, int col0,
+                                         const float (&h)[2][4]) {
+    if constexpr (TAP) {
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                tap_h<true>(htap, I, rowbase, row0 + 4 * (lane >> 4) + i, nvalid, col0 + 16 * jj + (lane & 15), h[jj][i]);
+    }
+}
+
 // One thread per row r < nrows: the row's E4M3 scale exponent (from the four column waves'
 // maxima) as the biased byte, in row order (s_ex) and in the order of the hs blocks,
 // [tile of the item][row % 16][row / 16] (s_exT), which a few 16-byte stores then copy out.
@@ -793,6 +813,7 @@ __device__ __forceinline__ void load_exponents4(const uint8_t* s_ex, int row0, i
     for (int i = 0; i < 4; ++i) ex[i] = (int)((b4 >> (8 * i)) & 0xFFu) - 127;
 }
 
+template <bool TAP>
 __global__ __launch_bounds__(512, 1) void k_gemm1_pf(G1Args a) {
     int ib, tile;
     if (!pf_work_item(a.ord, a.I / kGroup, __builtin_amdgcn_readfirstlane(*a.ntiles), tile, ib)) return;
@@ -939,6 +960,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pf(G1Args a) {
         if (mi < nact) {
             float m[4];
             swiglu_frag(acc[mi], hv[mi], m);
+            tap_frag<TAP>(a.htap, a.I, rowbase, (wm * 4 + mi) * 16, nvalid, ib * 128 + 2 * wn * 16, hv[mi]);
             if (r16 == 0) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) s_amax[(wm * 4 + mi) * 16 + 4 * (lane >> 4) + i][wn] = m[i];
@@ -1000,7 +1022,7 @@ __device__ __forceinline__ void dma4_async(const v4i_t& srd, uint32_t m0base, ui
                  : "memory", "m0");
 }
 
-template <int SVN>   // scale bytes a thread stages per item: KB <= 4 SVN
+template <int SVN, bool TAP>   // scale bytes a thread stages per item: KB <= 4 SVN
 __global__ __launch_bounds__(512, 1) void k_gemm1_pp(G1Args a) {
     __shared__ __align__(16) uint8_t buf[kPpStages * kPfStage];
     __shared__ __align__(16) uint8_t s_sa[2][kPpMaxKB * kPfBM];   // [item parity][kb][wm][row % 16][fragment of wm]
@@ -1167,6 +1189,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pp(G1Args a) {
             if (mi < nact) {
                 float m[4];
                 swiglu_frag(acc[mi], hv[mi], m);
+                tap_frag<TAP>(a.htap, a.I, it.w, (wm * 4 + mi) * 16, nvalid, ib * 128 + 2 * wn * 16, hv[mi]);
                 if (r16 == 0) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) s_amax[(wm * 4 + mi) * 16 + 4 * (lane >> 4) + i][wn] = m[i];
@@ -1372,6 +1395,7 @@ __global__ __launch_bounds__(1024) void k_pairs(const int32_t* __restrict__ coun
     if (e == 1023) *npairs = vp + ap;
 }
 
+template <bool TAP>
 __global__ __launch_bounds__(512, 1) void k_gemm1_p2(G1Args a) {
     int ib, pair;
     if (!pf_work_item(a.ord, a.I / kGroup, __builtin_amdgcn_readfirstlane(*a.npairs), pair, ib)) return;
@@ -1513,6 +1537,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_p2(G1Args a) {
         if (mi < nact) {
             float m[4];
             swiglu_frag(acc[mi], hv[mi], m);
+            tap_frag<TAP>(a.htap, a.I, rowbase, (wm * 8 + mi) * 16, nvalid, ib * 128 + 2 * wn * 16, hv[mi]);
             if (r16 == 0) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) s_amax[(wm * 8 + mi) * 16 + 4 * (lane >> 4) + i][wn] = m[i];
@@ -1690,12 +1715,22 @@ int ffn_super_tile_order(int ntiles_max) { return ntiles_max >= 512 ? 1 : 0; }
 // Zipf prefill's (1152 tiles, many pairs per expert) keep gaining from super-tiles.
 static int ffn_super_tile_order_down(int ntiles_max) { return ntiles_max >= 1024 ? 1 : 0; }
 
+// Launch a gate+up kernel template with TAP (the float32 h test output) on or off.
+#define MOE_LAUNCH_TAP(tap, KERNEL, grid, block, ...)                                       \
+    do {                                                                                     \
+        if (tap) hipLaunchKernelGGL((KERNEL<__VA_ARGS__ true>), grid, block, 0, st, g1);     \
+        else hipLaunchKernelGGL((KERNEL<__VA_ARGS__ false>), grid, block, 0, st, g1);        \
+    } while (0)
+
+static G1Args g1_args(const FfnArgs& f, const FfnWs& w, int ord) {
+    return G1Args{f.xq, f.xs, f.T, f.k, f.H, f.I, f.counts, f.offsets, f.sorted_assign, w.tiles, w.ntiles, f.w13p,
+                  f.w13s, w.hq, w.hs, ord, w.pairs, w.npairs, f.debug_h};
+}
+
 template <int MFW, int NFW1, int NFW2, int WM, int WN, int PF1, int PF2>
 static hipError_t run_ffn(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid) {
-    G1Args g1{f.xq, f.xs, f.T, f.k, f.H, f.I, f.counts, f.offsets, f.sorted_assign, w.tiles, w.ntiles, f.w13p, f.w13s,
-              w.hq, w.hs, ffn_super_tile_order(p.ntiles_max)};
-    hipLaunchKernelGGL((k_gemm1<MFW, NFW1, WM, WN, PF1>), dim3(p.ntiles_max, f.I / kGroup), dim3(64 * WM * WN), 0,
-                       st, g1);
+    const G1Args g1 = g1_args(f, w, ffn_super_tile_order(p.ntiles_max));
+    MOE_LAUNCH_TAP(f.debug_h, k_gemm1, dim3(p.ntiles_max, f.I / kGroup), dim3(64 * WM * WN), MFW, NFW1, WM, WN, PF1,);
     if (mid) {
         const hipError_t e = hipEventRecord(mid, st);
         if (e != hipSuccess) return e;
@@ -1710,9 +1745,8 @@ static hipError_t run_ffn(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hi
 
 template <int NFW1, int WN1, int PF1, int NFW2, int WN2, int PF2>
 static hipError_t run_ffn_dec(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid) {
-    G1Args g1{f.xq, f.xs, f.T, f.k, f.H, f.I, f.counts, f.offsets, f.sorted_assign, w.tiles, w.ntiles, f.w13p, f.w13s,
-              w.hq, w.hs, ffn_super_tile_order(p.ntiles_max)};
-    hipLaunchKernelGGL((k_gemm1_dec<NFW1, WN1, PF1>), dim3(p.ntiles_max, f.I / kGroup), dim3(64 * WN1), 0, st, g1);
+    const G1Args g1 = g1_args(f, w, ffn_super_tile_order(p.ntiles_max));
+    MOE_LAUNCH_TAP(f.debug_h, k_gemm1_dec, dim3(p.ntiles_max, f.I / kGroup), dim3(64 * WN1), NFW1, WN1, PF1,);
     if (mid) {
         const hipError_t e = hipEventRecord(mid, st);
         if (e != hipSuccess) return e;
@@ -1735,21 +1769,20 @@ static hipError_t launch_gemm2_p2(const FfnArgs& f, const FfnPlan& p, const FfnW
 
 static hipError_t run_ffn_pf(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid,
                              bool pairs_ready) {
-    G1Args g1{f.xq, f.xs, f.T, f.k, f.H, f.I, f.counts, f.offsets, f.sorted_assign, w.tiles, w.ntiles, f.w13p, f.w13s,
-              w.hq, w.hs, ffn_super_tile_order(p.ntiles_max)};
+    const G1Args g1 = g1_args(f, w, ffn_super_tile_order(p.ntiles_max));
     const int KB1 = f.H / kGroup, pgrid = persistent_grid();
 #ifndef MOE_NO_PP
     // the persistent kernel where its staged scales and item table fit
     if (KB1 >= 2 && KB1 <= kPpMaxKB && persistent_items_per_wg(p.ntiles_max, f.I / kGroup, pgrid) <= kPpMaxItems) {
-        if (KB1 <= 8) hipLaunchKernelGGL(k_gemm1_pp<2>, dim3(pgrid), dim3(512), 0, st, g1);
-        else if (KB1 <= 16) hipLaunchKernelGGL(k_gemm1_pp<4>, dim3(pgrid), dim3(512), 0, st, g1);
-        else hipLaunchKernelGGL(k_gemm1_pp<8>, dim3(pgrid), dim3(512), 0, st, g1);
+        if (KB1 <= 8) MOE_LAUNCH_TAP(f.debug_h, k_gemm1_pp, dim3(pgrid), dim3(512), 2,);
+        else if (KB1 <= 16) MOE_LAUNCH_TAP(f.debug_h, k_gemm1_pp, dim3(pgrid), dim3(512), 4,);
+        else MOE_LAUNCH_TAP(f.debug_h, k_gemm1_pp, dim3(pgrid), dim3(512), 8,);
     } else
 #endif
     {
         const int grid1 = g1.ord ? kXcds * ord_ranks(p.ntiles_max, f.I / kGroup)
                                  : (int)(ceil_div((int64_t)(f.I / kGroup) * p.ntiles_max, kXcds) * kXcds);
-        hipLaunchKernelGGL(k_gemm1_pf, dim3(grid1), dim3(512), 0, st, g1);
+        MOE_LAUNCH_TAP(f.debug_h, k_gemm1_pf, dim3(grid1), dim3(512),);
     }
     (void)pgrid;
     if (mid) {
@@ -1784,11 +1817,10 @@ static hipError_t run_ffn_p2(const FfnArgs& f, const FfnPlan& p, const FfnWs& w,
     if (!pairs_ready)
         hipLaunchKernelGGL(k_pairs, dim3(1), dim3(1024), 0, st, f.counts, f.offsets, f.E, w.pairs, w.npairs);
     const int ord = ffn_super_tile_order(p.ntiles_max);
-    G1Args g1{f.xq, f.xs, f.T, f.k, f.H, f.I, f.counts, f.offsets, f.sorted_assign, w.tiles, w.ntiles, f.w13p, f.w13s,
-              w.hq, w.hs, ord, w.pairs, w.npairs};
+    const G1Args g1 = g1_args(f, w, ord);
     const int grid1 = ord ? kXcds * ord_ranks(p.npairs_max, f.I / kGroup)
                           : (int)(ceil_div((int64_t)(f.I / kGroup) * p.npairs_max, kXcds) * kXcds);
-    hipLaunchKernelGGL(k_gemm1_p2, dim3(grid1), dim3(512), 0, st, g1);
+    MOE_LAUNCH_TAP(f.debug_h, k_gemm1_p2, dim3(grid1), dim3(512),);
     if (mid) {
         const hipError_t e = hipEventRecord(mid, st);
         if (e != hipSuccess) return e;
@@ -1810,6 +1842,62 @@ FfnWs carve_ffn_ws(const FfnArgs& f, void* ws) {
     return r;
 }
 
+// ----------------------------------------------------------------------------------------
+// Test outputs: copy the re-quantised h and its scales out of the down GEMM's operand layout
+// into row-major [A, I] and [A, I / group] in sorted order.  The hq layouts (tile slots of BM
+// rows, fragment mf = row / 16 of the slot, one 2 KB block per 128 columns; lane ln and half
+// hh hold 16 bytes b):
+//   E4M3 per 128 (decode, staged and plain 128-row tiles): row 16 mf + ln % 16, column
+//     32 (ln / 16) + 16 hh + b;
+//   MX (the instruction's K order for 32-element scales): row ln % 16, column
+//     64 hh + 16 (ln / 16) + b;
+//   W8A16: bf16 rows [tile][16][I].
+// The hs layouts: [tile * BM + row][I / 128] (decode and plain 128-row tiles),
+// [tile][I / 128][row % 16][row / 16] (staged 128-row tiles), [tile * 16 + row][I / 32] (MX).
+enum HLayout { kHlDec = 0, kHlStaged = 1, kHlPlain = 2, kHlMx = 3, kHlW16 = 4 };
+
+__global__ __launch_bounds__(256) void k_unpack_h(const int2* __restrict__ tiles, const int32_t* __restrict__ ntiles,
+                                                  const int32_t* __restrict__ counts,
+                                                  const int32_t* __restrict__ offsets, int BM, int I, int layout,
+                                                  const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs,
+                                                  uint8_t* __restrict__ dq, uint8_t* __restrict__ ds) {
+    const int tile = blockIdx.x;
+    if (tile >= *ntiles) return;
+    const int2 te = tiles[tile];
+    const int nvalid = min(BM, counts[te.x] - te.y);
+    const int64_t rowbase = offsets[te.x] + te.y;
+    if (layout == kHlW16) {
+        for (int idx = threadIdx.x; idx < nvalid * I; idx += 256) {
+            const int R = idx / I, c = idx - R * I;
+            reinterpret_cast<uint16_t*>(dq)[(rowbase + R) * I + c] =
+                reinterpret_cast<const uint16_t*>(hq)[((int64_t)tile * 16 + R) * I + c];
+        }
+        return;
+    }
+    const int KB2 = I / kGroup, MF = BM / 16;
+    for (int idx = threadIdx.x; idx < nvalid * I; idx += 256) {
+        const int R = idx / I, c = idx - R * I;
+        const int kb = c >> 7, cc = c & 127, mf = R >> 4, r = R & 15;
+        int ln, hh;
+        if (layout == kHlMx) {
+            hh = cc >> 6;
+            ln = r + 16 * ((cc >> 4) & 3);
+        } else {
+            hh = (cc >> 4) & 1;
+            ln = r + 16 * (cc >> 5);
+        }
+        dq[(rowbase + R) * I + c] = hq[(((int64_t)tile * MF + mf) * KB2 + kb) * kFragBytes + hh * 1024 + ln * 16 + (cc & 15)];
+    }
+    const int ng = layout == kHlMx ? I / 32 : KB2;
+    for (int idx = threadIdx.x; idx < nvalid * ng; idx += 256) {
+        const int R = idx / ng, g = idx - R * ng;
+        int64_t src;
+        if (layout == kHlStaged) src = ((int64_t)tile * KB2 + g) * 128 + (R & 15) * 8 + (R >> 4);
+        else src = ((int64_t)tile * BM + R) * ng + g;
+        ds[(rowbase + R) * ng + g] = hs[src];
+    }
+}
+
 hipError_t launch_grouped_ffn(const FfnArgs& f, void* ws, hipStream_t st, hipEvent_t mid, bool tiles_ready,
                               bool pairs_ready) {
     const FfnPlan p = ffn_plan(f.T, f.k, f.E, f.quant);
@@ -1818,19 +1906,35 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, void* ws, hipStream_t st, hipEve
         const hipError_t e = launch_tiles(f.counts, f.E, p.BM, w.tiles, w.ntiles, st);
         if (e != hipSuccess) return e;
     }
-    if (f.quant == kQuantW8A16) return launch_ffn_w16(f, p, w, st, mid);
-    if (f.quant != kQuantFp8Block128) return launch_ffn_mx(f, p, w, st, mid);
-    // output columns per workgroup of the down GEMM = 128, a divisor of H
-    if (p.BM == 16) return run_ffn_dec<MOE_DEC_GEMM1, MOE_DEC_GEMM2>(f, p, w, st, mid);
-    // 128-row tiles: the staged kernels need the tile's A scales in LDS and 256-column
-    // down-GEMM blocks; other shapes take the plain 128-row kernels
-    if (f.H / kGroup <= kPfMaxKB && f.I / kGroup <= kPfMaxKB && f.H % 256 == 0) {
+    hipError_t e;
+    int layout;
+    if (f.quant == kQuantW8A16) {
+        layout = kHlW16;
+        e = launch_ffn_w16(f, p, w, st, mid);
+    } else if (f.quant != kQuantFp8Block128) {
+        layout = kHlMx;
+        e = launch_ffn_mx(f, p, w, st, mid);
+    } else if (p.BM == 16) {
+        // output columns per workgroup of the down GEMM = 128, a divisor of H
+        layout = kHlDec;
+        e = run_ffn_dec<MOE_DEC_GEMM1, MOE_DEC_GEMM2>(f, p, w, st, mid);
+    } else if (f.H / kGroup <= kPfMaxKB && f.I / kGroup <= kPfMaxKB && f.H % 256 == 0) {
+        // 128-row tiles: the staged kernels need the tile's A scales in LDS and 256-column
+        // down-GEMM blocks; other shapes take the plain 128-row kernels
+        layout = kHlStaged;
 #ifndef MOE_NO_PAIRS
-        if (p.pairs) return run_ffn_p2(f, p, w, st, mid, pairs_ready);
+        if (p.pairs) e = run_ffn_p2(f, p, w, st, mid, pairs_ready);
+        else
 #endif
-        return run_ffn_pf(f, p, w, st, mid, pairs_ready);
+            e = run_ffn_pf(f, p, w, st, mid, pairs_ready);
+    } else {
+        layout = kHlPlain;
+        e = run_ffn<4, 4, 4, 2, 2, 2, 2>(f, p, w, st, mid);
     }
-    return run_ffn<4, 4, 4, 2, 2, 2, 2>(f, p, w, st, mid);
+    if (e != hipSuccess || !f.debug_h) return e;
+    hipLaunchKernelGGL(k_unpack_h, dim3(p.ntiles_max), dim3(256), 0, st, w.tiles, w.ntiles, f.counts, f.offsets, p.BM,
+                       f.I, layout, w.hq, w.hs, f.debug_hq, f.debug_hs);
+    return hipGetLastError();
 }
 
 // ----------------------------------------------------------------------------------------

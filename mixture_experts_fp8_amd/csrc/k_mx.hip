@@ -219,6 +219,7 @@ struct MxG1Args {
     const uint8_t* w13sp;       // packed scales [E][2I/16][H/128][64]
     uint8_t* hq;                // [tile][I/128][2 KB]
     uint8_t* hs;                // [tile*16 + row][I/32]
+    float* htap;                // test output: float32 h [A, I] (kernels built with TAP)
 };
 
 template <int WF>
@@ -244,7 +245,7 @@ __device__ __forceinline__ v4f mx_mfma(v8i a, v8i b, v4f acc, int sa, int sb) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, WF == kWfmtE2M1 ? 4 : 0, 0, sa, 0, sb);
 }
 
-template <int WF, int PF>
+template <int WF, int PF, bool TAP>
 __global__ __launch_bounds__(512) void k_gemm1_mx(MxG1Args a) {
     constexpr int WN = 8;                     // wave wn: gate and up columns 16 wn .. +15 of the block
     constexpr uint32_t FB = WF == kWfmtE2M1 ? 1024u : 2048u;
@@ -301,6 +302,7 @@ __global__ __launch_bounds__(512) void k_gemm1_mx(MxG1Args a) {
     for (int i = 0; i < 4; ++i) {
         const float g = accg[i];
         hv[i] = g / (1.0f + expf(-g)) * accu[i];
+        tap_h<TAP>(a.htap, a.I, rowbase, 4 * (lane >> 4) + i, nvalid, ib * 128 + wn * 16 + (lane & 15), hv[i]);
         const float m = max16(fabsf(hv[i]));
         if ((lane & 15) == 0) s_amax[wn][4 * (lane >> 4) + i] = m;
     }
@@ -445,8 +447,9 @@ hipError_t launch_prepack_mx(const uint8_t* q, const uint8_t* s, int E, int K, i
 template <int WF>
 static hipError_t run_ffn_mx(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid) {
     MxG1Args g1{f.xq, f.xs, f.T, f.k, f.H, f.I, f.counts, f.offsets, f.sorted_assign, w.tiles, w.ntiles,
-                f.w13p, f.w13s, w.hq, w.hs};
-    hipLaunchKernelGGL((k_gemm1_mx<WF, 2>), dim3(p.ntiles_max, f.I / kGroup), dim3(512), 0, st, g1);
+                f.w13p, f.w13s, w.hq, w.hs, f.debug_h};
+    if (f.debug_h) hipLaunchKernelGGL((k_gemm1_mx<WF, 2, true>), dim3(p.ntiles_max, f.I / kGroup), dim3(512), 0, st, g1);
+    else hipLaunchKernelGGL((k_gemm1_mx<WF, 2, false>), dim3(p.ntiles_max, f.I / kGroup), dim3(512), 0, st, g1);
     if (mid) {
         const hipError_t e = hipEventRecord(mid, st);
         if (e != hipSuccess) return e;

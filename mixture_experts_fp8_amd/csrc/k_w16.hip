@@ -40,6 +40,7 @@ struct W16G1Args {
     const uint8_t* w13p;   // packed E4M3 [E][2I/16][H/128][2 KB]
     const uint8_t* w13s;   // UE8M0 [E][H/128][2I/128]
     uint16_t* hb;          // [tile][16][I] bf16
+    float* htap;           // test output: float32 h [A, I] before the bf16 rounding (kernels built with TAP)
 };
 
 struct W16G2Args {
@@ -76,7 +77,7 @@ __device__ __forceinline__ void act_ops(const uint4 (&v)[4], v8bf (&a)[4]) {
 
 __device__ __forceinline__ float ue8m0_as_scale(uint32_t s) { return __uint_as_float(s << 23); }
 
-template <int PF>
+template <int PF, bool TAP>
 __global__ __launch_bounds__(512) void k_gemm1_w16(W16G1Args a) {
     const int tile = blockIdx.x;
     if (tile >= *a.ntiles) return;
@@ -144,6 +145,7 @@ __global__ __launch_bounds__(512) void k_gemm1_w16(W16G1Args a) {
     for (int i = 0; i < 4; ++i) {
         const float g = accg[i];
         const float h = g / (1.0f + expf(-g)) * accu[i];
+        tap_h<TAP>(a.htap, a.I, rowbase, 4 * (lane >> 4) + i, nvalid, ib * 128 + wn * 16 + (lane & 15), h);
         s_h[(4 * (lane >> 4) + i) * 128 + wn * 16 + (lane & 15)] = f32_to_bf16(h);
     }
     __syncthreads();
@@ -243,8 +245,10 @@ static void launch_gemm2_w16(const W16G2Args& g2, int ntiles_max, int H, hipStre
 hipError_t launch_ffn_w16(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid) {
     if (f.H / kGroup > kW16MaxKB || f.I / kGroup > kW16MaxKB) return hipErrorInvalidValue;
     uint16_t* hb = reinterpret_cast<uint16_t*>(w.hq);
-    W16G1Args g1{f.x, f.T, f.k, f.H, f.I, f.counts, f.offsets, f.sorted_assign, w.tiles, w.ntiles, f.w13p, f.w13s, hb};
-    hipLaunchKernelGGL(k_gemm1_w16<MOE_W16_PF1>, dim3(p.ntiles_max, f.I / kGroup), dim3(512), 0, st, g1);
+    W16G1Args g1{f.x, f.T, f.k, f.H, f.I, f.counts, f.offsets, f.sorted_assign, w.tiles, w.ntiles, f.w13p, f.w13s, hb,
+                 f.debug_h};
+    if (f.debug_h) hipLaunchKernelGGL((k_gemm1_w16<MOE_W16_PF1, true>), dim3(p.ntiles_max, f.I / kGroup), dim3(512), 0, st, g1);
+    else hipLaunchKernelGGL((k_gemm1_w16<MOE_W16_PF1, false>), dim3(p.ntiles_max, f.I / kGroup), dim3(512), 0, st, g1);
     if (mid) {
         const hipError_t e = hipEventRecord(mid, st);
         if (e != hipSuccess) return e;

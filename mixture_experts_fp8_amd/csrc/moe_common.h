@@ -167,6 +167,16 @@ __device__ __forceinline__ v8i buf_a32(rsrc_t r, uint32_t voff, uint32_t soff) {
 
 __host__ __device__ constexpr inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Test output of the gate+up epilogues (kernels built with TAP): the float32 h of row `row` of
+// an item whose rows start at sorted row `rowbase` (rows past nvalid are padding), column
+// `col` of h, into htap [A, I].
+template <bool TAP>
+__device__ __forceinline__ void tap_h(float* htap, int I, int rowbase, int row, int nvalid, int col, float h) {
+    if constexpr (TAP) {
+        if (row < nvalid) htap[(int64_t)(rowbase + row) * I + col] = h;
+    }
+}
+
 // Work order of the 128-row-tile GEMMs (items = tile x column block).  The workgroups of
 // one XCD share its L2; all XCDs share the Infinity Cache.  Items come in super-tiles of
 // 8 consecutive tiles x 4 column blocks (32 items, one per workgroup running on an XCD, so

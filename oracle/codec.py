@@ -177,6 +177,73 @@ def decision_margin_rows_128(v: np.ndarray) -> np.ndarray:
     return np.minimum(rel.min(axis=(1, 2)), srel.min(axis=1))
 
 
+def _e4m3_magnitudes() -> np.ndarray:
+    t = e4m3_decode_table()
+    return np.unique(np.abs(t[np.isfinite(t)]))          # 0 .. 448, increasing
+
+
+def near_tie_flips(v: np.ndarray, group: int, tol: float):
+    """The E4M3 re-quantisation decisions of ``quant`` per (row, `group` columns) of v (scale
+    rule above) that lie within relative distance `tol` of going the other way, and what
+    taking each the other way changes in the dequantised row.
+
+    A decision is
+      * an element's rounding: |v| / 2^e within tol * |v| / 2^e of the rounding midpoint
+        between its two nearest magnitudes; the other way is the magnitude across that
+        midpoint (same sign);
+      * a group's scale: its amax within tol * amax of 448 * 2^(e-1) (the other way is e - 1)
+        or of 448 * 2^e (the other way is e + 1); taking it re-quantises the whole group.
+    Returns (elem, scale): elem [R, C] float64 holding dequant(other code) - dequant(code) at
+    the near-tie elements and 0 elsewhere; scale a list of (row, first column, delta [group])
+    for the near-tie scales."""
+    v = np.asarray(v, dtype=np.float64)
+    R, C = v.shape
+    if C % group:
+        raise ValueError(f"columns must be a multiple of {group}")
+    g = v.reshape(R, C // group, group)
+    amax = np.abs(g).max(axis=2)
+    e = scale_exponent(amax)
+    pw = np.ldexp(1.0, e)[:, :, None]
+    s = np.abs(g) / pw
+    mags = _e4m3_magnitudes()
+    mids = (mags[1:] + mags[:-1]) / 2
+    # nearest midpoint m: between mags[m] and mags[m + 1]
+    j = np.clip(np.searchsorted(mids, s), 1, len(mids) - 1)
+    m = np.where(np.abs(s - mids[j - 1]) <= np.abs(s - mids[j]), j - 1, j)
+    near = (s > 0) & (np.abs(s - mids[m]) < tol * s)
+    chosen = np.abs(e4m3_decode(e4m3_encode(g / pw)))
+    other = np.where(chosen == mags[m], mags[m + 1], mags[m])
+    sign = np.where(np.signbit(g), -1.0, 1.0)
+    elem = np.where(near, sign * (other - chosen) * pw, 0.0).reshape(R, C)
+    scale = []
+    pos = amax > 0
+    lo = E4M3_MAX * np.ldexp(1.0, e - 1)
+    hi = E4M3_MAX * np.ldexp(1.0, e)
+    for alt, bound in ((-1, lo), (1, hi)):
+        for r, c in zip(*np.nonzero(pos & (np.abs(amax - bound) < tol * amax))):
+            grp = g[r, c]
+            cur = e4m3_decode(e4m3_encode(np.ldexp(grp, -e[r, c]))) * np.ldexp(1.0, e[r, c])
+            ea = int(np.clip(e[r, c] + alt, -127, 127))
+            new = e4m3_decode(e4m3_encode(np.ldexp(grp, -ea))) * np.ldexp(1.0, ea)
+            scale.append((int(r), int(c) * group, new - cur))
+    return elem, scale
+
+
+def flip_bound(v: np.ndarray, w: np.ndarray, group: int, tol: float) -> np.ndarray:
+    """Largest change of dequant(quant(v)) @ w, element by element, that taking any set of
+    the near-tie decisions of ``near_tie_flips`` the other way can make (each decision's
+    effect added in absolute value).  v [R, C], w [C, N] -> [R, N]."""
+    elem, scale = near_tie_flips(v, group, tol)
+    w = np.asarray(w, dtype=np.float64)
+    out = np.zeros((v.shape[0], w.shape[1]))
+    rows, cols = np.nonzero(elem)
+    if len(rows):
+        np.add.at(out, rows, np.abs(elem[rows, cols])[:, None] * np.abs(w[cols]))
+    for r, c0, d in scale:
+        out[r] += np.abs(d @ w[c0:c0 + len(d)])
+    return out
+
+
 def dequant_rows_128(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     R, C = q.shape
     vals = e4m3_decode(q).reshape(R, C // GROUP, GROUP)

@@ -72,20 +72,28 @@ class QuantizedExperts:
         return self._mem[e]
 
 
-def expert_ffn(xq_rows, xs_rows, q13, s13, q2, s2):
+# Relative distance from a re-quantisation decision within which a float32 computation of h
+# (the matrix cores' accumulation) may take it the other way: the default `tie_tol`.
+TIE_TOL = 3e-5
+
+
+def expert_ffn(xq_rows, xs_rows, q13, s13, q2, s2, tie_tol=TIE_TOL):
     """One expert on a stack of quantised rows.
 
-    Returns (o float64 [R, H], hq uint8 [R, I], hs uint8 [R, I/128], margin float64 [R]),
-    margin being the re-quantisation's decision margin per row
-    (``codec.decision_margin_rows_128``)."""
+    Returns (o float64 [R, H], hq uint8 [R, I], hs uint8 [R, I/128], margin float64 [R],
+    bound float64 [R, H], h float64 [R, I]): margin is the re-quantisation's decision margin per
+    row (``codec.decision_margin_rows_128``); bound is the largest change of o that taking any of
+    the row's near-tie re-quantisation decisions (within tie_tol) the other way can make
+    (``codec.flip_bound``); h is the SwiGLU output before re-quantisation."""
     x = codec.dequant_rows_128(xq_rows, xs_rows)
     w13 = codec.dequant_blocks_128(q13, s13)
     gu = x @ w13
     I = w13.shape[1] // 2
     h = silu(gu[:, :I]) * gu[:, I:]
     hq, hs = codec.quant_rows_128(h)
-    o = codec.dequant_rows_128(hq, hs) @ codec.dequant_blocks_128(q2, s2)
-    return o, hq, hs, codec.decision_margin_rows_128(h)
+    w2 = codec.dequant_blocks_128(q2, s2)
+    o = codec.dequant_rows_128(hq, hs) @ w2
+    return o, hq, hs, codec.decision_margin_rows_128(h), codec.flip_bound(h, w2, codec.GROUP, tie_tol), h
 
 
 def combine(o_flat: np.ndarray, weights: np.ndarray) -> np.ndarray:
@@ -95,15 +103,21 @@ def combine(o_flat: np.ndarray, weights: np.ndarray) -> np.ndarray:
     return (weights[:, :, None] * o).sum(axis=1)
 
 
-def forward(x_f64, ids, weights, experts: QuantizedExperts, tokens=None):
+def forward(x_f64, ids, weights, experts: QuantizedExperts, tokens=None, tie_tol=TIE_TOL, ffn_map=None):
     """Expert step for the given routing.
 
     x_f64 [T, H]: exact values of the bfloat16 hidden state.  ids/weights [T, k].
     tokens: optional array of token indices; only those rows of y are computed.
     Returns a dict with y float64 [len(tokens), H], o [len(tokens)*k, H] in flat
-    (t, j) order, hq/hs by assignment, xq/xs of the tokens, and the re-quantisation
+    (t, j) order, hq/hs and h by assignment, xq/xs of the tokens, the re-quantisation
     decision margin by assignment ("qmargin") and by token ("qmargin_tok", the smallest
-    over its k assignments)."""
+    over its k assignments), and the near-tie flip bounds of o ("o_bound", by assignment) and
+    of y ("y_bound" = sum_j |w[t, j]| * o_bound of slot j): the largest change of each output
+    element that the near-tie re-quantisation decisions (within tie_tol) could make.
+
+    ffn_map: optional callable (jobs, tie_tol) -> results that runs ``expert_ffn`` on each job
+    (e, xq rows, xs rows) with expert e's weights (e.g. in worker processes) and returns the
+    results in job order; by default they run here with ``experts.get(e)``."""
     T, k = ids.shape
     tok = np.arange(T) if tokens is None else np.asarray(tokens)
     xq, xs = codec.quant_rows_128(x_f64[tok])
@@ -111,26 +125,36 @@ def forward(x_f64, ids, weights, experts: QuantizedExperts, tokens=None):
     n = len(tok)
     H = x_f64.shape[1]
     o = np.zeros((n * k, H))
+    ob = np.zeros((n * k, H))
     qm = np.full(n * k, np.inf)
-    hq = hs = None
+    hq = hs = h = None
     flat_ids = sub_ids.reshape(-1)
-    for e in np.unique(flat_ids):
-        rows = np.nonzero(flat_ids == e)[0]            # flat positions (t_local*k + j)
-        q13, s13, q2, s2 = experts.get(int(e))
-        oe, hqe, hse, qme = expert_ffn(xq[rows // k], xs[rows // k], q13, s13, q2, s2)
+    groups = [(int(e), np.nonzero(flat_ids == e)[0]) for e in np.unique(flat_ids)]   # flat positions
+    jobs = [(e, xq[rows // k], xs[rows // k]) for e, rows in groups]
+    if ffn_map is None:
+        results = [expert_ffn(xr, sr, *experts.get(e), tie_tol) for e, xr, sr in jobs]
+    else:
+        results = ffn_map(jobs, tie_tol)
+    for (e, rows), (oe, hqe, hse, qme, obe, he) in zip(groups, results):
         if hq is None:
             hq = np.zeros((n * k, hqe.shape[1]), dtype=np.uint8)
             hs = np.zeros((n * k, hse.shape[1]), dtype=np.uint8)
+            h = np.zeros((n * k, he.shape[1]))
         o[rows] = oe
+        ob[rows] = obe
         hq[rows] = hqe
         hs[rows] = hse
+        h[rows] = he
         qm[rows] = qme
-    y = combine(o, np.asarray(weights, dtype=np.float64)[tok])
-    return {"y": y, "o": o, "hq": hq, "hs": hs, "xq": xq, "xs": xs, "tokens": tok,
-            "qmargin": qm, "qmargin_tok": qm.reshape(n, k).min(axis=1)}
+    w = np.asarray(weights, dtype=np.float64)[tok]
+    y = combine(o, w)
+    return {"y": y, "o": o, "hq": hq, "hs": hs, "h": h, "xq": xq, "xs": xs, "tokens": tok,
+            "qmargin": qm, "qmargin_tok": qm.reshape(n, k).min(axis=1),
+            "o_bound": ob, "y_bound": combine(ob, np.abs(w))}
 
 
-def forward_shared(x_f64, ids, weights, experts: QuantizedExperts, shared: int, tokens=None):
+def forward_shared(x_f64, ids, weights, experts: QuantizedExperts, shared: int, tokens=None, tie_tol=TIE_TOL,
+                   ffn_map=None):
     """Routed experts plus one shared expert that every token runs through, added with
     weight 1 (the metrale grouped FP8 MoE page: the W8A8 gate_up and down launches also take
     the shared expert's gate/up/down projections and write its activations and output
@@ -144,7 +168,7 @@ def forward_shared(x_f64, ids, weights, experts: QuantizedExperts, shared: int, 
     T = ids.shape[0]
     ids_all = np.concatenate([np.asarray(ids), np.full((T, 1), shared, dtype=np.asarray(ids).dtype)], axis=1)
     w_all = np.concatenate([np.asarray(weights, dtype=np.float64), np.ones((T, 1))], axis=1)
-    return forward(x_f64, ids_all, w_all, experts, tokens)
+    return forward(x_f64, ids_all, w_all, experts, tokens, tie_tol, ffn_map)
 
 
 def route_workload(inputs: dict, p: routing.RouteParams, prelude=None):

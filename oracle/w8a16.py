@@ -45,33 +45,44 @@ def bf16_rne(v) -> np.ndarray:
 
 def expert_ffn(x_rows, q13, s13, q2, s2):
     """One expert on a stack of bf16 activation rows (float64 values).
-    Returns (o float64 [R, H], hb float64 [R, I] holding bf16 values)."""
+    Returns (o float64 [R, H], hb float64 [R, I] holding bf16 values, h float64 [R, I] before
+    the rounding)."""
     w13 = codec.dequant_blocks_128(q13, s13)
     gu = np.asarray(x_rows, dtype=np.float64) @ w13
     I = w13.shape[1] // 2
-    hb = bf16_rne(moe.silu(gu[:, :I]) * gu[:, I:])
-    return hb @ codec.dequant_blocks_128(q2, s2), hb
+    h = moe.silu(gu[:, :I]) * gu[:, I:]
+    hb = bf16_rne(h)
+    return hb @ codec.dequant_blocks_128(q2, s2), hb, h
 
 
-def forward(x_f64, ids, weights, experts: moe.QuantizedExperts, tokens=None):
+def forward(x_f64, ids, weights, experts: moe.QuantizedExperts, tokens=None, ffn_map=None):
     """W8A16 expert step for the given routing (same experts object and result layout as
     ``oracle.moe.forward``).  There is no activation re-quantisation, so the decision
-    margins ("qmargin", "qmargin_tok") are infinite: no row is excused from the output bar."""
+    margins ("qmargin", "qmargin_tok") are infinite and the flip bounds ("o_bound", "y_bound")
+    zero: no output element is excused from the output bar.  ffn_map as in
+    ``oracle.moe.forward``, with jobs (e, x rows, None) for this module's ``expert_ffn``."""
     T, k = ids.shape
     tok = np.arange(T) if tokens is None else np.asarray(tokens)
     x = np.asarray(x_f64, dtype=np.float64)[tok]
     n = len(tok)
     H = x.shape[1]
     o = np.zeros((n * k, H))
-    hb = None
+    hb = h = None
     flat_ids = np.asarray(ids)[tok].reshape(-1)
-    for e in np.unique(flat_ids):
-        rows = np.nonzero(flat_ids == e)[0]            # flat positions (t_local*k + j)
-        oe, hbe = expert_ffn(x[rows // k], *experts.get(int(e)))
+    groups = [(int(e), np.nonzero(flat_ids == e)[0]) for e in np.unique(flat_ids)]   # flat positions
+    jobs = [(e, x[rows // k], None) for e, rows in groups]
+    if ffn_map is None:
+        results = [expert_ffn(xr, *experts.get(e)) for e, xr, _ in jobs]
+    else:
+        results = ffn_map(jobs, None)
+    for (e, rows), (oe, hbe, he) in zip(groups, results):
         if hb is None:
             hb = np.zeros((n * k, hbe.shape[1]))
+            h = np.zeros((n * k, he.shape[1]))
         o[rows] = oe
         hb[rows] = hbe
+        h[rows] = he
     y = moe.combine(o, np.asarray(weights, dtype=np.float64)[tok])
     qm = np.full(n * k, np.inf)
-    return {"y": y, "o": o, "hb": hb, "tokens": tok, "qmargin": qm, "qmargin_tok": qm.reshape(n, k).min(axis=1)}
+    return {"y": y, "o": o, "hb": hb, "h": h, "tokens": tok, "qmargin": qm, "qmargin_tok": qm.reshape(n, k).min(axis=1),
+            "o_bound": np.zeros_like(o), "y_bound": np.zeros_like(y)}

@@ -6,6 +6,12 @@ of the float32 weights; the GPU path quantises with moe_quant_weight_blocks.
 """
 from __future__ import annotations
 
+import atexit
+import collections
+import concurrent.futures as cf
+import multiprocessing
+import os
+
 import numpy as np
 import torch
 
@@ -23,6 +29,103 @@ def oracle_params(wl: W.Workload) -> orouting.RouteParams:
 def device_params(wl: W.Workload):
     return M.route_params(wl.E, wl.k, wl.scoring, wl.renormalize, wl.group_count, wl.k_group,
                           wl.group_select_mode, wl.routed_scaling_factor)
+
+
+# ---- the oracle over many experts.  Worker processes (spawned: fresh interpreters that never
+# touch the GPU) quantise each expert's regenerated float32 weights with the oracle's codec
+# and run the oracle's expert FFN on its rows; the quantised weights come back and are kept
+# here for the next call on the same workload (the last two workloads are kept).
+_POOL = None
+_QCACHE: "collections.OrderedDict" = collections.OrderedDict()
+
+
+def oracle_workers() -> int:
+    return int(os.environ.get("ORACLE_WORKERS", str(max(1, min(16, len(os.sched_getaffinity(0)))))))
+
+
+def _worker_init():
+    # one thread per worker process: the parallelism is across experts
+    torch.set_num_threads(1)
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(limits=1)
+    except ImportError:
+        pass
+
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        _POOL = cf.ProcessPoolExecutor(oracle_workers(), mp_context=multiprocessing.get_context("spawn"),
+                                       initializer=_worker_init)
+        atexit.register(_POOL.shutdown, wait=False, cancel_futures=True)
+    return _POOL
+
+
+def _mx_fmt(scheme: str) -> str:
+    from oracle import mx as omx
+    return omx.FMT_E2M1 if scheme == "w4a8" else omx.FMT_E4M3
+
+
+def _quantize(wl: W.Workload, scheme: str, e: int):
+    """Expert e's weights quantised by the oracle for `scheme` (W8A16 reads the FP8 ones)."""
+    from oracle import mx as omx
+    w13 = W.expert_weight_f32(wl, "w13", e).numpy()
+    w2 = W.expert_weight_f32(wl, "w2", e).numpy()
+    if scheme in ("fp8", "w8a16"):
+        return omoe.QuantizedExperts(lambda _: (w13, w2)).quantize(e)
+    return omx.QuantizedExpertsMX(lambda _: (w13, w2), _mx_fmt(scheme)).quantize(e)
+
+
+def _expert_job(args):
+    """Worker side: one expert's FFN in the oracle (quantising its weights first if needed)."""
+    from oracle import mx as omx
+    from oracle import w8a16 as ow16
+    wl, scheme, e, q, xr, sr, tie_tol = args
+    fresh = q is None
+    if fresh:
+        q = _quantize(wl, scheme, e)
+    if scheme == "fp8":
+        r = omoe.expert_ffn(xr, sr, *q, tie_tol)
+    elif scheme == "w8a16":
+        r = ow16.expert_ffn(xr, *q)
+    else:
+        r = omx.expert_ffn(xr, sr, *q, _mx_fmt(scheme), tie_tol)
+    return (q if fresh else None), r
+
+
+def oracle_ffn_map(wl: W.Workload, scheme: str = "fp8"):
+    """An ``ffn_map`` for the oracle's forward functions that runs the per-expert FFNs of
+    workload `wl` under quantisation scheme `scheme` ("fp8", "mxfp8", "w4a8", "w8a16") in the
+    worker processes."""
+    key = (wl, "fp8" if scheme == "w8a16" else scheme)
+    cache = _QCACHE.setdefault(key, {})
+    _QCACHE.move_to_end(key)
+    while len(_QCACHE) > 2:
+        _QCACHE.popitem(last=False)
+
+    def ffn_map(jobs, tie_tol):
+        args = [(wl, scheme, e, cache.get(e), xr, sr, tie_tol) for e, xr, sr in jobs]
+        out = []
+        for (e, _, _), (q, r) in zip(jobs, _pool().map(_expert_job, args)):
+            if q is not None:
+                cache[e] = q
+            out.append(r)
+        return out
+    return ffn_map
+
+
+def item_sample_tokens(ids: np.ndarray, E: int, every: int = 64, tile: int = 128) -> np.ndarray:
+    """Tokens whose rows cover every work item of the grouped GEMMs: in the oracle's stable
+    permutation of `ids` [T, k] over E experts, the middle row of each `tile`-row tile of each
+    expert (every 128-row tile, so both tiles of a 256-row item), plus every `every`-th token."""
+    T, k = ids.shape
+    counts, offsets, sorted_assign, _ = orouting.permute(ids, E)
+    rows = [offsets[e] + m + min(tile // 2, (counts[e] - m) // 2)
+            for e in range(E) for m in range(0, int(counts[e]), tile)]
+    tok = set((sorted_assign[np.asarray(rows, dtype=np.int64)] // k).tolist()) if rows else set()
+    tok |= set(range(0, T, every))
+    return np.array(sorted(tok), dtype=np.int64)
 
 
 def oracle_experts(wl: W.Workload, cache: int = 8) -> omoe.QuantizedExperts:
@@ -119,34 +222,32 @@ def rel_errors(y_dev: np.ndarray, y_ref: np.ndarray):
     return fro, mx
 
 
-# Re-quantisation near-ties.  The device computes h in float32 (matrix-core accumulation
-# carries relative error up to ~1e-5), so where the oracle's float64 h puts an E4M3
-# decision within this relative distance of a rounding midpoint or a scale boundary the
-# device may take that one code the other way.  One flipped code moves the output row by
-# an E4M3 spacing of that h element times a row of w2; with a narrow down projection
-# (I = 128) that can exceed 2e-2 of max |y| on its own.
-QMARGIN = 3e-5
-
-
-def assert_output_close(y_dev: np.ndarray, y_ref: np.ndarray, what: str = "", qmargin=None):
+def assert_output_close(y_dev: np.ndarray, y_ref: np.ndarray, what: str = "", bound=None):
     """The output bar: relative Frobenius error <= 5e-3 and max |err| <= 2e-2 * max |y|,
-    against the oracle's unrounded float64 y.  With qmargin (the oracle's per-row
-    re-quantisation decision margin) a row whose own max error exceeds the bar passes only
-    if one of its decisions is a near-tie (qmargin < QMARGIN); the Frobenius bar always
-    covers every row."""
+    against the oracle's unrounded float64 y.
+
+    `bound` (the oracle's "y_bound" / "o_bound", same shape as y) is the near-tie allowance:
+    for each output element, the largest change that the re-quantisation decisions lying
+    within the oracle's tie tolerance of a rounding midpoint or scale boundary could make if
+    the device's float32 h took them the other way (each decision's exact effect, added in
+    absolute value).  The max-error bar then applies to the error beyond that allowance,
+    element by element; the Frobenius bar always applies to the raw error.  The number of rows
+    whose raw error needed the allowance is printed."""
+    y_dev = np.asarray(y_dev, dtype=np.float64)
     fro, mx = rel_errors(y_dev, y_ref)
-    if qmargin is None or mx <= 2e-2:
+    if bound is None or mx <= 2e-2:
         assert fro <= 5e-3 and mx <= 2e-2, f"{what}: rel fro {fro:.3e}, rel max {mx:.3e}"
         return fro, mx
     scale = np.abs(y_ref).max()
-    row_mx = np.abs(np.asarray(y_dev, dtype=np.float64) - y_ref).max(axis=1) / scale
-    bad = row_mx > 2e-2
-    near = np.asarray(qmargin) < QMARGIN
+    d = np.abs(y_dev - y_ref)
+    excess = np.maximum(d - np.asarray(bound), 0.0)
+    mx_ex = excess.max() / scale
+    rows = int((d.max(axis=1) / scale > 2e-2).sum())
+    print(f"  {what}: {rows} of {len(d)} rows beyond rel max 2e-2 before the near-tie allowance "
+          f"(raw rel max {mx:.3e}); beyond the allowance rel max {mx_ex:.3e}", flush=True)
     assert fro <= 5e-3, f"{what}: rel fro {fro:.3e}"
-    assert np.all(near[bad]), f"{what}: rows {np.nonzero(bad & ~near)[0][:8]} exceed rel max 2e-2 without a near-tie"
-    mx_kept = row_mx[~near].max() if (~near).any() else 0.0
-    assert mx_kept <= 2e-2, f"{what}: rel max {mx_kept:.3e} on rows without near-ties"
-    return fro, mx_kept
+    assert mx_ex <= 2e-2, f"{what}: rel max {mx_ex:.3e} beyond the near-tie allowance"
+    return fro, mx_ex
 
 
 def bf16_to_f64(t: torch.Tensor) -> np.ndarray:

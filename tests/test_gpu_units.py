@@ -168,6 +168,21 @@ def test_route_gate_prelude():
     assert n_amb == 0
 
 
+def test_route_gate_prelude_golden_hand_cases():
+    # the hand-worked prelude cases of tests/golden/prelude_hand.txt through the device's
+    # RMSNorm + router + top-k + softmax-over-selected kernels (x exact in bf16)
+    import test_oracle_routing as tor
+    for name, x, nw, eps, W_r, pe, k, ids_exp, w_exp in tor._golden_prelude():
+        E, H = W_r.shape
+        xd = torch.from_numpy(x[None]).to(torch.bfloat16).to(DEV)
+        assert np.array_equal(xd.float().cpu().numpy()[0], x)
+        pre = M.Prelude(torch.from_numpy(nw).float().to(DEV), torch.from_numpy(W_r).float().contiguous().to(DEV),
+                        torch.from_numpy(pe).float().to(DEV), float(eps))
+        got = M.moe_route(M.route_params(E, k), 1, hidden_states=xd, prelude=pre)
+        assert got["topk_ids"].cpu().numpy()[0].tolist() == ids_exp, name
+        np.testing.assert_allclose(got["topk_weights"].cpu().numpy()[0], w_exp, rtol=2e-6, err_msg=name)
+
+
 def test_dispatch_of_given_ids_with_skew_and_empty_experts():
     # every token on expert 3 first, most experts empty; more than one dispatch chunk
     T, k, E = 3000, 4, 40

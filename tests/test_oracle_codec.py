@@ -176,3 +176,95 @@ def test_decision_margin_bounds_single_element_perturbations():
                     elif not same:
                         changed_above = True
         assert changed_above, r
+
+
+def _dq(v, group):
+    """dequant(quant(v)) per (row, group) through the pinned quantisers."""
+    if group == 128:
+        return codec.dequant_rows_128(*codec.quant_rows_128(v))
+    from oracle import mx
+    return mx.dequant_rows_32(*mx.quant_rows_32(v))
+
+
+def test_near_tie_flips_hand_values():
+    # 1.0625 sits on the midpoint of 1.0 and 1.125 (group amax 320, e = 0, no scale tie):
+    # round to nearest even takes 1.0 (code 0x38), the other way is 1.125; a negative copy
+    # flips to -1.125
+    row = np.ones(128)
+    row[0] = 320.0
+    row[5] = 1.0625
+    row[9] = -1.0625
+    elem, scale = codec.near_tie_flips(row[None], 128, 3e-5)
+    assert elem[0, 5] == 0.125 and elem[0, 9] == -0.125
+    assert np.count_nonzero(elem) == 2 and scale == []
+    # amax on the scale boundary 448 * 2^3: the other way is e + 1 = 4 (every code re-chosen)
+    b = row * 8.0
+    b[0] = 448.0 * 8.0
+    b[5] = b[9] = 8.0
+    elem, scale = codec.near_tie_flips(b[None], 128, 3e-5)
+    assert np.count_nonzero(elem) == 0 and len(scale) == 1
+    r, c0, d = scale[0]
+    assert (r, c0) == (0, 0)
+    cur = _dq(b[None], 128)[0]
+    alt = codec.e4m3_decode(codec.e4m3_encode(b / 16.0)) * 16.0
+    assert np.array_equal(d, alt - cur)
+
+
+@pytest.mark.parametrize("group", [128, 32])
+def test_near_tie_flips_against_perturbations(group):
+    # brute force through the pinned quantiser: every flagged element decision flips when its
+    # element alone moves by a relative amount below tol (in the direction of its midpoint),
+    # and the dequantised row then changes by exactly the reported delta; no unflagged element
+    # changes its code under any single-element move of relative size below tol
+    tol = 1e-3     # wide, so that random rows hold near ties
+    rng = np.random.default_rng(11)
+    R, C = 4, 256
+    v = rng.standard_normal((R, C)) * np.exp2(rng.integers(-4, 5, size=(R, 1)))
+    elem, scale = codec.near_tie_flips(v, group, tol)
+    assert np.count_nonzero(elem) > 5
+    base = _dq(v, group)
+    scale_groups = {(r, c0) for r, c0, _ in scale}
+    for r in range(R):
+        for i in range(C):
+            if (r, i - i % group) in scale_groups:
+                continue
+            flips = []
+            for f in (1 - tol * 0.999, 1 + tol * 0.999):
+                w = v[r].copy()
+                w[i] *= f
+                d = _dq(w[None], group)[0] - base[r]
+                if np.any(d != 0):
+                    flips.append(d)
+            if elem[r, i] != 0:
+                assert flips, (r, i)
+                for d in flips:   # only the element itself moved, by the reported delta
+                    assert d[i] == elem[r, i] and np.count_nonzero(d) == 1
+            else:
+                # a move may change the group's scale only if that is a flagged scale tie
+                assert not flips, (r, i)
+
+
+def test_flip_bound_covers_every_subset_and_is_exact_for_one():
+    # brute force over all subsets of a row's near-tie element decisions: the change of
+    # dequant(quant(v)) @ w never exceeds the bound, and with a single decision it equals it
+    tol = 2e-3
+    rng = np.random.default_rng(5)
+    v = rng.standard_normal((1, 128)) * 3.0
+    w = rng.standard_normal((128, 6))
+    elem, scale = codec.near_tie_flips(v, 128, tol)
+    idx = np.nonzero(elem[0])[0]
+    assert scale == [] and 2 <= len(idx) <= 10
+    bound = codec.flip_bound(v, w, 128, tol)[0]
+    base = _dq(v, 128)[0] @ w
+    import itertools
+    for n in range(1, len(idx) + 1):
+        for sub in itertools.combinations(idx, n):
+            hq = _dq(v, 128)[0].copy()
+            hq[list(sub)] += elem[0, list(sub)]
+            assert np.all(np.abs(hq @ w - base) <= bound * (1 + 1e-12))
+    one = v.copy()
+    keep = idx[0]
+    one[0, idx[1:]] = np.round(one[0, idx[1:]])          # move the other ties away
+    e1, s1 = codec.near_tie_flips(one, 128, tol)
+    if np.count_nonzero(e1) == 1 and not s1:
+        assert np.allclose(codec.flip_bound(one, w, 128, tol)[0], np.abs(e1[0, keep] * w[keep]))

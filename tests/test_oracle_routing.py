@@ -161,10 +161,14 @@ def test_prelude_matches_torch_rmsnorm_and_matmul():
     pe = rng.uniform(0.5, 1.5, 32)
     ids, w, l2, margin = routing.route_prelude(x, nw, W, pe, 1e-6, 4)
     assert np.array_equal(l, l2)
-    assert list(ids[0]) == brute_topk(l[0], 4)
-    sel = np.take_along_axis(l, ids.astype(np.int64), 1)
-    sm = np.exp(sel) / np.exp(sel).sum(1, keepdims=True)
-    np.testing.assert_allclose(w, sm * pe[ids], rtol=1e-12)
+    for t in range(len(x)):
+        assert list(ids[t]) == brute_topk(l[t], 4), t
+    # the weights through torch: the page's softmax over all experts, top-k, divide by the
+    # selected sum (equal to the softmax over the selected logits), times the scale
+    p_all = torch.softmax(torch.from_numpy(l), dim=1)
+    v, i = torch.topk(p_all, 4, dim=1)
+    assert np.array_equal(i.numpy(), ids)
+    np.testing.assert_allclose(w, (v / v.sum(1, keepdim=True)).numpy() * pe[ids], rtol=1e-12)
     assert (margin > 0).all()
 
 
@@ -182,3 +186,29 @@ def test_permute_invariants_and_stable_sort():
         for e in range(E):
             seg = sa[offsets[e]:offsets[e + 1]]
             assert (flat[seg] == e).all() and (np.diff(seg) > 0).all()
+
+
+def _golden_prelude():
+    def val(tok):
+        return float(np.log(float(tok[2:]))) if tok.startswith("ln") else float(tok)
+    cases = []
+    with open(os.path.join(os.path.dirname(__file__), "golden", "prelude_hand.txt")) as f:
+        for ln in f:
+            if not ln.strip() or ln.startswith("#"):
+                continue
+            name, x, nw, eps, rows, pe, k, ids, w = [c.strip() for c in ln.split("|")]
+            cases.append((name, np.array([val(t) for t in x.split()]), np.array([val(t) for t in nw.split()]),
+                          float(eps), np.array([[val(t) for t in r.split()] for r in rows.split(";")]),
+                          np.array([val(t) for t in pe.split()]), int(k), [int(t) for t in ids.split()],
+                          [float(t) for t in w.split()]))
+    return cases
+
+
+@pytest.mark.parametrize("case", _golden_prelude(), ids=lambda c: c[0])
+def test_prelude_golden_hand_cases(case):
+    # tests/golden/prelude_hand.txt: RMSNorm, router rows, top-k with the lower-id tie rule,
+    # softmax over the selected logits and the per-expert scale, all worked by hand
+    name, x, nw, eps, W_r, pe, k, ids_exp, w_exp = case
+    ids, w, l, margin = routing.route_prelude(x[None], nw, W_r, pe, eps, k)
+    assert ids[0].tolist() == ids_exp, name
+    assert np.allclose(w[0], w_exp, rtol=1e-12, atol=0), (name, w[0])
