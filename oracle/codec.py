@@ -182,17 +182,19 @@ def _e4m3_magnitudes() -> np.ndarray:
     return np.unique(np.abs(t[np.isfinite(t)]))          # 0 .. 448, increasing
 
 
-def near_tie_flips(v: np.ndarray, group: int, tol: float):
+def near_tie_flips(v: np.ndarray, group: int, tol):
     """The E4M3 re-quantisation decisions of ``quant`` per (row, `group` columns) of v (scale
-    rule above) that lie within relative distance `tol` of going the other way, and what
-    taking each the other way changes in the dequantised row.
+    rule above) that a computation of v carrying an absolute error up to `tol` (an array
+    broadcastable to v, or a number) could take the other way, and what taking each the other
+    way changes in the dequantised row.
 
     A decision is
-      * an element's rounding: |v| / 2^e within tol * |v| / 2^e of the rounding midpoint
-        between its two nearest magnitudes; the other way is the magnitude across that
+      * an element's rounding: |v| within tol of the rounding midpoint (times 2^e) between
+        the two magnitudes nearest to |v| / 2^e; the other way is the magnitude across that
         midpoint (same sign);
-      * a group's scale: its amax within tol * amax of 448 * 2^(e-1) (the other way is e - 1)
-        or of 448 * 2^e (the other way is e + 1); taking it re-quantises the whole group.
+      * a group's scale: its amax within the group's largest tol of 448 * 2^(e-1) (the other
+        way is e - 1) or of 448 * 2^e (the other way is e + 1); taking it re-quantises the
+        whole group.
     Returns (elem, scale): elem [R, C] float64 holding dequant(other code) - dequant(code) at
     the near-tie elements and 0 elsewhere; scale a list of (row, first column, delta [group])
     for the near-tie scales."""
@@ -200,6 +202,7 @@ def near_tie_flips(v: np.ndarray, group: int, tol: float):
     R, C = v.shape
     if C % group:
         raise ValueError(f"columns must be a multiple of {group}")
+    tol = np.broadcast_to(np.asarray(tol, dtype=np.float64), v.shape).reshape(R, C // group, group)
     g = v.reshape(R, C // group, group)
     amax = np.abs(g).max(axis=2)
     e = scale_exponent(amax)
@@ -210,17 +213,18 @@ def near_tie_flips(v: np.ndarray, group: int, tol: float):
     # nearest midpoint m: between mags[m] and mags[m + 1]
     j = np.clip(np.searchsorted(mids, s), 1, len(mids) - 1)
     m = np.where(np.abs(s - mids[j - 1]) <= np.abs(s - mids[j]), j - 1, j)
-    near = (s > 0) & (np.abs(s - mids[m]) < tol * s)
+    near = (s > 0) & (np.abs(s - mids[m]) * pw < tol)
     chosen = np.abs(e4m3_decode(e4m3_encode(g / pw)))
     other = np.where(chosen == mags[m], mags[m + 1], mags[m])
     sign = np.where(np.signbit(g), -1.0, 1.0)
     elem = np.where(near, sign * (other - chosen) * pw, 0.0).reshape(R, C)
     scale = []
     pos = amax > 0
+    gtol = tol.max(axis=2)
     lo = E4M3_MAX * np.ldexp(1.0, e - 1)
     hi = E4M3_MAX * np.ldexp(1.0, e)
     for alt, bound in ((-1, lo), (1, hi)):
-        for r, c in zip(*np.nonzero(pos & (np.abs(amax - bound) < tol * amax))):
+        for r, c in zip(*np.nonzero(pos & (np.abs(amax - bound) < gtol))):
             grp = g[r, c]
             cur = e4m3_decode(e4m3_encode(np.ldexp(grp, -e[r, c]))) * np.ldexp(1.0, e[r, c])
             ea = int(np.clip(e[r, c] + alt, -127, 127))
@@ -229,10 +233,10 @@ def near_tie_flips(v: np.ndarray, group: int, tol: float):
     return elem, scale
 
 
-def flip_bound(v: np.ndarray, w: np.ndarray, group: int, tol: float) -> np.ndarray:
+def flip_bound(v: np.ndarray, w: np.ndarray, group: int, tol) -> np.ndarray:
     """Largest change of dequant(quant(v)) @ w, element by element, that taking any set of
-    the near-tie decisions of ``near_tie_flips`` the other way can make (each decision's
-    effect added in absolute value).  v [R, C], w [C, N] -> [R, N]."""
+    the near-tie decisions of ``near_tie_flips`` (absolute tolerance `tol`) the other way can
+    make (each decision's effect added in absolute value).  v [R, C], w [C, N] -> [R, N]."""
     elem, scale = near_tie_flips(v, group, tol)
     w = np.asarray(w, dtype=np.float64)
     out = np.zeros((v.shape[0], w.shape[1]))

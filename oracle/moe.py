@@ -72,28 +72,46 @@ class QuantizedExperts:
         return self._mem[e]
 
 
-# Relative distance from a re-quantisation decision within which a float32 computation of h
-# (the matrix cores' accumulation) may take it the other way: the default `tie_tol`.
-TIE_TOL = 3e-5
+# Accumulation error of a computed dot product relative to the Euclidean norm of its products
+# (the float32 matrix-core accumulation, whose internal sums are not exact float32 sums; the
+# rounding errors of a long sum add up like a random walk, so their total scales with the norm
+# of the terms rather than with the sum of their magnitudes): the default `acc_err` of the h
+# error model below.
+ACC_ERR = 2.0 ** -13
 
 
-def expert_ffn(xq_rows, xs_rows, q13, s13, q2, s2, tie_tol=TIE_TOL):
+def h_error_bound(x, w13, gu, acc_err=ACC_ERR):
+    """Per element, how far a computation of h = silu(g) * u is taken to be from the exact
+    value: each gate and up sum g, u carries an error up to acc_err * sqrt(sum_i (x_i w_i)^2)
+    and the SwiGLU itself a relative acc_err; to first order
+    |dh| <= |silu'(g) u| dg + |silu(g)| du + acc_err |h|, silu'(g) = s (1 + g (1 - s)),
+    s = 1 / (1 + exp(-g)).  x [R, K], w13 [K, 2I], gu = x @ w13 -> [R, I]."""
+    S = np.sqrt((x * x) @ (w13 * w13))
+    I = w13.shape[1] // 2
+    g, u = gu[:, :I], gu[:, I:]
+    s = 1.0 / (1.0 + np.exp(-g))
+    return acc_err * (np.abs(s * (1.0 + g * (1.0 - s)) * u) * S[:, :I] + np.abs(g * s) * S[:, I:] + np.abs(g * s * u))
+
+
+def expert_ffn(xq_rows, xs_rows, q13, s13, q2, s2, acc_err=ACC_ERR):
     """One expert on a stack of quantised rows.
 
     Returns (o float64 [R, H], hq uint8 [R, I], hs uint8 [R, I/128], margin float64 [R],
-    bound float64 [R, H], h float64 [R, I]): margin is the re-quantisation's decision margin per
-    row (``codec.decision_margin_rows_128``); bound is the largest change of o that taking any of
-    the row's near-tie re-quantisation decisions (within tie_tol) the other way can make
-    (``codec.flip_bound``); h is the SwiGLU output before re-quantisation."""
+    bound float64 [R, H], h float64 [R, I], h_err float64 [R, I]): margin is the
+    re-quantisation's decision margin per row (``codec.decision_margin_rows_128``); h is the
+    SwiGLU output before re-quantisation and h_err its error bound (``h_error_bound``); bound is
+    the largest change of o that taking the other way any re-quantisation decision lying within
+    h_err of a tie can make (``codec.flip_bound``)."""
     x = codec.dequant_rows_128(xq_rows, xs_rows)
     w13 = codec.dequant_blocks_128(q13, s13)
     gu = x @ w13
     I = w13.shape[1] // 2
     h = silu(gu[:, :I]) * gu[:, I:]
+    h_err = h_error_bound(x, w13, gu, acc_err)
     hq, hs = codec.quant_rows_128(h)
     w2 = codec.dequant_blocks_128(q2, s2)
     o = codec.dequant_rows_128(hq, hs) @ w2
-    return o, hq, hs, codec.decision_margin_rows_128(h), codec.flip_bound(h, w2, codec.GROUP, tie_tol), h
+    return o, hq, hs, codec.decision_margin_rows_128(h), codec.flip_bound(h, w2, codec.GROUP, h_err), h, h_err
 
 
 def combine(o_flat: np.ndarray, weights: np.ndarray) -> np.ndarray:
@@ -103,19 +121,20 @@ def combine(o_flat: np.ndarray, weights: np.ndarray) -> np.ndarray:
     return (weights[:, :, None] * o).sum(axis=1)
 
 
-def forward(x_f64, ids, weights, experts: QuantizedExperts, tokens=None, tie_tol=TIE_TOL, ffn_map=None):
+def forward(x_f64, ids, weights, experts: QuantizedExperts, tokens=None, acc_err=ACC_ERR, ffn_map=None):
     """Expert step for the given routing.
 
     x_f64 [T, H]: exact values of the bfloat16 hidden state.  ids/weights [T, k].
     tokens: optional array of token indices; only those rows of y are computed.
     Returns a dict with y float64 [len(tokens), H], o [len(tokens)*k, H] in flat
-    (t, j) order, hq/hs and h by assignment, xq/xs of the tokens, the re-quantisation
-    decision margin by assignment ("qmargin") and by token ("qmargin_tok", the smallest
-    over its k assignments), and the near-tie flip bounds of o ("o_bound", by assignment) and
-    of y ("y_bound" = sum_j |w[t, j]| * o_bound of slot j): the largest change of each output
-    element that the near-tie re-quantisation decisions (within tie_tol) could make.
+    (t, j) order, hq/hs, h and its error bound h_err by assignment, xq/xs of the tokens, the
+    re-quantisation decision margin by assignment ("qmargin") and by token ("qmargin_tok", the
+    smallest over its k assignments), and the near-tie flip bounds of o ("o_bound", by
+    assignment) and of y ("y_bound" = sum_j |w[t, j]| * o_bound of slot j): the largest change
+    of each output element that re-quantisation decisions lying within h_err of a tie could
+    make (``expert_ffn``).
 
-    ffn_map: optional callable (jobs, tie_tol) -> results that runs ``expert_ffn`` on each job
+    ffn_map: optional callable (jobs, acc_err) -> results that runs ``expert_ffn`` on each job
     (e, xq rows, xs rows) with expert e's weights (e.g. in worker processes) and returns the
     results in job order; by default they run here with ``experts.get(e)``."""
     T, k = ids.shape
@@ -127,33 +146,35 @@ def forward(x_f64, ids, weights, experts: QuantizedExperts, tokens=None, tie_tol
     o = np.zeros((n * k, H))
     ob = np.zeros((n * k, H))
     qm = np.full(n * k, np.inf)
-    hq = hs = h = None
+    hq = hs = h = h_err = None
     flat_ids = sub_ids.reshape(-1)
     groups = [(int(e), np.nonzero(flat_ids == e)[0]) for e in np.unique(flat_ids)]   # flat positions
     jobs = [(e, xq[rows // k], xs[rows // k]) for e, rows in groups]
     if ffn_map is None:
-        results = [expert_ffn(xr, sr, *experts.get(e), tie_tol) for e, xr, sr in jobs]
+        results = [expert_ffn(xr, sr, *experts.get(e), acc_err) for e, xr, sr in jobs]
     else:
-        results = ffn_map(jobs, tie_tol)
-    for (e, rows), (oe, hqe, hse, qme, obe, he) in zip(groups, results):
+        results = ffn_map(jobs, acc_err)
+    for (e, rows), (oe, hqe, hse, qme, obe, he, hee) in zip(groups, results):
         if hq is None:
             hq = np.zeros((n * k, hqe.shape[1]), dtype=np.uint8)
             hs = np.zeros((n * k, hse.shape[1]), dtype=np.uint8)
             h = np.zeros((n * k, he.shape[1]))
+            h_err = np.zeros((n * k, he.shape[1]))
         o[rows] = oe
         ob[rows] = obe
         hq[rows] = hqe
         hs[rows] = hse
         h[rows] = he
+        h_err[rows] = hee
         qm[rows] = qme
     w = np.asarray(weights, dtype=np.float64)[tok]
     y = combine(o, w)
-    return {"y": y, "o": o, "hq": hq, "hs": hs, "h": h, "xq": xq, "xs": xs, "tokens": tok,
+    return {"y": y, "o": o, "hq": hq, "hs": hs, "h": h, "h_err": h_err, "xq": xq, "xs": xs, "tokens": tok,
             "qmargin": qm, "qmargin_tok": qm.reshape(n, k).min(axis=1),
             "o_bound": ob, "y_bound": combine(ob, np.abs(w))}
 
 
-def forward_shared(x_f64, ids, weights, experts: QuantizedExperts, shared: int, tokens=None, tie_tol=TIE_TOL,
+def forward_shared(x_f64, ids, weights, experts: QuantizedExperts, shared: int, tokens=None, acc_err=ACC_ERR,
                    ffn_map=None):
     """Routed experts plus one shared expert that every token runs through, added with
     weight 1 (the metrale grouped FP8 MoE page: the W8A8 gate_up and down launches also take
@@ -168,7 +189,7 @@ def forward_shared(x_f64, ids, weights, experts: QuantizedExperts, shared: int, 
     T = ids.shape[0]
     ids_all = np.concatenate([np.asarray(ids), np.full((T, 1), shared, dtype=np.asarray(ids).dtype)], axis=1)
     w_all = np.concatenate([np.asarray(weights, dtype=np.float64), np.ones((T, 1))], axis=1)
-    return forward(x_f64, ids_all, w_all, experts, tokens, tie_tol, ffn_map)
+    return forward(x_f64, ids_all, w_all, experts, tokens, acc_err, ffn_map)
 
 
 def route_workload(inputs: dict, p: routing.RouteParams, prelude=None):

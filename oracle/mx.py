@@ -209,24 +209,26 @@ class QuantizedExpertsMX(moe.QuantizedExperts):
         return q13, s13, q2, s2
 
 
-def expert_ffn(xq_rows, xs_rows, q13, s13, q2, s2, fmt: str, tie_tol=moe.TIE_TOL):
+def expert_ffn(xq_rows, xs_rows, q13, s13, q2, s2, fmt: str, acc_err=moe.ACC_ERR):
     """One expert on a stack of MX-quantised rows; weights in `fmt`.
     Returns (o float64 [R, H], hq uint8 [R, I], hs uint8 [R, I/32], margin float64 [R],
-    bound float64 [R, H], h float64 [R, I]): margin is the re-quantisation's decision margin per
-    row (``decision_margin_rows_32``), bound the largest change of o its near-tie decisions
-    (within tie_tol) could make (``codec.flip_bound`` on 32-column groups), h the SwiGLU output."""
+    bound float64 [R, H], h float64 [R, I], h_err float64 [R, I]): margin is the
+    re-quantisation's decision margin per row (``decision_margin_rows_32``), h the SwiGLU output
+    and h_err its error bound (``oracle.moe.h_error_bound``), bound the largest change of o the
+    decisions within h_err of a tie could make (``codec.flip_bound`` on 32-column groups)."""
     x = dequant_rows_32(xq_rows, xs_rows)
     w13 = dequant_weight_k32(q13, s13, fmt)
     gu = x @ w13
     I = w13.shape[1] // 2
     h = moe.silu(gu[:, :I]) * gu[:, I:]
+    h_err = moe.h_error_bound(x, w13, gu, acc_err)
     hq, hs = quant_rows_32(h)
     w2 = dequant_weight_k32(q2, s2, fmt)
     o = dequant_rows_32(hq, hs) @ w2
-    return o, hq, hs, decision_margin_rows_32(h), codec.flip_bound(h, w2, MX, tie_tol), h
+    return o, hq, hs, decision_margin_rows_32(h), codec.flip_bound(h, w2, MX, h_err), h, h_err
 
 
-def forward(x_f64, ids, weights, experts: QuantizedExpertsMX, tokens=None, tie_tol=moe.TIE_TOL, ffn_map=None):
+def forward(x_f64, ids, weights, experts: QuantizedExpertsMX, tokens=None, acc_err=moe.ACC_ERR, ffn_map=None):
     """Expert step for the given routing with MX activations and `experts.fmt` weights.
     Same contract as ``oracle.moe.forward`` (y float64 over the chosen tokens, o in flat
     (t, j) order, hq/hs and h by assignment, xq/xs of the tokens, margins and the near-tie
@@ -239,27 +241,29 @@ def forward(x_f64, ids, weights, experts: QuantizedExpertsMX, tokens=None, tie_t
     o = np.zeros((n * k, H))
     ob = np.zeros((n * k, H))
     qm = np.full(n * k, np.inf)
-    hq = hs = h = None
+    hq = hs = h = h_err = None
     flat_ids = ids[tok].reshape(-1)
     groups = [(int(e), np.nonzero(flat_ids == e)[0]) for e in np.unique(flat_ids)]
     jobs = [(e, xq[rows // k], xs[rows // k]) for e, rows in groups]
     if ffn_map is None:
-        results = [expert_ffn(xr, sr, *experts.get(e), experts.fmt, tie_tol) for e, xr, sr in jobs]
+        results = [expert_ffn(xr, sr, *experts.get(e), experts.fmt, acc_err) for e, xr, sr in jobs]
     else:
-        results = ffn_map(jobs, tie_tol)
-    for (e, rows), (oe, hqe, hse, qme, obe, he) in zip(groups, results):
+        results = ffn_map(jobs, acc_err)
+    for (e, rows), (oe, hqe, hse, qme, obe, he, hee) in zip(groups, results):
         if hq is None:
             hq = np.zeros((n * k, hqe.shape[1]), dtype=np.uint8)
             hs = np.zeros((n * k, hse.shape[1]), dtype=np.uint8)
             h = np.zeros((n * k, he.shape[1]))
+            h_err = np.zeros((n * k, he.shape[1]))
         o[rows] = oe
         ob[rows] = obe
         hq[rows] = hqe
         hs[rows] = hse
         h[rows] = he
+        h_err[rows] = hee
         qm[rows] = qme
     w = np.asarray(weights, dtype=np.float64)[tok]
     y = moe.combine(o, w)
-    return {"y": y, "o": o, "hq": hq, "hs": hs, "h": h, "xq": xq, "xs": xs, "tokens": tok,
+    return {"y": y, "o": o, "hq": hq, "hs": hs, "h": h, "h_err": h_err, "xq": xq, "xs": xs, "tokens": tok,
             "qmargin": qm, "qmargin_tok": qm.reshape(n, k).min(axis=1),
             "o_bound": ob, "y_bound": moe.combine(ob, np.abs(w))}

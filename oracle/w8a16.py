@@ -46,13 +46,14 @@ def bf16_rne(v) -> np.ndarray:
 def expert_ffn(x_rows, q13, s13, q2, s2):
     """One expert on a stack of bf16 activation rows (float64 values).
     Returns (o float64 [R, H], hb float64 [R, I] holding bf16 values, h float64 [R, I] before
-    the rounding)."""
+    the rounding, h_err float64 [R, I] its error bound (``oracle.moe.h_error_bound``))."""
     w13 = codec.dequant_blocks_128(q13, s13)
-    gu = np.asarray(x_rows, dtype=np.float64) @ w13
+    x = np.asarray(x_rows, dtype=np.float64)
+    gu = x @ w13
     I = w13.shape[1] // 2
     h = moe.silu(gu[:, :I]) * gu[:, I:]
     hb = bf16_rne(h)
-    return hb @ codec.dequant_blocks_128(q2, s2), hb, h
+    return hb @ codec.dequant_blocks_128(q2, s2), hb, h, moe.h_error_bound(x, w13, gu)
 
 
 def forward(x_f64, ids, weights, experts: moe.QuantizedExperts, tokens=None, ffn_map=None):
@@ -67,7 +68,7 @@ def forward(x_f64, ids, weights, experts: moe.QuantizedExperts, tokens=None, ffn
     n = len(tok)
     H = x.shape[1]
     o = np.zeros((n * k, H))
-    hb = h = None
+    hb = h = h_err = None
     flat_ids = np.asarray(ids)[tok].reshape(-1)
     groups = [(int(e), np.nonzero(flat_ids == e)[0]) for e in np.unique(flat_ids)]   # flat positions
     jobs = [(e, x[rows // k], None) for e, rows in groups]
@@ -75,14 +76,16 @@ def forward(x_f64, ids, weights, experts: moe.QuantizedExperts, tokens=None, ffn
         results = [expert_ffn(xr, *experts.get(e)) for e, xr, _ in jobs]
     else:
         results = ffn_map(jobs, None)
-    for (e, rows), (oe, hbe, he) in zip(groups, results):
+    for (e, rows), (oe, hbe, he, hee) in zip(groups, results):
         if hb is None:
             hb = np.zeros((n * k, hbe.shape[1]))
             h = np.zeros((n * k, he.shape[1]))
+            h_err = np.zeros((n * k, he.shape[1]))
         o[rows] = oe
         hb[rows] = hbe
         h[rows] = he
+        h_err[rows] = hee
     y = moe.combine(o, np.asarray(weights, dtype=np.float64)[tok])
     qm = np.full(n * k, np.inf)
-    return {"y": y, "o": o, "hb": hb, "h": h, "tokens": tok, "qmargin": qm, "qmargin_tok": qm.reshape(n, k).min(axis=1),
+    return {"y": y, "o": o, "hb": hb, "h": h, "h_err": h_err, "tokens": tok, "qmargin": qm, "qmargin_tok": qm.reshape(n, k).min(axis=1),
             "o_bound": np.zeros_like(o), "y_bound": np.zeros_like(y)}

@@ -23,10 +23,6 @@ pytestmark = pytest.mark.gpu
 M = pytest.importorskip("mixture_experts_fp8_amd")
 DEV = "cuda"
 
-# largest |h_device - h_oracle| relative to the row's largest |h| (float32 accumulation in the
-# matrix cores against float64)
-H_TOL = 1e-4
-
 FP8_CASES = {
     "cfg1_decode_tiles": W.CONFIGS[1],
     "cfg2_decode_gemma4": W.CONFIGS[2],
@@ -95,18 +91,25 @@ def _check(wl, scheme, tokens=None, extra_rows=()):
     fm = {"fp8": omoe.forward, "w8a16": ow.forward}.get(scheme, omx.forward)
     ref = fm(xf, ids_ref, w_ref, None, tokens=tok, ffn_map=HN.oracle_ffn_map(wl, scheme))
     h_dev = h[torch.from_numpy(slots).to(DEV)].cpu().numpy().astype(np.float64)
-    err = np.abs(h_dev - ref["h"]) / np.maximum(np.abs(ref["h"]).max(axis=1, keepdims=True), 1e-300)
-    big = np.abs(ref["h"]) > 1e-2 * np.abs(ref["h"]).max(axis=1, keepdims=True)
-    rel = (np.abs(h_dev - ref["h"]) / np.abs(ref["h"]))[big]
-    print(f"  {len(rows)} rows byte-checked; h: max err / row max {err.max():.2e}, max relative error of "
-          f"elements above 1% of the row max {rel.max():.2e}", flush=True)
-    assert err.max() <= H_TOL
-    # 3. diagnostic: codes that match the oracle's own re-quantisation of its float64 h
+    d = np.abs(h_dev - ref["h"])
+    ratio = d / np.maximum(ref["h_err"], 1e-300)
+    rowmax = np.maximum(np.abs(ref["h"]).max(axis=1, keepdims=True), 1e-300)
+    print(f"  {len(rows)} rows byte-checked; |h - h_oracle|: max {(d / rowmax).max():.2e} of the row max, "
+          f"max {ratio.max():.3f} of the oracle's error bound h_err", flush=True)
+    assert ratio.max() <= 1.0, "the device's h is outside the oracle's error bound"
+    # 3. the device's codes differ from the oracle's own re-quantisation only at decisions that
+    #    lie within h_err of a tie (the allowance of the output bar)
     if scheme != "w8a16":
         hq_dev = hq[torch.from_numpy(slots).to(DEV)].cpu().numpy()
-        rate = (hq_dev == ref["hq"]).mean()
-        print(f"  hq codes equal to the oracle's: {rate:.6f}", flush=True)
-        assert rate >= 0.999
+        grp = 128 if scheme == "fp8" else 32
+        elem, scale = codec.near_tie_flips(ref["h"], grp, ref["h_err"])
+        allowed = elem != 0
+        for r_, c0, _ in scale:
+            allowed[r_, c0:c0 + grp] = True
+        diff = hq_dev != ref["hq"]
+        print(f"  hq codes equal to the oracle's: {1 - diff.mean():.6f}; {diff.sum()} differ, "
+              f"{allowed.sum()} decisions within h_err of a tie", flush=True)
+        assert not (diff & ~allowed).any(), "a code differs from the oracle's away from any near tie"
 
 
 @pytest.mark.parametrize("name", list(FP8_CASES))

@@ -212,15 +212,16 @@ def test_near_tie_flips_hand_values():
 
 @pytest.mark.parametrize("group", [128, 32])
 def test_near_tie_flips_against_perturbations(group):
-    # brute force through the pinned quantiser: every flagged element decision flips when its
-    # element alone moves by a relative amount below tol (in the direction of its midpoint),
+    # brute force through the pinned quantiser (tolerance tol * |v|, i.e. relative): every
+    # flagged element decision flips when its element alone moves by a relative amount below
+    # tol (in the direction of its midpoint),
     # and the dequantised row then changes by exactly the reported delta; no unflagged element
     # changes its code under any single-element move of relative size below tol
     tol = 1e-3     # wide, so that random rows hold near ties
     rng = np.random.default_rng(11)
     R, C = 4, 256
     v = rng.standard_normal((R, C)) * np.exp2(rng.integers(-4, 5, size=(R, 1)))
-    elem, scale = codec.near_tie_flips(v, group, tol)
+    elem, scale = codec.near_tie_flips(v, group, tol * np.abs(v))
     assert np.count_nonzero(elem) > 5
     base = _dq(v, group)
     scale_groups = {(r, c0) for r, c0, _ in scale}
@@ -251,10 +252,10 @@ def test_flip_bound_covers_every_subset_and_is_exact_for_one():
     rng = np.random.default_rng(5)
     v = rng.standard_normal((1, 128)) * 3.0
     w = rng.standard_normal((128, 6))
-    elem, scale = codec.near_tie_flips(v, 128, tol)
+    elem, scale = codec.near_tie_flips(v, 128, tol * np.abs(v))
     idx = np.nonzero(elem[0])[0]
     assert scale == [] and 2 <= len(idx) <= 10
-    bound = codec.flip_bound(v, w, 128, tol)[0]
+    bound = codec.flip_bound(v, w, 128, tol * np.abs(v))[0]
     base = _dq(v, 128)[0] @ w
     import itertools
     for n in range(1, len(idx) + 1):
@@ -265,6 +266,6 @@ def test_flip_bound_covers_every_subset_and_is_exact_for_one():
     one = v.copy()
     keep = idx[0]
     one[0, idx[1:]] = np.round(one[0, idx[1:]])          # move the other ties away
-    e1, s1 = codec.near_tie_flips(one, 128, tol)
-    if np.count_nonzero(e1) == 1 and not s1:
-        assert np.allclose(codec.flip_bound(one, w, 128, tol)[0], np.abs(e1[0, keep] * w[keep]))
+    e1, s1 = codec.near_tie_flips(one, 128, tol * np.abs(one))
+    assert np.count_nonzero(e1) == 1 and not s1
+    assert np.allclose(codec.flip_bound(one, w, 128, tol * np.abs(one))[0], np.abs(e1[0, keep] * w[keep]))
