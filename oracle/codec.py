@@ -191,7 +191,7 @@ def near_tie_flips(v: np.ndarray, group: int, tol):
     A decision is
       * an element's rounding: |v| within tol of the rounding midpoint (times 2^e) between
         the two magnitudes nearest to |v| / 2^e; the other way is the magnitude across that
-        midpoint (same sign);
+        midpoint (same sign; for a zero element, either sign);
       * a group's scale: its amax within the group's largest tol of 448 * 2^(e-1) (the other
         way is e - 1) or of 448 * 2^e (the other way is e + 1); taking it re-quantises the
         whole group.
@@ -213,7 +213,7 @@ def near_tie_flips(v: np.ndarray, group: int, tol):
     # nearest midpoint m: between mags[m] and mags[m + 1]
     j = np.clip(np.searchsorted(mids, s), 1, len(mids) - 1)
     m = np.where(np.abs(s - mids[j - 1]) <= np.abs(s - mids[j]), j - 1, j)
-    near = (s > 0) & (np.abs(s - mids[m]) * pw < tol)
+    near = np.abs(s - mids[m]) * pw < tol      # a zero element too: a computed one may not be zero
     chosen = np.abs(e4m3_decode(e4m3_encode(g / pw)))
     other = np.where(chosen == mags[m], mags[m + 1], mags[m])
     sign = np.where(np.signbit(g), -1.0, 1.0)
