@@ -172,16 +172,18 @@ size_t moe_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k,
     return moe::fused_ws_layout(T, H, I, E + sh, k + sh, (flags & MOE_FUSED_EXPERT_OUT_BF16) ? 2 : 4).end;
 }
 
-int moe_fused(const moe_fused_args* a) {
-    const char* op = "moe_fused";
-    int rc = moe::host::check_fused(a);
-    if (rc) return rc;
+}  // extern "C"
+
+namespace {
+
+// The whole step on validated arguments, with its temporaries carved from `base` (at least
+// fused_ws_layout(...).end bytes of device memory, 256-byte aligned).
+int run_fused(const char* op, const moe_fused_args* a, uint8_t* base) {
     const int T = a->T, H = a->H, I = a->I, E = a->route.num_experts, k = a->route.top_k;
     // with the shared expert the FFN, dispatch and combine see E + 1 experts and k + 1 slots
     const int sh = (a->flags & MOE_FUSED_SHARED_EXPERT) ? 1 : 0, Ef = E + sh, kf = k + sh;
     const int bf = (a->flags & MOE_FUSED_EXPERT_OUT_BF16) ? 1 : 0;
     const moe::FusedWsLayout L = moe::fused_ws_layout(T, H, I, Ef, kf, bf ? 2 : 4);
-    uint8_t* base = static_cast<uint8_t*>(a->workspace);
     int32_t* ids = a->topk_ids ? a->topk_ids : reinterpret_cast<int32_t*>(base + L.ids);
     float* wts = a->topk_weights ? a->topk_weights : reinterpret_cast<float*>(base + L.wts);
     int32_t* counts = a->expert_counts ? a->expert_counts : reinterpret_cast<int32_t*>(base + L.counts);
@@ -236,6 +238,16 @@ int moe_fused(const moe_fused_args* a) {
     mark(6);
     if (e != hipSuccess) return hip_fail(op, e);
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_fused(const moe_fused_args* a) {
+    int rc = moe::host::check_fused(a);
+    if (rc) return rc;
+    return run_fused("moe_fused", a, static_cast<uint8_t*>(a->workspace));
 }
 
 }  // extern "C"
