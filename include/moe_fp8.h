@@ -359,6 +359,20 @@ typedef struct moe_fused_args {
 int moe_fused(const moe_fused_args* a);
 size_t moe_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, int32_t flags);
 
+/* moe_fused_static: moe_fused for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  The step's
+ * temporaries live in a scratch array of MOE_STATIC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on until the process ends; the call allocates nothing.  Arguments are
+ * those of moe_fused except that workspace must be NULL and workspace_bytes 0; steps whose
+ * moe_workspace_size(T, H, I, E, k, flags) exceeds MOE_STATIC_SCRATCH_BYTES are rejected
+ * with MOE_ERR_UNSUPPORTED before anything is launched.  Every call on one GPU uses that
+ * GPU's one array: calls that overlap on one GPU (other streams, other host threads) race
+ * and must be serialised by the caller; the array keeps the last call's contents, and the
+ * step needs none of them to start at zero.  The first call on a device looks the array's
+ * address up with that device current. */
+#define MOE_STATIC_SCRATCH_BYTES (64u << 20)
+int moe_fused_static(const moe_fused_args* a);
+
 /* Thread-local description of the last error returned on this thread ("" after success). */
 const char* moe_last_error(void);
 

@@ -32,7 +32,8 @@ QUANT_SCHEMES = {"fp8": MOE_QUANT_FP8_BLOCK128, "mxfp8": MOE_QUANT_MXFP8, "w4a8"
 EXPORTED = ["moe_route", "moe_route_workspace_size", "moe_quant_act", "moe_quant_weight_blocks",
             "moe_prepack_weights", "moe_grouped_ffn", "moe_ffn_workspace_size", "moe_combine",
             "moe_fused", "moe_workspace_size", "moe_last_error", "moe_quant_act_mx", "moe_quant_weight_mx",
-            "moe_prepack_weights_mx"]
+            "moe_prepack_weights_mx", "moe_fused_static"]
+MOE_STATIC_SCRATCH_BYTES = 64 << 20
 
 
 class MoeError(RuntimeError):
@@ -111,6 +112,8 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp, vp]
         L.moe_fused.restype = ctypes.c_int
         L.moe_fused.argtypes = [ctypes.POINTER(FusedArgs)]
+        L.moe_fused_static.restype = ctypes.c_int
+        L.moe_fused_static.argtypes = [ctypes.POINTER(FusedArgs)]
         L.moe_workspace_size.restype = sz
         L.moe_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
         L.moe_quant_act_mx.restype = ctypes.c_int
@@ -377,7 +380,10 @@ class MoeFused:
                  expert_out_bf16: bool = False, y: Optional[torch.Tensor] = None,
                  topk_ids: Optional[torch.Tensor] = None, topk_weights: Optional[torch.Tensor] = None,
                  expert_counts: Optional[torch.Tensor] = None, shared_expert: bool = False,
-                 act_q: Optional[torch.Tensor] = None, act_scales: Optional[torch.Tensor] = None):
+                 act_q: Optional[torch.Tensor] = None, act_scales: Optional[torch.Tensor] = None,
+                 static_scratch: bool = False):
+        """static_scratch: call moe_fused_static (the library's own scratch array, no
+        workspace) instead of moe_fused."""
         H = hidden_states.shape[1]
         _need(hidden_states, "hidden_states", torch.bfloat16, (T, H))
         if router_logits is not None:
@@ -388,8 +394,12 @@ class MoeFused:
         self.flags = ((MOE_FUSED_EXPERT_OUT_BF16 if expert_out_bf16 else 0) |
                       (MOE_FUSED_SHARED_EXPERT if shared_expert else 0))
         self.y = y if y is not None else torch.empty(T, H, dtype=torch.bfloat16, device=hidden_states.device)
-        nbytes = lib().moe_workspace_size(T, H, w.I, params.num_experts, params.top_k, self.flags)
-        self.ws = workspace(max(nbytes, 256), hidden_states.device)
+        self.static = static_scratch
+        if static_scratch:
+            self.ws = None
+        else:
+            nbytes = lib().moe_workspace_size(T, H, w.I, params.num_experts, params.top_k, self.flags)
+            self.ws = workspace(max(nbytes, 256), hidden_states.device)
         if act_q is not None:
             _need(act_q, "act_q", torch.uint8, (T, H))
         if act_scales is not None:
@@ -401,7 +411,8 @@ class MoeFused:
                               ctypes.pointer(self._pre) if self._pre is not None else None,
                               _ptr(w.w13), _ptr(w.w13_scale), _ptr(w.w2), _ptr(w.w2_scale), _ptr(self.y),
                               _ptr(topk_ids), _ptr(topk_weights), _ptr(expert_counts), self.flags, _ptr(self.ws),
-                              self.ws.numel(), None, None, w.quant, _ptr(act_q), _ptr(act_scales))
+                              0 if self.ws is None else self.ws.numel(), None, None, w.quant, _ptr(act_q),
+                              _ptr(act_scales))
 
     def __call__(self, stream: Optional[int] = None, stage_events=None) -> torch.Tensor:
         """stage_events: None or a ctypes array of MOE_STAGES + 1 hipEvent_t handles that the
@@ -414,19 +425,22 @@ class MoeFused:
                 raise ValueError(f"stage_events: need {MOE_STAGES + 1} hipEvent_t slots")
             self._ev_arr = stage_events
             self.args.stage_events = ctypes.cast(stage_events, ctypes.POINTER(ctypes.c_void_p))
-        _check(lib().moe_fused(ctypes.byref(self.args)))
+        fn = lib().moe_fused_static if self.static else lib().moe_fused
+        _check(fn(ctypes.byref(self.args)))
         return self.y
 
 
 def moe_fused(params: RouteParams, hidden_states: torch.Tensor, w: PackedWeights,
               router_logits: Optional[torch.Tensor] = None, prelude: Optional[Prelude] = None,
               expert_out_bf16: bool = False, return_routing: bool = False, shared_expert: bool = False,
-              act_q: Optional[torch.Tensor] = None, act_scales: Optional[torch.Tensor] = None):
+              act_q: Optional[torch.Tensor] = None, act_scales: Optional[torch.Tensor] = None,
+              static_scratch: bool = False):
     """The whole step in one C call.  Returns y bf16 [T, H] (and ids, weights, counts).
     shared_expert: w holds num_experts + 1 experts, the last one run on every token and added
     with weight 1 (ids / weights then have top_k + 1 columns, counts num_experts + 1 entries).
     act_q, act_scales: optional uint8 tensors ([T, H] and [T, H/128], or [T, H/32] for the
-    micro-scaled schemes) that receive the step's quantised activations."""
+    micro-scaled schemes) that receive the step's quantised activations.
+    static_scratch: run through moe_fused_static (no workspace; the library's scratch array)."""
     T = hidden_states.shape[0]
     dev = hidden_states.device
     ids = weights = counts = None
@@ -436,6 +450,17 @@ def moe_fused(params: RouteParams, hidden_states: torch.Tensor, w: PackedWeights
         weights = torch.empty(T, params.top_k + sh, dtype=torch.float32, device=dev)
         counts = torch.empty(params.num_experts + sh, dtype=torch.int32, device=dev)
     f = MoeFused(params, T, w, hidden_states, router_logits, prelude, expert_out_bf16, None, ids, weights, counts,
-                 shared_expert, act_q, act_scales)
+                 shared_expert, act_q, act_scales, static_scratch)
     y = f()
     return (y, ids, weights, counts) if return_routing else y
+
+
+def moe_fused_static(params: RouteParams, hidden_states: torch.Tensor, w: PackedWeights,
+                     router_logits: Optional[torch.Tensor] = None, prelude: Optional[Prelude] = None,
+                     expert_out_bf16: bool = False, return_routing: bool = False, shared_expert: bool = False,
+                     act_q: Optional[torch.Tensor] = None, act_scales: Optional[torch.Tensor] = None):
+    """moe_fused through the C entry point moe_fused_static: no workspace, the library's own
+    scratch array (MOE_STATIC_SCRATCH_BYTES per GPU).  Same arguments and results as
+    moe_fused; steps that need more scratch raise MoeError (MOE_ERR_UNSUPPORTED)."""
+    return moe_fused(params, hidden_states, w, router_logits, prelude, expert_out_bf16, return_routing,
+                     shared_expert, act_q, act_scales, static_scratch=True)

@@ -2,6 +2,7 @@
 // every entry point are checked first by the plain C++ validators of moe_host.cpp, so a
 // rejected call enqueues nothing.
 #include <cstdio>
+#include <mutex>
 
 #include "../../include/moe_fp8.h"
 #include "moe_common.h"
@@ -240,9 +241,48 @@ int run_fused(const char* op, const moe_fused_args* a, uint8_t* base) {
     return ok();
 }
 
+// Scratch memory of moe_fused_static: a file-scope device array that every GPU the library
+// runs on holds until the process ends.  Host code never passes the array's name to a kernel
+// (on the host it is only a stand-in symbol): its device address is looked up once per device,
+// with that device current, and kept.
+constexpr size_t kStaticScratchBytes = (size_t)MOE_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxDevices] = {};
+
+// this device's address of `scratch` (nullptr and *err set on failure)
+uint8_t* scratch_on_current_device(hipError_t* err) {
+    int dev = -1;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        *err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (*err != hipSuccess) return nullptr;
+        g_scratch_ptr[dev] = static_cast<uint8_t*>(ptr);
+    }
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
+
+int moe_fused_static(const moe_fused_args* a) {
+    int rc = moe::host::check_fused_static(a, kStaticScratchBytes);
+    if (rc) return rc;
+    hipError_t e = hipSuccess;
+    uint8_t* base = scratch_on_current_device(&e);
+    if (!base) return hip_fail("moe_fused_static", e);
+    return run_fused("moe_fused_static", a, base);
+}
 
 int moe_fused(const moe_fused_args* a) {
     int rc = moe::host::check_fused(a);

@@ -367,8 +367,39 @@ int check_combine(const void* eo, int32_t dtype, const int32_t* pos, const float
     return MOE_OK;
 }
 
+namespace {
+int check_fused_common(const char* op, const moe_fused_args* a, size_t* need);
+}
+
 int check_fused(const moe_fused_args* a) {
     const char* op = "moe_fused";
+    size_t need = 0;
+    int rc = check_fused_common(op, a, &need);
+    if (rc) return rc;
+    if (!a->workspace || a->workspace_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "%s: workspace too small: need %zu bytes, have %zu", op, need,
+                    a->workspace ? a->workspace_bytes : (size_t)0);
+    if (!aligned(a->workspace, 256)) return fail(MOE_ERR_INVALID, "%s: workspace must be 256-byte aligned", op);
+    return MOE_OK;
+}
+
+int check_fused_static(const moe_fused_args* a, size_t scratch_bytes) {
+    const char* op = "moe_fused_static";
+    size_t need = 0;
+    int rc = check_fused_common(op, a, &need);
+    if (rc) return rc;
+    if (a->workspace || a->workspace_bytes)
+        return fail(MOE_ERR_INVALID, "%s: runs in the library's own scratch array: workspace must be NULL and "
+                    "workspace_bytes 0", op);
+    if (need > scratch_bytes)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: the step needs %zu bytes of scratch, above the library's maximum of "
+                    "%zu (use moe_fused with a workspace)", op, need, scratch_bytes);
+    return MOE_OK;
+}
+
+namespace {
+// every check of moe_fused except the workspace's; *need = the workspace bytes the step uses
+int check_fused_common(const char* op, const moe_fused_args* a, size_t* need_out) {
     if (!a) return fail(MOE_ERR_INVALID, "%s: args must not be NULL", op);
     int rc = check_route_params(op, &a->route, a->T);
     if (rc) return rc;
@@ -388,11 +419,7 @@ int check_fused(const moe_fused_args* a) {
     if (!valid_quant(a->quant)) return fail(MOE_ERR_INVALID, "%s: quant (%d) must be one of MOE_QUANT_*", op, a->quant);
     if (!aligned(a->hidden_states, 16) || !aligned(a->y, 8))
         return fail(MOE_ERR_UNSUPPORTED, "%s: hidden_states must be 16-byte and y 8-byte aligned", op);
-    const size_t need = fused_ws_layout(T, H, I, E + sh, k + sh, (a->flags & MOE_FUSED_EXPERT_OUT_BF16) ? 2 : 4).end;
-    if (!a->workspace || a->workspace_bytes < need)
-        return fail(MOE_ERR_WORKSPACE, "%s: workspace too small: need %zu bytes, have %zu", op, need,
-                    a->workspace ? a->workspace_bytes : (size_t)0);
-    if (!aligned(a->workspace, 256)) return fail(MOE_ERR_INVALID, "%s: workspace must be 256-byte aligned", op);
+    *need_out = fused_ws_layout(T, H, I, E + sh, k + sh, (a->flags & MOE_FUSED_EXPERT_OUT_BF16) ? 2 : 4).end;
     if ((a->act_q && !aligned(a->act_q, 16)) || (a->act_scales && !aligned(a->act_scales, 16)))
         return fail(MOE_ERR_INVALID, "%s: act_q and act_scales must be 16-byte aligned", op);
     if (a->quant == MOE_QUANT_W8A16 && (a->act_q || a->act_scales))
@@ -400,6 +427,7 @@ int check_fused(const moe_fused_args* a) {
                     op);
     return MOE_OK;
 }
+}  // namespace
 
 }  // namespace host
 }  // namespace moe

@@ -76,6 +76,8 @@ int check_grouped_ffn(const moe_ffn_args* a);
 int check_combine(const void* eo, int32_t dtype, const int32_t* pos, const float* w, int32_t T, int32_t k, int32_t H,
                   const uint16_t* y);
 int check_fused(const moe_fused_args* a);
+// moe_fused_static: the library's scratch array of `scratch_bytes` replaces the workspace
+int check_fused_static(const moe_fused_args* a, size_t scratch_bytes);
 }  // namespace host
 
 }  // namespace moe

@@ -215,6 +215,30 @@ static void fused_checks() {
     CHECK(host::check_fused(&a) == MOE_ERR_INVALID);
 }
 
+static void static_checks() {
+    // the scratch-array variant: no workspace, and steps above the scratch size are rejected
+    const size_t lim = (size_t)64 << 20;
+    moe_fused_args a = fused(32, 2816, 768, 128, 8);
+    a.workspace = nullptr;
+    a.workspace_bytes = 0;
+    CHECK(host::check_fused_static(&a, lim) == MOE_OK);
+    CHECK(host::check_fused(&a) == MOE_ERR_WORKSPACE);
+    a.workspace = fake();
+    CHECK(host::check_fused_static(&a, lim) == MOE_ERR_INVALID);
+    a.workspace = nullptr;
+    a.workspace_bytes = 16;
+    CHECK(host::check_fused_static(&a, lim) == MOE_ERR_INVALID);
+    a = fused(2048, 768, 1152, 256, 8);
+    a.workspace = nullptr;
+    a.workspace_bytes = 0;
+    CHECK(host::check_fused_static(&a, lim) == MOE_ERR_UNSUPPORTED && std::strstr(host::last_error(), "scratch"));
+    CHECK(fused_ws_layout(2048, 768, 1152, 256, 8, 4).end > lim);
+    a = fused(4, 100, 256, 8, 2);   // the other checks still apply
+    a.workspace = nullptr;
+    a.workspace_bytes = 0;
+    CHECK(host::check_fused_static(&a, lim) == MOE_ERR_UNSUPPORTED);
+}
+
 static void helper_checks() {
     CHECK(host::check_quant_act("q", fp<uint16_t>(), 4, 128, 128, fp<uint8_t>(), fp<uint8_t>(), 128) == MOE_OK);
     CHECK(host::check_quant_act("q", fp<uint16_t>(), 4, 100, 128, fp<uint8_t>(), fp<uint8_t>(), 128) ==
@@ -241,6 +265,7 @@ int main() {
     route_checks();
     ffn_checks();
     fused_checks();
+    static_checks();
     helper_checks();
     // the message buffer is bounded: an overlong message is truncated, never overrun
     std::vector<char> big(4096, 'x');

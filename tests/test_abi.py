@@ -196,6 +196,21 @@ def test_fused_validation():
     assert M.lib().moe_fused(None) == B.MOE_ERR_INVALID
 
 
+def test_fused_static_validation():
+    # the scratch-array entry point: a workspace is an error; a step above the scratch size is
+    # unsupported (both rejected before any launch, so the fake pointers are never used)
+    L = M.lib()
+    a = B.FusedArgs(T=4, H=256, I=256, route=M.route_params(8, 2), hidden_states=FAKE, router_logits=FAKE,
+                    prelude=None, w13=FAKE, w13_scale=FAKE, w2=FAKE, w2_scale=FAKE, y=FAKE, topk_ids=None,
+                    topk_weights=None, expert_counts=None, flags=0, workspace=FAKE, workspace_bytes=1 << 20,
+                    stream=None)
+    assert L.moe_fused_static(ctypes.byref(a)) == B.MOE_ERR_INVALID and "NULL" in M.moe_last_error()
+    a.workspace, a.workspace_bytes = None, 0
+    a.T, a.H, a.I, a.route = 2048, 768, 1152, M.route_params(256, 8)
+    assert L.moe_fused_static(ctypes.byref(a)) == B.MOE_ERR_UNSUPPORTED and "scratch" in M.moe_last_error()
+    assert L.moe_fused_static(None) == B.MOE_ERR_INVALID
+
+
 def test_workspace_sizes_are_monotone_and_cover_parts():
     L = M.lib()
     for (T, H, I, E, k) in [(64, 256, 512, 8, 2), (32, 2816, 768, 128, 8), (4096, 7168, 2048, 256, 8)]:
