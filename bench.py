@@ -50,7 +50,10 @@ def parse():
     ap.add_argument("--shared", action="store_true",
                     help="add one shared expert (same H, I) run on every token in the same launches")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0, help="0: the workload's own default sample")
-    ap.add_argument("--expert-out-bf16", action="store_true", help="keep per-assignment expert outputs in bf16")
+    ap.add_argument("--expert-out", default="auto", choices=["auto", "fp32", "bf16"],
+                    help="dtype of the per-assignment expert outputs between the down GEMM and the combine; auto: "
+                         "bf16 when their round trip exceeds 256 MB (the prefill shapes), else fp32")
+    ap.add_argument("--expert-out-bf16", action="store_true", help="same as --expert-out bf16")
     ap.add_argument("--quant", default="fp8", choices=["fp8", "mxfp8", "w4a8", "w8a16"],
                     help="fp8: E4M3 with 128-element scales (default); mxfp8: 32-element scales; "
                          "w4a8: E2M1 weights with MXFP8 activations; w8a16: the fp8 weights with bf16 activations")
@@ -244,6 +247,11 @@ def main():
     wl = W.CONFIGS[args.config]
     if args.shared:
         wl = wl.replace(shared=1)
+    if args.expert_out_bf16:
+        args.expert_out = "bf16"
+    if args.expert_out == "auto":
+        args.expert_out = "bf16" if wl.T * (wl.k + wl.shared) * wl.H * 4 > (256 << 20) else "fp32"
+    args.expert_out_bf16 = args.expert_out == "bf16"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] workload {wl.name}: {W.describe(wl)}", file=sys.stderr, flush=True)

@@ -1687,20 +1687,60 @@ __global__ __launch_bounds__(512, 1) void k_gemm2_p2(G2Args a) {
         }
     }
 
-    // lane holds rows wm * 128 + 16 mi + r0 + i; one per-lane limit for the row tests
-    const int r0 = 4 * (lane >> 4), lim = nvalid - wm * kPfBM - r0;
-    const int64_t o0 = (int64_t)(rowbase + wm * kPfBM + r0) * a.H + nb * 256 + wn * 64 + r16;
+    // Output: the tile goes through the LDS stages (free after the K loop) so that it leaves as
+    // whole 16-byte pieces of full rows.  A lane holds rows wm * 128 + 16 mi + 4 (lane / 16) + i
+    // of columns wn * 64 + 16 j + lane % 16.  LDS rows are swizzled by 16 columns times
+    // (row / 4) % 4, so the four rows one store instruction writes land in distinct banks.
+    __syncthreads();   // every wave is done reading the stages
+    const int r0 = 4 * (lane >> 4);
+    if (a.out_bf16) {
+        // one pass: 256 rows x 256 bf16 (512 bytes a row); neighbour lanes pair their columns
+        uint32_t* s_o = reinterpret_cast<uint32_t*>(buf);
+        if (nact > 0) {
 #pragma unroll
-    for (int mi = 0; mi < 8; ++mi) {
+            for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (mi * 16 + i < lim) {
-                const int64_t o = o0 + (int64_t)(mi * 16 + i) * a.H;
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o + j * 16] = f32_to_bf16(acc[mi][j][i]);
-                    else reinterpret_cast<float*>(a.out)[o + j * 16] = acc[mi][j][i];
-                }
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t v = f32_to_bf16(acc[mi][j][i]);
+                        const uint32_t nbv = dpp_u32<0xB1>(v);   // lane ^ 1
+                        if (!(lane & 1)) {
+                            const int R = wm * kPfBM + mi * 16 + r0 + i, c = wn * 64 + 16 * j + r16;
+                            s_o[(R * 256 + (c ^ (16 * ((R >> 2) & 3)))) >> 1] = v | (nbv << 16);
+                        }
+                    }
+        }
+        __syncthreads();
+        uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+        for (int t = tid; t < nvalid * 32; t += 512) {
+            const int R = t >> 5, m = t & 31;
+            const uint4 v = *reinterpret_cast<const uint4*>(buf + (R * 256 + ((8 * m) ^ (16 * ((R >> 2) & 3)))) * 2);
+            *reinterpret_cast<uint4*>(out + (int64_t)(rowbase + R) * a.H + nb * 256 + 8 * m) = v;
+        }
+    } else {
+        // two passes of 128 rows x 256 float32 (1 KB a row): the waves of row half h stage it
+        float* s_o = reinterpret_cast<float*>(buf);
+        float* out = reinterpret_cast<float*>(a.out);
+        for (int h = 0; h < (second ? 2 : 1); ++h) {
+            if (h) __syncthreads();   // the first half has left the LDS
+            if (wm == h && nact > 0) {
+#pragma unroll
+                for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int R = mi * 16 + r0 + i, c = wn * 64 + 16 * j + r16;
+                            s_o[R * 256 + (c ^ (16 * ((R >> 2) & 3)))] = acc[mi][j][i];
+                        }
+            }
+            __syncthreads();
+            const int nr = min(kPfBM, nvalid - h * kPfBM);
+            for (int t = tid; t < nr * 64; t += 512) {
+                const int R = t >> 6, m = t & 63;
+                const float4 v = *reinterpret_cast<const float4*>(s_o + R * 256 + ((4 * m) ^ (16 * ((R >> 2) & 3))));
+                *reinterpret_cast<float4*>(out + (int64_t)(rowbase + h * kPfBM + R) * a.H + nb * 256 + 4 * m) = v;
             }
         }
     }

@@ -186,7 +186,13 @@ __device__ __forceinline__ void tap_h(float* htap, int I, int rowbase, int row, 
 // consecutive tiles (mostly one expert) and the same weight columns, which the Infinity
 // Cache then serves from one HBM read.  Rank r of XCD x -> item (tile, col); false for the
 // holes past the last tile or column.
-constexpr int kOrdTiles = 8, kOrdCols = 4, kOrdXcds = 8, kOrdSlots = kOrdTiles * kOrdCols;
+#ifndef MOE_ORD_TILES
+#define MOE_ORD_TILES 8
+#endif
+#ifndef MOE_ORD_COLS
+#define MOE_ORD_COLS 4
+#endif
+constexpr int kOrdTiles = MOE_ORD_TILES, kOrdCols = MOE_ORD_COLS, kOrdXcds = 8, kOrdSlots = kOrdTiles * kOrdCols;
 __host__ __device__ inline int ord_ranks(int ntiles, int ncol) {
     const int ngroups = (ntiles + kOrdTiles - 1) / kOrdTiles;
     const int nwin = (ngroups + kOrdXcds - 1) / kOrdXcds;

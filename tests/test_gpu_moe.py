@@ -204,30 +204,32 @@ def test_fused_workload_full(cfg):
     print(f"  rel fro {fro:.2e} rel max {mx:.2e} active experts {(counts > 0).sum()}", flush=True)
 
 
-def _fused_routing(wl, expert_out_bf16=False):
-    """The fused call with every routing output: y, ids, weights, counts and the dispatch
-    (offsets, sorted_assign, assign_pos) re-derived by moe_route from the fused call's ids."""
+def _fused_routing(wl):
+    """The fused call with every routing output: y (with float32 and with bf16 expert outputs),
+    ids, counts and the dispatch (offsets, sorted_assign, assign_pos) re-derived by moe_route
+    from the fused call's ids."""
     x, logits, pre = HN.device_inputs(wl)
     w = HN.device_weights(wl)
     p = HN.device_params(wl)
-    y, ids, wts, counts = M.moe_fused(p, x, w, router_logits=logits, prelude=pre,
-                                      expert_out_bf16=expert_out_bf16, return_routing=True)
+    y, ids, wts, counts = M.moe_fused(p, x, w, router_logits=logits, prelude=pre, return_routing=True)
+    yb = M.moe_fused(p, x, w, router_logits=logits, prelude=pre, expert_out_bf16=True)
     r = M.moe_route(p, wl.T, topk_ids=ids, topk_weights=wts, device=DEV)
     torch.cuda.synchronize()
-    return y, ids.cpu().numpy(), counts.cpu().numpy(), {k: v.cpu().numpy() for k, v in r.items()}
+    return (y, yb), ids.cpu().numpy(), counts.cpu().numpy(), {k: v.cpu().numpy() for k, v in r.items()}
 
 
 # The prefill shapes at full size, in the launch configuration the benchmark times: the
 # oracle computes the tokens whose rows cover every 128-row tile of every expert (so every
 # 256-row item and every position of the super-tile work order holds a checked row) plus
 # every 64th token.  The dispatch is compared with the oracle's stable permutation of the
-# same ids, bit for bit, over the whole batch.
+# same ids, bit for bit, over the whole batch.  Both expert-output dtypes are checked (the
+# benchmark keeps them in bf16 for these shapes).
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("cfg", [4, 5, 6])
 def test_fused_workload_sampled(cfg):
     wl = W.CONFIGS[cfg]
     print("fused sampled", cfg, W.describe(wl), flush=True)
-    y, ids, counts, r = _fused_routing(wl)
+    ys, ids, counts, r = _fused_routing(wl)
     xf = W.bf16_to_f64(W.hidden_bf16(wl))
     ids_ref, w_ref, margin = HN.oracle_route(wl, x_f64=xf, logits=None if wl.prelude else W.router_logits(wl))
     ok = margin >= 1e-6
@@ -240,8 +242,10 @@ def test_fused_workload_sampled(cfg):
     tokens = tokens[ok[tokens]]
     print(f"  {len(tokens)} of {wl.T} tokens, {(~ok).sum()} near-tie routings", flush=True)
     ref = omoe.forward(xf, ids_ref, w_ref, None, tokens=tokens, ffn_map=HN.oracle_ffn_map(wl))
-    fro, mx = HN.assert_output_close(HN.bf16_to_f64(y)[tokens], ref["y"], f"cfg{cfg}", ref["y_bound"])
-    print(f"  rel fro {fro:.2e} rel max {mx:.2e}", flush=True)
+    for y, eo in zip(ys, ("fp32", "bf16")):
+        fro, mx = HN.assert_output_close(HN.bf16_to_f64(y)[tokens], ref["y"], f"cfg{cfg} {eo} expert_out",
+                                         ref["y_bound"])
+        print(f"  {eo} expert_out: rel fro {fro:.2e} rel max {mx:.2e}", flush=True)
 
 
 # Tile pairs at H/128 = 16 and 32 with a few hundred 256-row items over a few skewed experts:
