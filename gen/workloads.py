@@ -20,7 +20,8 @@ Value recipes (all seeded, all synthetic; no dataset is involved):
 * expert weights w13 [E,H,2I] and w2 [E,I,H]: N(0,0.02) float32, one stream per
   expert; the caller quantises them to E4M3 with 128x128 UE8M0 block scales;
 * gate prelude (decode shape): RMSNorm weight 1+N(0,0.1), router weight N(0,0.02)
-  float32 [E,H], per-expert scale U(0.5,1.5).
+  float32 [E,H], per-expert scale U(0.5,1.5);
+* optional expert biases: w13_bias N(0,0.25) float32 [E,2I], w2_bias N(0,0.1) [E,H].
 
 Small per-expert vectors (biases, norm weight, router weight, per-expert scale) are
 always generated on the CPU and moved, so that nothing here relies on a device's
@@ -37,7 +38,7 @@ import torch
 from . import rng
 
 # stream ids
-S_X, S_LOGITS, S_BIAS, S_W13, S_W2, S_WR, S_WNORM, S_PESCALE = range(8)
+S_X, S_LOGITS, S_BIAS, S_W13, S_W2, S_WR, S_WNORM, S_PESCALE, S_B13, S_B2 = range(10)
 
 # Zipf(s=1.1) bias profile: bias_e = -1.1 * ZIPF_ALPHA * ln(e + 1).  ZIPF_ALPHA was
 # calibrated at seed 0 so that experts 0..7 receive about 40% of the top-8 assignments
@@ -67,6 +68,7 @@ class Workload:
     bias: str = "none"             # "none" | "normal1.5" | "zipf"
     seed: int = 0
     shared: int = 0                # 1: one shared expert (weights of expert index E) on every token
+    ffn_bias: bool = False         # per-expert gate/up and down biases (w13_bias, w2_bias)
 
     @property
     def A(self) -> int:
@@ -150,6 +152,16 @@ def expert_weight_f32(wl: Workload, which: str, e: int, device="cpu") -> torch.T
     return rng.normal_f32_chunked(wl.key(s, e), K * N, 0.02, device).view(K, N)
 
 
+def expert_ffn_biases(wl: Workload, device="cpu"):
+    """(w13_bias [E', 2I], w2_bias [E', H]) float32, E' = E + shared: N(0, 0.25) on the
+    gate/up sums, N(0, 0.1) on the down output (about the spread of the unbiased sums and
+    outputs of the workloads above), generated on the CPU."""
+    ne = wl.E + wl.shared
+    b13 = rng.normal_f32(wl.key(S_B13), ne * 2 * wl.I, 0.25).view(ne, 2 * wl.I)
+    b2 = rng.normal_f32(wl.key(S_B2), ne * wl.H, 0.1).view(ne, wl.H)
+    return b13.to(device), b2.to(device)
+
+
 def make_small_inputs(wl: Workload, device="cpu") -> dict:
     """All inputs of a small workload as tensors (weights still float32)."""
     d = {"x": hidden_bf16(wl, device)}
@@ -178,6 +190,8 @@ def describe(wl: Workload) -> str:
         r += " +RMSNorm/router prelude"
     if wl.shared:
         r += " +shared expert"
+    if wl.ffn_bias:
+        r += " +ffn biases"
     if wl.bias != "none":
         r += f" bias={wl.bias}"
     return f"T={wl.T} H={wl.H} I={wl.I} E={wl.E} k={wl.k} ({r})"

@@ -16,6 +16,9 @@ gate+up producing quantised SiLU products, then down):
    Mega MoE page; no clamp);
 5. re-quantise h per (assignment row, 128 columns of I) to E4M3;
 6. down: o = dequant(hq) @ dequant(w2[e]), w2[e] is [I, H], float64;
+   optional biases (the ``w13_bias`` [experts, 2I] and ``w2_bias`` [experts, H] of the
+   ``fused_moe`` parameter table): w13_bias[e] is added to gate+up before SwiGLU (step 3),
+   w2_bias[e] to o (step 6), before the routing weight;
 7. combine: y[t] = sum_j w[t, j] * o[(t, j)], float64 (the ``combine`` stage; the MATE
    page's contiguous bfloat16 output is the caller-side rounding of this value).
 
@@ -93,7 +96,7 @@ def h_error_bound(x, w13, gu, acc_err=ACC_ERR):
     return acc_err * (np.abs(s * (1.0 + g * (1.0 - s)) * u) * S[:, :I] + np.abs(g * s) * S[:, I:] + np.abs(g * s * u))
 
 
-def expert_ffn(xq_rows, xs_rows, q13, s13, q2, s2, acc_err=ACC_ERR):
+def expert_ffn(xq_rows, xs_rows, q13, s13, q2, s2, acc_err=ACC_ERR, b13=None, b2=None):
     """One expert on a stack of quantised rows.
 
     Returns (o float64 [R, H], hq uint8 [R, I], hs uint8 [R, I/128], margin float64 [R],
@@ -101,16 +104,21 @@ def expert_ffn(xq_rows, xs_rows, q13, s13, q2, s2, acc_err=ACC_ERR):
     re-quantisation's decision margin per row (``codec.decision_margin_rows_128``); h is the
     SwiGLU output before re-quantisation and h_err its error bound (``h_error_bound``); bound is
     the largest change of o that taking the other way any re-quantisation decision lying within
-    h_err of a tie can make (``codec.flip_bound``)."""
+    h_err of a tie can make (``codec.flip_bound``).  b13 [2I] / b2 [H]: optional biases of the
+    gate+up sums and of o."""
     x = codec.dequant_rows_128(xq_rows, xs_rows)
     w13 = codec.dequant_blocks_128(q13, s13)
     gu = x @ w13
+    if b13 is not None:
+        gu = gu + np.asarray(b13, dtype=np.float64)
     I = w13.shape[1] // 2
     h = silu(gu[:, :I]) * gu[:, I:]
     h_err = h_error_bound(x, w13, gu, acc_err)
     hq, hs = codec.quant_rows_128(h)
     w2 = codec.dequant_blocks_128(q2, s2)
     o = codec.dequant_rows_128(hq, hs) @ w2
+    if b2 is not None:
+        o = o + np.asarray(b2, dtype=np.float64)
     return o, hq, hs, codec.decision_margin_rows_128(h), codec.flip_bound(h, w2, codec.GROUP, h_err), h, h_err
 
 
@@ -121,7 +129,8 @@ def combine(o_flat: np.ndarray, weights: np.ndarray) -> np.ndarray:
     return (weights[:, :, None] * o).sum(axis=1)
 
 
-def forward(x_f64, ids, weights, experts: QuantizedExperts, tokens=None, acc_err=ACC_ERR, ffn_map=None):
+def forward(x_f64, ids, weights, experts: QuantizedExperts, tokens=None, acc_err=ACC_ERR, ffn_map=None,
+            biases=None):
     """Expert step for the given routing.
 
     x_f64 [T, H]: exact values of the bfloat16 hidden state.  ids/weights [T, k].
@@ -135,8 +144,9 @@ def forward(x_f64, ids, weights, experts: QuantizedExperts, tokens=None, acc_err
     make (``expert_ffn``).
 
     ffn_map: optional callable (jobs, acc_err) -> results that runs ``expert_ffn`` on each job
-    (e, xq rows, xs rows) with expert e's weights (e.g. in worker processes) and returns the
-    results in job order; by default they run here with ``experts.get(e)``."""
+    (e, xq rows, xs rows, b13 or None, b2 or None) with expert e's weights (e.g. in worker
+    processes) and returns the results in job order; by default they run here with
+    ``experts.get(e)``.  biases: optional (w13_bias [E, 2I], w2_bias [E, H]) float arrays."""
     T, k = ids.shape
     tok = np.arange(T) if tokens is None else np.asarray(tokens)
     xq, xs = codec.quant_rows_128(x_f64[tok])
@@ -149,9 +159,10 @@ def forward(x_f64, ids, weights, experts: QuantizedExperts, tokens=None, acc_err
     hq = hs = h = h_err = None
     flat_ids = sub_ids.reshape(-1)
     groups = [(int(e), np.nonzero(flat_ids == e)[0]) for e in np.unique(flat_ids)]   # flat positions
-    jobs = [(e, xq[rows // k], xs[rows // k]) for e, rows in groups]
+    jobs = [(e, xq[rows // k], xs[rows // k], None if biases is None else biases[0][e],
+             None if biases is None else biases[1][e]) for e, rows in groups]
     if ffn_map is None:
-        results = [expert_ffn(xr, sr, *experts.get(e), acc_err) for e, xr, sr in jobs]
+        results = [expert_ffn(xr, sr, *experts.get(e), acc_err, b13, b2) for e, xr, sr, b13, b2 in jobs]
     else:
         results = ffn_map(jobs, acc_err)
     for (e, rows), (oe, hqe, hse, qme, obe, he, hee) in zip(groups, results):
@@ -175,7 +186,7 @@ def forward(x_f64, ids, weights, experts: QuantizedExperts, tokens=None, acc_err
 
 
 def forward_shared(x_f64, ids, weights, experts: QuantizedExperts, shared: int, tokens=None, acc_err=ACC_ERR,
-                   ffn_map=None):
+                   ffn_map=None, biases=None):
     """Routed experts plus one shared expert that every token runs through, added with
     weight 1 (the metrale grouped FP8 MoE page: the W8A8 gate_up and down launches also take
     the shared expert's gate/up/down projections and write its activations and output
@@ -189,7 +200,7 @@ def forward_shared(x_f64, ids, weights, experts: QuantizedExperts, shared: int, 
     T = ids.shape[0]
     ids_all = np.concatenate([np.asarray(ids), np.full((T, 1), shared, dtype=np.asarray(ids).dtype)], axis=1)
     w_all = np.concatenate([np.asarray(weights, dtype=np.float64), np.ones((T, 1))], axis=1)
-    return forward(x_f64, ids_all, w_all, experts, tokens, acc_err, ffn_map)
+    return forward(x_f64, ids_all, w_all, experts, tokens, acc_err, ffn_map, biases)
 
 
 def route_workload(inputs: dict, p: routing.RouteParams, prelude=None):

@@ -209,26 +209,32 @@ class QuantizedExpertsMX(moe.QuantizedExperts):
         return q13, s13, q2, s2
 
 
-def expert_ffn(xq_rows, xs_rows, q13, s13, q2, s2, fmt: str, acc_err=moe.ACC_ERR):
+def expert_ffn(xq_rows, xs_rows, q13, s13, q2, s2, fmt: str, acc_err=moe.ACC_ERR, b13=None, b2=None):
     """One expert on a stack of MX-quantised rows; weights in `fmt`.
     Returns (o float64 [R, H], hq uint8 [R, I], hs uint8 [R, I/32], margin float64 [R],
     bound float64 [R, H], h float64 [R, I], h_err float64 [R, I]): margin is the
     re-quantisation's decision margin per row (``decision_margin_rows_32``), h the SwiGLU output
     and h_err its error bound (``oracle.moe.h_error_bound``), bound the largest change of o the
-    decisions within h_err of a tie could make (``codec.flip_bound`` on 32-column groups)."""
+    decisions within h_err of a tie could make (``codec.flip_bound`` on 32-column groups).
+    b13 / b2: optional biases as in ``oracle.moe.expert_ffn``."""
     x = dequant_rows_32(xq_rows, xs_rows)
     w13 = dequant_weight_k32(q13, s13, fmt)
     gu = x @ w13
+    if b13 is not None:
+        gu = gu + np.asarray(b13, dtype=np.float64)
     I = w13.shape[1] // 2
     h = moe.silu(gu[:, :I]) * gu[:, I:]
     h_err = moe.h_error_bound(x, w13, gu, acc_err)
     hq, hs = quant_rows_32(h)
     w2 = dequant_weight_k32(q2, s2, fmt)
     o = dequant_rows_32(hq, hs) @ w2
+    if b2 is not None:
+        o = o + np.asarray(b2, dtype=np.float64)
     return o, hq, hs, decision_margin_rows_32(h), codec.flip_bound(h, w2, MX, h_err), h, h_err
 
 
-def forward(x_f64, ids, weights, experts: QuantizedExpertsMX, tokens=None, acc_err=moe.ACC_ERR, ffn_map=None):
+def forward(x_f64, ids, weights, experts: QuantizedExpertsMX, tokens=None, acc_err=moe.ACC_ERR, ffn_map=None,
+            biases=None):
     """Expert step for the given routing with MX activations and `experts.fmt` weights.
     Same contract as ``oracle.moe.forward`` (y float64 over the chosen tokens, o in flat
     (t, j) order, hq/hs and h by assignment, xq/xs of the tokens, margins and the near-tie
@@ -244,9 +250,10 @@ def forward(x_f64, ids, weights, experts: QuantizedExpertsMX, tokens=None, acc_e
     hq = hs = h = h_err = None
     flat_ids = ids[tok].reshape(-1)
     groups = [(int(e), np.nonzero(flat_ids == e)[0]) for e in np.unique(flat_ids)]
-    jobs = [(e, xq[rows // k], xs[rows // k]) for e, rows in groups]
+    jobs = [(e, xq[rows // k], xs[rows // k], None if biases is None else biases[0][e],
+             None if biases is None else biases[1][e]) for e, rows in groups]
     if ffn_map is None:
-        results = [expert_ffn(xr, sr, *experts.get(e), experts.fmt, acc_err) for e, xr, sr in jobs]
+        results = [expert_ffn(xr, sr, *experts.get(e), experts.fmt, acc_err, b13, b2) for e, xr, sr, b13, b2 in jobs]
     else:
         results = ffn_map(jobs, acc_err)
     for (e, rows), (oe, hqe, hse, qme, obe, he, hee) in zip(groups, results):

@@ -43,20 +43,26 @@ def bf16_rne(v) -> np.ndarray:
     return np.rint(v / ulp) * ulp                  # rint rounds halves to even
 
 
-def expert_ffn(x_rows, q13, s13, q2, s2):
+def expert_ffn(x_rows, q13, s13, q2, s2, b13=None, b2=None):
     """One expert on a stack of bf16 activation rows (float64 values).
     Returns (o float64 [R, H], hb float64 [R, I] holding bf16 values, h float64 [R, I] before
-    the rounding, h_err float64 [R, I] its error bound (``oracle.moe.h_error_bound``))."""
+    the rounding, h_err float64 [R, I] its error bound (``oracle.moe.h_error_bound``)).
+    b13 / b2: optional biases as in ``oracle.moe.expert_ffn``."""
     w13 = codec.dequant_blocks_128(q13, s13)
     x = np.asarray(x_rows, dtype=np.float64)
     gu = x @ w13
+    if b13 is not None:
+        gu = gu + np.asarray(b13, dtype=np.float64)
     I = w13.shape[1] // 2
     h = moe.silu(gu[:, :I]) * gu[:, I:]
     hb = bf16_rne(h)
-    return hb @ codec.dequant_blocks_128(q2, s2), hb, h, moe.h_error_bound(x, w13, gu)
+    o = hb @ codec.dequant_blocks_128(q2, s2)
+    if b2 is not None:
+        o = o + np.asarray(b2, dtype=np.float64)
+    return o, hb, h, moe.h_error_bound(x, w13, gu)
 
 
-def forward(x_f64, ids, weights, experts: moe.QuantizedExperts, tokens=None, ffn_map=None):
+def forward(x_f64, ids, weights, experts: moe.QuantizedExperts, tokens=None, ffn_map=None, biases=None):
     """W8A16 expert step for the given routing (same experts object and result layout as
     ``oracle.moe.forward``).  There is no activation re-quantisation, so the decision
     margins ("qmargin", "qmargin_tok") are infinite and the flip bounds ("o_bound", "y_bound")
@@ -71,9 +77,10 @@ def forward(x_f64, ids, weights, experts: moe.QuantizedExperts, tokens=None, ffn
     hb = h = h_err = None
     flat_ids = np.asarray(ids)[tok].reshape(-1)
     groups = [(int(e), np.nonzero(flat_ids == e)[0]) for e in np.unique(flat_ids)]   # flat positions
-    jobs = [(e, x[rows // k], None) for e, rows in groups]
+    jobs = [(e, x[rows // k], None, None if biases is None else biases[0][e], None if biases is None else biases[1][e])
+            for e, rows in groups]
     if ffn_map is None:
-        results = [expert_ffn(xr, *experts.get(e)) for e, xr, _ in jobs]
+        results = [expert_ffn(xr, *experts.get(e), b13, b2) for e, xr, _, b13, b2 in jobs]
     else:
         results = ffn_map(jobs, None)
     for (e, rows), (oe, hbe, he, hee) in zip(groups, results):

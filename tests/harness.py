@@ -81,16 +81,16 @@ def _expert_job(args):
     """Worker side: one expert's FFN in the oracle (quantising its weights first if needed)."""
     from oracle import mx as omx
     from oracle import w8a16 as ow16
-    wl, scheme, e, q, xr, sr, acc_err = args
+    wl, scheme, e, q, xr, sr, b13, b2, acc_err = args
     fresh = q is None
     if fresh:
         q = _quantize(wl, scheme, e)
     if scheme == "fp8":
-        r = omoe.expert_ffn(xr, sr, *q, acc_err)
+        r = omoe.expert_ffn(xr, sr, *q, acc_err, b13, b2)
     elif scheme == "w8a16":
-        r = ow16.expert_ffn(xr, *q)
+        r = ow16.expert_ffn(xr, *q, b13, b2)
     else:
-        r = omx.expert_ffn(xr, sr, *q, _mx_fmt(scheme), acc_err)
+        r = omx.expert_ffn(xr, sr, *q, _mx_fmt(scheme), acc_err, b13, b2)
     return (q if fresh else None), r
 
 
@@ -105,9 +105,9 @@ def oracle_ffn_map(wl: W.Workload, scheme: str = "fp8"):
         _QCACHE.popitem(last=False)
 
     def ffn_map(jobs, acc_err):
-        args = [(wl, scheme, e, cache.get(e), xr, sr, acc_err) for e, xr, sr in jobs]
+        args = [(wl, scheme, e, cache.get(e), xr, sr, b13, b2, acc_err) for e, xr, sr, b13, b2 in jobs]
         out = []
-        for (e, _, _), (q, r) in zip(jobs, _pool().map(_expert_job, args)):
+        for (e, *_), (q, r) in zip(jobs, _pool().map(_expert_job, args)):
             if q is not None:
                 cache[e] = q
             out.append(r)

@@ -144,3 +144,78 @@ def test_shared_expert_adds_its_mlp_to_the_routed_output():
     np.testing.assert_allclose(both["y"] - routed["y"], ref, rtol=1e-9, atol=1e-12)
     # the routed slots are untouched: same per-assignment outputs in slots 0..k-1
     np.testing.assert_array_equal(both["o"].reshape(T, k + 1, -1)[:, :k], routed["o"].reshape(T, k, -1))
+
+
+def _golden(name):
+    g = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for ln in f:
+            if ln.strip() and not ln.startswith("#"):
+                key, val = ln.split()
+                g[key] = val
+    return g
+
+
+def test_golden_hand_ffn_with_biases():
+    # tests/golden/ffn_bias_hand.txt: gate bias +1, up bias -1, down bias 0.25, worked by hand
+    g = _golden("ffn_bias_hand.txt")
+    H = I = 128
+    x = np.full((1, H), float(g["x"]))
+    w13 = np.concatenate([np.full((H, I), float(g["w13_gate"])), np.full((H, I), float(g["w13_up"]))], axis=1)
+    w2 = np.full((I, H), float(g["w2"]))
+    b13 = np.concatenate([np.full(I, float(g["b13_gate"])), np.full(I, float(g["b13_up"]))])[None]
+    b2 = np.full((1, H), float(g["b2"]))
+    out = moe.forward(x, np.zeros((1, 1), np.int32), np.ones((1, 1)), _experts_from_dense([w13], [w2]),
+                      biases=(b13, b2))
+    np.testing.assert_allclose(out["h"], float(g["h_exact"]), rtol=1e-15)
+    assert (out["hq"] == int(g["hq"], 16)).all() and (out["hs"] == int(g["hs"])).all()
+    assert (out["y"] == float(g["y"])).all()
+
+
+def test_biased_expert_is_torch_linear_swiglu_linear():
+    # the dense biased SwiGLU MLP written with torch.nn.functional.linear (bias argument) on
+    # the dequantised operands, with h re-quantised between the projections
+    rng = np.random.default_rng(21)
+    T, H, I, E, k = 6, 256, 128, 3, 2
+    x, logits, ex = _random_case(T=T, H=H, I=I, E=E, k=k, seed=21)
+    b13 = rng.normal(0, 0.3, (E, 2 * I))
+    b2 = rng.normal(0, 0.3, (E, H))
+    ids, w, _ = routing.route(logits, routing.RouteParams(E, k, "softmax", True))
+    out = moe.forward(x, ids, w, ex, biases=(b13, b2))
+    F = torch.nn.functional
+    y = np.zeros((T, H))
+    for t in range(T):
+        for j in range(k):
+            e = ids[t, j]
+            q13, s13, q2, s2 = ex.get(e)
+            xd = torch.from_numpy(codec.dequant_rows_128(out["xq"][t:t + 1], out["xs"][t:t + 1]))
+            w13d = torch.from_numpy(codec.dequant_blocks_128(q13, s13))
+            gu = F.linear(xd, w13d.T, torch.from_numpy(b13[e]))
+            h = F.silu(gu[:, :I]) * gu[:, I:]
+            hq, hs = codec.quant_rows_128(h.numpy())
+            o = F.linear(torch.from_numpy(codec.dequant_rows_128(hq, hs)),
+                         torch.from_numpy(codec.dequant_blocks_128(q2, s2)).T, torch.from_numpy(b2[e]))
+            y[t] += w[t, j] * o.numpy()[0]
+    np.testing.assert_allclose(out["y"], y, rtol=1e-12, atol=1e-14)
+
+
+def test_down_bias_adds_weighted_sum_and_zero_biases_change_nothing():
+    # y with a down bias alone = y without biases + sum_j w_j * b2[e_j] (the bias is taken
+    # before the routing weight); zero biases reproduce the unbiased result bit for bit
+    rng = np.random.default_rng(22)
+    T, H, I, E, k = 8, 256, 256, 4, 2
+    x, logits, ex = _random_case(T=T, H=H, I=I, E=E, k=k, seed=22)
+    ids, w, _ = routing.route(logits, routing.RouteParams(E, k, "softmax", True, routed_scaling_factor=1.7))
+    y0 = moe.forward(x, ids, w, ex)
+    z = moe.forward(x, ids, w, ex, biases=(np.zeros((E, 2 * I)), np.zeros((E, H))))
+    assert np.array_equal(z["y"], y0["y"]) and np.array_equal(z["hq"], y0["hq"])
+    b2 = rng.normal(0, 1, (E, H))
+    yb = moe.forward(x, ids, w, ex, biases=(np.zeros((E, 2 * I)), b2))["y"]
+    np.testing.assert_allclose(yb - y0["y"], (w[:, :, None] * b2[ids]).sum(1), rtol=1e-10, atol=1e-12)
+    # a gate/up bias moves h exactly as adding it to the sums does: with x = 0 the sums are the
+    # biases alone, h = silu(b_gate) * b_up
+    zq = np.zeros((1, H))
+    b13 = rng.normal(0, 1, (E, 2 * I))
+    r = moe.forward(zq, np.zeros((1, 1), np.int32), np.ones((1, 1)), ex, biases=(b13, np.zeros((E, H))))
+    hb = b13[0, :I] / (1 + np.exp(-b13[0, :I])) * b13[0, I:]
+    np.testing.assert_allclose(r["h"][0], hb, rtol=1e-14)

@@ -165,3 +165,28 @@ def test_mx_decision_margin_hand_values_and_perturbations():
                 w[j] *= 1 + sgn * m[i] * (1 - 1e-6)
                 q, s_ = mx.quant_rows_32(w[None])
                 assert np.array_equal(q[0], q0[i]) and np.array_equal(s_[0], s0[i])
+
+
+def test_mx_biased_expert_is_torch_linear_swiglu_linear():
+    # biases as in the FP8 step: w13_bias before SwiGLU, w2_bias on o before the routing weight
+    H, I = 128, 96
+    g = torch.Generator().manual_seed(9)
+    x = torch.randn(2, H, generator=g).to(torch.bfloat16).double().numpy()
+    w13 = (torch.randn(H, 2 * I, generator=g) * 0.05).double().numpy()
+    w2 = (torch.randn(I, H, generator=g) * 0.05).double().numpy()
+    b13 = (torch.randn(1, 2 * I, generator=g) * 0.5).double().numpy()
+    b2 = (torch.randn(1, H, generator=g) * 0.5).double().numpy()
+    F = torch.nn.functional
+    for fmt in (mx.FMT_E4M3, mx.FMT_E2M1):
+        ex = mx.QuantizedExpertsMX(lambda e: (w13, w2), fmt)
+        w = np.array([[0.75], [1.5]])
+        out = mx.forward(x, np.zeros((2, 1), np.int32), w, ex, biases=(b13, b2))
+        q13, s13, q2, s2 = ex.get(0)
+        xd = torch.from_numpy(mx.dequant_rows_32(out["xq"], out["xs"]))
+        gu = F.linear(xd, torch.from_numpy(mx.dequant_weight_k32(q13, s13, fmt)).T, torch.from_numpy(b13[0]))
+        h = F.silu(gu[:, :I]) * gu[:, I:]
+        hq, hs = mx.quant_rows_32(h.numpy())
+        assert np.array_equal(hq, out["hq"]) and np.array_equal(hs, out["hs"])
+        o = F.linear(torch.from_numpy(mx.dequant_rows_32(hq, hs)),
+                     torch.from_numpy(mx.dequant_weight_k32(q2, s2, fmt)).T, torch.from_numpy(b2[0]))
+        np.testing.assert_allclose(out["y"], w * o.numpy(), rtol=1e-12, atol=1e-14)

@@ -92,3 +92,34 @@ def test_equals_w8a8_step_when_activations_are_exact_in_both():
     assert np.array_equal(ow.bf16_rne(a["hb"]), a["hb"])
     assert np.array_equal(codec.dequant_rows_128(b["hq"], b["hs"]), a["hb"])
     assert np.array_equal(a["y"], b["y"])
+
+
+def test_biased_expert_hand_values_and_torch_linear():
+    # the hand case of tests/golden/ffn_bias_hand.txt under W8A16: h = silu(2) = 1.76159...
+    # rounds to the bf16 value 225 * 2^-7 = 1.7578125 (step 2^-7 in [1, 2)), so
+    # o = 128 * 1.7578125 * 2^-7 + 0.25 = 2.0078125
+    H = I = 128
+    w13 = np.concatenate([np.full((H, I), 2.0 ** -7), np.full((H, I), 2.0 ** -6)], axis=1)
+    w2 = np.full((I, H), 2.0 ** -7)
+    b13 = np.concatenate([np.ones(I), -np.ones(I)])[None]
+    b2 = np.full((1, H), 0.25)
+    out = ow.forward(np.ones((1, H)), np.zeros((1, 1), np.int32), np.ones((1, 1)),
+                     _experts_from_dense([w13], [w2]), biases=(b13, b2))
+    assert (out["hb"] == 1.7578125).all() and (out["y"] == 2.0078125).all()
+    # random biased case against torch.nn.functional.linear with its bias argument
+    rng = np.random.default_rng(23)
+    H, I = 256, 128
+    x = torch.randn(3, H, generator=torch.Generator().manual_seed(4)).to(torch.bfloat16).double()
+    w13 = rng.normal(0, 0.02, (H, 2 * I))
+    w2 = rng.normal(0, 0.02, (I, H))
+    b13 = rng.normal(0, 0.5, (1, 2 * I))
+    b2 = rng.normal(0, 0.5, (1, H))
+    ex = _experts_from_dense([w13], [w2])
+    out = ow.forward(x.numpy(), np.zeros((3, 1), np.int32), np.ones((3, 1)), ex, biases=(b13, b2))
+    q13, s13, q2, s2 = ex.get(0)
+    F = torch.nn.functional
+    gu = F.linear(x, torch.from_numpy(codec.dequant_blocks_128(q13, s13)).T, torch.from_numpy(b13[0]))
+    hb = ow.bf16_rne((F.silu(gu[:, :I]) * gu[:, I:]).numpy())
+    assert np.array_equal(hb, out["hb"])
+    o = F.linear(torch.from_numpy(hb), torch.from_numpy(codec.dequant_blocks_128(q2, s2)).T, torch.from_numpy(b2[0]))
+    np.testing.assert_allclose(out["y"], o.numpy(), rtol=1e-12, atol=1e-14)
