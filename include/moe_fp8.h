@@ -279,6 +279,12 @@ typedef struct moe_ffn_args {
     float*         debug_h;
     uint8_t*       debug_hq;
     uint8_t*       debug_hs;
+    /* Optional per-expert biases (the w13_bias / w2_bias of the "Fused MoE" page's interface
+     * table), float32 device memory, 4-byte aligned, NULL for none; rows indexed by expert:
+     *   w13_bias [E, 2I]: gate columns then up columns, added to gu before SwiGLU;
+     *   w2_bias  [E, H]:  added to expert_out (before the routing weight of moe_combine). */
+    const float*   w13_bias;
+    const float*   w2_bias;
 } moe_ffn_args;
 
 int moe_grouped_ffn(const moe_ffn_args* a);
@@ -354,6 +360,12 @@ typedef struct moe_fused_args {
     int32_t        quant;       /* MOE_QUANT_*: packed weights and scales of that scheme */
     uint8_t*       act_q;       /* optional: the step's quantised activations go here */
     uint8_t*       act_scales;  /* optional: their UE8M0 scales */
+    /* Optional per-expert biases as in moe_ffn_args (float32, NULL for none): w13_bias [E, 2I]
+     * on the gate/up sums before SwiGLU, w2_bias [E, H] on each expert's output before its
+     * routing weight; with MOE_FUSED_SHARED_EXPERT both have E + 1 rows (row E: the shared
+     * expert's). */
+    const float*   w13_bias;
+    const float*   w2_bias;
 } moe_fused_args;
 
 int moe_fused(const moe_fused_args* a);

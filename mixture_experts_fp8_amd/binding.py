@@ -62,7 +62,7 @@ class FfnArgs(ctypes.Structure):
                 ("out_dtype", ctypes.c_int32), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p), ("quant", ctypes.c_int32),
                 ("x", ctypes.c_void_p), ("debug_h", ctypes.c_void_p), ("debug_hq", ctypes.c_void_p),
-                ("debug_hs", ctypes.c_void_p)]
+                ("debug_hs", ctypes.c_void_p), ("w13_bias", ctypes.c_void_p), ("w2_bias", ctypes.c_void_p)]
 
 
 class FusedArgs(ctypes.Structure):
@@ -74,7 +74,8 @@ class FusedArgs(ctypes.Structure):
                 ("expert_counts", ctypes.c_void_p), ("flags", ctypes.c_int32), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p),
                 ("stage_events", ctypes.POINTER(ctypes.c_void_p)), ("quant", ctypes.c_int32),
-                ("act_q", ctypes.c_void_p), ("act_scales", ctypes.c_void_p)]
+                ("act_q", ctypes.c_void_p), ("act_scales", ctypes.c_void_p), ("w13_bias", ctypes.c_void_p),
+                ("w2_bias", ctypes.c_void_p)]
 
 
 MOE_STAGES = 6
@@ -292,6 +293,8 @@ class PackedWeights:
     w2: torch.Tensor        # packed [E*I*H]
     w2_scale: torch.Tensor  # [E, I/128, H/128]
     quant: int = MOE_QUANT_FP8_BLOCK128   # MX schemes: packed MX weights and packed scales
+    w13_bias: Optional[torch.Tensor] = None   # optional float32 [E, 2I]: gate/up sums, before SwiGLU
+    w2_bias: Optional[torch.Tensor] = None    # optional float32 [E, H]: each expert's output
 
     @staticmethod
     def from_logical(w13q: torch.Tensor, w13s: torch.Tensor, w2q: torch.Tensor, w2s: torch.Tensor) -> "PackedWeights":
@@ -305,6 +308,14 @@ class PackedWeights:
         if self.quant != MOE_QUANT_FP8_BLOCK128 or quant not in (MOE_QUANT_FP8_BLOCK128, MOE_QUANT_W8A16):
             raise ValueError("only the 128-block E4M3 weights serve both MOE_QUANT_FP8_BLOCK128 and MOE_QUANT_W8A16")
         return dataclasses.replace(self, quant=quant)
+
+    def with_biases(self, w13_bias: Optional[torch.Tensor], w2_bias: Optional[torch.Tensor]) -> "PackedWeights":
+        """The same weights with per-expert biases (either may be None)."""
+        if w13_bias is not None:
+            _need(w13_bias, "w13_bias", torch.float32, (self.E, 2 * self.I))
+        if w2_bias is not None:
+            _need(w2_bias, "w2_bias", torch.float32, (self.E, self.H))
+        return dataclasses.replace(self, w13_bias=w13_bias, w2_bias=w2_bias)
 
 
 def pack_weights_mx(w13: torch.Tensor, w2: torch.Tensor, quant: int) -> PackedWeights:
@@ -351,7 +362,7 @@ def moe_grouped_ffn(xq: Optional[torch.Tensor], xs: Optional[torch.Tensor], rout
     a = FfnArgs(T, k, H, w.I, w.E, _ptr(xq), _ptr(xs), _ptr(routing["expert_counts"]),
                 _ptr(routing["expert_offsets"]), _ptr(routing["sorted_assign"]), _ptr(w.w13), _ptr(w.w13_scale),
                 _ptr(w.w2), _ptr(w.w2_scale), _ptr(out), dt, _ptr(ws), ws.numel(), _stream(), w.quant, _ptr(x),
-                _ptr(dh), _ptr(dhq), _ptr(dhs))
+                _ptr(dh), _ptr(dhq), _ptr(dhs), _ptr(w.w13_bias), _ptr(w.w2_bias))
     _check(lib().moe_grouped_ffn(ctypes.byref(a)))
     return (out, dh, dhq, dhs) if debug else out
 
@@ -412,7 +423,7 @@ class MoeFused:
                               _ptr(w.w13), _ptr(w.w13_scale), _ptr(w.w2), _ptr(w.w2_scale), _ptr(self.y),
                               _ptr(topk_ids), _ptr(topk_weights), _ptr(expert_counts), self.flags, _ptr(self.ws),
                               0 if self.ws is None else self.ws.numel(), None, None, w.quant, _ptr(act_q),
-                              _ptr(act_scales))
+                              _ptr(act_scales), _ptr(w.w13_bias), _ptr(w.w2_bias))
 
     def __call__(self, stream: Optional[int] = None, stage_events=None) -> torch.Tensor:
         """stage_events: None or a ctypes array of MOE_STAGES + 1 hipEvent_t handles that the

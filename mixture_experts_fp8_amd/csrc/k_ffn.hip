@@ -81,6 +81,7 @@ struct G1Args {
     const int4* pairs;       // 256-row items: {first tile, expert, first sorted row, valid rows}
     const int32_t* npairs;   // and the pair count
     float* htap;             // test output: float32 h [A, I] in sorted order (kernels built with TAP)
+    const float* b13;        // optional gate/up bias [E, 2I]
 };
 
 
@@ -229,6 +230,9 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm1(G1Args a) {
     }
 
     // ---- epilogue: h = silu(g) * u; per-row amax over the 128 columns; E4M3 requant
+    GuBias bias[NFW];
+#pragma unroll
+    for (int j = 0; j < NFW; ++j) bias[j] = gu_bias(a.b13, e, a.I, ib * 128 + (wn * NFW + j) * 16 + (lane & 15));
     float hv[MFW][NFW][4];
 #pragma unroll
     for (int mi = 0; mi < MFW; ++mi) {
@@ -237,8 +241,8 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm1(G1Args a) {
             float m = 0.f;
 #pragma unroll
             for (int j = 0; j < NFW; ++j) {
-                const float g = accg[mi][j][i];
-                const float h = g / (1.0f + expf(-g)) * accu[mi][j][i];
+                const float g = add_bias(a.b13, accg[mi][j][i], bias[j].g);
+                const float h = g / (1.0f + expf(-g)) * add_bias(a.b13, accu[mi][j][i], bias[j].u);
                 hv[mi][j][i] = h;
                 m = fmaxf(m, fabsf(h));
                 tap_h<TAP>(a.htap, a.I, rowbase, (wm * MFW + mi) * 16 + 4 * (lane >> 4) + i, nvalid,
@@ -292,6 +296,7 @@ struct G2Args {
     int ord;
     const int4* pairs;
     const int32_t* npairs;
+    const float* b2;         // optional down bias [E, H]
 };
 
 // down GEMM: wave (wm, wn) computes MFW m-frags x NFW column frags; the workgroup covers
@@ -400,6 +405,9 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm2(G2Args a) {
     }
 
     // ---- epilogue: rows in expert-sorted slot order
+    float bias[NFW];
+#pragma unroll
+    for (int j = 0; j < NFW; ++j) bias[j] = out_bias(a.b2, e, a.H, (n16 + j) * 16 + (lane & 15));
 #pragma unroll
     for (int mi = 0; mi < MFW; ++mi) {
 #pragma unroll
@@ -410,8 +418,9 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm2(G2Args a) {
 #pragma unroll
                 for (int j = 0; j < NFW; ++j) {
                     const int col = (n16 + j) * 16 + (lane & 15);
-                    if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o + col] = f32_to_bf16(acc[mi][j][i]);
-                    else reinterpret_cast<float*>(a.out)[o + col] = acc[mi][j][i];
+                    const float v = add_bias(a.b2, acc[mi][j][i], bias[j]);
+                    if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o + col] = f32_to_bf16(v);
+                    else reinterpret_cast<float*>(a.out)[o + col] = v;
                 }
             }
         }
@@ -523,14 +532,17 @@ __global__ __launch_bounds__(64 * WN) void k_gemm1_dec(G1Args a) {
         }
     }
     // epilogue: SwiGLU, row amax over the 128 columns (across the WN waves), requant
+    GuBias bias[NFW];
+#pragma unroll
+    for (int j = 0; j < NFW; ++j) bias[j] = gu_bias(a.b13, e, a.I, ib * 128 + (wn * NFW + j) * 16 + (lane & 15));
     float hv[NFW][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         float m = 0.f;
 #pragma unroll
         for (int j = 0; j < NFW; ++j) {
-            const float g = accg[j][i];
-            const float h = g / (1.0f + expf(-g)) * accu[j][i];
+            const float g = add_bias(a.b13, accg[j][i], bias[j].g);
+            const float h = g / (1.0f + expf(-g)) * add_bias(a.b13, accu[j][i], bias[j].u);
             hv[j][i] = h;
             m = fmaxf(m, fabsf(h));
             tap_h<TAP>(a.htap, a.I, rowbase, 4 * (lane >> 4) + i, nvalid, ib * 128 + (wn * NFW + j) * 16 + (lane & 15), h);
@@ -621,6 +633,9 @@ __global__ __launch_bounds__(64 * WN) void k_gemm2_dec(G2Args a) {
             }
         }
     }
+    float bias[NFW];
+#pragma unroll
+    for (int j = 0; j < NFW; ++j) bias[j] = out_bias(a.b2, e, a.H, (n16 + j) * 16 + (lane & 15));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = 4 * (lane >> 4) + i;
@@ -629,8 +644,9 @@ __global__ __launch_bounds__(64 * WN) void k_gemm2_dec(G2Args a) {
 #pragma unroll
             for (int j = 0; j < NFW; ++j) {
                 const int col = (n16 + j) * 16 + (lane & 15);
-                if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o + col] = f32_to_bf16(acc[j][i]);
-                else reinterpret_cast<float*>(a.out)[o + col] = acc[j][i];
+                const float v = add_bias(a.b2, acc[j][i], bias[j]);
+                if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o + col] = f32_to_bf16(v);
+                else reinterpret_cast<float*>(a.out)[o + col] = v;
             }
         }
     }
@@ -749,17 +765,19 @@ __device__ __forceinline__ void max16x4(float (&m)[4]) {
     for (int i = 0; i < 4; ++i) m[i] = fmaxf(m[i], dpp_f32<0x128>(m[i]));
 }
 
-// SwiGLU of one 16-row fragment: gate columns acc[jj], up columns acc[2 + jj] (jj = 0, 1)
-// -> h[jj][i]; m[i] = max |h| of row 4 (lane / 16) + i over the 32 columns of the two
-// fragments (in every lane of the 16-lane group).
-__device__ __forceinline__ void swiglu_frag(const v4f* acc, float (&h)[2][4], float (&m)[4]) {
+// SwiGLU of one 16-row fragment: gate columns acc[jj], up columns acc[2 + jj] (jj = 0, 1),
+// plus the lane's column biases when b13 is set -> h[jj][i]; m[i] = max |h| of row
+// 4 (lane / 16) + i over the 32 columns of the two fragments (in every lane of the 16-lane group).
+__device__ __forceinline__ void swiglu_frag(const v4f* acc, const float* b13, const GuBias (&bias)[2],
+                                            float (&h)[2][4], float (&m)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         m[i] = 0.f;
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
-            const float g = acc[jj][i];
-            h[jj][i] = g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.44269504f)) * acc[2 + jj][i];
+            const float g = add_bias(b13, acc[jj][i], bias[jj].g);
+            h[jj][i] = g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.44269504f)) *
+                       add_bias(b13, acc[2 + jj][i], bias[jj].u);
             m[i] = fmaxf(m[i], fabsf(h[jj][i]));
         }
     }
@@ -954,12 +972,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pf(G1Args a) {
     }
 
     // SwiGLU and per-row amax over the tile's 128 h columns (4 waves x 2 fragments)
+    GuBias bias[2];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) bias[jj] = gu_bias(a.b13, e, a.I, ib * 128 + (2 * wn + jj) * 16 + r16);
     float hv[4][2][4];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
         if (mi < nact) {
             float m[4];
-            swiglu_frag(acc[mi], hv[mi], m);
+            swiglu_frag(acc[mi], a.b13, bias, hv[mi], m);
             tap_frag<TAP>(a.htap, a.I, rowbase, (wm * 4 + mi) * 16, nvalid, ib * 128 + 2 * wn * 16, hv[mi]);
             if (r16 == 0) {
 #pragma unroll
@@ -1183,12 +1204,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pp(G1Args a) {
         }
 
         // ---- epilogue of item n (the next item's first block is in flight in the other stage)
+        GuBias bias[2];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) bias[jj] = gu_bias(a.b13, it.z, a.I, ib * 128 + (2 * wn + jj) * 16 + r16);
         float hv[4][2][4];
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
             if (mi < nact) {
                 float m[4];
-                swiglu_frag(acc[mi], hv[mi], m);
+                swiglu_frag(acc[mi], a.b13, bias, hv[mi], m);
                 tap_frag<TAP>(a.htap, a.I, it.w, (wm * 4 + mi) * 16, nvalid, ib * 128 + 2 * wn * 16, hv[mi]);
                 if (r16 == 0) {
 #pragma unroll
@@ -1330,6 +1354,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm2_pf(G2Args a) {
         }
     }
 
+    float bias[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bias[j] = out_bias(a.b2, e, a.H, nb * 256 + (wn * 4 + j) * 16 + (lane & 15));
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
@@ -1340,8 +1367,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm2_pf(G2Args a) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int col = nb * 256 + (wn * 4 + j) * 16 + (lane & 15);
-                    if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o + col] = f32_to_bf16(acc[mi][j][i]);
-                    else reinterpret_cast<float*>(a.out)[o + col] = acc[mi][j][i];
+                    const float v = add_bias(a.b2, acc[mi][j][i], bias[j]);
+                    if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o + col] = f32_to_bf16(v);
+                    else reinterpret_cast<float*>(a.out)[o + col] = v;
                 }
             }
         }
@@ -1531,12 +1559,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_p2(G1Args a) {
     else loop(std::false_type{});
 
     // SwiGLU, per-row amax over the item's 128 h columns (4 waves x 2 fragments)
+    GuBias bias[2];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) bias[jj] = gu_bias(a.b13, e, a.I, ib * 128 + (2 * wn + jj) * 16 + r16);
     float hv[8][2][4];
 #pragma unroll
     for (int mi = 0; mi < 8; ++mi) {
         if (mi < nact) {
             float m[4];
-            swiglu_frag(acc[mi], hv[mi], m);
+            swiglu_frag(acc[mi], a.b13, bias, hv[mi], m);
             tap_frag<TAP>(a.htap, a.I, rowbase, (wm * 8 + mi) * 16, nvalid, ib * 128 + 2 * wn * 16, hv[mi]);
             if (r16 == 0) {
 #pragma unroll
@@ -1687,6 +1718,17 @@ __global__ __launch_bounds__(512, 1) void k_gemm2_p2(G2Args a) {
         }
     }
 
+    if (a.b2) {   // down bias of the lane's columns
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float bv = a.b2[(int64_t)e * a.H + nb * 256 + wn * 64 + 16 * j + r16];
+#pragma unroll
+            for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[mi][j][i] += bv;
+        }
+    }
+
     // Output: the tile goes through the LDS stages (free after the K loop) so that it leaves as
     // whole 16-byte pieces of full rows.  A lane holds rows wm * 128 + 16 mi + 4 (lane / 16) + i
     // of columns wn * 64 + 16 j + lane % 16.  LDS rows are swizzled by 16 columns times
@@ -1764,7 +1806,12 @@ static int ffn_super_tile_order_down(int ntiles_max) { return ntiles_max >= 1024
 
 static G1Args g1_args(const FfnArgs& f, const FfnWs& w, int ord) {
     return G1Args{f.xq, f.xs, f.T, f.k, f.H, f.I, f.counts, f.offsets, f.sorted_assign, w.tiles, w.ntiles, f.w13p,
-                  f.w13s, w.hq, w.hs, ord, w.pairs, w.npairs, f.debug_h};
+                  f.w13s, w.hq, w.hs, ord, w.pairs, w.npairs, f.debug_h, f.b13};
+}
+
+static G2Args g2_args(const FfnArgs& f, const FfnWs& w, int ord) {
+    return G2Args{w.hq, w.hs, f.H, f.I, f.counts, f.offsets, w.tiles, w.ntiles, f.w2p, f.w2s, f.out, f.out_bf16,
+                  ord, w.pairs, w.npairs, f.b2};
 }
 
 template <int MFW, int NFW1, int NFW2, int WM, int WN, int PF1, int PF2>
@@ -1775,8 +1822,7 @@ static hipError_t run_ffn(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hi
         const hipError_t e = hipEventRecord(mid, st);
         if (e != hipSuccess) return e;
     }
-    G2Args g2{w.hq, w.hs, f.H, f.I, f.counts, f.offsets, w.tiles, w.ntiles, f.w2p, f.w2s, f.out, f.out_bf16,
-              ffn_super_tile_order(p.ntiles_max)};
+    const G2Args g2 = g2_args(f, w, ffn_super_tile_order(p.ntiles_max));
     const int ncols = 16 * NFW2 * WN;
     hipLaunchKernelGGL((k_gemm2<MFW, NFW2, WM, WN, PF2>), dim3(p.ntiles_max, f.H / ncols), dim3(64 * WM * WN), 0,
                        st, g2);
@@ -1791,16 +1837,14 @@ static hipError_t run_ffn_dec(const FfnArgs& f, const FfnPlan& p, const FfnWs& w
         const hipError_t e = hipEventRecord(mid, st);
         if (e != hipSuccess) return e;
     }
-    G2Args g2{w.hq, w.hs, f.H, f.I, f.counts, f.offsets, w.tiles, w.ntiles, f.w2p, f.w2s, f.out, f.out_bf16,
-              ffn_super_tile_order(p.ntiles_max)};
+    const G2Args g2 = g2_args(f, w, ffn_super_tile_order(p.ntiles_max));
     hipLaunchKernelGGL((k_gemm2_dec<NFW2, WN2, PF2>), dim3(p.ntiles_max, f.H / (16 * NFW2 * WN2)), dim3(64 * WN2), 0,
                        st, g2);
     return hipGetLastError();
 }
 
 static hipError_t launch_gemm2_p2(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, int ord, hipStream_t st) {
-    G2Args g2{w.hq, w.hs, f.H, f.I, f.counts, f.offsets, w.tiles, w.ntiles, f.w2p, f.w2s, f.out, f.out_bf16, ord,
-              w.pairs, w.npairs};
+    const G2Args g2 = g2_args(f, w, ord);
     const int grid2 = ord ? kXcds * ord_ranks(p.npairs_max, f.H / 256)
                           : (int)(ceil_div((int64_t)(f.H / 256) * p.npairs_max, kXcds) * kXcds);
     hipLaunchKernelGGL(k_gemm2_p2, dim3(grid2), dim3(512), 0, st, g2);
@@ -1834,8 +1878,7 @@ static hipError_t run_ffn_pf(const FfnArgs& f, const FfnPlan& p, const FfnWs& w,
             hipLaunchKernelGGL(k_pairs, dim3(1), dim3(1024), 0, st, f.counts, f.offsets, f.E, w.pairs, w.npairs);
         return launch_gemm2_p2(f, p, w, ffn_super_tile_order_down(p.ntiles_max), st);
     }
-    G2Args g2{w.hq, w.hs, f.H, f.I, f.counts, f.offsets, w.tiles, w.ntiles, f.w2p, f.w2s, f.out, f.out_bf16,
-              ffn_super_tile_order(p.ntiles_max)};
+    const G2Args g2 = g2_args(f, w, ffn_super_tile_order(p.ntiles_max));
 #ifndef MOE_NO_RB
     // the persistent down GEMM (k_ffn_rb.hip) where its item tables fit
     if (ffn_rb_supported(f.H, f.I, f.E, p.ntiles_max)) return launch_gemm2_rb(f, w, p.ntiles_max, g2.ord, st);

@@ -140,6 +140,7 @@ struct Rb2Args {
     void* out;                  // [A, H] fp32 or bf16, expert-sorted rows
     int out_bf16;
     int ord;                    // 1: super-tile work order (ord_item), 0: column blocks per tile group
+    const float* b2;            // optional down bias [E, H]
 };
 
 template <int P, int MT>
@@ -237,6 +238,9 @@ __global__ __launch_bounds__(kRbThreads, 1) void k_gemm2_rb(Rb2Args a) {
         // tests as comparisons with constants
         const int r0 = 4 * (lane >> 4), lim = nvalid - r0;
         const int64_t o0 = (int64_t)(rowbase + r0) * a.H + col * 256 + wv * 32 + (lane & 15);
+        float bias[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) bias[j] = out_bias(a.b2, it.z, a.H, col * 256 + wv * 32 + 16 * j + (lane & 15));
 #pragma unroll
         for (int mi = 0; mi < MF; ++mi) {
 #pragma unroll
@@ -245,8 +249,9 @@ __global__ __launch_bounds__(kRbThreads, 1) void k_gemm2_rb(Rb2Args a) {
                     const int64_t o = o0 + (int64_t)(mi * 16 + i) * a.H;
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
-                        if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o + j * 16] = f32_to_bf16(acc[mi][j][i]);
-                        else reinterpret_cast<float*>(a.out)[o + j * 16] = acc[mi][j][i];
+                        const float v = add_bias(a.b2, acc[mi][j][i], bias[j]);
+                        if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o + j * 16] = f32_to_bf16(v);
+                        else reinterpret_cast<float*>(a.out)[o + j * 16] = v;
                     }
                 }
             }
@@ -341,7 +346,7 @@ hipError_t launch_gemm2_rb(const FfnArgs& f, const FfnWs& w, int ntiles_max, int
     hipLaunchKernelGGL(k_rb_scales, dim3((unsigned)std::min<int64_t>(1024, ceil_div(n, 256))), dim3(256), 0, st, f.w2s,
                        f.E, KB, NBS, w.bs);
     Rb2Args g2{w.hq, w.hs, w.bs, f.H, f.I, f.E, ntiles_max, w.tiles, w.ntiles, f.counts, f.offsets, f.w2p, f.out,
-               f.out_bf16, ord};
+               f.out_bf16, ord, f.b2};
     hipLaunchKernelGGL((k_gemm2_rb<MOE_RB_P, MOE_RB_MT>), dim3(persistent_grid()), dim3(kRbThreads), 0, st, g2);
     return hipGetLastError();
 }

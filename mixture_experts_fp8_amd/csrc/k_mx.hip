@@ -220,6 +220,7 @@ struct MxG1Args {
     uint8_t* hq;                // [tile][I/128][2 KB]
     uint8_t* hs;                // [tile*16 + row][I/32]
     float* htap;                // test output: float32 h [A, I] (kernels built with TAP)
+    const float* b13;           // optional gate/up bias [E, 2I]
 };
 
 template <int WF>
@@ -297,11 +298,12 @@ __global__ __launch_bounds__(512) void k_gemm1_mx(MxG1Args a) {
         }
     }
     // SwiGLU, then E4M3 per (row, 32 columns): the pair of waves 2g, 2g+1 holds group g
+    const GuBias bias = gu_bias(a.b13, e, a.I, ib * 128 + wn * 16 + (lane & 15));
     float hv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const float g = accg[i];
-        hv[i] = g / (1.0f + expf(-g)) * accu[i];
+        const float g = add_bias(a.b13, accg[i], bias.g);
+        hv[i] = g / (1.0f + expf(-g)) * add_bias(a.b13, accu[i], bias.u);
         tap_h<TAP>(a.htap, a.I, rowbase, 4 * (lane >> 4) + i, nvalid, ib * 128 + wn * 16 + (lane & 15), hv[i]);
         const float m = max16(fabsf(hv[i]));
         if ((lane & 15) == 0) s_amax[wn][4 * (lane >> 4) + i] = m;
@@ -337,6 +339,7 @@ struct MxG2Args {
     const uint8_t* w2sp;        // packed scales [E][H/16][I/128][64]
     void* out;
     int out_bf16;
+    const float* b2;            // optional down bias [E, H]
 };
 
 // workgroup: one 16-row tile x 128 output columns, 4 waves of 2 fragments
@@ -388,6 +391,9 @@ __global__ __launch_bounds__(256) void k_gemm2_mx(MxG2Args a) {
             }
         }
     }
+    float bias[NFW];
+#pragma unroll
+    for (int j = 0; j < NFW; ++j) bias[j] = out_bias(a.b2, e, a.H, (n16 + j) * 16 + (lane & 15));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = 4 * (lane >> 4) + i;
@@ -396,8 +402,9 @@ __global__ __launch_bounds__(256) void k_gemm2_mx(MxG2Args a) {
 #pragma unroll
             for (int j = 0; j < NFW; ++j) {
                 const int col = (n16 + j) * 16 + (lane & 15);
-                if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o + col] = f32_to_bf16(acc[j][i]);
-                else reinterpret_cast<float*>(a.out)[o + col] = acc[j][i];
+                const float v = add_bias(a.b2, acc[j][i], bias[j]);
+                if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o + col] = f32_to_bf16(v);
+                else reinterpret_cast<float*>(a.out)[o + col] = v;
             }
         }
     }
@@ -447,14 +454,14 @@ hipError_t launch_prepack_mx(const uint8_t* q, const uint8_t* s, int E, int K, i
 template <int WF>
 static hipError_t run_ffn_mx(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid) {
     MxG1Args g1{f.xq, f.xs, f.T, f.k, f.H, f.I, f.counts, f.offsets, f.sorted_assign, w.tiles, w.ntiles,
-                f.w13p, f.w13s, w.hq, w.hs, f.debug_h};
+                f.w13p, f.w13s, w.hq, w.hs, f.debug_h, f.b13};
     if (f.debug_h) hipLaunchKernelGGL((k_gemm1_mx<WF, 2, true>), dim3(p.ntiles_max, f.I / kGroup), dim3(512), 0, st, g1);
     else hipLaunchKernelGGL((k_gemm1_mx<WF, 2, false>), dim3(p.ntiles_max, f.I / kGroup), dim3(512), 0, st, g1);
     if (mid) {
         const hipError_t e = hipEventRecord(mid, st);
         if (e != hipSuccess) return e;
     }
-    MxG2Args g2{w.hq, w.hs, f.H, f.I, f.counts, f.offsets, w.tiles, w.ntiles, f.w2p, f.w2s, f.out, f.out_bf16};
+    MxG2Args g2{w.hq, w.hs, f.H, f.I, f.counts, f.offsets, w.tiles, w.ntiles, f.w2p, f.w2s, f.out, f.out_bf16, f.b2};
     hipLaunchKernelGGL((k_gemm2_mx<WF, 2>), dim3(p.ntiles_max, f.H / 128), dim3(256), 0, st, g2);
     return hipGetLastError();
 }

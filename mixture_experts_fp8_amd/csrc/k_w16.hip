@@ -41,6 +41,7 @@ struct W16G1Args {
     const uint8_t* w13s;   // UE8M0 [E][H/128][2I/128]
     uint16_t* hb;          // [tile][16][I] bf16
     float* htap;           // test output: float32 h [A, I] before the bf16 rounding (kernels built with TAP)
+    const float* b13;      // optional gate/up bias [E, 2I]
 };
 
 struct W16G2Args {
@@ -54,6 +55,7 @@ struct W16G2Args {
     const uint8_t* w2s;    // UE8M0 [E][I/128][H/128]
     void* out;
     int out_bf16;
+    const float* b2;       // optional down bias [E, H]
 };
 
 // The 32 bf16 weights of one lane's fragment, scaled by 2^(s - 127) (sc carries s in its
@@ -141,10 +143,11 @@ __global__ __launch_bounds__(512) void k_gemm1_w16(W16G1Args a) {
     }
     // SwiGLU in float32, one bf16 rounding; lane holds rows 4 (lane / 16) + i of column
     // wn * 16 + lane % 16 of the block
+    const GuBias bias = gu_bias(a.b13, e, a.I, ib * 128 + wn * 16 + (lane & 15));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const float g = accg[i];
-        const float h = g / (1.0f + expf(-g)) * accu[i];
+        const float g = add_bias(a.b13, accg[i], bias.g);
+        const float h = g / (1.0f + expf(-g)) * add_bias(a.b13, accu[i], bias.u);
         tap_h<TAP>(a.htap, a.I, rowbase, 4 * (lane >> 4) + i, nvalid, ib * 128 + wn * 16 + (lane & 15), h);
         s_h[(4 * (lane >> 4) + i) * 128 + wn * 16 + (lane & 15)] = f32_to_bf16(h);
     }
@@ -214,6 +217,9 @@ __global__ __launch_bounds__(64 * WN) void k_gemm2_w16(W16G2Args a) {
             }
         }
     }
+    float bias[NFW];
+#pragma unroll
+    for (int j = 0; j < NFW; ++j) bias[j] = out_bias(a.b2, e, a.H, (n16 + j) * 16 + (lane & 15));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = 4 * (lane >> 4) + i;
@@ -222,8 +228,9 @@ __global__ __launch_bounds__(64 * WN) void k_gemm2_w16(W16G2Args a) {
 #pragma unroll
             for (int j = 0; j < NFW; ++j) {
                 const int col = (n16 + j) * 16 + (lane & 15);
-                if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o + col] = f32_to_bf16(acc[j][i]);
-                else reinterpret_cast<float*>(a.out)[o + col] = acc[j][i];
+                const float v = add_bias(a.b2, acc[j][i], bias[j]);
+                if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o + col] = f32_to_bf16(v);
+                else reinterpret_cast<float*>(a.out)[o + col] = v;
             }
         }
     }
@@ -246,14 +253,14 @@ hipError_t launch_ffn_w16(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hi
     if (f.H / kGroup > kW16MaxKB || f.I / kGroup > kW16MaxKB) return hipErrorInvalidValue;
     uint16_t* hb = reinterpret_cast<uint16_t*>(w.hq);
     W16G1Args g1{f.x, f.T, f.k, f.H, f.I, f.counts, f.offsets, f.sorted_assign, w.tiles, w.ntiles, f.w13p, f.w13s, hb,
-                 f.debug_h};
+                 f.debug_h, f.b13};
     if (f.debug_h) hipLaunchKernelGGL((k_gemm1_w16<MOE_W16_PF1, true>), dim3(p.ntiles_max, f.I / kGroup), dim3(512), 0, st, g1);
     else hipLaunchKernelGGL((k_gemm1_w16<MOE_W16_PF1, false>), dim3(p.ntiles_max, f.I / kGroup), dim3(512), 0, st, g1);
     if (mid) {
         const hipError_t e = hipEventRecord(mid, st);
         if (e != hipSuccess) return e;
     }
-    W16G2Args g2{hb, f.H, f.I, f.counts, f.offsets, w.tiles, w.ntiles, f.w2p, f.w2s, f.out, f.out_bf16};
+    W16G2Args g2{hb, f.H, f.I, f.counts, f.offsets, w.tiles, w.ntiles, f.w2p, f.w2s, f.out, f.out_bf16, f.b2};
     launch_gemm2_w16<MOE_W16_GEMM2>(g2, p.ntiles_max, f.H, st);
     return hipGetLastError();
 }

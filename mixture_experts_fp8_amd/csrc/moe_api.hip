@@ -151,7 +151,7 @@ int moe_grouped_ffn(const moe_ffn_args* a) {
     moe::FfnArgs f{a->T, a->k, a->H, a->I, a->E, a->xq, a->xs, a->expert_counts, a->expert_offsets,
                    a->sorted_assign, a->w13, a->w13_scale, a->w2, a->w2_scale, a->expert_out,
                    a->out_dtype == MOE_DTYPE_BF16, a->quant, w16 ? a->x : nullptr,
-                   a->debug_h, a->debug_hq, a->debug_hs};
+                   a->debug_h, a->debug_hq, a->debug_hs, a->w13_bias, a->w2_bias};
     const hipError_t e = moe::launch_grouped_ffn(f, a->workspace, static_cast<hipStream_t>(a->stream));
     if (e != hipSuccess) return hip_fail("moe_grouped_ffn", e);
     return ok();
@@ -209,7 +209,7 @@ int run_fused(const char* op, const moe_fused_args* a, uint8_t* base) {
     const bool mx = a->quant == MOE_QUANT_MXFP8 || a->quant == MOE_QUANT_W4A8;
     const bool w16 = a->quant == MOE_QUANT_W8A16;   // the bf16 hidden states go in as they are
     moe::FfnArgs f{T, kf, H, I, Ef, xq, xs, counts, offsets, sorted, a->w13, a->w13_scale, a->w2, a->w2_scale, eo, bf,
-                   a->quant, w16 ? a->hidden_states : nullptr};
+                   a->quant, w16 ? a->hidden_states : nullptr, nullptr, nullptr, nullptr, a->w13_bias, a->w2_bias};
     const moe::FfnWs fw = moe::carve_ffn_ws(f, fws);
     const moe::FfnPlan plan = moe::ffn_plan(T, kf, Ef, a->quant);
     moe::RouteCfg rcfg = route_cfg(&a->route, T, a->prelude != nullptr);

@@ -177,6 +177,22 @@ __device__ __forceinline__ void tap_h(float* htap, int I, int rowbase, int row, 
     }
 }
 
+// Optional per-expert biases, float32, NULL for none: b13 [E, 2I] (gate columns, then up
+// columns) is added to the gate and up sums before SwiGLU, b2 [E, H] to the down GEMM's output
+// row.  Without biases the sums pass through unchanged (no +0 is added).
+struct GuBias {
+    float g, u;
+};
+__device__ __forceinline__ GuBias gu_bias(const float* b13, int e, int I, int col) {
+    if (!b13) return GuBias{0.f, 0.f};
+    const float* p = b13 + (int64_t)e * 2 * I + col;
+    return GuBias{p[0], p[I]};
+}
+__device__ __forceinline__ float add_bias(const float* b, float v, float bv) { return b ? v + bv : v; }
+__device__ __forceinline__ float out_bias(const float* b2, int e, int H, int col) {
+    return b2 ? b2[(int64_t)e * H + col] : 0.f;
+}
+
 // Work order of the 128-row-tile GEMMs (items = tile x column block).  The workgroups of
 // one XCD share its L2; all XCDs share the Infinity Cache.  Items come in super-tiles of
 // 8 consecutive tiles x 4 column blocks (32 items, one per workgroup running on an XCD, so

@@ -132,6 +132,13 @@ thread_local char g_err[512];
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// optional float32 biases: NULL or 4-byte aligned
+int check_biases(const char* op, const float* b13, const float* b2) {
+    if ((b13 && !aligned(b13, 4)) || (b2 && !aligned(b2, 4)))
+        return fail(MOE_ERR_INVALID, "%s: w13_bias and w2_bias must be 4-byte aligned", op);
+    return MOE_OK;
+}
+
 bool valid_quant(int q) {
     return q == MOE_QUANT_FP8_BLOCK128 || q == MOE_QUANT_MXFP8 || q == MOE_QUANT_W4A8 || q == MOE_QUANT_W8A16;
 }
@@ -338,6 +345,7 @@ int check_grouped_ffn(const moe_ffn_args* a) {
         return fail(MOE_ERR_INVALID, "%s: out_dtype (%d) must be MOE_DTYPE_F32 or MOE_DTYPE_BF16", op, a->out_dtype);
     if (!aligned(w16 ? (const void*)a->x : (const void*)a->xq, 16))
         return fail(MOE_ERR_UNSUPPORTED, "%s: %s must be 16-byte aligned", op, w16 ? "x" : "xq");
+    if ((rc = check_biases(op, a->w13_bias, a->w2_bias))) return rc;
     if (a->debug_h) {
         if (!a->debug_hq || (!w16 && !a->debug_hs))
             return fail(MOE_ERR_INVALID, "%s: debug_h needs debug_hq%s", op, w16 ? "" : " and debug_hs");
@@ -419,6 +427,7 @@ int check_fused_common(const char* op, const moe_fused_args* a, size_t* need_out
     if (!valid_quant(a->quant)) return fail(MOE_ERR_INVALID, "%s: quant (%d) must be one of MOE_QUANT_*", op, a->quant);
     if (!aligned(a->hidden_states, 16) || !aligned(a->y, 8))
         return fail(MOE_ERR_UNSUPPORTED, "%s: hidden_states must be 16-byte and y 8-byte aligned", op);
+    if ((rc = check_biases(op, a->w13_bias, a->w2_bias))) return rc;
     *need_out = fused_ws_layout(T, H, I, E + sh, k + sh, (a->flags & MOE_FUSED_EXPERT_OUT_BF16) ? 2 : 4).end;
     if ((a->act_q && !aligned(a->act_q, 16)) || (a->act_scales && !aligned(a->act_scales, 16)))
         return fail(MOE_ERR_INVALID, "%s: act_q and act_scales must be 16-byte aligned", op);

@@ -78,6 +78,9 @@ struct FfnArgs {
     float* debug_h = nullptr;
     uint8_t* debug_hq = nullptr;
     uint8_t* debug_hs = nullptr;
+    // optional float32 biases: gate/up sums [E, 2I] (before SwiGLU), down output [E, H]
+    const float* b13 = nullptr;
+    const float* b2 = nullptr;
 };
 struct FfnWs {
     int2* tiles;

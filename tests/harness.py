@@ -158,7 +158,19 @@ def device_weights(wl: W.Workload, device="cuda") -> M.PackedWeights:
         q, s = M.moe_quant_weight_blocks(W.expert_weight_f32(wl, "w2", e, device)[None])
         w2s[e] = s[0]
         w2p[e * I * H:(e + 1) * I * H] = M.moe_prepack_weights(q)
-    return M.PackedWeights(E, H, I, w13p, w13s, w2p, w2s)
+    return _with_biases(wl, M.PackedWeights(E, H, I, w13p, w13s, w2p, w2s), device)
+
+
+def _with_biases(wl: W.Workload, w: M.PackedWeights, device) -> M.PackedWeights:
+    return w.with_biases(*W.expert_ffn_biases(wl, device)) if wl.ffn_bias else w
+
+
+def oracle_biases(wl: W.Workload):
+    """The workload's expert biases as float64 arrays for the oracle, or None."""
+    if not wl.ffn_bias:
+        return None
+    b13, b2 = W.expert_ffn_biases(wl)
+    return b13.numpy().astype(np.float64), b2.numpy().astype(np.float64)
 
 
 def device_weights_mx(wl: W.Workload, quant: int, device="cuda") -> M.PackedWeights:
@@ -180,7 +192,7 @@ def device_weights_mx(wl: W.Workload, quant: int, device="cuda") -> M.PackedWeig
         pq, ps = M.moe_prepack_weights_mx(q, s, wfmt)
         w2p[e * n2:(e + 1) * n2] = pq
         w2s[e * ps.numel():(e + 1) * ps.numel()] = ps
-    return M.PackedWeights(E, H, I, w13p, w13s, w2p, w2s, quant)
+    return _with_biases(wl, M.PackedWeights(E, H, I, w13p, w13s, w2p, w2s, quant), device)
 
 
 def oracle_experts_mx_for(wl: W.Workload, fmt: str, experts, workers: int = 8):

@@ -137,6 +137,10 @@ def test_grouped_ffn_validation():
     assert _ffn(debug_hq=FAKE) == B.MOE_ERR_INVALID and "only with debug_h" in M.moe_last_error()
     assert _ffn(debug_h=FAKE, debug_hq=FAKE) == B.MOE_ERR_INVALID and "debug_hs" in M.moe_last_error()
     assert _ffn(debug_h=FAKE, debug_hq=FAKE, debug_hs=FAKE, workspace_bytes=10) == B.MOE_ERR_WORKSPACE
+    # the optional float32 biases: 4-byte aligned; valid ones pass on to the workspace check
+    assert _ffn(w13_bias=FAKE + 2) == B.MOE_ERR_INVALID and "w13_bias" in M.moe_last_error()
+    assert _ffn(w2_bias=FAKE + 1) == B.MOE_ERR_INVALID
+    assert _ffn(w13_bias=FAKE + 4, w2_bias=FAKE, workspace_bytes=10) == B.MOE_ERR_WORKSPACE
 
 
 def test_32bit_offset_limits():
@@ -190,6 +194,9 @@ def test_fused_validation():
     assert _fused(act_scales=FAKE + 4) == B.MOE_ERR_INVALID
     assert _fused(quant=B.MOE_QUANT_W8A16, act_q=FAKE) == B.MOE_ERR_INVALID
     assert "W8A16" in M.moe_last_error()
+    assert _fused(w13_bias=FAKE + 2) == B.MOE_ERR_INVALID and "bias" in M.moe_last_error()
+    assert _fused(w2_bias=FAKE + 6, workspace_bytes=1000) == B.MOE_ERR_INVALID
+    assert _fused(w13_bias=FAKE, w2_bias=FAKE + 4, workspace_bytes=1000) == B.MOE_ERR_WORKSPACE
     # 1024 routed experts plus the shared one exceed the dispatch's expert limit
     assert _fused(route=M.route_params(1024, 8), flags=B.MOE_FUSED_SHARED_EXPERT) == B.MOE_ERR_UNSUPPORTED
     assert "exceeds max" in M.moe_last_error()

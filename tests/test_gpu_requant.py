@@ -89,7 +89,7 @@ def _check(wl, scheme, tokens=None, extra_rows=()):
         assert len(bad) == 0, f"{len(bad)} rows differ, first sorted rows {rows[bad[:8]]}"
     # 2. h against the oracle's float64 h on the sampled tokens' rows
     fm = {"fp8": omoe.forward, "w8a16": ow.forward}.get(scheme, omx.forward)
-    ref = fm(xf, ids_ref, w_ref, None, tokens=tok, ffn_map=HN.oracle_ffn_map(wl, scheme))
+    ref = fm(xf, ids_ref, w_ref, None, tokens=tok, ffn_map=HN.oracle_ffn_map(wl, scheme), biases=HN.oracle_biases(wl))
     h_dev = h[torch.from_numpy(slots).to(DEV)].cpu().numpy().astype(np.float64)
     d = np.abs(h_dev - ref["h"])
     ratio = d / np.maximum(ref["h_err"], 1e-300)
