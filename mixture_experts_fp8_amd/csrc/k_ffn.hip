@@ -17,6 +17,7 @@
 // from memory into registers PF K-blocks ahead, 2 KB contiguous per operand.
 #include "moe_common.h"
 #include "moe_internal.h"
+#include "mx_common.h"
 #include "work_items.h"
 
 #include <algorithm>
@@ -1377,6 +1378,353 @@ __global__ __launch_bounds__(512, 1) void k_gemm2_pf(G2Args a) {
 }
 
 // ----------------------------------------------------------------------------------------
+// Micro-scaled gate/up and down GEMMs on 128-row tiles (MXFP8: E4M3 weights; W4A8: E2M1
+// weights): the tile shape, work order and three-stage LDS ring of k_gemm1_pf / k_gemm2_pf
+// with one UE8M0 scale per 32 elements.  Per K block a stage holds the A operand (128 rows of
+// 128 bytes), the 16 weight fragments (2 KB E4M3 or 1 KB E2M1, packed as for the 16-row MX
+// kernels), the A rows' four scale bytes (one dword per row) and the fragments' 64 per-lane
+// scale bytes; the scales ride LDS-DMA copies beside the operands, so one wait covers a
+// block.  Every E4M3 operand is in the matrix instruction's K order (lane group G = lane / 16
+// holds K 16 G .. +15 and 64 + 16 G .. +15 of its row), so each lane's scale byte covers one
+// 32-element group: the activation fragment reads take 16-byte chunks G and G + 4 of the
+// swizzled row, the re-quantised h is stored for the down GEMM in that order, and its scales
+// as [tile row][I / 32].
+template <int WF>
+struct MxPf {
+    static constexpr int FB = WF == kWfmtE2M1 ? 1024 : 2048;   // bytes per weight fragment
+    static constexpr int NBI = 16 * FB / 8192;                 // weight copies per thread and block
+    static constexpr int SA = kPfStageA + 16 * FB;             // A-row scales: one dword per row
+    static constexpr int SB = SA + kPfBM * 4;                  // weight scales: [fragment][lane]
+    static constexpr int Stage = SB + 16 * 64;
+    static constexpr int Ops = 2 + NBI + 1;                    // copies per thread and block
+};
+
+// The stage's weight fragment f as an operand (E2M1: the lane's 16 bytes, upper half unused).
+template <int WF>
+__device__ __forceinline__ v8i mx_lds_wfrag(const uint8_t* stage, int f, int lane) {
+    if constexpr (WF == kWfmtE2M1) {
+        const uint4 v = *reinterpret_cast<const uint4*>(stage + kPfStageA + f * 1024 + lane * 16);
+        return v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+    } else {
+        return lds_frag(stage + kPfStageA + f * 2048, lane);
+    }
+}
+
+// Scale byte of lane group G from a stage's A-row scale dword of row `row`.
+template <int WF>
+__device__ __forceinline__ int mx_lds_ascale(const uint8_t* stage, int row, int G) {
+    return (int)((*reinterpret_cast<const uint32_t*>(stage + MxPf<WF>::SA + row * 4) >> (8 * G)) & 0xFFu);
+}
+
+template <int WF, bool TAP>
+__global__ __launch_bounds__(512, 1) void k_gemm1_mxpf(G1Args a) {
+    using C = MxPf<WF>;
+    int ib, tile;
+    if (!pf_work_item(a.ord, a.I / kGroup, __builtin_amdgcn_readfirstlane(*a.ntiles), tile, ib)) return;
+    const int2 te = a.tiles[tile];
+    const int e = __builtin_amdgcn_readfirstlane(te.x), m0 = __builtin_amdgcn_readfirstlane(te.y);
+    const int nvalid = min(kPfBM, a.counts[e] - m0);
+    const int rowbase = __builtin_amdgcn_readfirstlane(a.offsets[e] + m0);
+    const int KB = a.H / kGroup, KS = a.H / kMx;
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wv >> 2, wn = wv & 3;
+
+    __shared__ __align__(16) uint8_t buf[kPfdStages * C::Stage];
+
+    const int NB16 = 2 * a.I / 16;
+    const v4i_t ra = make_srd(a.xq, (uint32_t)a.T * a.H);
+    const v4i_t rw = make_srd(a.w13p + (int64_t)e * NB16 * KB * C::FB, (uint32_t)NB16 * KB * C::FB);
+    const v4i_t rxs = make_srd(a.xs, (uint32_t)a.T * KS);
+    const v4i_t rws = make_srd(a.w13s + (int64_t)e * NB16 * KB * 64, (uint32_t)NB16 * KB * 64);
+    auto n16_of = [&](int f) { return f < 8 ? ib * 8 + f : a.I / 16 + ib * 8 + (f - 8); };
+    // A pieces as in k_gemm1_pf: rows 8 (wv + 8 i) + lane / 8, whole lines, chunk c of row r at
+    // r * 128 + 16 (c ^ (r % 8)).  Scale copies, one dword per lane: waves 0, 1 (and, as
+    // duplicates of the same bytes, 6, 7) bring row (wv % 2) * 64 + lane's four A scales of the
+    // block; waves 2..5 bring the 16 fragments' per-lane weight scales.
+    const bool sc_a = wv < 2 || wv >= 6;
+    const int sr = (wv & 1) * 64 + lane;
+    int tok[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        const int r = i < 2 ? 8 * (wv + 8 * i) + (lane >> 3) : sr;
+        tok[i] = a.sorted_assign[rowbase + min(r, nvalid - 1)] / a.k;
+    }
+    uint32_t aoff[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) aoff[i] = (uint32_t)tok[i] * a.H + (((lane & 7) ^ (lane >> 3)) << 4);
+    uint32_t bsoff[C::NBI];
+#pragma unroll
+    for (int i = 0; i < C::NBI; ++i) {
+        const int b = (wv * 64 + 512 * i) * 16;   // this wave's byte of the stage's fragments
+        bsoff[i] = __builtin_amdgcn_readfirstlane(n16_of(b / C::FB) * KB * C::FB + b % C::FB);
+    }
+    uint32_t scoff;
+    if (sc_a) {
+        scoff = (uint32_t)tok[2] * KS;
+    } else {
+        const int t = (wv - 2) * 64 + lane;
+        scoff = (uint32_t)n16_of(t >> 4) * KB * 64 + (t & 15) * 4;
+    }
+    const uint32_t l16 = lane * 16;
+    const uint32_t lds_w = lds_addr(buf) + wv * 1024;
+    const uint32_t lds_s = lds_addr(buf) + (sc_a ? C::SA + (wv & 1) * 256 : C::SB + (wv - 2) * 256);
+    auto issue = [&](int kb, int s) {
+        const uint32_t st = __builtin_amdgcn_readfirstlane(lds_w + s * C::Stage);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) dma16_async(ra, st + i * 8192, aoff[i], kb * kGroup);
+#pragma unroll
+        for (int i = 0; i < C::NBI; ++i) dma16_async(rw, st + kPfStageA + i * 8192, l16, bsoff[i] + kb * C::FB);
+        const uint32_t ss = __builtin_amdgcn_readfirstlane(lds_s + s * C::Stage);
+        if (sc_a) dma4_async(rxs, ss, scoff, kb * 4);
+        else dma4_async(rws, ss, scoff, kb * 64);
+    };
+    issue(0, 0);
+    if (KB > 1) issue(1, 1);
+    if (KB > 2) issue(2, 2);
+
+    v4f acc[4][4];   // [row fragment][gate 0, 1 | up 2, 3]
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    struct Frags {
+        v8i a[4], b[4];
+        int sa[4], sb[4];
+    };
+    const int r16 = lane & 15, x8 = r16 & 7, G = lane >> 4;
+    const int nact = __builtin_amdgcn_readfirstlane(min(4, max(0, (nvalid - wm * 64 + 15) >> 4)));
+    auto read = [&](int st, Frags& F) {
+        const uint8_t* cur = buf + st * C::Stage;
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            const int row = (wm * 4 + mi) * 16 + r16;
+            const uint8_t* rowp = cur + row * kGroup;
+            const uint4 lo = *reinterpret_cast<const uint4*>(rowp + ((G ^ x8) << 4));
+            const uint4 hi = *reinterpret_cast<const uint4*>(rowp + (((G + 4) ^ x8) << 4));
+            F.a[mi] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            F.sa[mi] = mx_lds_ascale<WF>(cur, row, G);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int f = j < 2 ? 2 * wn + j : 6 + 2 * wn + j;
+            F.b[j] = mx_lds_wfrag<WF>(cur, f, lane);
+            F.sb[j] = cur[C::SB + f * 64 + lane];
+        }
+    };
+    // as k_gemm1_pf: wait for block kb + 1 everywhere, refill stage st with block kb + 3, read
+    // block kb + 1, then block kb's 16 instructions
+    auto step = [&](int kb, int st, Frags& F, Frags& N) __attribute__((always_inline)) {
+        if (kb + 2 < KB) wait_vm<C::Ops>();
+        else wait_vm<0>();
+        __syncthreads();
+        if (kb + 3 < KB) issue(kb + 3, st);
+        if (kb + 1 < KB) read(st == 2 ? 0 : st + 1, N);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+                if (mi < nact) acc[mi][j] = mx_mfma<WF>(F.a[mi], F.b[j], acc[mi][j], F.sa[mi], F.sb[j]);
+    };
+    if (KB > 2) wait_vm<2 * C::Ops>();
+    else if (KB > 1) wait_vm<C::Ops>();
+    else wait_vm<0>();
+    __syncthreads();
+    Frags F0, F1;
+    read(0, F0);
+    int st = 0;
+    for (int kb = 0; kb < KB; kb += 2) {
+        step(kb, st, F0, F1);
+        st = st == 2 ? 0 : st + 1;
+        if (kb + 1 < KB) {
+            step(kb + 1, st, F1, F0);
+            st = st == 2 ? 0 : st + 1;
+        }
+    }
+
+    // SwiGLU; a wave's two fragments are the 32 h columns 32 wn .. of the block, one MX group,
+    // so each row's amax is the swiglu_frag maximum and the scale needs no other wave
+    GuBias bias[2];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) bias[jj] = gu_bias(a.b13, e, a.I, ib * 128 + (2 * wn + jj) * 16 + r16);
+    float hv[4][2][4];
+    int ex[4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        if (mi < nact) {
+            float m[4];
+            swiglu_frag(acc[mi], a.b13, bias, hv[mi], m);
+            tap_frag<TAP>(a.htap, a.I, rowbase, (wm * 4 + mi) * 16, nvalid, ib * 128 + 2 * wn * 16, hv[mi]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ex[mi][i] = mx_scale_exponent<kWfmtE4M3>(m[i]);
+        }
+    }
+    __syncthreads();   // every wave is done reading the stages before buf is reused
+    // E4M3 bytes staged as [128 rows][128] (16-byte chunks XOR-swizzled by row % 8), one dword
+    // (4 columns of one row) per lane and fragment; the scales straight to hs
+    uint8_t* s_h = buf;
+    const int q = lane & 3, g4 = 4 * (lane >> 4), KS2 = a.I / kMx;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        if (mi < nact) {
+            const int row = (wm * 4 + mi) * 16 + g4 + q;
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+                *reinterpret_cast<uint32_t*>(s_h + row * 128 + (((2 * wn + jj) ^ (row & 7)) << 4) + 4 * (r16 >> 2)) =
+                    e4m3_quad_rows(hv[mi][jj], ex[mi], q);
+            if (r16 == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    a.hs[((int64_t)tile * kPfBM + (wm * 4 + mi) * 16 + g4 + i) * KS2 + ib * 4 + wn] =
+                        (uint8_t)(ex[mi][i] + 127);
+            }
+        }
+    }
+    __syncthreads();
+    // out in the down GEMM's operand order: fragment (row fragment mf, half hh), lane ln holds
+    // row mf * 16 + ln % 16, columns 64 hh + 16 (ln / 16) .. +15 (chunk 4 hh + ln / 16)
+    const int KB2 = a.I / kGroup;
+    for (int q2 = tid; q2 < 8 * 128; q2 += 512) {
+        const int mf = q2 >> 7, w = q2 & 127, hh = w >> 6, ln = w & 63;
+        const int R = mf * 16 + (ln & 15), c = 4 * hh + (ln >> 4);
+        const uint4 v = *reinterpret_cast<const uint4*>(s_h + R * 128 + ((c ^ (R & 7)) << 4));
+        *reinterpret_cast<uint4*>(a.hq + (((int64_t)tile * 8 + mf) * KB2 + ib) * kFragBytes + hh * 1024 + ln * 16) = v;
+    }
+}
+
+template <int WF>
+__global__ __launch_bounds__(512, 1) void k_gemm2_mxpf(G2Args a) {
+    using C = MxPf<WF>;
+    int nb, tile;
+    if (!pf_work_item(a.ord, a.H / 256, __builtin_amdgcn_readfirstlane(*a.ntiles), tile, nb)) return;
+    const int2 te = a.tiles[tile];
+    const int e = __builtin_amdgcn_readfirstlane(te.x), m0 = __builtin_amdgcn_readfirstlane(te.y);
+    const int nvalid = min(kPfBM, a.counts[e] - m0);
+    const int rowbase = __builtin_amdgcn_readfirstlane(a.offsets[e] + m0);
+    const int KB = a.I / kGroup, KS2 = a.I / kMx;
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wv >> 2, wn = wv & 3;
+
+    __shared__ __align__(16) uint8_t buf[kPfdStages * C::Stage];
+
+    const int NB16 = a.H / 16;
+    const v4i_t ra = make_srd(a.hq + (int64_t)tile * 8 * KB * kFragBytes, (uint32_t)8 * KB * kFragBytes);
+    const v4i_t rw = make_srd(a.w2p + (int64_t)e * NB16 * KB * C::FB, (uint32_t)NB16 * KB * C::FB);
+    const v4i_t rhs = make_srd(a.hs + (int64_t)tile * kPfBM * KS2, (uint32_t)kPfBM * KS2);
+    const v4i_t rws = make_srd(a.w2s + (int64_t)e * NB16 * KB * 64, (uint32_t)NB16 * KB * 64);
+    const uint32_t l16 = lane * 16;
+    uint32_t asoff[2], bsoff[C::NBI];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int p = wv * 64 + 512 * i, mf = p >> 7, hh = (p >> 6) & 1;
+        asoff[i] = __builtin_amdgcn_readfirstlane(mf * KB * kFragBytes + hh * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < C::NBI; ++i) {
+        const int b = (wv * 64 + 512 * i) * 16;
+        bsoff[i] = __builtin_amdgcn_readfirstlane((nb * 16 + b / C::FB) * KB * C::FB + b % C::FB);
+    }
+    // scale copies as in k_gemm1_mxpf: A-row scales of the tile's hs rows, weight scales of
+    // the item's 16 fragments
+    const bool sc_a = wv < 2 || wv >= 6;
+    uint32_t scoff;
+    if (sc_a) {
+        scoff = (uint32_t)((wv & 1) * 64 + lane) * KS2;
+    } else {
+        const int t = (wv - 2) * 64 + lane;
+        scoff = (uint32_t)(nb * 16 + (t >> 4)) * KB * 64 + (t & 15) * 4;
+    }
+    const uint32_t lds_w = lds_addr(buf) + wv * 1024;
+    const uint32_t lds_s = lds_addr(buf) + (sc_a ? C::SA + (wv & 1) * 256 : C::SB + (wv - 2) * 256);
+    auto issue = [&](int kb, int s) {
+        const uint32_t st = __builtin_amdgcn_readfirstlane(lds_w + s * C::Stage);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) dma16_async(ra, st + i * 8192, l16, asoff[i] + kb * kFragBytes);
+#pragma unroll
+        for (int i = 0; i < C::NBI; ++i) dma16_async(rw, st + kPfStageA + i * 8192, l16, bsoff[i] + kb * C::FB);
+        const uint32_t ss = __builtin_amdgcn_readfirstlane(lds_s + s * C::Stage);
+        if (sc_a) dma4_async(rhs, ss, scoff, kb * 4);
+        else dma4_async(rws, ss, scoff, kb * 64);
+    };
+    issue(0, 0);
+    if (KB > 1) issue(1, 1);
+    if (KB > 2) issue(2, 2);
+
+    v4f acc[4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    struct Frags {
+        v8i a[4], b[4];
+        int sa[4], sb[4];
+    };
+    const int G = lane >> 4, r16 = lane & 15;
+    auto read = [&](int st, Frags& F) {
+        const uint8_t* cur = buf + st * C::Stage;
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            const int mf = wm * 4 + mi;
+            F.a[mi] = lds_frag(cur + mf * kFragBytes, lane);
+            F.sa[mi] = mx_lds_ascale<WF>(cur, mf * 16 + r16, G);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            F.b[j] = mx_lds_wfrag<WF>(cur, wn * 4 + j, lane);
+            F.sb[j] = cur[C::SB + (wn * 4 + j) * 64 + lane];
+        }
+    };
+    auto step = [&](int kb, int st, Frags& F, Frags& N) __attribute__((always_inline)) {
+        if (kb + 2 < KB) wait_vm<C::Ops>();
+        else wait_vm<0>();
+        __syncthreads();
+        if (kb + 3 < KB) issue(kb + 3, st);
+        if (kb + 1 < KB) read(st == 2 ? 0 : st + 1, N);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) acc[mi][j] = mx_mfma<WF>(F.a[mi], F.b[j], acc[mi][j], F.sa[mi], F.sb[j]);
+    };
+    if (KB > 2) wait_vm<2 * C::Ops>();
+    else if (KB > 1) wait_vm<C::Ops>();
+    else wait_vm<0>();
+    __syncthreads();
+    Frags F0, F1;
+    read(0, F0);
+    int st = 0;
+    for (int kb = 0; kb < KB; kb += 2) {
+        step(kb, st, F0, F1);
+        st = st == 2 ? 0 : st + 1;
+        if (kb + 1 < KB) {
+            step(kb + 1, st, F1, F0);
+            st = st == 2 ? 0 : st + 1;
+        }
+    }
+
+    float bias[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bias[j] = out_bias(a.b2, e, a.H, nb * 256 + (wn * 4 + j) * 16 + r16);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = (wm * 4 + mi) * 16 + 4 * (lane >> 4) + i;
+            if (row < nvalid) {
+                const int64_t o = (int64_t)(rowbase + row) * a.H;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int col = nb * 256 + (wn * 4 + j) * 16 + r16;
+                    const float v = add_bias(a.b2, acc[mi][j][i], bias[j]);
+                    if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o + col] = f32_to_bf16(v);
+                    else reinterpret_cast<float*>(a.out)[o + col] = v;
+                }
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------------------
 // 256-row items for experts with many rows: an item is a pair of consecutive 128-row tiles
 // of one expert (the second may be absent) and 256 columns, so each K block moves 64 KB
 // (A 32 KB + B 32 KB) per 256 x 256 x 128 product instead of 48 KB per 128 x 256 x 128:
@@ -1851,6 +2199,31 @@ static hipError_t launch_gemm2_p2(const FfnArgs& f, const FfnPlan& p, const FfnW
     return hipGetLastError();
 }
 
+template <int WF>
+static hipError_t run_ffn_mx_pf(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid) {
+    const G1Args g1 = g1_args(f, w, ffn_super_tile_order(p.ntiles_max));
+    const int grid1 = g1.ord ? kXcds * ord_ranks(p.ntiles_max, f.I / kGroup)
+                             : (int)(ceil_div((int64_t)(f.I / kGroup) * p.ntiles_max, kXcds) * kXcds);
+    if (f.debug_h) hipLaunchKernelGGL((k_gemm1_mxpf<WF, true>), dim3(grid1), dim3(512), 0, st, g1);
+    else hipLaunchKernelGGL((k_gemm1_mxpf<WF, false>), dim3(grid1), dim3(512), 0, st, g1);
+    if (mid) {
+        const hipError_t e = hipEventRecord(mid, st);
+        if (e != hipSuccess) return e;
+    }
+    const G2Args g2 = g2_args(f, w, ffn_super_tile_order(p.ntiles_max));
+    const int grid2 = g2.ord ? kXcds * ord_ranks(p.ntiles_max, f.H / 256)
+                             : (int)(ceil_div((int64_t)(f.H / 256) * p.ntiles_max, kXcds) * kXcds);
+    hipLaunchKernelGGL((k_gemm2_mxpf<WF>), dim3(grid2), dim3(512), 0, st, g2);
+    return hipGetLastError();
+}
+
+// The MX schemes on 128-row tiles (the plan takes them for H % 256 == 0).
+hipError_t launch_ffn_mx_pf(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid) {
+    if (f.H % 256 != 0) return hipErrorInvalidValue;
+    return f.quant == kQuantW4A8 ? run_ffn_mx_pf<kWfmtE2M1>(f, p, w, st, mid)
+                                 : run_ffn_mx_pf<kWfmtE4M3>(f, p, w, st, mid);
+}
+
 static hipError_t run_ffn_pf(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid,
                              bool pairs_ready) {
     const G1Args g1 = g1_args(f, w, ffn_super_tile_order(p.ntiles_max));
@@ -1919,7 +2292,7 @@ FfnWs carve_ffn_ws(const FfnArgs& f, void* ws) {
     r.ntiles = reinterpret_cast<int32_t*>(w + l.ntiles);
     r.hq = w + l.hq;
     r.hs = w + l.hs;
-    r.bs = ffn_plan(f.T, f.k, f.E, f.quant).BM == 128 ? reinterpret_cast<uint32_t*>(w + l.bs) : nullptr;
+    r.bs = ffn_plan(f.T, f.k, f.E, f.quant, f.H).BM == 128 ? reinterpret_cast<uint32_t*>(w + l.bs) : nullptr;
     r.pairs = reinterpret_cast<int4*>(w + l.pairs);
     r.npairs = reinterpret_cast<int32_t*>(w + l.npairs);
     return r;
@@ -1983,7 +2356,7 @@ __global__ __launch_bounds__(256) void k_unpack_h(const int2* __restrict__ tiles
 
 hipError_t launch_grouped_ffn(const FfnArgs& f, void* ws, hipStream_t st, hipEvent_t mid, bool tiles_ready,
                               bool pairs_ready) {
-    const FfnPlan p = ffn_plan(f.T, f.k, f.E, f.quant);
+    const FfnPlan p = ffn_plan(f.T, f.k, f.E, f.quant, f.H);
     const FfnWs w = carve_ffn_ws(f, ws);
     if (!tiles_ready) {
         const hipError_t e = launch_tiles(f.counts, f.E, p.BM, w.tiles, w.ntiles, st);
@@ -1996,7 +2369,7 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, void* ws, hipStream_t st, hipEve
         e = launch_ffn_w16(f, p, w, st, mid);
     } else if (f.quant != kQuantFp8Block128) {
         layout = kHlMx;
-        e = launch_ffn_mx(f, p, w, st, mid);
+        e = p.BM == 128 ? launch_ffn_mx_pf(f, p, w, st, mid) : launch_ffn_mx(f, p, w, st, mid);
     } else if (p.BM == 16) {
         // output columns per workgroup of the down GEMM = 128, a divisor of H
         layout = kHlDec;

@@ -22,25 +22,11 @@
 // The weight operand's format (E4M3 or E2M1) is the instruction's B-format field.
 #include "moe_common.h"
 #include "moe_internal.h"
+#include "mx_common.h"
 
 #include <algorithm>
 
 namespace moe {
-
-constexpr int kMx = 32;
-
-// Smallest integer e with amax <= M * 2^e for M = 1.75 * 2^8 (E4M3) or 1.5 * 2^2 (E2M1),
-// clamped to [-127, 127]; 0 for amax == 0.  Exact on the float32 bits: amax = 1.m * 2^(E-127).
-template <int WF>
-__device__ __forceinline__ int mx_scale_exponent(float amax) {
-    const uint32_t u = __float_as_uint(amax) & 0x7FFFFFFFu;
-    if (u == 0) return 0;
-    const int E = (int)(u >> 23);
-    if (E == 0) return -127;
-    const uint32_t m = u & 0x7FFFFFu;
-    const int e = WF == kWfmtE2M1 ? E - 129 + (m > 0x400000u ? 1 : 0) : E - 135 + (m > 0x600000u ? 1 : 0);
-    return e < -127 ? -127 : (e > 127 ? 127 : e);
-}
 
 // E2M1 code of v / 2^ex (|v / 2^ex| <= 6): round to nearest, ties to the even code; the
 // thresholds are the midpoints 0.25 0.75 1.25 1.75 2.5 3.5 5 of the magnitudes
@@ -241,10 +227,6 @@ __device__ __forceinline__ v8i mx_arow(rsrc_t r, uint32_t voff, uint32_t soff) {
     return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-template <int WF>
-__device__ __forceinline__ v4f mx_mfma(v8i a, v8i b, v4f acc, int sa, int sb) {
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, WF == kWfmtE2M1 ? 4 : 0, 0, sa, 0, sb);
-}
 
 template <int WF, int PF, bool TAP>
 __global__ __launch_bounds__(512) void k_gemm1_mx(MxG1Args a) {

@@ -211,7 +211,7 @@ int run_fused(const char* op, const moe_fused_args* a, uint8_t* base) {
     moe::FfnArgs f{T, kf, H, I, Ef, xq, xs, counts, offsets, sorted, a->w13, a->w13_scale, a->w2, a->w2_scale, eo, bf,
                    a->quant, w16 ? a->hidden_states : nullptr, nullptr, nullptr, nullptr, a->w13_bias, a->w2_bias};
     const moe::FfnWs fw = moe::carve_ffn_ws(f, fws);
-    const moe::FfnPlan plan = moe::ffn_plan(T, kf, Ef, a->quant);
+    const moe::FfnPlan plan = moe::ffn_plan(T, kf, Ef, a->quant, H);
     moe::RouteCfg rcfg = route_cfg(&a->route, T, a->prelude != nullptr);
     rcfg.ld = kf;
     rcfg.shared_id = sh ? E : -1;

@@ -41,14 +41,18 @@ namespace moe {
 #define MOE_PAIR_DOWN_MIN_AVG_ROWS 64
 #endif
 
-FfnPlan ffn_plan(int T, int k, int E, int quant) {
+FfnPlan ffn_plan(int T, int k, int E, int quant, int H) {
     const int64_t A = (int64_t)T * k;
     const int64_t avg = A / E;
     FfnPlan p;
-    p.BM = (avg <= MOE_DEC_MAX_AVG_ROWS || quant != kQuantFp8Block128) ? 16 : 128;
+    // 128-row tiles once experts average more than a decode batch's rows: every shape for the
+    // 128-element scheme (its plain kernels take any H), H % 256 == 0 for the MX schemes (their
+    // down GEMM works in 256-column blocks); W8A16 stays on 16-row tiles
+    const bool fp8 = quant == kQuantFp8Block128, mx = quant == kQuantMxfp8 || quant == kQuantW4A8;
+    p.BM = avg > MOE_DEC_MAX_AVG_ROWS && (fp8 || (mx && H % 256 == 0)) ? 128 : 16;
     p.ntiles_max = (int)(cdiv(A, p.BM) + std::min<int64_t>(E, A));
-    p.pairs = p.BM == 128 && avg >= MOE_PAIR_MIN_AVG_ROWS;
-    p.pairs_down = p.pairs || (p.BM == 128 && avg >= MOE_PAIR_DOWN_MIN_AVG_ROWS);
+    p.pairs = fp8 && p.BM == 128 && avg >= MOE_PAIR_MIN_AVG_ROWS;
+    p.pairs_down = fp8 && (p.pairs || (p.BM == 128 && avg >= MOE_PAIR_DOWN_MIN_AVG_ROWS));
     // an expert's pairs number ceil(tiles / 2)
     p.npairs_max = (p.ntiles_max + (int)std::min<int64_t>(E, A)) / 2 + 1;
     return p;
@@ -60,7 +64,7 @@ size_t ffn_rb_scale_table_bytes(int H, int I, int E) { return (size_t)E * (I / 1
 static size_t h_bytes(int quant) { return quant == kQuantW8A16 ? 2 : 1; }
 
 FfnWsLayout ffn_ws_layout(int T, int H, int I, int E, int k, int quant) {
-    const FfnPlan p = ffn_plan(T, k, E, quant);
+    const FfnPlan p = ffn_plan(T, k, E, quant, H);
     const size_t rows = (size_t)p.ntiles_max * p.BM;
     FfnWsLayout l;
     size_t o = 0;

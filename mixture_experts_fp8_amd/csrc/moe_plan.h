@@ -32,7 +32,7 @@ struct FfnPlan {
                       //    threshold, where gate/up keeps 128-row tiles)
     int npairs_max;   // grid bound on pairs
 };
-FfnPlan ffn_plan(int T, int k, int E, int quant = kQuantFp8Block128);
+FfnPlan ffn_plan(int T, int k, int E, int quant, int H);
 
 // Byte offsets of the grouped FFN's workspace regions (from a 256-byte aligned base):
 // tiles int2 [ntiles_max] | ntiles | hq [rows, I] (bf16 for W8A16) | hs [rows, I/32] |

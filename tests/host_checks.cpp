@@ -82,8 +82,13 @@ static void layouts() {
     for (auto& s : shapes) {
         const int T = s[0], H = s[1], I = s[2], E = s[3], k = s[4];
         for (int q = 0; q < 4; ++q) {
-            const FfnPlan p = ffn_plan(T, k, E, q);
+            const FfnPlan p = ffn_plan(T, k, E, q, H);
             CHECK(p.BM == 16 || p.BM == 128);
+            // the MX schemes take 128-row tiles only with 256-column down blocks; pairs are the
+            // 128-element scheme's, W8A16 stays on 16-row tiles
+            CHECK(q == kQuantFp8Block128 || (!p.pairs && !p.pairs_down));
+            CHECK(q != kQuantW8A16 || p.BM == 16);
+            CHECK(!(q == kQuantMxfp8 || q == kQuantW4A8) || p.BM == 16 || H % 256 == 0);
             CHECK((int64_t)p.ntiles_max * p.BM >= (int64_t)T * k);   // every row has a tile slot
             CHECK(!p.pairs || p.pairs_down);
             const FfnWsLayout l = ffn_ws_layout(T, H, I, E, k, q);

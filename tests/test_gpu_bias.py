@@ -129,6 +129,14 @@ def test_bias_fused_mx_w8a16(scheme):
     _fused_check(W.Workload(167, "bfmx", T=70, H=384, I=256, E=8, k=3, bias="normal1.5", ffn_bias=True), scheme)
 
 
+@pytest.mark.parametrize("scheme", ["mxfp8", "w4a8"])
+def test_bias_mx_prefill_tiles(scheme):
+    # the 128-row MX kernels (experts averaging > 24 rows, H % 256 == 0)
+    wl = W.Workload(169, "bmxp", T=400, H=512, I=256, E=4, k=2, ffn_bias=True)
+    RQ._check(wl, scheme)
+    _fused_check(wl, scheme)
+
+
 def test_bias_fused_decode_gemma4_full():
     # the Gemma-4-shaped decode step (RMSNorm + router prelude, 128 experts, top-8) with biases
     _fused_check(W.CONFIGS[2].replace(ffn_bias=True))

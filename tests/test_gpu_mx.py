@@ -120,6 +120,31 @@ def test_mx_fused_small(scheme, name):
     print(f"  rel fro {fro:.2e} rel max {mxe:.2e}", flush=True)
 
 
+# prefill-sized shapes on the 128-row MX kernels (experts averaging > 24 rows, H % 256 == 0):
+# several K blocks, one K block in the down GEMM (I = 128), ragged and skewed tiles; and the
+# 16-row kernels at prefill size where H % 256 != 0
+PREFILL = {
+    "tiles128": W.Workload(134, "mx_t128", T=600, H=512, I=384, E=8, k=3),
+    "down_kb1": W.Workload(135, "mx_kb1", T=400, H=256, I=128, E=4, k=2),
+    "skewed_ragged": W.Workload(136, "mx_skew", T=777, H=768, I=640, E=16, k=4, bias="normal1.5"),
+    "H384_16row": W.Workload(137, "mx_h384", T=500, H=384, I=256, E=4, k=2),
+}
+
+
+@pytest.mark.parametrize("scheme", list(SCHEMES))
+@pytest.mark.parametrize("name", list(PREFILL))
+def test_mx_fused_prefill_tiles(scheme, name):
+    quant, fmt = SCHEMES[scheme]
+    wl = PREFILL[name]
+    print("mx fused prefill", scheme, name, W.describe(wl), flush=True)
+    y, ids, counts = _run(wl, quant)
+    ref, ids_ref, margin = _oracle(wl, scheme)
+    ok = margin >= 1e-5
+    assert np.array_equal(ids[ok], ids_ref[ok])
+    fro, mxe = HN.assert_output_close(HN.bf16_to_f64(y)[ok], ref["y"][ok], f"{scheme} {name}", ref["y_bound"][ok])
+    print(f"  rel fro {fro:.2e} rel max {mxe:.2e}", flush=True)
+
+
 # configs 2 in full; 3 and 5 on the tokens whose rows cover every 128 rows of every expert
 # (every 16-row tile group of these kernels' tile list holds a checked row at most 128 rows
 # away) plus every 64th token
