@@ -2137,6 +2137,395 @@ __global__ __launch_bounds__(512, 1) void k_gemm2_p2(G2Args a) {
 }
 
 // ----------------------------------------------------------------------------------------
+// Micro-scaled gate/up and down GEMMs on 256-row items (tile pairs), for experts averaging
+// >= 128 rows: the item list, waves (2 x 4 of 128 x 64), two LDS stages and output paths of
+// k_gemm1_p2 / k_gemm2_p2, with the per-stage scale copies of the 128-row MX kernels.  Stage:
+// A 256 rows (32 KB), 16 weight fragments, 256 A-row scale dwords, 16 x 64 weight-scale bytes.
+template <int WF>
+struct MxP2 {
+    static constexpr int FB = WF == kWfmtE2M1 ? 1024 : 2048;
+    static constexpr int NBI = 16 * FB / 8192;
+    static constexpr int SA = kP2StageA + 16 * FB;
+    static constexpr int SB = SA + kP2Rows * 4;
+    static constexpr int Stage = SB + 16 * 64;
+};
+
+template <int WF>
+__device__ __forceinline__ v8i mx_lds_wfrag_at(const uint8_t* wbase, int f, int lane) {
+    if constexpr (WF == kWfmtE2M1) {
+        const uint4 v = *reinterpret_cast<const uint4*>(wbase + f * 1024 + lane * 16);
+        return v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+    } else {
+        return lds_frag(wbase + f * 2048, lane);
+    }
+}
+
+// Output of a 256-row down item through an LDS staging buffer of BUF bytes (free after the K
+// loop), as whole 16-byte pieces of full rows, in passes of RP rows: bf16 RP = 256 if the
+// buffer holds them (512 bytes a row), else 128; float32 RP = 128 or 64 (1 KB a row).  A lane holds rows wm * 128 + 16 mi + 4 (lane / 16) + i of
+// columns wn * 64 + 16 j + lane % 16; staged rows are swizzled by 16 columns times
+// (row / 4) % 4, which for a lane's rows is lane / 16, so the lane's offsets per j are formed
+// once.  The caller has synchronised the workgroup after its last read of the buffer.
+template <int BUF>
+__device__ __forceinline__ void p2_store_output(const G2Args& a, v4f (&acc)[8][4], uint8_t* buf, int rowbase,
+                                                int nvalid, int nb, int nact) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wv >> 2, wn = wv & 3, r16 = lane & 15, r0 = 4 * (lane >> 4), q4 = lane >> 4;
+    if (a.out_bf16) {
+        constexpr int RP = BUF >= 256 * 512 ? 256 : 128;
+        static_assert(BUF >= RP * 512, "staging buffer too small");
+        uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+#pragma unroll
+        for (int q = 0; q < 256 / RP; ++q) {
+            const int nr = min(RP, nvalid - q * RP);
+            if (nr <= 0) break;
+            if (q) __syncthreads();   // the previous pass has left the LDS
+            uint32_t ob[4];           // bytes: row r0 of the pass, swizzled column of fragment j
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ob[j] = r0 * 512 + 2 * (wn * 64 + 16 * (j ^ q4) + r16);
+#pragma unroll
+            for (int mi = 0; mi < 8; ++mi) {
+                const int R0 = wm * kPfBM + mi * 16 - q * RP;   // wave-uniform
+                if (mi < nact && R0 >= 0 && R0 < RP) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const uint32_t v = f32_to_bf16(acc[mi][j][i]);
+                            const uint32_t nbv = dpp_u32<0xB1>(v);   // lane ^ 1
+                            if (!(lane & 1)) *reinterpret_cast<uint32_t*>(buf + ob[j] + (R0 + i) * 512) = v | (nbv << 16);
+                        }
+                }
+            }
+            __syncthreads();
+            for (int t = tid; t < nr * 32; t += 512) {
+                const int R = t >> 5, m = t & 31;
+                const uint4 v = *reinterpret_cast<const uint4*>(buf + (R * 256 + ((8 * m) ^ (16 * ((R >> 2) & 3)))) * 2);
+                *reinterpret_cast<uint4*>(out + (int64_t)(rowbase + q * RP + R) * a.H + nb * 256 + 8 * m) = v;
+            }
+        }
+    } else {
+        constexpr int RP = BUF >= 128 * 1024 ? 128 : 64;
+        static_assert(BUF >= RP * 1024, "staging buffer too small");
+        float* out = reinterpret_cast<float*>(a.out);
+#pragma unroll
+        for (int q = 0; q < 256 / RP; ++q) {
+            const int nr = min(RP, nvalid - q * RP);
+            if (nr <= 0) break;
+            if (q) __syncthreads();
+            uint32_t ob[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ob[j] = r0 * 1024 + 4 * (wn * 64 + 16 * (j ^ q4) + r16);
+#pragma unroll
+            for (int mi = 0; mi < 8; ++mi) {
+                const int R0 = wm * kPfBM + mi * 16 - q * RP;
+                if (mi < nact && R0 >= 0 && R0 < RP) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            *reinterpret_cast<float*>(buf + ob[j] + (R0 + i) * 1024) = acc[mi][j][i];
+                }
+            }
+            __syncthreads();
+            const float* s_o = reinterpret_cast<const float*>(buf);
+            for (int t = tid; t < nr * 64; t += 512) {
+                const int R = t >> 6, m = t & 63;
+                const float4 v = *reinterpret_cast<const float4*>(s_o + R * 256 + ((4 * m) ^ (16 * ((R >> 2) & 3))));
+                *reinterpret_cast<float4*>(out + (int64_t)(rowbase + q * RP + R) * a.H + nb * 256 + 4 * m) = v;
+            }
+        }
+    }
+}
+
+template <int WF, bool TAP>
+__global__ __launch_bounds__(512, 1) void k_gemm1_mxp2(G1Args a) {
+    using C = MxP2<WF>;
+    int ib, pair;
+    if (!pf_work_item(a.ord, a.I / kGroup, __builtin_amdgcn_readfirstlane(*a.npairs), pair, ib)) return;
+    const int4 pi = a.pairs[pair];
+    const int t0 = __builtin_amdgcn_readfirstlane(pi.x), e = __builtin_amdgcn_readfirstlane(pi.y);
+    const int rowbase = __builtin_amdgcn_readfirstlane(pi.z), nvalid = __builtin_amdgcn_readfirstlane(pi.w);
+    const bool second = nvalid > kPfBM;
+    const int KB = a.H / kGroup, KS = a.H / kMx;
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wv >> 2, wn = wv & 3;
+
+    __shared__ __align__(16) uint8_t buf[2 * C::Stage];
+
+    const int NB16 = 2 * a.I / 16;
+    const v4i_t ra = make_srd(a.xq, (uint32_t)a.T * a.H);
+    const v4i_t rw = make_srd(a.w13p + (int64_t)e * NB16 * KB * C::FB, (uint32_t)NB16 * KB * C::FB);
+    const v4i_t rxs = make_srd(a.xs, (uint32_t)a.T * KS);
+    const v4i_t rws = make_srd(a.w13s + (int64_t)e * NB16 * KB * 64, (uint32_t)NB16 * KB * 64);
+    auto n16_of = [&](int f) { return f < 8 ? ib * 8 + f : a.I / 16 + ib * 8 + (f - 8); };
+    // A: wave instruction i moves rows 8 (wv + 8 i) .. +7 as whole lines (chunk c of row r at
+    // r * 128 + 16 (c ^ (r % 8))).  Scale copies, one dword per lane: waves 0..3 the four A
+    // scales of row wv * 64 + lane, waves 4..7 the per-lane weight scales of the 16 fragments.
+    const bool sc_a = wv < 4;
+    int tok[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        const int r = i < 4 ? 8 * (wv + 8 * i) + (lane >> 3) : (wv & 3) * 64 + lane;
+        tok[i] = a.sorted_assign[rowbase + min(r, nvalid - 1)] / a.k;
+    }
+    uint32_t aoff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) aoff[i] = (uint32_t)tok[i] * a.H + (((lane & 7) ^ (lane >> 3)) << 4);
+    uint32_t bsoff[C::NBI];
+#pragma unroll
+    for (int i = 0; i < C::NBI; ++i) {
+        const int b = (wv * 64 + 512 * i) * 16;
+        bsoff[i] = __builtin_amdgcn_readfirstlane(n16_of(b / C::FB) * KB * C::FB + b % C::FB);
+    }
+    uint32_t scoff;
+    if (sc_a) {
+        scoff = (uint32_t)tok[4] * KS;
+    } else {
+        const int t = (wv - 4) * 64 + lane;
+        scoff = (uint32_t)n16_of(t >> 4) * KB * 64 + (t & 15) * 4;
+    }
+    const uint32_t l16 = lane * 16;
+    const uint32_t lds_w = lds_addr(buf) + wv * 1024;
+    const uint32_t lds_s = lds_addr(buf) + (sc_a ? C::SA + wv * 256 : C::SB + (wv - 4) * 256);
+    auto issue = [&](int kb, int s) __attribute__((always_inline)) {
+        const uint32_t st = __builtin_amdgcn_readfirstlane(lds_w + s * C::Stage);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)   // rows 128.. only for a pair with a second tile (uniform)
+            if (i < 2 || second) dma16_async(ra, st + i * 8192, aoff[i], kb * kGroup);
+#pragma unroll
+        for (int i = 0; i < C::NBI; ++i) dma16_async(rw, st + kP2StageA + i * 8192, l16, bsoff[i] + kb * C::FB);
+        const uint32_t ss = __builtin_amdgcn_readfirstlane(lds_s + s * C::Stage);
+        if (sc_a) dma4_async(rxs, ss, scoff, kb * 4);
+        else dma4_async(rws, ss, scoff, kb * 64);
+    };
+    issue(0, 0);
+
+    v4f acc[8][4];   // [row fragment][gate 0, 1 | up 2, 3]
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    const int r16 = lane & 15, x8 = r16 & 7, G = lane >> 4;
+    const int nact = __builtin_amdgcn_readfirstlane(min(8, max(0, (nvalid - wm * kPfBM + 15) >> 4)));
+    for (int kb = 0; kb < KB; ++kb) {
+        wait_vm<0>();      // block kb landed (this thread's pieces) ...
+        __syncthreads();   // ... and everyone's; every wave is done with block kb - 1's stage
+        if (kb + 1 < KB) issue(kb + 1, (kb + 1) & 1);
+        if (nact > 0) {
+            const uint8_t* cur = buf + (kb & 1) * C::Stage;
+            v8i bf[4];
+            int sb[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int f = j < 2 ? 2 * wn + j : 6 + 2 * wn + j;
+                bf[j] = mx_lds_wfrag_at<WF>(cur + kP2StageA, f, lane);
+                sb[j] = cur[C::SB + f * 64 + lane];
+            }
+            auto afrag = [&](int mi, int& sa) __attribute__((always_inline)) {
+                const int row = (wm * 8 + mi) * 16 + r16;
+                const uint8_t* rowp = cur + row * kGroup;
+                const uint4 lo = *reinterpret_cast<const uint4*>(rowp + ((G ^ x8) << 4));
+                const uint4 hi = *reinterpret_cast<const uint4*>(rowp + (((G + 4) ^ x8) << 4));
+                sa = (int)((*reinterpret_cast<const uint32_t*>(cur + C::SA + row * 4) >> (8 * G)) & 0xFFu);
+                return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            };
+            int s0, s1;
+            v8i a0 = afrag(0, s0), a1 = afrag(1, s1);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                v8i n0 = a0, n1 = a1;
+                int t0s = s0, t1s = s1;
+                if (p < 3) {
+                    n0 = afrag(2 * p + 2, t0s);
+                    n1 = afrag(2 * p + 3, t1s);
+                }
+                if (2 * p < nact) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[2 * p][j] = mx_mfma<WF>(a0, bf[j], acc[2 * p][j], s0, sb[j]);
+                }
+                if (2 * p + 1 < nact) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[2 * p + 1][j] = mx_mfma<WF>(a1, bf[j], acc[2 * p + 1][j], s1, sb[j]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                a0 = n0;
+                a1 = n1;
+                s0 = t0s;
+                s1 = t1s;
+            }
+        }
+    }
+
+    // SwiGLU; the wave's two fragments are one 32-column MX group (see k_gemm1_mxpf)
+    GuBias bias[2];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) bias[jj] = gu_bias(a.b13, e, a.I, ib * 128 + (2 * wn + jj) * 16 + r16);
+    float hv[8][2][4];
+    int ex[8][4];
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi) {
+        if (mi < nact) {
+            float m[4];
+            swiglu_frag(acc[mi], a.b13, bias, hv[mi], m);
+            tap_frag<TAP>(a.htap, a.I, rowbase, (wm * 8 + mi) * 16, nvalid, ib * 128 + 2 * wn * 16, hv[mi]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ex[mi][i] = mx_scale_exponent<kWfmtE4M3>(m[i]);
+        }
+    }
+    __syncthreads();   // every wave is done reading the stages before buf is reused
+    uint8_t* s_h = buf;   // [256 rows][128], 16-byte chunks XOR-swizzled by row % 8
+    const int q = lane & 3, g4 = 4 * (lane >> 4), KS2 = a.I / kMx;
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi) {
+        if (mi < nact) {
+            const int row = (wm * 8 + mi) * 16 + g4 + q;
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+                *reinterpret_cast<uint32_t*>(s_h + row * 128 + (((2 * wn + jj) ^ (row & 7)) << 4) + 4 * (r16 >> 2)) =
+                    e4m3_quad_rows(hv[mi][jj], ex[mi], q);
+            if (r16 == 0) {   // the pair's two tiles are consecutive: tile row t0 * 128 + row
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    a.hs[((int64_t)t0 * kPfBM + (wm * 8 + mi) * 16 + g4 + i) * KS2 + ib * 4 + wn] =
+                        (uint8_t)(ex[mi][i] + 127);
+            }
+        }
+    }
+    __syncthreads();
+    const int KB2 = a.I / kGroup, nf = second ? 16 : 8;
+    for (int q2 = tid; q2 < nf * 128; q2 += 512) {
+        const int mf = q2 >> 7, w = q2 & 127, hh = w >> 6, ln = w & 63;
+        const int R = mf * 16 + (ln & 15), c = 4 * hh + (ln >> 4);
+        const uint4 v = *reinterpret_cast<const uint4*>(s_h + R * 128 + ((c ^ (R & 7)) << 4));
+        *reinterpret_cast<uint4*>(a.hq + (((int64_t)t0 * 8 + mf) * KB2 + ib) * kFragBytes + hh * 1024 + ln * 16) = v;
+    }
+}
+
+template <int WF>
+__global__ __launch_bounds__(512, 1) void k_gemm2_mxp2(G2Args a) {
+    using C = MxP2<WF>;
+    int nb, pair;
+    if (!pf_work_item(a.ord, a.H / 256, __builtin_amdgcn_readfirstlane(*a.npairs), pair, nb)) return;
+    const int4 pi = a.pairs[pair];
+    const int t0 = __builtin_amdgcn_readfirstlane(pi.x), e = __builtin_amdgcn_readfirstlane(pi.y);
+    const int rowbase = __builtin_amdgcn_readfirstlane(pi.z), nvalid = __builtin_amdgcn_readfirstlane(pi.w);
+    const bool second = nvalid > kPfBM;
+    const int KB = a.I / kGroup, KS2 = a.I / kMx;
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wv >> 2, wn = wv & 3;
+
+    __shared__ __align__(16) uint8_t buf[2 * C::Stage];
+
+    const int NB16 = a.H / 16, nt = second ? 2 : 1;
+    // a missing second tile reads as zeros (outside the descriptors' ranges)
+    const v4i_t ra = make_srd(a.hq + (int64_t)t0 * 8 * KB * kFragBytes, (uint32_t)nt * 8 * KB * kFragBytes);
+    const v4i_t rw = make_srd(a.w2p + (int64_t)e * NB16 * KB * C::FB, (uint32_t)NB16 * KB * C::FB);
+    const v4i_t rhs = make_srd(a.hs + (int64_t)t0 * kPfBM * KS2, (uint32_t)nt * kPfBM * KS2);
+    const v4i_t rws = make_srd(a.w2s + (int64_t)e * NB16 * KB * 64, (uint32_t)NB16 * KB * 64);
+    const uint32_t l16 = lane * 16;
+    uint32_t asoff[4], bsoff[C::NBI];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int g = wv + 8 * i;   // piece group: fragment g / 2, half g % 2 of the pair's 16 row fragments
+        asoff[i] = __builtin_amdgcn_readfirstlane((g >> 1) * KB * kFragBytes + (g & 1) * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < C::NBI; ++i) {
+        const int b = (wv * 64 + 512 * i) * 16;
+        bsoff[i] = __builtin_amdgcn_readfirstlane((nb * 16 + b / C::FB) * KB * C::FB + b % C::FB);
+    }
+    const bool sc_a = wv < 4;
+    uint32_t scoff;
+    if (sc_a) {
+        scoff = (uint32_t)(wv * 64 + lane) * KS2;
+    } else {
+        const int t = (wv - 4) * 64 + lane;
+        scoff = (uint32_t)(nb * 16 + (t >> 4)) * KB * 64 + (t & 15) * 4;
+    }
+    const uint32_t lds_w = lds_addr(buf) + wv * 1024;
+    const uint32_t lds_s = lds_addr(buf) + (sc_a ? C::SA + wv * 256 : C::SB + (wv - 4) * 256);
+    auto issue = [&](int kb, int s) __attribute__((always_inline)) {
+        const uint32_t st = __builtin_amdgcn_readfirstlane(lds_w + s * C::Stage);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)   // fragments 8.. only for a pair with a second tile (uniform)
+            if (i < 2 || second) dma16_async(ra, st + i * 8192, l16, asoff[i] + kb * kFragBytes);
+#pragma unroll
+        for (int i = 0; i < C::NBI; ++i) dma16_async(rw, st + kP2StageA + i * 8192, l16, bsoff[i] + kb * C::FB);
+        const uint32_t ss = __builtin_amdgcn_readfirstlane(lds_s + s * C::Stage);
+        if (sc_a) dma4_async(rhs, ss, scoff, kb * 4);
+        else dma4_async(rws, ss, scoff, kb * 64);
+    };
+    issue(0, 0);
+
+    v4f acc[8][4];
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[mi][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    const int r16 = lane & 15, G = lane >> 4;
+    const int nact = __builtin_amdgcn_readfirstlane(min(8, max(0, (nvalid - wm * kPfBM + 15) >> 4)));
+    for (int kb = 0; kb < KB; ++kb) {
+        wait_vm<0>();
+        __syncthreads();
+        if (kb + 1 < KB) issue(kb + 1, (kb + 1) & 1);
+        if (nact > 0) {
+            const uint8_t* cur = buf + (kb & 1) * C::Stage;
+            v8i bf[4];
+            int sb[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                bf[j] = mx_lds_wfrag_at<WF>(cur + kP2StageA, wn * 4 + j, lane);
+                sb[j] = cur[C::SB + (wn * 4 + j) * 64 + lane];
+            }
+            auto afrag = [&](int mi, int& sa) __attribute__((always_inline)) {
+                const int mf = wm * 8 + mi;
+                sa = (int)((*reinterpret_cast<const uint32_t*>(cur + C::SA + (mf * 16 + r16) * 4) >> (8 * G)) & 0xFFu);
+                return lds_frag(cur + mf * kFragBytes, lane);
+            };
+            int s0, s1;
+            v8i a0 = afrag(0, s0), a1 = afrag(1, s1);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                v8i n0 = a0, n1 = a1;
+                int t0s = s0, t1s = s1;
+                if (p < 3) {
+                    n0 = afrag(2 * p + 2, t0s);
+                    n1 = afrag(2 * p + 3, t1s);
+                }
+                if (2 * p < nact) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[2 * p][j] = mx_mfma<WF>(a0, bf[j], acc[2 * p][j], s0, sb[j]);
+                }
+                if (2 * p + 1 < nact) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[2 * p + 1][j] = mx_mfma<WF>(a1, bf[j], acc[2 * p + 1][j], s1, sb[j]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                a0 = n0;
+                a1 = n1;
+                s0 = t0s;
+                s1 = t1s;
+            }
+        }
+    }
+    if (a.b2) {   // down bias of the lane's columns
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float bv = a.b2[(int64_t)e * a.H + nb * 256 + wn * 64 + 16 * j + r16];
+#pragma unroll
+            for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[mi][j][i] += bv;
+        }
+    }
+    __syncthreads();   // every wave is done reading the stages
+    p2_store_output<2 * C::Stage>(a, acc, buf, rowbase, nvalid, nb, nact);
+}
+
+// ----------------------------------------------------------------------------------------
 // The super-tile order pays off once the tiles fill several of its 64-tile windows.
 int ffn_super_tile_order(int ntiles_max) { return ntiles_max >= 512 ? 1 : 0; }
 // The 256-row down GEMM takes the super-tile order from twice as many tiles on: on the
@@ -2217,9 +2606,37 @@ static hipError_t run_ffn_mx_pf(const FfnArgs& f, const FfnPlan& p, const FfnWs&
     return hipGetLastError();
 }
 
-// The MX schemes on 128-row tiles (the plan takes them for H % 256 == 0).
-hipError_t launch_ffn_mx_pf(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid) {
+template <int WF>
+static hipError_t run_ffn_mx_p2(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid,
+                                bool pairs_ready) {
+    if (!pairs_ready)
+        hipLaunchKernelGGL(k_pairs, dim3(1), dim3(1024), 0, st, f.counts, f.offsets, f.E, w.pairs, w.npairs);
+    const int ord = ffn_super_tile_order(p.ntiles_max);
+    const G1Args g1 = g1_args(f, w, ord);
+    const int grid1 = ord ? kXcds * ord_ranks(p.npairs_max, f.I / kGroup)
+                          : (int)(ceil_div((int64_t)(f.I / kGroup) * p.npairs_max, kXcds) * kXcds);
+    if (f.debug_h) hipLaunchKernelGGL((k_gemm1_mxp2<WF, true>), dim3(grid1), dim3(512), 0, st, g1);
+    else hipLaunchKernelGGL((k_gemm1_mxp2<WF, false>), dim3(grid1), dim3(512), 0, st, g1);
+    if (mid) {
+        const hipError_t e = hipEventRecord(mid, st);
+        if (e != hipSuccess) return e;
+    }
+    const int ord2 = ffn_super_tile_order_down(p.ntiles_max);
+    const G2Args g2 = g2_args(f, w, ord2);
+    const int grid2 = ord2 ? kXcds * ord_ranks(p.npairs_max, f.H / 256)
+                           : (int)(ceil_div((int64_t)(f.H / 256) * p.npairs_max, kXcds) * kXcds);
+    hipLaunchKernelGGL((k_gemm2_mxp2<WF>), dim3(grid2), dim3(512), 0, st, g2);
+    return hipGetLastError();
+}
+
+// The MX schemes on 128-row tiles, or on 256-row items (tile pairs) when the plan asks for them
+// (the plan takes either only for H % 256 == 0).
+hipError_t launch_ffn_mx_pf(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid,
+                            bool pairs_ready) {
     if (f.H % 256 != 0) return hipErrorInvalidValue;
+    if (p.pairs)
+        return f.quant == kQuantW4A8 ? run_ffn_mx_p2<kWfmtE2M1>(f, p, w, st, mid, pairs_ready)
+                                     : run_ffn_mx_p2<kWfmtE4M3>(f, p, w, st, mid, pairs_ready);
     return f.quant == kQuantW4A8 ? run_ffn_mx_pf<kWfmtE2M1>(f, p, w, st, mid)
                                  : run_ffn_mx_pf<kWfmtE4M3>(f, p, w, st, mid);
 }
@@ -2369,7 +2786,7 @@ hipError_t launch_grouped_ffn(const FfnArgs& f, void* ws, hipStream_t st, hipEve
         e = launch_ffn_w16(f, p, w, st, mid);
     } else if (f.quant != kQuantFp8Block128) {
         layout = kHlMx;
-        e = p.BM == 128 ? launch_ffn_mx_pf(f, p, w, st, mid) : launch_ffn_mx(f, p, w, st, mid);
+        e = p.BM == 128 ? launch_ffn_mx_pf(f, p, w, st, mid, pairs_ready) : launch_ffn_mx(f, p, w, st, mid);
     } else if (p.BM == 16) {
         // output columns per workgroup of the down GEMM = 128, a divisor of H
         layout = kHlDec;

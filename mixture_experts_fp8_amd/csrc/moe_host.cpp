@@ -51,8 +51,10 @@ FfnPlan ffn_plan(int T, int k, int E, int quant, int H) {
     const bool fp8 = quant == kQuantFp8Block128, mx = quant == kQuantMxfp8 || quant == kQuantW4A8;
     p.BM = avg > MOE_DEC_MAX_AVG_ROWS && (fp8 || (mx && H % 256 == 0)) ? 128 : 16;
     p.ntiles_max = (int)(cdiv(A, p.BM) + std::min<int64_t>(E, A));
-    p.pairs = fp8 && p.BM == 128 && avg >= MOE_PAIR_MIN_AVG_ROWS;
-    p.pairs_down = fp8 && (p.pairs || (p.BM == 128 && avg >= MOE_PAIR_DOWN_MIN_AVG_ROWS));
+    // 256-row items: both GEMMs from 128 rows per expert on; the 128-element scheme's down GEMM
+    // takes them from 64 on
+    p.pairs = p.BM == 128 && avg >= MOE_PAIR_MIN_AVG_ROWS;
+    p.pairs_down = p.pairs || (fp8 && p.BM == 128 && avg >= MOE_PAIR_DOWN_MIN_AVG_ROWS);
     // an expert's pairs number ceil(tiles / 2)
     p.npairs_max = (p.ntiles_max + (int)std::min<int64_t>(E, A)) / 2 + 1;
     return p;

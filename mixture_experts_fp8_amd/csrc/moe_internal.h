@@ -99,7 +99,8 @@ hipError_t launch_grouped_ffn(const FfnArgs& a, void* ws, hipStream_t st, hipEve
 // MX schemes on 16-row tiles (k_mx.hip)
 hipError_t launch_ffn_mx(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid);
 // MX schemes on 128-row tiles (k_ffn.hip)
-hipError_t launch_ffn_mx_pf(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid);
+hipError_t launch_ffn_mx_pf(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid,
+                            bool pairs_ready);
 // W8A16 on 16-row tiles (k_w16.hip); h in bf16 takes the hq region (sized 2 bytes per element)
 hipError_t launch_ffn_w16(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, hipStream_t st, hipEvent_t mid);
 

@@ -84,9 +84,9 @@ static void layouts() {
         for (int q = 0; q < 4; ++q) {
             const FfnPlan p = ffn_plan(T, k, E, q, H);
             CHECK(p.BM == 16 || p.BM == 128);
-            // the MX schemes take 128-row tiles only with 256-column down blocks; pairs are the
-            // 128-element scheme's, W8A16 stays on 16-row tiles
-            CHECK(q == kQuantFp8Block128 || (!p.pairs && !p.pairs_down));
+            // the MX schemes take 128-row tiles (and pairs) only with 256-column down blocks, and
+            // pairs for both GEMMs or neither; W8A16 stays on 16-row tiles
+            CHECK(q == kQuantFp8Block128 || p.pairs == p.pairs_down);
             CHECK(q != kQuantW8A16 || p.BM == 16);
             CHECK(!(q == kQuantMxfp8 || q == kQuantW4A8) || p.BM == 16 || H % 256 == 0);
             CHECK((int64_t)p.ntiles_max * p.BM >= (int64_t)T * k);   // every row has a tile slot

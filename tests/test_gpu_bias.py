@@ -130,9 +130,11 @@ def test_bias_fused_mx_w8a16(scheme):
 
 
 @pytest.mark.parametrize("scheme", ["mxfp8", "w4a8"])
-def test_bias_mx_prefill_tiles(scheme):
-    # the 128-row MX kernels (experts averaging > 24 rows, H % 256 == 0)
-    wl = W.Workload(169, "bmxp", T=400, H=512, I=256, E=4, k=2, ffn_bias=True)
+@pytest.mark.parametrize("wl", [W.Workload(169, "bmxp", T=400, H=512, I=256, E=4, k=2, ffn_bias=True),
+                                W.Workload(170, "bmxt", T=200, H=512, I=256, E=16, k=4, ffn_bias=True)],
+                         ids=["pairs", "tiles128"])
+def test_bias_mx_prefill_tiles(scheme, wl):
+    # the larger MX tiles (H % 256 == 0): 256-row items, and 128-row tiles below 128 rows per expert
     RQ._check(wl, scheme)
     _fused_check(wl, scheme)
 

@@ -120,13 +120,16 @@ def test_mx_fused_small(scheme, name):
     print(f"  rel fro {fro:.2e} rel max {mxe:.2e}", flush=True)
 
 
-# prefill-sized shapes on the 128-row MX kernels (experts averaging > 24 rows, H % 256 == 0):
-# several K blocks, one K block in the down GEMM (I = 128), ragged and skewed tiles; and the
-# 16-row kernels at prefill size where H % 256 != 0
+# prefill-sized shapes on the larger MX tiles (H % 256 == 0): 128-row tiles where experts
+# average 25..127 rows, 256-row items from 128 on; several K blocks, one K block in the down
+# GEMM (I = 128), ragged and skewed tiles, single-tile items; and the 16-row kernels at prefill
+# size where H % 256 != 0
 PREFILL = {
-    "tiles128": W.Workload(134, "mx_t128", T=600, H=512, I=384, E=8, k=3),
-    "down_kb1": W.Workload(135, "mx_kb1", T=400, H=256, I=128, E=4, k=2),
-    "skewed_ragged": W.Workload(136, "mx_skew", T=777, H=768, I=640, E=16, k=4, bias="normal1.5"),
+    "tiles128": W.Workload(139, "mx_t128", T=300, H=512, I=384, E=16, k=4),
+    "tiles128_down_kb1": W.Workload(140, "mx_t128kb1", T=200, H=256, I=128, E=8, k=3),
+    "pairs": W.Workload(134, "mx_pairs", T=600, H=512, I=384, E=8, k=3),
+    "pairs_down_kb1": W.Workload(135, "mx_kb1", T=400, H=256, I=128, E=4, k=2),
+    "pairs_skewed_ragged": W.Workload(136, "mx_skew", T=777, H=768, I=640, E=16, k=4, bias="normal1.5"),
     "H384_16row": W.Workload(137, "mx_h384", T=500, H=384, I=256, E=4, k=2),
 }
 

@@ -137,8 +137,9 @@ def test_requant_unit_fp8_prefill_sampled(cfg):
 
 @pytest.mark.parametrize("scheme", ["mxfp8", "w4a8"])
 @pytest.mark.parametrize("wl", [W.CONFIGS[2], W.Workload(131, "p2s", T=1500, H=256, I=256, E=8, k=4, bias="normal1.5"),
-                                W.Workload(138, "mxt", T=700, H=512, I=384, E=8, k=3)],
-                         ids=["decode_gemma4", "skewed_prefill", "tiles128_I384"])
+                                W.Workload(138, "mxt", T=700, H=512, I=384, E=8, k=3),
+                                W.Workload(141, "mxpf", T=300, H=512, I=384, E=16, k=4)],
+                         ids=["decode_gemma4", "skewed_prefill_pairs", "pairs_I384", "tiles128_I384"])
 def test_requant_unit_mx(scheme, wl):
     _check(wl, scheme)
 
