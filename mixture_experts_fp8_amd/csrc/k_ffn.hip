@@ -1966,6 +1966,106 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_p2(G1Args a) {
             *reinterpret_cast<const uint4*>(s_exT + tid * 16);
 }
 
+// Two float32 values as packed bf16 (round to nearest even), a in the low half: one
+// conversion instruction on gfx950.
+typedef float v2f_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_bits(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f_t{a, b}, bf16x2_t));
+}
+
+// Output of a 256-row down item through an LDS staging buffer of BUF bytes (free after the K
+// loop), as whole 16-byte pieces of full rows, in passes of RP rows: bf16 RP = 256 if the
+// buffer holds them (512 bytes a row), else 128; float32 RP = 128 or 64 (1 KB a row).  A lane
+// holds rows wm * 128 + 16 mi + 4 (lane / 16) + i of columns wn * 64 + 16 j + lane % 16;
+// staged rows are swizzled by 16 columns times (row / 4) % 4, which for a lane's rows is
+// lane / 16, so the lane's offsets per j are formed once.  The two lanes of a column pair
+// swap one value of each row pair, so that the even lane holds rows 0 and 2 and the odd lane
+// rows 1 and 3 of both columns; each lane then writes both columns of each of its two rows
+// (bf16: one conversion of the pair into a dword; float32: 8 bytes).  The bf16 read-out walks
+// 16 rows a step with offsets fixed per thread.  The caller has synchronised the workgroup
+// after its last read of the buffer.
+template <int BUF>
+__device__ __forceinline__ void p2_store_output(const G2Args& a, v4f (&acc)[8][4], uint8_t* buf, int rowbase,
+                                                int nvalid, int nb, int nact) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wv >> 2, wn = wv & 3, r16 = lane & 15, r0 = 4 * (lane >> 4), q4 = lane >> 4;
+    const int odd = lane & 1;
+    if (a.out_bf16) {
+        constexpr int RP = BUF >= 256 * 512 ? 256 : 128;
+        static_assert(BUF >= RP * 512, "staging buffer too small");
+#pragma unroll
+        for (int q = 0; q < 256 / RP; ++q) {
+            const int nr = min(RP, nvalid - q * RP);
+            if (nr <= 0) break;
+            if (q) __syncthreads();   // the previous pass has left the LDS
+            uint32_t ob[4];           // bytes: row r0 + odd of the pass, swizzled column pair of fragment j
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ob[j] = (r0 + odd) * 512 + 2 * (wn * 64 + 16 * (j ^ q4) + (r16 & 14));
+#pragma unroll
+            for (int mi = 0; mi < 8; ++mi) {
+                const int R0 = wm * kPfBM + mi * 16 - q * RP;   // wave-uniform
+                if (mi < nact && R0 >= 0 && R0 < RP) {
+#pragma unroll
+                    for (int ip = 0; ip < 2; ++ip)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const float lo = acc[mi][j][2 * ip], hi = acc[mi][j][2 * ip + 1];
+                            const float got = dpp_f32<0xB1>(odd ? lo : hi);   // from lane ^ 1
+                            // even lane: row 2 ip, columns (own, neighbour's); odd: row 2 ip + 1
+                            const uint32_t v = bf16x2_bits(odd ? got : lo, odd ? hi : got);
+                            *reinterpret_cast<uint32_t*>(buf + ob[j] + (R0 + 2 * ip) * 512) = v;
+                        }
+                }
+            }
+            __syncthreads();
+            // thread t moves 16 bytes (8 columns) of rows t / 32 + 16 s: its LDS swizzle and
+            // column stay fixed
+            const int m = tid & 31, R1 = tid >> 5;
+            const uint8_t* src = buf + (R1 * 256 + ((8 * m) ^ (16 * ((R1 >> 2) & 3)))) * 2;
+            uint8_t* dst = reinterpret_cast<uint8_t*>(a.out) + ((int64_t)(rowbase + q * RP + R1) * a.H + nb * 256 + 8 * m) * 2;
+            const int64_t rstep = (int64_t)16 * a.H * 2;
+            for (int R = R1; R < nr; R += 16, src += 16 * 512, dst += rstep)
+                *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+        }
+    } else {
+        constexpr int RP = BUF >= 128 * 1024 ? 128 : 64;
+        static_assert(BUF >= RP * 1024, "staging buffer too small");
+        float* out = reinterpret_cast<float*>(a.out);
+#pragma unroll
+        for (int q = 0; q < 256 / RP; ++q) {
+            const int nr = min(RP, nvalid - q * RP);
+            if (nr <= 0) break;
+            if (q) __syncthreads();
+            uint32_t ob[4];   // bytes: row r0 + odd, swizzled column pair of fragment j
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ob[j] = (r0 + odd) * 1024 + 4 * (wn * 64 + 16 * (j ^ q4) + (r16 & 14));
+#pragma unroll
+            for (int mi = 0; mi < 8; ++mi) {
+                const int R0 = wm * kPfBM + mi * 16 - q * RP;
+                if (mi < nact && R0 >= 0 && R0 < RP) {
+#pragma unroll
+                    for (int ip = 0; ip < 2; ++ip)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {   // the column-pair exchange of the bf16 path
+                            const float lo = acc[mi][j][2 * ip], hi = acc[mi][j][2 * ip + 1];
+                            const float got = dpp_f32<0xB1>(odd ? lo : hi);
+                            *reinterpret_cast<v2f_t*>(buf + ob[j] + (R0 + 2 * ip) * 1024) =
+                                v2f_t{odd ? got : lo, odd ? hi : got};
+                        }
+                }
+            }
+            __syncthreads();
+            const float* s_o = reinterpret_cast<const float*>(buf);
+            for (int t = tid; t < nr * 64; t += 512) {
+                const int R = t >> 6, m = t & 63;
+                const float4 v = *reinterpret_cast<const float4*>(s_o + R * 256 + ((4 * m) ^ (16 * ((R >> 2) & 3))));
+                *reinterpret_cast<float4*>(out + (int64_t)(rowbase + q * RP + R) * a.H + nb * 256 + 4 * m) = v;
+            }
+        }
+    }
+}
+
 __global__ __launch_bounds__(512, 1) void k_gemm2_p2(G2Args a) {
     int nb, pair;
     if (!pf_work_item(a.ord, a.H / 256, __builtin_amdgcn_readfirstlane(*a.npairs), pair, nb)) return;
@@ -2087,63 +2187,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm2_p2(G2Args a) {
         }
     }
 
-    // Output: the tile goes through the LDS stages (free after the K loop) so that it leaves as
-    // whole 16-byte pieces of full rows.  A lane holds rows wm * 128 + 16 mi + 4 (lane / 16) + i
-    // of columns wn * 64 + 16 j + lane % 16.  LDS rows are swizzled by 16 columns times
-    // (row / 4) % 4, so the four rows one store instruction writes land in distinct banks.
     __syncthreads();   // every wave is done reading the stages
-    const int r0 = 4 * (lane >> 4);
-    if (a.out_bf16) {
-        // one pass: 256 rows x 256 bf16 (512 bytes a row); neighbour lanes pair their columns
-        uint32_t* s_o = reinterpret_cast<uint32_t*>(buf);
-        if (nact > 0) {
-#pragma unroll
-            for (int mi = 0; mi < 8; ++mi)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const uint32_t v = f32_to_bf16(acc[mi][j][i]);
-                        const uint32_t nbv = dpp_u32<0xB1>(v);   // lane ^ 1
-                        if (!(lane & 1)) {
-                            const int R = wm * kPfBM + mi * 16 + r0 + i, c = wn * 64 + 16 * j + r16;
-                            s_o[(R * 256 + (c ^ (16 * ((R >> 2) & 3)))) >> 1] = v | (nbv << 16);
-                        }
-                    }
-        }
-        __syncthreads();
-        uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
-        for (int t = tid; t < nvalid * 32; t += 512) {
-            const int R = t >> 5, m = t & 31;
-            const uint4 v = *reinterpret_cast<const uint4*>(buf + (R * 256 + ((8 * m) ^ (16 * ((R >> 2) & 3)))) * 2);
-            *reinterpret_cast<uint4*>(out + (int64_t)(rowbase + R) * a.H + nb * 256 + 8 * m) = v;
-        }
-    } else {
-        // two passes of 128 rows x 256 float32 (1 KB a row): the waves of row half h stage it
-        float* s_o = reinterpret_cast<float*>(buf);
-        float* out = reinterpret_cast<float*>(a.out);
-        for (int h = 0; h < (second ? 2 : 1); ++h) {
-            if (h) __syncthreads();   // the first half has left the LDS
-            if (wm == h && nact > 0) {
-#pragma unroll
-                for (int mi = 0; mi < 8; ++mi)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const int R = mi * 16 + r0 + i, c = wn * 64 + 16 * j + r16;
-                            s_o[R * 256 + (c ^ (16 * ((R >> 2) & 3)))] = acc[mi][j][i];
-                        }
-            }
-            __syncthreads();
-            const int nr = min(kPfBM, nvalid - h * kPfBM);
-            for (int t = tid; t < nr * 64; t += 512) {
-                const int R = t >> 6, m = t & 63;
-                const float4 v = *reinterpret_cast<const float4*>(s_o + R * 256 + ((4 * m) ^ (16 * ((R >> 2) & 3))));
-                *reinterpret_cast<float4*>(out + (int64_t)(rowbase + h * kPfBM + R) * a.H + nb * 256 + 4 * m) = v;
-            }
-        }
-    }
+    p2_store_output<2 * kP2Stage>(a, acc, buf, rowbase, nvalid, nb, nact);
 }
 
 // ----------------------------------------------------------------------------------------
@@ -2167,84 +2212,6 @@ __device__ __forceinline__ v8i mx_lds_wfrag_at(const uint8_t* wbase, int f, int 
         return v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
     } else {
         return lds_frag(wbase + f * 2048, lane);
-    }
-}
-
-// Output of a 256-row down item through an LDS staging buffer of BUF bytes (free after the K
-// loop), as whole 16-byte pieces of full rows, in passes of RP rows: bf16 RP = 256 if the
-// buffer holds them (512 bytes a row), else 128; float32 RP = 128 or 64 (1 KB a row).  A lane holds rows wm * 128 + 16 mi + 4 (lane / 16) + i of
-// columns wn * 64 + 16 j + lane % 16; staged rows are swizzled by 16 columns times
-// (row / 4) % 4, which for a lane's rows is lane / 16, so the lane's offsets per j are formed
-// once.  The caller has synchronised the workgroup after its last read of the buffer.
-template <int BUF>
-__device__ __forceinline__ void p2_store_output(const G2Args& a, v4f (&acc)[8][4], uint8_t* buf, int rowbase,
-                                                int nvalid, int nb, int nact) {
-    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wv >> 2, wn = wv & 3, r16 = lane & 15, r0 = 4 * (lane >> 4), q4 = lane >> 4;
-    if (a.out_bf16) {
-        constexpr int RP = BUF >= 256 * 512 ? 256 : 128;
-        static_assert(BUF >= RP * 512, "staging buffer too small");
-        uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
-#pragma unroll
-        for (int q = 0; q < 256 / RP; ++q) {
-            const int nr = min(RP, nvalid - q * RP);
-            if (nr <= 0) break;
-            if (q) __syncthreads();   // the previous pass has left the LDS
-            uint32_t ob[4];           // bytes: row r0 of the pass, swizzled column of fragment j
-#pragma unroll
-            for (int j = 0; j < 4; ++j) ob[j] = r0 * 512 + 2 * (wn * 64 + 16 * (j ^ q4) + r16);
-#pragma unroll
-            for (int mi = 0; mi < 8; ++mi) {
-                const int R0 = wm * kPfBM + mi * 16 - q * RP;   // wave-uniform
-                if (mi < nact && R0 >= 0 && R0 < RP) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const uint32_t v = f32_to_bf16(acc[mi][j][i]);
-                            const uint32_t nbv = dpp_u32<0xB1>(v);   // lane ^ 1
-                            if (!(lane & 1)) *reinterpret_cast<uint32_t*>(buf + ob[j] + (R0 + i) * 512) = v | (nbv << 16);
-                        }
-                }
-            }
-            __syncthreads();
-            for (int t = tid; t < nr * 32; t += 512) {
-                const int R = t >> 5, m = t & 31;
-                const uint4 v = *reinterpret_cast<const uint4*>(buf + (R * 256 + ((8 * m) ^ (16 * ((R >> 2) & 3)))) * 2);
-                *reinterpret_cast<uint4*>(out + (int64_t)(rowbase + q * RP + R) * a.H + nb * 256 + 8 * m) = v;
-            }
-        }
-    } else {
-        constexpr int RP = BUF >= 128 * 1024 ? 128 : 64;
-        static_assert(BUF >= RP * 1024, "staging buffer too small");
-        float* out = reinterpret_cast<float*>(a.out);
-#pragma unroll
-        for (int q = 0; q < 256 / RP; ++q) {
-            const int nr = min(RP, nvalid - q * RP);
-            if (nr <= 0) break;
-            if (q) __syncthreads();
-            uint32_t ob[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) ob[j] = r0 * 1024 + 4 * (wn * 64 + 16 * (j ^ q4) + r16);
-#pragma unroll
-            for (int mi = 0; mi < 8; ++mi) {
-                const int R0 = wm * kPfBM + mi * 16 - q * RP;
-                if (mi < nact && R0 >= 0 && R0 < RP) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            *reinterpret_cast<float*>(buf + ob[j] + (R0 + i) * 1024) = acc[mi][j][i];
-                }
-            }
-            __syncthreads();
-            const float* s_o = reinterpret_cast<const float*>(buf);
-            for (int t = tid; t < nr * 64; t += 512) {
-                const int R = t >> 6, m = t & 63;
-                const float4 v = *reinterpret_cast<const float4*>(s_o + R * 256 + ((4 * m) ^ (16 * ((R >> 2) & 3))));
-                *reinterpret_cast<float4*>(out + (int64_t)(rowbase + q * RP + R) * a.H + nb * 256 + 4 * m) = v;
-            }
-        }
     }
 }
 

@@ -240,3 +240,44 @@ def test_combine_parity_on_generated_expert_out(T, k, H):
     ob = eob.double().numpy()[perm.numpy().astype(np.int64)]
     y_ref_b = omoe.combine(ob, w.double().numpy())
     assert np.all(np.abs(yb - y_ref_b) <= np.abs(y_ref_b) * 2.0 ** -8 + 1e-6 * omoe.combine(np.abs(ob), w.double().numpy()))
+
+
+# bf16 expert outputs against the float32 ones of the same call rounded to nearest even on the
+# host, bit for bit: the conversion and the lane exchange of every down kernel's bf16 store
+# (256-row items FP8 and MX, 128-row tiles, 16-row decode tiles, W8A16)
+BF16_OUT_CASES = {
+    "fp8_pairs": (W.Workload(190, "bo_p2", T=1500, H=512, I=256, E=8, k=4, bias="normal1.5"), "fp8"),
+    "fp8_tiles128": (W.Workload(191, "bo_t128", T=600, H=256, I=384, E=32, k=2), "fp8"),
+    "fp8_decode": (W.Workload(192, "bo_dec", T=24, H=512, I=256, E=16, k=4), "fp8"),
+    "mxfp8_pairs": (W.Workload(193, "bo_mxp2", T=600, H=512, I=384, E=8, k=3), "mxfp8"),
+    "w4a8_pairs_ragged": (W.Workload(194, "bo_w4p2", T=700, H=512, I=256, E=4, k=2, bias="zipf"), "w4a8"),
+    "w4a8_tiles128": (W.Workload(195, "bo_w4t", T=300, H=512, I=384, E=16, k=4), "w4a8"),
+    "w8a16": (W.Workload(196, "bo_w16", T=40, H=256, I=384, E=8, k=3), "w8a16"),
+}
+
+
+@pytest.mark.parametrize("name", list(BF16_OUT_CASES))
+def test_bf16_expert_out_is_rounded_float32(name):
+    wl, scheme = BF16_OUT_CASES[name]
+    print("bf16 expert_out", name, scheme, W.describe(wl), flush=True)
+    x, logits, _ = HN.device_inputs(wl)
+    if scheme == "fp8":
+        w = HN.device_weights(wl)
+    elif scheme == "w8a16":
+        w = HN.device_weights(wl).with_quant(M.MOE_QUANT_W8A16)
+    else:
+        w = HN.device_weights_mx(wl, M.QUANT_SCHEMES[scheme])
+    r = M.moe_route(HN.device_params(wl), wl.T, router_logits=logits)
+    xq = xs = None
+    kw = {}
+    if scheme == "w8a16":
+        kw["x"] = x
+    else:
+        xq, xs = (M.moe_quant_act if scheme == "fp8" else M.moe_quant_act_mx)(x)
+    e32 = M.moe_grouped_ffn(xq, xs, r, w, wl.k, out_dtype=torch.float32, **kw)
+    e16 = M.moe_grouped_ffn(xq, xs, r, w, wl.k, out_dtype=torch.bfloat16, **kw)
+    ref = e32.to(torch.bfloat16)
+    diff = (e16.view(torch.int16) != ref.view(torch.int16)).sum().item()
+    ties = ((e32.view(torch.int32) & 0xFFFF) == 0x8000).sum().item()
+    print(f"  {e16.numel()} values, {ties} exact ties in float32, {diff} differ", flush=True)
+    assert diff == 0
