@@ -769,20 +769,27 @@ __device__ __forceinline__ void max16x4(float (&m)[4]) {
 // SwiGLU of one 16-row fragment: gate columns acc[jj], up columns acc[2 + jj] (jj = 0, 1),
 // plus the lane's column biases when b13 is set -> h[jj][i]; m[i] = max |h| of row
 // 4 (lane / 16) + i over the 32 columns of the two fragments (in every lane of the 16-lane group).
-__device__ __forceinline__ void swiglu_frag(const v4f* acc, const float* b13, const GuBias (&bias)[2],
-                                            float (&h)[2][4], float (&m)[4]) {
+template <bool BIAS>
+__device__ __forceinline__ void swiglu_frag_b(const v4f* acc, const GuBias (&bias)[2], float (&h)[2][4],
+                                              float (&m)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         m[i] = 0.f;
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
-            const float g = add_bias(b13, acc[jj][i], bias[jj].g);
-            h[jj][i] = g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.44269504f)) *
-                       add_bias(b13, acc[2 + jj][i], bias[jj].u);
+            const float g = BIAS ? acc[jj][i] + bias[jj].g : acc[jj][i];
+            const float u = BIAS ? acc[2 + jj][i] + bias[jj].u : acc[2 + jj][i];
+            h[jj][i] = g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.44269504f)) * u;
             m[i] = fmaxf(m[i], fabsf(h[jj][i]));
         }
     }
     max16x4(m);
+}
+// (the bias test is uniform: one branch per fragment instead of a select per value)
+__device__ __forceinline__ void swiglu_frag(const v4f* acc, const float* b13, const GuBias (&bias)[2],
+                                            float (&h)[2][4], float (&m)[4]) {
+    if (b13) swiglu_frag_b<true>(acc, bias, h, m);
+    else swiglu_frag_b<false>(acc, bias, h, m);
 }
 
 // E4M3 bytes of a lane quad's 4 x 4 block (lane 4Q + q of a 16-lane group holds column
