@@ -1095,7 +1095,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pp(G1Args a) {
                        (uint32_t)(rowbase + wv * 64) * 4);
         }
     };
-    uint32_t sv[SVN], sgu = 0;
+    uint32_t sv[SVN], sgu_g = 0, sgu_u = 0;   // combined only where stored (see below)
     auto scale_loads = [&](int n) __attribute__((always_inline)) {
         const int4 it = s_it[n];
         const int ib = __builtin_amdgcn_readfirstlane(it.y), e = __builtin_amdgcn_readfirstlane(it.z);
@@ -1108,7 +1108,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pp(G1Args a) {
         }
         if (tid < KB) {
             const uint8_t* sb = a.w13s + ((int64_t)e * KB + tid) * NBS;
-            sgu = (uint32_t)sb[ib] | (uint32_t)sb[ncol + ib] << 8;
+            sgu_g = sb[ib];
+            sgu_u = sb[ncol + ib];
         }
     };
     auto scale_stores = [&](int n) __attribute__((always_inline)) {
@@ -1118,7 +1119,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pp(G1Args a) {
             const int kb = (tid & 3) + 4 * t;
             if (kb < KB) s_sa[n & 1][kb * kPfBM + sa_pos] = (uint8_t)sv[t];
         }
-        if (tid < KB) s_sgu[n & 1][tid] = (uint16_t)sgu;
+        if (tid < KB) s_sgu[n & 1][tid] = (uint16_t)(sgu_g | sgu_u << 8);
     };
     // DMA stream state: the item whose blocks are being issued
     uint32_t aoff[2], bsoff[4];
@@ -1186,9 +1187,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pp(G1Args a) {
             if (g + 1 < G) wait_vm<6>();   // block g landed (block g + 1's 6 DMAs may be in flight) ...
             else wait_vm<0>();
             __syncthreads();               // ... everywhere; every wave is done with block g - 1's stage
-            // the ids DMA and scale loads go before this step's block DMA (see the waits above)
-            if (kb == KB - 1 && more) scale_stores(n + 1);
-            if (kb == KB - 2 && more) scale_loads(n + 1);
+            // the ids DMA goes before this step's block DMA (see the waits above)
             if (kb == 0 && n + 2 < cnt) tok_dma(n + 2);
             if (g + 2 < G) {   // block g + 2 into the stage of block g - 1
                 if (++dkb == KB) {
@@ -1221,23 +1220,38 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pp(G1Args a) {
                 }
         }
 
-        // ---- epilogue of item n (the next item's first block is in flight in the other stage)
-        GuBias bias[2];
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) bias[jj] = gu_bias(a.b13, it.z, a.I, ib * 128 + (2 * wn + jj) * 16 + r16);
+        // ---- epilogue of item n (the next item's first blocks are in flight in the other stages)
+        // The compiler does not see the DMAs, so its wait for any load it issued (vmcnt counts
+        // in issue order) also waits for every DMA issued before; such waits must come only
+        // after those blocks have landed, late in the epilogue.  Hence: the next item's
+        // scales are loaded here and stored at the end (after the last item the current
+        // item's are reloaded into its own table, so that no load is left unused on any path
+        // through the loop), and the bias loads and their SwiGLU form a branch of their own,
+        // so that without biases no load is pending at the SwiGLU's register writes.
+        const int sn = more ? n + 1 : n;
+        scale_loads(sn);
         float hv[4][2][4];
+        auto swiglu_all = [&](auto HASB) __attribute__((always_inline)) {
+            GuBias bias[2] = {};
+            if constexpr (decltype(HASB)::value) {
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            if (mi < nact) {
-                float m[4];
-                swiglu_frag(acc[mi], a.b13, bias, hv[mi], m);
-                tap_frag<TAP>(a.htap, a.I, it.w, (wm * 4 + mi) * 16, nvalid, ib * 128 + 2 * wn * 16, hv[mi]);
-                if (r16 == 0) {
+                for (int jj = 0; jj < 2; ++jj) bias[jj] = gu_bias(a.b13, it.z, a.I, ib * 128 + (2 * wn + jj) * 16 + r16);
+            }
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) s_amax[(wm * 4 + mi) * 16 + 4 * (lane >> 4) + i][wn] = m[i];
+            for (int mi = 0; mi < 4; ++mi) {
+                if (mi < nact) {
+                    float m[4];
+                    swiglu_frag_b<decltype(HASB)::value>(acc[mi], bias, hv[mi], m);
+                    tap_frag<TAP>(a.htap, a.I, it.w, (wm * 4 + mi) * 16, nvalid, ib * 128 + 2 * wn * 16, hv[mi]);
+                    if (r16 == 0) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) s_amax[(wm * 4 + mi) * 16 + 4 * (lane >> 4) + i][wn] = m[i];
+                    }
                 }
             }
-        }
+        };
+        if (a.b13) swiglu_all(std::true_type{});
+        else swiglu_all(std::false_type{});
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
@@ -1270,6 +1284,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pp(G1Args a) {
         if (tid < 8)   // the tile's hs block for this column block: [row % 16][row / 16]
             *reinterpret_cast<uint4*>(a.hs + ((int64_t)tile * ncol + ib) * 128 + tid * 16) =
                 *reinterpret_cast<const uint4*>(s_exT + tid * 16);
+        scale_stores(sn);   // read after the next item's first barrier
     }
     wait_vm<0>();
 }

@@ -98,6 +98,9 @@ __device__ __forceinline__ int it_fill_items(int ord, int ncol, int ntiles, cons
         base += tot;
         __syncthreads();
     }
+    // Every load above has been used; the wait (which the compiler sees) keeps a load it
+    // skipped on some path from being waited for later, inside the caller's DMA stream.
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     return min(base, cap);
 }
 
