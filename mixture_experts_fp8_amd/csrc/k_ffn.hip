@@ -2001,7 +2001,9 @@ __device__ __forceinline__ uint32_t bf16x2_bits(float a, float b) {
 // buffer holds them (512 bytes a row), else 128; float32 RP = 128 or 64 (1 KB a row).  A lane
 // holds rows wm * 128 + 16 mi + 4 (lane / 16) + i of columns wn * 64 + 16 j + lane % 16;
 // staged rows are swizzled by 16 columns times (row / 4) % 4, which for a lane's rows is
-// lane / 16, so the lane's offsets per j are formed once.  The two lanes of a column pair
+// lane / 16, so the lane's offsets per j are formed once; a row-parity term keeps the two rows a
+// lane pair writes together in different banks (odd rows: the 16-column index also XOR 2 for
+// bf16, XOR 1 for float32).  The two lanes of a column pair
 // swap one value of each row pair, so that the even lane holds rows 0 and 2 and the odd lane
 // rows 1 and 3 of both columns; each lane then writes both columns of each of its two rows
 // (bf16: one conversion of the pair into a dword; float32: 8 bytes).  The bf16 read-out walks
@@ -2023,7 +2025,7 @@ __device__ __forceinline__ void p2_store_output(const G2Args& a, v4f (&acc)[8][4
             if (q) __syncthreads();   // the previous pass has left the LDS
             uint32_t ob[4];           // bytes: row r0 + odd of the pass, swizzled column pair of fragment j
 #pragma unroll
-            for (int j = 0; j < 4; ++j) ob[j] = (r0 + odd) * 512 + 2 * (wn * 64 + 16 * (j ^ q4) + (r16 & 14));
+            for (int j = 0; j < 4; ++j) ob[j] = (r0 + odd) * 512 + 2 * (wn * 64 + 16 * (j ^ q4 ^ (2 * odd)) + (r16 & 14));
 #pragma unroll
             for (int mi = 0; mi < 8; ++mi) {
                 const int R0 = wm * kPfBM + mi * 16 - q * RP;   // wave-uniform
@@ -2044,7 +2046,7 @@ __device__ __forceinline__ void p2_store_output(const G2Args& a, v4f (&acc)[8][4
             // thread t moves 16 bytes (8 columns) of rows t / 32 + 16 s: its LDS swizzle and
             // column stay fixed
             const int m = tid & 31, R1 = tid >> 5;
-            const uint8_t* src = buf + (R1 * 256 + ((8 * m) ^ (16 * ((R1 >> 2) & 3)))) * 2;
+            const uint8_t* src = buf + (R1 * 256 + ((8 * m) ^ (16 * (((R1 >> 2) & 3) ^ (2 * (R1 & 1)))))) * 2;
             uint8_t* dst = reinterpret_cast<uint8_t*>(a.out) + ((int64_t)(rowbase + q * RP + R1) * a.H + nb * 256 + 8 * m) * 2;
             const int64_t rstep = (int64_t)16 * a.H * 2;
             for (int R = R1; R < nr; R += 16, src += 16 * 512, dst += rstep)
@@ -2061,7 +2063,7 @@ __device__ __forceinline__ void p2_store_output(const G2Args& a, v4f (&acc)[8][4
             if (q) __syncthreads();
             uint32_t ob[4];   // bytes: row r0 + odd, swizzled column pair of fragment j
 #pragma unroll
-            for (int j = 0; j < 4; ++j) ob[j] = (r0 + odd) * 1024 + 4 * (wn * 64 + 16 * (j ^ q4) + (r16 & 14));
+            for (int j = 0; j < 4; ++j) ob[j] = (r0 + odd) * 1024 + 4 * (wn * 64 + 16 * (j ^ q4 ^ odd) + (r16 & 14));
 #pragma unroll
             for (int mi = 0; mi < 8; ++mi) {
                 const int R0 = wm * kPfBM + mi * 16 - q * RP;
@@ -2081,7 +2083,7 @@ __device__ __forceinline__ void p2_store_output(const G2Args& a, v4f (&acc)[8][4
             const float* s_o = reinterpret_cast<const float*>(buf);
             for (int t = tid; t < nr * 64; t += 512) {
                 const int R = t >> 6, m = t & 63;
-                const float4 v = *reinterpret_cast<const float4*>(s_o + R * 256 + ((4 * m) ^ (16 * ((R >> 2) & 3))));
+                const float4 v = *reinterpret_cast<const float4*>(s_o + R * 256 + ((4 * m) ^ (16 * (((R >> 2) & 3) ^ (R & 1)))));
                 *reinterpret_cast<float4*>(out + (int64_t)(rowbase + q * RP + R) * a.H + nb * 256 + 4 * m) = v;
             }
         }
