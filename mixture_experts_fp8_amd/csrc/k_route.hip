@@ -480,20 +480,21 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ cc, int nch
     }
 }
 
-__global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ ids, int A, int E, int nbits,
-                                                 const int32_t* __restrict__ chunk_base,
-                                                 int32_t* __restrict__ sorted_assign,
-                                                 int32_t* __restrict__ assign_pos) {
-    extern __shared__ int s_wc[];   // [4][E] per-wave running counts, then per-wave bases
+// The chunk's ranking and stores, given its per-expert bases base(e) (offsets[e] plus the
+// earlier chunks' counts of e).  s_wc: [4][E] ints of LDS.
+template <typename BaseFn>
+__device__ __forceinline__ void scatter_chunk(const int32_t* __restrict__ ids, int A, int E, int nbits, BaseFn base,
+                                              int32_t* __restrict__ sorted_assign, int32_t* __restrict__ assign_pos,
+                                              int* s_wc) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     for (int i = threadIdx.x; i < 4 * E; i += 256) s_wc[i] = 0;
     __syncthreads();
     const uint64_t lt = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
-    const int64_t base = (int64_t)blockIdx.x * kScatterChunk + wv * (kScatterChunk / 4);
+    const int64_t b0 = (int64_t)blockIdx.x * kScatterChunk + wv * (kScatterChunk / 4);
     int rank[kScatterChunk / 256], eid[kScatterChunk / 256];
 #pragma unroll
     for (int r = 0; r < kScatterChunk / 256; ++r) {
-        const int64_t f = base + r * 64 + lane;
+        const int64_t f = b0 + r * 64 + lane;
         int e = f < A ? ids[f] : 0;
         const bool valid = f < A && (unsigned)e < (unsigned)E;
         if (!valid) e = 0;
@@ -524,12 +525,135 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ ids
     for (int r = 0; r < kScatterChunk / 256; ++r) {
         const int e = eid[r];
         if (e >= 0) {
-            const int64_t f = base + r * 64 + lane;
-            const int pos = chunk_base[(int64_t)blockIdx.x * E + e] + s_wc[wv * E + e] + rank[r];
+            const int64_t f = b0 + r * 64 + lane;
+            const int pos = base(e) + s_wc[wv * E + e] + rank[r];
             sorted_assign[pos] = (int32_t)f;
             assign_pos[f] = pos;
         }
     }
+}
+
+__global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ ids, int A, int E, int nbits,
+                                                 const int32_t* __restrict__ chunk_base,
+                                                 int32_t* __restrict__ sorted_assign,
+                                                 int32_t* __restrict__ assign_pos) {
+    extern __shared__ int s_wc[];   // [4][E] per-wave running counts, then per-wave bases
+    const int32_t* cb = chunk_base + (int64_t)blockIdx.x * E;
+    scatter_chunk(ids, A, E, nbits, [&](int e) { return cb[e]; }, sorted_assign, assign_pos, s_wc);
+}
+
+// Exclusive scan over a workgroup of 256 threads; *total receives the sum (every thread).
+__device__ int block_exclusive_scan_256(int v, int* s_tmp /*[4]*/, int* total) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(x, o);
+        if (lane >= o) x += u;
+    }
+    if (lane == 63) s_tmp[wv] = x;
+    __syncthreads();
+    int add = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        add += w < wv ? s_tmp[w] : 0;
+        all += s_tmp[w];
+    }
+    __syncthreads();
+    *total = all;
+    return add + x - v;
+}
+
+// Scatter that forms its own bases, for launches where every chunk's counts are few
+// (at most kScanInScatterMaxChunks chunks and nchunks * E <= kScanInScatterMax): each workgroup (one chunk) sums all chunks' counts per
+// expert, scans the totals over the experts (offsets) and adds the earlier chunks' counts,
+// which is what k_scan writes for it; workgroup 0 also writes counts, offsets and the tile /
+// pair lists.  One launch instead of k_scan + k_scatter.
+constexpr int kScanInScatterMax = 32768, kScanInScatterMaxChunks = 256;
+constexpr int kSisEpt = MOE_DISPATCH_MAX_E / 256;   // experts per thread
+__global__ __launch_bounds__(256) void k_scatter_scan(const int32_t* __restrict__ ids, int A, int E, int nbits,
+                                                      const int32_t* __restrict__ cc, int nchunks,
+                                                      int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ sorted_assign,
+                                                      int32_t* __restrict__ assign_pos, int BM,
+                                                      int2* __restrict__ tiles, int32_t* __restrict__ ntiles,
+                                                      int4* __restrict__ pairs, int32_t* __restrict__ npairs) {
+    extern __shared__ int s_dyn[];   // [4][E] for the ranking, then [E] chunk bases
+    int* s_cb = s_dyn + 4 * E;
+    __shared__ int s_tmp[4];
+    const int tid = threadIdx.x, c0 = blockIdx.x;
+    int tot[kSisEpt], bef[kSisEpt];
+#pragma unroll
+    for (int q = 0; q < kSisEpt; ++q) {   // expert e = tid + 256 q
+        const int e = tid + 256 * q;
+        int t = 0, b = 0;
+        if (e < E) {
+            for (int c = 0; c < nchunks; c += 32) {   // 32 loads in flight
+                int v[32];
+#pragma unroll
+                for (int u = 0; u < 32; ++u) v[u] = c + u < nchunks ? cc[(int64_t)(c + u) * E + e] : 0;
+#pragma unroll
+                for (int u = 0; u < 32; ++u) {
+                    t += v[u];
+                    b += c + u < c0 ? v[u] : 0;
+                }
+            }
+        }
+        tot[q] = t;
+        bef[q] = b;
+    }
+    // expert offsets: exclusive scan of the totals in expert order (q outer, thread inner)
+    int run = 0, off[kSisEpt];
+#pragma unroll
+    for (int q = 0; q < kSisEpt; ++q) {
+        if (256 * q >= E) {   // uniform
+            off[q] = run;
+            continue;
+        }
+        int all;
+        off[q] = run + block_exclusive_scan_256(tot[q], s_tmp, &all);
+        run += all;
+    }
+#pragma unroll
+    for (int q = 0; q < kSisEpt; ++q) {
+        const int e = tid + 256 * q;
+        if (e < E) s_cb[e] = off[q] + bef[q];
+    }
+    if (c0 == 0) {   // uniform: counts, offsets, tile and pair lists (as k_scan writes them)
+#pragma unroll
+        for (int q = 0; q < kSisEpt; ++q) {
+            const int e = tid + 256 * q;
+            if (e < E) {
+                counts[e] = tot[q];
+                offsets[e] = off[q];
+                if (e == E - 1) offsets[E] = off[q] + tot[q];
+            }
+        }
+        if (tiles) {
+            int trun = 0, prun = 0;
+#pragma unroll
+            for (int q = 0; q < kSisEpt; ++q) {
+                if (256 * q >= E) continue;   // uniform
+                const int e = tid + 256 * q;
+                const int nt = e < E ? (tot[q] + BM - 1) / BM : 0;
+                const int np = e < E && pairs ? (tot[q] + 2 * BM - 1) / (2 * BM) : 0;
+                int allt, allp;
+                const int t0 = trun + block_exclusive_scan_256(nt, s_tmp, &allt);
+                const int p0 = prun + block_exclusive_scan_256(np, s_tmp, &allp);
+                for (int i = 0; i < nt; ++i) tiles[t0 + i] = make_int2(e, i * BM);
+                for (int i = 0; i < np; ++i)
+                    pairs[p0 + i] = make_int4(t0 + 2 * i, e, off[q] + 2 * BM * i, min(2 * BM, tot[q] - 2 * BM * i));
+                trun += allt;
+                prun += allp;
+            }
+            if (tid == 0) {
+                *ntiles = trun;
+                if (pairs) *npairs = prun;
+            }
+        }
+    }
+    __syncthreads();   // s_cb complete before the ranking uses it
+    scatter_chunk(ids, A, E, nbits, [&](int e) { return s_cb[e]; }, sorted_assign, assign_pos, s_dyn);
 }
 
 // Single-workgroup dispatch for small A (8 waves).  Wave w owns the contiguous segment
@@ -688,6 +812,12 @@ hipError_t launch_dispatch(const int32_t* ids, int A, int E, int32_t* chunk_ws, 
     }
     const int nchunks = (int)ceil_div(A, kScatterChunk);
     hipLaunchKernelGGL(k_hist, dim3(nchunks), dim3(256), (size_t)E * 4, st, ids, A, E, chunk_ws);
+    if (nchunks <= kScanInScatterMaxChunks && (int64_t)nchunks * E <= kScanInScatterMax) {
+        hipLaunchKernelGGL(k_scatter_scan, dim3(nchunks), dim3(256), (size_t)5 * E * 4, st, ids, A, E, nbits, chunk_ws,
+                           nchunks, counts, offsets, sorted_assign, assign_pos, BM, tiles, ntiles,
+                           tiles ? pairs : nullptr, npairs);
+        return hipGetLastError();
+    }
     int Ep = 1;
     while (Ep < E) Ep <<= 1;
     hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, chunk_ws, nchunks, E, Ep, counts, offsets, BM, tiles, ntiles,
