@@ -202,7 +202,11 @@ def test_dispatch_of_given_ids_with_skew_and_empty_experts():
     assert np.array_equal(got["assign_pos"].cpu().numpy(), ap)
 
 
-@pytest.mark.parametrize("T,k,E", [(75000, 4, 100), (20000, 8, 1024), (5000, 1, 3), (40000, 6, 256)])
+# the scatter that forms its own bases takes up to 256 chunks of 1024 assignments and up to
+# 32768 chunk counts: (32768, 8, 128) and (16384, 8, 256) sit at those limits, (32769, 8, 128)
+# is one chunk past them (the three-kernel path, as the other large cases)
+@pytest.mark.parametrize("T,k,E", [(75000, 4, 100), (20000, 8, 1024), (5000, 1, 3), (40000, 6, 256),
+                                   (32768, 8, 128), (16384, 8, 256), (32769, 8, 128)])
 def test_dispatch_many_chunks(T, k, E):
     # hundreds of dispatch chunks, expert counts that are not powers of two, E = 1024, k = 1:
     # the chunk-parallel scan and the scatter must still give the stable counting sort
