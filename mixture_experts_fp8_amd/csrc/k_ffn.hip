@@ -1043,14 +1043,16 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pf(G1Args a) {
 // k_gemm1_pf).  One workgroup per CU walks its item list (tile, I column block) as one
 // stream of K blocks through three 48 KB LDS stages (two blocks in flight), so no item starts
 // from an empty pipeline:
-//   * the sorted assignment ids of item n + 1's rows reach LDS by a dword LDS-DMA issued at
+//   * the sorted assignment ids of item n + 2's rows reach LDS by a dword LDS-DMA issued at
 //     item n's first K block;
-//   * its A row scales (gathered through those ids) and gate/up weight scales are loaded at
-//     item n's K block KB - 2 and stored to the other half of a double table at block KB - 1;
-//   * its first two K blocks are issued at item n's last two blocks.
+//   * item n + 1's first two K blocks are issued at item n's last two blocks;
+//   * its A row scales (gathered through those ids) and gate/up weight scales are loaded at the
+//     start of item n's epilogue and stored to the other half of a double table at its end.
 // Waits: before computing block g, every vector-memory op older than block g + 1's DMA must be
-// done (vmcnt <= 6: that DMA is 6 ops per thread), so the ids DMA and the scale loads are
-// issued before a step's block DMA.  Needs 2 <= KB <= 32 and KB <= 4 SVN.
+// done (vmcnt <= 6: that DMA is 6 ops per thread), so the ids DMA is issued before a step's
+// block DMA.  The compiler does not see the DMAs, so its own wait for a load it issued also
+// waits for every DMA issued before: the loads it sees (the scales) are issued and used within
+// the epilogue only.  Needs 2 <= KB <= 32 and KB <= 4 SVN.
 constexpr int kPpMaxItems = 128, kPpMaxKB = 32, kPpStages = 3;
 
 // 4 bytes per lane from the buffer at voff + soff into LDS at m0base + 4 * lane.
@@ -1065,7 +1067,7 @@ template <int SVN, bool TAP>   // scale bytes a thread stages per item: KB <= 4 
 __global__ __launch_bounds__(512, 1) void k_gemm1_pp(G1Args a) {
     __shared__ __align__(16) uint8_t buf[kPpStages * kPfStage];
     __shared__ __align__(16) uint8_t s_sa[2][kPpMaxKB * kPfBM];   // [item parity][kb][wm][row % 16][fragment of wm]
-    __shared__ uint16_t s_sgu[2][kPpMaxKB];                      // gate scale | up scale << 8
+    __shared__ uint16_t s_sgu[2][kPpMaxKB + 1];                  // gate scale | up scale << 8 (+ a dummy slot)
     __shared__ __align__(16) int s_tok[2][kPfBM];                // sorted assignment ids of the item's rows
     __shared__ __align__(16) float s_amax[kPfBM][4];
     __shared__ __align__(16) uint8_t s_ex[kPfBM], s_exT[kPfBM];
@@ -1095,31 +1097,28 @@ __global__ __launch_bounds__(512, 1) void k_gemm1_pp(G1Args a) {
                        (uint32_t)(rowbase + wv * 64) * 4);
         }
     };
-    uint32_t sv[SVN], sgu_g = 0, sgu_u = 0;   // combined only where stored (see below)
+    // Every thread loads and stores on every path (sources clamped into range; the bytes of
+    // blocks kb >= KB land in table slots no one reads, kb < 4 SVN <= kPpMaxKB, and the gate/up
+    // scales of threads tid >= KB in a dummy slot): a load that one path skipped, or left
+    // unused, would make the compiler wait for it at the next write of its register, which
+    // falls inside the next item's DMA stream (see the epilogue).
+    uint32_t sv[SVN], sgu_g, sgu_u;   // combined only where stored (see below)
     auto scale_loads = [&](int n) __attribute__((always_inline)) {
         const int4 it = s_it[n];
         const int ib = __builtin_amdgcn_readfirstlane(it.y), e = __builtin_amdgcn_readfirstlane(it.z);
         const int nv = __builtin_amdgcn_readfirstlane(s_nv[n]);
         const uint8_t* src = a.xs + (int64_t)(s_tok[n & 1][min(rs, nv - 1)] / a.k) * KB;
 #pragma unroll
-        for (int t = 0; t < SVN; ++t) {
-            const int kb = (tid & 3) + 4 * t;
-            sv[t] = kb < KB ? src[kb] : 0u;
-        }
-        if (tid < KB) {
-            const uint8_t* sb = a.w13s + ((int64_t)e * KB + tid) * NBS;
-            sgu_g = sb[ib];
-            sgu_u = sb[ncol + ib];
-        }
+        for (int t = 0; t < SVN; ++t) sv[t] = src[min((tid & 3) + 4 * t, KB - 1)];
+        const uint8_t* sb = a.w13s + ((int64_t)e * KB + min(tid, KB - 1)) * NBS;
+        sgu_g = sb[ib];
+        sgu_u = sb[ncol + ib];
     };
     auto scale_stores = [&](int n) __attribute__((always_inline)) {
         const int sa_pos = (rs >> 6) * 64 + (rs & 15) * 4 + ((rs >> 4) & 3);
 #pragma unroll
-        for (int t = 0; t < SVN; ++t) {
-            const int kb = (tid & 3) + 4 * t;
-            if (kb < KB) s_sa[n & 1][kb * kPfBM + sa_pos] = (uint8_t)sv[t];
-        }
-        if (tid < KB) s_sgu[n & 1][tid] = (uint16_t)(sgu_g | sgu_u << 8);
+        for (int t = 0; t < SVN; ++t) s_sa[n & 1][((tid & 3) + 4 * t) * kPfBM + sa_pos] = (uint8_t)sv[t];
+        s_sgu[n & 1][min(tid, kPpMaxKB)] = (uint16_t)(sgu_g | sgu_u << 8);
     };
     // DMA stream state: the item whose blocks are being issued
     uint32_t aoff[2], bsoff[4];

@@ -38,6 +38,8 @@ SMALL = {
     # and the per-tile kernel for a single K block
     "persistent_tiles_skewed": W.Workload(133, "ppS", T=900, H=512, I=384, E=32, k=3, bias="normal1.5"),
     "persistent_tiles_kb12": W.Workload(134, "pp12", T=700, H=1536, I=256, E=16, k=2),
+    # two or three items in all: most XCD shares of the persistent kernel's work queues are empty
+    "persistent_tiles_few_items": W.Workload(171, "ppfew", T=200, H=256, I=128, E=2, k=1),
     "staged_tiles_kb1": W.Workload(135, "pfkb1", T=800, H=128, I=256, E=16, k=2),
     "sigmoid_groups": W.Workload(125, "grp", T=96, H=384, I=256, E=32, k=4, scoring="sigmoid", group_count=4,
                                  k_group=2, group_select_mode=1, routed_scaling_factor=2.5),
@@ -255,6 +257,11 @@ def test_fused_workload_sampled(cfg):
 MEDIUM = {
     "persistent_tile_pairs_kb16": W.Workload(136, "p2pk16", T=4096, H=2048, I=2048, E=4, k=2, bias="normal1.5"),
     "persistent_tile_pairs_kb32": W.Workload(137, "p2pk32", T=6144, H=4096, I=1024, E=4, k=2, bias="normal1.5"),
+    # at least 512 tiles of experts averaging under 128 rows: the persistent gate/up kernel on
+    # the super-tile work order (a fixed item list per workgroup), then the 256-row down items
+    # (64 rows per expert on average) or the persistent 128-row down kernel (32)
+    "persistent_tiles_super_order": W.Workload(172, "ppso", T=4096, H=256, I=256, E=512, k=8, bias="normal1.5"),
+    "persistent_tiles_super_order_rb_down": W.Workload(173, "ppsorb", T=2048, H=256, I=256, E=512, k=8),
 }
 
 
