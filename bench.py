@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=0, help="0: the workload's own default sample")
     ap.add_argument("--expert-out", default="auto", choices=["auto", "fp32", "bf16"],
                     help="dtype of the per-assignment expert outputs between the down GEMM and the combine; auto: "
-                         "bf16 when their round trip exceeds 256 MB (the prefill shapes), else fp32")
+                         "bf16 when they would take 16 MB or more as fp32 (the prefill shapes), else fp32")
     ap.add_argument("--expert-out-bf16", action="store_true", help="same as --expert-out bf16")
     ap.add_argument("--quant", default="fp8", choices=["fp8", "mxfp8", "w4a8", "w8a16"],
                     help="fp8: E4M3 with 128-element scales (default); mxfp8: 32-element scales; "
@@ -231,6 +231,15 @@ def cpu_baseline(wl, sample_tokens: int, quant: str = "fp8", min_seconds: float 
                       f"of the full batch included; {reps} passes, {dt:.1f} s on one host thread"}
 
 
+def expert_out_dtype(wl, choice):
+    """dtype of the per-assignment expert outputs: the choice, or for "auto" bf16 once they would
+    take 16 MB or more as float32 (the prefill shapes, where writing and re-reading them is a
+    visible share of the step's traffic) and float32 below (the decode shapes, where it is free)."""
+    if choice != "auto":
+        return choice
+    return "bf16" if wl.T * (wl.k + wl.shared) * wl.H * 4 >= (16 << 20) else "fp32"
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -249,9 +258,7 @@ def main():
         wl = wl.replace(shared=1)
     if args.expert_out_bf16:
         args.expert_out = "bf16"
-    if args.expert_out == "auto":
-        args.expert_out = "bf16" if wl.T * (wl.k + wl.shared) * wl.H * 4 > (256 << 20) else "fp32"
-    args.expert_out_bf16 = args.expert_out == "bf16"
+    args.expert_out_bf16 = expert_out_dtype(wl, args.expert_out) == "bf16"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] workload {wl.name}: {W.describe(wl)}", file=sys.stderr, flush=True)

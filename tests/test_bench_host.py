@@ -89,3 +89,12 @@ def test_traffic_is_dropped_once_the_kernels_change(tmp_path, monkeypatch):
     (tmp_path / "traffic_gate_up_gemm_w.json").write_text(json.dumps(rec))
     assert bench.load_traffic("w", "gate_up_gemm") is None
     assert bench.load_traffic("absent", "gate_up_gemm") is None
+
+
+def test_expert_out_auto_is_bf16_for_the_prefill_shapes_only():
+    from gen import workloads as W
+    auto = {c: bench.expert_out_dtype(W.CONFIGS[c], "auto") for c in W.CONFIGS}
+    assert auto == {1: "fp32", 2: "fp32", 3: "bf16", 4: "bf16", 5: "bf16", 6: "bf16"}
+    assert bench.expert_out_dtype(W.CONFIGS[2].replace(shared=1), "auto") == "fp32"
+    assert bench.expert_out_dtype(W.CONFIGS[5], "fp32") == "fp32"
+    assert bench.expert_out_dtype(W.CONFIGS[1], "bf16") == "bf16"

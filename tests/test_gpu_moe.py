@@ -198,12 +198,15 @@ def test_determinism_and_row_independence():
 def test_fused_workload_full(cfg):
     wl = W.CONFIGS[cfg]
     print("fused full", cfg, W.describe(wl), flush=True)
-    y, ids, _, counts, _ = _run_fused(wl)
+    y, ids, _, counts, w = _run_fused(wl)
+    yb, ids_b, _, _, _ = _run_fused(wl, weights=w, expert_out_bf16=True)
     ref, ids_ref, _, margin = _oracle(wl)
     ok = margin >= 1e-5
-    assert np.array_equal(ids[ok], ids_ref[ok])
-    fro, mx = HN.assert_output_close(HN.bf16_to_f64(y)[ok], ref["y"][ok], f"cfg{cfg}", ref["y_bound"][ok])
-    print(f"  rel fro {fro:.2e} rel max {mx:.2e} active experts {(counts > 0).sum()}", flush=True)
+    assert np.array_equal(ids[ok], ids_ref[ok]) and np.array_equal(ids_b, ids)
+    for out, eo in ((y, "fp32"), (yb, "bf16")):
+        fro, mx = HN.assert_output_close(HN.bf16_to_f64(out)[ok], ref["y"][ok], f"cfg{cfg} {eo} expert_out",
+                                         ref["y_bound"][ok])
+        print(f"  {eo} expert_out: rel fro {fro:.2e} rel max {mx:.2e} active experts {(counts > 0).sum()}", flush=True)
 
 
 def _fused_routing(wl):
