@@ -148,12 +148,12 @@ def test_mx_fused_prefill_tiles(scheme, name):
     print(f"  rel fro {fro:.2e} rel max {mxe:.2e}", flush=True)
 
 
-# configs 2 in full; 3 and 5 on the tokens whose rows cover every 128 rows of every expert
+# configs 2 in full; 3, 4 and 5 on the tokens whose rows cover every 128 rows of every expert
 # (every 16-row tile group of these kernels' tile list holds a checked row at most 128 rows
 # away) plus every 64th token
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("scheme", list(SCHEMES))
-@pytest.mark.parametrize("cfg", [2, 3, 5])
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
 def test_mx_fused_workloads(scheme, cfg):
     quant, fmt = SCHEMES[scheme]
     wl = W.CONFIGS[cfg]
