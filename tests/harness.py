@@ -34,9 +34,23 @@ def device_params(wl: W.Workload):
 # ---- the oracle over many experts.  Worker processes (spawned: fresh interpreters that never
 # touch the GPU) quantise each expert's regenerated float32 weights with the oracle's codec
 # and run the oracle's expert FFN on its rows; the quantised weights come back and are kept
-# here for the next call on the same workload (the last two workloads are kept).
+# here for later calls that use the same weights (least recently used sets dropped first once
+# the kept bytes pass ORACLE_QCACHE_GIB, default 64).  Quantising the weights is most of the
+# oracle's time on the full-size prefill shapes, which several tests check under one scheme.
 _POOL = None
-_QCACHE: "collections.OrderedDict" = collections.OrderedDict()
+_QCACHE: "collections.OrderedDict" = collections.OrderedDict()   # weights key -> {expert: quantised}
+_QBYTES: dict = {}
+
+
+def _weights_key(wl: W.Workload, scheme: str):
+    """What an expert's quantised weights depend on: the stream keys of gen.workloads
+    (seed, workload id, expert index), the shape (H, I) and the quantisation (W8A16 reads
+    the FP8 weights)."""
+    return (wl.seed, wl.cfg, wl.H, wl.I, "fp8" if scheme == "w8a16" else scheme)
+
+
+def _qcache_budget() -> int:
+    return int(float(os.environ.get("ORACLE_QCACHE_GIB", "64")) * 2**30)
 
 
 def oracle_workers() -> int:
@@ -98,11 +112,9 @@ def oracle_ffn_map(wl: W.Workload, scheme: str = "fp8"):
     """An ``ffn_map`` for the oracle's forward functions that runs the per-expert FFNs of
     workload `wl` under quantisation scheme `scheme` ("fp8", "mxfp8", "w4a8", "w8a16") in the
     worker processes."""
-    key = (wl, "fp8" if scheme == "w8a16" else scheme)
+    key = _weights_key(wl, scheme)
     cache = _QCACHE.setdefault(key, {})
     _QCACHE.move_to_end(key)
-    while len(_QCACHE) > 2:
-        _QCACHE.popitem(last=False)
 
     def ffn_map(jobs, acc_err):
         args = [(wl, scheme, e, cache.get(e), xr, sr, b13, b2, acc_err) for e, xr, sr, b13, b2 in jobs]
@@ -110,7 +122,12 @@ def oracle_ffn_map(wl: W.Workload, scheme: str = "fp8"):
         for (e, *_), (q, r) in zip(jobs, _pool().map(_expert_job, args)):
             if q is not None:
                 cache[e] = q
+                _QBYTES[key] = _QBYTES.get(key, 0) + sum(int(np.asarray(a).nbytes) for a in q)
             out.append(r)
+        _QCACHE.move_to_end(key)
+        while sum(_QBYTES.get(k, 0) for k in _QCACHE) > _qcache_budget() and len(_QCACHE) > 1:
+            old, _ = _QCACHE.popitem(last=False)
+            _QBYTES.pop(old, None)
         return out
     return ffn_map
 

@@ -324,9 +324,10 @@ def test_fused_shared_expert(name):
 
 @pytest.mark.timeout(900)
 def test_fused_shared_expert_dsv3_prefill_sampled():
-    # the DeepSeek-V3-shaped prefill with its one shared expert (same I): tokens covering every
-    # 128-row tile of the routed experts, and with them the shared expert's tiles at every 64th
-    wl = W.CONFIGS[4].replace(cfg=145, shared=1)
+    # the DeepSeek-V3-shaped prefill with its one shared expert (same I; the routed experts'
+    # inputs and weights are the workload's own): tokens covering every 128-row tile of the
+    # routed experts, and with them the shared expert's tiles at every 64th
+    wl = W.CONFIGS[4].replace(shared=1)
     print("fused shared sampled", W.describe(wl), flush=True)
     _check_shared(wl, tokens=lambda ids: HN.item_sample_tokens(ids, wl.E))
 
