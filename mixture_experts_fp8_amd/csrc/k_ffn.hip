@@ -2048,8 +2048,13 @@ __device__ __forceinline__ void p2_store_output(const G2Args& a, v4f (&acc)[8][4
             const uint8_t* src = buf + (R1 * 256 + ((8 * m) ^ (16 * (((R1 >> 2) & 3) ^ (2 * (R1 & 1)))))) * 2;
             uint8_t* dst = reinterpret_cast<uint8_t*>(a.out) + ((int64_t)(rowbase + q * RP + R1) * a.H + nb * 256 + 8 * m) * 2;
             const int64_t rstep = (int64_t)16 * a.H * 2;
-            for (int R = R1; R < nr; R += 16, src += 16 * 512, dst += rstep)
-                *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+            // non-temporal: the expert outputs are read once, by the combine, and do not fit the
+            // caches; streaming them past the L2 and Infinity Cache leaves those to the weights
+            // and hq tiles that other items still read
+            for (int R = R1; R < nr; R += 16, src += 16 * 512, dst += rstep) {
+                typedef unsigned v4 __attribute__((ext_vector_type(4)));
+                __builtin_nontemporal_store(*reinterpret_cast<const v4*>(src), reinterpret_cast<v4*>(dst));
+            }
         }
     } else {
         constexpr int RP = BUF >= 128 * 1024 ? 128 : 64;
@@ -2082,8 +2087,9 @@ __device__ __forceinline__ void p2_store_output(const G2Args& a, v4f (&acc)[8][4
             const float* s_o = reinterpret_cast<const float*>(buf);
             for (int t = tid; t < nr * 64; t += 512) {
                 const int R = t >> 6, m = t & 63;
-                const float4 v = *reinterpret_cast<const float4*>(s_o + R * 256 + ((4 * m) ^ (16 * (((R >> 2) & 3) ^ (R & 1)))));
-                *reinterpret_cast<float4*>(out + (int64_t)(rowbase + q * RP + R) * a.H + nb * 256 + 4 * m) = v;
+                typedef float v4 __attribute__((ext_vector_type(4)));   // non-temporal as above
+                const v4 v = *reinterpret_cast<const v4*>(s_o + R * 256 + ((4 * m) ^ (16 * (((R >> 2) & 3) ^ (R & 1)))));
+                __builtin_nontemporal_store(v, reinterpret_cast<v4*>(out + (int64_t)(rowbase + q * RP + R) * a.H + nb * 256 + 4 * m));
             }
         }
     }
