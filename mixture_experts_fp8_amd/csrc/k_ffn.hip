@@ -298,6 +298,7 @@ struct G2Args {
     const int4* pairs;
     const int32_t* npairs;
     const float* b2;         // optional down bias [E, H]
+    int wnt = 0;             // 256-row down items: weights by non-temporal loads (each read by one item)
 };
 
 // down GEMM: wave (wm, wn) computes MFW m-frags x NFW column frags; the workgroup covers
@@ -724,6 +725,14 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // 16 bytes per lane from the buffer at voff + soff into LDS at m0base + 16 * lane.
 __device__ __forceinline__ void dma16_async(const v4i_t& srd, uint32_t m0base, uint32_t voff, uint32_t soff) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(m0base), "v"(voff), "s"(srd), "s"(soff)
+                 : "memory", "m0");
+}
+
+// dma16_async with the non-temporal cache policy (data read once).
+__device__ __forceinline__ void dma16_async_nt(const v4i_t& srd, uint32_t m0base, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
                  :
                  : "s"(m0base), "v"(voff), "s"(srd), "s"(soff)
                  : "memory", "m0");
@@ -2132,7 +2141,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm2_p2(G2Args a) {
         for (int i = 0; i < 4; ++i)   // fragments 8.. only for a pair with a second tile (uniform)
             if (i < 2 || second) dma16_async(ra, st + i * 8192, l16, asoff[i] + kb * kFragBytes);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma16_async(rw, st + kP2StageA + i * 8192, l16, bsoff[i] + kb * kFragBytes);
+        for (int i = 0; i < 4; ++i) {
+            if (a.wnt) dma16_async_nt(rw, st + kP2StageA + i * 8192, l16, bsoff[i] + kb * kFragBytes);
+            else dma16_async(rw, st + kP2StageA + i * 8192, l16, bsoff[i] + kb * kFragBytes);
+        }
     };
     // scales (loaded before the first DMAs, stored after): the pair's hs blocks as dwords
     // (same layout in LDS), the two weight-block scales per K block
@@ -2587,7 +2599,10 @@ static hipError_t run_ffn_dec(const FfnArgs& f, const FfnPlan& p, const FfnWs& w
 }
 
 static hipError_t launch_gemm2_p2(const FfnArgs& f, const FfnPlan& p, const FfnWs& w, int ord, hipStream_t st) {
-    const G2Args g2 = g2_args(f, w, ord);
+    G2Args g2 = g2_args(f, w, ord);
+    // experts averaging at most one 256-row item: each weight byte is read by one workgroup,
+    // and streaming the weights past the caches leaves those to the hq tiles
+    g2.wnt = (int64_t)f.T * f.k <= (int64_t)256 * f.E;
     const int grid2 = ord ? kXcds * ord_ranks(p.npairs_max, f.H / 256)
                           : (int)(ceil_div((int64_t)(f.H / 256) * p.npairs_max, kXcds) * kXcds);
     hipLaunchKernelGGL(k_gemm2_p2, dim3(grid2), dim3(512), 0, st, g2);
