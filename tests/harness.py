@@ -113,6 +113,8 @@ def oracle_ffn_map(wl: W.Workload, scheme: str = "fp8"):
     workload `wl` under quantisation scheme `scheme` ("fp8", "mxfp8", "w4a8", "w8a16") in the
     worker processes."""
     key = _weights_key(wl, scheme)
+    if key not in _QCACHE:   # new, or dropped earlier: its bytes start from zero
+        _QBYTES[key] = 0
     cache = _QCACHE.setdefault(key, {})
     _QCACHE.move_to_end(key)
 
